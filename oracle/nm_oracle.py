@@ -1,0 +1,280 @@
+"""CPU oracle for input-adaptive N:M activation pruning fused with a linear layer.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test-suite, the package's
+smoke check and the benchmark's CPU-baseline leg may import this module.  It
+shares no code, table or constant with the HIP library and never imports it.
+
+Plain, slow, obviously-correct numpy.  The mask pipeline runs in float32, one
+IEEE-rounded elementwise operation at a time (numpy never fuses a multiply
+and an add); sums whose order would matter are taken exactly with
+``math.fsum`` and rounded once.  The output ``y`` and the variance factor run
+in float64.
+
+Sources (page titles; sections as numbered on each page):
+
+* [Guide]   "Activation sparsification: a dynamic pruning method for efficient
+            LLM inference" -- s2.1 N:M patterns table, s2.2.1 magnitude pruning
+            (ACT), s2.2.3 cosine-loss activation score (CLACT), s3.1 dynamic
+            per-token shift (D-PTS / S-PTS), s3.2 variance correction (VAR),
+            s6.1 prototype N:M operator.
+* [WiSparse] "LLM inference optimisation: WiSparse activation sparsification
+            explained" -- s2.1, equation (4): weight-aware channel score.
+* [SqReLU]  "Accelerating Transformer training and inference with 2:4
+            sparsity and Squared-ReLU" -- s2.2, s3.3: squared-ReLU output as
+            the 2:4 operand; non-zeros stored contiguously with a mask.
+
+Readings taken where the pages are silent or disagree (each is listed in the
+design notes as well):
+
+* Ties at the top-N boundary: exactly N are kept per block and, among equal
+  scores, the lower in-block index wins.  (The magnitude code in [Guide]
+  s2.2.1 keeps every value >= the N-th largest, so it keeps more than N on
+  ties; the prototype in s6.1 leaves the tie order to ``topk``.)
+* What is scored under a shift: |x - eta| (the shifted value is pruned and
+  kept).
+* The weight norm of channel k is taken over the outputs: for y = x W^T with
+  W[n_out, k], it is the 2-norm of column k of W.
+* f_k = ||W[:,k]||_2^alpha is formed once from the exact sum of squares,
+  raised to alpha/2 in float64 and rounded to float32.
+* eta (D-PTS) = float32(float64(exact row sum) / K).
+* CLACT: the column energy runs over the tokens of the call, squares and
+  adds rounded in float32 with tokens in ascending order, then a correctly
+  rounded float32 square root.  The per-row factor 1/||x_i|| is a positive
+  constant of the row and cannot change any in-block ranking, so the score
+  is |x_ik - eta_i| * c_k.
+* VAR: the closed form of [Guide] s3.2 per token, population variances in
+  float64 over all K positions; a zero denominator gives nu = 1.
+* The dense term of (x_sparse + eta) W^T is split as
+  (x_hat * m) W^T + eta * (W 1): only kept rows of W^T are read.
+* Packed values are the float32 shifted values rounded to the storage dtype
+  (round-to-nearest-even); the index metadata is one uint8 in-block position
+  per kept value, ascending.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+
+
+# ----------------------------------------------------------------------------
+# Storage-dtype rounding
+# ----------------------------------------------------------------------------
+
+def round_to_dtype(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to the storage dtype (round-to-nearest-even).
+
+    Returns float32 values exactly representable in ``dtype``.  bfloat16 is
+    the upper 16 bits of an IEEE binary32; rounding to nearest-even adds
+    0x7FFF plus the lowest kept bit before truncating (finite inputs only).
+    """
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    if dtype == "f32":
+        return v.copy()
+    if dtype == "f16":
+        return v.astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        u = v.view(np.uint32).astype(np.uint64)
+        lsb = (u >> np.uint64(16)) & np.uint64(1)
+        r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+        return r.astype(np.uint32).view(np.float32)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# Weight-side precomputation (off the timed path)
+# ----------------------------------------------------------------------------
+
+def channel_factor(w: np.ndarray, alpha: float) -> np.ndarray:
+    """f_k = ||W[:,k]||_2 ** alpha as float32  ([WiSparse] s2.1, eq. (4)).
+
+    ``w`` is [n_out, k] (float32 values of the stored weight).  The sum of
+    squares is exact (``math.fsum``; each square of a float32 is exact in
+    float64), rounded once to float64; the power is taken as
+    ``sumsq ** (alpha / 2)`` in float64 and rounded to float32.
+    """
+    w64 = np.asarray(w, dtype=np.float64)
+    sq = w64 * w64                      # exact: 24x24-bit products fit in 53 bits
+    k = w64.shape[1]
+    f = np.empty(k, dtype=np.float32)
+    for c in range(k):
+        sumsq = math.fsum(sq[:, c].tolist())
+        f[c] = np.float32(sumsq ** (alpha / 2.0))
+    return f
+
+
+def row_sum(w: np.ndarray) -> np.ndarray:
+    """s_j = sum_k W[j,k], exact then rounded to float64 (the W 1 of the shift term)."""
+    w64 = np.asarray(w, dtype=np.float64)
+    return np.array([math.fsum(r.tolist()) for r in w64], dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Per-token steps ([Guide] s2.2, s3.1, s3.2; [WiSparse] s2.1)
+# ----------------------------------------------------------------------------
+
+def token_mean(x: np.ndarray) -> np.ndarray:
+    """D-PTS shift eta_i = mean over channels of x_i  ([Guide] s3.1).
+
+    float32(float64(exact sum) / K).
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    k = x64.shape[1]
+    return np.array([np.float32(math.fsum(r.tolist()) / k) for r in x64], dtype=np.float32)
+
+
+def shift(x: np.ndarray, eta: np.ndarray) -> np.ndarray:
+    """x_hat = x - eta, one float32 subtraction per element ([Guide] s3.1)."""
+    return np.asarray(x, dtype=np.float32) - np.asarray(eta, dtype=np.float32)[:, None]
+
+
+def clact_colnorm(xhat: np.ndarray) -> np.ndarray:
+    """CLACT column energy c_k = sqrt(sum_p xhat_pk^2)  ([Guide] s2.2.3).
+
+    Tokens in ascending order; every square and every add rounded to float32;
+    correctly rounded float32 square root.
+    """
+    xhat = np.asarray(xhat, dtype=np.float32)
+    acc = np.zeros(xhat.shape[1], dtype=np.float32)
+    for p in range(xhat.shape[0]):
+        sq = xhat[p] * xhat[p]
+        acc = acc + sq
+    return np.sqrt(acc)
+
+
+def scores(xhat: np.ndarray, f: Optional[np.ndarray]) -> np.ndarray:
+    """score_ik = |xhat_ik| * f_k, one float32 multiply ([Guide] s2.2.1, [WiSparse] eq. (4)).
+
+    ``f`` None means the magnitude criterion (f = 1).
+    """
+    a = np.abs(np.asarray(xhat, dtype=np.float32))
+    if f is None:
+        return a
+    return a * np.asarray(f, dtype=np.float32)[None, :]
+
+
+def topn_mask(score: np.ndarray, n: int, m: int) -> np.ndarray:
+    """Keep the top-n of every m consecutive channels ([Guide] s2.1).
+
+    Position k of a block is kept iff fewer than n positions j of the same
+    block beat it, where j beats k when score_j > score_k, or the scores are
+    equal and j < k.  Exactly n are kept per block.
+    """
+    t, k = score.shape
+    s = np.asarray(score, dtype=np.float32).reshape(t, k // m, m)
+    sj = s[:, :, :, None]          # candidate beater j on axis 2
+    sk = s[:, :, None, :]          # position k on axis 3
+    j_idx = np.arange(m)[:, None]
+    k_idx = np.arange(m)[None, :]
+    beats = (sj > sk) | ((sj == sk) & (j_idx < k_idx))
+    rank = beats.sum(axis=2)
+    return (rank < n).reshape(t, k)
+
+
+def pack(xhat: np.ndarray, keep: np.ndarray, n: int, m: int, dtype: str):
+    """Packed kept values plus uint8 in-block positions, ascending ([SqReLU] s3.3).
+
+    Returns ``(vals, idx)``: ``vals`` [t, k*n/m] float32 holding the values of
+    ``dtype`` (round-to-nearest-even of the float32 x_hat); ``idx`` [t, k*n/m]
+    uint8.
+    """
+    t, k = xhat.shape
+    pos = np.broadcast_to(np.tile(np.arange(m, dtype=np.uint8), k // m), (t, k))
+    idx = pos[keep].reshape(t, k // m * n)
+    vals = round_to_dtype(xhat, dtype)[keep].reshape(t, k // m * n)
+    return vals, idx
+
+
+def var_factor(xhat: np.ndarray, keep: np.ndarray) -> np.ndarray:
+    """nu_i = sqrt(Var[x_hat_i] / Var[x_hat_i * m_i])  ([Guide] s3.2), float64 -> float32.
+
+    Population variances over all K positions (the 1/K vs 1/(K-1) choice
+    cancels in the ratio).  A zero denominator gives nu = 1.
+    """
+    xh = np.asarray(xhat, dtype=np.float64)
+    xm = xh * keep
+    num = xh.var(axis=1)
+    den = xm.var(axis=1)
+    nu = np.ones(xh.shape[0], dtype=np.float64)
+    ok = den > 0
+    nu[ok] = np.sqrt(num[ok] / den[ok])
+    return nu.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# The whole pruning step and the linear layer
+# ----------------------------------------------------------------------------
+
+def prune(x, dtype: str, n: int, m: int, score: str = "magnitude", f=None, shift_mode: str = "none",
+          eta_in=None, var_rescale: bool = False) -> dict:
+    """Score -> per-block top-n -> pack -> (nu), for X[t, k] given as float32 values.
+
+    ``score``: "magnitude" | "weight" (needs ``f``) | "clact".
+    ``shift_mode``: "none" | "token_mean" (D-PTS) | "given" (S-PTS, ``eta_in``).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    t, k = x.shape
+    if not (1 <= n <= m) or k % m:
+        raise ValueError("need 1 <= n <= m and m | k")
+    if shift_mode == "none":
+        eta = np.zeros(t, dtype=np.float32)
+    elif shift_mode == "token_mean":
+        eta = token_mean(x)
+    elif shift_mode == "given":
+        eta = np.asarray(eta_in, dtype=np.float32).copy()
+    else:
+        raise ValueError(shift_mode)
+    xhat = shift(x, eta)
+    if score == "magnitude":
+        factor = None
+    elif score == "weight":
+        factor = np.asarray(f, dtype=np.float32)
+    elif score == "clact":
+        factor = clact_colnorm(xhat)
+    else:
+        raise ValueError(score)
+    sc = scores(xhat, factor)
+    keep = topn_mask(sc, n, m)
+    vals, idx = pack(xhat, keep, n, m, dtype)
+    out = dict(eta=eta, xhat=xhat, factor=factor, score=sc, keep=keep, vals=vals, idx=idx)
+    out["nu"] = var_factor(xhat, keep) if var_rescale else np.ones(t, dtype=np.float32)
+    return out
+
+
+def linear(pr: dict, w, s=None) -> np.ndarray:
+    """y_i = nu_i * (x_hat_i * m_i) W^T + eta_i * (W 1), float64  ([Guide] s3.1, s3.2).
+
+    ``w`` [n_out, k] float32 values; ``s`` the exact row sums (computed when None).
+    """
+    w64 = np.asarray(w, dtype=np.float64)
+    if s is None:
+        s = row_sum(w)
+    xs = pr["xhat"].astype(np.float64) * pr["keep"]
+    y = xs @ w64.T
+    y = pr["nu"].astype(np.float64)[:, None] * y
+    return y + pr["eta"].astype(np.float64)[:, None] * np.asarray(s, dtype=np.float64)[None, :]
+
+
+def linear_pages_form(pr: dict, w) -> np.ndarray:
+    """The shifted output exactly as [Guide] s3.1 writes it: (x_sparse + eta) W^T (no nu)."""
+    w64 = np.asarray(w, dtype=np.float64)
+    xs = pr["xhat"].astype(np.float64) * pr["keep"] + pr["eta"].astype(np.float64)[:, None]
+    return xs @ w64.T
+
+
+def rowwise_error(y_test: np.ndarray, y_ref: np.ndarray) -> float:
+    """max_i ( max_j |y_test - y_ref| / max_j |y_ref| ): the row-normwise relative error."""
+    y_test = np.asarray(y_test, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    if y_ref.size == 0:
+        return 0.0
+    num = np.abs(y_test - y_ref).max(axis=1)
+    den = np.abs(y_ref).max(axis=1)
+    den = np.where(den > 0, den, 1.0)
+    return float((num / den).max())
+
+
+TOLERANCE = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}

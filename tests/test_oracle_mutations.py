@@ -1,0 +1,111 @@
+"""Planted-mistake check of the oracle's pins (CPU only).
+
+Each case swaps one oracle function for a plausible wrong variant (on the
+CPU, in this process only) and asserts that at least one pin in
+``test_oracle_pins`` then fails.  This shows the pins are tight enough to
+catch that class of slip.
+"""
+import numpy as np
+import pytest
+
+from oracle import nm_oracle as O
+import test_oracle_pins as P
+
+
+def _tie_high(score, n, m):
+    t, k = score.shape
+    s = score.reshape(t, k // m, m)
+    sj, sk = s[:, :, :, None], s[:, :, None, :]
+    j, kk = np.arange(m)[:, None], np.arange(m)[None, :]
+    beats = (sj > sk) | ((sj == sk) & (j > kk))          # wrong: higher index wins
+    return (beats.sum(axis=2) < n).reshape(t, k)
+
+
+def _ge_threshold(score, n, m):                          # keeps > n on ties
+    t, k = score.shape
+    b = score.reshape(t, k // m, m)
+    thr = -np.sort(-b, axis=-1)[..., n - 1:n]
+    return (b >= thr).reshape(t, k)
+
+
+def _shift_plus(x, eta):
+    return np.asarray(x, np.float32) + np.asarray(eta, np.float32)[:, None]
+
+
+def _linear_no_eta(pr, w, s=None):
+    w64 = np.asarray(w, np.float64)
+    xs = pr["xhat"].astype(np.float64) * pr["keep"]
+    return pr["nu"].astype(np.float64)[:, None] * (xs @ w64.T)
+
+
+def _factor_rows(w, alpha):                              # transposed operand: norm of rows
+    f = _orig_factor(np.asarray(w).T.copy(), alpha)
+    return np.resize(f, np.asarray(w).shape[1]).astype(np.float32)
+
+
+def _var_inverted(xhat, keep):
+    nu = _orig_var(xhat, keep)
+    return (1.0 / nu).astype(np.float32)
+
+
+def _clact_abs(xhat):
+    return np.abs(np.asarray(xhat, np.float32)).sum(axis=0).astype(np.float32)
+
+
+def _mean_wrong_div(x):
+    x64 = np.asarray(x, np.float64)
+    return np.float32(x64.sum(axis=1) / (x64.shape[1] - 1))
+
+
+def _bf16_truncate(v, dtype):
+    v = np.ascontiguousarray(v, np.float32)
+    if dtype == "bf16":
+        return (v.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    return _orig_round(v, dtype)
+
+
+_orig_factor = O.channel_factor
+_orig_var = O.var_factor
+_orig_round = O.round_to_dtype
+
+PINS = [name for name in dir(P) if name.startswith("test_")]
+
+MUTANTS = {
+    "tie_to_higher_index": ("topn_mask", _tie_high),
+    "threshold_keeps_ties": ("topn_mask", _ge_threshold),
+    "shift_sign": ("shift", _shift_plus),
+    "drop_shift_term": ("linear", _linear_no_eta),
+    "factor_transposed": ("channel_factor", _factor_rows),
+    "nu_inverted": ("var_factor", _var_inverted),
+    "clact_no_square": ("clact_colnorm", _clact_abs),
+    "mean_wrong_divisor": ("token_mean", _mean_wrong_div),
+    "bf16_truncation": ("round_to_dtype", _bf16_truncate),
+}
+
+
+def _run_pin(fn):
+    import inspect
+    params = inspect.signature(fn).parameters
+    marks = getattr(fn, "pytestmark", [])
+    cases = [{}]
+    for mk in marks:
+        if mk.name == "parametrize":
+            names = [s.strip() for s in mk.args[0].split(",")]
+            vals = mk.args[1]
+            cases = [dict(c, **dict(zip(names, v if len(names) > 1 else (v,)))) for c in cases for v in vals]
+    for c in cases:
+        fn(**{k: c[k] for k in params})
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_some_pin_catches(mutant, monkeypatch):
+    attr, fake = MUTANTS[mutant]
+    monkeypatch.setattr(O, attr, fake)
+    failures = []
+    for name in PINS:
+        try:
+            _run_pin(getattr(P, name))
+        except Exception:                                 # noqa: BLE001 - any failure counts
+            failures.append(name)
+            break
+    assert failures, f"no pin failed with mutant {mutant}"

@@ -1,0 +1,397 @@
+"""Pins of the CPU oracle to facts other than itself (CPU only).
+
+Each test checks an oracle function against something the pages or plain
+mathematics fix: values the pages print, closed forms, brute force over all
+subsets, exact rational arithmetic, invariants, or an independent library
+routine.  A plausible slip in the oracle (a dropped term, a flipped sign or
+comparison, a transposed operand, a wrong tie order) fails at least one.
+"""
+import itertools
+import json
+import math
+import os
+import statistics
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import nm_oracle as O
+import workloads as wl
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as fh:
+        return json.load(fh)
+
+
+def _x32(t):
+    return t.float().numpy()
+
+
+# --------------------------------------------------------------------------
+# top-N rule
+# --------------------------------------------------------------------------
+
+def _brute_force_keep(scores_block, n):
+    """Best n-subset by exact sum; ties broken by the smallest sorted index tuple."""
+    best = None
+    for sub in itertools.combinations(range(len(scores_block)), n):
+        tot = sum(Fraction(float(scores_block[i])) for i in sub)
+        key = (tot, tuple(-i for i in sub))
+        if best is None or key > best[0]:
+            best = (key, sub)
+    return set(best[1])
+
+
+@pytest.mark.parametrize("n,m", [(1, 4), (2, 4), (3, 4), (4, 4), (2, 8), (4, 8), (5, 8), (8, 16), (3, 16)])
+def test_topn_matches_brute_force(n, m):
+    rng = np.random.Generator(np.random.PCG64(n * 100 + m))
+    blocks = [
+        rng.random(m).astype(np.float32),
+        np.full(m, 0.5, np.float32),
+        np.zeros(m, np.float32),
+        rng.choice(np.array([0.0, 0.25, 1.0], np.float32), m),
+        np.abs(np.repeat(rng.standard_normal(m // 2), 2)).astype(np.float32),
+    ]
+    one_big = np.full(m, 0.25, np.float32)
+    one_big[m // 3] = 4.0
+    blocks.append(one_big)
+    sc = np.stack(blocks)
+    keep = O.topn_mask(sc, n, m)
+    for r in range(sc.shape[0]):
+        got = set(np.nonzero(keep[r])[0].tolist())
+        assert got == _brute_force_keep(sc[r], n), (r, sc[r])
+
+
+def test_subset_counts_match_printed_table():
+    tab = _gold("nm_pattern_table.json")["rows"]
+    for row in tab:
+        c = math.comb(row["m"], row["n"])
+        if row["combinations"] is not None:
+            assert c == row["combinations"]
+            if row["m"] <= 16:
+                assert sum(1 for _ in itertools.combinations(range(row["m"]), row["n"])) == c
+        else:
+            # printed as "6x10^8"
+            assert c == 601080390 and round(c / 1e8) == 6
+
+
+def test_metadata_bits_match_printed_table():
+    # Information content of one block, ceil(log2 C(m,n)) bits, spread over m elements.
+    tab = _gold("nm_pattern_table.json")["rows"]
+    for row in tab:
+        bits = math.ceil(math.log2(math.comb(row["m"], row["n"]))) / row["m"]
+        if row["pattern"] == "4:8":
+            # printed 0.81; ceil(log2 70)/8 = 0.875 and log2(70)/8 = 0.766: a slip on the page
+            assert bits == 0.875
+            continue
+        assert round(bits, 2) == round(row["bits_per_element"], 2), row
+
+
+def test_tie_rule_examples():
+    for case in _gold("tie_rule_examples.json")["cases"]:
+        sc = np.array([case["scores"]], np.float32)
+        keep = O.topn_mask(sc, case["n"], case["m"])
+        assert np.nonzero(keep[0])[0].tolist() == case["kept"]
+        _, idx = O.pack(sc, keep, case["n"], case["m"], "f32")
+        assert idx[0].tolist() == case["kept"]
+
+
+@pytest.mark.parametrize("m", [4, 8, 16, 32])
+def test_exactly_n_per_block(m):
+    rng = np.random.Generator(np.random.PCG64(m))
+    for n in sorted({1, m // 4 or 1, m // 2, m - 1, m}):
+        for kind in ["random", "equal", "zeros", "signed_pairs", "signed_zero", "one_big", "few_levels"]:
+            if kind == "random":
+                x = rng.standard_normal((5, 4 * m)).astype(np.float32)
+            else:
+                x = _x32(wl.adversarial_x(kind, 5, 4 * m, m, "f32", seed=m))
+            keep = O.topn_mask(O.scores(x, None), n, m)
+            assert (keep.reshape(5, 4, m).sum(-1) == n).all(), (n, kind)
+
+
+def test_tie_free_mask_equals_page_threshold_rule():
+    # Magnitude code of the guide, s2.2.1: keep |x| >= the n-th largest |x| of its block.
+    rng = np.random.Generator(np.random.PCG64(5))
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    for n, m in [(2, 4), (4, 8), (8, 16), (16, 32)]:
+        blocks = np.abs(x).reshape(64, -1, m)
+        assert all(len(set(b.tolist())) == m for b in blocks.reshape(-1, m))  # tie free
+        thr = -np.sort(-blocks, axis=-1)[..., n - 1:n]
+        page = (blocks >= thr).reshape(64, 256)
+        assert (O.topn_mask(O.scores(x, None), n, m) == page).all()
+
+
+# --------------------------------------------------------------------------
+# shift, scores, rescale
+# --------------------------------------------------------------------------
+
+def test_token_mean_exact_rational():
+    rng = np.random.Generator(np.random.PCG64(11))
+    x = rng.standard_normal((3, 16)).astype(np.float32) * np.float32(3.0)
+    eta = O.token_mean(x)
+    for i in range(3):
+        exact = sum(Fraction(float(v)) for v in x[i]) / 16
+        assert eta[i] == np.float32(float(exact))  # one rounding of the exact mean (K a power of 2)
+
+
+def test_token_mean_order_stable_on_workloads():
+    # The mean is the exact sum rounded once; on the decode/prefill inputs a
+    # float64 sum in any order gives the same value.
+    for name in ["decode", "prefill"]:
+        spec = wl.SPECS[name].with_(t=min(wl.SPECS[name].t, 16))
+        x, _ = wl.make_inputs(spec, with_weight=False)
+        x = _x32(x).astype(np.float64)
+        eta = O.token_mean(x)
+        for order in [slice(None), slice(None, None, -1)]:
+            naive = np.array([np.float32(float(np.add.reduce(r[order], dtype=np.float64)) / x.shape[1]) for r in x])
+            assert (naive == eta).all()
+        pairwise = np.float32(x.sum(axis=1) / x.shape[1])
+        assert (pairwise == eta).all()
+
+
+def test_shift_identity_pages_form():
+    # (x_hat*m + eta) W^T  ==  (x_hat*m) W^T + eta * (W 1)
+    spec = wl.SPECS["prefill"].with_(t=6, k=64, n_out=24, n_outliers=2)
+    x, w = wl.make_inputs(spec, seed=3)
+    x, w = _x32(x), _x32(w)
+    pr = O.prune(x, "bf16", 2, 4, shift_mode="token_mean")
+    assert np.abs(pr["eta"]).max() > 0
+    a = O.linear(pr, w)
+    b = O.linear_pages_form(pr, w)
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(b).max()
+    # dropping the shift term must be visible
+    pr0 = dict(pr, eta=np.zeros_like(pr["eta"]))
+    assert np.abs(O.linear(pr0, w) - b).max() > 1e-3 * np.abs(b).max()
+
+
+def test_n_equals_m_reproduces_dense_exact():
+    rng = np.random.Generator(np.random.PCG64(2))
+    x = rng.standard_normal((2, 8)).astype(np.float32)
+    w = rng.standard_normal((3, 8)).astype(np.float32)
+    pr = O.prune(x, "f32", 4, 4)
+    assert pr["keep"].all()
+    assert (pr["idx"].reshape(2, 2, 4) == np.arange(4)).all()
+    y = O.linear(pr, w)
+    for i in range(2):
+        for j in range(3):
+            exact = sum(Fraction(float(x[i, c])) * Fraction(float(w[j, c])) for c in range(8))
+            assert abs(Fraction(float(y[i, j])) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 60)
+
+
+def test_n_equals_m_with_shift_matches_torch_dense():
+    spec = wl.SPECS["decode"].with_(t=3, k=256, n_out=40)
+    x, w = wl.make_inputs(spec, seed=1)
+    pr = O.prune(_x32(x), "bf16", 16, 16, shift_mode="token_mean")
+    y = O.linear(pr, _x32(w))
+    dense = (x.double() @ w.double().T).numpy()
+    assert O.rowwise_error(y, dense) <= 1e-6
+
+
+def test_var_factor_closed_form_rational():
+    rng = np.random.Generator(np.random.PCG64(4))
+    x = rng.laplace(0, 0.3, size=(3, 32)).astype(np.float32)
+    pr = O.prune(x, "f32", 4, 8, var_rescale=True)
+    for i in range(3):
+        full = [Fraction(float(v)) for v in pr["xhat"][i]]
+        kept = [v if k else Fraction(0) for v, k in zip(full, pr["keep"][i])]
+        ratio = statistics.pvariance(full) / statistics.pvariance(kept)
+        assert abs(float(pr["nu"][i]) - math.sqrt(ratio)) <= 1e-6 * math.sqrt(ratio)
+        assert pr["nu"][i] > 1.0      # pruning removes variance
+
+
+def test_var_factor_degenerate():
+    x = np.zeros((2, 8), np.float32)
+    x[1, 3] = 1.0
+    pr = O.prune(x, "f32", 2, 4, var_rescale=True)
+    assert pr["nu"][0] == 1.0                      # all-zero row: 0/0 -> 1
+    assert abs(pr["nu"][1] - 1.0) < 1e-7           # the single non-zero is kept: ratio 1
+
+
+def test_nu_rescales_output():
+    rng = np.random.Generator(np.random.PCG64(8))
+    x = rng.laplace(0, 0.3, (2, 64)).astype(np.float32)
+    w = rng.normal(0, 0.02, (5, 64)).astype(np.float32)
+    pr = O.prune(x, "f16", 16, 32, score="clact", var_rescale=True)
+    y = O.linear(pr, w)
+    plain = (pr["xhat"].astype(np.float64) * pr["keep"]) @ w.astype(np.float64).T
+    assert np.allclose(y, pr["nu"][:, None].astype(np.float64) * plain, rtol=1e-12, atol=0)
+
+
+def test_weight_factor_independent_norm():
+    spec = wl.SPECS["decode"].with_(k=96, n_out=300)
+    _, w = wl.make_inputs(spec)
+    w32 = _x32(w)
+    for alpha in [0.0, 0.5, 1.0, 0.3]:
+        f = O.channel_factor(w32, alpha)
+        ref = torch.linalg.vector_norm(w.double(), dim=0) ** alpha
+        assert np.allclose(f, ref.numpy(), rtol=2 ** -23, atol=0)
+    assert (O.channel_factor(w32, 0.0) == 1.0).all()
+
+
+def test_weight_factor_exact_tiny():
+    w = np.array([[3.0, 1.0], [4.0, 1.0]], np.float32)
+    assert O.channel_factor(w, 1.0).tolist() == [5.0, np.float32(math.sqrt(2.0))]
+    assert O.channel_factor(w, 2.0).tolist() == [25.0, 2.0]
+    assert O.row_sum(w).tolist() == [4.0, 5.0]
+
+
+def test_weight_aware_uses_column_norm_of_w():
+    # The factor multiplies input channel k by the norm of W's column k (outputs),
+    # so a channel whose weights are large survives against a larger activation.
+    x = np.array([[1.0, 0.9, 0.1, 0.1]], np.float32)
+    w = np.ones((3, 4), np.float32)
+    w[:, 1] = 4.0
+    f = O.channel_factor(w, 1.0)
+    pr_w = O.prune(x, "f32", 1, 4, score="weight", f=f)
+    pr_m = O.prune(x, "f32", 1, 4)
+    assert pr_m["idx"].tolist() == [[0]]
+    assert pr_w["idx"].tolist() == [[1]]
+
+
+def test_alpha_zero_equals_magnitude():
+    spec = wl.SPECS["decode"].with_(t=4, k=512, n_out=64)
+    x, w = wl.make_inputs(spec)
+    f = O.channel_factor(_x32(w), 0.0)
+    a = O.prune(_x32(x), "bf16", 8, 16, score="weight", f=f, shift_mode="token_mean")
+    b = O.prune(_x32(x), "bf16", 8, 16, score="magnitude", shift_mode="token_mean")
+    assert (a["keep"] == b["keep"]).all() and (a["vals"] == b["vals"]).all()
+
+
+def test_clact_single_token_equals_magnitude():
+    spec = wl.SPECS["batched"].with_(t=1, k=1024)
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    x = _x32(x)
+    c = O.clact_colnorm(x)
+    assert (c == np.abs(x[0])).all()   # fp16 squares are exact in fp32; sqrt of a square
+    a = O.prune(x, "f16", 16, 32, score="clact")
+    b = O.prune(x, "f16", 16, 32)
+    assert (a["keep"] == b["keep"]).all()
+
+
+def test_clact_colnorm_vs_float64_norm():
+    spec = wl.SPECS["batched"].with_(t=32, k=2048)
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    x = _x32(x)
+    c = O.clact_colnorm(x)
+    ref = np.sqrt((x.astype(np.float64) ** 2).sum(axis=0))
+    assert np.allclose(c, ref, rtol=32 * 2 ** -24, atol=0)
+
+
+def test_clact_row_factor_does_not_change_masks():
+    # The page's CLACT score also divides by the row norm ||x_i||.
+    spec = wl.SPECS["batched"].with_(t=8, k=2048)
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    x = _x32(x)
+    pr = O.prune(x, "f16", 16, 32, score="clact")
+    x64 = x.astype(np.float64)
+    full = np.abs(x64) / np.sqrt((x64 ** 2).sum(axis=1, keepdims=True)) * np.sqrt((x64 ** 2).sum(axis=0))
+    keep_full = O.topn_mask(full.astype(np.float32), 16, 32)
+    assert (keep_full != pr["keep"]).sum() == 0
+
+
+def test_scale_by_power_of_two_invariant():
+    rng = np.random.Generator(np.random.PCG64(9))
+    x = rng.standard_normal((4, 128)).astype(np.float32)
+    for n, m in [(2, 4), (8, 16), (16, 32)]:
+        a = O.topn_mask(O.scores(x, None), n, m)
+        b = O.topn_mask(O.scores(x * np.float32(8.0), None), n, m)
+        c = O.topn_mask(O.scores(x * np.float32(0.0625), None), n, m)
+        assert (a == b).all() and (a == c).all()
+
+
+def test_score_uses_shifted_value():
+    # Under a shift the score is |x - eta|: a value equal to the mean is pruned first.
+    x = np.array([[1.0, 1.0, 1.0, 5.0, 3.0, 3.0, 3.0, 3.0]], np.float32)
+    pr = O.prune(x, "f32", 1, 4, shift_mode="token_mean")
+    assert pr["eta"][0] == 2.5
+    # block 1 scores 1.5,1.5,1.5,2.5 -> position 3; block 2 all 0.5 -> position 0
+    assert pr["idx"].tolist() == [[3, 0]]
+    assert np.array_equal(pr["vals"][0], np.array([2.5, 0.5], np.float32))
+
+
+# --------------------------------------------------------------------------
+# pack and storage rounding
+# --------------------------------------------------------------------------
+
+def test_pack_reconstructs_masked_values():
+    spec = wl.SPECS["relu2"].with_(t=16, k=256)
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    x = _x32(x)
+    for dtype in ["bf16", "f16", "f32"]:
+        pr = O.prune(x, dtype, 2, 4)
+        dense = np.zeros_like(x)
+        blk = np.repeat(np.arange(x.shape[1] // 4) * 4, 2)[None, :]
+        np.put_along_axis(dense, blk + pr["idx"].astype(np.int64), pr["vals"], axis=1)
+        assert np.array_equal(dense, O.round_to_dtype(x, dtype) * pr["keep"])
+        assert (np.diff(pr["idx"].reshape(16, -1, 2).astype(int), axis=-1) > 0).all()
+
+
+@pytest.mark.parametrize("dtype,tdt", [("bf16", torch.bfloat16), ("f16", torch.float16)])
+def test_round_to_dtype_matches_torch(dtype, tdt):
+    rng = np.random.Generator(np.random.PCG64(1))
+    v = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-3).astype(np.float32),
+        np.array([0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -(1.0 + 2 ** -8)], np.float32),
+    ])
+    # exact bf16 halfway points: low 16 bits == 0x8000
+    halves = (rng.integers(0x3F000000, 0x40800000, 500, dtype=np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    v = np.concatenate([v, halves.view(np.float32)])
+    ref = torch.from_numpy(v).to(tdt).float().numpy()
+    got = O.round_to_dtype(v, dtype)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# workload statistics (generator and mask together)
+# --------------------------------------------------------------------------
+
+def test_squared_relu_standard_normal_half_zeros():
+    gold = _gold("squared_relu_sparsity.json")
+    spec = wl.SPECS["relu2"].with_(t=256, k=4096, x_dist="relu2_standard")
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    frac = float((x == 0).float().mean())
+    assert abs(frac - gold["zero_fraction_standard_normal"]) < 0.005
+
+
+def test_relu2_workload_statistics_closed_form():
+    spec = wl.SPECS["relu2"].with_(t=512)
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    x = _x32(x)
+    p = 0.5 * math.erfc(1.0 / math.sqrt(2.0))           # P(z > 0), z ~ N(-1, 1)
+    zeros = float((x == 0).mean())
+    assert abs(zeros - (1 - p)) < 0.002
+    pr = O.prune(x, "bf16", 2, 4)
+    nz = (x != 0)
+    dropped = float((nz & ~pr["keep"]).sum()) / float(nz.sum())
+    p3 = 4 * p ** 3 * (1 - p)
+    p4 = p ** 4
+    expect = (p3 * 1 + p4 * 2) / (4 * p)
+    assert abs(dropped - expect) < 0.002                # about 2.3 % of non-zeros
+    # the mask never prefers a zero over a non-zero
+    blocks_nz = nz.reshape(512, -1, 4).sum(-1)
+    kept_nz = (nz & pr["keep"]).reshape(512, -1, 4).sum(-1)
+    assert (kept_nz == np.minimum(blocks_nz, 2)).all()
+
+
+def test_workload_shapes_and_outliers():
+    spec = wl.SPECS["decode"]
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    assert x.shape == (1, 4096) and x.dtype == torch.bfloat16
+    # recipe: base values, then the outlier columns, each multiplied by the gain
+    rng = np.random.Generator(np.random.PCG64(0))
+    base = 0.5 * rng.standard_t(3.0, size=(1, 4096))
+    cols = rng.choice(4096, 8, replace=False)
+    base[:, cols] *= 20.0
+    ref = torch.from_numpy(base.astype(np.float32)).to(torch.bfloat16)
+    assert torch.equal(x, ref)
+    assert float(x[0, cols].float().abs().mean()) > 10 * float(x.float().abs().mean())
+    spec = wl.SPECS["prefill"].with_(t=64)
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    col_rms = x.float().pow(2).mean(0).sqrt()
+    assert int((col_rms > 5).sum()) == 41
