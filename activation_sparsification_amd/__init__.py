@@ -1,0 +1,18 @@
+"""N:M activation pruning fused with its linear layer, for MI355X (gfx950).
+
+The compute runs in ``libspa.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/spa.h``); this package is its thin Python binding.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    PreparedWeight,
+    PruneConfig,
+    SpaError,
+    lib,
+    prepare_weight,
+    prune_nm,
+    sparse_linear_decode,
+    sparse_linear_prefill,
+    workspace,
+    workspace_bytes,
+)

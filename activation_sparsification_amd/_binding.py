@@ -1,0 +1,207 @@
+"""ctypes binding of ``libspa.so``: argument marshalling only.
+
+Every step of the hot path runs in the library's HIP kernels.  torch is used
+for device memory, dtypes and the current stream; nothing here computes.
+If the library is missing, importing this module raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspa.so")
+
+SPA_OK, SPA_ERR_INVALID, SPA_ERR_UNSUPPORTED, SPA_ERR_HIP = 0, 1, 2, 3
+DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+SCORE = {"magnitude": 0, "weight": 1, "clact": 2}
+SHIFT = {"none": 0, "token_mean": 1, "given": 2}
+ENTRY_PRUNE, ENTRY_DECODE, ENTRY_PREFILL = 0, 1, 2
+
+
+class SpaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {lib().spa_status_str(status).decode()} (status {status})")
+        self.status = status
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("m", ctypes.c_int32), ("score", ctypes.c_int32),
+                ("shift", ctypes.c_int32), ("var_rescale", ctypes.c_int32)]
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("n_out", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("w", ctypes.c_void_p), ("wt", ctypes.c_void_p), ("chan_scale", ctypes.c_void_p),
+                ("row_sum", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is not built; run `python -m activation_sparsification_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.spa_status_str.restype = ctypes.c_char_p
+        L.spa_status_str.argtypes = [ctypes.c_int]
+        L.spa_workspace_bytes.restype = sz
+        L.spa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(_Cfg)]
+        L.prepare_weight.restype = ctypes.c_int
+        L.prepare_weight.argtypes = [vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp]
+        L.prune_nm.restype = ctypes.c_int
+        L.prune_nm.argtypes = [vp, i32, i32, i32, ctypes.POINTER(_Cfg), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for name in ("sparse_linear_decode", "sparse_linear_prefill"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [vp, i32, ctypes.POINTER(_Weight), ctypes.POINTER(_Cfg), vp, vp, vp, vp, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+EXPORTS = ("prepare_weight", "prune_nm", "sparse_linear_decode", "sparse_linear_prefill",
+           "spa_workspace_bytes", "spa_status_str")
+
+
+@dataclasses.dataclass(frozen=True)
+class PruneConfig:
+    """Keep ``n`` of every ``m`` channels; ``score`` / ``shift`` as in the C header."""
+    n: int
+    m: int
+    score: str = "magnitude"
+    shift: str = "none"
+    var_rescale: bool = False
+
+    def c(self) -> _Cfg:
+        return _Cfg(self.n, self.m, SCORE[self.score], SHIFT[self.shift], int(self.var_rescale))
+
+
+@dataclasses.dataclass
+class PreparedWeight:
+    w: torch.Tensor                      # [n_out, k]
+    wt: Optional[torch.Tensor]           # [k, n_out]
+    chan_scale: Optional[torch.Tensor]   # [k] float32
+    row_sum: Optional[torch.Tensor]      # [n_out] float32
+
+    @property
+    def n_out(self) -> int:
+        return self.w.shape[0]
+
+    @property
+    def k(self) -> int:
+        return self.w.shape[1]
+
+    def c(self, wt: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None) -> _Weight:
+        wt = self.wt if wt is None else wt
+        w = self.w if w is None else w
+        return _Weight(DTYPE[self.w.dtype], self.n_out, self.k, _ptr(w), _ptr(wt), _ptr(self.chan_scale),
+                       _ptr(self.row_sum))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != SPA_OK:
+        raise SpaError(status, where)
+
+
+def _dev(t: torch.Tensor):
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.device
+
+
+def workspace_bytes(entry: int, t: int, k: int, n_out: int, dtype: torch.dtype, cfg: PruneConfig) -> int:
+    c = cfg.c()
+    return int(lib().spa_workspace_bytes(entry, t, k, n_out, DTYPE[dtype], ctypes.byref(c)))
+
+
+_WS_CACHE: dict = {}
+
+
+def workspace(entry: int, t: int, k: int, n_out: int, dtype: torch.dtype, cfg: PruneConfig, device) -> Optional[torch.Tensor]:
+    """A zero-filled workspace of the size the library asks for (cached per device and size)."""
+    nbytes = workspace_bytes(entry, t, k, n_out, dtype, cfg)
+    if nbytes == 0:
+        return None
+    key = (str(device), entry, nbytes)
+    ws = _WS_CACHE.get(key)
+    if ws is None:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _WS_CACHE[key] = ws
+    return ws
+
+
+def prepare_weight(w: torch.Tensor, alpha: float = 0.0, want_wt: bool = True) -> PreparedWeight:
+    """Channel-major copy, per-channel norm^alpha and row sums of W[n_out, k]."""
+    dev = _dev(w)
+    n_out, k = w.shape
+    wt = torch.empty((k, n_out), dtype=w.dtype, device=dev) if want_wt else None
+    cs = torch.empty(k, dtype=torch.float32, device=dev)
+    rs = torch.empty(n_out, dtype=torch.float32, device=dev)
+    _check(lib().prepare_weight(_ptr(w), DTYPE[w.dtype], n_out, k, float(alpha), _ptr(wt), _ptr(cs), _ptr(rs),
+                                _stream(dev)), "prepare_weight")
+    return PreparedWeight(w, wt, cs, rs)
+
+
+def prune_nm(x: torch.Tensor, cfg: PruneConfig, chan_scale: Optional[torch.Tensor] = None,
+             eta_in: Optional[torch.Tensor] = None, want_idx: bool = True):
+    """Returns ``(vals [t, k*n/m], idx [t, k*n/m] uint8 or None, eta [t], nu [t])``."""
+    dev = _dev(x)
+    t, k = x.shape
+    kept = k // cfg.m * cfg.n
+    vals = torch.empty((t, kept), dtype=x.dtype, device=dev)
+    idx = torch.empty((t, kept), dtype=torch.uint8, device=dev) if want_idx else None
+    eta = torch.empty(t, dtype=torch.float32, device=dev)
+    nu = torch.empty(t, dtype=torch.float32, device=dev)
+    ws = workspace(ENTRY_PRUNE, t, k, 0, x.dtype, cfg, dev)
+    c = cfg.c()
+    _check(lib().prune_nm(_ptr(x), DTYPE[x.dtype], t, k, ctypes.byref(c), _ptr(chan_scale), _ptr(eta_in),
+                          _ptr(vals), _ptr(idx), _ptr(eta), _ptr(nu), _ptr(ws), 0 if ws is None else ws.numel(),
+                          _stream(dev)), "prune_nm")
+    return vals, idx, eta, nu
+
+
+def _linear(fn_name: str, entry: int, x: torch.Tensor, pw: PreparedWeight, cfg: PruneConfig,
+            eta_in: Optional[torch.Tensor], want_idx: bool, want_nu: bool, out: Optional[torch.Tensor],
+            ws: Optional[torch.Tensor], wt: Optional[torch.Tensor] = None):
+    dev = _dev(x)
+    t, k = x.shape
+    y = torch.empty((t, pw.n_out), dtype=x.dtype, device=dev) if out is None else out
+    idx = torch.empty((t, k // cfg.m * cfg.n), dtype=torch.uint8, device=dev) if want_idx else None
+    nu = torch.empty(t, dtype=torch.float32, device=dev) if want_nu else None
+    if ws is None:
+        ws = workspace(entry, t, k, pw.n_out, x.dtype, cfg, dev)
+    c = cfg.c()
+    wd = pw.c(wt=wt)
+    st = getattr(lib(), fn_name)(_ptr(x), t, ctypes.byref(wd), ctypes.byref(c), _ptr(eta_in), _ptr(y), _ptr(idx),
+                                 _ptr(nu), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    _check(st, fn_name)
+    return y, idx, nu
+
+
+def sparse_linear_decode(x, pw: PreparedWeight, cfg: PruneConfig, eta_in=None, want_idx=False, want_nu=False,
+                         out=None, ws=None, wt=None):
+    """Fused prune + row-skipping GEMV for 1..32 tokens.  Returns ``(y, idx, nu)``."""
+    return _linear("sparse_linear_decode", ENTRY_DECODE, x, pw, cfg, eta_in, want_idx, want_nu, out, ws, wt)
+
+
+def sparse_linear_prefill(x, pw: PreparedWeight, cfg: PruneConfig, eta_in=None, want_idx=False, want_nu=False,
+                          out=None, ws=None):
+    """Prune/pack pass + matrix-core GEMM (sparse MFMA for 2:4).  Returns ``(y, idx, nu)``."""
+    return _linear("sparse_linear_prefill", ENTRY_PREFILL, x, pw, cfg, eta_in, want_idx, want_nu, out, ws)

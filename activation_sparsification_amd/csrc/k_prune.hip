@@ -1,0 +1,295 @@
+// Pruning pass: shift, score, per-block top-n, pack, variance factor.
+//
+// One workgroup (256 threads) per token row.  Each lane owns a segment of
+// max(16, m) consecutive channels -- whole m-blocks -- and ranks every block
+// in registers with m(m-1)/2 pairwise comparisons (guide s2.1: keep n of
+// every m; ties to the lower channel index, so exactly n survive).
+//
+// Outputs (any subset): packed values + uint8 in-block positions; the
+// 2:4 nibble metadata the sparse MFMA consumes; or masked dense rows for
+// the dense-MFMA path of other n:m patterns.
+#include "spa_common.h"
+#include "spa_launch.h"
+
+namespace spa {
+
+template <int DT, int SEG>
+__device__ __forceinline__ void load_segment(const typename Dt<DT>::T* __restrict__ p, float (&v)[SEG]) {
+  if constexpr (DT == SPA_F32) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int i = 0; i < SEG / 4; ++i) {
+      const float4 f = q[i];
+      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+  } else {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < SEG / 8; ++i) {
+      const uint4 u = q[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[8 * i + e] = elem16<DT>(u, e);
+    }
+  }
+}
+
+// Keep bits of one m-block (bit j set = channel j kept).
+template <int M>
+__device__ __forceinline__ uint32_t block_keep(const float* sc, int n) {
+  int rank[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) rank[j] = 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+#pragma unroll
+    for (int q = j + 1; q < M; ++q) {
+      // j < q: j beats q unless q's score is strictly larger.
+      const bool jwins = sc[j] >= sc[q];
+      rank[q] += jwins ? 1 : 0;
+      rank[j] += jwins ? 0 : 1;
+    }
+  }
+  uint32_t keep = 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) keep |= (rank[j] < n ? 1u : 0u) << j;
+  return keep;
+}
+
+template <int DT>
+__device__ __forceinline__ float row_mean(const typename Dt<DT>::T* __restrict__ row, int k, double* s_red) {
+  double s = 0.0;
+  for (int c = threadIdx.x; c < k; c += 256) s += (double)to_f32<DT>(row[c]);
+  const double tot = block_sum(s, s_red);
+  return (float)(tot / (double)k);
+}
+
+template <int DT, int M>
+__global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
+  using T = typename Dt<DT>::T;
+  constexpr int SEG = M > 16 ? M : 16;
+  constexpr int BPS = SEG / M;
+  __shared__ double s_red[4];
+  // staging for packed outputs of one wave-iteration: 64 lanes x SEG*n/m values
+  extern __shared__ unsigned char s_dyn[];
+
+  const int row = blockIdx.x;
+  const int n = a.n;
+  const int kept_row = a.k / M * n;        // packed values per row
+  const int kept_seg = BPS * n;            // packed values per segment
+  const T* xr = static_cast<const T*>(a.x) + (size_t)row * a.k;
+
+  float eta = 0.f;
+  if (a.shift_mean) {
+    eta = row_mean<DT>(xr, a.k, s_red);
+  } else if (a.eta_given) {
+    eta = a.eta_given[row];
+  }
+  if (threadIdx.x == 0) {
+    if (a.eta_out) a.eta_out[row] = eta;
+  }
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  T* s_vals = reinterpret_cast<T*>(s_dyn) + (size_t)wv * 64 * kept_seg;
+  uint8_t* s_idx = reinterpret_cast<uint8_t*>(s_dyn + (size_t)4 * 64 * kept_seg * sizeof(T)) + (size_t)wv * 64 * kept_seg;
+
+  double sx = 0.0, sxx = 0.0, sm = 0.0, smm = 0.0;
+  const int nseg = a.k / SEG;
+  // All lanes of a wave run the same number of iterations so the wave-wide
+  // copy-out below stays convergent.
+  const int iters = (nseg + 255) / 256;
+  for (int it = 0; it < iters; ++it) {
+    const int seg = it * 256 + threadIdx.x;
+    const bool active = seg < nseg;
+    uint32_t keepbits[BPS];
+    float xh[SEG];
+    if (active) {
+      float xv[SEG];
+      load_segment<DT, SEG>(xr + (size_t)seg * SEG, xv);
+#pragma unroll
+      for (int j = 0; j < SEG; ++j) xh[j] = xv[j] - eta;
+      float sc[SEG];
+      if (a.colnorm) {
+        const float* f = a.colnorm + (size_t)seg * SEG;
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) sc[j] = __builtin_fabsf(xh[j]) * f[j];
+      } else if (a.chan_scale) {
+        const float* f = a.chan_scale + (size_t)seg * SEG;
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) sc[j] = __builtin_fabsf(xh[j]) * f[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) sc[j] = __builtin_fabsf(xh[j]);
+      }
+#pragma unroll
+      for (int b = 0; b < BPS; ++b) keepbits[b] = block_keep<M>(sc + b * M, n);
+
+      if (a.var) {
+#pragma unroll
+        for (int b = 0; b < BPS; ++b)
+#pragma unroll
+          for (int j = 0; j < M; ++j) {
+            const double v = (double)xh[b * M + j];
+            sx += v;
+            sxx += v * v;
+            if ((keepbits[b] >> j) & 1u) { sm += v; smm += v * v; }
+          }
+      }
+      if (a.pack & kPackMeta24) {
+        // 2:4: per block the nibble (lo | hi << 2); four blocks per uint16.
+        uint32_t meta = 0;
+#pragma unroll
+        for (int b = 0; b < BPS; ++b) {
+          const uint32_t kb = keepbits[b];
+          const uint32_t lo = __builtin_ctz(kb);
+          const uint32_t hi = 31 - __builtin_clz(kb);
+          meta |= (lo | (hi << 2)) << (4 * b);
+        }
+        a.meta[(size_t)row * (a.k / 16) + seg] = (uint16_t)meta;
+      }
+      if (a.pack & kPackDense) {
+        T* d = static_cast<T*>(a.dense) + (size_t)row * a.k + (size_t)seg * SEG;
+        if constexpr (DT == SPA_F32) {
+#pragma unroll
+          for (int i = 0; i < SEG / 4; ++i) {
+            float4 f;
+            f.x = ((keepbits[(4 * i) / M] >> ((4 * i) % M)) & 1u) ? xh[4 * i] : 0.f;
+            f.y = ((keepbits[(4 * i + 1) / M] >> ((4 * i + 1) % M)) & 1u) ? xh[4 * i + 1] : 0.f;
+            f.z = ((keepbits[(4 * i + 2) / M] >> ((4 * i + 2) % M)) & 1u) ? xh[4 * i + 2] : 0.f;
+            f.w = ((keepbits[(4 * i + 3) / M] >> ((4 * i + 3) % M)) & 1u) ? xh[4 * i + 3] : 0.f;
+            reinterpret_cast<float4*>(d)[i] = f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < SEG / 8; ++i) {
+            uint32_t wds[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const int j0 = 8 * i + 2 * p, j1 = j0 + 1;
+              const uint32_t v0 = ((keepbits[j0 / M] >> (j0 % M)) & 1u) ? (uint32_t)from_f32<DT>(xh[j0]) : 0u;
+              const uint32_t v1 = ((keepbits[j1 / M] >> (j1 % M)) & 1u) ? (uint32_t)from_f32<DT>(xh[j1]) : 0u;
+              wds[p] = v0 | (v1 << 16);
+            }
+            reinterpret_cast<uint4*>(d)[i] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+          }
+        }
+      }
+      if (a.pack & kPackVals) {
+        // Kept values in ascending channel order, staged per wave in LDS.
+        int pos = lane * kept_seg;
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) {
+          if ((keepbits[j / M] >> (j % M)) & 1u) {
+            s_vals[pos] = from_f32<DT>(xh[j]);
+            s_idx[pos] = (uint8_t)(j % M);
+            ++pos;
+          }
+        }
+      }
+    }
+    if (a.pack & kPackVals) {
+      // Copy the wave's contiguous run of packed values out.
+      __syncthreads();
+      const int seg0 = it * 256 + wv * 64;
+      const int nseg_w = min(64, nseg - seg0);
+      if (nseg_w > 0) {
+        const int cnt = nseg_w * kept_seg;
+        T* vdst = a.vals ? static_cast<T*>(a.vals) + (size_t)row * kept_row + (size_t)seg0 * kept_seg : nullptr;
+        if (a.vals)
+          for (int e = lane; e < cnt; e += 64) vdst[e] = s_vals[e];
+        if (a.idx) {
+          uint8_t* idst = a.idx + (size_t)row * kept_row + (size_t)seg0 * kept_seg;
+          for (int e = lane; e < cnt; e += 64) idst[e] = s_idx[e];
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  if (a.var || a.nu_out) {
+    float nu = 1.f;
+    if (a.var) {
+      const double tx = block_sum(sx, s_red);
+      const double txx = block_sum(sxx, s_red);
+      const double tm = block_sum(sm, s_red);
+      const double tmm = block_sum(smm, s_red);
+      const double kk = (double)a.k;
+      const double var_full = txx / kk - (tx / kk) * (tx / kk);
+      const double var_mask = tmm / kk - (tm / kk) * (tm / kk);
+      if (var_mask > 0.0) nu = (float)__builtin_sqrt(var_full / var_mask);
+    }
+    if (threadIdx.x == 0 && a.nu_out) a.nu_out[row] = nu;
+  }
+}
+
+template <int DT>
+__global__ void __launch_bounds__(256) k_token_mean(const typename Dt<DT>::T* __restrict__ x, int k,
+                                                    float* __restrict__ eta) {
+  __shared__ double s_red[4];
+  const float e = row_mean<DT>(x + (size_t)blockIdx.x * k, k, s_red);
+  if (threadIdx.x == 0) eta[blockIdx.x] = e;
+}
+
+// CLACT column energy, one thread per channel, tokens in ascending order.
+template <int DT>
+__global__ void __launch_bounds__(256) k_colnorm(const typename Dt<DT>::T* __restrict__ x,
+                                                 const float* __restrict__ eta, int t, int k, float* __restrict__ c) {
+  const int ch = blockIdx.x * 256 + threadIdx.x;
+  if (ch >= k) return;
+  float acc = 0.f;
+  for (int p = 0; p < t; ++p) {
+    const float v = to_f32<DT>(x[(size_t)p * k + ch]) - (eta ? eta[p] : 0.f);
+    acc = clact_accumulate(acc, v);
+  }
+  c[ch] = sqrt_rn(acc);
+}
+
+template <int DT, int M>
+static hipError_t prune_m(const PruneArgs& a, hipStream_t st) {
+  constexpr int SEG = M > 16 ? M : 16;
+  const int kept_seg = SEG / M * a.n;
+  const size_t lds = (a.pack & kPackVals) ? (size_t)4 * 64 * kept_seg * (Dt<DT>::bytes + 1) : 0;
+  hipLaunchKernelGGL((k_prune<DT, M>), dim3(a.t), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t prune_dt(const PruneArgs& a, hipStream_t st) {
+  switch (a.m) {
+    case 4: return prune_m<DT, 4>(a, st);
+    case 8: return prune_m<DT, 8>(a, st);
+    case 16: return prune_m<DT, 16>(a, st);
+    default: return prune_m<DT, 32>(a, st);
+  }
+}
+
+hipError_t launch_prune(int dtype, const PruneArgs& a, hipStream_t st) {
+  if (a.t == 0) return hipSuccess;
+  switch (dtype) {
+    case SPA_F32: return prune_dt<SPA_F32>(a, st);
+    case SPA_F16: return prune_dt<SPA_F16>(a, st);
+    default: return prune_dt<SPA_BF16>(a, st);
+  }
+}
+
+hipError_t launch_token_mean(int dtype, const void* x, int t, int k, float* eta, hipStream_t st) {
+  if (t == 0) return hipSuccess;
+  switch (dtype) {
+    case SPA_F32: hipLaunchKernelGGL(k_token_mean<SPA_F32>, dim3(t), dim3(256), 0, st, (const float*)x, k, eta); break;
+    case SPA_F16: hipLaunchKernelGGL(k_token_mean<SPA_F16>, dim3(t), dim3(256), 0, st, (const uint16_t*)x, k, eta); break;
+    default: hipLaunchKernelGGL(k_token_mean<SPA_BF16>, dim3(t), dim3(256), 0, st, (const uint16_t*)x, k, eta); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_colnorm(int dtype, const void* x, const float* eta, int t, int k, float* c, hipStream_t st) {
+  const dim3 grid((k + 255) / 256);
+  switch (dtype) {
+    case SPA_F32: hipLaunchKernelGGL(k_colnorm<SPA_F32>, grid, dim3(256), 0, st, (const float*)x, eta, t, k, c); break;
+    case SPA_F16: hipLaunchKernelGGL(k_colnorm<SPA_F16>, grid, dim3(256), 0, st, (const uint16_t*)x, eta, t, k, c); break;
+    default: hipLaunchKernelGGL(k_colnorm<SPA_BF16>, grid, dim3(256), 0, st, (const uint16_t*)x, eta, t, k, c); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace spa

@@ -1,0 +1,241 @@
+// C ABI of the library: argument validation, workspace layout, dispatch.
+// Every rejection happens here, before anything is launched.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/spa.h"
+#include "spa_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int dtype_bytes(int dt) { return dt == SPA_F32 ? 4 : 2; }
+bool valid_dtype(int dt) { return dt == SPA_F32 || dt == SPA_F16 || dt == SPA_BF16; }
+
+bool valid_cfg(const spa_prune_cfg* c) {
+  if (!c) return false;
+  if (c->m != 4 && c->m != 8 && c->m != 16 && c->m != 32) return false;
+  if (c->n < 1 || c->n > c->m) return false;
+  if (c->score < SPA_SCORE_MAGNITUDE || c->score > SPA_SCORE_CLACT) return false;
+  if (c->shift < SPA_SHIFT_NONE || c->shift > SPA_SHIFT_GIVEN) return false;
+  if (c->var_rescale != 0 && c->var_rescale != 1) return false;
+  return true;
+}
+
+// k must hold whole m-blocks and whole 16-channel segments of the pruning pass.
+bool valid_k(int64_t k, const spa_prune_cfg* c) { return k >= 16 && k <= kMaxDim && k % 16 == 0 && k % c->m == 0; }
+
+spa_status hip_status(hipError_t e) { return e == hipSuccess ? SPA_OK : SPA_ERR_HIP; }
+
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// ---- prune workspace: [colnorm k f32][eta t f32] (CLACT only) ----
+size_t prune_ws(int t, int k, const spa_prune_cfg* c) {
+  if (c->score != SPA_SCORE_CLACT) return 0;
+  return round256((size_t)k * 4) + round256((size_t)t * 4);
+}
+
+// ---- prefill workspace ----
+struct PrefillPlan {
+  size_t vals, meta, eta, nu, colnorm, bytes;
+};
+PrefillPlan prefill_plan(int t, int k, int dtype, const spa_prune_cfg* c) {
+  PrefillPlan p{};
+  const bool s24 = c->n == 2 && c->m == 4;
+  size_t off = 0;
+  p.vals = off; off += round256((size_t)t * (s24 ? k / 2 : k) * dtype_bytes(dtype));
+  p.meta = off; off += s24 ? round256((size_t)t * (k / 16) * 2) : 0;
+  p.eta = off; off += round256((size_t)t * 4);
+  p.nu = off; off += round256((size_t)t * 4);
+  p.colnorm = off; off += c->score == SPA_SCORE_CLACT ? round256((size_t)k * 4) : 0;
+  p.bytes = off;
+  return p;
+}
+
+spa_status check_linear(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg, const float* eta_in,
+                        const void* y, bool decode) {
+  if (!x || !y || !w || !valid_cfg(cfg)) return SPA_ERR_INVALID;
+  if (!valid_dtype(w->dtype)) return SPA_ERR_INVALID;
+  if (decode ? (t < 1 || t > 32) : (t < 0 || t > kMaxDim)) return SPA_ERR_INVALID;
+  if (w->n_out < 1 || w->n_out > kMaxDim || !valid_k(w->k, cfg)) return SPA_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(y)) return SPA_ERR_INVALID;
+  if (cfg->score == SPA_SCORE_WEIGHT && !w->chan_scale) return SPA_ERR_INVALID;
+  if (cfg->shift == SPA_SHIFT_GIVEN && !eta_in) return SPA_ERR_INVALID;
+  if (cfg->shift != SPA_SHIFT_NONE && !w->row_sum) return SPA_ERR_INVALID;
+  if (decode) {
+    if (!w->wt || !aligned16(w->wt)) return SPA_ERR_INVALID;
+    if (w->n_out % (16 / dtype_bytes(w->dtype))) return SPA_ERR_INVALID;
+  } else {
+    if (!w->w || !aligned16(w->w)) return SPA_ERR_INVALID;
+    if (w->k % 64) return SPA_ERR_INVALID;
+  }
+  return SPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spa_status_str(spa_status s) {
+  switch (s) {
+    case SPA_OK: return "ok";
+    case SPA_ERR_INVALID: return "invalid argument";
+    case SPA_ERR_UNSUPPORTED: return "unsupported combination";
+    case SPA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t spa_workspace_bytes(int32_t entry, int32_t t, int32_t k, int32_t n_out, int32_t dtype,
+                           const spa_prune_cfg* cfg) {
+  if (!valid_cfg(cfg) || !valid_dtype(dtype) || !valid_k(k, cfg) || t < 0 || t > kMaxDim || n_out < 0 ||
+      n_out > kMaxDim)
+    return 0;
+  switch (entry) {
+    case SPA_ENTRY_PRUNE: return prune_ws(t, k, cfg);
+    case SPA_ENTRY_DECODE:
+      if (t < 1 || t > 32 || n_out < 1) return 0;
+      return spa::decode_workspace(t, k, n_out, dtype, cfg->n, cfg->m, cfg->score, cfg->shift, cfg->var_rescale,
+                                   nullptr);
+    case SPA_ENTRY_PREFILL: return prefill_plan(t, k, dtype, cfg).bytes;
+    default: return 0;
+  }
+}
+
+spa_status prepare_weight(const void* w, int32_t dtype, int32_t n_out, int32_t k, float alpha, void* wt_out,
+                          float* chan_scale_out, float* row_sum_out, void* stream) {
+  if (!w || !valid_dtype(dtype) || n_out < 1 || k < 1 || n_out > kMaxDim || k > kMaxDim) return SPA_ERR_INVALID;
+  if (!(alpha >= 0.f && alpha <= 16.f)) return SPA_ERR_INVALID;
+  return hip_status(spa::launch_prepare(dtype, w, n_out, k, alpha, wt_out, chan_scale_out, row_sum_out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const spa_prune_cfg* cfg,
+                    const float* chan_scale, const float* eta_in, void* vals_out, uint8_t* idx_out, float* eta_out,
+                    float* nu_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_cfg(cfg) || !valid_dtype(dtype) || !valid_k(k, cfg) || t < 0 || t > kMaxDim) return SPA_ERR_INVALID;
+  if (t == 0) return SPA_OK;
+  if (!x || !vals_out || !aligned16(x) || !aligned16(vals_out)) return SPA_ERR_INVALID;
+  if (cfg->score == SPA_SCORE_WEIGHT && !chan_scale) return SPA_ERR_INVALID;
+  if (cfg->shift == SPA_SHIFT_GIVEN && !eta_in) return SPA_ERR_INVALID;
+  const size_t need = prune_ws(t, k, cfg);
+  if (need && (!workspace || workspace_bytes < need || !aligned16(workspace))) return SPA_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  spa::PruneArgs a{};
+  a.x = x; a.t = t; a.k = k; a.n = cfg->n; a.m = cfg->m;
+  a.var = cfg->var_rescale;
+  a.chan_scale = cfg->score == SPA_SCORE_WEIGHT ? chan_scale : nullptr;
+  a.eta_given = cfg->shift == SPA_SHIFT_GIVEN ? eta_in : nullptr;
+  a.shift_mean = cfg->shift == SPA_SHIFT_TOKEN_MEAN;
+  if (cfg->score == SPA_SCORE_CLACT) {
+    float* colnorm = reinterpret_cast<float*>(workspace);
+    float* eta_ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)k * 4));
+    const float* eta = a.eta_given;
+    if (cfg->shift == SPA_SHIFT_TOKEN_MEAN) {
+      if (hipError_t e = spa::launch_token_mean(dtype, x, t, k, eta_ws, st)) return hip_status(e);
+      eta = eta_ws;
+      a.eta_given = eta_ws;
+      a.shift_mean = 0;
+    }
+    if (hipError_t e = spa::launch_colnorm(dtype, x, eta, t, k, colnorm, st)) return hip_status(e);
+    a.colnorm = colnorm;
+  }
+  a.pack = spa::kPackVals;
+  a.vals = vals_out;
+  a.idx = idx_out;
+  a.eta_out = eta_out;
+  a.nu_out = nu_out;
+  return hip_status(spa::launch_prune(dtype, a, st));
+}
+
+spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
+                                const float* eta_in, void* y, uint8_t* idx_out, float* nu_out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (spa_status s = check_linear(x, t, w, cfg, eta_in, y, true)) return s;
+  if (w->dtype == SPA_F32 && t > 8) return SPA_ERR_UNSUPPORTED;
+  spa::DecodeArgs a{};
+  const size_t need = spa::decode_workspace(t, w->k, w->n_out, w->dtype, cfg->n, cfg->m, cfg->score, cfg->shift,
+                                            cfg->var_rescale, &a);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SPA_ERR_INVALID;
+  char* base = static_cast<char*>(workspace);
+  auto fix = [&](auto*& ptr) { ptr = reinterpret_cast<std::remove_reference_t<decltype(ptr)>>(base + reinterpret_cast<uintptr_t>(ptr)); };
+  fix(a.partial);
+  fix(a.stats);
+  fix(a.counters);
+  fix(a.eta_ws);
+  if (a.tokmask) fix(a.tokmask);
+  if (a.coef) fix(a.coef);
+  a.x = x;
+  a.wt = w->wt;
+  a.chan_scale = w->chan_scale;
+  a.row_sum = w->row_sum;
+  a.eta = cfg->shift == SPA_SHIFT_GIVEN ? eta_in : nullptr;
+  a.y = y;
+  a.idx_out = idx_out;
+  a.nu_out = nu_out;
+  return hip_status(spa::launch_decode(w->dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
+                                 const float* eta_in, void* y, uint8_t* idx_out, float* nu_out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (spa_status s = check_linear(x, t, w, cfg, eta_in, y, false)) return s;
+  if (w->dtype == SPA_F32) return SPA_ERR_UNSUPPORTED;
+  if (t == 0) return SPA_OK;
+  const int k = w->k;
+  const PrefillPlan pl = prefill_plan(t, k, w->dtype, cfg);
+  if (!workspace || workspace_bytes < pl.bytes || !aligned16(workspace)) return SPA_ERR_INVALID;
+  char* base = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool s24 = cfg->n == 2 && cfg->m == 4;
+  float* eta_ws = reinterpret_cast<float*>(base + pl.eta);
+  float* nu_ptr = nu_out ? nu_out : reinterpret_cast<float*>(base + pl.nu);
+
+  spa::PruneArgs a{};
+  a.x = x; a.t = t; a.k = k; a.n = cfg->n; a.m = cfg->m;
+  a.var = cfg->var_rescale;
+  a.chan_scale = cfg->score == SPA_SCORE_WEIGHT ? w->chan_scale : nullptr;
+  a.eta_given = cfg->shift == SPA_SHIFT_GIVEN ? eta_in : nullptr;
+  a.shift_mean = cfg->shift == SPA_SHIFT_TOKEN_MEAN;
+  if (cfg->score == SPA_SCORE_CLACT) {
+    float* colnorm = reinterpret_cast<float*>(base + pl.colnorm);
+    if (cfg->shift == SPA_SHIFT_TOKEN_MEAN) {
+      if (hipError_t e = spa::launch_token_mean(w->dtype, x, t, k, eta_ws, st)) return hip_status(e);
+      a.eta_given = eta_ws;
+      a.shift_mean = 0;
+    }
+    if (hipError_t e = spa::launch_colnorm(w->dtype, x, a.eta_given, t, k, colnorm, st)) return hip_status(e);
+    a.colnorm = colnorm;
+  }
+  a.eta_out = eta_ws;
+  a.nu_out = (cfg->var_rescale || nu_out) ? nu_ptr : nullptr;
+  if (s24) {
+    a.pack = spa::kPackVals | spa::kPackMeta24;
+    a.vals = base + pl.vals;
+    a.meta = reinterpret_cast<uint16_t*>(base + pl.meta);
+    a.idx = idx_out;
+  } else {
+    a.pack = spa::kPackDense | (idx_out ? spa::kPackVals : 0);
+    a.dense = base + pl.vals;
+    a.vals = nullptr;
+    a.idx = idx_out;
+  }
+  if (hipError_t e = spa::launch_prune(w->dtype, a, st)) return hip_status(e);
+
+  spa::PrefillArgs g{};
+  g.w = w->w;
+  g.row_sum = w->row_sum;
+  g.a_vals = base + pl.vals;
+  g.a_meta = s24 ? reinterpret_cast<const uint16_t*>(base + pl.meta) : nullptr;
+  g.eta = cfg->shift != SPA_SHIFT_NONE ? eta_ws : nullptr;
+  g.nu = cfg->var_rescale ? nu_ptr : nullptr;
+  g.y = y;
+  g.t = t; g.k = k; g.n_out = w->n_out;
+  g.sparse24 = s24 ? 1 : 0;
+  return hip_status(spa::launch_gemm(w->dtype, g, st));
+}
+
+}  // extern "C"

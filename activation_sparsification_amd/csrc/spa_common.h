@@ -1,0 +1,106 @@
+// Shared device helpers of the N:M activation-pruning library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/spa.h"
+
+namespace spa {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Storage dtypes.  16-bit values travel as raw uint16_t bits.
+// ---------------------------------------------------------------------------
+template <int DT> struct Dt;
+template <> struct Dt<SPA_F32> { using T = float; static constexpr int bytes = 4; };
+template <> struct Dt<SPA_F16> { using T = uint16_t; static constexpr int bytes = 2; };
+template <> struct Dt<SPA_BF16> { using T = uint16_t; static constexpr int bytes = 2; };
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float f16_to_f32(uint32_t u) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)u);
+}
+// Round-to-nearest-even float -> bfloat16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t f32_to_f16(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <int DT> __device__ __forceinline__ float to_f32(typename Dt<DT>::T v);
+template <> __device__ __forceinline__ float to_f32<SPA_F32>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<SPA_F16>(uint16_t v) { return f16_to_f32(v); }
+template <> __device__ __forceinline__ float to_f32<SPA_BF16>(uint16_t v) { return bf16_to_f32(v); }
+
+template <int DT> __device__ __forceinline__ typename Dt<DT>::T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<SPA_F32>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t from_f32<SPA_F16>(float v) { return (uint16_t)f32_to_f16(v); }
+template <> __device__ __forceinline__ uint16_t from_f32<SPA_BF16>(float v) { return (uint16_t)f32_to_bf16(v); }
+
+// Element e (0..7) of a 16-byte vector of 16-bit values.
+template <int DT> __device__ __forceinline__ float elem16(const uint4& v, int e) {
+  uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+  return DT == SPA_BF16 ? bf16_to_f32(h) : f16_to_f32(h);
+}
+
+// ---------------------------------------------------------------------------
+// The mask arithmetic.  Every helper is a single IEEE operation so that the
+// GPU reproduces the reference definition bit for bit.
+// ---------------------------------------------------------------------------
+// CLACT column energy: one float32 square and one float32 add per token, in
+// token order, never fused into an FMA.
+__device__ __forceinline__ float clact_accumulate(float acc, float v) {
+#pragma clang fp contract(off)
+  float sq = v * v;
+  return acc + sq;
+}
+// Correctly rounded float32 square root: the float64 root of a float32 is
+// rounded once more without error (53 >= 2*24 + 2).
+__device__ __forceinline__ float sqrt_rn(float a) { return (float)__builtin_sqrt((double)a); }
+
+// "j beats k" in the top-n rule: a larger score, or an equal score at a lower index.
+__device__ __forceinline__ bool beats(float sj, int j, float sk, int k) {
+  return (sj > sk) || (sj == sk && j < k);
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup reductions (blockDim.x == 256).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Sum of one double per thread, identical on every thread.  Fixed order:
+// butterfly within each wave, then waves 0..3 in order.
+__device__ __forceinline__ double block_sum(double v, double* s_tmp /*[4]*/) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) s_tmp[w] = v;
+  __syncthreads();
+  return ((s_tmp[0] + s_tmp[1]) + s_tmp[2]) + s_tmp[3];
+}
+
+// Exclusive prefix count of `flag` over the 256 threads; *total gets the sum.
+__device__ __forceinline__ int block_exclusive_count(bool flag, int* s_tmp /*[4]*/, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const unsigned long long bal = __ballot(flag);
+  const int before = __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+  __syncthreads();
+  if (lane == 0) s_tmp[w] = __popcll(bal);
+  __syncthreads();
+  int off = 0;
+  for (int i = 0; i < w; ++i) off += s_tmp[i];
+  *total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+  return off + before;
+}
+
+}  // namespace spa

@@ -1,0 +1,81 @@
+// Host-side launchers of the kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spa {
+
+hipError_t launch_prepare(int dtype, const void* w, int n_out, int k, float alpha, void* wt, float* cs, float* rs,
+                          hipStream_t st);
+
+// ---- pruning pass (one workgroup per token row) ----
+enum PackFormat : int {
+  kPackVals = 1,    // vals[t][k*n/m] (dtype) + optional idx[t][k*n/m] (uint8)
+  kPackMeta24 = 2,  // 2:4 only: meta16[t][k/16], one nibble (lo | hi << 2) per block
+  kPackDense = 4,   // masked dense rows xm[t][k] (dtype), zeros at pruned channels
+};
+
+struct PruneArgs {
+  const void* x;
+  const float* chan_scale;   // weight score factor, or NULL
+  const float* colnorm;      // CLACT factor (from launch_colnorm), or NULL
+  const float* eta_given;    // precomputed / caller shift, or NULL
+  int t, k, n, m;
+  int shift_mean;            // compute the token mean in-kernel
+  int var;
+  int pack;                  // PackFormat bits
+  void* vals;                // kPackVals
+  uint8_t* idx;              // kPackVals, may be NULL
+  uint16_t* meta;            // kPackMeta24
+  void* dense;               // kPackDense
+  float* eta_out;            // may be NULL
+  float* nu_out;             // may be NULL
+};
+hipError_t launch_prune(int dtype, const PruneArgs& a, hipStream_t st);
+hipError_t launch_token_mean(int dtype, const void* x, int t, int k, float* eta, hipStream_t st);
+hipError_t launch_colnorm(int dtype, const void* x, const float* eta, int t, int k, float* c, hipStream_t st);
+
+// ---- decode ----
+struct DecodeArgs {
+  const void* x;
+  const void* wt;
+  const float* chan_scale;
+  const float* row_sum;
+  const float* eta;          // precomputed or caller-given shift, or NULL
+  void* y;
+  uint8_t* idx_out;
+  float* nu_out;
+  int t, k, n_out, n, m;
+  int score;                 // SPA_SCORE_*
+  int shift;                 // SPA_SHIFT_*
+  int var;
+  // workspace carve-up
+  float* partial;            // [splits][t][n_out]
+  double* stats;             // [tiles][splits][t][4] or [mask groups][t][4]
+  unsigned* counters;        // [tiles]
+  uint32_t* tokmask;         // [k]            (mask-then-stream path)
+  uint16_t* coef;            // [k][32] dtype  (mask-then-stream path)
+  float* eta_ws;             // [t]
+  int tiles, splits, k_len, col_tile, mask_groups;
+};
+size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int score, int shift, int var,
+                        DecodeArgs* plan);
+hipError_t launch_decode(int dtype, DecodeArgs& a, hipStream_t st);
+
+// ---- prefill ----
+struct PrefillArgs {
+  const void* w;             // [n_out][k]
+  const float* row_sum;
+  const void* a_vals;        // 2:4: packed [t][k/2]; other n:m: masked dense [t][k]
+  const uint16_t* a_meta;    // 2:4 only
+  const float* eta;          // [t] or NULL
+  const float* nu;           // [t] or NULL
+  void* y;
+  int t, k, n_out;
+  int sparse24;
+};
+hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st);
+
+}  // namespace spa

@@ -1,0 +1,170 @@
+/*
+ * spa.h -- C ABI of the MI355X (gfx950) library for input-adaptive N:M
+ * activation pruning fused with the linear layer that consumes it.
+ *
+ * For each token x (a row of X[t][k]) and a linear layer y = x W^T with
+ * W[n_out][k]:
+ *
+ *   eta      per-token shift: 0, the token mean (dynamic per-token shift,
+ *            "Activation sparsification: a dynamic pruning method for
+ *            efficient LLM inference" s3.1), or a caller-given value (the
+ *            static variant of the same section);
+ *   x_hat    = x - eta, one float32 subtraction;
+ *   score_k  = |x_hat_k| * f_k with f_k = 1 (magnitude, same guide s2.2.1),
+ *            f_k = ||W[:,k]||_2^alpha (weight-aware, "LLM inference
+ *            optimisation: WiSparse activation sparsification explained"
+ *            s2.1 eq. (4)), or f_k = sqrt(sum over the call's tokens of
+ *            x_hat_pk^2) (cosine-loss CLACT score, guide s2.2.3; the per-row
+ *            factor of that score cannot change an in-block ranking);
+ *   mask     keep the n largest scores of every m consecutive channels
+ *            (guide s2.1); equal scores go to the lower channel index, so
+ *            exactly n are kept per block;
+ *   nu       optional variance rescale sqrt(Var[x_hat] / Var[x_hat * mask])
+ *            per token (guide s3.2, closed form; 1 when the denominator is 0);
+ *   y        = nu * (x_hat * mask) W^T + eta * (W 1), which equals the
+ *            guide's (x_sparse + eta) W^T without reading pruned rows of W.
+ *
+ * Numerics of the mask: eta is the float64 sum rounded to float64, divided
+ * by k in float64, rounded to float32; scores are single float32 products;
+ * CLACT sums squares in float32 over tokens in ascending order (no fused
+ * multiply-add) and takes a correctly rounded square root.  Masks, packed
+ * values and indices are therefore reproducible bit for bit.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked [device] are device memory owned by the caller; the
+ *    library never allocates, frees or keeps them.  Host pointers (the
+ *    config and weight descriptors) are read during the call only.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *    default stream) and performs no host synchronisation.
+ *  - Return codes only: SPA_ERR_INVALID is returned before anything is
+ *    launched when an argument is rejected; SPA_ERR_HIP when a launch fails.
+ *  - Device buffers must be 16-byte aligned; rows are dense (no padding).
+ *  - dtype is one of SPA_F32, SPA_F16, SPA_BF16 and applies to x, w, wt,
+ *    vals and y alike.  Accumulation is float32.
+ *  - Inputs must be finite.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef SPA_H_
+#define SPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spa_status {
+  SPA_OK = 0,
+  SPA_ERR_INVALID = 1,      /* rejected argument; nothing launched */
+  SPA_ERR_UNSUPPORTED = 2,  /* valid combination this build does not implement */
+  SPA_ERR_HIP = 3           /* a HIP launch or runtime call failed */
+} spa_status;
+
+enum { SPA_F32 = 0, SPA_F16 = 1, SPA_BF16 = 2 };
+enum { SPA_SCORE_MAGNITUDE = 0, SPA_SCORE_WEIGHT = 1, SPA_SCORE_CLACT = 2 };
+enum { SPA_SHIFT_NONE = 0, SPA_SHIFT_TOKEN_MEAN = 1, SPA_SHIFT_GIVEN = 2 };
+enum { SPA_ENTRY_PRUNE = 0, SPA_ENTRY_DECODE = 1, SPA_ENTRY_PREFILL = 2 };
+
+/* Pruning configuration.  m in {4, 8, 16, 32}; 1 <= n <= m; k % m == 0. */
+typedef struct spa_prune_cfg {
+  int32_t n;
+  int32_t m;
+  int32_t score;        /* SPA_SCORE_* */
+  int32_t shift;        /* SPA_SHIFT_* */
+  int32_t var_rescale;  /* 0 or 1 */
+} spa_prune_cfg;
+
+/* A prepared linear layer.  Fields not needed by an entry point may be NULL:
+ * decode reads wt, prefill reads w; chan_scale is needed for
+ * SPA_SCORE_WEIGHT, row_sum whenever shift != SPA_SHIFT_NONE. */
+typedef struct spa_weight {
+  int32_t dtype;
+  int32_t n_out;
+  int32_t k;
+  const void* w;            /* [device] [n_out][k], the layer's own layout        */
+  const void* wt;           /* [device] [k][n_out], channel-major (from prepare)  */
+  const float* chan_scale;  /* [device] [k], ||W[:,k]||_2^alpha (from prepare)    */
+  const float* row_sum;     /* [device] [n_out], sum_k W[j,k] (from prepare)      */
+} spa_weight;
+
+/*
+ * prepare_weight -- once per layer, off the timed path.
+ * Writes wt = W^T ([k][n_out], so that channel k's weights are one
+ * contiguous row and a pruned channel skips that whole row), chan_scale[c] =
+ * float32((sum_j W[j,c]^2)^(alpha/2)) and row_sum[j] = float32(sum_c W[j,c]),
+ * both sums formed in double-double arithmetic (WiSparse s2.1: the weight
+ * norms can be computed ahead of time).  Any output pointer may be NULL to
+ * skip it.  w: [device] [n_out][k].  Requires n_out >= 1, k >= 1,
+ * 0 <= alpha <= 16.
+ */
+spa_status prepare_weight(const void* w, int32_t dtype, int32_t n_out, int32_t k, float alpha,
+                          void* wt_out, float* chan_scale_out, float* row_sum_out, void* stream);
+
+/*
+ * prune_nm -- score, per-block top-n, pack (guide s2.1, s2.2, s3.1, s3.2).
+ *  x          [device] [t][k]
+ *  chan_scale [device] [k]   required iff cfg->score == SPA_SCORE_WEIGHT
+ *  eta_in     [device] [t]   required iff cfg->shift == SPA_SHIFT_GIVEN
+ *  vals_out   [device] [t][k*n/m] kept values of x_hat rounded to dtype
+ *             (round-to-nearest-even), in ascending channel order
+ *  idx_out    [device] [t][k*n/m] uint8 in-block position of each kept value
+ *  eta_out    [device] [t] float32 or NULL
+ *  nu_out     [device] [t] float32 or NULL (1.0 when cfg->var_rescale == 0)
+ *  workspace  [device] spa_workspace_bytes(SPA_ENTRY_PRUNE, ...) bytes
+ *             (only CLACT uses it; may be NULL otherwise)
+ * Requires t >= 0 (t == 0 is a no-op), k >= m, k % m == 0.
+ */
+spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const spa_prune_cfg* cfg,
+                    const float* chan_scale, const float* eta_in, void* vals_out, uint8_t* idx_out,
+                    float* eta_out, float* nu_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sparse_linear_decode -- the fused decode step, 1 <= t <= 32 tokens:
+ * prune in registers, then stream only the rows of wt that some token of
+ * the call keeps (the memory-bound GEMV; guide s1.1 and s12.3: zero
+ * activations need not move, and bandwidth comes first), accumulate in
+ * float32, and apply
+ * y = nu * acc + eta * row_sum.
+ *  x        [device] [t][k]
+ *  w        weight descriptor; wt required (n_out % 8 == 0 for 16-bit
+ *           dtypes, % 4 for float32)
+ *  eta_in   [device] [t], required iff cfg->shift == SPA_SHIFT_GIVEN
+ *  y        [device] [t][n_out]
+ *  idx_out  [device] [t][k*n/m] or NULL: the in-block positions the layer used
+ *  nu_out   [device] [t] or NULL
+ *  workspace [device] spa_workspace_bytes(SPA_ENTRY_DECODE, ...) bytes,
+ *           zero-filled before its first use; each call leaves it reusable.
+ */
+spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
+                                const float* eta_in, void* y, uint8_t* idx_out, float* nu_out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sparse_linear_prefill -- prompt-size batches, t >= 1 (16-bit dtypes):
+ * a pruning pass packs the kept values, then an LDS-tiled matrix-core GEMM
+ * with w ([n_out][k]) as the dense operand computes y.  2:4 runs on the
+ * gfx950 sparse MFMA (smfmac), which skips the pruned half of the products
+ * ("Accelerating Transformer training and inference with 2:4 sparsity and
+ * Squared-ReLU" s2.1, s3.1); every other n:m runs dense MFMA on the
+ * masked activations.
+ *  Arguments as for sparse_linear_decode; w->w required, n_out % 8 == 0,
+ *  k % 64 == 0.  workspace: spa_workspace_bytes(SPA_ENTRY_PREFILL, ...).
+ */
+spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
+                                 const float* eta_in, void* y, uint8_t* idx_out, float* nu_out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes an entry point needs for these sizes (0 if none); 0 for
+ * invalid arguments as well. */
+size_t spa_workspace_bytes(int32_t entry, int32_t t, int32_t k, int32_t n_out, int32_t dtype,
+                           const spa_prune_cfg* cfg);
+
+/* Static, NUL-terminated description of a status code. */
+const char* spa_status_str(spa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPA_H_ */

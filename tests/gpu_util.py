@@ -1,0 +1,42 @@
+"""Helpers shared by the GPU parity tests (no method arithmetic here)."""
+import numpy as np
+import torch
+
+from oracle import nm_oracle as O
+
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def storage_bits(v32: np.ndarray, dtype: str) -> np.ndarray:
+    """Bit patterns of float32 values that are exactly representable in ``dtype``."""
+    v32 = np.ascontiguousarray(v32, dtype=np.float32)
+    if dtype == "f32":
+        return v32.view(np.uint32)
+    if dtype == "f16":
+        return v32.astype(np.float16).view(np.uint16)
+    return (v32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def tensor_bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def oracle_for(spec, x_cpu, w_cpu, f=None, eta_in=None, rows=None):
+    """Oracle prune (+ linear when w_cpu is given) for ``spec`` on CPU tensors."""
+    x = f32(x_cpu) if rows is None else f32(x_cpu[rows])
+    if spec.score == "weight" and f is None:
+        f = O.channel_factor(f32(w_cpu), spec.alpha)
+    eta = None if eta_in is None else (f32(eta_in) if rows is None else f32(eta_in[rows]))
+    pr = O.prune(x, spec.dtype, spec.n, spec.m, score=spec.score, f=f, shift_mode=spec.shift, eta_in=eta,
+                 var_rescale=spec.var_rescale)
+    if w_cpu is not None:
+        pr["y"] = O.linear(pr, f32(w_cpu))
+    pr["f"] = f
+    return pr

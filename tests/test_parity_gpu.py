@@ -1,0 +1,191 @@
+"""GPU parity: the HIP library against the CPU oracle, element by element.
+
+Masks (in-block positions), packed values and the per-token shift must
+match bit for bit; the output y within the row-normwise tolerance (2e-2 for
+16-bit storage, 1e-5 for float32); nu within 1e-6 relative.  Inputs are the
+seeded workloads; the oracle never sees anything the GPU computed.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import nm_oracle as O
+from gpu_util import TORCH_DT, f32, oracle_for, storage_bits, tensor_bits
+
+pytestmark = pytest.mark.gpu
+
+spa = pytest.importorskip("activation_sparsification_amd")
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    return torch.device("cuda:0")
+
+
+def _cfg(spec, n=None, m=None):
+    return spa.PruneConfig(n or spec.n, m or spec.m, spec.score, spec.shift, spec.var_rescale)
+
+
+def _check_prune(pr, vals, idx, eta, nu, dtype):
+    assert np.array_equal(tensor_bits(vals), storage_bits(pr["vals"], dtype)), "packed values differ"
+    assert np.array_equal(idx.cpu().numpy(), pr["idx"]), "in-block positions differ"
+    assert np.array_equal(f32(eta).view(np.uint32), pr["eta"].view(np.uint32)), "eta differs"
+    assert np.allclose(f32(nu), pr["nu"], rtol=1e-6, atol=0), "nu differs"
+
+
+# ---------------------------------------------------------------------------
+# prepare_weight
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "decode_small", "batched_small_t8"])
+@pytest.mark.parametrize("alpha", [0.0, 0.5, 1.0])
+def test_prepare_weight(name, alpha):
+    spec = {s.name: s for s in wl.parity_specs()}[name]
+    _, w = wl.make_inputs(spec)
+    dev = _dev()
+    pw = spa.prepare_weight(w.to(dev), alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(pw.wt.cpu(), w.t().contiguous())
+    f = O.channel_factor(f32(w), alpha)
+    got = f32(pw.chan_scale)
+    assert np.array_equal(got.view(np.uint32), f.view(np.uint32)), (np.abs(got - f) / f).max()
+    s = O.row_sum(f32(w)).astype(np.float32)
+    assert np.array_equal(f32(pw.row_sum), s)
+
+
+# ---------------------------------------------------------------------------
+# prune_nm
+# ---------------------------------------------------------------------------
+PRUNE_CASES = []
+for s in wl.parity_specs():
+    PRUNE_CASES.append((s.name, s))
+for dt in ["bf16", "f16", "f32"]:
+    for n, m in [(1, 4), (2, 4), (3, 8), (4, 8), (8, 16), (5, 16), (16, 32), (8, 32), (32, 32)]:
+        for score, shift, var in [("magnitude", "none", False), ("weight", "token_mean", True),
+                                  ("clact", "given", True)]:
+            base = wl.SPECS["decode"].with_(name="sweep", t=3, k=256, n_out=64, dtype=dt, n=n, m=m, score=score,
+                                            shift=shift, var_rescale=var, alpha=0.5)
+            PRUNE_CASES.append((f"{dt}-{n}:{m}-{score}-{shift}-{int(var)}", base))
+
+
+@pytest.mark.parametrize("label,spec", PRUNE_CASES, ids=[c[0] for c in PRUNE_CASES])
+def test_prune_parity(label, spec):
+    dev = _dev()
+    x, w = wl.make_inputs(spec)
+    eta_in = wl.make_eta(spec.t, 3) if spec.shift == "given" else None
+    f = O.channel_factor(f32(w), spec.alpha) if spec.score == "weight" else None
+    pr = oracle_for(spec, x, None, f=f, eta_in=eta_in)
+    vals, idx, eta, nu = spa.prune_nm(x.to(dev), _cfg(spec),
+                                      chan_scale=None if f is None else torch.from_numpy(f).to(dev),
+                                      eta_in=None if eta_in is None else eta_in.to(dev))
+    torch.cuda.synchronize()
+    _check_prune(pr, vals, idx, eta, nu, spec.dtype)
+
+
+ADV_KINDS = ["equal", "zeros", "signed_pairs", "signed_zero", "one_big", "few_levels"]
+
+
+@pytest.mark.parametrize("kind", ADV_KINDS)
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32), (1, 32)])
+def test_prune_ties(kind, n, m):
+    dev = _dev()
+    spec = wl.SPECS["relu2"].with_(t=5, k=512, n=n, m=m, dtype="bf16")
+    x = wl.adversarial_x(kind, spec.t, spec.k, m, "bf16", seed=n + m)
+    pr = oracle_for(spec, x, None)
+    vals, idx, eta, nu = spa.prune_nm(x.to(dev), _cfg(spec))
+    torch.cuda.synchronize()
+    _check_prune(pr, vals, idx, eta, nu, "bf16")
+
+
+def test_prune_empty_and_invalid():
+    dev = _dev()
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=dev)
+    vals, idx, eta, nu = spa.prune_nm(x, spa.PruneConfig(2, 4))
+    assert vals.shape == (0, 32)
+    with pytest.raises(spa.SpaError):
+        spa.prune_nm(torch.zeros((2, 60), dtype=torch.bfloat16, device=dev), spa.PruneConfig(2, 4))
+    with pytest.raises(spa.SpaError):
+        spa.prune_nm(torch.zeros((2, 64), dtype=torch.bfloat16, device=dev), spa.PruneConfig(5, 4))
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+DECODE_CASES = [s for s in wl.parity_specs() if s.t <= 32]
+for t in [1, 2, 3, 4, 5, 8, 13, 16, 17, 32]:
+    DECODE_CASES.append(wl.SPECS["decode"].with_(name=f"decode_t{t}", t=t, k=1024, n_out=776))
+for dt in ["bf16", "f16"]:
+    for n, m in [(2, 4), (4, 8), (8, 16), (16, 32), (16, 16)]:
+        DECODE_CASES.append(wl.SPECS["batched"].with_(name=f"dec_{dt}_{n}_{m}_t3", t=3, k=512, n_out=136, dtype=dt,
+                                                      n=n, m=m))
+        DECODE_CASES.append(wl.SPECS["batched"].with_(name=f"dec_{dt}_{n}_{m}_t20", t=20, k=512, n_out=136,
+                                                      dtype=dt, n=n, m=m, score="magnitude", shift="token_mean",
+                                                      var_rescale=False))
+DECODE_CASES.append(wl.SPECS["tiny"].with_(name="tiny_f32_t8", t=8, shift="token_mean"))
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="decode_given_shift", t=2, k=512, n_out=256, shift="given"))
+
+
+@pytest.mark.parametrize("spec", DECODE_CASES, ids=[s.name for s in DECODE_CASES])
+def test_decode_parity(spec):
+    dev = _dev()
+    x, w = wl.make_inputs(spec)
+    eta_in = wl.make_eta(spec.t, 5) if spec.shift == "given" else None
+    pw = spa.prepare_weight(w.to(dev), spec.alpha)
+    f = f32(pw.chan_scale) if spec.score == "weight" else None
+    if f is not None:
+        assert np.array_equal(f.view(np.uint32), O.channel_factor(f32(w), spec.alpha).view(np.uint32))
+    pr = oracle_for(spec, x, w, f=f, eta_in=eta_in)
+    y, idx, nu = spa.sparse_linear_decode(x.to(dev), pw, _cfg(spec),
+                                          eta_in=None if eta_in is None else eta_in.to(dev), want_idx=True,
+                                          want_nu=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), pr["idx"]), "decode masks differ"
+    assert np.allclose(f32(nu), pr["nu"], rtol=1e-6, atol=0)
+    err = O.rowwise_error(f32(y), pr["y"])
+    assert err <= O.TOLERANCE[spec.dtype], err
+
+
+def test_decode_repeat_reuses_workspace():
+    # Counters left at zero: a second call on the same workspace gives the same bytes.
+    dev = _dev()
+    spec = wl.SPECS["decode"].with_(t=1, k=2048, n_out=4096)
+    x, w = wl.make_inputs(spec)
+    pw = spa.prepare_weight(w.to(dev), spec.alpha)
+    xd = x.to(dev)
+    y1, _, _ = spa.sparse_linear_decode(xd, pw, _cfg(spec))
+    y2, _, _ = spa.sparse_linear_decode(xd, pw, _cfg(spec))
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+PREFILL_CASES = [s for s in wl.parity_specs() if s.dtype != "f32"]
+for dt in ["bf16", "f16"]:
+    for n, m in [(2, 4), (1, 4), (4, 8), (8, 16), (16, 32), (4, 4)]:
+        PREFILL_CASES.append(wl.SPECS["prefill"].with_(name=f"pre_{dt}_{n}_{m}", t=77, k=320, n_out=300, dtype=dt,
+                                                       n=n, m=m, n_outliers=3))
+PREFILL_CASES.append(wl.SPECS["prefill"].with_(name="pre_weight_var", t=300, k=512, n_out=272, score="weight",
+                                               alpha=0.5, var_rescale=True))
+PREFILL_CASES.append(wl.SPECS["prefill"].with_(name="pre_given", t=40, k=256, n_out=520, shift="given"))
+PREFILL_CASES.append(wl.SPECS["batched"].with_(name="pre_clact", t=96, k=512, n_out=264, n=2, m=4))
+PREFILL_CASES.append(wl.SPECS["prefill"].with_(name="pre_one_row", t=1, k=128, n_out=8))
+
+
+@pytest.mark.parametrize("spec", PREFILL_CASES, ids=[s.name for s in PREFILL_CASES])
+def test_prefill_parity(spec):
+    dev = _dev()
+    x, w = wl.make_inputs(spec)
+    eta_in = wl.make_eta(spec.t, 9) if spec.shift == "given" else None
+    pw = spa.prepare_weight(w.to(dev), spec.alpha, want_wt=False)
+    f = f32(pw.chan_scale) if spec.score == "weight" else None
+    pr = oracle_for(spec, x, w, f=f, eta_in=eta_in)
+    y, idx, nu = spa.sparse_linear_prefill(x.to(dev), pw, _cfg(spec),
+                                           eta_in=None if eta_in is None else eta_in.to(dev), want_idx=True,
+                                           want_nu=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), pr["idx"]), "prefill masks differ"
+    assert np.allclose(f32(nu), pr["nu"], rtol=1e-6, atol=0)
+    err = O.rowwise_error(f32(y), pr["y"])
+    assert err <= O.TOLERANCE[spec.dtype], err
