@@ -5,6 +5,7 @@ declared in ``include/spa.h``); this package is its thin Python binding.
 """
 from ._binding import (  # noqa: F401
     EXPORTS,
+    PreparedCall,
     PreparedWeight,
     PruneConfig,
     SpaError,

@@ -205,3 +205,27 @@ def sparse_linear_prefill(x, pw: PreparedWeight, cfg: PruneConfig, eta_in=None, 
                           out=None, ws=None):
     """Prune/pack pass + matrix-core GEMM (sparse MFMA for 2:4).  Returns ``(y, idx, nu)``."""
     return _linear("sparse_linear_prefill", ENTRY_PREFILL, x, pw, cfg, eta_in, want_idx, want_nu, out, ws)
+
+
+class PreparedCall:
+    """A library call with every argument marshalled once (for tight loops and timing).
+
+    ``__call__`` issues exactly one C call on the stream that was current at
+    construction; outputs land in the tensors given here.
+    """
+
+    def __init__(self, fn_name: str, x, pw: PreparedWeight, cfg: PruneConfig, y, ws, eta_in=None, idx=None,
+                 nu=None, wt=None, w=None):
+        self._keep = (x, pw, y, ws, eta_in, idx, nu, wt, w)
+        self._cfg = cfg.c()
+        self._wd = pw.c(wt=wt, w=w)
+        self._fn = getattr(lib(), fn_name)
+        self._name = fn_name
+        t = x.shape[0]
+        self._args = (_ptr(x), t, ctypes.byref(self._wd), ctypes.byref(self._cfg), _ptr(eta_in), _ptr(y),
+                      _ptr(idx), _ptr(nu), _ptr(ws), 0 if ws is None else ws.numel(), _stream(x.device))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != SPA_OK:
+            raise SpaError(st, self._name)

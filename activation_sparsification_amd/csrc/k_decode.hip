@@ -24,6 +24,7 @@
 //    tokens x rows x columns product on matrix cores (mfma 16x16x32).
 #include "spa_common.h"
 #include "spa_launch.h"
+#include "spa_select.h"
 
 namespace spa {
 
@@ -34,249 +35,454 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMaxTok = 32;
 
 // ---------------------------------------------------------------------------
-// Epilogue shared by both variants: arrive at the tile's ticket; the last
-// arrival reduces the partials and writes y.
+// Split-K hand-off without cache-wide maintenance.  A partial is stored with
+// agent-scope atomic stores (coherent across the XCDs' private L2s), every
+// wave waits for its stores to complete, then one lane takes a ticket with an
+// agent-scope atomic.  The last arrival reads the partials back with
+// agent-scope atomic loads.  (A device-wide __threadfence() would instead
+// write back and invalidate the whole L2 once per workgroup.)
 // ---------------------------------------------------------------------------
-template <int DT>
-__device__ void finish_tile(const DecodeArgs& a, int tile, int split, const float* s_eta, int* s_flag,
-                            float* s_nu) {
-  __threadfence();
+template <class V>
+__device__ __forceinline__ void coherent_store(V* p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class V>
+__device__ __forceinline__ V coherent_load(const V* p) {
+  return __hip_atomic_load(const_cast<V*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's stores are complete (vmcnt = 0).
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Every thread calls this after its coherent stores; returns true in the
+// workgroup that arrives last at this tile.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, int expected, int* s_flag) {
+  wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned ticket = atomicAdd(&a.counters[tile], 1u);
-    *s_flag = (ticket == (unsigned)(a.splits - 1)) ? 1 : 0;
+    const unsigned ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = ticket == (unsigned)(expected - 1);
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+    *s_flag = last;
   }
   __syncthreads();
-  if (!*s_flag) return;
-  __threadfence();
+  return *s_flag != 0;
+}
 
-  const int T = a.t;
-  if ((int)threadIdx.x < T) {
-    float nu = 1.f;
-    if (a.var) {
-      const int i = threadIdx.x;
-      double s[4] = {0.0, 0.0, 0.0, 0.0};
-      // the statistics of every channel group, in group order
-      const int groups = a.mask_groups > 0 ? a.mask_groups : a.splits;
-      const double* base = a.mask_groups > 0 ? a.stats : a.stats + (size_t)tile * a.splits * T * 4;
-      // fused path: every tile keeps its own copy, so the reducer never waits on another tile
-      for (int g = 0; g < groups; ++g)
-        for (int q = 0; q < 4; ++q) s[q] += base[((size_t)g * T + i) * 4 + q];
-      const double kk = (double)a.k;
-      const double vf = s[1] / kk - (s[0] / kk) * (s[0] / kk);
-      const double vm = s[3] / kk - (s[2] / kk) * (s[2] / kk);
-      if (vm > 0.0) nu = (float)__builtin_sqrt(vf / vm);
-    }
-    s_nu[threadIdx.x] = nu;
-    if (tile == 0 && a.nu_out) a.nu_out[threadIdx.x] = nu;
-  }
+// nu from the four per-token sums (sum x, sum x^2, sum kept x, sum kept x^2) over all k.
+__device__ __forceinline__ float nu_from_stats(const double* s, int k) {
+  const double kk = (double)k;
+  const double vf = s[1] / kk - (s[0] / kk) * (s[0] / kk);
+  const double vm = s[3] / kk - (s[2] / kk) * (s[2] / kk);
+  return vm > 0.0 ? (float)__builtin_sqrt(vf / vm) : 1.f;
+}
+
+template <int NW>
+__device__ __forceinline__ double wg_sum(double v, double* s_tmp /*[NW]*/) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
   __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) s_tmp[w] = v;
+  __syncthreads();
+  double t = s_tmp[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) t += s_tmp[i];
+  return t;
+}
 
-  using T_ = typename Dt<DT>::T;
-  T_* y = static_cast<T_*>(a.y);
-  const int c0 = tile * a.col_tile;
-  const int cw = min(a.col_tile, a.n_out - c0);
-  for (int p = threadIdx.x; p < T * cw; p += 256) {
-    const int i = p / cw, cc = p % cw, col = c0 + cc;
-    float acc = 0.f;
-    for (int s = 0; s < a.splits; ++s) acc += a.partial[((size_t)s * T + i) * a.n_out + col];
-    float v = s_nu[i] * acc;
-    if (a.shift != SPA_SHIFT_NONE) v += s_eta[i] * a.row_sum[col];
-    y[(size_t)i * a.n_out + col] = from_f32<DT>(v);
+// Exclusive prefix sum over the 64 lanes of a wave (Hillis-Steele), *total = sum.
+__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
+  const int lane = threadIdx.x & 63;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += o;
   }
-  if (threadIdx.x == 0) a.counters[tile] = 0u;
+  *total = __shfl(inc, 63, kWave);
+  return inc - v;
 }
 
 // ---------------------------------------------------------------------------
-// Fused variant (t <= TOK <= 8).
+// Fused variant (t <= TOK).  512 threads = 8 waves.  The workgroup owns C
+// columns (8 lanes x one 16-byte load = one 128-byte line of a weight row)
+// and a range of channels.  Each thread owns whole m-blocks of the range:
+// it shifts and scores its block for every token, selects the top n in
+// registers, and lists the block's union rows (with each token's kept value,
+// 0 where that token pruned the channel) in a workgroup-shared LDS list.
+// All eight waves then stream the listed rows, 8 rows per load instruction,
+// and accumulate in float32.
 // ---------------------------------------------------------------------------
-template <int DT, int M, int TOK>
-__global__ void __launch_bounds__(256) k_decode_fused(DecodeArgs a) {
-  using T = typename Dt<DT>::T;
-  constexpr int CPL = 16 / Dt<DT>::bytes;   // columns per lane (one 16-byte load)
-  constexpr int C = 64 * CPL;               // column tile
-  constexpr int UNR = 8;                    // rows in flight per lane
+template <int DT, int M>
+__device__ __forceinline__ void load_block(const typename Dt<DT>::T* __restrict__ p, uint4 (&raw)[Dt<DT>::bytes * M / 16 > 0 ? Dt<DT>::bytes * M / 16 : 1]) {
+  constexpr int NV = Dt<DT>::bytes * M / 16;
+  if constexpr (NV == 0) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);  // 4 x 16-bit
+    raw[0] = make_uint4(u.x, u.y, 0u, 0u);
+  } else {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) raw[q] = reinterpret_cast<const uint4*>(p)[q];
+  }
+}
+template <int DT>
+__device__ __forceinline__ float raw_elem(const uint4* raw, int j) {
+  if constexpr (DT == SPA_F32) {
+    const uint4& u = raw[j >> 2];
+    const uint32_t w = (j & 3) == 0 ? u.x : (j & 3) == 1 ? u.y : (j & 3) == 2 ? u.z : u.w;
+    return __uint_as_float(w);
+  } else {
+    return elem16<DT>(raw[j >> 3], j & 7);
+  }
+}
 
-  extern __shared__ unsigned char s_dyn[];
-  __shared__ double s_red[4];
-  __shared__ int s_cnt[4];
+// Waves per workgroup: 8 for the light cases; 4 (so each wave may use up to 512
+// registers) when several tokens or 32-wide blocks are ranked per lane.
+template <int M, int TOK>
+constexpr int fused_waves() { return (TOK >= 2 || M >= 32) ? 4 : 8; }
+
+template <int DT, int M, int TOK>
+__global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(DecodeArgs a) {
+  using T = typename Dt<DT>::T;
+  constexpr int NW = fused_waves<M, TOK>();
+  constexpr int NT = NW * 64;
+  constexpr int CPL = 16 / Dt<DT>::bytes;                 // columns per 16-byte load
+  constexpr int C = 8 * CPL;                              // columns per workgroup
+  constexpr int UNR = TOK >= 8 ? 4 : (TOK >= 4 || M >= 32 || DT == SPA_F32) ? 8 : 16;  // loads per batch per lane
+  constexpr int NV = Dt<DT>::bytes * M / 16 > 0 ? Dt<DT>::bytes * M / 16 : 1;
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
   __shared__ float s_eta[TOK];
   __shared__ float s_nu[TOK];
+  __shared__ double s_red[TOK][NW];
+  __shared__ int s_wcnt[NW];
   __shared__ int s_flag;
+  __shared__ float s_acc[NW][TOK][C];
+  __shared__ double s_st[NW][TOK][4];
 
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int T_ = a.t;
   const int tile = blockIdx.x % a.tiles;
   const int split = blockIdx.x / a.tiles;
+  const int c0 = tile * C;
   const int kb = split * a.k_len;
-  const int KL = min(a.k_len, a.k - kb);    // the last split may be shorter
+  const int KL = min(a.k_len, a.k - kb);
+  const int nb = KL / M;
+  const int lcap = a.list_cap;                                       // entries per workgroup
+  int* s_rows = reinterpret_cast<int*>(s_dyn);                       // [lcap]
+  float* s_coef = reinterpret_cast<float*>(s_dyn) + lcap;            // [TOK][lcap]
   const T* x = static_cast<const T*>(a.x);
+  const T* wt = static_cast<const T*>(a.wt);
 
-  // LDS carve-up (strides use KL; sizes were reserved for k_len)
-  float* s_sc = reinterpret_cast<float*>(s_dyn);                // [TOK][KL] scores
-  float* s_coef = s_sc + TOK * a.k_len;                         // [TOK][KL] x_hat, then kept-or-0
-  int* s_rows = reinterpret_cast<int*>(s_coef + TOK * a.k_len); // [KL] token masks, then union rows
-  uint8_t* s_keep = reinterpret_cast<uint8_t*>(s_rows + a.k_len);  // [TOK][KL]
-  float* s_acc = reinterpret_cast<float*>(s_keep + ((TOK * a.k_len + 15) & ~15));  // [4][TOK][C]
-
-  // 1. shift
-  for (int i = 0; i < T_; ++i) {
-    float e = 0.f;
-    if (a.shift == SPA_SHIFT_TOKEN_MEAN && a.eta == nullptr) {
-      double s = 0.0;
-      for (int c = threadIdx.x; c < a.k; c += 256) s += (double)to_f32<DT>(x[(size_t)i * a.k + c]);
-      e = (float)(block_sum(s, s_red) / (double)a.k);
-    } else if (a.eta != nullptr) {
-      e = a.eta[i];
-    }
-    if (threadIdx.x == 0) s_eta[i] = e;
-  }
-  __syncthreads();
-
-  // 2. channel factor and scores
-  for (int c = threadIdx.x; c < KL; c += 256) {
-    float f = 1.f;
-    if (a.score == SPA_SCORE_WEIGHT) {
-      f = a.chan_scale[kb + c];
-    } else if (a.score == SPA_SCORE_CLACT) {
-      float acc = 0.f;
-      for (int p = 0; p < T_; ++p) acc = clact_accumulate(acc, to_f32<DT>(x[(size_t)p * a.k + kb + c]) - s_eta[p]);
-      f = sqrt_rn(acc);
-    }
-    for (int i = 0; i < T_; ++i) {
-      const float xh = to_f32<DT>(x[(size_t)i * a.k + kb + c]) - s_eta[i];
-      s_coef[i * KL + c] = xh;
-      s_sc[i * KL + c] = a.score == SPA_SCORE_MAGNITUDE ? __builtin_fabsf(xh) : __builtin_fabsf(xh) * f;
-    }
-  }
-  __syncthreads();
-
-  // 3. per-element rank within its block
-  for (int c = threadIdx.x; c < KL; c += 256) {
-    const int j = c % M, base = c - j;
-    uint32_t tokmask = 0;
-    for (int i = 0; i < T_; ++i) {
-      const float* sc = s_sc + i * KL + base;
-      const float me = sc[j];
-      int rank = 0;
+  // 0. prefetch this thread's first block (every token) and its weight factors
+  uint4 raw[TOK][NV];
+  float f[M];
 #pragma unroll
-      for (int q = 0; q < M; ++q) rank += beats(sc[q], q, me, j) ? 1 : 0;
-      const bool keep = rank < a.n;
-      s_keep[i * KL + c] = keep ? 1 : 0;
-      if (keep) tokmask |= 1u << i;
+  for (int j = 0; j < M; ++j) f[j] = 1.f;
+  if ((int)threadIdx.x < nb) {
+    const int ch0 = kb + (int)threadIdx.x * M;
+#pragma unroll
+    for (int i = 0; i < TOK; ++i)
+      if (i < T_) load_block<DT, M>(x + (size_t)i * a.k + ch0, raw[i]);
+    if (a.score == SPA_SCORE_WEIGHT) {
+#pragma unroll
+      for (int q = 0; q < M / 4; ++q) {
+        const float4 v = reinterpret_cast<const float4*>(a.chan_scale + ch0)[q];
+        f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
+      }
     }
-    s_rows[c] = (int)tokmask;
   }
-  __syncthreads();
 
-  // 3b. in-block positions (one workgroup per split writes them), kept-or-zero
-  //     coefficients, variance statistics of this channel range
-  const bool write_idx = (a.idx_out != nullptr) && tile == 0;
-  for (int c = threadIdx.x; c < KL; c += 256) {
-    const int j = c % M, base = c - j;
-    for (int i = 0; i < T_; ++i) {
-      if (s_keep[i * KL + c]) {
-        if (write_idx) {
-          int before = 0;
-          for (int q = 0; q < j; ++q) before += s_keep[i * KL + base + q];
-          a.idx_out[(size_t)i * (a.k / M * a.n) + (size_t)(kb + base) / M * a.n + before] = (uint8_t)j;
+  // 1. per-token shift: float64 row sums over all k channels (every token at once,
+  //    one barrier), fixed reduction order
+  if (a.shift == SPA_SHIFT_TOKEN_MEAN && a.eta == nullptr) {
+    double sum[TOK];
+#pragma unroll
+    for (int i = 0; i < TOK; ++i) sum[i] = 0.0;
+    const int nq = a.k / CPL;
+    for (int q = threadIdx.x; q < nq; q += NT) {
+#pragma unroll
+      for (int i = 0; i < TOK; ++i) {
+        if (i < T_) {
+          const uint4 u = *reinterpret_cast<const uint4*>(x + (size_t)i * a.k + (size_t)q * CPL);
+          if constexpr (DT == SPA_F32) {
+            sum[i] += (double)__uint_as_float(u.x) + (double)__uint_as_float(u.y) + (double)__uint_as_float(u.z) +
+                      (double)__uint_as_float(u.w);
+          } else {
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) sum[i] += (double)elem16<DT>(u, e2);
+          }
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < TOK; ++i) {
+      const double ws = wave_sum(sum[i]);
+      if (lane == 0) s_red[i][wv] = ws;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < T_) {
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += s_red[threadIdx.x][w];
+      s_eta[threadIdx.x] = (float)(tot / (double)a.k);
+    }
+  } else if ((int)threadIdx.x < T_) {
+    s_eta[threadIdx.x] = a.eta != nullptr ? a.eta[threadIdx.x] : 0.f;
   }
-  if (a.var) {
-    for (int i = 0; i < T_; ++i) {
-      double ts[4] = {0.0, 0.0, 0.0, 0.0};
-      for (int c = threadIdx.x; c < KL; c += 256) {
-        const double v = (double)s_coef[i * KL + c];
-        ts[0] += v; ts[1] += v * v;
-        if (s_keep[i * KL + c]) { ts[2] += v; ts[3] += v * v; }
-      }
-      for (int q = 0; q < 4; ++q) {
-        const double tot = block_sum(ts[q], s_red);
-        if (threadIdx.x == 0) a.stats[(((size_t)tile * a.splits + split) * T_ + i) * 4 + q] = tot;
+  if (lane == 0)
+    for (int i = 0; i < TOK; ++i)
+      for (int q = 0; q < 4; ++q) s_st[wv][i][q] = 0.0;
+  __syncthreads();
+  float eta[TOK];
+#pragma unroll
+  for (int i = 0; i < TOK; ++i) eta[i] = i < T_ ? s_eta[i] : 0.f;
+
+  // 2. select and list, one block per thread per pass
+  const bool write_idx = a.idx_out != nullptr && tile == 0;
+  const int kept_row = a.k / M * a.n;
+  int base = 0;
+  const int npass = (nb + NT - 1) / NT;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int b = pass * NT + threadIdx.x;
+    const bool own = b < nb;
+    const int ch0 = kb + b * M;
+    if (pass > 0 && own) {
+#pragma unroll
+      for (int i = 0; i < TOK; ++i)
+        if (i < T_) load_block<DT, M>(x + (size_t)i * a.k + ch0, raw[i]);
+      if (a.score == SPA_SCORE_WEIGHT) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) f[j] = a.chan_scale[ch0 + j];
       }
     }
+    uint32_t kbits[TOK];
+    uint32_t ub = 0;
+#pragma unroll
+    for (int i = 0; i < TOK; ++i) kbits[i] = 0;
+    if (own) {
+      if (a.score == SPA_SCORE_CLACT) {
+        // column energy over the call's tokens, tokens in order, float32, no FMA
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+          float acc2 = 0.f;
+#pragma unroll
+          for (int i = 0; i < TOK; ++i)
+            if (i < T_) acc2 = clact_accumulate(acc2, raw_elem<DT>(raw[i], j) - eta[i]);
+          f[j] = sqrt_rn(acc2);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TOK; ++i) {
+        if (i < T_) {
+          uint32_t sb[M];
+#pragma unroll
+          for (int j = 0; j < M; ++j) {
+            const float ax = __builtin_fabsf(raw_elem<DT>(raw[i], j) - eta[i]);
+            sb[j] = __float_as_uint(a.score == SPA_SCORE_MAGNITUDE ? ax : ax * f[j]);
+          }
+          kbits[i] = topn_keep_bits<M>(sb, a.n);
+          ub |= kbits[i];
+          if (write_idx) {
+            uint8_t* ip = a.idx_out + (size_t)i * kept_row + (size_t)(ch0 / M) * a.n;
+            int q = 0;
+            for (int j = 0; j < M; ++j)
+              if ((kbits[i] >> j) & 1u) ip[q++] = (uint8_t)j;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one token's network at a time (register pressure)
+      }
+    }
+    if (a.var) {
+      // this pass's per-token sums, added to the wave totals in pass order
+#pragma unroll
+      for (int i = 0; i < TOK; ++i) {
+        if (i < T_) {
+          double bs[4] = {0.0, 0.0, 0.0, 0.0};
+          if (own) {
+            for (int j = 0; j < M; ++j) {
+              const double v = (double)(raw_elem<DT>(raw[i], j) - eta[i]);
+              const double kv = ((kbits[i] >> j) & 1u) ? v : 0.0;
+              bs[0] += v;
+              bs[1] += v * v;
+              bs[2] += kv;
+              bs[3] += kv * kv;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const double tot = wave_sum(bs[q]);
+            if (lane == 0) s_st[wv][i][q] += tot;
+          }
+        }
+      }
+    }
+    // list slots in block order: with one token every block lists exactly n rows;
+    // otherwise an exclusive prefix of the union counts over the workgroup
+    int slot, total;
+    if (T_ == 1) {
+      slot = base + b * a.n;
+      total = min(NT, nb - pass * NT) * a.n;
+    } else {
+      int wtot;
+      const int wpos = wave_excl_scan(__builtin_popcount(ub), &wtot);
+      if (lane == 0) s_wcnt[wv] = wtot;
+      __syncthreads();
+      int off = base;
+      total = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int c = s_wcnt[w];
+        off += w < wv ? c : 0;
+        total += c;
+      }
+      slot = off + wpos;
+    }
+    if (own) {
+#pragma unroll
+      for (int j = 0; j < M; ++j) {
+        if ((ub >> j) & 1u) {
+          s_rows[slot] = ch0 + j;
+#pragma unroll
+          for (int i = 0; i < TOK; ++i)
+            if (i < T_) s_coef[i * lcap + slot] = ((kbits[i] >> j) & 1u) ? raw_elem<DT>(raw[i], j) - eta[i] : 0.f;
+          ++slot;
+        }
+      }
+    }
+    base += total;
+    __syncthreads();
   }
-  __syncthreads();
-  for (int c = threadIdx.x; c < KL; c += 256)
-    for (int i = 0; i < T_; ++i)
-      if (!s_keep[i * KL + c]) s_coef[i * KL + c] = 0.f;
 
-  // 4. union of kept rows, ascending
-  int U = 0;
-  for (int c0 = 0; c0 < KL; c0 += 256) {
-    const int c = c0 + threadIdx.x;
-    const bool f = c < KL && s_rows[c] != 0;
-    int total;
-    const int pos = block_exclusive_count(f, s_cnt, &total);
-    if (f) s_acc[U + pos] = __int_as_float(c);  // s_acc is free until the main loop ends
-    U += total;
-  }
-  __syncthreads();
-  for (int u = threadIdx.x; u < U; u += 256) s_rows[u] = __float_as_int(s_acc[u]);
-  __syncthreads();
-
-  // 5. stream the kept rows of wt
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int col = tile * C + lane * CPL;
+  // 3. stream the listed rows: row group g covers slots 8g..8g+7; wave w takes groups
+  //    w, w+NW, ...; lane (rs, cg) loads slot 8g + rs, columns col..col+CPL; two
+  //    batches of UNR loads in flight
+  const int L = base;
+  const int rs = lane >> 3, cg = lane & 7;
+  const int col = c0 + cg * CPL;
   const bool cvalid = col < a.n_out;
   float acc[TOK][CPL];
 #pragma unroll
   for (int i = 0; i < TOK; ++i)
 #pragma unroll
     for (int e = 0; e < CPL; ++e) acc[i][e] = 0.f;
-
-  const T* wt = static_cast<const T*>(a.wt);
-  for (int u0 = wv; u0 < U; u0 += 4 * UNR) {
-    uint4 wv16[UNR];
-    int rr[UNR];
+  const int G = (L + 7) / 8;
+  uint4 wa[UNR], wb[UNR];
+  auto issue = [&](uint4 (&w)[UNR], int it) {
 #pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      const int u = u0 + 4 * r;
-      rr[r] = u < U ? s_rows[u] : -1;
-      if (rr[r] >= 0 && cvalid)
-        wv16[r] = *reinterpret_cast<const uint4*>(wt + (size_t)(kb + rr[r]) * a.n_out + col);
+    for (int j = 0; j < UNR; ++j) {
+      const int u = ((it * UNR + j) * NW + wv) * 8 + rs;
+      if (u < L && cvalid)
+        w[j] = *reinterpret_cast<const uint4*>(wt + (size_t)s_rows[u] * a.n_out + col);
       else
-        wv16[r] = make_uint4(0u, 0u, 0u, 0u);
+        w[j] = make_uint4(0u, 0u, 0u, 0u);
     }
+  };
+  auto consume = [&](const uint4 (&w)[UNR], int it) {
 #pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      if (rr[r] < 0) continue;
-      float wf[CPL];
-      if constexpr (DT == SPA_F32) {
-        wf[0] = __uint_as_float(wv16[r].x); wf[1] = __uint_as_float(wv16[r].y);
-        wf[2] = __uint_as_float(wv16[r].z); wf[3] = __uint_as_float(wv16[r].w);
-      } else {
+    for (int j = 0; j < UNR; ++j) {
+      const int u = ((it * UNR + j) * NW + wv) * 8 + rs;
+      if (u < L) {
+        float wf[CPL];
+        if constexpr (DT == SPA_F32) {
+          wf[0] = __uint_as_float(w[j].x); wf[1] = __uint_as_float(w[j].y);
+          wf[2] = __uint_as_float(w[j].z); wf[3] = __uint_as_float(w[j].w);
+        } else {
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) wf[e] = elem16<DT>(wv16[r], e);
-      }
+          for (int e = 0; e < CPL; ++e) wf[e] = elem16<DT>(w[j], e);
+        }
 #pragma unroll
-      for (int i = 0; i < TOK; ++i) {
-        if (i < T_) {
-          const float cf = s_coef[i * KL + rr[r]];
+        for (int i = 0; i < TOK; ++i) {
+          if (i < T_) {
+            const float cf = s_coef[i * lcap + u];
 #pragma unroll
-          for (int e = 0; e < CPL; ++e) acc[i][e] += cf * wf[e];
+            for (int e = 0; e < CPL; ++e) acc[i][e] += cf * wf[e];
+          }
         }
       }
     }
+  };
+  const int nit = (G + NW * UNR - 1) / (NW * UNR);   // batches, uniform across the workgroup
+  if (nit > 0) issue(wa, 0);
+  for (int it = 0; it < nit; it += 2) {
+    if (it + 1 < nit) issue(wb, it + 1);
+    consume(wa, it);
+    if (it + 2 < nit) issue(wa, it + 2);
+    if (it + 1 < nit) consume(wb, it + 1);
   }
-  __syncthreads();  // s_acc held the union list
 
-  // 6. reduce the four waves, write this split's partial
+  // 5. reduce: the 8 row lanes of each column group, then the waves in order
 #pragma unroll
   for (int i = 0; i < TOK; ++i)
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) s_acc[(wv * TOK + i) * C + lane * CPL + e] = acc[i][e];
-  __syncthreads();
-  const int c0 = tile * C;
-  const int cw = min(C, a.n_out - c0);
-  for (int p = threadIdx.x; p < T_ * cw; p += 256) {
-    const int i = p / cw, cc = p % cw;
-    const float v = ((s_acc[(0 * TOK + i) * C + cc] + s_acc[(1 * TOK + i) * C + cc]) + s_acc[(2 * TOK + i) * C + cc]) +
-                    s_acc[(3 * TOK + i) * C + cc];
-    a.partial[((size_t)split * T_ + i) * a.n_out + c0 + cc] = v;
+    for (int e = 0; e < CPL; ++e) {
+      float v = acc[i][e];
+      v += __shfl_xor(v, 8, kWave);
+      v += __shfl_xor(v, 16, kWave);
+      v += __shfl_xor(v, 32, kWave);
+      acc[i][e] = v;
+    }
+  if (rs == 0) {
+#pragma unroll
+    for (int i = 0; i < TOK; ++i)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) s_acc[wv][i][cg * CPL + e] = acc[i][e];
   }
-  finish_tile<DT>(a, tile, split, s_eta, &s_flag, s_nu);
+  __syncthreads();
+
+  const int p = threadIdx.x;            // one (token, column) per thread: T_ * C <= 256
+  const int pi = p / C, pc = p % C, pcol = c0 + pc;
+  const bool pact = pi < T_ && pcol < a.n_out;
+  float v = 0.f;
+  if (pact) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += s_acc[w][pi][pc];
+  }
+  double stats[4] = {0.0, 0.0, 0.0, 0.0};
+  if (a.var && pi < T_ && pc == 0) {
+    for (int w = 0; w < NW; ++w)
+      for (int q = 0; q < 4; ++q) stats[q] += s_st[w][pi][q];
+  }
+
+  if (a.splits > 1) {
+    if (pact) coherent_store(&a.partial[((size_t)split * T_ + pi) * a.n_out + pcol], v);
+    if (a.var && pi < T_ && pc == 0)
+      for (int q = 0; q < 4; ++q)
+        coherent_store(&a.stats[(((size_t)tile * a.splits + split) * T_ + pi) * 4 + q], stats[q]);
+    if (!arrive_last(&a.counters[tile], a.splits, &s_flag)) return;
+    if (pact) {
+      // all loads first, then the sum in split order
+      v = 0.f;
+      for (int s0 = 0; s0 < a.splits; s0 += 16) {
+        float part[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          part[q] = s0 + q < a.splits ? coherent_load(&a.partial[((size_t)(s0 + q) * T_ + pi) * a.n_out + pcol]) : 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (s0 + q < a.splits) v += part[q];
+      }
+    }
+    if (a.var && pi < T_ && pc == 0) {
+      for (int q = 0; q < 4; ++q) stats[q] = 0.0;
+      for (int s2 = 0; s2 < a.splits; ++s2)
+        for (int q = 0; q < 4; ++q)
+          stats[q] += coherent_load(&a.stats[(((size_t)tile * a.splits + s2) * T_ + pi) * 4 + q]);
+    }
+  }
+  // 6. epilogue
+  if (pi < T_ && pc == 0) {
+    const float nu = a.var ? nu_from_stats(stats, a.k) : 1.f;
+    s_nu[pi] = nu;
+    if (tile == 0 && a.nu_out) a.nu_out[pi] = nu;
+  }
+  __syncthreads();
+  if (pact) {
+    float out = s_nu[pi] * v;
+    if (a.shift != SPA_SHIFT_NONE) out += s_eta[pi] * a.row_sum[pcol];
+    static_cast<T*>(a.y)[(size_t)pi * a.n_out + pcol] = from_f32<DT>(out);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -506,10 +712,43 @@ __global__ void __launch_bounds__(256) k_decode_stream(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = 16 * p + 4 * g + r;
-        if (tok < T_ && col < a.n_out) a.partial[((size_t)split * T_ + tok) * a.n_out + col] = acc[p][q][r];
+        if (tok < T_ && col < a.n_out)
+          coherent_store(&a.partial[((size_t)split * T_ + tok) * a.n_out + col], acc[p][q][r]);
       }
     }
-  finish_tile<DT>(a, tile, split, s_eta, &s_flag, s_nu);
+  if (!arrive_last(&a.counters[tile], a.splits, &s_flag)) return;
+
+  // last workgroup of the tile: nu from the mask kernel's per-group sums, then y
+  if ((int)threadIdx.x < T_) {
+    float nu = 1.f;
+    if (a.var) {
+      double st[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int g2 = 0; g2 < a.mask_groups; ++g2)
+        for (int q = 0; q < 4; ++q) st[q] += a.stats[((size_t)g2 * T_ + threadIdx.x) * 4 + q];
+      nu = nu_from_stats(st, a.k);
+    }
+    s_nu[threadIdx.x] = nu;
+    if (tile == 0 && a.nu_out) a.nu_out[threadIdx.x] = nu;
+  }
+  __syncthreads();
+  T* y = static_cast<T*>(a.y);
+  const int cw = min(C, a.n_out - c0);
+  for (int pidx = threadIdx.x; pidx < T_ * cw; pidx += 256) {
+    const int tok = pidx / cw, col = c0 + pidx % cw;
+    float v = 0.f;
+    for (int s0 = 0; s0 < a.splits; s0 += 16) {
+      float part[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        part[q] = s0 + q < a.splits ? coherent_load(&a.partial[((size_t)(s0 + q) * T_ + tok) * a.n_out + col]) : 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (s0 + q < a.splits) v += part[q];
+    }
+    float out = s_nu[tok] * v;
+    if (a.shift != SPA_SHIFT_NONE) out += s_eta[tok] * a.row_sum[col];
+    y[(size_t)tok * a.n_out + col] = from_f32<DT>(out);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -533,23 +772,31 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
   size_t bytes = 0;
   auto carve = [&](size_t nbytes) { size_t off = bytes; bytes += (nbytes + 255) & ~(size_t)255; return off; };
   if (fused) {
+    // 8 lanes x one 16-byte load = one 128-byte cache line of every listed row
     const int cpl = dtype == SPA_F32 ? 4 : 8;
-    p.col_tile = 64 * cpl;
+    p.col_tile = 8 * cpl;
     p.tiles = (n_out + p.col_tile - 1) / p.col_tile;
-    // aim for ~4 workgroups per CU; keep the partial traffic near 5 % of the weight bytes
-    int target = (1024 + p.tiles - 1) / p.tiles;
+    // split the channels only when the column tiles alone cannot fill the 256 CUs;
+    // each wave keeps at least one block, and the partial traffic stays near 5 % of the weight bytes
+    const int blocks = k / m;
+    int sp = p.tiles >= 192 ? 1 : (256 + p.tiles - 1) / p.tiles;
+    const int max_by_waves = blocks / 8 > 1 ? blocks / 8 : 1;
     const double wbytes = (double)k * n / m * n_out * 2.0;
-    const int cap = (int)(0.05 * wbytes / (8.0 * t * n_out));
-    if (target > cap) target = cap > 1 ? cap : 1;
-    // the fused kernel's LDS (scores, coefficients, rows, keep flags, wave partials) stays within 64 KiB
+    const int max_by_traffic = (int)(0.05 * wbytes / (8.0 * t * n_out));
+    if (sp > max_by_waves) sp = max_by_waves;
+    if (sp > max_by_traffic) sp = max_by_traffic > 1 ? max_by_traffic : 1;
+    // the workgroup's row list (row index + one coefficient per token per entry) lives in LDS:
+    // at most 54 KiB
     const int tok = t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : 8;
-    int max_kl = (65536 - 16 * tok * p.col_tile) / (4 * (1 + 2 * tok) + tok + 1);
-    max_kl = max_kl < 1024 ? max_kl : 1024;
-    max_kl = max_kl / 64 * 64;
-    if (max_kl < m) max_kl = m;
-    const int bl = pick_splits(k, m, target, max_kl);
+    const int per_block = m < n * t ? m : n * t;          // union rows one block can contribute
+    const int max_entries = 55296 / (4 * (1 + tok));
+    const int max_blocks = max_entries / per_block > 1 ? max_entries / per_block : 1;
+    int bl = (blocks + sp - 1) / sp;
+    if (bl > max_blocks) bl = max_blocks;
     p.k_len = bl * m;
     p.splits = (k + p.k_len - 1) / p.k_len;
+    p.list_cap = bl * per_block;
+    p.chunk_blocks = bl;
     p.mask_groups = 0;
     const size_t o_part = carve((size_t)p.splits * t * n_out * 4);
     const size_t o_stats = carve(var ? (size_t)p.tiles * p.splits * t * 4 * 8 : 0);
@@ -582,10 +829,9 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
 
 template <int DT, int M, int TOK>
 static hipError_t fused_launch(DecodeArgs& a, hipStream_t st) {
-  const int C = a.col_tile;
-  const size_t lds = (size_t)a.k_len * 4 * (1 + 2 * TOK) + (((size_t)TOK * a.k_len + 15) & ~(size_t)15) +
-                     (size_t)4 * TOK * C * 4;
-  hipLaunchKernelGGL((k_decode_fused<DT, M, TOK>), dim3(a.tiles * a.splits), dim3(256), lds, st, a);
+  constexpr int NW = fused_waves<M, TOK>();
+  const size_t lds = (size_t)a.list_cap * 4 * (1 + TOK);
+  hipLaunchKernelGGL((k_decode_fused<DT, M, TOK>), dim3(a.tiles * a.splits), dim3(NW * 64), lds, st, a);
   return hipGetLastError();
 }
 
@@ -594,7 +840,8 @@ static hipError_t fused_tok(DecodeArgs& a, hipStream_t st) {
   if (a.t <= 1) return fused_launch<DT, M, 1>(a, st);
   if (a.t <= 2) return fused_launch<DT, M, 2>(a, st);
   if (a.t <= 4) return fused_launch<DT, M, 4>(a, st);
-  return fused_launch<DT, M, 8>(a, st);
+  if constexpr (DT == SPA_F32) return fused_launch<DT, M, 8>(a, st);  // 16-bit t > 4 takes the MFMA path
+  return hipErrorInvalidValue;
 }
 
 template <int DT>

@@ -3,7 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/spa.h"
+#include "spa.h"
 #include "spa_launch.h"
 
 namespace {

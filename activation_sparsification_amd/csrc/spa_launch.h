@@ -59,6 +59,8 @@ struct DecodeArgs {
   uint16_t* coef;            // [k][32] dtype  (mask-then-stream path)
   float* eta_ws;             // [t]
   int tiles, splits, k_len, col_tile, mask_groups;
+  int list_cap;              // fused path: LDS list entries per wave
+  int chunk_blocks;          // fused path: m-blocks a wave selects and streams at a time
 };
 size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int score, int shift, int var,
                         DecodeArgs* plan);

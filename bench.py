@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the N:M activation-pruned linear layer on one MI355X.
+
+A step is one call of the library's hot path on one batch of synthetic
+input that is already resident in HBM.  The headline workload is the
+decode GEMV: X[1,4096] bf16, W[14336,4096] bf16, 8:16 weight-aware
+(alpha = 0.5) with the per-token mean shift -- one call of
+``sparse_linear_decode`` (shift, score, top-8-of-16, row-skipping GEMV,
+epilogue).  Its metric is the effective HBM bandwidth: algorithmic bytes
+(kept weight rows + x + per-channel factors + row sums + y) per step time.
+
+The weight is rotated over several device copies whose total exceeds the
+256 MB Infinity Cache three times over, so every step reads HBM.  Calls are
+queued behind a device sleep so that the timed region measures the GPU, not
+the Python launcher.
+
+Also reported, on the same line: the prefill workloads (TFLOP/s of kept
+products), the batched CLACT decode at t = 1, 8, 32, the oracle timed on the
+host cores (a baseline, not a target), and the roofline of the dominant
+kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16/fp16 matrix peak
+MALL_BYTES = 256 * 2 ** 20
+METRIC = "decode: effective HBM GB/s; prefill: TFLOP/s; both as % of MI355X peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fused_bf16_t1_k4096_n14336_traffic.txt")
+DECODE_SOURCES = ["activation_sparsification_amd/csrc/k_decode.hip", "activation_sparsification_amd/csrc/spa_common.h"]
+
+WORKLOADS = {
+    "decode": ("decode", dict()),
+    "prefill": ("prefill", dict()),
+    "relu2": ("relu2", dict()),
+    "batched_t1": ("batched", dict(t=1)),
+    "batched_t8": ("batched", dict(t=8)),
+    "batched_t32": ("batched", dict(t=32)),
+}
+DESCRIPTION = {
+    "decode": "decode GEMV 8:16 weight-aware alpha=0.5 + per-token mean shift, X[1,4096] bf16, W[14336,4096] bf16",
+    "prefill": "prefill 2:4 magnitude + per-token mean shift, X[2048,4096] bf16, W[14336,4096] bf16, smfmac",
+    "relu2": "squared-ReLU down-projection 2:4, X[4096,16384] bf16, W[4096,16384] bf16, smfmac",
+    "batched_t1": "batched decode 16:32 CLACT + variance rescale, X[1,14336] fp16, W[4096,14336] fp16",
+    "batched_t8": "batched decode 16:32 CLACT + variance rescale, X[8,14336] fp16, W[4096,14336] fp16",
+    "batched_t32": "batched decode 16:32 CLACT + variance rescale, X[32,14336] fp16, W[4096,14336] fp16",
+}
+
+
+def spec_of(name):
+    base, kw = WORKLOADS[name]
+    return wl.SPECS[base].with_(**kw)
+
+
+def sources_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per launch of the decode kernel from the committed counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.loads(fh.readline())
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sources_sha(DECODE_SOURCES):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+class Workload:
+    """Device-resident inputs, rotated weight copies and pre-marshalled calls."""
+
+    def __init__(self, name, seed=0):
+        import activation_sparsification_amd as spa
+        self.spa = spa
+        self.name = name
+        self.spec = spec = spec_of(name)
+        self.decode = name.startswith("decode") or name.startswith("batched")
+        dev = torch.device("cuda:0")
+        x, w = wl.make_inputs(spec, seed=seed)
+        self.x_cpu, self.w_cpu = x, w
+        self.x = x.to(dev)
+        wd = w.to(dev)
+        self.pw = spa.prepare_weight(wd, spec.alpha, want_wt=self.decode)
+        self.cfg = spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, spec.var_rescale)
+        big = self.pw.wt if self.decode else self.pw.w
+        wbytes = big.numel() * big.element_size()
+        self.copies = max(3, math.ceil(3 * MALL_BYTES / wbytes))
+        mats = [big] + [big.clone() for _ in range(self.copies - 1)]
+        self.y = torch.empty((spec.t, spec.n_out), dtype=x.dtype, device=dev)
+        entry = 1 if self.decode else 2
+        self.ws = spa.workspace(entry, spec.t, spec.k, spec.n_out, x.dtype, self.cfg, dev)
+        fn = "sparse_linear_decode" if self.decode else "sparse_linear_prefill"
+        if self.decode:
+            self.calls = [spa.PreparedCall(fn, self.x, self.pw, self.cfg, self.y, self.ws, wt=m) for m in mats]
+        else:
+            self.calls = [spa.PreparedCall(fn, self.x, self.pw, self.cfg, self.y, self.ws, w=m) for m in mats]
+        self._mats = mats
+        torch.cuda.synchronize()
+
+    def union_rows(self):
+        """Channels kept by at least one token of the call (the rows of W^T read)."""
+        spec = self.spec
+        y, idx, nu = self.spa.sparse_linear_decode(self.x, self.pw, self.cfg, want_idx=True)
+        torch.cuda.synchronize()
+        idx = idx.cpu().numpy().astype(np.int64).reshape(spec.t, spec.k // spec.m, spec.n)
+        ch = idx + (np.arange(spec.k // spec.m) * spec.m)[None, :, None]
+        return int(np.unique(ch).size)
+
+    def work(self):
+        """(algorithmic bytes, kept flops) of one step."""
+        s = self.spec
+        el = self.x.element_size()
+        if self.decode:
+            rows = self.union_rows()
+            b = rows * s.n_out * el + s.t * s.k * el + s.t * s.n_out * el
+            if s.score == "weight":
+                b += s.k * 4
+            if s.shift != "none":
+                b += s.n_out * 4
+            flops = 2.0 * s.t * s.n_out * s.k * s.n / s.m
+            return b, flops, rows
+        b = s.n_out * s.k * el + s.t * s.k * el + s.t * s.n_out * el
+        flops = 2.0 * s.t * s.n_out * s.k * s.n / s.m
+        return b, flops, None
+
+    def time(self, steps, warmup):
+        calls = self.calls
+        for i in range(warmup):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        ev_s, ev0, ev1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        # keep the GPU busy while the host queues every timed call
+        ev_s.record()
+        torch.cuda._sleep(int(2e6) + 60000 * steps)
+        ev0.record()
+        h0 = time.perf_counter()
+        for i in range(steps):
+            calls[i % len(calls)]()
+        host_s = time.perf_counter() - h0
+        ev1.record()
+        torch.cuda.synchronize()
+        gpu_ms = ev0.elapsed_time(ev1)
+        sleep_ms = ev_s.elapsed_time(ev0)
+        return gpu_ms / steps, dict(host_enqueue_ms=host_s * 1e3, sleep_ms=sleep_ms,
+                                    gpu_bound=sleep_ms > host_s * 1e3)
+
+
+def measure(name, steps, warmup):
+    w = Workload(name)
+    ms, info = w.time(steps, warmup)
+    b, flops, rows = w.work()
+    rec = dict(workload=name, desc=DESCRIPTION[name], ms_per_step=ms, weight_copies=w.copies, **info)
+    if w.decode:
+        gbs = b / (ms * 1e-3) / 1e9
+        rec.update(unit="GB/s", value=gbs, pct_of_peak=100.0 * gbs / PEAK_HBM_GBS, algorithmic_bytes=b,
+                   union_rows=rows, union_fraction=rows / w.spec.k)
+    else:
+        tf = flops / (ms * 1e-3) / 1e12
+        rec.update(unit="TFLOP/s", value=tf, pct_of_peak=100.0 * tf / PEAK_BF16_TFLOPS, kept_flops=flops,
+                   algorithmic_bytes=b)
+    del w
+    torch.cuda.empty_cache()
+    return rec
+
+
+def cpu_baseline(name, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the workload on the host cores."""
+    from oracle import nm_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = None
+    spec = spec_of(name)
+    x, w = wl.make_inputs(spec)
+    x32 = x.float().numpy()
+    w32 = w.float().numpy()
+    f = O.channel_factor(w32, spec.alpha) if spec.score == "weight" else None  # weight prep: off the timed path
+    s = O.row_sum(w32)
+    # one step = oracle prune + linear of the step's tokens
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        pr = O.prune(x32, spec.dtype, spec.n, spec.m, score=spec.score, f=f, shift_mode=spec.shift,
+                     var_rescale=spec.var_rescale)
+        O.linear(pr, w32, s)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 200:
+            break
+    per_step = el / n
+    rows = int(pr["keep"].any(axis=0).sum())
+    el_b = x.element_size()
+    b = rows * spec.n_out * el_b + spec.t * spec.k * el_b + spec.t * spec.n_out * el_b
+    b += (spec.k * 4 if spec.score == "weight" else 0) + (spec.n_out * 4 if spec.shift != "none" else 0)
+    cores = len(os.sched_getaffinity(0))
+    return dict(value=b / per_step / 1e9, unit="GB/s", cores=blas_threads or cores, host_cores=cores,
+                kind="oracle", sample=f"{n} steps of the {name} workload (t={spec.t}), oracle prune + float64 "
+                f"linear per step, {el:.1f} s", s_per_step=per_step)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--only", action="store_true", help="time the headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the pruned linear layer runs on a single MI355X "
+              "(multi-GPU sharding is described in the design notes, not built)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.calib_copy:
+        src = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    head = measure(args.workload, args.steps, args.warmup)
+    secondary = []
+    if not args.only:
+        for name in ["prefill", "relu2", "batched_t1", "batched_t8", "batched_t32"]:
+            if name == args.workload:
+                continue
+            st = max(10, args.steps // 4) if name in ("prefill", "relu2") else args.steps
+            secondary.append(measure(name, st, max(5, args.warmup // 2)))
+
+    decode = head["unit"] == "GB/s"
+    traffic = read_traffic() if args.workload == "decode" else None
+    roof = dict(bound="hbm" if decode else "mfma",
+                achieved=head["value"],
+                peak=PEAK_HBM_GBS if decode else PEAK_BF16_TFLOPS,
+                unit=head["unit"],
+                frac=head["value"] / (PEAK_HBM_GBS if decode else PEAK_BF16_TFLOPS),
+                traffic=traffic,
+                kernel="k_decode_fused<bf16,16,1>" if args.workload == "decode" else None,
+                per_unit="bytes per kept weight row = n_out * 2; one launch reads the call's kept rows")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload if decode else "decode")
+        cpu["value"] = float(cpu["value"])
+    spec = spec_of(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded, numpy PCG64; see workloads/)",
+        "config": {"workload": head["desc"], "t": spec.t, "k": spec.k, "n_out": spec.n_out,
+                   "pattern": f"{spec.n}:{spec.m}", "score": spec.score, "alpha": spec.alpha, "shift": spec.shift,
+                   "var_rescale": spec.var_rescale, "parallelism": "single GPU"},
+        "pct_of_peak": head["pct_of_peak"],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": head,
+        "secondary": secondary,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
