@@ -4,23 +4,24 @@
 // operands contiguous along k, which is how the matrix-core fragments want
 // them).  For 2:4 the pruning pass has packed A to its kept half plus one
 // nibble of in-block positions per block, and the gfx950 sparse MFMA
-// (v_smfmac_f32_16x16x64) skips the pruned products -- the 2:4 scheme of
+// (v_smfmac_f32_32x32x32) skips the pruned products -- the 2:4 scheme of
 // "Accelerating Transformer training and inference with 2:4 sparsity and
 // Squared-ReLU" s2.1/s3.1 on CDNA4's own instruction.  Other n:m patterns
-// run dense MFMA (v_mfma_f32_16x16x32) on the masked rows.
+// run dense MFMA (v_mfma_f32_32x32x16) on the masked rows.
 //
-// Fragment layouts (gfx950, lane l, g = l / 16):
-//   smfmac A: row l%16, 8 packed values = logical k [16g, 16g+16) of the
-//             64-wide step, position bits from the 16-bit half given by abid;
-//   smfmac B: column l%16, k = 8g..8g+7 then 32+8g..32+8g+7;
-//   mfma   A: row l%16, k = 8g..8g+7;  B: column l%16, k = 8g..8g+7;
-//   D:        column l%16, rows 4g..4g+3.
+// Fragment layouts (gfx950, lane l, l32 = l % 32, g = l / 32):
+//   smfmac A: row l32, 8 packed values = logical k [16g, 16g+16) of each
+//             32-wide half step, position bits from the 16-bit half of the
+//             index operand;
+//   smfmac B: column l32, k = 8g..8g+7 then 16+8g..16+8g+7 (per half step);
+//   mfma   A: row l32, k = 8g..8g+7;  B: column l32, same k;
+//   D:        register r holds row 8(r/4) + 4g + r%4, column l32.
 //
-// Tiling: BM x BN per workgroup, four waves in a 2 x 2 grid, k in steps of
-// 64 (logical).  Global tiles go through registers into a double-buffered
-// LDS stage (rows padded by 16 bytes against bank conflicts).  Workgroups
-// are ordered so that one XCD (each has its own L2) works through all the
-// token tiles of one weight tile before moving on.
+// Both kernels stream 64-wide k steps through a three-stage LDS ring filled
+// by direct global->LDS loads (no register staging), 512 threads = 8 waves
+// (two per SIMD, so one wave's matrix instructions cover the other's LDS
+// reads), and order workgroups so that one XCD (each has its own L2) works
+// through all the token tiles of one weight tile before moving on.
 #include "spa_common.h"
 #include "spa_launch.h"
 
@@ -30,206 +31,446 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int DT> struct Frag;
 template <> struct Frag<SPA_BF16> { using V8 = bf16x8; using V16 = bf16x16; };
 template <> struct Frag<SPA_F16> { using V8 = f16x8; using V16 = f16x16; };
 
-template <int DT>
-__device__ __forceinline__ f32x4 smfmac(const typename Frag<DT>::V8& a, const typename Frag<DT>::V16& b, f32x4 c,
-                                        int idx) {
-  if constexpr (DT == SPA_BF16) return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a, b, c, idx, 0, 0);
-  else return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, b, c, idx, 0, 0);
-}
-template <int DT>
-__device__ __forceinline__ f32x4 mfma(const typename Frag<DT>::V8& a, const typename Frag<DT>::V8& b, f32x4 c) {
-  if constexpr (DT == SPA_BF16) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  else return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
 template <class V>
 __device__ __forceinline__ V as_vec(const uint4& u) { return __builtin_bit_cast(V, u); }
 
-// SPARSE: A row holds 32 packed halves (64 B) + 4 uint16 meta per 64-wide step.
-// DENSE : A row holds 64 halves (128 B).
-template <int DT, bool SPARSE, int BM, int BN>
-__global__ void __launch_bounds__(256) k_gemm(PrefillArgs p) {
-  constexpr int BK = 64;
-  constexpr int AH = SPARSE ? 32 : 64;          // A halves per row per step
-  constexpr int APAD = AH + 8;                  // padded LDS row (halves)
-  constexpr int BPAD = BK + 8;
-  constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
-  constexpr int FM = WM / 16, FN = WN / 16;     // fragments per wave
-  constexpr int A_SEGS = BM * AH / 8;           // 16-byte segments per A tile
-  constexpr int B_SEGS = BN * BK / 8;
-  constexpr int A_PER = (A_SEGS + 255) / 256;
-  constexpr int B_PER = (B_SEGS + 255) / 256;
-  constexpr int A_SEG_ROW = AH / 8, B_SEG_ROW = BK / 8;
-  using V8 = typename Frag<DT>::V8;
-  using V16 = typename Frag<DT>::V16;
+// Two 16-byte chunks as one 16-element operand (lo = elements 0..7).
+template <int DT>
+__device__ __forceinline__ typename Frag<DT>::V16 cat16(const uint4& lo, const uint4& hi) {
+  const uint4 both[2] = {lo, hi};
+  return __builtin_bit_cast(typename Frag<DT>::V16, both);
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM][APAD];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[2][BN][BPAD];
-  __shared__ uint16_t s_m[2][SPARSE ? BM : 1][4];
+template <int DT>
+__device__ __forceinline__ f32x16 smfmac32(const typename Frag<DT>::V8& a, const typename Frag<DT>::V16& b, f32x16 c,
+                                           int idx) {
+  if constexpr (DT == SPA_BF16) return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a, b, c, idx, 0, 0);
+  else return __builtin_amdgcn_smfmac_f32_32x32x32_f16(a, b, c, idx, 0, 0);
+}
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(const typename Frag<DT>::V8& a, const typename Frag<DT>::V8& b, f32x16 c) {
+  if constexpr (DT == SPA_BF16) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
-  const int T = p.t, K = p.k, N = p.n_out;
+// ---------------------------------------------------------------------------
+// Direct global->LDS loads and the waits that order them.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+// Lane l's 16 (or 4) bytes at sbase + voff land at LDS address lds + 16 l
+// (4 l); sbase and lds are wave-uniform.  Issued from asm so that the
+// compiler does not add waits of its own before later LDS reads: the kernels
+// order these copies with explicit vmcnt waits and the workgroup barrier.
+// No register is written, so nothing but LDS bytes is left in flight.  An
+// LDS-DMA reading M0 needs one wait state after the M0 write (s_nop 0).
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
+               : "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
+               : "m0");
+}
+
+// Wait until at most KEEP of this wave's vector-memory operations are
+// outstanding (keep != 0), or none (keep == 0).
+template <int KEEP>
+__device__ __forceinline__ void wait_vm(int keep) {
+  static_assert(KEEP >= 0 && KEEP < 16, "vmcnt field");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (keep) __builtin_amdgcn_s_waitcnt(0x0F70 | KEEP);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Workgroup barrier after this wave's own LDS reads have completed (the stage
+// they read is refilled by direct loads right after the barrier).  Vector
+// memory is ordered by the explicit wait_vm before it, not here.
+__device__ __forceinline__ void bare_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD gets a
+// contiguous run of tile indices, token tiles fastest, so one XCD's L2
+// serves a weight tile to the token tiles that use it.
+__device__ __forceinline__ void xcd_tile(int T, int N, int BM, int BN, int& tm, int& tn) {
   const int tiles_m = (T + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int total = tiles_m * tiles_n;
-  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous
-  // run of tile indices, token tiles fastest.
   int bid = blockIdx.x;
   const int per_xcd = total / 8;
   if (bid < per_xcd * 8) bid = (bid % 8) * per_xcd + bid / 8;
-  const int tm = bid % tiles_m, tn = bid / tiles_m;
-  const int m0 = tm * BM, n0 = tn * BN;
+  tm = bid % tiles_m;
+  tn = bid / tiles_m;
+}
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
-  const int wm0 = (wv >> 1) * WM, wn0 = (wv & 1) * WN;
-
-  const uint16_t* A = static_cast<const uint16_t*>(p.a_vals);
-  const uint16_t* W = static_cast<const uint16_t*>(p.w);
-  const int a_row_halves = SPARSE ? K / 2 : K;
-
-  uint4 ra[A_PER], rb[B_PER];
-  uint2 rm;
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int s = threadIdx.x + 256 * i;
-      const int r = s / A_SEG_ROW, c = s % A_SEG_ROW;
-      const int row = m0 + r;
-      if (s < A_SEGS && row < T)
-        ra[i] = *reinterpret_cast<const uint4*>(A + (size_t)row * a_row_halves + (size_t)kt * AH + c * 8);
-      else
-        ra[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      const int s = threadIdx.x + 256 * i;
-      const int r = s / B_SEG_ROW, c = s % B_SEG_ROW;
-      const int row = n0 + r;
-      if (s < B_SEGS && row < N)
-        rb[i] = *reinterpret_cast<const uint4*>(W + (size_t)row * K + (size_t)kt * BK + c * 8);
-      else
-        rb[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    if constexpr (SPARSE) {
-      const int row = m0 + (int)threadIdx.x;
-      if ((int)threadIdx.x < BM && row < T)
-        rm = *reinterpret_cast<const uint2*>(p.a_meta + (size_t)row * (K / 16) + (size_t)kt * 4);
-      else
-        rm = make_uint2(0x44444444u, 0x44444444u);  // positions (0,1): valid, multiplies zeros
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int s = threadIdx.x + 256 * i;
-      if (s < A_SEGS) {
-        const int r = s / A_SEG_ROW, c = s % A_SEG_ROW;
-        *reinterpret_cast<uint4*>(&s_a[buf][r][c * 8]) = ra[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      const int s = threadIdx.x + 256 * i;
-      if (s < B_SEGS) {
-        const int r = s / B_SEG_ROW, c = s % B_SEG_ROW;
-        *reinterpret_cast<uint4*>(&s_b[buf][r][c * 8]) = rb[i];
-      }
-    }
-    if constexpr (SPARSE) {
-      if ((int)threadIdx.x < BM) *reinterpret_cast<uint2*>(&s_m[buf][threadIdx.x][0]) = rm;
-    }
-  };
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    if constexpr (SPARSE) {
-      V16 bf[FN];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint16_t* br = &s_b[buf][wn0 + j * 16 + l16][0];
-        const uint4 lo = *reinterpret_cast<const uint4*>(br + 8 * g);
-        const uint4 hi = *reinterpret_cast<const uint4*>(br + 32 + 8 * g);
-        const uint4 both[2] = {lo, hi};
-        bf[j] = __builtin_bit_cast(V16, both);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm0 + i * 16 + l16;
-        const V8 af = as_vec<V8>(*reinterpret_cast<const uint4*>(&s_a[buf][r][8 * g]));
-        const int idx = (int)s_m[buf][r][g];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = smfmac<DT>(af, bf[j], acc[i][j], idx);
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        V8 bf[FN];
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bf[j] = as_vec<V8>(*reinterpret_cast<const uint4*>(&s_b[buf][wn0 + j * 16 + l16][32 * s + 8 * g]));
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const V8 af = as_vec<V8>(*reinterpret_cast<const uint4*>(&s_a[buf][wm0 + i * 16 + l16][32 * s + 8 * g]));
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma<DT>(af, bf[j], acc[i][j]);
-        }
-      }
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
+// Epilogue operands of one tile (BM rows, BN columns): each thread fetches at
+// most one nu, one eta and one row sum when the workgroup starts, holds them
+// in registers across the main loop and parks them in LDS at the end.
+template <int BM, int BN>
+struct TileScalars {
+  float nu, eta, rs;
+  __device__ __forceinline__ void fetch(const PrefillArgs& p, int m0, int n0) {
+    const int i = threadIdx.x;
+    const int row = min(m0 + (i & (BM - 1)), p.t - 1);
+    nu = (p.nu && i < BM) ? p.nu[row] : 1.f;
+    eta = (p.eta && i < BM) ? p.eta[row] : 0.f;
+    rs = (p.eta && i < BN) ? p.row_sum[min(n0 + i, p.n_out - 1)] : 0.f;
   }
+  __device__ __forceinline__ void park(float* s_nu, float* s_eta, float* s_rs) const {
+    const int i = threadIdx.x;
+    if (i < BM) {
+      s_nu[i] = nu;
+      s_eta[i] = eta;
+    }
+    if (i < BN) s_rs[i] = rs;
+  }
+};
 
-  // epilogue: y = nu_i * acc + eta_i * rowsum_j
+// y = nu_i * acc + eta_i * rowsum_j for a wave's FM x FN fragments of 32 x 32
+// at tile-relative (r0, c0) of the tile that starts at (m0, n0).
+template <int DT, int FM, int FN>
+__device__ __forceinline__ void store_tile(const PrefillArgs& p, const f32x16 (&acc)[FM][FN], int m0, int n0,
+                                           int r0, int c0, int g, int l32, const float* s_nu, const float* s_eta,
+                                           const float* s_rs) {
   uint16_t* Y = static_cast<uint16_t*>(p.y);
+  float rs[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) rs[j] = s_rs[c0 + 32 * j + l32];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = m0 + wm0 + i * 16 + 4 * g + r;
-      if (row >= T) continue;
-      const float nu = p.nu ? p.nu[row] : 1.f;
-      const float eta = p.eta ? p.eta[row] : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      const int tr = r0 + 32 * i + 8 * (r / 4) + 4 * g + (r % 4);
+      const int row = m0 + tr;
+      if (row >= p.t) continue;
+      const float nu = s_nu[tr], eta = s_eta[tr];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn0 + j * 16 + l16;
-        if (col < N) {
-          float v = nu * acc[i][j][r];
-          if (p.eta) v += eta * p.row_sum[col];
-          Y[(size_t)row * N + col] = (uint16_t)from_f32<DT>(v);
+        const int col = n0 + c0 + 32 * j + l32;
+        if (col < p.n_out) {
+          const float v = nu * acc[i][j][r] + eta * rs[j];
+          Y[(size_t)row * p.n_out + col] = (uint16_t)from_f32<DT>(v);
         }
       }
     }
   }
 }
 
-template <int DT, bool SPARSE>
-static hipError_t gemm_launch(const PrefillArgs& a, hipStream_t st) {
+// ---------------------------------------------------------------------------
+// 2:4 smfmac GEMM.  The pruning pass stores the packed activations and their
+// position words step-major (per 64-channel step: rows padded to t_pad, 64 B
+// of packed values and 8 B of position words per row), so a 256-row tile of
+// one step is one contiguous run.  BM = BN = 256; waves in a 2 x 4 grid of
+// 128 x 64 (4 x 2 fragments of 32 x 32).  Every wave issues exactly seven
+// direct loads per step (two 1 KB runs of packed values, four 1 KB groups of
+// weight rows, one 256 B run of position words); waiting for vmcnt <= 7
+// therefore means "the older of the two steps in flight has landed".
+//
+// Each stage lives in its own __shared__ arrays.  Rows are unpadded; 16-byte
+// chunks are XOR-swizzled against bank conflicts: chunk c of activation row r
+// sits at c ^ ((r >> 2) & 3), of weight row r at c ^ ((r >> 1) & 7).  Weight
+// rows past n_out re-read the last row; padded activation rows hold whatever
+// the workspace held.  Neither reaches y: outputs are stored for rows < t and
+// columns < n_out only, and no row's result depends on another row.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ void __launch_bounds__(512, 1) k_gemm24(PrefillArgs p) {
   constexpr int BM = 256, BN = 256;
-  const int tiles = ((a.t + BM - 1) / BM) * ((a.n_out + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm<DT, SPARSE, BM, BN>), dim3(tiles), dim3(256), 0, st, a);
-  return hipGetLastError();
+  constexpr int WM = 128, WN = 64, FM = 4, FN = 2;
+  using V8 = typename Frag<DT>::V8;
+  using V16 = typename Frag<DT>::V16;
+  // stage = packed activations (BM x 64 B) followed by their position words
+  // (BM x 8 B): six LDS objects in all
+  constexpr int AMH = BM * 32 + BM * 4;
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[AMH];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[AMH];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA2[AMH];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BN * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BN * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB2[BN * 64];
+  __shared__ float s_nu[BM], s_eta[BM], s_rs[BN];
+  uint16_t* const sM0 = sA0 + BM * 32;
+  uint16_t* const sM1 = sA1 + BM * 32;
+  uint16_t* const sM2 = sA2 + BM * 32;
+
+  const int K = p.k, N = p.n_out, TP = p.t_pad;
+  int tm, tn;
+  xcd_tile(p.t, N, BM, BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  TileScalars<BM, BN> ts;
+  ts.fetch(p, m0, n0);
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int wm0 = (wv >> 2) * WM, wn0 = (wv & 3) * WN;
+
+  // ---- direct-load sources: uniform per-step bases + 32-bit lane offsets ----
+  const char* baseA = static_cast<const char*>(p.a_vals) + (size_t)m0 * 64;
+  const char* baseM = reinterpret_cast<const char*>(p.a_meta) + (size_t)m0 * 8;
+  const char* baseW = static_cast<const char*>(p.w) + (size_t)n0 * K * 2;
+  const size_t stepA = (size_t)TP * 64, stepM = (size_t)TP * 8;
+  // activation run h of wave wv: LDS slot s holds row 16 (2 wv + h) + s/4
+  const int ra0 = 32 * wv + (lane >> 2), ra1 = ra0 + 16;
+  const uint32_t offA0 = (uint32_t)(ra0 * 64 + (((lane & 3) ^ ((ra0 >> 2) & 3)) * 16));
+  const uint32_t offA1 = (uint32_t)(ra1 * 64 + (((lane & 3) ^ ((ra1 >> 2) & 3)) * 16));
+  // weight group h of wave wv: LDS slot s holds row 8 (4 wv + h) + s/8
+  uint32_t offB[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int r = 32 * wv + 8 * h + (lane >> 3);
+    const int rr = min(n0 + r, N - 1) - n0;
+    offB[h] = (uint32_t)rr * (uint32_t)K * 2u + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) * 16);
+  }
+  const uint32_t offM = (uint32_t)((wv * 64 + lane) * 4);
+
+  // ---- LDS fragment offsets (bytes); the swizzle terms do not depend on i or j ----
+  const int qa = (l32 >> 2) & 3, qb = (l32 >> 1) & 7;
+  const int rowA = wm0 + l32, rowB = wn0 + l32;
+  int ldsA[2], ldsBlo[2], ldsBhi[2], ldsM[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    ldsA[s] = rowA * 64 + (((2 * s + g) ^ qa) * 16);
+    ldsBlo[s] = rowB * 128 + (((4 * s + g) ^ qb) * 16);
+    ldsBhi[s] = rowB * 128 + (((4 * s + 2 + g) ^ qb) * 16);
+    ldsM[s] = rowA * 8 + (2 * s + g) * 2;
+  }
+
+#define SPA_ISSUE24(KT, SA, SB, SM)                                                      \
+  do {                                                                                   \
+    const char* a_ = baseA + (size_t)(KT) * stepA;                                       \
+    const char* w_ = baseW + (size_t)(KT) * 128;                                         \
+    const uint32_t la_ = lds_addr(SA) + wv * 2048, lb_ = lds_addr(SB) + wv * 4096;       \
+    lds_dma16(a_, offA0, la_);                                                           \
+    lds_dma16(a_, offA1, la_ + 1024);                                                    \
+    lds_dma16(w_, offB[0], lb_);                                                         \
+    lds_dma16(w_, offB[1], lb_ + 1024);                                                  \
+    lds_dma16(w_, offB[2], lb_ + 2048);                                                  \
+    lds_dma16(w_, offB[3], lb_ + 3072);                                                  \
+    lds_dma4(baseM + (size_t)(KT) * stepM, offM, lds_addr(SM) + wv * 256);               \
+  } while (0)
+
+#define SPA_COMPUTE24(SA, SB, SM)                                                                    \
+  do {                                                                                              \
+    const char* a_ = reinterpret_cast<const char*>(SA);                                             \
+    const char* b_ = reinterpret_cast<const char*>(SB);                                             \
+    const char* m_ = reinterpret_cast<const char*>(SM);                                             \
+    _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                                 \
+      V16 bf[FN];                                                                                   \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                                \
+        bf[j] = cat16<DT>(*reinterpret_cast<const uint4*>(b_ + ldsBlo[s] + j * 4096),               \
+                          *reinterpret_cast<const uint4*>(b_ + ldsBhi[s] + j * 4096));              \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                              \
+        const V8 af = as_vec<V8>(*reinterpret_cast<const uint4*>(a_ + ldsA[s] + i * 2048));         \
+        const int idx = (int)*reinterpret_cast<const uint16_t*>(m_ + ldsM[s] + i * 256);            \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] = smfmac32<DT>(af, bf[j], acc[i][j], idx); \
+      }                                                                                             \
+    }                                                                                               \
+  } while (0)
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Step kt is read from stage kt % 3.  Before computing it: wait until only
+  // step kt+1's loads (if issued) are still in flight, barrier (everyone's
+  // copies of step kt landed, everyone finished step kt-1, whose stage is
+  // refilled next), then request step kt+2 into that stage.
+  const int nk = K / 64;
+  const int nq = nk / 3, nr = nk - 3 * nq;
+  SPA_ISSUE24(0, sA0, sB0, sM0);
+  if (nk > 1) SPA_ISSUE24(1, sA1, sB1, sM1);
+  for (int q = 0; q < nq; ++q) {
+    const int kt = 3 * q;
+    wait_vm<7>(kt + 1 < nk);
+    bare_barrier();
+    SPA_ISSUE24(kt + 2, sA2, sB2, sM2);
+    SPA_COMPUTE24(sA0, sB0, sM0);
+    wait_vm<7>(1);
+    bare_barrier();
+    if (kt + 3 < nk) SPA_ISSUE24(kt + 3, sA0, sB0, sM0);
+    SPA_COMPUTE24(sA1, sB1, sM1);
+    wait_vm<7>(kt + 3 < nk);
+    bare_barrier();
+    if (kt + 4 < nk) SPA_ISSUE24(kt + 4, sA1, sB1, sM1);
+    SPA_COMPUTE24(sA2, sB2, sM2);
+  }
+  if (nr >= 1) {                       // step 3nq in stage 0 (step 3nq+1, if any, in flight)
+    wait_vm<7>(nr == 2);
+    bare_barrier();
+    SPA_COMPUTE24(sA0, sB0, sM0);
+  }
+  if (nr == 2) {                       // step 3nq+1 in stage 1
+    wait_vm<7>(0);
+    bare_barrier();
+    SPA_COMPUTE24(sA1, sB1, sM1);
+  }
+#undef SPA_ISSUE24
+#undef SPA_COMPUTE24
+
+  ts.park(s_nu, s_eta, s_rs);
+  __syncthreads();
+  store_tile<DT, FM, FN>(p, acc, m0, n0, wm0, wn0, g, l32, s_nu, s_eta, s_rs);
+}
+
+// ---------------------------------------------------------------------------
+// Dense MFMA on masked rows (n:m other than 2:4): BM = 256 tokens x BN = 128
+// outputs per workgroup, waves in a 4 x 2 grid of 64 x 64 (2 x 2 fragments of
+// 32 x 32).  A stage is 256 activation rows + 128 weight rows of 128 B; each
+// wave issues six 1 KB direct loads per step, so vmcnt <= 6 means "the older
+// step in flight has landed".  Rows past t (or n_out) re-read the last row;
+// their outputs are never stored.  Chunk c of any row r sits at c ^ ((r>>1)&7).
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ void __launch_bounds__(512, 1) k_gemm_dense(PrefillArgs p) {
+  constexpr int BM = 256, BN = 128;
+  constexpr int WM = 64, WN = 64, FM = 2, FN = 2;
+  using V8 = typename Frag<DT>::V8;
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[BM * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[BM * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA2[BM * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BN * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BN * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB2[BN * 64];
+  __shared__ float s_nu[BM], s_eta[BM], s_rs[BN];
+
+  const int T = p.t, K = p.k, N = p.n_out;
+  int tm, tn;
+  xcd_tile(T, N, BM, BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  TileScalars<BM, BN> ts;
+  ts.fetch(p, m0, n0);
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int wm0 = (wv >> 1) * WM, wn0 = (wv & 1) * WN;
+
+  const char* baseA = static_cast<const char*>(p.a_vals) + (size_t)m0 * K * 2;
+  const char* baseW = static_cast<const char*>(p.w) + (size_t)n0 * K * 2;
+  uint32_t offA[4], offB[2];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int r = 32 * wv + 8 * h + (lane >> 3);
+    const int rr = min(m0 + r, T - 1) - m0;
+    offA[h] = (uint32_t)rr * (uint32_t)K * 2u + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) * 16);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 16 * wv + 8 * h + (lane >> 3);
+    const int rr = min(n0 + r, N - 1) - n0;
+    offB[h] = (uint32_t)rr * (uint32_t)K * 2u + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) * 16);
+  }
+  const int q = (l32 >> 1) & 7;
+  int ldsA[4], ldsB[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    ldsA[s] = (wm0 + l32) * 128 + (((2 * s + g) ^ q) * 16);
+    ldsB[s] = (wn0 + l32) * 128 + (((2 * s + g) ^ q) * 16);
+  }
+
+#define SPA_ISSUED(KT, SA, SB)                                                     \
+  do {                                                                             \
+    const char* a_ = baseA + (size_t)(KT) * 128;                                   \
+    const char* w_ = baseW + (size_t)(KT) * 128;                                   \
+    const uint32_t la_ = lds_addr(SA) + wv * 4096, lb_ = lds_addr(SB) + wv * 2048; \
+    lds_dma16(a_, offA[0], la_);                                                   \
+    lds_dma16(a_, offA[1], la_ + 1024);                                            \
+    lds_dma16(a_, offA[2], la_ + 2048);                                            \
+    lds_dma16(a_, offA[3], la_ + 3072);                                            \
+    lds_dma16(w_, offB[0], lb_);                                                   \
+    lds_dma16(w_, offB[1], lb_ + 1024);                                            \
+  } while (0)
+
+#define SPA_COMPUTED(SA, SB)                                                                         \
+  do {                                                                                              \
+    const char* a_ = reinterpret_cast<const char*>(SA);                                             \
+    const char* b_ = reinterpret_cast<const char*>(SB);                                             \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                                 \
+      V8 bf[FN];                                                                                    \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                                \
+        bf[j] = as_vec<V8>(*reinterpret_cast<const uint4*>(b_ + ldsB[s] + j * 4096));              \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                              \
+        const V8 af = as_vec<V8>(*reinterpret_cast<const uint4*>(a_ + ldsA[s] + i * 4096));         \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(af, bf[j], acc[i][j]); \
+      }                                                                                             \
+    }                                                                                               \
+  } while (0)
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = K / 64;
+  const int nq = nk / 3, nr = nk - 3 * nq;
+  SPA_ISSUED(0, sA0, sB0);
+  if (nk > 1) SPA_ISSUED(1, sA1, sB1);
+  for (int qq = 0; qq < nq; ++qq) {
+    const int kt = 3 * qq;
+    wait_vm<6>(kt + 1 < nk);
+    bare_barrier();
+    SPA_ISSUED(kt + 2, sA2, sB2);
+    SPA_COMPUTED(sA0, sB0);
+    wait_vm<6>(1);
+    bare_barrier();
+    if (kt + 3 < nk) SPA_ISSUED(kt + 3, sA0, sB0);
+    SPA_COMPUTED(sA1, sB1);
+    wait_vm<6>(kt + 3 < nk);
+    bare_barrier();
+    if (kt + 4 < nk) SPA_ISSUED(kt + 4, sA1, sB1);
+    SPA_COMPUTED(sA2, sB2);
+  }
+  if (nr >= 1) {
+    wait_vm<6>(nr == 2);
+    bare_barrier();
+    SPA_COMPUTED(sA0, sB0);
+  }
+  if (nr == 2) {
+    wait_vm<6>(0);
+    bare_barrier();
+    SPA_COMPUTED(sA1, sB1);
+  }
+#undef SPA_ISSUED
+#undef SPA_COMPUTED
+
+  ts.park(s_nu, s_eta, s_rs);
+  __syncthreads();
+  store_tile<DT, FM, FN>(p, acc, m0, n0, wm0, wn0, g, l32, s_nu, s_eta, s_rs);
 }
 
 hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st) {
   if (a.t == 0) return hipSuccess;
-  if (dtype == SPA_F16) return a.sparse24 ? gemm_launch<SPA_F16, true>(a, st) : gemm_launch<SPA_F16, false>(a, st);
-  return a.sparse24 ? gemm_launch<SPA_BF16, true>(a, st) : gemm_launch<SPA_BF16, false>(a, st);
+  if (a.sparse24) {
+    const int tiles = ((a.t + 255) / 256) * ((a.n_out + 255) / 256);
+    if (dtype == SPA_F16) hipLaunchKernelGGL(k_gemm24<SPA_F16>, dim3(tiles), dim3(512), 0, st, a);
+    else hipLaunchKernelGGL(k_gemm24<SPA_BF16>, dim3(tiles), dim3(512), 0, st, a);
+  } else {
+    const int tiles = ((a.t + 255) / 256) * ((a.n_out + 127) / 128);
+    if (dtype == SPA_F16) hipLaunchKernelGGL(k_gemm_dense<SPA_F16>, dim3(tiles), dim3(512), 0, st, a);
+    else hipLaunchKernelGGL(k_gemm_dense<SPA_BF16>, dim3(tiles), dim3(512), 0, st, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace spa

@@ -135,17 +135,31 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
             if ((keepbits[b] >> j) & 1u) { sm += v; smm += v * v; }
           }
       }
-      if (a.pack & kPackMeta24) {
-        // 2:4: per block the nibble (lo | hi << 2); four blocks per uint16.
-        uint32_t meta = 0;
+      if (a.pack & kPackTiled24) {
+        // 2:4: the segment's 16 channels are 4 blocks -> 8 kept values (16 bytes) and
+        // one 16-bit word of positions, stored at step seg / 4, slot seg % 4
+        if constexpr (M == 4 && DT != SPA_F32) {
+          uint32_t meta = 0;
+          uint32_t wds[4];
 #pragma unroll
-        for (int b = 0; b < BPS; ++b) {
-          const uint32_t kb = keepbits[b];
-          const uint32_t lo = __builtin_ctz(kb);
-          const uint32_t hi = 31 - __builtin_clz(kb);
-          meta |= (lo | (hi << 2)) << (4 * b);
+          for (int b = 0; b < BPS; ++b) {
+            const uint32_t kb = keepbits[b];
+            const uint32_t lo = __builtin_ctz(kb);
+            const uint32_t hi = 31 - __builtin_clz(kb);
+            meta |= (lo | (hi << 2)) << (4 * b);
+            float vlo = xh[4 * b], vhi = xh[4 * b];
+#pragma unroll
+            for (int j = 1; j < 4; ++j) {
+              vlo = (int)lo == j ? xh[4 * b + j] : vlo;
+              vhi = (int)hi == j ? xh[4 * b + j] : vhi;
+            }
+            wds[b] = (uint32_t)from_f32<DT>(vlo) | ((uint32_t)from_f32<DT>(vhi) << 16);
+          }
+          const size_t rowpos = (size_t)(seg / 4) * a.t_pad + row;
+          reinterpret_cast<uint4*>(static_cast<T*>(a.tiled_vals) + rowpos * 32)[seg % 4] =
+              make_uint4(wds[0], wds[1], wds[2], wds[3]);
+          a.tiled_meta[rowpos * 4 + seg % 4] = (uint16_t)meta;
         }
-        a.meta[(size_t)row * (a.k / 16) + seg] = (uint16_t)meta;
       }
       if (a.pack & kPackDense) {
         T* d = static_cast<T*>(a.dense) + (size_t)row * a.k + (size_t)seg * SEG;

@@ -41,12 +41,16 @@ size_t prune_ws(int t, int k, const spa_prune_cfg* c) {
 struct PrefillPlan {
   size_t vals, meta, eta, nu, colnorm, bytes;
 };
+// Rows of the 2:4 tiled operand are padded to the GEMM's 256-token tile.
+int tiled_rows(int t) { return (t + 255) / 256 * 256; }
+
 PrefillPlan prefill_plan(int t, int k, int dtype, const spa_prune_cfg* c) {
   PrefillPlan p{};
   const bool s24 = c->n == 2 && c->m == 4;
+  const size_t rows = s24 ? (size_t)tiled_rows(t) : (size_t)t;
   size_t off = 0;
-  p.vals = off; off += round256((size_t)t * (s24 ? k / 2 : k) * dtype_bytes(dtype));
-  p.meta = off; off += s24 ? round256((size_t)t * (k / 16) * 2) : 0;
+  p.vals = off; off += round256(rows * (s24 ? k / 2 : k) * dtype_bytes(dtype));
+  p.meta = off; off += s24 ? round256(rows * (k / 16) * 2) : 0;
   p.eta = off; off += round256((size_t)t * 4);
   p.nu = off; off += round256((size_t)t * 4);
   p.colnorm = off; off += c->score == SPA_SCORE_CLACT ? round256((size_t)k * 4) : 0;
@@ -213,9 +217,11 @@ spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, 
   a.eta_out = eta_ws;
   a.nu_out = (cfg->var_rescale || nu_out) ? nu_ptr : nullptr;
   if (s24) {
-    a.pack = spa::kPackVals | spa::kPackMeta24;
-    a.vals = base + pl.vals;
-    a.meta = reinterpret_cast<uint16_t*>(base + pl.meta);
+    a.pack = spa::kPackTiled24 | (idx_out ? spa::kPackVals : 0);
+    a.tiled_vals = base + pl.vals;
+    a.tiled_meta = reinterpret_cast<uint16_t*>(base + pl.meta);
+    a.t_pad = tiled_rows(t);
+    a.vals = nullptr;
     a.idx = idx_out;
   } else {
     a.pack = spa::kPackDense | (idx_out ? spa::kPackVals : 0);
@@ -230,6 +236,7 @@ spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, 
   g.row_sum = w->row_sum;
   g.a_vals = base + pl.vals;
   g.a_meta = s24 ? reinterpret_cast<const uint16_t*>(base + pl.meta) : nullptr;
+  g.t_pad = s24 ? tiled_rows(t) : t;
   g.eta = cfg->shift != SPA_SHIFT_NONE ? eta_ws : nullptr;
   g.nu = cfg->var_rescale ? nu_ptr : nullptr;
   g.y = y;

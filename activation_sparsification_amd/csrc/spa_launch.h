@@ -13,7 +13,9 @@ hipError_t launch_prepare(int dtype, const void* w, int n_out, int k, float alph
 // ---- pruning pass (one workgroup per token row) ----
 enum PackFormat : int {
   kPackVals = 1,    // vals[t][k*n/m] (dtype) + optional idx[t][k*n/m] (uint8)
-  kPackMeta24 = 2,  // 2:4 only: meta16[t][k/16], one nibble (lo | hi << 2) per block
+  kPackTiled24 = 2, // 2:4 only, the prefill GEMM's layout: per 64-channel step kt, rows padded to
+                    // t_pad: vals[kt][t_pad][32] (dtype) and meta[kt][t_pad][4] (uint16, one
+                    // nibble lo | hi << 2 per block, four blocks per word)
   kPackDense = 4,   // masked dense rows xm[t][k] (dtype), zeros at pruned channels
 };
 
@@ -28,7 +30,9 @@ struct PruneArgs {
   int pack;                  // PackFormat bits
   void* vals;                // kPackVals
   uint8_t* idx;              // kPackVals, may be NULL
-  uint16_t* meta;            // kPackMeta24
+  void* tiled_vals;          // kPackTiled24
+  uint16_t* tiled_meta;      // kPackTiled24
+  int t_pad;                 // kPackTiled24: rows per step (t rounded up to the GEMM tile)
   void* dense;               // kPackDense
   float* eta_out;            // may be NULL
   float* nu_out;             // may be NULL
@@ -70,8 +74,9 @@ hipError_t launch_decode(int dtype, DecodeArgs& a, hipStream_t st);
 struct PrefillArgs {
   const void* w;             // [n_out][k]
   const float* row_sum;
-  const void* a_vals;        // 2:4: packed [t][k/2]; other n:m: masked dense [t][k]
-  const uint16_t* a_meta;    // 2:4 only
+  const void* a_vals;        // 2:4: tiled packed values (kPackTiled24); other n:m: masked dense [t][k]
+  const uint16_t* a_meta;    // 2:4 only: tiled position words
+  int t_pad;                 // 2:4 only: rows per step of the tiled layout
   const float* eta;          // [t] or NULL
   const float* nu;           // [t] or NULL
   void* y;

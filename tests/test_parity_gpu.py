@@ -171,6 +171,13 @@ PREFILL_CASES.append(wl.SPECS["prefill"].with_(name="pre_weight_var", t=300, k=5
 PREFILL_CASES.append(wl.SPECS["prefill"].with_(name="pre_given", t=40, k=256, n_out=520, shift="given"))
 PREFILL_CASES.append(wl.SPECS["batched"].with_(name="pre_clact", t=96, k=512, n_out=264, n=2, m=4))
 PREFILL_CASES.append(wl.SPECS["prefill"].with_(name="pre_one_row", t=1, k=128, n_out=8))
+# k-step counts 1, 3 and 12 (the GEMMs run three k steps per loop turn with a
+# peeled tail), and several ragged tiles in both directions
+for n, m in [(2, 4), (4, 8)]:
+    PREFILL_CASES.append(wl.SPECS["prefill"].with_(name=f"pre_k64_{n}_{m}", t=5, k=64, n_out=40, n=n, m=m))
+    PREFILL_CASES.append(wl.SPECS["prefill"].with_(name=f"pre_k192_{n}_{m}", t=260, k=192, n_out=300, n=n, m=m))
+    PREFILL_CASES.append(wl.SPECS["prefill"].with_(name=f"pre_tiles_{n}_{m}", t=600, k=768, n_out=1100, n=n, m=m,
+                                                   n_outliers=8))
 
 
 @pytest.mark.parametrize("spec", PREFILL_CASES, ids=[s.name for s in PREFILL_CASES])
