@@ -486,268 +486,294 @@ __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(D
 }
 
 // ---------------------------------------------------------------------------
-// Mask kernel (t > 4): 64 channels x all tokens per workgroup.
-// tokmask[c]: bit i set when token i keeps channel c.  coef[c][i]: kept
-// x_hat rounded to the storage dtype (0 when pruned), tokens padded to 32.
+// Pruning pass of the matrix-core decode (t > 4): few token rows, so the
+// work is cut by channels instead of rows.  A workgroup owns 8 m-blocks of
+// channels for every token of the call: it stages x_hat = x - eta for those
+// channels in LDS, forms the channel factors there (the CLACT column energy
+// needs every token of a channel, which this workgroup holds), then one
+// thread per (token, block) scores, selects the top n with the selection
+// network and writes the masked row segment, the kept positions and its
+// four variance sums.  The sums of the eight blocks are added in block order
+// and stored per (workgroup, token); the GEMM folds them into nu.
 // ---------------------------------------------------------------------------
 template <int DT, int M>
-__global__ void __launch_bounds__(256) k_decode_mask(DecodeArgs a) {
+__global__ void __launch_bounds__(256) k_prune_cols(DecodeArgs a) {
   using T = typename Dt<DT>::T;
-  constexpr int KM = 64;
-  __shared__ float s_sc[kMaxTok][KM];
-  __shared__ float s_xh[kMaxTok][KM];
-  __shared__ uint8_t s_keep[kMaxTok][KM];
-  __shared__ uint32_t s_tm[KM];
-  __shared__ float s_f[KM];
-  __shared__ double s_red[4];
-  const int T_ = a.t;
-  const int kb = blockIdx.x * KM;
-  const int KV = min(KM, a.k - kb);          // a whole number of m-blocks
+  constexpr int NB = 8, CH = NB * M;
+  __shared__ float s_x[kMaxTok][CH + 1];
+  __shared__ float s_f[CH];
+  __shared__ double s_st[kMaxTok][NB][4];
+  const int T_ = a.t, K = a.k;
+  const int c0 = blockIdx.x * CH;
   const T* x = static_cast<const T*>(a.x);
-  const float* eta = a.eta;
-
-  if ((int)threadIdx.x < KM) {
-    const int c = threadIdx.x;
-    s_tm[c] = 0u;
+  for (int e = threadIdx.x; e < T_ * CH; e += 256) {
+    const int i = e / CH, c = e % CH, ch = c0 + c;
+    float xh = 0.f;
+    if (ch < K) xh = to_f32<DT>(x[(size_t)i * K + ch]) - (a.eta ? a.eta[i] : 0.f);
+    s_x[i][c] = xh;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < CH; c += 256) {
     float f = 1.f;
-    if (c < KV) {
+    if (c0 + c < K) {
       if (a.score == SPA_SCORE_WEIGHT) {
-        f = a.chan_scale[kb + c];
+        f = a.chan_scale[c0 + c];
       } else if (a.score == SPA_SCORE_CLACT) {
         float acc = 0.f;
-        for (int p = 0; p < T_; ++p)
-          acc = clact_accumulate(acc, to_f32<DT>(x[(size_t)p * a.k + kb + c]) - (eta ? eta[p] : 0.f));
+        for (int i = 0; i < T_; ++i) acc = clact_accumulate(acc, s_x[i][c]);
         f = sqrt_rn(acc);
       }
     }
     s_f[c] = f;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < T_ * KM; e += 256) {
-    const int i = e / KM, c = e % KM;
-    float xh = 0.f;
-    if (c < KV) xh = to_f32<DT>(x[(size_t)i * a.k + kb + c]) - (eta ? eta[i] : 0.f);
-    s_xh[i][c] = xh;
-    s_sc[i][c] = a.score == SPA_SCORE_MAGNITUDE ? __builtin_fabsf(xh) : __builtin_fabsf(xh) * s_f[c];
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < T_ * KM; e += 256) {
-    const int i = e / KM, c = e % KM, j = c % M, base = c - j;
-    if (c >= KV) { s_keep[i][c] = 0; continue; }
-    const float me = s_sc[i][c];
-    int rank = 0;
+  const int i = threadIdx.x / NB, b = threadIdx.x % NB;
+  const int cb = c0 + b * M;
+  double st[4] = {0.0, 0.0, 0.0, 0.0};
+  if (i < T_ && cb < K) {
+    float xh[M];
+    uint32_t sc[M];
 #pragma unroll
-    for (int q = 0; q < M; ++q) rank += beats(s_sc[i][base + q], q, me, j) ? 1 : 0;
-    const bool keep = rank < a.n;
-    s_keep[i][c] = keep ? 1 : 0;
-    if (keep) atomicOr(&s_tm[c], 1u << i);
-  }
-  __syncthreads();
-  const int kept_row = a.k / M * a.n;
-  uint16_t* coef = a.coef;
-  for (int e = threadIdx.x; e < kMaxTok * KV; e += 256) {
-    const int c = e / kMaxTok, i = e % kMaxTok;
-    uint16_t v = 0;
-    if (i < T_ && s_keep[i][c]) v = (uint16_t)from_f32<DT>(s_xh[i][c]);
-    coef[(size_t)(kb + c) * kMaxTok + i] = v;
-    if (i < T_ && s_keep[i][c] && a.idx_out) {
-      const int j = c % M, base = c - j;
-      int before = 0;
-      for (int q = 0; q < j; ++q) before += s_keep[i][base + q];
-      a.idx_out[(size_t)i * kept_row + (size_t)(kb + base) / M * a.n + before] = (uint8_t)j;
+    for (int j = 0; j < M; ++j) {
+      xh[j] = s_x[i][b * M + j];
+      const float ax = __builtin_fabsf(xh[j]);
+      sc[j] = __float_as_uint(a.score == SPA_SCORE_MAGNITUDE ? ax : ax * s_f[b * M + j]);
+    }
+    const uint32_t keep = topn_keep_bits<M>(sc, a.n);
+    // masked row segment, 8 values per 16-byte store
+    T* dst = static_cast<T*>(a.dense) + (size_t)i * K + cb;
+#pragma unroll
+    for (int q = 0; q < M / 8; ++q) {
+      uint32_t wds[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int j0 = 8 * q + 2 * h;
+        const uint32_t lo = ((keep >> j0) & 1u) ? (uint32_t)from_f32<DT>(xh[j0]) : 0u;
+        const uint32_t hi = ((keep >> (j0 + 1)) & 1u) ? (uint32_t)from_f32<DT>(xh[j0 + 1]) : 0u;
+        wds[h] = lo | (hi << 16);
+      }
+      reinterpret_cast<uint4*>(dst)[q] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+    }
+    if constexpr (M == 4) {     // one 8-byte store per block of 4
+      uint32_t wds[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t lo = ((keep >> (2 * h)) & 1u) ? (uint32_t)from_f32<DT>(xh[2 * h]) : 0u;
+        const uint32_t hi = ((keep >> (2 * h + 1)) & 1u) ? (uint32_t)from_f32<DT>(xh[2 * h + 1]) : 0u;
+        wds[h] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint2*>(dst) = make_uint2(wds[0], wds[1]);
+    }
+    if (a.idx_out) {
+      uint8_t* id = a.idx_out + (size_t)i * (K / M * a.n) + (size_t)(cb / M) * a.n;
+      uint32_t kb = keep;
+      for (int q = 0; q < a.n; ++q) {
+        id[q] = (uint8_t)__builtin_ctz(kb);
+        kb &= kb - 1u;
+      }
+    }
+    if (a.var) {
+#pragma unroll
+      for (int j = 0; j < M; ++j) {
+        const double v = (double)xh[j];
+        st[0] += v;
+        st[1] += v * v;
+        if ((keep >> j) & 1u) { st[2] += v; st[3] += v * v; }
+      }
     }
   }
-  if ((int)threadIdx.x < KV) a.tokmask[kb + threadIdx.x] = s_tm[threadIdx.x];
   if (a.var) {
-    for (int i = 0; i < T_; ++i) {
-      double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
-      if ((int)threadIdx.x < KV) {
-        const int c = threadIdx.x;
-        const double v = (double)s_xh[i][c];
-        v0 = v; v1 = v * v;
-        if (s_keep[i][c]) { v2 = v; v3 = v * v; }
-      }
-      const double t0 = block_sum(v0, s_red);
-      const double t1 = block_sum(v1, s_red);
-      const double t2 = block_sum(v2, s_red);
-      const double t3 = block_sum(v3, s_red);
-      if (threadIdx.x == 0) {
-        double* st = a.stats + ((size_t)blockIdx.x * T_ + i) * 4;
-        st[0] = t0; st[1] = t1; st[2] = t2; st[3] = t3;
-      }
+    if (i < T_)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s_st[i][b][q] = st[q];
+    __syncthreads();
+    if ((int)threadIdx.x < T_) {
+      double tot[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int b2 = 0; b2 < NB; ++b2)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[q] += s_st[threadIdx.x][b2][q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a.stats[((size_t)blockIdx.x * T_ + threadIdx.x) * 4 + q] = tot[q];
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Stream kernel (t > 4): union rows x 128 columns per workgroup on MFMA.
+// Matrix-core decode (t > 4, 16-bit).  With several tokens the union of kept
+// channels covers nearly every row of the weight (each token keeps its own
+// n of every m), so the product runs as a skinny dense GEMM over the masked
+// rows xm[t][k] that the pruning pass writes (zeros at pruned channels):
+//   y[i][j] = nu_i * sum_k xm[i][k] w[j][k] + eta_i * s_j.
+// The weight is read row-major: the lane that owns output row j and lane
+// group g loads 32 contiguous bytes of w[j] per 64-channel step, and the lane
+// that owns token i loads the same 32 bytes' worth of xm[i]; the two 16-byte
+// halves are the operands of two mfma_f32_16x16x32 (window h uses channels
+// 64 s + 16 g + 8 h .. +7 of step s in lane group g, for both operands, so
+// the contraction is over every channel exactly once).
+//
+// Workgroup = 16 output rows, 8 waves; wave w takes steps w, w+8, ...; the
+// eight partial 16 x t tiles are added in wave order in LDS (no split across
+// workgroups, no atomics), then the epilogue writes y.
 // ---------------------------------------------------------------------------
-template <int DT, int MT>
-__global__ void __launch_bounds__(256) k_decode_stream(DecodeArgs a) {
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
+  if constexpr (DT == SPA_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+}
+
+// 16 bytes at p when ok, else zeros (a load under the lane mask, never from a select).
+__device__ __forceinline__ uint4 load16_if(const void* p, bool ok) {
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (ok) v = *reinterpret_cast<const uint4*>(p);
+  return v;
+}
+
+// Fragment lane d = m + 16 g (row m, lane group g) takes the 16 bytes that
+// lane 4 m + g loaded: the loads run four lanes per row, so each row's 128-byte
+// line is one cache access instead of four.
+__device__ __forceinline__ uint4 to_fragment(const uint4& v, int src_addr) {
+  return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src_addr, (int)v.x),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(src_addr, (int)v.y),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(src_addr, (int)v.z),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(src_addr, (int)v.w));
+}
+
+template <int DT, int TT>
+__global__ void __launch_bounds__(1024) k_decode_mm(DecodeArgs a) {
   using T = typename Dt<DT>::T;
-  constexpr int C = 128;        // columns per workgroup: 4 waves x 2 n-tiles of 16
-  constexpr int NT = 2;
-  constexpr int KC = 32;        // union rows per MFMA step
-  constexpr int WROW = C + 8;   // padded LDS row (halves)
-  __shared__ uint16_t s_w[2][KC][WROW];
-  __shared__ uint16_t s_a[2][KC][kMaxTok + 2];
-  __shared__ int s_rows[256];
-  __shared__ int s_cnt[4];
-  __shared__ float s_eta[kMaxTok];
+  constexpr int RG = 4, KG = 4, U = 2, RN = 16 * RG;   // 16 waves: 4 row groups x 4 k groups
+  __shared__ float s_red[KG][RG][TT][16][17];
   __shared__ float s_nu[kMaxTok];
   __shared__ int s_flag;
-
-  const int T_ = a.t;
-  const int tile = blockIdx.x % a.tiles;
-  const int split = blockIdx.x / a.tiles;
-  const int kb = split * a.k_len;
-  const int kend = min(a.k, kb + a.k_len);
-  const int c0 = tile * C;
+  const int T_ = a.t, K = a.k, N = a.n_out;
+  const int tile = blockIdx.x % a.tiles, split = blockIdx.x / a.tiles;
+  const int n0 = tile * RN;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
-  const T* wt = static_cast<const T*>(a.wt);
-  const uint16_t* coef = reinterpret_cast<const uint16_t*>(a.coef);
-
-  if ((int)threadIdx.x < T_) s_eta[threadIdx.x] = a.eta ? a.eta[threadIdx.x] : 0.f;
-
-  f32x4 acc[MT][NT];
+  const int rg = wv % RG, kg = wv / RG;
+  const int l16 = lane & 15, g = lane >> 4;
+  // loads: lane s reads row (or token) s / 4, channels 16 (s % 4) .. +15 of each step
+  const int lr = lane >> 2, lq = lane & 3;
+  const int src_addr = 4 * (4 * l16 + g);
+  const int row = min(n0 + 16 * rg + lr, N - 1);
+  const T* wrow = static_cast<const T*>(a.w) + (size_t)row * K + 16 * lq;
+  const T* xrow[TT];
+  bool tok_ok[TT];
 #pragma unroll
-  for (int p = 0; p < MT; ++p)
-#pragma unroll
-    for (int q = 0; q < NT; ++q) acc[p][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // W chunk: KC rows x C columns = 32 x 16 segments of 16 bytes -> 2 per thread.
-  // Coefficient chunk: KC rows x 64 bytes = 32 x 4 segments -> threads 0..127.
-  for (int cb = kb; cb < kend; cb += 256) {
-    // union rows of this 256-channel window
-    const int c = cb + threadIdx.x;
-    const bool f = c < kend && a.tokmask[c] != 0u;
-    int U;
-    const int pos = block_exclusive_count(f, s_cnt, &U);
-    if (f) s_rows[pos] = c;
-    __syncthreads();
-    const int nchunk = (U + KC - 1) / KC;
-    uint4 wreg[2], areg;
-    auto load_chunk = [&](int ch) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int sidx = threadIdx.x + 256 * h;
-        const int r = sidx >> 4, sg = sidx & 15;
-        const int u = ch * KC + r;
-        const int colg = c0 + sg * 8;
-        if (u < U && colg < a.n_out)
-          wreg[h] = *reinterpret_cast<const uint4*>(wt + (size_t)s_rows[u] * a.n_out + colg);
-        else
-          wreg[h] = make_uint4(0u, 0u, 0u, 0u);
-      }
-      if (threadIdx.x < 128) {
-        const int r = threadIdx.x >> 2, sg = threadIdx.x & 3;
-        const int u = ch * KC + r;
-        if (u < U)
-          areg = *reinterpret_cast<const uint4*>(coef + (size_t)s_rows[u] * kMaxTok + sg * 8);
-        else
-          areg = make_uint4(0u, 0u, 0u, 0u);
-      }
-    };
-    auto store_chunk = [&](int buf) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int sidx = threadIdx.x + 256 * h;
-        const int r = sidx >> 4, sg = sidx & 15;
-        uint32_t* d = reinterpret_cast<uint32_t*>(&s_w[buf][r][sg * 8]);
-        d[0] = wreg[h].x; d[1] = wreg[h].y; d[2] = wreg[h].z; d[3] = wreg[h].w;
-      }
-      if (threadIdx.x < 128) {
-        const int r = threadIdx.x >> 2, sg = threadIdx.x & 3;
-        uint16_t* d = &s_a[buf][r][sg * 8];
-        const uint32_t wds[4] = {areg.x, areg.y, areg.z, areg.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { d[2 * e] = (uint16_t)(wds[e] & 0xFFFFu); d[2 * e + 1] = (uint16_t)(wds[e] >> 16); }
-      }
-    };
-    if (nchunk > 0) {
-      load_chunk(0);
-      store_chunk(0);
-    }
-    __syncthreads();
-    for (int ch = 0; ch < nchunk; ++ch) {
-      const int buf = ch & 1;
-      if (ch + 1 < nchunk) load_chunk(ch + 1);
-      // fragments from LDS
-#pragma unroll
-      for (int q = 0; q < NT; ++q) {
-        const int ncol = wv * (NT * 16) + q * 16 + l16;
-        uint16_t bh[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bh[j] = s_w[buf][8 * g + j][ncol];
-#pragma unroll
-        for (int p = 0; p < MT; ++p) {
-          uint16_t ah[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) ah[j] = s_a[buf][8 * g + j][16 * p + l16];
-          if constexpr (DT == SPA_F16) {
-            f16x8 av, bv;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) { av[j] = __builtin_bit_cast(_Float16, ah[j]); bv[j] = __builtin_bit_cast(_Float16, bh[j]); }
-            acc[p][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[p][q], 0, 0, 0);
-          } else {
-            bf16x8 av, bv;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) { av[j] = __builtin_bit_cast(__bf16, ah[j]); bv[j] = __builtin_bit_cast(__bf16, bh[j]); }
-            acc[p][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[p][q], 0, 0, 0);
-          }
-        }
-      }
-      if (ch + 1 < nchunk) store_chunk(buf ^ 1);
-      __syncthreads();
-    }
+  for (int tt = 0; tt < TT; ++tt) {
+    const int tok = 16 * tt + lr;
+    tok_ok[tt] = tok < T_;
+    xrow[tt] = static_cast<const T*>(a.dense) + (size_t)min(tok, T_ - 1) * K + 16 * lq;
   }
+  f32x4 acc[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // partial: D lane layout -> token 16p + 4g + r, column l16 of the n-tile
+  // this workgroup's 64-channel steps; the k groups interleave within them.
+  // Rows of w lie k*2 bytes apart, so workgroups walking k in step would all
+  // hit the same few memory channels at once; each tile therefore starts its
+  // walk at a different step (a rotation of the same set of steps).
+  const int nsteps = (K + 63) / 64;
+  const int sps = a.k_len / 64;
+  const int s_beg = split * sps, s_end = min(nsteps, s_beg + sps);
+  const int span = s_end - s_beg;
+  const int rot = span > 0 ? (int)(((unsigned)tile * 37u) % (unsigned)span) : 0;
+  // two register batches of U steps: the next batch is in flight while the
+  // current one is permuted and multiplied
+  uint4 wa[2][U][2], xb[2][U][TT][2];
+#define SPA_MM_LOAD(B, L0)                                                        \
+  do {                                                                            \
+    _Pragma("unroll") for (int u = 0; u < U; ++u) {                               \
+      const int ls = (L0) + KG * u;                                               \
+      int st = ls + rot;                                                          \
+      st = s_beg + (st >= span ? st - span : st);                                 \
+      const int off = st * 64;                                                    \
+      const bool ok = ls < span && off + 16 * lq < K;                             \
+      wa[B][u][0] = load16_if(wrow + off, ok);                                    \
+      wa[B][u][1] = load16_if(wrow + off + 8, ok);                                \
+      _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) {                         \
+        xb[B][u][tt][0] = load16_if(xrow[tt] + off, ok && tok_ok[tt]);            \
+        xb[B][u][tt][1] = load16_if(xrow[tt] + off + 8, ok && tok_ok[tt]);        \
+      }                                                                           \
+    }                                                                             \
+  } while (0)
+#define SPA_MM_COMPUTE(B)                                                                    \
+  do {                                                                                       \
+    _Pragma("unroll") for (int u = 0; u < U; ++u) {                                          \
+      const uint4 w0 = to_fragment(wa[B][u][0], src_addr), w1 = to_fragment(wa[B][u][1], src_addr); \
+      _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) {                                    \
+        acc[tt] = mfma16<DT>(w0, to_fragment(xb[B][u][tt][0], src_addr), acc[tt]);           \
+        acc[tt] = mfma16<DT>(w1, to_fragment(xb[B][u][tt][1], src_addr), acc[tt]);           \
+      }                                                                                      \
+    }                                                                                        \
+  } while (0)
+  constexpr int STRIDE = KG * U;
+  SPA_MM_LOAD(0, kg);
+  for (int l0 = kg; l0 < span; l0 += 2 * STRIDE) {
+    SPA_MM_LOAD(1, l0 + STRIDE);
+    SPA_MM_COMPUTE(0);
+    if (l0 + STRIDE >= span) break;
+    SPA_MM_LOAD(0, l0 + 2 * STRIDE);
+    SPA_MM_COMPUTE(1);
+  }
+#undef SPA_MM_LOAD
+#undef SPA_MM_COMPUTE
+  // D register r of lane (l16, g): output row 16 rg + 4g + r, token 16 tt + l16
 #pragma unroll
-  for (int p = 0; p < MT; ++p)
+  for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-    for (int q = 0; q < NT; ++q) {
-      const int col = c0 + wv * (NT * 16) + q * 16 + l16;
+    for (int r = 0; r < 4; ++r) s_red[kg][rg][tt][4 * g + r][l16] = acc[tt][r];
+  __syncthreads();
+  // this workgroup's sum over its k groups, in k-group order
+  auto wg_sum = [&](int j, int tok) {
+    float v = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = 16 * p + 4 * g + r;
-        if (tok < T_ && col < a.n_out)
-          coherent_store(&a.partial[((size_t)split * T_ + tok) * a.n_out + col], acc[p][q][r]);
-      }
+    for (int q = 0; q < KG; ++q) v += s_red[q][j / 16][tok / 16][j % 16][tok % 16];
+    return v;
+  };
+  const int rows = min(RN, N - n0);
+  if (a.splits > 1) {
+    for (int e = threadIdx.x; e < rows * T_; e += 1024) {
+      const int tok = e / rows, j = e % rows;
+      coherent_store(&a.partial[((size_t)split * T_ + tok) * N + n0 + j], wg_sum(j, tok));
     }
-  if (!arrive_last(&a.counters[tile], a.splits, &s_flag)) return;
-
-  // last workgroup of the tile: nu from the mask kernel's per-group sums, then y
-  if ((int)threadIdx.x < T_) {
+    if (!arrive_last(&a.counters[tile], a.splits, &s_flag)) return;
+  }
+  // nu of token i from the pruning pass's per-chunk sums: lane l adds chunks
+  // l, l+64, ..., then a fixed butterfly (the same result in every workgroup)
+  for (int i = wv; i < T_; i += 16) {
     float nu = 1.f;
     if (a.var) {
-      double st[4] = {0.0, 0.0, 0.0, 0.0};
-      for (int g2 = 0; g2 < a.mask_groups; ++g2)
-        for (int q = 0; q < 4; ++q) st[q] += a.stats[((size_t)g2 * T_ + threadIdx.x) * 4 + q];
-      nu = nu_from_stats(st, a.k);
+      double sum4[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int c = lane; c < a.chunks; c += 64)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum4[q] += a.stats[((size_t)c * T_ + i) * 4 + q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sum4[q] = wave_sum(sum4[q]);
+      nu = nu_from_stats(sum4, K);
     }
-    s_nu[threadIdx.x] = nu;
-    if (tile == 0 && a.nu_out) a.nu_out[threadIdx.x] = nu;
+    if (lane == 0) {
+      s_nu[i] = nu;
+      if (tile == 0 && a.nu_out) a.nu_out[i] = nu;
+    }
   }
   __syncthreads();
   T* y = static_cast<T*>(a.y);
-  const int cw = min(C, a.n_out - c0);
-  for (int pidx = threadIdx.x; pidx < T_ * cw; pidx += 256) {
-    const int tok = pidx / cw, col = c0 + pidx % cw;
-    float v = 0.f;
-    for (int s0 = 0; s0 < a.splits; s0 += 16) {
-      float part[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-        part[q] = s0 + q < a.splits ? coherent_load(&a.partial[((size_t)(s0 + q) * T_ + tok) * a.n_out + col]) : 0.f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (s0 + q < a.splits) v += part[q];
+  for (int e = threadIdx.x; e < rows * T_; e += 1024) {
+    const int tok = e / rows, j = e % rows, col = n0 + j;
+    float v;
+    if (a.splits > 1) {
+      v = 0.f;
+      for (int s2 = 0; s2 < a.splits; ++s2) v += coherent_load(&a.partial[((size_t)s2 * T_ + tok) * N + col]);
+    } else {
+      v = wg_sum(j, tok);
     }
     float out = s_nu[tok] * v;
-    if (a.shift != SPA_SHIFT_NONE) out += s_eta[tok] * a.row_sum[col];
-    y[(size_t)tok * a.n_out + col] = from_f32<DT>(out);
+    if (a.shift != SPA_SHIFT_NONE) out += a.eta[tok] * a.row_sum[col];
+    y[(size_t)tok * N + col] = from_f32<DT>(out);
   }
 }
 
@@ -797,7 +823,6 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
     p.splits = (k + p.k_len - 1) / p.k_len;
     p.list_cap = bl * per_block;
     p.chunk_blocks = bl;
-    p.mask_groups = 0;
     const size_t o_part = carve((size_t)p.splits * t * n_out * 4);
     const size_t o_stats = carve(var ? (size_t)p.tiles * p.splits * t * 4 * 8 : 0);
     const size_t o_cnt = carve((size_t)p.tiles * 4);
@@ -805,23 +830,24 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
     p.partial = (float*)o_part; p.stats = (double*)o_stats; p.counters = (unsigned*)o_cnt;
     p.eta_ws = (float*)o_eta;
   } else {
-    p.col_tile = 128;
-    p.tiles = (n_out + 127) / 128;
-    int target = (512 + p.tiles - 1) / p.tiles;
-    const int cap = (int)(0.025 * k / t);
-    if (target > cap) target = cap > 1 ? cap : 1;
-    const int bl = pick_splits(k, 64, target, 1 << 30);
-    p.k_len = bl * 64;
-    p.splits = (k + p.k_len - 1) / p.k_len;
-    p.mask_groups = (k + 63) / 64;
-    const size_t o_part = carve((size_t)p.splits * t * n_out * 4);
-    const size_t o_stats = carve(var ? (size_t)p.mask_groups * t * 4 * 8 : 0);
-    const size_t o_cnt = carve((size_t)p.tiles * 4);
-    const size_t o_tm = carve((size_t)k * 4);
-    const size_t o_coef = carve((size_t)k * kMaxTok * 2);
+    // matrix-core path: prune once into masked rows (channel chunks of 8
+    // m-blocks), then one pass over w by 64-row tiles, split over k until
+    // about 256 workgroups run
+    p.tiles = (n_out + 63) / 64;
+    const int nsteps = (k + 63) / 64;
+    int sp = (256 + p.tiles - 1) / p.tiles;
+    if (sp > nsteps) sp = nsteps;
+    const int sps = (nsteps + sp - 1) / sp;
+    p.k_len = sps * 64;
+    p.splits = (nsteps + sps - 1) / sps;
+    p.chunks = (k + 8 * m - 1) / (8 * m);
+    const size_t o_dense = carve((size_t)t * k * 2);
+    const size_t o_stats = carve(var ? (size_t)p.chunks * t * 4 * 8 : 0);
     const size_t o_eta = carve((size_t)t * 4);
-    p.partial = (float*)o_part; p.stats = (double*)o_stats; p.counters = (unsigned*)o_cnt;
-    p.tokmask = (uint32_t*)o_tm; p.coef = (uint16_t*)o_coef; p.eta_ws = (float*)o_eta;
+    const size_t o_part = carve(p.splits > 1 ? (size_t)p.splits * t * n_out * 4 : 0);
+    const size_t o_cnt = carve((size_t)p.tiles * 4);
+    p.dense = (void*)o_dense; p.stats = (double*)o_stats; p.eta_ws = (float*)o_eta;
+    p.partial = (float*)o_part; p.counters = (unsigned*)o_cnt;
   }
   if (plan) *plan = p;
   return bytes;
@@ -847,7 +873,10 @@ static hipError_t fused_tok(DecodeArgs& a, hipStream_t st) {
 template <int DT>
 static hipError_t decode_dt(DecodeArgs& a, hipStream_t st) {
   const bool fused = a.t <= 4 || DT == SPA_F32;
-  if (a.shift == SPA_SHIFT_TOKEN_MEAN && (!fused || (size_t)a.t * a.k > 65536)) {
+  // the token mean ahead of the main kernel: for long fused rows, and for CLACT
+  // (its column norms are taken over the shifted values)
+  const bool mean_first = fused ? (size_t)a.t * a.k > 65536 : true;
+  if (a.shift == SPA_SHIFT_TOKEN_MEAN && mean_first) {
     if (hipError_t e = launch_token_mean(DT, a.x, a.t, a.k, a.eta_ws, st)) return e;
     a.eta = a.eta_ws;
   }
@@ -860,18 +889,20 @@ static hipError_t decode_dt(DecodeArgs& a, hipStream_t st) {
     }
   }
   if constexpr (DT != SPA_F32) {
-    const dim3 mg(a.mask_groups);
+    // prune every token once (score, top-n, masked rows, positions, variance sums) ...
+    const dim3 pg(a.chunks);
     switch (a.m) {
-      case 4: hipLaunchKernelGGL((k_decode_mask<DT, 4>), mg, dim3(256), 0, st, a); break;
-      case 8: hipLaunchKernelGGL((k_decode_mask<DT, 8>), mg, dim3(256), 0, st, a); break;
-      case 16: hipLaunchKernelGGL((k_decode_mask<DT, 16>), mg, dim3(256), 0, st, a); break;
-      default: hipLaunchKernelGGL((k_decode_mask<DT, 32>), mg, dim3(256), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((k_prune_cols<DT, 4>), pg, dim3(256), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((k_prune_cols<DT, 8>), pg, dim3(256), 0, st, a); break;
+      case 16: hipLaunchKernelGGL((k_prune_cols<DT, 16>), pg, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((k_prune_cols<DT, 32>), pg, dim3(256), 0, st, a); break;
     }
     if (hipError_t e = hipGetLastError()) return e;
+    // ... then one pass over the row-major weight on the matrix cores
     if (a.t <= 16)
-      hipLaunchKernelGGL((k_decode_stream<DT, 1>), dim3(a.tiles * a.splits), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_decode_mm<DT, 1>), dim3(a.tiles * a.splits), dim3(1024), 0, st, a);
     else
-      hipLaunchKernelGGL((k_decode_stream<DT, 2>), dim3(a.tiles * a.splits), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_decode_mm<DT, 2>), dim3(a.tiles * a.splits), dim3(1024), 0, st, a);
   }
   return hipGetLastError();
 }

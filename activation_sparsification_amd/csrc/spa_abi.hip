@@ -69,8 +69,14 @@ spa_status check_linear(const void* x, int32_t t, const spa_weight* w, const spa
   if (cfg->shift == SPA_SHIFT_GIVEN && !eta_in) return SPA_ERR_INVALID;
   if (cfg->shift != SPA_SHIFT_NONE && !w->row_sum) return SPA_ERR_INVALID;
   if (decode) {
-    if (!w->wt || !aligned16(w->wt)) return SPA_ERR_INVALID;
-    if (w->n_out % (16 / dtype_bytes(w->dtype))) return SPA_ERR_INVALID;
+    // 1..4 tokens (and float32) stream the channel-major copy; more tokens of a
+    // 16-bit type run on the matrix cores over the row-major weight
+    if (t <= 4 || w->dtype == SPA_F32) {
+      if (!w->wt || !aligned16(w->wt)) return SPA_ERR_INVALID;
+      if (w->n_out % (16 / dtype_bytes(w->dtype))) return SPA_ERR_INVALID;
+    } else {
+      if (!w->w || !aligned16(w->w)) return SPA_ERR_INVALID;
+    }
   } else {
     if (!w->w || !aligned16(w->w)) return SPA_ERR_INVALID;
     if (w->k % 64) return SPA_ERR_INVALID;
@@ -170,10 +176,10 @@ spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, c
   fix(a.stats);
   fix(a.counters);
   fix(a.eta_ws);
-  if (a.tokmask) fix(a.tokmask);
-  if (a.coef) fix(a.coef);
+  if (t > 4 && w->dtype != SPA_F32) fix(a.dense);   // matrix-core path (its offset is 0)
   a.x = x;
   a.wt = w->wt;
+  a.w = w->w;
   a.chan_scale = w->chan_scale;
   a.row_sum = w->row_sum;
   a.eta = cfg->shift == SPA_SHIFT_GIVEN ? eta_in : nullptr;

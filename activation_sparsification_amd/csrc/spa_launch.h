@@ -44,7 +44,8 @@ hipError_t launch_colnorm(int dtype, const void* x, const float* eta, int t, int
 // ---- decode ----
 struct DecodeArgs {
   const void* x;
-  const void* wt;
+  const void* wt;            // [k][n_out] channel-major (t <= 4, and float32)
+  const void* w;             // [n_out][k] row-major (16-bit, t > 4)
   const float* chan_scale;
   const float* row_sum;
   const float* eta;          // precomputed or caller-given shift, or NULL
@@ -56,13 +57,13 @@ struct DecodeArgs {
   int shift;                 // SPA_SHIFT_*
   int var;
   // workspace carve-up
-  float* partial;            // [splits][t][n_out]
-  double* stats;             // [tiles][splits][t][4] or [mask groups][t][4]
-  unsigned* counters;        // [tiles]
-  uint32_t* tokmask;         // [k]            (mask-then-stream path)
-  uint16_t* coef;            // [k][32] dtype  (mask-then-stream path)
+  float* partial;            // fused: [splits][t][n_out]
+  double* stats;             // fused: [tiles][splits][t][4]; matrix-core: [chunks][t][4]
+  unsigned* counters;        // fused: [tiles]
+  void* dense;               // matrix-core path: masked rows [t][k] (dtype)
   float* eta_ws;             // [t]
-  int tiles, splits, k_len, col_tile, mask_groups;
+  int tiles, splits, k_len, col_tile;
+  int chunks;                // matrix-core path: channel chunks of the pruning pass
   int list_cap;              // fused path: LDS list entries per wave
   int chunk_blocks;          // fused path: m-blocks a wave selects and streams at a time
 };

@@ -106,7 +106,10 @@ class Workload:
         wd = w.to(dev)
         self.pw = spa.prepare_weight(wd, spec.alpha, want_wt=self.decode)
         self.cfg = spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, spec.var_rescale)
-        big = self.pw.wt if self.decode else self.pw.w
+        # decode streams the channel-major copy for 1..4 tokens (and float32); more tokens
+        # of a 16-bit type read the row-major weight on the matrix cores
+        self.reads_wt = self.decode and (spec.t <= 4 or spec.dtype == "f32")
+        big = self.pw.wt if self.reads_wt else self.pw.w
         wbytes = big.numel() * big.element_size()
         self.copies = max(3, math.ceil(3 * MALL_BYTES / wbytes))
         mats = [big] + [big.clone() for _ in range(self.copies - 1)]
@@ -114,7 +117,7 @@ class Workload:
         entry = 1 if self.decode else 2
         self.ws = spa.workspace(entry, spec.t, spec.k, spec.n_out, x.dtype, self.cfg, dev)
         fn = "sparse_linear_decode" if self.decode else "sparse_linear_prefill"
-        if self.decode:
+        if self.reads_wt:
             self.calls = [spa.PreparedCall(fn, self.x, self.pw, self.cfg, self.y, self.ws, wt=m) for m in mats]
         else:
             self.calls = [spa.PreparedCall(fn, self.x, self.pw, self.cfg, self.y, self.ws, w=m) for m in mats]

@@ -120,21 +120,28 @@ spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const sp
                     float* eta_out, float* nu_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * sparse_linear_decode -- the fused decode step, 1 <= t <= 32 tokens:
- * prune in registers, then stream only the rows of wt that some token of
- * the call keeps (the memory-bound GEMV; guide s1.1 and s12.3: zero
- * activations need not move, and bandwidth comes first), accumulate in
- * float32, and apply
- * y = nu * acc + eta * row_sum.
+ * sparse_linear_decode -- the decode step, 1 <= t <= 32 tokens, float32
+ * accumulation, y = nu * acc + eta * row_sum.
+ *  - 1..4 tokens, and float32 (t <= 8): prune in registers, then stream
+ *    only the rows of wt that some token of the call keeps (the
+ *    memory-bound GEMV; guide s1.1 and s12.3: zero activations need not
+ *    move, and bandwidth comes first).
+ *  - 5..32 tokens of a 16-bit type: every token keeps its own n of each m
+ *    channels, so their union covers nearly all of wt; a pruning pass
+ *    writes the masked rows, and one pass over the row-major w on the
+ *    matrix cores forms the product (per-token masks differ within a
+ *    batch; WiSparse s5.1 separates small-batch from large-batch use).
  *  x        [device] [t][k]
- *  w        weight descriptor; wt required (n_out % 8 == 0 for 16-bit
- *           dtypes, % 4 for float32)
+ *  w        weight descriptor: wt required for 1..4 tokens and for float32
+ *           (n_out % 8 == 0 for 16-bit dtypes, % 4 for float32); w->w
+ *           required for 5..32 tokens of a 16-bit dtype
  *  eta_in   [device] [t], required iff cfg->shift == SPA_SHIFT_GIVEN
  *  y        [device] [t][n_out]
  *  idx_out  [device] [t][k*n/m] or NULL: the in-block positions the layer used
  *  nu_out   [device] [t] or NULL
  *  workspace [device] spa_workspace_bytes(SPA_ENTRY_DECODE, ...) bytes,
  *           zero-filled before its first use; each call leaves it reusable.
+ * Returns SPA_ERR_UNSUPPORTED for float32 with t > 8.
  */
 spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
                                 const float* eta_in, void* y, uint8_t* idx_out, float* nu_out,
