@@ -487,23 +487,33 @@ __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(D
 
 // ---------------------------------------------------------------------------
 // Pruning pass of the matrix-core decode (t > 4): few token rows, so the
-// work is cut by channels instead of rows.  A workgroup owns 8 m-blocks of
-// channels for every token of the call: it stages x_hat = x - eta for those
-// channels in LDS, forms the channel factors there (the CLACT column energy
-// needs every token of a channel, which this workgroup holds), then one
-// thread per (token, block) scores, selects the top n with the selection
-// network and writes the masked row segment, the kept positions and its
-// four variance sums.  The sums of the eight blocks are added in block order
-// and stored per (workgroup, token); the GEMM folds them into nu.
+// work is cut by channels instead of rows.  A workgroup owns 64 channels
+// (64/m blocks) for every token of the call: it stages x_hat = x - eta for
+// them in LDS, forms the channel factors there (the CLACT column energy needs
+// every token of a channel, which this workgroup holds), then one thread per
+// (token, block) scores, selects the top n with the selection network and
+// writes the masked values, the kept positions and its four variance sums.
+// The sums of the blocks are added in block order per (chunk, token); the
+// GEMM folds the chunks into nu.
+//
+// The masked activations are written in the GEMM's operand order ("fragment
+// order"): for 64-channel step s, token block tb (16 tokens) and window h,
+// one 1 KB run where lane d = m + 16 g holds channels 64 s + 16 g + 8 h .. +7
+// of token 16 tb + m.  Token lanes past t are never written or read.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ size_t frag_offset(int step, int tb, int ntb, int h, int lane) {
+  return ((((size_t)step * ntb + tb) * 2 + h) * 64 + lane) * 8;   // in 16-bit elements
+}
+
 template <int DT, int M>
 __global__ void __launch_bounds__(256) k_prune_cols(DecodeArgs a) {
   using T = typename Dt<DT>::T;
-  constexpr int NB = 8, CH = NB * M;
+  constexpr int CH = 64, NB = CH / M;
   __shared__ float s_x[kMaxTok][CH + 1];
   __shared__ float s_f[CH];
   __shared__ double s_st[kMaxTok][NB][4];
   const int T_ = a.t, K = a.k;
+  const int ntb = (T_ + 15) / 16;
   const int c0 = blockIdx.x * CH;
   const T* x = static_cast<const T*>(a.x);
   for (int e = threadIdx.x; e < T_ * CH; e += 256) {
@@ -513,7 +523,8 @@ __global__ void __launch_bounds__(256) k_prune_cols(DecodeArgs a) {
     s_x[i][c] = xh;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < CH; c += 256) {
+  if ((int)threadIdx.x < CH) {
+    const int c = threadIdx.x;
     float f = 1.f;
     if (c0 + c < K) {
       if (a.score == SPA_SCORE_WEIGHT) {
@@ -527,65 +538,70 @@ __global__ void __launch_bounds__(256) k_prune_cols(DecodeArgs a) {
     s_f[c] = f;
   }
   __syncthreads();
-  const int i = threadIdx.x / NB, b = threadIdx.x % NB;
-  const int cb = c0 + b * M;
-  double st[4] = {0.0, 0.0, 0.0, 0.0};
-  if (i < T_ && cb < K) {
-    float xh[M];
-    uint32_t sc[M];
-#pragma unroll
-    for (int j = 0; j < M; ++j) {
-      xh[j] = s_x[i][b * M + j];
-      const float ax = __builtin_fabsf(xh[j]);
-      sc[j] = __float_as_uint(a.score == SPA_SCORE_MAGNITUDE ? ax : ax * s_f[b * M + j]);
-    }
-    const uint32_t keep = topn_keep_bits<M>(sc, a.n);
-    // masked row segment, 8 values per 16-byte store
-    T* dst = static_cast<T*>(a.dense) + (size_t)i * K + cb;
-#pragma unroll
-    for (int q = 0; q < M / 8; ++q) {
-      uint32_t wds[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int j0 = 8 * q + 2 * h;
-        const uint32_t lo = ((keep >> j0) & 1u) ? (uint32_t)from_f32<DT>(xh[j0]) : 0u;
-        const uint32_t hi = ((keep >> (j0 + 1)) & 1u) ? (uint32_t)from_f32<DT>(xh[j0 + 1]) : 0u;
-        wds[h] = lo | (hi << 16);
-      }
-      reinterpret_cast<uint4*>(dst)[q] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
-    }
-    if constexpr (M == 4) {     // one 8-byte store per block of 4
-      uint32_t wds[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t lo = ((keep >> (2 * h)) & 1u) ? (uint32_t)from_f32<DT>(xh[2 * h]) : 0u;
-        const uint32_t hi = ((keep >> (2 * h + 1)) & 1u) ? (uint32_t)from_f32<DT>(xh[2 * h + 1]) : 0u;
-        wds[h] = lo | (hi << 16);
-      }
-      *reinterpret_cast<uint2*>(dst) = make_uint2(wds[0], wds[1]);
-    }
-    if (a.idx_out) {
-      uint8_t* id = a.idx_out + (size_t)i * (K / M * a.n) + (size_t)(cb / M) * a.n;
-      uint32_t kb = keep;
-      for (int q = 0; q < a.n; ++q) {
-        id[q] = (uint8_t)__builtin_ctz(kb);
-        kb &= kb - 1u;
-      }
-    }
-    if (a.var) {
+  const int step = c0 / 64;
+  for (int pr = threadIdx.x; pr < T_ * NB; pr += 256) {
+    const int i = pr / NB, b = pr % NB;
+    const int cb = c0 + b * M;
+    double st[4] = {0.0, 0.0, 0.0, 0.0};
+    if (cb < K) {
+      float xh[M];
+      uint32_t sc[M];
 #pragma unroll
       for (int j = 0; j < M; ++j) {
-        const double v = (double)xh[j];
-        st[0] += v;
-        st[1] += v * v;
-        if ((keep >> j) & 1u) { st[2] += v; st[3] += v * v; }
+        xh[j] = s_x[i][b * M + j];
+        const float ax = __builtin_fabsf(xh[j]);
+        sc[j] = __float_as_uint(a.score == SPA_SCORE_MAGNITUDE ? ax : ax * s_f[b * M + j]);
+      }
+      const uint32_t keep = topn_keep_bits<M>(sc, a.n);
+      // masked values in fragment order: each 8-channel group is 16 bytes of one lane
+      uint16_t* xf = static_cast<uint16_t*>(a.dense);
+      const int lm = i % 16, tb = i / 16;
+#pragma unroll
+      for (int q = 0; q < (M + 7) / 8; ++q) {
+        const int o = b * M + 8 * q;                 // channel offset within the step (M >= 8)
+        const int gg = (o % 64) / 16, hh = ((o % 64) / 8) % 2;
+        uint32_t wds[4];
+        const int nv = M < 8 ? M : 8;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int j0 = 8 * q + 2 * e2;
+          uint32_t lo = 0u, hi = 0u;
+          if (2 * e2 < nv) {
+            lo = ((keep >> j0) & 1u) ? (uint32_t)from_f32<DT>(xh[j0]) : 0u;
+            hi = ((keep >> (j0 + 1)) & 1u) ? (uint32_t)from_f32<DT>(xh[j0 + 1]) : 0u;
+          }
+          wds[e2] = lo | (hi << 16);
+        }
+        uint16_t* dst = xf + frag_offset(step, tb, ntb, hh, lm + 16 * gg);
+        if constexpr (M >= 8) {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+        } else {                                     // a block of 4 is half of one lane's 16 bytes
+          *reinterpret_cast<uint2*>(dst + (o % 8)) = make_uint2(wds[0], wds[1]);
+        }
+      }
+      if (a.idx_out) {
+        uint8_t* id = a.idx_out + (size_t)i * (K / M * a.n) + (size_t)(cb / M) * a.n;
+        uint32_t kb = keep;
+        for (int q = 0; q < a.n; ++q) {
+          id[q] = (uint8_t)__builtin_ctz(kb);
+          kb &= kb - 1u;
+        }
+      }
+      if (a.var) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+          const double v = (double)xh[j];
+          st[0] += v;
+          st[1] += v * v;
+          if ((keep >> j) & 1u) { st[2] += v; st[3] += v * v; }
+        }
       }
     }
-  }
-  if (a.var) {
-    if (i < T_)
+    if (a.var)
 #pragma unroll
       for (int q = 0; q < 4; ++q) s_st[i][b][q] = st[q];
+  }
+  if (a.var) {
     __syncthreads();
     if ((int)threadIdx.x < T_) {
       double tot[4] = {0.0, 0.0, 0.0, 0.0};
@@ -632,6 +648,10 @@ __device__ __forceinline__ uint4 load16_if(const void* p, bool ok) {
   return v;
 }
 
+__device__ __forceinline__ uint4 zero_unless(const uint4& v, bool ok) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
 // Fragment lane d = m + 16 g (row m, lane group g) takes the 16 bytes that
 // lane 4 m + g loaded: the loads run four lanes per row, so each row's 128-byte
 // line is one cache access instead of four.
@@ -660,14 +680,12 @@ __global__ void __launch_bounds__(1024) k_decode_mm(DecodeArgs a) {
   const int src_addr = 4 * (4 * l16 + g);
   const int row = min(n0 + 16 * rg + lr, N - 1);
   const T* wrow = static_cast<const T*>(a.w) + (size_t)row * K + 16 * lq;
-  const T* xrow[TT];
+  // masked activations, already in fragment order (one coalesced 1 KB run per fragment)
+  const uint16_t* xf = static_cast<const uint16_t*>(a.dense);
+  const int ntb = (T_ + 15) / 16;
   bool tok_ok[TT];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int tok = 16 * tt + lr;
-    tok_ok[tt] = tok < T_;
-    xrow[tt] = static_cast<const T*>(a.dense) + (size_t)min(tok, T_ - 1) * K + 16 * lq;
-  }
+  for (int tt = 0; tt < TT; ++tt) tok_ok[tt] = 16 * tt + l16 < T_;
   f32x4 acc[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -684,19 +702,26 @@ __global__ void __launch_bounds__(1024) k_decode_mm(DecodeArgs a) {
   // two register batches of U steps: the next batch is in flight while the
   // current one is permuted and multiplied
   uint4 wa[2][U][2], xb[2][U][TT][2];
+  bool okb[2][U][TT];
 #define SPA_MM_LOAD(B, L0)                                                        \
   do {                                                                            \
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                               \
       const int ls = (L0) + KG * u;                                               \
       int st = ls + rot;                                                          \
       st = s_beg + (st >= span ? st - span : st);                                 \
-      const int off = st * 64;                                                    \
-      const bool ok = ls < span && off + 16 * lq < K;                             \
-      wa[B][u][0] = load16_if(wrow + off, ok);                                    \
-      wa[B][u][1] = load16_if(wrow + off + 8, ok);                                \
+      const bool in = ls < span;                                                  \
+      const int stc = in ? st : s_beg;             /* an in-bounds step */        \
+      const int off = stc * 64;                                                   \
+      const int offw = off + 16 * lq < K ? off : 0;                               \
+      const bool okx = in && off + 16 * g < K;                                    \
+      /* unconditional loads (exact wait counting); the weight needs no mask:   \
+         its partner activation is zero wherever the step is not this one's */  \
+      wa[B][u][0] = *reinterpret_cast<const uint4*>(wrow + offw);                 \
+      wa[B][u][1] = *reinterpret_cast<const uint4*>(wrow + offw + 8);             \
       _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) {                         \
-        xb[B][u][tt][0] = load16_if(xrow[tt] + off, ok && tok_ok[tt]);            \
-        xb[B][u][tt][1] = load16_if(xrow[tt] + off + 8, ok && tok_ok[tt]);        \
+        okb[B][u][tt] = okx && tok_ok[tt];         /* applied when multiplied */  \
+        xb[B][u][tt][0] = *reinterpret_cast<const uint4*>(xf + frag_offset(stc, tt, ntb, 0, lane)); \
+        xb[B][u][tt][1] = *reinterpret_cast<const uint4*>(xf + frag_offset(stc, tt, ntb, 1, lane)); \
       }                                                                           \
     }                                                                             \
   } while (0)
@@ -705,17 +730,22 @@ __global__ void __launch_bounds__(1024) k_decode_mm(DecodeArgs a) {
     _Pragma("unroll") for (int u = 0; u < U; ++u) {                                          \
       const uint4 w0 = to_fragment(wa[B][u][0], src_addr), w1 = to_fragment(wa[B][u][1], src_addr); \
       _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) {                                    \
-        acc[tt] = mfma16<DT>(w0, to_fragment(xb[B][u][tt][0], src_addr), acc[tt]);           \
-        acc[tt] = mfma16<DT>(w1, to_fragment(xb[B][u][tt][1], src_addr), acc[tt]);           \
+        acc[tt] = mfma16<DT>(w0, zero_unless(xb[B][u][tt][0], okb[B][u][tt]), acc[tt]);      \
+        acc[tt] = mfma16<DT>(w1, zero_unless(xb[B][u][tt][1], okb[B][u][tt]), acc[tt]);      \
       }                                                                                      \
     }                                                                                        \
   } while (0)
+  // An even number of batches, so the loop body has no exit in the middle and
+  // the compiler can count the loads in flight exactly; steps past the span
+  // re-read an in-bounds step and multiply zeros.
   constexpr int STRIDE = KG * U;
+  const int nbatch = (span - kg + STRIDE - 1) / STRIDE;
+  const int npair = (nbatch + 1) / 2;
   SPA_MM_LOAD(0, kg);
-  for (int l0 = kg; l0 < span; l0 += 2 * STRIDE) {
+  for (int pi = 0; pi < npair; ++pi) {
+    const int l0 = kg + 2 * STRIDE * pi;
     SPA_MM_LOAD(1, l0 + STRIDE);
     SPA_MM_COMPUTE(0);
-    if (l0 + STRIDE >= span) break;
     SPA_MM_LOAD(0, l0 + 2 * STRIDE);
     SPA_MM_COMPUTE(1);
   }
@@ -742,6 +772,23 @@ __global__ void __launch_bounds__(1024) k_decode_mm(DecodeArgs a) {
     }
     if (!arrive_last(&a.counters[tile], a.splits, &s_flag)) return;
   }
+  // Final sums of this tile (the last workgroup when split): the loads of the
+  // split partials and of the nu sums are issued before either is waited for.
+  float v[2] = {0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = threadIdx.x + 1024 * q;
+    if (e < rows * T_) {
+      const int tok = e / rows, j = e % rows;
+      if (a.splits > 1) {
+        const float* pp = a.partial + (size_t)tok * N + n0 + j;
+        const size_t stride = (size_t)T_ * N;
+        for (int s2 = 0; s2 < a.splits; ++s2) v[q] += coherent_load(pp + s2 * stride);
+      } else {
+        v[q] = wg_sum(j, tok);
+      }
+    }
+  }
   // nu of token i from the pruning pass's per-chunk sums: lane l adds chunks
   // l, l+64, ..., then a fixed butterfly (the same result in every workgroup)
   for (int i = wv; i < T_; i += 16) {
@@ -762,18 +809,15 @@ __global__ void __launch_bounds__(1024) k_decode_mm(DecodeArgs a) {
   }
   __syncthreads();
   T* y = static_cast<T*>(a.y);
-  for (int e = threadIdx.x; e < rows * T_; e += 1024) {
-    const int tok = e / rows, j = e % rows, col = n0 + j;
-    float v;
-    if (a.splits > 1) {
-      v = 0.f;
-      for (int s2 = 0; s2 < a.splits; ++s2) v += coherent_load(&a.partial[((size_t)s2 * T_ + tok) * N + col]);
-    } else {
-      v = wg_sum(j, tok);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = threadIdx.x + 1024 * q;
+    if (e < rows * T_) {
+      const int tok = e / rows, j = e % rows, col = n0 + j;
+      float out = s_nu[tok] * v[q];
+      if (a.shift != SPA_SHIFT_NONE) out += a.eta[tok] * a.row_sum[col];
+      y[(size_t)tok * N + col] = from_f32<DT>(out);
     }
-    float out = s_nu[tok] * v;
-    if (a.shift != SPA_SHIFT_NONE) out += a.eta[tok] * a.row_sum[col];
-    y[(size_t)tok * N + col] = from_f32<DT>(out);
   }
 }
 
@@ -840,8 +884,8 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
     const int sps = (nsteps + sp - 1) / sp;
     p.k_len = sps * 64;
     p.splits = (nsteps + sps - 1) / sps;
-    p.chunks = (k + 8 * m - 1) / (8 * m);
-    const size_t o_dense = carve((size_t)t * k * 2);
+    p.chunks = (k + 63) / 64;
+    const size_t o_dense = carve((size_t)nsteps * ((t + 15) / 16) * 2048);   // fragment order
     const size_t o_stats = carve(var ? (size_t)p.chunks * t * 4 * 8 : 0);
     const size_t o_eta = carve((size_t)t * 4);
     const size_t o_part = carve(p.splits > 1 ? (size_t)p.splits * t * n_out * 4 : 0);
