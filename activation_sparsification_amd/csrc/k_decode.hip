@@ -486,6 +486,236 @@ __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(D
 }
 
 // ---------------------------------------------------------------------------
+// One token, 16-bit (the latency-critical GEMV).  The work split of the fused
+// variant, with a shorter path to the first weight load:
+//   - selection runs one m-block per lane on full waves (64 blocks per wave,
+//     as few waves as the range needs, one per SIMD for 256 blocks): it is
+//     VALU-bound, and a half-empty wave costs as much as a full one;
+//   - each selecting wave sums the whole token row itself for the mean shift
+//     (all loads issued first, fixed order, so every wave and workgroup gets
+//     the same eta) -- no barrier before the selection;
+//   - one token keeps exactly n rows per block, so block b lists its rows at
+//     slots b*n .. b*n+n-1 without a scan; one barrier publishes the list,
+//     then all 8 waves stream it, up to 32 loads of 16 B per lane in flight.
+// ---------------------------------------------------------------------------
+constexpr int kT1Waves = 8, kT1MaxBlocks = kT1Waves * 64, kT1MaxRows = 4096, kT1Loads = 32;
+
+template <int DT, int M>
+__global__ void __launch_bounds__(kT1Waves * 64) k_decode_t1(DecodeArgs a) {
+  using T = typename Dt<DT>::T;
+  constexpr int NW = kT1Waves, CPL = 8, C = 8 * CPL;
+  constexpr int NV = M * 2 / 16 > 0 ? M * 2 / 16 : 1;
+  __shared__ uint2 s_list[kT1MaxRows + NW * 64];           // (row, coefficient bits); then one trash slot per lane
+  __shared__ float s_acc[NW][C];
+  __shared__ double s_st[NW][4];
+  __shared__ float s_eta, s_nu;
+  __shared__ int s_flag;
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int tile = blockIdx.x % a.tiles, split = blockIdx.x / a.tiles;
+  const int c0 = tile * C;
+  const int kb = split * a.k_len;
+  const int KL = min(a.k_len, a.k - kb);
+  const int nb = KL / M;                                   // <= kT1MaxBlocks
+  const int nsel = (nb + 63) / 64;                         // selecting waves
+  const T* x = static_cast<const T*>(a.x);
+  const T* wt = static_cast<const T*>(a.wt);
+
+  double st[4] = {0.0, 0.0, 0.0, 0.0};
+  if (wv < nsel) {
+    // 0. this lane's block and its factors, requested before anything waits
+    const int blk = wv * 64 + lane;
+    const bool own = blk < nb;
+    const int ch0 = kb + blk * M;
+    uint4 raw[NV];
+    float f[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) f[j] = 1.f;
+    if (own) {
+      load_block<DT, M>(x + ch0, raw);
+      if (a.score == SPA_SCORE_WEIGHT) {
+#pragma unroll
+        for (int q = 0; q < M / 4; ++q) {
+          const float4 v = reinterpret_cast<const float4*>(a.chan_scale + ch0)[q];
+          f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
+        }
+      }
+    }
+    // 1. the shift: this wave's float64 sum of the whole row, 8 loads per lane
+    //    in flight, 8 partial sums combined in a fixed order
+    float eta = 0.f;
+    if (a.shift == SPA_SHIFT_TOKEN_MEAN && a.eta == nullptr) {
+      const int nq = a.k / CPL;
+      double part[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) part[r] = 0.0;
+      for (int q0 = 0; q0 < nq; q0 += 512) {
+        uint4 u[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int q = q0 + 64 * r + lane;
+          u[r] = q < nq ? reinterpret_cast<const uint4*>(x)[q] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2) part[r] += (double)elem16<DT>(u[r], e2);
+      }
+      double sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+      eta = (float)(wave_sum(sum) / (double)a.k);
+    } else if (a.eta != nullptr) {
+      eta = a.eta[0];
+    }
+    if (wv == 0 && lane == 0) s_eta = eta;
+    // 2. score, select, list
+    if (own) {
+      float xh[M];
+#pragma unroll
+      for (int j = 0; j < M; ++j) xh[j] = raw_elem<DT>(raw, j) - eta;
+      // scores: one loop per score kind under a uniform branch (if-converting
+      // them would make every kind pay for CLACT's square roots)
+      uint32_t sb[M];
+      if (a.score == SPA_SCORE_MAGNITUDE) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) sb[j] = __float_as_uint(__builtin_fabsf(xh[j]));
+      } else if (a.score == SPA_SCORE_WEIGHT) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) sb[j] = __float_as_uint(__builtin_fabsf(xh[j]) * f[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < M; ++j)   // one token: the column energy is the square alone
+          sb[j] = __float_as_uint(__builtin_fabsf(xh[j]) * sqrt_rn(clact_accumulate(0.f, xh[j])));
+      }
+      const uint32_t keep = topn_keep_bits<M>(sb, a.n);
+      // kept channel j goes to slot blk*n + (kept channels below j); a pruned one
+      // to this lane's trash slot -- one store per channel, no branches
+      uint2* const mine = s_list + blk * a.n;
+      uint2* const trash = s_list + kT1MaxRows + threadIdx.x;
+#pragma unroll
+      for (int j = 0; j < M; ++j) {
+        const bool kj = (keep >> j) & 1u;
+        const int slot = __builtin_popcount(keep & ((1u << j) - 1u));
+        *(kj ? mine + slot : trash) = make_uint2((uint32_t)(ch0 + j), __float_as_uint(xh[j]));
+      }
+      if (a.idx_out != nullptr && tile == 0) {
+        uint8_t* ip = a.idx_out + (size_t)(ch0 / M) * a.n;
+        uint32_t kb3 = keep;
+        for (int q = 0; q < a.n; ++q) {
+          ip[q] = (uint8_t)__builtin_ctz(kb3);
+          kb3 &= kb3 - 1u;
+        }
+      }
+      if (a.var) {
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+          const double v = (double)xh[j];
+          st[0] += v;
+          st[1] += v * v;
+          if ((keep >> j) & 1u) { st[2] += v; st[3] += v * v; }
+        }
+      }
+    }
+  }
+  if (a.var) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double tot = wave_sum(st[q]);
+      if (lane == 0) s_st[wv][q] = tot;                     // 0 for non-selecting waves
+    }
+  }
+  __syncthreads();
+
+  // 3. stream the listed rows: row group r8 covers slots 8 r8 .. 8 r8 + 7, wave w
+  //    takes groups w, w + 8, ...; lane (rs, cg) loads slot 8 r8 + rs, columns
+  //    col .. col + 7
+  const int L = nb * a.n;
+  const int rs = lane >> 3, cg = lane & 7;
+  const int col = c0 + cg * CPL;
+  const bool cvalid = col < a.n_out;
+  float acc[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
+  for (int u0 = 0; u0 < L; u0 += NW * 8 * kT1Loads) {
+    uint4 w[kT1Loads];
+#pragma unroll
+    for (int j = 0; j < kT1Loads; ++j) {
+      const int u = u0 + (j * NW + wv) * 8 + rs;
+      w[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (u < L && cvalid) w[j] = *reinterpret_cast<const uint4*>(wt + (size_t)s_list[u].x * a.n_out + col);
+    }
+#pragma unroll
+    for (int j = 0; j < kT1Loads; ++j) {
+      const int u = u0 + (j * NW + wv) * 8 + rs;
+      if (u < L) {
+        const float cf = __uint_as_float(s_list[u].y);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) acc[e] += cf * elem16<DT>(w[j], e);
+      }
+    }
+  }
+  // 4. the 8 row lanes of each column group, then the waves in order
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    float v = acc[e];
+    v += __shfl_xor(v, 8, kWave);
+    v += __shfl_xor(v, 16, kWave);
+    v += __shfl_xor(v, 32, kWave);
+    acc[e] = v;
+  }
+  if (rs == 0) {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) s_acc[wv][cg * CPL + e] = acc[e];
+  }
+  __syncthreads();
+  const int pc = threadIdx.x, pcol = c0 + pc;
+  const bool pact = pc < C && pcol < a.n_out;
+  const float rsum = (pact && a.shift != SPA_SHIFT_NONE) ? a.row_sum[pcol] : 0.f;
+  float v = 0.f;
+  if (pact) {
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) v += s_acc[w2][pc];
+  }
+  double stats[4] = {0.0, 0.0, 0.0, 0.0};
+  if (a.var && threadIdx.x == 0)
+    for (int w2 = 0; w2 < NW; ++w2)
+      for (int q = 0; q < 4; ++q) stats[q] += s_st[w2][q];
+  if (a.splits > 1) {
+    if (pact) coherent_store(&a.partial[(size_t)split * a.n_out + pcol], v);
+    if (a.var && threadIdx.x == 0)
+      for (int q = 0; q < 4; ++q) coherent_store(&a.stats[((size_t)tile * a.splits + split) * 4 + q], stats[q]);
+    if (!arrive_last(&a.counters[tile], a.splits, &s_flag)) return;
+    if (pact) {
+      v = 0.f;
+      for (int s0 = 0; s0 < a.splits; s0 += 16) {
+        float part[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          part[q] = s0 + q < a.splits ? coherent_load(&a.partial[(size_t)(s0 + q) * a.n_out + pcol]) : 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (s0 + q < a.splits) v += part[q];
+      }
+    }
+    if (a.var && threadIdx.x == 0) {
+      for (int q = 0; q < 4; ++q) stats[q] = 0.0;
+      for (int s2 = 0; s2 < a.splits; ++s2)
+        for (int q = 0; q < 4; ++q) stats[q] += coherent_load(&a.stats[((size_t)tile * a.splits + s2) * 4 + q]);
+    }
+  }
+  if (threadIdx.x == 0) {
+    const float nu = a.var ? nu_from_stats(stats, a.k) : 1.f;
+    s_nu = nu;
+    if (tile == 0 && a.nu_out) a.nu_out[0] = nu;
+  }
+  __syncthreads();
+  if (pact) {
+    float out = s_nu * v;
+    if (a.shift != SPA_SHIFT_NONE) out += s_eta * rsum;
+    static_cast<T*>(a.y)[pcol] = from_f32<DT>(out);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Pruning pass of the matrix-core decode (t > 4): few token rows, so the
 // work is cut by channels instead of rows.  A workgroup owns 64 channels
 // (64/m blocks) for every token of the call: it stages x_hat = x - eta for
@@ -863,6 +1093,12 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
     const int max_blocks = max_entries / per_block > 1 ? max_entries / per_block : 1;
     int bl = (blocks + sp - 1) / sp;
     if (bl > max_blocks) bl = max_blocks;
+    if (t == 1 && dtype != SPA_F32) {
+      // one-token kernel: at most 64 blocks per wave and kT1MaxRows listed rows
+      int cap = kT1MaxBlocks;
+      if (cap * n > kT1MaxRows) cap = kT1MaxRows / n;
+      if (bl > cap) bl = cap;
+    }
     p.k_len = bl * m;
     p.splits = (k + p.k_len - 1) / p.k_len;
     p.list_cap = bl * per_block;
@@ -907,6 +1143,12 @@ static hipError_t fused_launch(DecodeArgs& a, hipStream_t st) {
 
 template <int DT, int M>
 static hipError_t fused_tok(DecodeArgs& a, hipStream_t st) {
+  if constexpr (DT != SPA_F32) {
+    if (a.t == 1) {
+      hipLaunchKernelGGL((k_decode_t1<DT, M>), dim3(a.tiles * a.splits), dim3(kT1Waves * 64), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   if (a.t <= 1) return fused_launch<DT, M, 1>(a, st);
   if (a.t <= 2) return fused_launch<DT, M, 2>(a, st);
   if (a.t <= 4) return fused_launch<DT, M, 4>(a, st);
