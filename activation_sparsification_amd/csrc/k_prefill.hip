@@ -104,16 +104,24 @@ __device__ __forceinline__ void bare_barrier() {
 }
 
 // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD gets a
-// contiguous run of tile indices, token tiles fastest, so one XCD's L2
-// serves a weight tile to the token tiles that use it.
+// contiguous run of tile indices.  Tiles are numbered in groups of (up to) 8
+// token tiles times every weight tile, token tiles fastest, so an XCD's run
+// is a block of at most 8 token tiles by a few weight tiles: its L2 serves
+// each weight tile to those token tiles and each token tile to those weight
+// tiles (instead of every XCD reading every token tile).
 __device__ __forceinline__ void xcd_tile(int T, int N, int BM, int BN, int& tm, int& tn) {
+  constexpr int GM = 8;
   const int tiles_m = (T + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int total = tiles_m * tiles_n;
   int bid = blockIdx.x;
   const int per_xcd = total / 8;
   if (bid < per_xcd * 8) bid = (bid % 8) * per_xcd + bid / 8;
-  tm = bid % tiles_m;
-  tn = bid / tiles_m;
+  const int group = bid / (GM * tiles_n);
+  const int m_first = group * GM;
+  const int gm = min(tiles_m - m_first, GM);
+  const int r = bid - group * GM * tiles_n;
+  tm = m_first + r % gm;
+  tn = r / gm;
 }
 
 // Epilogue operands of one tile (BM rows, BN columns): each thread fetches at

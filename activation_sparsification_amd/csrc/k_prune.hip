@@ -2,14 +2,16 @@
 //
 // One workgroup (256 threads) per token row.  Each lane owns a segment of
 // max(16, m) consecutive channels -- whole m-blocks -- and ranks every block
-// in registers with m(m-1)/2 pairwise comparisons (guide s2.1: keep n of
-// every m; ties to the lower channel index, so exactly n survive).
+// in registers (guide s2.1: keep n of every m; ties to the lower channel
+// index, so exactly n survive): six pairwise comparisons for m = 4, the
+// selection network of spa_select.h for wider blocks.
 //
 // Outputs (any subset): packed values + uint8 in-block positions; the
 // 2:4 nibble metadata the sparse MFMA consumes; or masked dense rows for
 // the dense-MFMA path of other n:m patterns.
 #include "spa_common.h"
 #include "spa_launch.h"
+#include "spa_select.h"
 
 namespace spa {
 
@@ -55,11 +57,32 @@ __device__ __forceinline__ uint32_t block_keep(const float* sc, int n) {
   return keep;
 }
 
+// Token mean of a long row: 16-byte loads, four in flight per thread, four
+// float64 partial sums combined in a fixed order, then the workgroup sum.
 template <int DT>
 __device__ __forceinline__ float row_mean(const typename Dt<DT>::T* __restrict__ row, int k, double* s_red) {
-  double s = 0.0;
-  for (int c = threadIdx.x; c < k; c += 256) s += (double)to_f32<DT>(row[c]);
-  const double tot = block_sum(s, s_red);
+  constexpr int PER = 16 / Dt<DT>::bytes;
+  const int nq = k / PER;
+  double part[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int q0 = 0; q0 < nq; q0 += 4 * 256) {
+    uint4 u[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = q0 + r * 256 + (int)threadIdx.x;
+      u[r] = q < nq ? reinterpret_cast<const uint4*>(row)[q] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (DT == SPA_F32) {
+        part[r] += ((double)__uint_as_float(u[r].x) + (double)__uint_as_float(u[r].y)) +
+                   ((double)__uint_as_float(u[r].z) + (double)__uint_as_float(u[r].w));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[r] += (double)elem16<DT>(u[r], e);
+      }
+    }
+  }
+  const double tot = block_sum((part[0] + part[1]) + (part[2] + part[3]), s_red);
   return (float)(tot / (double)k);
 }
 
@@ -78,9 +101,26 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
   const int kept_seg = BPS * n;            // packed values per segment
   const T* xr = static_cast<const T*>(a.x) + (size_t)row * a.k;
 
+  const int nseg = a.k / SEG;
+  // All lanes of a wave run the same number of iterations so the wave-wide
+  // copy-out below stays convergent.
+  const int iters = (nseg + 255) / 256;
+  // the first pass's segment is requested before the shift is known; when the
+  // whole row is one pass, the shift is summed from these same registers
+  float xv0[SEG];
+  if ((int)threadIdx.x < nseg) load_segment<DT, SEG>(xr + (size_t)threadIdx.x * SEG, xv0);
   float eta = 0.f;
   if (a.shift_mean) {
-    eta = row_mean<DT>(xr, a.k, s_red);
+    if (iters == 1) {
+      double s = 0.0;
+      if ((int)threadIdx.x < nseg) {
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) s += (double)xv0[j];
+      }
+      eta = (float)(block_sum(s, s_red) / (double)a.k);
+    } else {
+      eta = row_mean<DT>(xr, a.k, s_red);
+    }
   } else if (a.eta_given) {
     eta = a.eta_given[row];
   }
@@ -94,10 +134,6 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
   uint8_t* s_idx = reinterpret_cast<uint8_t*>(s_dyn + (size_t)4 * 64 * kept_seg * sizeof(T)) + (size_t)wv * 64 * kept_seg;
 
   double sx = 0.0, sxx = 0.0, sm = 0.0, smm = 0.0;
-  const int nseg = a.k / SEG;
-  // All lanes of a wave run the same number of iterations so the wave-wide
-  // copy-out below stays convergent.
-  const int iters = (nseg + 255) / 256;
   for (int it = 0; it < iters; ++it) {
     const int seg = it * 256 + threadIdx.x;
     const bool active = seg < nseg;
@@ -105,7 +141,12 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
     float xh[SEG];
     if (active) {
       float xv[SEG];
-      load_segment<DT, SEG>(xr + (size_t)seg * SEG, xv);
+      if (it == 0) {
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) xv[j] = xv0[j];
+      } else {
+        load_segment<DT, SEG>(xr + (size_t)seg * SEG, xv);
+      }
 #pragma unroll
       for (int j = 0; j < SEG; ++j) xh[j] = xv[j] - eta;
       float sc[SEG];
@@ -122,7 +163,16 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
         for (int j = 0; j < SEG; ++j) sc[j] = __builtin_fabsf(xh[j]);
       }
 #pragma unroll
-      for (int b = 0; b < BPS; ++b) keepbits[b] = block_keep<M>(sc + b * M, n);
+      for (int b = 0; b < BPS; ++b) {
+        if constexpr (M >= 8) {            // selection network on the score bits
+          uint32_t sb[M];
+#pragma unroll
+          for (int j = 0; j < M; ++j) sb[j] = __float_as_uint(sc[b * M + j]);
+          keepbits[b] = topn_keep_bits<M>(sb, n);
+        } else {                           // 4 channels: six pairwise comparisons
+          keepbits[b] = block_keep<M>(sc + b * M, n);
+        }
+      }
 
       if (a.var) {
 #pragma unroll
