@@ -1,0 +1,80 @@
+"""GPU parity at the benchmark's full sizes, through the calls the benchmark times.
+
+The oracle cannot form every output of these workloads in seconds, so:
+- the in-block positions the layer used are compared bit for bit on sampled
+  token rows, and checked on every row against what holds at any size
+  (exactly n per block, ascending, inside the block);
+- nu is compared on the sampled rows (1e-6 relative);
+- y is compared on sampled rows x sampled columns against the float64 oracle
+  (row-normwise over the sampled columns, 2e-2 for 16-bit outputs).
+The weight factor is the float32 vector prepare_weight returned (the same
+factor feeds both sides); everything else the oracle forms from the inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import nm_oracle as O
+from gpu_util import f32
+
+pytestmark = pytest.mark.gpu
+
+spa = pytest.importorskip("activation_sparsification_amd")
+
+FULL = {
+    "decode": wl.SPECS["decode"],
+    "prefill": wl.SPECS["prefill"],
+    "relu2": wl.SPECS["relu2"],
+    "batched_t1": wl.SPECS["batched"].with_(t=1),
+    "batched_t8": wl.SPECS["batched"].with_(t=8),
+    "batched_t32": wl.SPECS["batched"].with_(t=32),
+}
+DECODE = {"decode", "batched_t1", "batched_t8", "batched_t32"}
+
+
+def _sample(total, count, seed):
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(total, size=min(total, count), replace=False)
+    return np.unique(np.concatenate([pick, [0, total - 1]]))
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled(name):
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    dev = torch.device("cuda:0")
+    spec = FULL[name]
+    print(f"[full-size parity] {name}: t={spec.t} k={spec.k} n_out={spec.n_out} {spec.n}:{spec.m}", flush=True)
+    x, w = wl.make_inputs(spec)
+    xd, wd = x.to(dev), w.to(dev)
+    pw = spa.prepare_weight(wd, spec.alpha, want_wt=name in DECODE)
+    cfg = spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, spec.var_rescale)
+    fn = spa.sparse_linear_decode if name in DECODE else spa.sparse_linear_prefill
+    y, idx, nu = fn(xd, pw, cfg, want_idx=True, want_nu=True)
+    torch.cuda.synchronize()
+
+    # every row: exactly n ascending positions inside each block
+    kpos = idx.cpu().numpy().reshape(spec.t, spec.k // spec.m, spec.n).astype(np.int64)
+    assert kpos.min() >= 0 and kpos.max() < spec.m
+    if spec.n > 1:
+        assert (np.diff(kpos, axis=-1) > 0).all(), "positions not strictly ascending within a block"
+
+    # sampled rows: the oracle's prune (CLACT needs every token of the call for its column norm)
+    rows = _sample(spec.t, 24, 1)
+    f = f32(pw.chan_scale) if spec.score == "weight" else None
+    xs = f32(x) if spec.score == "clact" else f32(x[torch.as_tensor(rows)])
+    pr = O.prune(xs, spec.dtype, spec.n, spec.m, score=spec.score, f=f, shift_mode=spec.shift,
+                 var_rescale=spec.var_rescale)
+    if spec.score == "clact":
+        pr = {key: (v[rows] if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == spec.t and key != "factor"
+                    else v) for key, v in pr.items()}
+    got_idx = idx.cpu().numpy()[rows]
+    assert np.array_equal(got_idx, pr["idx"]), f"{name}: in-block positions differ on sampled rows"
+    assert np.allclose(f32(nu)[rows], pr["nu"], rtol=1e-6, atol=0), f"{name}: nu differs"
+
+    # sampled outputs
+    cols = _sample(spec.n_out, 96, 2)
+    y_ref = O.linear(pr, f32(w[torch.as_tensor(cols)]))
+    y_got = f32(y)[np.ix_(rows, cols)]
+    err = O.rowwise_error(y_got, y_ref)
+    assert err <= O.TOLERANCE[spec.dtype], f"{name}: sampled y error {err}"
