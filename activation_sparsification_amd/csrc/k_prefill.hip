@@ -201,18 +201,11 @@ __global__ void __launch_bounds__(512, 1) k_gemm24(PrefillArgs p) {
   using V8 = typename Frag<DT>::V8;
   using V16 = typename Frag<DT>::V16;
   // stage = packed activations (BM x 64 B) followed by their position words
-  // (BM x 8 B): six LDS objects in all
-  constexpr int AMH = BM * 32 + BM * 4;
-  __shared__ __attribute__((aligned(1024))) uint16_t sA0[AMH];
-  __shared__ __attribute__((aligned(1024))) uint16_t sA1[AMH];
-  __shared__ __attribute__((aligned(1024))) uint16_t sA2[AMH];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB0[BN * 64];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB1[BN * 64];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB2[BN * 64];
+  // (BM x 8 B); three stages of each operand, back to back
+  constexpr int AST = BM * 72, BST = BN * 128;            // bytes per stage
+  __shared__ __attribute__((aligned(1024))) unsigned char sA[3 * AST];
+  __shared__ __attribute__((aligned(1024))) unsigned char sB[3 * BST];
   __shared__ float s_nu[BM], s_eta[BM], s_rs[BN];
-  uint16_t* const sM0 = sA0 + BM * 32;
-  uint16_t* const sM1 = sA1 + BM * 32;
-  uint16_t* const sM2 = sA2 + BM * 32;
 
   const int K = p.k, N = p.n_out, TP = p.t_pad;
   int tm, tn;
@@ -244,6 +237,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm24(PrefillArgs p) {
     offB[h] = (uint32_t)rr * (uint32_t)K * 2u + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) * 16);
   }
   const uint32_t offM = (uint32_t)((wv * 64 + lane) * 4);
+  const uint32_t ldsA0 = lds_addr(sA), ldsB0 = lds_addr(sB);
 
   // ---- LDS fragment offsets (bytes); the swizzle terms do not depend on i or j ----
   const int qa = (l32 >> 2) & 3, qb = (l32 >> 1) & 7;
@@ -254,39 +248,45 @@ __global__ void __launch_bounds__(512, 1) k_gemm24(PrefillArgs p) {
     ldsA[s] = rowA * 64 + (((2 * s + g) ^ qa) * 16);
     ldsBlo[s] = rowB * 128 + (((4 * s + g) ^ qb) * 16);
     ldsBhi[s] = rowB * 128 + (((4 * s + 2 + g) ^ qb) * 16);
-    ldsM[s] = rowA * 8 + (2 * s + g) * 2;
+    ldsM[s] = BM * 64 + rowA * 8 + (2 * s + g) * 2;
   }
 
-#define SPA_ISSUE24(KT, SA, SB, SM)                                                      \
+#define SPA_ISSUE24(KT, ST)                                                              \
   do {                                                                                   \
     const char* a_ = baseA + (size_t)(KT) * stepA;                                       \
     const char* w_ = baseW + (size_t)(KT) * 128;                                         \
-    const uint32_t la_ = lds_addr(SA) + wv * 2048, lb_ = lds_addr(SB) + wv * 4096;       \
+    const uint32_t la_ = ldsA0 + (ST) * AST + wv * 2048, lb_ = ldsB0 + (ST) * BST + wv * 4096; \
     lds_dma16(a_, offA0, la_);                                                           \
     lds_dma16(a_, offA1, la_ + 1024);                                                    \
     lds_dma16(w_, offB[0], lb_);                                                         \
     lds_dma16(w_, offB[1], lb_ + 1024);                                                  \
     lds_dma16(w_, offB[2], lb_ + 2048);                                                  \
     lds_dma16(w_, offB[3], lb_ + 3072);                                                  \
-    lds_dma4(baseM + (size_t)(KT) * stepM, offM, lds_addr(SM) + wv * 256);               \
+    lds_dma4(baseM + (size_t)(KT) * stepM, offM, ldsA0 + (ST) * AST + BM * 64 + wv * 256); \
   } while (0)
 
-#define SPA_COMPUTE24(SA, SB, SM)                                                                    \
-  do {                                                                                              \
-    const char* a_ = reinterpret_cast<const char*>(SA);                                             \
-    const char* b_ = reinterpret_cast<const char*>(SB);                                             \
-    const char* m_ = reinterpret_cast<const char*>(SM);                                             \
-    _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                                 \
-      V16 bf[FN];                                                                                   \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                                \
-        bf[j] = cat16<DT>(*reinterpret_cast<const uint4*>(b_ + ldsBlo[s] + j * 4096),               \
-                          *reinterpret_cast<const uint4*>(b_ + ldsBhi[s] + j * 4096));              \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                              \
-        const V8 af = as_vec<V8>(*reinterpret_cast<const uint4*>(a_ + ldsA[s] + i * 2048));         \
-        const int idx = (int)*reinterpret_cast<const uint16_t*>(m_ + ldsM[s] + i * 256);            \
-        _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] = smfmac32<DT>(af, bf[j], acc[i][j], idx); \
-      }                                                                                             \
-    }                                                                                               \
+  // fragments of one 32-wide half step, two register sets (set 0: first
+  // half of a step, set 1: second half)
+  V16 bf[2][FN];
+  V8 af[2][FM];
+  int ix[2][FM];
+#define SPA_READ24(ST, S)                                                                \
+  do {                                                                                   \
+    const unsigned char* a_ = sA + (ST) * AST;                                           \
+    const unsigned char* b_ = sB + (ST) * BST;                                           \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j)                                       \
+      bf[S][j] = cat16<DT>(*reinterpret_cast<const uint4*>(b_ + ldsBlo[S] + j * 4096),   \
+                           *reinterpret_cast<const uint4*>(b_ + ldsBhi[S] + j * 4096));  \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                     \
+      af[S][i] = as_vec<V8>(*reinterpret_cast<const uint4*>(a_ + ldsA[S] + i * 2048));   \
+      ix[S][i] = (int)*reinterpret_cast<const uint16_t*>(a_ + ldsM[S] + i * 256);        \
+    }                                                                                    \
+  } while (0)
+#define SPA_MMA24(S)                                                                     \
+  do {                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                       \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                     \
+        acc[i][j] = smfmac32<DT>(af[S][i], bf[S][j], acc[i][j], ix[S][i]);               \
   } while (0)
 
   f32x16 acc[FM][FN];
@@ -297,41 +297,36 @@ __global__ void __launch_bounds__(512, 1) k_gemm24(PrefillArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Step kt is read from stage kt % 3.  Before computing it: wait until only
-  // step kt+1's loads (if issued) are still in flight, barrier (everyone's
-  // copies of step kt landed, everyone finished step kt-1, whose stage is
-  // refilled next), then request step kt+2 into that stage.
+  // Step kt lives in stage kt % 3.  Barrier B_kt sits between the two halves
+  // of step kt-1's products: before it, every wave has read all of step kt-1
+  // (so that stage is refilled with step kt+2 right after it) and waited for
+  // its own copies of step kt; after it, the wave reads step kt's first half
+  // while the matrix cores run step kt-1's second half from registers, so the
+  // barrier never leaves the matrix cores without operands.
   const int nk = K / 64;
-  const int nq = nk / 3, nr = nk - 3 * nq;
-  SPA_ISSUE24(0, sA0, sB0, sM0);
-  if (nk > 1) SPA_ISSUE24(1, sA1, sB1, sM1);
-  for (int q = 0; q < nq; ++q) {
-    const int kt = 3 * q;
-    wait_vm<7>(kt + 1 < nk);
-    bare_barrier();
-    SPA_ISSUE24(kt + 2, sA2, sB2, sM2);
-    SPA_COMPUTE24(sA0, sB0, sM0);
-    wait_vm<7>(1);
-    bare_barrier();
-    if (kt + 3 < nk) SPA_ISSUE24(kt + 3, sA0, sB0, sM0);
-    SPA_COMPUTE24(sA1, sB1, sM1);
-    wait_vm<7>(kt + 3 < nk);
-    bare_barrier();
-    if (kt + 4 < nk) SPA_ISSUE24(kt + 4, sA1, sB1, sM1);
-    SPA_COMPUTE24(sA2, sB2, sM2);
+  SPA_ISSUE24(0, 0);
+  if (nk > 1) SPA_ISSUE24(1, 1);
+  wait_vm<7>(nk > 1);
+  bare_barrier();
+  if (nk > 2) SPA_ISSUE24(2, 2);
+  SPA_READ24(0, 0);
+  SPA_READ24(0, 1);
+  SPA_MMA24(0);
+  int st = 0;
+  for (int kt = 1; kt < nk; ++kt) {
+    st = st == 2 ? 0 : st + 1;                 // kt % 3
+    wait_vm<7>(kt + 1 < nk);                   // step kt landed (kt+1 may be in flight)
+    bare_barrier();                            // B_kt
+    if (kt + 2 < nk) SPA_ISSUE24(kt + 2, st == 0 ? 2 : st - 1);
+    SPA_READ24(st, 0);
+    SPA_MMA24(1);                              // step kt-1, second half
+    SPA_READ24(st, 1);
+    SPA_MMA24(0);                              // step kt, first half
   }
-  if (nr >= 1) {                       // step 3nq in stage 0 (step 3nq+1, if any, in flight)
-    wait_vm<7>(nr == 2);
-    bare_barrier();
-    SPA_COMPUTE24(sA0, sB0, sM0);
-  }
-  if (nr == 2) {                       // step 3nq+1 in stage 1
-    wait_vm<7>(0);
-    bare_barrier();
-    SPA_COMPUTE24(sA1, sB1, sM1);
-  }
+  SPA_MMA24(1);                                // last step, second half
 #undef SPA_ISSUE24
-#undef SPA_COMPUTE24
+#undef SPA_READ24
+#undef SPA_MMA24
 
   ts.park(s_nu, s_eta, s_rs);
   __syncthreads();
