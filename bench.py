@@ -41,7 +41,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16/fp16 matrix peak
 MALL_BYTES = 256 * 2 ** 20
 METRIC = "decode: effective HBM GB/s; prefill: TFLOP/s; both as % of MI355X peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fused_bf16_t1_k4096_n14336_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_t1_bf16_k4096_n14336_traffic.txt")
 DECODE_SOURCES = ["activation_sparsification_amd/csrc/k_decode.hip", "activation_sparsification_amd/csrc/spa_common.h"]
 
 WORKLOADS = {
@@ -270,7 +270,7 @@ def main():
                 unit=head["unit"],
                 frac=head["value"] / (PEAK_HBM_GBS if decode else PEAK_BF16_TFLOPS),
                 traffic=traffic,
-                kernel="k_decode_fused<bf16,16,1>" if args.workload == "decode" else None,
+                kernel="k_decode_t1<bf16,16>" if args.workload == "decode" else None,
                 per_unit="bytes per kept weight row = n_out * 2; one launch reads the call's kept rows")
     cpu = None
     if not args.no_cpu_baseline:
