@@ -14,14 +14,17 @@
 // partials in split order, so results do not depend on arrival order, and
 // applies the epilogue.  Counters are left at zero for the next call.
 //
-// Two variants:
-//  * fused (t <= 4): each workgroup prunes its own channel range in LDS
-//    (the same few thousand comparisons in every tile) and streams the kept
-//    rows with float32 VALU FMAs, 16 bytes per lane per row;
-//  * mask + stream (t > 4, 16-bit): one mask kernel prunes every channel
-//    once, recording which tokens keep each channel and the kept values;
-//    the stream kernel reads the union of kept rows once and runs the
-//    tokens x rows x columns product on matrix cores (mfma 16x16x32).
+// Variants:
+//  * one token, 16-bit weights under 2 GiB (k_decode_t1): selection on full
+//    waves, one barrier, then every wave streams the kept rows with buffer
+//    loads, 32 per lane in flight;
+//  * fused (t <= 4, and float32): each workgroup prunes its own channel range
+//    in LDS (the same few thousand comparisons in every tile) and streams the
+//    union of kept rows with float32 VALU FMAs, 16 bytes per lane per row;
+//  * matrix-core (5..32 tokens, 16-bit): the union of kept rows is nearly all
+//    of W, so k_prune_cols prunes every channel once into masked rows in the
+//    matrix cores' operand order, and k_decode_mm reads the row-major W once
+//    and runs the product on matrix cores (mfma 16x16x32).
 #include "spa_common.h"
 #include "spa_launch.h"
 #include "spa_select.h"
@@ -77,6 +80,22 @@ __device__ __forceinline__ float nu_from_stats(const double* s, int k) {
   const double vf = s[1] / kk - (s[0] / kk) * (s[0] / kk);
   const double vm = s[3] / kk - (s[2] / kk) * (s[2] / kk);
   return vm > 0.0 ? (float)__builtin_sqrt(vf / vm) : 1.f;
+}
+
+// Sum over the splits of a tile, in split order, of entry `e` of each split's
+// float64 block (blocks `stride` apart): all loads in flight before the adds.
+__device__ __forceinline__ double split_sum_f64(const double* base, int splits, int stride, int e) {
+  double acc = 0.0;
+  for (int s0 = 0; s0 < splits; s0 += 16) {
+    double part[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      part[q] = s0 + q < splits ? coherent_load(base + (size_t)(s0 + q) * stride + e) : 0.0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if (s0 + q < splits) acc += part[q];
+  }
+  return acc;
 }
 
 template <int NW>
@@ -160,6 +179,7 @@ __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(D
   __shared__ int s_flag;
   __shared__ float s_acc[NW][TOK][C];
   __shared__ double s_st[NW][TOK][4];
+  __shared__ double s_stsum[TOK * 4];
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int T_ = a.t;
@@ -464,11 +484,12 @@ __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(D
           if (s0 + q < a.splits) v += part[q];
       }
     }
-    if (a.var && pi < T_ && pc == 0) {
-      for (int q = 0; q < 4; ++q) stats[q] = 0.0;
-      for (int s2 = 0; s2 < a.splits; ++s2)
-        for (int q = 0; q < 4; ++q)
-          stats[q] += coherent_load(&a.stats[(((size_t)tile * a.splits + s2) * T_ + pi) * 4 + q]);
+    if (a.var) {   // one thread per (token, sum), every split's value in flight at once
+      if ((int)threadIdx.x < T_ * 4)
+        s_stsum[threadIdx.x] = split_sum_f64(a.stats + (size_t)tile * a.splits * T_ * 4, a.splits, T_ * 4, threadIdx.x);
+      __syncthreads();
+      if (pi < T_ && pc == 0)
+        for (int q = 0; q < 4; ++q) stats[q] = s_stsum[pi * 4 + q];
     }
   }
   // 6. epilogue
@@ -486,189 +507,206 @@ __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(D
 }
 
 // ---------------------------------------------------------------------------
-// One token, 16-bit (the latency-critical GEMV).  The work split of the fused
-// variant, with a shorter path to the first weight load:
-//   - selection runs one m-block per lane on full waves (64 blocks per wave,
-//     as few waves as the range needs, one per SIMD for 256 blocks): it is
-//     VALU-bound, and a half-empty wave costs as much as a full one;
-//   - each selecting wave sums the whole token row itself for the mean shift
-//     (all loads issued first, fixed order, so every wave and workgroup gets
-//     the same eta) -- no barrier before the selection;
-//   - one token keeps exactly n rows per block, so block b lists its rows at
-//     slots b*n .. b*n+n-1 without a scan; one barrier publishes the list,
-//     then all 8 waves stream it, up to 32 loads of 16 B per lane in flight.
+// One token, 16-bit weights, wide outputs (the latency-critical GEMV).
+//   * Work split: workgroup (tile, split) owns 512 columns and a channel range
+//     of at most kT1MaxChan channels; a load instruction reads 1 KB of one
+//     weight row (long runs per row stream HBM faster than eight 128-byte
+//     pieces of eight rows).  Splits hand off through the ticket above.
+//   * The mean shift: every thread sums its share of the token row in
+//     float64 (one 16-byte load per thread per 4096 channels); the waves'
+//     sums are combined in a fixed order after the only barrier before the
+//     stream.
+//   * Each wave then works alone on 64 channels at a time: a lane scores its
+//     channel, counts the positions of its m-block that beat it (larger
+//     score, or equal score at a lower position) with xor shuffles inside the
+//     block, and keeps the channel when fewer than n do.  A ballot orders the
+//     wave's kept channels; their (row, coefficient) pairs pass through the
+//     wave's own LDS slots, and the wave streams exactly those rows, up to
+//     kT1Loads loads per lane in flight, row offsets and coefficients held in
+//     scalar registers.  No wave waits for another before its stream.
 // ---------------------------------------------------------------------------
-constexpr int kT1Waves = 8, kT1MaxBlocks = kT1Waves * 64, kT1MaxRows = 4096, kT1Loads = 32;
+constexpr int kT1Waves = 8, kT1Threads = kT1Waves * 64, kT1Cols = 512, kT1MaxChan = 2048, kT1Loads = 32;
+
+// The one-token kernel: 16-bit weights under kBufferOutOfRange bytes (32-bit
+// offsets) and at least eight 512-column tiles.
+__host__ __device__ inline bool t1_kernel(int t, int dtype, int k, int n_out) {
+  return t == 1 && dtype != SPA_F32 && n_out >= 8 * kT1Cols &&
+         (uint64_t)k * (uint64_t)n_out * 2u < (uint64_t)kBufferOutOfRange;
+}
+
+// so[q] = v of lane (lane ^ q), q = 1 .. M-1, inside groups of 32 lanes
+// (ds_swizzle bit mode: and-mask 31, xor-mask q).
+template <int M, int Q = 1>
+__device__ __forceinline__ void swizzle_xor_all(uint32_t v, uint32_t (&so)[M]) {
+  if constexpr (Q < M) {
+    so[Q] = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (Q << 10));
+    swizzle_xor_all<M, Q + 1>(v, so);
+  }
+}
 
 template <int DT, int M>
-__global__ void __launch_bounds__(kT1Waves * 64) k_decode_t1(DecodeArgs a) {
+__global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
   using T = typename Dt<DT>::T;
-  constexpr int NW = kT1Waves, CPL = 8, C = 8 * CPL;
-  constexpr int NV = M * 2 / 16 > 0 ? M * 2 / 16 : 1;
-  __shared__ uint2 s_list[kT1MaxRows + NW * 64];           // (row, coefficient bits); then one trash slot per lane
+  constexpr int NW = kT1Waves, NT = kT1Threads, CPL = 8, C = kT1Cols;
+  constexpr int R = kT1MaxChan / NT;                       // channel rounds per thread
+  static_assert(64 % M == 0 && M <= 32, "an m-block must sit inside one wave");
   __shared__ float s_acc[NW][C];
-  __shared__ double s_st[NW][4];
-  __shared__ float s_eta, s_nu;
+  __shared__ uint2 s_ent[NW][64];                          // per wave: (row, coefficient bits) of its kept channels
+  __shared__ double s_part[NW][5];                         // row-sum partial, then the four variance sums
+  __shared__ double s_stsum[4];
+  __shared__ float s_nu;
   __shared__ int s_flag;
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int tile = blockIdx.x % a.tiles, split = blockIdx.x / a.tiles;
   const int c0 = tile * C;
   const int kb = split * a.k_len;
-  const int KL = min(a.k_len, a.k - kb);
-  const int nb = KL / M;                                   // <= kT1MaxBlocks
-  const int nsel = (nb + 63) / 64;                         // selecting waves
+  const int KL = min(a.k_len, a.k - kb);                   // a multiple of M, <= kT1MaxChan
   const T* x = static_cast<const T*>(a.x);
   const T* wt = static_cast<const T*>(a.wt);
 
+  // 0. this thread's channels (and their factors), then its share of the row
+  //    for the mean: buffer loads, all issued before anything waits (offsets
+  //    past the end read zeros, so no load sits under a branch)
+  const bool wscore = a.score == SPA_SCORE_WEIGHT;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(x), (short)0, a.k * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
+      wscore ? (void*)a.chan_scale : const_cast<T*>(x), (short)0, wscore ? a.k * 4 : 0, kBufferWord3);
+  uint32_t xraw[R], fraw[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = NT * r + threadIdx.x;
+    xraw[r] = buffer_load_u16(xr, c < KL ? (uint32_t)(kb + c) * 2u : kBufferOutOfRange);
+    fraw[r] = buffer_load_u32(fr, c < KL ? (uint32_t)(kb + c) * 4u : kBufferOutOfRange);
+  }
+  // 1. the shift
+  const bool mean = a.shift == SPA_SHIFT_TOKEN_MEAN && a.eta == nullptr;
+  if (mean) {
+    const int nq = a.k / 8;
+    double part[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int q0 = 0; q0 < nq; q0 += 4 * NT) {
+      uint4 u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = q0 + NT * i + threadIdx.x;
+        u[i] = buffer_load16(xr, q < nq ? (uint32_t)q * 16u : kBufferOutOfRange);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[i] += (double)elem16<DT>(u[i], e);
+    }
+    const double tot = wave_sum((part[0] + part[1]) + (part[2] + part[3]));
+    if (lane == 0) s_part[wv][0] = tot;
+    __syncthreads();
+  }
+  float eta = 0.f;
+  if (mean) {
+    double s = 0.0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) s += s_part[w2][0];
+    eta = (float)(s / (double)a.k);
+  } else if (a.eta != nullptr) {
+    eta = a.eta[0];
+  }
+
+  const uint32_t wt_bytes = (uint32_t)a.k * (uint32_t)a.n_out * 2u;
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(wt), (short)0,
+                                                                          (int)wt_bytes, kBufferWord3);
+  const uint32_t col_bytes = (uint32_t)min(c0 + lane * CPL, a.n_out - CPL) * 2u;   // lanes past n_out: never stored
+  const uint32_t row_bytes = (uint32_t)a.n_out * 2u;
+  const int j = lane % M;
+  float acc[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
   double st[4] = {0.0, 0.0, 0.0, 0.0};
-  if (wv < nsel) {
-    // 0. this lane's block and its factors, requested before anything waits
-    const int blk = wv * 64 + lane;
-    const bool own = blk < nb;
-    const int ch0 = kb + blk * M;
-    uint4 raw[NV];
-    float f[M];
+
 #pragma unroll
-    for (int j = 0; j < M; ++j) f[j] = 1.f;
-    if (own) {
-      load_block<DT, M>(x + ch0, raw);
-      if (a.score == SPA_SCORE_WEIGHT) {
-#pragma unroll
-        for (int q = 0; q < M / 4; ++q) {
-          const float4 v = reinterpret_cast<const float4*>(a.chan_scale + ch0)[q];
-          f[4 * q] = v.x; f[4 * q + 1] = v.y; f[4 * q + 2] = v.z; f[4 * q + 3] = v.w;
-        }
-      }
+  for (int r = 0; r < R; ++r) {
+    const int cw = NT * r + 64 * wv;                       // this wave's first channel of the round
+    if (cw >= KL) break;                                   // uniform
+    const int c = cw + lane;
+    // 2. score (one loop per score kind under a uniform branch: if-converted,
+    //    every kind would pay for CLACT's square root)
+    const float xh = to_f32<DT>((T)xraw[r]) - eta;
+    uint32_t sb;
+    if (a.score == SPA_SCORE_MAGNITUDE) {
+      sb = __float_as_uint(__builtin_fabsf(xh));
+    } else if (a.score == SPA_SCORE_WEIGHT) {
+      sb = __float_as_uint(__builtin_fabsf(xh) * __uint_as_float(fraw[r]));
+    } else {                                               // one token: the column energy is the square alone
+      sb = __float_as_uint(__builtin_fabsf(xh) * sqrt_rn(clact_accumulate(0.f, xh)));
     }
-    // 1. the shift: this wave's float64 sum of the whole row, 8 loads per lane
-    //    in flight, 8 partial sums combined in a fixed order
-    float eta = 0.f;
-    if (a.shift == SPA_SHIFT_TOKEN_MEAN && a.eta == nullptr) {
-      const int nq = a.k / CPL;
-      double part[8];
+    // 3. rank inside the block: scores are non-negative floats, so their bit
+    //    patterns order like the values and stay below 2^31; adding 1 for a
+    //    lower position turns "greater or equal" into "greater"
+    //    (xor swizzles inside 32-lane groups, all issued before the first compare)
+    uint32_t so[M];
+    swizzle_xor_all<M>(sb, so);
+    __builtin_amdgcn_sched_barrier(0);
+    int beat = 0;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) part[r] = 0.0;
-      for (int q0 = 0; q0 < nq; q0 += 512) {
-        uint4 u[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int q = q0 + 64 * r + lane;
-          u[r] = q < nq ? reinterpret_cast<const uint4*>(x)[q] : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) part[r] += (double)elem16<DT>(u[r], e2);
-      }
-      double sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-      eta = (float)(wave_sum(sum) / (double)a.k);
-    } else if (a.eta != nullptr) {
-      eta = a.eta[0];
+    for (int q = 1; q < M; ++q) beat += (so[q] + ((j ^ q) < j ? 1u : 0u)) > sb ? 1 : 0;
+    const bool keep = c < KL && beat < a.n;
+    const unsigned long long kmask = __ballot(keep);
+    const int cnt = __popcll(kmask);                        // uniform
+    const int slot = __popcll(kmask & ((1ull << lane) - 1ull));
+    if (keep) {
+      s_ent[wv][slot] = make_uint2((uint32_t)(kb + c), __float_as_uint(xh));
+      if (a.idx_out != nullptr && tile == 0)
+        a.idx_out[(size_t)(kb + c - j) / M * a.n + (slot - (lane / M) * a.n)] = (uint8_t)j;
     }
-    if (wv == 0 && lane == 0) s_eta = eta;
-    // 2. score, select, list
-    if (own) {
-      float xh[M];
+    if (a.var && c < KL) {
+      const double v = (double)xh;
+      st[0] += v;
+      st[1] += v * v;
+      if (keep) { st[2] += v; st[3] += v * v; }
+    }
+    // the wave's LDS writes are complete before its reads (one wave, in order)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint2 mine = s_ent[wv][lane];                    // entry `lane` (stale past cnt, never used)
+    // 4. stream the wave's kept rows, kT1Loads at a time
+    for (int b0 = 0; b0 < cnt; b0 += kT1Loads) {
+      uint32_t soff[kT1Loads], voff[kT1Loads];
+      float cf[kT1Loads];
 #pragma unroll
-      for (int j = 0; j < M; ++j) xh[j] = raw_elem<DT>(raw, j) - eta;
-      // scores: one loop per score kind under a uniform branch (if-converting
-      // them would make every kind pay for CLACT's square roots)
-      uint32_t sb[M];
-      if (a.score == SPA_SCORE_MAGNITUDE) {
-#pragma unroll
-        for (int j = 0; j < M; ++j) sb[j] = __float_as_uint(__builtin_fabsf(xh[j]));
-      } else if (a.score == SPA_SCORE_WEIGHT) {
-#pragma unroll
-        for (int j = 0; j < M; ++j) sb[j] = __float_as_uint(__builtin_fabsf(xh[j]) * f[j]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < M; ++j)   // one token: the column energy is the square alone
-          sb[j] = __float_as_uint(__builtin_fabsf(xh[j]) * sqrt_rn(clact_accumulate(0.f, xh[j])));
+      for (int i = 0; i < kT1Loads; ++i) {
+        const int e = b0 + i;
+        const bool ok = e < cnt;                             // uniform
+        const uint32_t row = (uint32_t)__builtin_amdgcn_readlane((int)mine.x, e & 63);
+        soff[i] = ok ? row * row_bytes : 0u;
+        voff[i] = ok ? col_bytes : kBufferOutOfRange;
+        cf[i] = ok ? __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)mine.y, e & 63)) : 0.f;
       }
-      const uint32_t keep = topn_keep_bits<M>(sb, a.n);
-      // kept channel j goes to slot blk*n + (kept channels below j); a pruned one
-      // to this lane's trash slot -- one store per channel, no branches
-      uint2* const mine = s_list + blk * a.n;
-      uint2* const trash = s_list + kT1MaxRows + threadIdx.x;
+      uint4 w[kT1Loads];
 #pragma unroll
-      for (int j = 0; j < M; ++j) {
-        const bool kj = (keep >> j) & 1u;
-        const int slot = __builtin_popcount(keep & ((1u << j) - 1u));
-        *(kj ? mine + slot : trash) = make_uint2((uint32_t)(ch0 + j), __float_as_uint(xh[j]));
+      for (int i = 0; i < kT1Loads; ++i) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)voff[i], (int)soff[i], 0);
+        w[i] = make_uint4(v[0], v[1], v[2], v[3]);
       }
-      if (a.idx_out != nullptr && tile == 0) {
-        uint8_t* ip = a.idx_out + (size_t)(ch0 / M) * a.n;
-        uint32_t kb3 = keep;
-        for (int q = 0; q < a.n; ++q) {
-          ip[q] = (uint8_t)__builtin_ctz(kb3);
-          kb3 &= kb3 - 1u;
-        }
-      }
-      if (a.var) {
+      __builtin_amdgcn_sched_barrier(0);                   // every load issued before the first use
 #pragma unroll
-        for (int j = 0; j < M; ++j) {
-          const double v = (double)xh[j];
-          st[0] += v;
-          st[1] += v * v;
-          if ((keep >> j) & 1u) { st[2] += v; st[3] += v * v; }
-        }
+      for (int i = 0; i < kT1Loads; ++i) {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) acc[e] += cf[i] * elem16<DT>(w[i], e);
       }
     }
   }
+  // 5. the waves in order
   if (a.var) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const double tot = wave_sum(st[q]);
-      if (lane == 0) s_st[wv][q] = tot;                     // 0 for non-selecting waves
+      if (lane == 0) s_part[wv][1 + q] = tot;
     }
   }
-  __syncthreads();
-
-  // 3. stream the listed rows: row group r8 covers slots 8 r8 .. 8 r8 + 7, wave w
-  //    takes groups w, w + 8, ...; lane (rs, cg) loads slot 8 r8 + rs, columns
-  //    col .. col + 7
-  const int L = nb * a.n;
-  const int rs = lane >> 3, cg = lane & 7;
-  const int col = c0 + cg * CPL;
-  const bool cvalid = col < a.n_out;
-  float acc[CPL];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) acc[e] = 0.f;
-  for (int u0 = 0; u0 < L; u0 += NW * 8 * kT1Loads) {
-    uint4 w[kT1Loads];
-#pragma unroll
-    for (int j = 0; j < kT1Loads; ++j) {
-      const int u = u0 + (j * NW + wv) * 8 + rs;
-      w[j] = make_uint4(0u, 0u, 0u, 0u);
-      if (u < L && cvalid) w[j] = *reinterpret_cast<const uint4*>(wt + (size_t)s_list[u].x * a.n_out + col);
-    }
-#pragma unroll
-    for (int j = 0; j < kT1Loads; ++j) {
-      const int u = u0 + (j * NW + wv) * 8 + rs;
-      if (u < L) {
-        const float cf = __uint_as_float(s_list[u].y);
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) acc[e] += cf * elem16<DT>(w[j], e);
-      }
-    }
-  }
-  // 4. the 8 row lanes of each column group, then the waves in order
-#pragma unroll
-  for (int e = 0; e < CPL; ++e) {
-    float v = acc[e];
-    v += __shfl_xor(v, 8, kWave);
-    v += __shfl_xor(v, 16, kWave);
-    v += __shfl_xor(v, 32, kWave);
-    acc[e] = v;
-  }
-  if (rs == 0) {
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) s_acc[wv][cg * CPL + e] = acc[e];
-  }
+  for (int e = 0; e < CPL; ++e) s_acc[wv][lane * CPL + e] = acc[e];
   __syncthreads();
   const int pc = threadIdx.x, pcol = c0 + pc;
-  const bool pact = pc < C && pcol < a.n_out;
+  const bool pact = pcol < a.n_out;
   const float rsum = (pact && a.shift != SPA_SHIFT_NONE) ? a.row_sum[pcol] : 0.f;
   float v = 0.f;
   if (pact) {
@@ -678,7 +716,7 @@ __global__ void __launch_bounds__(kT1Waves * 64) k_decode_t1(DecodeArgs a) {
   double stats[4] = {0.0, 0.0, 0.0, 0.0};
   if (a.var && threadIdx.x == 0)
     for (int w2 = 0; w2 < NW; ++w2)
-      for (int q = 0; q < 4; ++q) stats[q] += s_st[w2][q];
+      for (int q = 0; q < 4; ++q) stats[q] += s_part[w2][1 + q];
   if (a.splits > 1) {
     if (pact) coherent_store(&a.partial[(size_t)split * a.n_out + pcol], v);
     if (a.var && threadIdx.x == 0)
@@ -696,12 +734,14 @@ __global__ void __launch_bounds__(kT1Waves * 64) k_decode_t1(DecodeArgs a) {
           if (s0 + q < a.splits) v += part[q];
       }
     }
-    if (a.var && threadIdx.x == 0) {
-      for (int q = 0; q < 4; ++q) stats[q] = 0.0;
-      for (int s2 = 0; s2 < a.splits; ++s2)
-        for (int q = 0; q < 4; ++q) stats[q] += coherent_load(&a.stats[((size_t)tile * a.splits + s2) * 4 + q]);
+    if (a.var) {   // one thread per sum, every split's value in flight at once
+      if (threadIdx.x < 4) s_stsum[threadIdx.x] = split_sum_f64(a.stats + (size_t)tile * a.splits * 4, a.splits, 4, threadIdx.x);
+      __syncthreads();
+      if (threadIdx.x == 0)
+        for (int q = 0; q < 4; ++q) stats[q] = s_stsum[q];
     }
   }
+  // 6. epilogue
   if (threadIdx.x == 0) {
     const float nu = a.var ? nu_from_stats(stats, a.k) : 1.f;
     s_nu = nu;
@@ -710,7 +750,7 @@ __global__ void __launch_bounds__(kT1Waves * 64) k_decode_t1(DecodeArgs a) {
   __syncthreads();
   if (pact) {
     float out = s_nu * v;
-    if (a.shift != SPA_SHIFT_NONE) out += s_eta * rsum;
+    if (a.shift != SPA_SHIFT_NONE) out += eta * rsum;
     static_cast<T*>(a.y)[pcol] = from_f32<DT>(out);
   }
 }
@@ -1071,7 +1111,29 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
   const bool fused = t <= 4 || dtype == SPA_F32;
   size_t bytes = 0;
   auto carve = [&](size_t nbytes) { size_t off = bytes; bytes += (nbytes + 255) & ~(size_t)255; return off; };
-  if (fused) {
+  if (t1_kernel(t, dtype, k, n_out)) {
+    // one-token kernel: 512-column tiles (1 KB of each kept row per load
+    // instruction); channel splits until about 256 workgroups run, each split
+    // at most kT1MaxChan channels, the partial traffic near 5 % of the weight bytes
+    p.col_tile = kT1Cols;
+    p.tiles = (n_out + p.col_tile - 1) / p.col_tile;
+    const int blocks = k / m;
+    int sp = 256 / p.tiles > 1 ? 256 / p.tiles : 1;
+    const double wbytes = (double)k * n / m * n_out * 2.0;
+    const int max_by_traffic = (int)(0.05 * wbytes / (8.0 * n_out));
+    if (sp > max_by_traffic) sp = max_by_traffic > 1 ? max_by_traffic : 1;
+    if (sp > blocks) sp = blocks;
+    int bl = (blocks + sp - 1) / sp;
+    if (bl * m > kT1MaxChan) bl = kT1MaxChan / m;
+    p.k_len = bl * m;
+    p.splits = (blocks + bl - 1) / bl;
+    const size_t o_part = carve((size_t)p.splits * n_out * 4);
+    const size_t o_stats = carve(var ? (size_t)p.tiles * p.splits * 4 * 8 : 0);
+    const size_t o_cnt = carve((size_t)p.tiles * 4);
+    const size_t o_eta = carve(4);
+    p.partial = (float*)o_part; p.stats = (double*)o_stats; p.counters = (unsigned*)o_cnt;
+    p.eta_ws = (float*)o_eta;
+  } else if (fused) {
     // 8 lanes x one 16-byte load = one 128-byte cache line of every listed row
     const int cpl = dtype == SPA_F32 ? 4 : 8;
     p.col_tile = 8 * cpl;
@@ -1093,12 +1155,6 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
     const int max_blocks = max_entries / per_block > 1 ? max_entries / per_block : 1;
     int bl = (blocks + sp - 1) / sp;
     if (bl > max_blocks) bl = max_blocks;
-    if (t == 1 && dtype != SPA_F32) {
-      // one-token kernel: at most 64 blocks per wave and kT1MaxRows listed rows
-      int cap = kT1MaxBlocks;
-      if (cap * n > kT1MaxRows) cap = kT1MaxRows / n;
-      if (bl > cap) bl = cap;
-    }
     p.k_len = bl * m;
     p.splits = (k + p.k_len - 1) / p.k_len;
     p.list_cap = bl * per_block;
@@ -1144,8 +1200,8 @@ static hipError_t fused_launch(DecodeArgs& a, hipStream_t st) {
 template <int DT, int M>
 static hipError_t fused_tok(DecodeArgs& a, hipStream_t st) {
   if constexpr (DT != SPA_F32) {
-    if (a.t == 1) {
-      hipLaunchKernelGGL((k_decode_t1<DT, M>), dim3(a.tiles * a.splits), dim3(kT1Waves * 64), 0, st, a);
+    if (t1_kernel(a.t, DT, a.k, a.n_out)) {
+      hipLaunchKernelGGL((k_decode_t1<DT, M>), dim3(a.tiles * a.splits), dim3(kT1Threads), 0, st, a);
       return hipGetLastError();
     }
   }

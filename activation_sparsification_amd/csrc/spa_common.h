@@ -48,6 +48,22 @@ template <int DT> __device__ __forceinline__ float elem16(const uint4& v, int e)
   return DT == SPA_BF16 ? bf16_to_f32(h) : f16_to_f32(h);
 }
 
+// Raw buffer loads (CDNA): a descriptor of base, size in bytes and the gfx9
+// format word; a 32-bit byte offset per lane; a load at or past the size
+// returns zeros instead of touching memory.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr uint32_t kBufferOutOfRange = 0x80000000u;   // past every buffer smaller than 2 GiB
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t buffer_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buffer_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // The mask arithmetic.  Every helper is a single IEEE operation so that the
 // GPU reproduces the reference definition bit for bit.
