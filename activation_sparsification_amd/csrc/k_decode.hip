@@ -879,7 +879,7 @@ __global__ void __launch_bounds__(256) k_prune_cols(DecodeArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) tot[q] += s_st[threadIdx.x][b2][q];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) a.stats[((size_t)blockIdx.x * T_ + threadIdx.x) * 4 + q] = tot[q];
+      for (int q = 0; q < 4; ++q) a.stats[((size_t)threadIdx.x * 4 + q) * a.chunks + blockIdx.x] = tot[q];   // [token][sum][chunk]
     }
   }
 }
@@ -1042,37 +1042,66 @@ __global__ void __launch_bounds__(1024) k_decode_mm(DecodeArgs a) {
     }
     if (!arrive_last(&a.counters[tile], a.splits, &s_flag)) return;
   }
-  // Final sums of this tile (the last workgroup when split): the loads of the
-  // split partials and of the nu sums are issued before either is waited for.
+  // Final sums of this tile (the last workgroup when split).
   float v[2] = {0.f, 0.f};
+  double nsum[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int e = threadIdx.x + 1024 * q;
     if (e < rows * T_) {
       const int tok = e / rows, j = e % rows;
-      if (a.splits > 1) {
+      if (a.splits > 1) {   // every split's partial in flight before the adds, split order
         const float* pp = a.partial + (size_t)tok * N + n0 + j;
         const size_t stride = (size_t)T_ * N;
-        for (int s2 = 0; s2 < a.splits; ++s2) v[q] += coherent_load(pp + s2 * stride);
+        for (int s0 = 0; s0 < a.splits; s0 += 8) {
+          float part[8];
+#pragma unroll
+          for (int s2 = 0; s2 < 8; ++s2) part[s2] = s0 + s2 < a.splits ? coherent_load(pp + (s0 + s2) * stride) : 0.f;
+#pragma unroll
+          for (int s2 = 0; s2 < 8; ++s2)
+            if (s0 + s2 < a.splits) v[q] += part[s2];
+        }
       } else {
         v[q] = wg_sum(j, tok);
       }
     }
   }
-  // nu of token i from the pruning pass's per-chunk sums: lane l adds chunks
-  // l, l+64, ..., then a fixed butterfly (the same result in every workgroup)
-  for (int i = wv; i < T_; i += 16) {
-    float nu = 1.f;
-    if (a.var) {
-      double sum4[4] = {0.0, 0.0, 0.0, 0.0};
-      for (int c = lane; c < a.chunks; c += 64)
+  // nu of token i from the pruning pass's per-chunk sums (laid out
+  // [token][sum][chunk]): wave w takes tokens w and w + 16, lane l adds chunks
+  // l, l+64, l+128, l+192 (all of a pass's loads in flight before the adds,
+  // 512 contiguous bytes per load instruction), then a fixed butterfly: the
+  // same result in every workgroup
+  if (a.var) {
+    for (int c0 = 0; c0 < a.chunks; c0 += 256) {
+      double ld[2][4][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sum4[q] += a.stats[((size_t)c * T_ + i) * 4 + q];
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sum4[q] = wave_sum(sum4[q]);
-      nu = nu_from_stats(sum4, K);
+        for (int u = 0; u < 4; ++u) {
+          const int i = wv + 16 * h, c = c0 + lane + 64 * u;
+          const bool ok = i < T_ && c < a.chunks;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ld[h][u][q] = a.stats[((size_t)(ok ? i : 0) * 4 + q) * a.chunks + (ok ? c : 0)];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ld[h][u][q] = ok ? ld[h][u][q] : 0.0;
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) nsum[h][q] += ld[h][u][q];
     }
-    if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) nsum[h][q] = wave_sum(nsum[h][q]);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = wv + 16 * h;
+    if (i < T_ && lane == 0) {
+      const float nu = a.var ? nu_from_stats(nsum[h], K) : 1.f;
       s_nu[i] = nu;
       if (tile == 0 && a.nu_out) a.nu_out[i] = nu;
     }

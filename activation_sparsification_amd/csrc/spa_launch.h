@@ -58,7 +58,7 @@ struct DecodeArgs {
   int var;
   // workspace carve-up
   float* partial;            // fused: [splits][t][n_out]
-  double* stats;             // fused: [tiles][splits][t][4]; matrix-core: [chunks][t][4]
+  double* stats;             // fused: [tiles][splits][t][4]; matrix-core: [t][4][chunks]
   unsigned* counters;        // fused: [tiles]
   void* dense;               // matrix-core path: masked rows [t][k] (dtype)
   float* eta_ws;             // [t]
