@@ -36,6 +36,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxTok = 32;
+constexpr int kPruneChan = 256;  // channels per workgroup of the matrix-core path's pruning pass
 
 // ---------------------------------------------------------------------------
 // Split-K hand-off without cache-wide maintenance.  A partial is stored with
@@ -757,14 +758,14 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Pruning pass of the matrix-core decode (t > 4): few token rows, so the
-// work is cut by channels instead of rows.  A workgroup owns 64 channels
-// (64/m blocks) for every token of the call: it stages x_hat = x - eta for
-// them in LDS, forms the channel factors there (the CLACT column energy needs
-// every token of a channel, which this workgroup holds), then one thread per
-// (token, block) scores, selects the top n with the selection network and
-// writes the masked values, the kept positions and its four variance sums.
-// The sums of the blocks are added in block order per (chunk, token); the
-// GEMM folds the chunks into nu.
+// work is cut by channels instead of rows.  A workgroup owns kPruneChan
+// channels (kPruneChan/m blocks) for every token of the call: it stages
+// x_hat = x - eta for them in LDS, forms the channel factors there (the CLACT
+// column energy needs every token of a channel, which this workgroup holds),
+// then one thread per (token, block) scores, selects the top n with the
+// selection network and writes the masked values, the kept positions and its
+// four variance sums.  The sums of the blocks are added in block order per
+// (chunk, token); the matrix-core pass folds the chunks into nu.
 //
 // The masked activations are written in the GEMM's operand order ("fragment
 // order"): for 64-channel step s, token block tb (16 tokens) and window h,
@@ -778,19 +779,27 @@ __device__ __forceinline__ size_t frag_offset(int step, int tb, int ntb, int h, 
 template <int DT, int M>
 __global__ void __launch_bounds__(256) k_prune_cols(DecodeArgs a) {
   using T = typename Dt<DT>::T;
-  constexpr int CH = 64, NB = CH / M;
+  constexpr int CH = kPruneChan, NB = CH / M;
   __shared__ float s_x[kMaxTok][CH + 1];
   __shared__ float s_f[CH];
   __shared__ double s_st[kMaxTok][NB][4];
   const int T_ = a.t, K = a.k;
   const int ntb = (T_ + 15) / 16;
   const int c0 = blockIdx.x * CH;
-  const T* x = static_cast<const T*>(a.x);
-  for (int e = threadIdx.x; e < T_ * CH; e += 256) {
-    const int i = e / CH, c = e % CH, ch = c0 + c;
-    float xh = 0.f;
-    if (ch < K) xh = to_f32<DT>(x[(size_t)i * K + ch]) - (a.eta ? a.eta[i] : 0.f);
-    s_x[i][c] = xh;
+  static_assert(CH == 256, "one channel per thread");
+  {
+    // thread c stages channel c0 + c of every token: all loads issued before
+    // any is used (buffer loads; offsets past the end read zeros)
+    const int c = threadIdx.x, ch = c0 + c;
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), (short)0, T_ * K * 2, kBufferWord3);
+    uint32_t raw[kMaxTok];
+#pragma unroll
+    for (int i = 0; i < kMaxTok; ++i)
+      raw[i] = buffer_load_u16(xr, i < T_ && ch < K ? (uint32_t)(i * K + ch) * 2u : kBufferOutOfRange);
+#pragma unroll
+    for (int i = 0; i < kMaxTok; ++i)
+      if (i < T_) s_x[i][c] = ch < K ? to_f32<DT>((T)raw[i]) - (a.eta ? a.eta[i] : 0.f) : 0.f;
   }
   __syncthreads();
   if ((int)threadIdx.x < CH) {
@@ -808,10 +817,10 @@ __global__ void __launch_bounds__(256) k_prune_cols(DecodeArgs a) {
     s_f[c] = f;
   }
   __syncthreads();
-  const int step = c0 / 64;
   for (int pr = threadIdx.x; pr < T_ * NB; pr += 256) {
     const int i = pr / NB, b = pr % NB;
     const int cb = c0 + b * M;
+    const int step = cb / 64;                        // an m-block lies inside one 64-channel step
     double st[4] = {0.0, 0.0, 0.0, 0.0};
     if (cb < K) {
       float xh[M];
@@ -872,6 +881,7 @@ __global__ void __launch_bounds__(256) k_prune_cols(DecodeArgs a) {
       for (int q = 0; q < 4; ++q) s_st[i][b][q] = st[q];
   }
   if (a.var) {
+    // this chunk's four sums per token, blocks in order
     __syncthreads();
     if ((int)threadIdx.x < T_) {
       double tot[4] = {0.0, 0.0, 0.0, 0.0};
@@ -888,18 +898,23 @@ __global__ void __launch_bounds__(256) k_prune_cols(DecodeArgs a) {
 // Matrix-core decode (t > 4, 16-bit).  With several tokens the union of kept
 // channels covers nearly every row of the weight (each token keeps its own
 // n of every m), so the product runs as a skinny dense GEMM over the masked
-// rows xm[t][k] that the pruning pass writes (zeros at pruned channels):
+// rows xm that the pruning pass writes in fragment order (zeros at pruned
+// channels):
 //   y[i][j] = nu_i * sum_k xm[i][k] w[j][k] + eta_i * s_j.
-// The weight is read row-major: the lane that owns output row j and lane
-// group g loads 32 contiguous bytes of w[j] per 64-channel step, and the lane
-// that owns token i loads the same 32 bytes' worth of xm[i]; the two 16-byte
-// halves are the operands of two mfma_f32_16x16x32 (window h uses channels
-// 64 s + 16 g + 8 h .. +7 of step s in lane group g, for both operands, so
-// the contraction is over every channel exactly once).
-//
-// Workgroup = 16 output rows, 8 waves; wave w takes steps w, w+8, ...; the
-// eight partial 16 x t tiles are added in wave order in LDS (no split across
-// workgroups, no atomics), then the epilogue writes y.
+// Workgroup = 64 output rows x a channel range (split), 8 waves.  The weight
+// rows and the activation fragments stream through a kMmStages-deep LDS ring
+// by direct global->LDS loads (no registers held by loads in flight), one
+// stage = kMmSteps 64-channel steps.  Per stage every wave issues the same
+// loads: four 1 KB weight loads (two rows x 512 contiguous bytes each; the
+// 16-byte chunk c of row r is stored at slot c ^ (r & 15), which makes the
+// fragment reads conflict-free) and one 1 KB activation load per 16-token
+// block.  So a vmcnt wait means "this stage has landed", and one barrier per
+// stage makes it visible and frees the stage refilled next.  Wave w multiplies
+// rows 16 (w % 4) .. +15 with window h = w / 4 of each step (mfma 16x16x32;
+// lane group g of window h holds channels 16 g + 8 h .. +7, the order of the
+// activation fragments); the two windows are added in LDS, then the splits
+// through the ticket.  Each workgroup folds nu from the pruning pass's chunk
+// sums while its first stages load.
 // ---------------------------------------------------------------------------
 template <int DT>
 __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
@@ -911,143 +926,176 @@ __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c)
                                                    0, 0);
 }
 
-// 16 bytes at p when ok, else zeros (a load under the lane mask, never from a select).
-__device__ __forceinline__ uint4 load16_if(const void* p, bool ok) {
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (ok) v = *reinterpret_cast<const uint4*>(p);
-  return v;
-}
-
 __device__ __forceinline__ uint4 zero_unless(const uint4& v, bool ok) {
   return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
 }
 
-// Fragment lane d = m + 16 g (row m, lane group g) takes the 16 bytes that
-// lane 4 m + g loaded: the loads run four lanes per row, so each row's 128-byte
-// line is one cache access instead of four.
-__device__ __forceinline__ uint4 to_fragment(const uint4& v, int src_addr) {
-  return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src_addr, (int)v.x),
-                    (uint32_t)__builtin_amdgcn_ds_bpermute(src_addr, (int)v.y),
-                    (uint32_t)__builtin_amdgcn_ds_bpermute(src_addr, (int)v.z),
-                    (uint32_t)__builtin_amdgcn_ds_bpermute(src_addr, (int)v.w));
-}
+constexpr int kMmStages = 3, kMmRows = 64, kMmSteps = 4;   // ring stages of kMmSteps 64-channel steps
+
+template <int TT>
+constexpr int mm_stage_bytes() { return kMmRows * 128 * kMmSteps + TT * 2048 * kMmSteps; }
 
 template <int DT, int TT>
-__global__ void __launch_bounds__(1024) k_decode_mm(DecodeArgs a) {
+__global__ void __launch_bounds__(512) k_decode_mm(DecodeArgs a) {
   using T = typename Dt<DT>::T;
-  constexpr int RG = 4, KG = 4, U = 2, RN = 16 * RG;   // 16 waves: 4 row groups x 4 k groups
-  __shared__ float s_red[KG][RG][TT][16][17];
+  constexpr int NS = kMmStages, RN = kMmRows, SU = kMmSteps, PER = 4 + TT;
+  constexpr int RB = 128 * SU;                             // bytes of one weight row per stage
+  constexpr int SW = RN * RB, SS = mm_stage_bytes<TT>();
+  static_assert(RN * RB / 1024 == 4 * 8, "four 1 KB weight loads per wave");
+  __shared__ __attribute__((aligned(16))) unsigned char s_ring[NS * SS];
   __shared__ float s_nu[kMaxTok];
   __shared__ int s_flag;
   const int T_ = a.t, K = a.k, N = a.n_out;
   const int tile = blockIdx.x % a.tiles, split = blockIdx.x / a.tiles;
   const int n0 = tile * RN;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int rg = wv % RG, kg = wv / RG;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  // loads: lane s reads row (or token) s / 4, channels 16 (s % 4) .. +15 of each step
-  const int lr = lane >> 2, lq = lane & 3;
-  const int src_addr = 4 * (4 * l16 + g);
-  const int row = min(n0 + 16 * rg + lr, N - 1);
-  const T* wrow = static_cast<const T*>(a.w) + (size_t)row * K + 16 * lq;
-  // masked activations, already in fragment order (one coalesced 1 KB run per fragment)
-  const uint16_t* xf = static_cast<const uint16_t*>(a.dense);
+  const int rf = wv & 3, hw = wv >> 2;                     // row fragment, window
   const int ntb = (T_ + 15) / 16;
-  bool tok_ok[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) tok_ok[tt] = 16 * tt + l16 < T_;
-  f32x4 acc[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // this workgroup's 64-channel steps; the k groups interleave within them.
-  // Rows of w lie k*2 bytes apart, so workgroups walking k in step would all
-  // hit the same few memory channels at once; each tile therefore starts its
-  // walk at a different step (a rotation of the same set of steps).
+  // this workgroup's 64-channel steps, taken SU at a time ("stages"); each
+  // tile starts its walk at a different stage (rows of w lie k*2 bytes apart,
+  // so workgroups walking k in step would all hit the same few memory
+  // channels at once)
   const int nsteps = (K + 63) / 64;
   const int sps = a.k_len / 64;
   const int s_beg = split * sps, s_end = min(nsteps, s_beg + sps);
   const int span = s_end - s_beg;
-  const int rot = span > 0 ? (int)(((unsigned)tile * 37u) % (unsigned)span) : 0;
-  // two register batches of U steps: the next batch is in flight while the
-  // current one is permuted and multiplied
-  uint4 wa[2][U][2], xb[2][U][TT][2];
-  bool okb[2][U][TT];
-#define SPA_MM_LOAD(B, L0)                                                        \
-  do {                                                                            \
-    _Pragma("unroll") for (int u = 0; u < U; ++u) {                               \
-      const int ls = (L0) + KG * u;                                               \
-      int st = ls + rot;                                                          \
-      st = s_beg + (st >= span ? st - span : st);                                 \
-      const bool in = ls < span;                                                  \
-      const int stc = in ? st : s_beg;             /* an in-bounds step */        \
-      const int off = stc * 64;                                                   \
-      const int offw = off + 16 * lq < K ? off : 0;                               \
-      const bool okx = in && off + 16 * g < K;                                    \
-      /* unconditional loads (exact wait counting); the weight needs no mask:   \
-         its partner activation is zero wherever the step is not this one's */  \
-      wa[B][u][0] = *reinterpret_cast<const uint4*>(wrow + offw);                 \
-      wa[B][u][1] = *reinterpret_cast<const uint4*>(wrow + offw + 8);             \
-      _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) {                         \
-        okb[B][u][tt] = okx && tok_ok[tt];         /* applied when multiplied */  \
-        xb[B][u][tt][0] = *reinterpret_cast<const uint4*>(xf + frag_offset(stc, tt, ntb, 0, lane)); \
-        xb[B][u][tt][1] = *reinterpret_cast<const uint4*>(xf + frag_offset(stc, tt, ntb, 1, lane)); \
-      }                                                                           \
-    }                                                                             \
-  } while (0)
-#define SPA_MM_COMPUTE(B)                                                                    \
-  do {                                                                                       \
-    _Pragma("unroll") for (int u = 0; u < U; ++u) {                                          \
-      const uint4 w0 = to_fragment(wa[B][u][0], src_addr), w1 = to_fragment(wa[B][u][1], src_addr); \
-      _Pragma("unroll") for (int tt = 0; tt < TT; ++tt) {                                    \
-        acc[tt] = mfma16<DT>(w0, zero_unless(xb[B][u][tt][0], okb[B][u][tt]), acc[tt]);      \
-        acc[tt] = mfma16<DT>(w1, zero_unless(xb[B][u][tt][1], okb[B][u][tt]), acc[tt]);      \
-      }                                                                                      \
-    }                                                                                        \
-  } while (0)
-  // An even number of batches, so the loop body has no exit in the middle and
-  // the compiler can count the loads in flight exactly; steps past the span
-  // re-read an in-bounds step and multiply zeros.
-  constexpr int STRIDE = KG * U;
-  const int nbatch = (span - kg + STRIDE - 1) / STRIDE;
-  const int npair = (nbatch + 1) / 2;
-  SPA_MM_LOAD(0, kg);
-  for (int pi = 0; pi < npair; ++pi) {
-    const int l0 = kg + 2 * STRIDE * pi;
-    SPA_MM_LOAD(1, l0 + STRIDE);
-    SPA_MM_COMPUTE(0);
-    SPA_MM_LOAD(0, l0 + 2 * STRIDE);
-    SPA_MM_COMPUTE(1);
+  const int nst = (span + SU - 1) / SU;
+  const int rot = nst > 0 ? (int)(((unsigned)tile * 37u) % (unsigned)nst) : 0;
+  auto stage_of = [&](int i) {                             // first step of stage i
+    const int v = i + rot;
+    return s_beg + SU * (v >= nst ? v - nst : v);
+  };
+
+  // load sources.  Weight: wave w, load j reads 512 contiguous bytes (4 steps)
+  // of tile row dr = 8 w + 2 j + lane / 32; lane position p = lane % 32 of the
+  // row's LDS run holds channel chunk p ^ (dr & 15) of the stage, which makes
+  // the fragment reads (16 rows, one chunk) conflict-free.  Activations: the
+  // stage's SU steps x TT token blocks are one contiguous run of the
+  // fragment-order buffer, TT 1 KB loads per wave.
+  const int dp = lane & 31;
+  const T* wbase = static_cast<const T*>(a.w) + (size_t)n0 * K;
+  const uint16_t* xf = static_cast<const uint16_t*>(a.dense);
+  const uint32_t ring = lds_addr(s_ring);
+  auto issue = [&](int i) {                                // stage i into slot i % NS
+    const int st0 = stage_of(i);
+    const uint32_t q = ring + (uint32_t)(i % NS) * SS;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int dr = 8 * wv + 2 * j + (lane >> 5);
+      const uint32_t rbytes = (uint32_t)(min(n0 + dr, N - 1) - n0) * (uint32_t)K * 2u;
+      const int kc = st0 * 64 + 8 * (dp ^ (dr & 15));       // chunks past k read chunk 0 (their activations are zero)
+      lds_dma16(wbase, rbytes + (uint32_t)(kc < K ? kc : 0) * 2u, q + (uint32_t)(wv * 4 + j) * 1024u);
+    }
+    // steps past this split or past k: any in-bounds activations (multiplied as zeros)
+    const int stx = min(st0, nsteps - SU > 0 ? nsteps - SU : 0);
+#pragma unroll
+    for (int tb = 0; tb < TT; ++tb)
+      lds_dma16(xf, (uint32_t)(frag_offset(stx, 0, ntb, 0, 0) * 2) + (uint32_t)(wv * TT + tb) * 1024u + (uint32_t)lane * 16u,
+                q + SW + (uint32_t)(wv * TT + tb) * 1024u);
+  };
+
+  f32x4 acc[TT];
+#pragma unroll
+  for (int tb = 0; tb < TT; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool tok_ok[TT];
+#pragma unroll
+  for (int tb = 0; tb < TT; ++tb) tok_ok[tb] = 16 * tb + l16 < T_;
+  const int wr = 16 * rf + l16;                            // this lane's fragment row
+  // window h of lane group g is channels 16 g + 8 h .. +7 of a step (the
+  // activation fragments' order): weight chunk 8 j + 2 g + h of step j
+  const uint32_t xfrag = (uint32_t)SW + (uint32_t)hw * 1024u + (uint32_t)lane * 16u;
+
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < nst) issue(i);
+  // nu of tokens w, w+8, w+16, w+24 (wave w) from the pruning pass's chunk
+  // sums [token][sum][chunk], while the first stages load.  Lane l takes
+  // (token w + 8 (l / 16), sum (l / 4) % 4) and chunks l % 4, l % 4 + 4, ...
+  // (all loads in flight), then a fixed two-step butterfly over the four
+  // parts: the same result in every workgroup
+  if (a.var) {
+    const int pr = lane >> 2, part = lane & 3;
+    const int i = wv + 8 * (pr >> 2), q = pr & 3;
+    double sacc = 0.0;
+    for (int c0 = 0; c0 < a.chunks; c0 += 64) {
+      double ld[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int c = c0 + part + 4 * u;
+        const bool ok = i < T_ && c < a.chunks;
+        ld[u] = a.stats[((size_t)(ok ? i : 0) * 4 + q) * a.chunks + (ok ? c : 0)];
+        ld[u] = ok ? ld[u] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) sacc += ld[u];
+    }
+    sacc += __shfl_xor(sacc, 1, kWave);
+    sacc += __shfl_xor(sacc, 2, kWave);
+    double sums[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) sums[qq] = __shfl(sacc, ((lane & 3) * 4 + qq) * 4, kWave);   // lane l < 4: token slot l
+    if (lane < 4) {
+      const int it = wv + 8 * lane;
+      if (it < T_) {
+        const float nu = nu_from_stats(sums, K);
+        s_nu[it] = nu;
+        if (blockIdx.x == 0 && a.nu_out) a.nu_out[it] = nu;
+      }
+    }
+  } else if ((int)threadIdx.x < T_) {
+    s_nu[threadIdx.x] = 1.f;
+    if (blockIdx.x == 0 && a.nu_out) a.nu_out[threadIdx.x] = 1.f;
   }
-#undef SPA_MM_LOAD
-#undef SPA_MM_COMPUTE
-  // D register r of lane (l16, g): output row 16 rg + 4g + r, token 16 tt + l16
+  for (int i = 0; i < nst; ++i) {
+    if (i + NS - 2 < nst) wait_vm<(NS - 2) * PER>(1);     // the newer stages may still be in flight
+    else wait_vm<0>(0);                                    // the last stages: everything issued has landed
+    bare_barrier();
+    if (i + NS - 1 < nst) issue(i + NS - 1);
+    const unsigned char* stg = s_ring + (size_t)(i % NS) * SS;
+    const int st0 = stage_of(i);
+    const int stx = min(st0, nsteps - SU > 0 ? nsteps - SU : 0);
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
+    for (int j = 0; j < SU; ++j) {
+      const int st = st0 + j;
+      const bool kin = st < s_end && st * 64 + 16 * g + 8 * hw < K;
+      const uint4 wfr = *reinterpret_cast<const uint4*>(stg + wr * RB + (((8 * j + 2 * g + hw) ^ (wr & 15)) * 16));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s_red[kg][rg][tt][4 * g + r][l16] = acc[tt][r];
+      for (int tb = 0; tb < TT; ++tb) {
+        // the activation run starts at step stx: step st sits (st - stx) steps in
+        const int jx = st - stx;
+        const bool in = kin && jx >= 0 && jx < SU;
+        const uint4 xv = *reinterpret_cast<const uint4*>(stg + xfrag + ((in ? jx : 0) * TT + tb) * 2048);
+        acc[tb] = mfma16<DT>(wfr, zero_unless(xv, in && tok_ok[tb]), acc[tb]);
+      }
+    }
+  }
+  // D register r of lane (l16, g): output row 16 rf + 4g + r, token 16 tb + l16;
+  // the two windows meet in LDS (the ring is free once every wave is past it)
   __syncthreads();
-  // this workgroup's sum over its k groups, in k-group order
-  auto wg_sum = [&](int j, int tok) {
-    float v = 0.f;
+  float (*s_red)[4][TT][16][17] = reinterpret_cast<float (*)[4][TT][16][17]>(s_ring);
 #pragma unroll
-    for (int q = 0; q < KG; ++q) v += s_red[q][j / 16][tok / 16][j % 16][tok % 16];
-    return v;
+  for (int tb = 0; tb < TT; ++tb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_red[hw][rf][tb][4 * g + r][l16] = acc[tb][r];
+  __syncthreads();
+  auto wg_sum = [&](int j, int tok) {                      // window 0, then window 1
+    return s_red[0][j / 16][tok / 16][j % 16][tok % 16] + s_red[1][j / 16][tok / 16][j % 16][tok % 16];
   };
   const int rows = min(RN, N - n0);
   if (a.splits > 1) {
-    for (int e = threadIdx.x; e < rows * T_; e += 1024) {
+    for (int e = threadIdx.x; e < rows * T_; e += 512) {
       const int tok = e / rows, j = e % rows;
       coherent_store(&a.partial[((size_t)split * T_ + tok) * N + n0 + j], wg_sum(j, tok));
     }
     if (!arrive_last(&a.counters[tile], a.splits, &s_flag)) return;
   }
   // Final sums of this tile (the last workgroup when split).
-  float v[2] = {0.f, 0.f};
-  double nsum[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = threadIdx.x + 1024 * q;
+  for (int q = 0; q < 4; ++q) {
+    const int e = threadIdx.x + 512 * q;
     if (e < rows * T_) {
       const int tok = e / rows, j = e % rows;
       if (a.splits > 1) {   // every split's partial in flight before the adds, split order
@@ -1066,51 +1114,11 @@ __global__ void __launch_bounds__(1024) k_decode_mm(DecodeArgs a) {
       }
     }
   }
-  // nu of token i from the pruning pass's per-chunk sums (laid out
-  // [token][sum][chunk]): wave w takes tokens w and w + 16, lane l adds chunks
-  // l, l+64, l+128, l+192 (all of a pass's loads in flight before the adds,
-  // 512 contiguous bytes per load instruction), then a fixed butterfly: the
-  // same result in every workgroup
-  if (a.var) {
-    for (int c0 = 0; c0 < a.chunks; c0 += 256) {
-      double ld[2][4][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = wv + 16 * h, c = c0 + lane + 64 * u;
-          const bool ok = i < T_ && c < a.chunks;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) ld[h][u][q] = a.stats[((size_t)(ok ? i : 0) * 4 + q) * a.chunks + (ok ? c : 0)];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) ld[h][u][q] = ok ? ld[h][u][q] : 0.0;
-        }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) nsum[h][q] += ld[h][u][q];
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) nsum[h][q] = wave_sum(nsum[h][q]);
-  }
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int i = wv + 16 * h;
-    if (i < T_ && lane == 0) {
-      const float nu = a.var ? nu_from_stats(nsum[h], K) : 1.f;
-      s_nu[i] = nu;
-      if (tile == 0 && a.nu_out) a.nu_out[i] = nu;
-    }
-  }
   __syncthreads();
   T* y = static_cast<T*>(a.y);
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = threadIdx.x + 1024 * q;
+  for (int q = 0; q < 4; ++q) {
+    const int e = threadIdx.x + 512 * q;
     if (e < rows * T_) {
       const int tok = e / rows, j = e % rows, col = n0 + j;
       float out = s_nu[tok] * v[q];
@@ -1205,8 +1213,9 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
     const int sps = (nsteps + sp - 1) / sp;
     p.k_len = sps * 64;
     p.splits = (nsteps + sps - 1) / sps;
-    p.chunks = (k + 63) / 64;
-    const size_t o_dense = carve((size_t)nsteps * ((t + 15) / 16) * 2048);   // fragment order
+    p.chunks = (k + kPruneChan - 1) / kPruneChan;
+    // fragment order; at least kMmSteps steps, since the matrix-core pass reads them kMmSteps at a time
+    const size_t o_dense = carve((size_t)(nsteps > kMmSteps ? nsteps : kMmSteps) * ((t + 15) / 16) * 2048);
     const size_t o_stats = carve(var ? (size_t)p.chunks * t * 4 * 8 : 0);
     const size_t o_eta = carve((size_t)t * 4);
     const size_t o_part = carve(p.splits > 1 ? (size_t)p.splits * t * n_out * 4 : 0);
@@ -1271,9 +1280,9 @@ static hipError_t decode_dt(DecodeArgs& a, hipStream_t st) {
     if (hipError_t e = hipGetLastError()) return e;
     // ... then one pass over the row-major weight on the matrix cores
     if (a.t <= 16)
-      hipLaunchKernelGGL((k_decode_mm<DT, 1>), dim3(a.tiles * a.splits), dim3(1024), 0, st, a);
+      hipLaunchKernelGGL((k_decode_mm<DT, 1>), dim3(a.tiles * a.splits), dim3(512), 0, st, a);
     else
-      hipLaunchKernelGGL((k_decode_mm<DT, 2>), dim3(a.tiles * a.splits), dim3(1024), 0, st, a);
+      hipLaunchKernelGGL((k_decode_mm<DT, 2>), dim3(a.tiles * a.splits), dim3(512), 0, st, a);
   }
   return hipGetLastError();
 }

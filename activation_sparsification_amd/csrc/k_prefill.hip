@@ -59,50 +59,6 @@ __device__ __forceinline__ f32x16 mfma32(const typename Frag<DT>::V8& a, const t
   else return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------------------
-// Direct global->LDS loads and the waits that order them.
-// ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void;
-
-// LDS byte address of a __shared__ pointer.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_void*)p;
-}
-// Lane l's 16 (or 4) bytes at sbase + voff land at LDS address lds + 16 l
-// (4 l); sbase and lds are wave-uniform.  Issued from asm so that the
-// compiler does not add waits of its own before later LDS reads: the kernels
-// order these copies with explicit vmcnt waits and the workgroup barrier.
-// No register is written, so nothing but LDS bytes is left in flight.  An
-// LDS-DMA reading M0 needs one wait state after the M0 write (s_nop 0).
-__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
-               : "m0");
-}
-__device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
-               : "m0");
-}
-
-// Wait until at most KEEP of this wave's vector-memory operations are
-// outstanding (keep != 0), or none (keep == 0).
-template <int KEEP>
-__device__ __forceinline__ void wait_vm(int keep) {
-  static_assert(KEEP >= 0 && KEEP < 16, "vmcnt field");
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (keep) __builtin_amdgcn_s_waitcnt(0x0F70 | KEEP);
-  else __builtin_amdgcn_s_waitcnt(0x0F70);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-// Workgroup barrier after this wave's own LDS reads have completed (the stage
-// they read is refilled by direct loads right after the barrier).  Vector
-// memory is ordered by the explicit wait_vm before it, not here.
-__device__ __forceinline__ void bare_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD gets a
 // contiguous run of tile indices.  Tiles are numbered in groups of (up to) 8
 // token tiles times every weight tile, token tiles fastest, so an XCD's run

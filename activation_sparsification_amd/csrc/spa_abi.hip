@@ -176,7 +176,9 @@ spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, c
   fix(a.stats);
   fix(a.counters);
   fix(a.eta_ws);
-  if (t > 4 && w->dtype != SPA_F32) fix(a.dense);   // matrix-core path (its offset is 0)
+  if (t > 4 && w->dtype != SPA_F32) {                // matrix-core path (the dense offset is 0)
+    fix(a.dense);
+  }
   a.x = x;
   a.wt = w->wt;
   a.w = w->w;

@@ -65,6 +65,53 @@ __device__ __forceinline__ uint32_t buffer_load_u32(__amdgpu_buffer_rsrc_t r, ui
 }
 
 // ---------------------------------------------------------------------------
+// Direct global->LDS loads and the waits that order them.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+// Lane l's 16 (or 4) bytes at sbase + voff land at LDS address lds + 16 l
+// (4 l); sbase and lds are wave-uniform.  Issued from asm so that the
+// compiler does not add waits of its own before later LDS reads: the kernels
+// order these copies with explicit vmcnt waits and the workgroup barrier.
+// No register is written, so nothing but LDS bytes is left in flight.  An
+// LDS-DMA reading M0 needs one wait state after the M0 write (s_nop 0).
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
+               : "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
+               : "m0");
+}
+
+// Wait until at most KEEP of this wave's vector-memory operations are
+// outstanding (keep != 0), or none (keep == 0).  The gfx9 s_waitcnt field:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at
+// their maxima (no wait).
+template <int KEEP>
+__device__ __forceinline__ void wait_vm(int keep) {
+  static_assert(KEEP >= 0 && KEEP < 64, "vmcnt field");
+  constexpr int kEnc = 0x0F70 | (KEEP & 15) | ((KEEP >> 4) << 14);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (keep) __builtin_amdgcn_s_waitcnt(kEnc);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Workgroup barrier after this wave's own LDS reads have completed (the stage
+// they read is refilled by direct loads right after the barrier).  Vector
+// memory is ordered by the explicit wait_vm before it, not here.
+__device__ __forceinline__ void bare_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// ---------------------------------------------------------------------------
 // The mask arithmetic.  Every helper is a single IEEE operation so that the
 // GPU reproduces the reference definition bit for bit.
 // ---------------------------------------------------------------------------
