@@ -914,7 +914,7 @@ __global__ void __launch_bounds__(256) k_prune_cols(DecodeArgs a) {
 // lane group g of window h holds channels 16 g + 8 h .. +7, the order of the
 // activation fragments); the two windows are added in LDS, then the splits
 // through the ticket.  Each workgroup folds nu from the pruning pass's chunk
-// sums while its first stages load.
+// sums, loaded ahead of its first stage.
 // ---------------------------------------------------------------------------
 template <int DT>
 __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
@@ -1008,46 +1008,26 @@ __global__ void __launch_bounds__(512) k_decode_mm(DecodeArgs a) {
   // activation fragments' order): weight chunk 8 j + 2 g + h of step j
   const uint32_t xfrag = (uint32_t)SW + (uint32_t)hw * 1024u + (uint32_t)lane * 16u;
 
+  // nu of tokens w, w+8, w+16, w+24 (wave w) from the pruning pass's chunk
+  // sums [token][sum][chunk]: lane l takes (token w + 8 (l / 16), sum
+  // (l / 4) % 4) and chunks l % 4, l % 4 + 4, ...  Its loads go out before the
+  // first stage's (the stage waits then cover them) and are added after the
+  // main loop; a fixed two-step butterfly joins the four parts, the same in
+  // every workgroup.
+  const int npr = lane >> 2, npart = lane & 3;
+  const int nti = wv + 8 * (npr >> 2), nq = npr & 3;
+  double nld[16];
+  const bool nu_one_pass = a.chunks <= 64;
+  if (a.var && nu_one_pass) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int c = npart + 4 * u;
+      const bool ok = nti < T_ && c < a.chunks;
+      nld[u] = a.stats[((size_t)(ok ? nti : 0) * 4 + nq) * a.chunks + (ok ? c : 0)];
+    }
+  }
   for (int i = 0; i < NS - 1; ++i)
     if (i < nst) issue(i);
-  // nu of tokens w, w+8, w+16, w+24 (wave w) from the pruning pass's chunk
-  // sums [token][sum][chunk], while the first stages load.  Lane l takes
-  // (token w + 8 (l / 16), sum (l / 4) % 4) and chunks l % 4, l % 4 + 4, ...
-  // (all loads in flight), then a fixed two-step butterfly over the four
-  // parts: the same result in every workgroup
-  if (a.var) {
-    const int pr = lane >> 2, part = lane & 3;
-    const int i = wv + 8 * (pr >> 2), q = pr & 3;
-    double sacc = 0.0;
-    for (int c0 = 0; c0 < a.chunks; c0 += 64) {
-      double ld[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int c = c0 + part + 4 * u;
-        const bool ok = i < T_ && c < a.chunks;
-        ld[u] = a.stats[((size_t)(ok ? i : 0) * 4 + q) * a.chunks + (ok ? c : 0)];
-        ld[u] = ok ? ld[u] : 0.0;
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) sacc += ld[u];
-    }
-    sacc += __shfl_xor(sacc, 1, kWave);
-    sacc += __shfl_xor(sacc, 2, kWave);
-    double sums[4];
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) sums[qq] = __shfl(sacc, ((lane & 3) * 4 + qq) * 4, kWave);   // lane l < 4: token slot l
-    if (lane < 4) {
-      const int it = wv + 8 * lane;
-      if (it < T_) {
-        const float nu = nu_from_stats(sums, K);
-        s_nu[it] = nu;
-        if (blockIdx.x == 0 && a.nu_out) a.nu_out[it] = nu;
-      }
-    }
-  } else if ((int)threadIdx.x < T_) {
-    s_nu[threadIdx.x] = 1.f;
-    if (blockIdx.x == 0 && a.nu_out) a.nu_out[threadIdx.x] = 1.f;
-  }
   for (int i = 0; i < nst; ++i) {
     if (i + NS - 2 < nst) wait_vm<(NS - 2) * PER>(1);     // the newer stages may still be in flight
     else wait_vm<0>(0);                                    // the last stages: everything issued has landed
@@ -1071,6 +1051,32 @@ __global__ void __launch_bounds__(512) k_decode_mm(DecodeArgs a) {
       }
     }
   }
+  if (a.var) {
+    double sacc = 0.0;
+    if (nu_one_pass) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) sacc += (nti < T_ && npart + 4 * u < a.chunks) ? nld[u] : 0.0;
+    } else {
+      for (int c = npart; c < a.chunks; c += 4)
+        if (nti < T_) sacc += a.stats[((size_t)nti * 4 + nq) * a.chunks + c];
+    }
+    sacc += __shfl_xor(sacc, 1, kWave);
+    sacc += __shfl_xor(sacc, 2, kWave);
+    double sums[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) sums[qq] = __shfl(sacc, ((lane & 3) * 4 + qq) * 4, kWave);   // lane l < 4: token slot l
+    if (lane < 4) {
+      const int it = wv + 8 * lane;
+      if (it < T_) {
+        const float nu = nu_from_stats(sums, K);
+        s_nu[it] = nu;
+        if (blockIdx.x == 0 && a.nu_out) a.nu_out[it] = nu;
+      }
+    }
+  } else if ((int)threadIdx.x < T_) {
+    s_nu[threadIdx.x] = 1.f;
+    if (blockIdx.x == 0 && a.nu_out) a.nu_out[threadIdx.x] = 1.f;
+  }
   // D register r of lane (l16, g): output row 16 rf + 4g + r, token 16 tb + l16;
   // the two windows meet in LDS (the ring is free once every wave is past it)
   __syncthreads();
@@ -1092,26 +1098,34 @@ __global__ void __launch_bounds__(512) k_decode_mm(DecodeArgs a) {
     if (!arrive_last(&a.counters[tile], a.splits, &s_flag)) return;
   }
   // Final sums of this tile (the last workgroup when split).
+  // this thread's (row, token) pairs e = thread + 512 q; with splits, every
+  // pair's partials of a batch of 8 splits are in flight before the adds
+  // (split order)
   float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.splits > 1) {
+    const size_t stride = (size_t)T_ * N;
+    for (int s0 = 0; s0 < a.splits; s0 += 8) {
+      float part[4][8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = threadIdx.x + 512 * q;
-    if (e < rows * T_) {
-      const int tok = e / rows, j = e % rows;
-      if (a.splits > 1) {   // every split's partial in flight before the adds, split order
-        const float* pp = a.partial + (size_t)tok * N + n0 + j;
-        const size_t stride = (size_t)T_ * N;
-        for (int s0 = 0; s0 < a.splits; s0 += 8) {
-          float part[8];
+      for (int q = 0; q < 4; ++q) {
+        const int e = threadIdx.x + 512 * q;
+        const bool ok = e < rows * T_;
+        const float* pp = a.partial + (size_t)(ok ? e / rows : 0) * N + n0 + (ok ? e % rows : 0);
 #pragma unroll
-          for (int s2 = 0; s2 < 8; ++s2) part[s2] = s0 + s2 < a.splits ? coherent_load(pp + (s0 + s2) * stride) : 0.f;
-#pragma unroll
-          for (int s2 = 0; s2 < 8; ++s2)
-            if (s0 + s2 < a.splits) v[q] += part[s2];
-        }
-      } else {
-        v[q] = wg_sum(j, tok);
+        for (int s2 = 0; s2 < 8; ++s2)
+          part[q][s2] = ok && s0 + s2 < a.splits ? coherent_load(pp + (s0 + s2) * stride) : 0.f;
       }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2)
+          if (s0 + s2 < a.splits) v[q] += part[q][s2];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = threadIdx.x + 512 * q;
+      if (e < rows * T_) v[q] = wg_sum(e % rows, e / rows);
     }
   }
   __syncthreads();
