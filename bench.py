@@ -168,8 +168,20 @@ class Workload:
         torch.cuda.synchronize()
         gpu_ms = ev0.elapsed_time(ev1)
         sleep_ms = ev_s.elapsed_time(ev0)
+        # per-call durations in a second pass: an event after every call (the
+        # events add a little to each step, so the headline is the pass above)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda._sleep(int(2e6) + 60000 * steps)
+        evs[0].record()
+        for i in range(steps):
+            calls[i % len(calls)]()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(steps))
+        pct = lambda q: per[min(len(per) - 1, int(q * (len(per) - 1) + 0.5))]
         return gpu_ms / steps, dict(host_enqueue_ms=host_s * 1e3, sleep_ms=sleep_ms,
-                                    gpu_bound=sleep_ms > host_s * 1e3)
+                                    gpu_bound=sleep_ms > host_s * 1e3,
+                                    per_call_us_event_pass=dict(median=pct(0.5), p10=pct(0.1), p90=pct(0.9)))
 
 
 def measure(name, steps, warmup):
@@ -205,25 +217,48 @@ def cpu_baseline(name, budget_s=12.0):
     f = O.channel_factor(w32, spec.alpha) if spec.score == "weight" else None  # weight prep: off the timed path
     s = O.row_sum(w32)
     # one step = oracle prune + linear of the step's tokens
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        pr = O.prune(x32, spec.dtype, spec.n, spec.m, score=spec.score, f=f, shift_mode=spec.shift,
-                     var_rescale=spec.var_rescale)
-        O.linear(pr, w32, s)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 200:
-            break
+    def run(budget):
+        t_prune = t_lin = 0.0
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            a = time.perf_counter()
+            pr = O.prune(x32, spec.dtype, spec.n, spec.m, score=spec.score, f=f, shift_mode=spec.shift,
+                         var_rescale=spec.var_rescale)
+            b_ = time.perf_counter()
+            O.linear(pr, w32, s)
+            t_prune += b_ - a
+            t_lin += time.perf_counter() - b_
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget or n >= 200:
+                return pr, n, el, t_prune / n, t_lin / n
+    pr, n, el, prune_s, lin_s = run(budget_s)
     per_step = el / n
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            _, n1, el1, _, _ = run(budget_s / 3)
+        single = el1 / n1
+    except Exception:  # noqa: BLE001
+        pass
     rows = int(pr["keep"].any(axis=0).sum())
     el_b = x.element_size()
     b = rows * spec.n_out * el_b + spec.t * spec.k * el_b + spec.t * spec.n_out * el_b
     b += (spec.k * 4 if spec.score == "weight" else 0) + (spec.n_out * 4 if spec.shift != "none" else 0)
     cores = len(os.sched_getaffinity(0))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return dict(value=b / per_step / 1e9, unit="GB/s", cores=blas_threads or cores, host_cores=cores,
                 kind="oracle", sample=f"{n} steps of the {name} workload (t={spec.t}), oracle prune + float64 "
-                f"linear per step, {el:.1f} s", s_per_step=per_step)
+                f"linear per step, {el:.1f} s", s_per_step=per_step, prune_s_per_step=prune_s,
+                linear_s_per_step=lin_s, cpu_model=model,
+                single_thread=None if single is None else dict(value=b / single / 1e9, s_per_step=single))
 
 
 def main():
