@@ -15,23 +15,32 @@
 
 namespace spa {
 
+// One segment of a row as raw 16-byte words through a buffer descriptor over
+// the row (an offset past the row reads zeros, so the load needs no branch).
 template <int DT, int SEG>
-__device__ __forceinline__ void load_segment(const typename Dt<DT>::T* __restrict__ p, float (&v)[SEG]) {
+struct RawSeg {
+  static constexpr int NQ = SEG * Dt<DT>::bytes / 16;
+  uint4 q[NQ];
+};
+template <int DT, int SEG>
+__device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t r, int seg, bool ok, RawSeg<DT, SEG>& out) {
+#pragma unroll
+  for (int i = 0; i < RawSeg<DT, SEG>::NQ; ++i)
+    out.q[i] = buffer_load16(r, ok ? (uint32_t)(seg * SEG * Dt<DT>::bytes + 16 * i) : kBufferOutOfRange);
+}
+template <int DT, int SEG>
+__device__ __forceinline__ void unpack_raw(const RawSeg<DT, SEG>& in, float (&v)[SEG]) {
   if constexpr (DT == SPA_F32) {
-    const float4* q = reinterpret_cast<const float4*>(p);
 #pragma unroll
     for (int i = 0; i < SEG / 4; ++i) {
-      const float4 f = q[i];
-      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+      v[4 * i] = __uint_as_float(in.q[i].x); v[4 * i + 1] = __uint_as_float(in.q[i].y);
+      v[4 * i + 2] = __uint_as_float(in.q[i].z); v[4 * i + 3] = __uint_as_float(in.q[i].w);
     }
   } else {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
 #pragma unroll
-    for (int i = 0; i < SEG / 8; ++i) {
-      const uint4 u = q[i];
+    for (int i = 0; i < SEG / 8; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[8 * i + e] = elem16<DT>(u, e);
-    }
+      for (int e = 0; e < 8; ++e) v[8 * i + e] = elem16<DT>(in.q[i], e);
   }
 }
 
@@ -106,9 +115,14 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
   // copy-out below stays convergent.
   const int iters = (nseg + 255) / 256;
   // the first pass's segment is requested before the shift is known; when the
-  // whole row is one pass, the shift is summed from these same registers
+  // whole row is one pass, the shift is summed from these same registers.
+  // Each pass then requests the next pass's segment before its own work.
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(xr), (short)0, a.k * (int)sizeof(T), kBufferWord3);
+  RawSeg<DT, SEG> raw_next;
+  load_raw<DT, SEG>(xrs, (int)threadIdx.x, (int)threadIdx.x < nseg, raw_next);
   float xv0[SEG];
-  if ((int)threadIdx.x < nseg) load_segment<DT, SEG>(xr + (size_t)threadIdx.x * SEG, xv0);
+  unpack_raw<DT, SEG>(raw_next, xv0);
   float eta = 0.f;
   if (a.shift_mean) {
     if (iters == 1) {
@@ -139,14 +153,15 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
     const bool active = seg < nseg;
     uint32_t keepbits[BPS];
     float xh[SEG];
-    if (active) {
-      float xv[SEG];
-      if (it == 0) {
+    float xv[SEG];
+    if (it == 0) {
 #pragma unroll
-        for (int j = 0; j < SEG; ++j) xv[j] = xv0[j];
-      } else {
-        load_segment<DT, SEG>(xr + (size_t)seg * SEG, xv);
-      }
+      for (int j = 0; j < SEG; ++j) xv[j] = xv0[j];
+    } else {
+      unpack_raw<DT, SEG>(raw_next, xv);
+    }
+    if (it + 1 < iters) load_raw<DT, SEG>(xrs, seg + 256, seg + 256 < nseg, raw_next);
+    if (active) {
 #pragma unroll
       for (int j = 0; j < SEG; ++j) xh[j] = xv[j] - eta;
       float sc[SEG];

@@ -122,6 +122,29 @@ for dt in ["bf16", "f16"]:
                                                       dtype=dt, n=n, m=m, score="magnitude", shift="token_mean",
                                                       var_rescale=False))
 DECODE_CASES.append(wl.SPECS["tiny"].with_(name="tiny_f32_t8", t=8, shift="token_mean"))
+# one token, outputs of at least eight 512-column tiles (the wide one-token kernel):
+# a ragged last tile, a channel split whose last wave is partial, more kept rows
+# per wave than one batch of loads (3:4), several channel rounds per workgroup,
+# every block width, both 16-bit types and every score and shift
+T1_WIDE = [
+    ("t1w_ragged_tile", dict(k=4096, n_out=4104)),
+    ("t1w_partial_wave", dict(k=1040, n_out=4096)),
+    ("t1w_3of4", dict(k=8192, n_out=4096, n=3, m=4, score="magnitude")),
+    ("t1w_rounds", dict(k=32768, n_out=4096, shift="none")),
+    ("t1w_1of8_given", dict(k=2048, n_out=4608, n=1, m=8, shift="given")),
+    ("t1w_f16_clact_var", dict(k=2048, n_out=4096, n=16, m=32, dtype="f16", score="clact", shift="none",
+                               var_rescale=True)),
+    ("t1w_f16_2of4_var", dict(k=1024, n_out=5120, n=2, m=4, dtype="f16", score="magnitude", var_rescale=True)),
+]
+for nm, kw in T1_WIDE:
+    DECODE_CASES.append(wl.SPECS["decode"].with_(name=nm, t=1, **kw))
+# matrix-core path: fewer 64-channel steps than one ring stage, a ragged last step
+# (k % 64 = 16), a ragged pruning chunk (k % 256 != 0), and a ragged row tile
+DECODE_CASES.append(wl.SPECS["batched"].with_(name="mm_two_steps", t=8, k=128, n_out=200))
+DECODE_CASES.append(wl.SPECS["batched"].with_(name="mm_ragged_step", t=24, k=1040, n_out=328, n=8, m=16))
+DECODE_CASES.append(wl.SPECS["batched"].with_(name="mm_bf16_weight_mean", t=12, k=1600, n_out=264, dtype="bf16",
+                                              n=2, m=4, score="weight", alpha=0.5, shift="token_mean",
+                                              var_rescale=True))
 DECODE_CASES.append(wl.SPECS["decode"].with_(name="decode_given_shift", t=2, k=512, n_out=256, shift="given"))
 
 
