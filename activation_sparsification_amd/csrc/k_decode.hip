@@ -597,7 +597,7 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) part[i] += (double)elem16<DT>(u[i], e);
     }
-    const double tot = wave_sum((part[0] + part[1]) + (part[2] + part[3]));
+    const double tot = wave_sum_dpp((part[0] + part[1]) + (part[2] + part[3]));
     if (lane == 0) s_part[wv][0] = tot;
     __syncthreads();
   }
@@ -699,7 +699,7 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
   if (a.var) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const double tot = wave_sum(st[q]);
+      const double tot = wave_sum_dpp(st[q]);
       if (lane == 0) s_part[wv][1 + q] = tot;
     }
   }

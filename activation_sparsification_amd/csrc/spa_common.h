@@ -140,6 +140,33 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// One DPP move of a double (both halves with the same control); lanes outside
+// row_mask read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+// Sum over the 64 lanes of a wave in a fixed order, on every lane, with DPP
+// moves instead of LDS permutes: pairs and quads (quad_perm), 8 and 16 lanes
+// (half-row and row mirrors), then the rows (row_bcast15 into rows 1 and 3,
+// row_bcast31 into rows 2 and 3); the total lands in row 3 and lane 63 is
+// read back.
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  v += dpp_d<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+  v += dpp_d<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+  v += dpp_d<0x141, 0xF>(v);   // row_half_mirror
+  v += dpp_d<0x140, 0xF>(v);   // row_mirror
+  v += dpp_d<0x142, 0xA>(v);   // row_bcast15 -> rows 1, 3
+  v += dpp_d<0x143, 0xC>(v);   // row_bcast31 -> rows 2, 3
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // Sum of one double per thread, identical on every thread.  Fixed order:
 // butterfly within each wave, then waves 0..3 in order.
 __device__ __forceinline__ double block_sum(double v, double* s_tmp /*[4]*/) {
