@@ -15,12 +15,14 @@
 // applies the epilogue.  Counters are left at zero for the next call.
 //
 // Variants:
-//  * one token, 16-bit weights under 2 GiB (k_decode_t1): selection on full
-//    waves, one barrier, then every wave streams the kept rows with buffer
-//    loads, 32 per lane in flight;
-//  * fused (t <= 4, and float32): each workgroup prunes its own channel range
-//    in LDS (the same few thousand comparisons in every tile) and streams the
-//    union of kept rows with float32 VALU FMAs, 16 bytes per lane per row;
+//  * one token, 16-bit weights under 2 GiB, at least eight 512-column tiles
+//    (k_decode_t1): after one barrier for the shift, each wave selects its
+//    own 64 channels by in-block rank and streams its kept rows, 1 KB of a
+//    row per load, 32 buffer loads per lane in flight;
+//  * fused (2..4 tokens, float32, and one token with narrower outputs): each
+//    workgroup prunes its own channel range in LDS (the same few thousand
+//    comparisons in every tile) and streams the union of kept rows with
+//    float32 VALU FMAs, 16 bytes per lane per row;
 //  * matrix-core (5..32 tokens, 16-bit): the union of kept rows is nearly all
 //    of W, so k_prune_cols prunes every channel once into masked rows in the
 //    matrix cores' operand order, and k_decode_mm reads the row-major W once

@@ -126,13 +126,9 @@ __device__ __forceinline__ float clact_accumulate(float acc, float v) {
 // rounded once more without error (53 >= 2*24 + 2).
 __device__ __forceinline__ float sqrt_rn(float a) { return (float)__builtin_sqrt((double)a); }
 
-// "j beats k" in the top-n rule: a larger score, or an equal score at a lower index.
-__device__ __forceinline__ bool beats(float sj, int j, float sk, int k) {
-  return (sj > sk) || (sj == sk && j < k);
-}
 
 // ---------------------------------------------------------------------------
-// Workgroup reductions (blockDim.x == 256).
+// Wave and workgroup reductions (block_sum: blockDim.x == 256).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
@@ -176,21 +172,6 @@ __device__ __forceinline__ double block_sum(double v, double* s_tmp /*[4]*/) {
   if ((threadIdx.x & (kWave - 1)) == 0) s_tmp[w] = v;
   __syncthreads();
   return ((s_tmp[0] + s_tmp[1]) + s_tmp[2]) + s_tmp[3];
-}
-
-// Exclusive prefix count of `flag` over the 256 threads; *total gets the sum.
-__device__ __forceinline__ int block_exclusive_count(bool flag, int* s_tmp /*[4]*/, int* total) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-  const unsigned long long bal = __ballot(flag);
-  const int before = __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-  __syncthreads();
-  if (lane == 0) s_tmp[w] = __popcll(bal);
-  __syncthreads();
-  int off = 0;
-  for (int i = 0; i < w; ++i) off += s_tmp[i];
-  *total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
-  return off + before;
 }
 
 }  // namespace spa
