@@ -1166,12 +1166,15 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
   auto carve = [&](size_t nbytes) { size_t off = bytes; bytes += (nbytes + 255) & ~(size_t)255; return off; };
   if (t1_kernel(t, dtype, k, n_out)) {
     // one-token kernel: 512-column tiles (1 KB of each kept row per load
-    // instruction); channel splits until about 256 workgroups run, each split
-    // at most kT1MaxChan channels, the partial traffic near 5 % of the weight bytes
+    // instruction); channel splits until about 224 workgroups run (one per CU
+    // for 7/8 of the chip: measured a little faster than 252 for the 8:16
+    // decode shape, where each wave then lists exactly one batch of rows),
+    // each split at most kT1MaxChan channels, the partial traffic near 5 % of
+    // the weight bytes
     p.col_tile = kT1Cols;
     p.tiles = (n_out + p.col_tile - 1) / p.col_tile;
     const int blocks = k / m;
-    int sp = 256 / p.tiles > 1 ? 256 / p.tiles : 1;
+    int sp = 224 / p.tiles > 1 ? 224 / p.tiles : 1;
     const double wbytes = (double)k * n / m * n_out * 2.0;
     const int max_by_traffic = (int)(0.05 * wbytes / (8.0 * n_out));
     if (sp > max_by_traffic) sp = max_by_traffic > 1 ? max_by_traffic : 1;
