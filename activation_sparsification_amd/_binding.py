@@ -20,6 +20,7 @@ SPA_OK, SPA_ERR_INVALID, SPA_ERR_UNSUPPORTED, SPA_ERR_HIP = 0, 1, 2, 3
 DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 SCORE = {"magnitude": 0, "weight": 1, "clact": 2}
 SHIFT = {"none": 0, "token_mean": 1, "given": 2}
+ACT = {"none": 0, "relu2": 1}
 ENTRY_PRUNE, ENTRY_DECODE, ENTRY_PREFILL = 0, 1, 2
 
 
@@ -31,7 +32,7 @@ class SpaError(RuntimeError):
 
 class _Cfg(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("m", ctypes.c_int32), ("score", ctypes.c_int32),
-                ("shift", ctypes.c_int32), ("var_rescale", ctypes.c_int32)]
+                ("shift", ctypes.c_int32), ("var_rescale", ctypes.c_int32), ("act", ctypes.c_int32)]
 
 
 class _Weight(ctypes.Structure):
@@ -72,15 +73,16 @@ EXPORTS = ("prepare_weight", "prune_nm", "sparse_linear_decode", "sparse_linear_
 
 @dataclasses.dataclass(frozen=True)
 class PruneConfig:
-    """Keep ``n`` of every ``m`` channels; ``score`` / ``shift`` as in the C header."""
+    """Keep ``n`` of every ``m`` channels; ``score`` / ``shift`` / ``act`` as in the C header."""
     n: int
     m: int
     score: str = "magnitude"
     shift: str = "none"
     var_rescale: bool = False
+    act: str = "none"
 
     def c(self) -> _Cfg:
-        return _Cfg(self.n, self.m, SCORE[self.score], SHIFT[self.shift], int(self.var_rescale))
+        return _Cfg(self.n, self.m, SCORE[self.score], SHIFT[self.shift], int(self.var_rescale), ACT[self.act])
 
 
 @dataclasses.dataclass

@@ -159,6 +159,27 @@ __device__ __forceinline__ float raw_elem(const uint4* raw, int j) {
   }
 }
 
+// The squared-ReLU input transform applied in place to raw words (16-bit
+// halves or float32 words).  Its results are representable in the dtype, so
+// the words stay exact.
+template <int DT, int NQ>
+__device__ __forceinline__ void act_raw(uint4 (&raw)[NQ]) {
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    uint32_t* w = reinterpret_cast<uint32_t*>(&raw[q]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (DT == SPA_F32) {
+        w[e] = __float_as_uint(relu2<DT>(__uint_as_float(w[e])));
+      } else {
+        const uint32_t lo = (uint32_t)from_f32<DT>(relu2<DT>(to_f32<DT>((uint16_t)(w[e] & 0xFFFFu))));
+        const uint32_t hi = (uint32_t)from_f32<DT>(relu2<DT>(to_f32<DT>((uint16_t)(w[e] >> 16))));
+        w[e] = lo | (hi << 16);
+      }
+    }
+  }
+}
+
 // Waves per workgroup: 8 for the light cases; 4 (so each wave may use up to 512
 // registers) when several tokens or 32-wide blocks are ranked per lane.
 template <int M, int TOK>
@@ -230,11 +251,13 @@ __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(D
         if (i < T_) {
           const uint4 u = *reinterpret_cast<const uint4*>(x + (size_t)i * a.k + (size_t)q * CPL);
           if constexpr (DT == SPA_F32) {
-            sum[i] += (double)__uint_as_float(u.x) + (double)__uint_as_float(u.y) + (double)__uint_as_float(u.z) +
-                      (double)__uint_as_float(u.w);
+            sum[i] += (double)apply_act<DT>(__uint_as_float(u.x), a.act) +
+                      (double)apply_act<DT>(__uint_as_float(u.y), a.act) +
+                      (double)apply_act<DT>(__uint_as_float(u.z), a.act) +
+                      (double)apply_act<DT>(__uint_as_float(u.w), a.act);
           } else {
 #pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) sum[i] += (double)elem16<DT>(u, e2);
+            for (int e2 = 0; e2 < 8; ++e2) sum[i] += (double)apply_act<DT>(elem16<DT>(u, e2), a.act);
           }
         }
       }
@@ -279,6 +302,11 @@ __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(D
 #pragma unroll
         for (int j = 0; j < M; ++j) f[j] = a.chan_scale[ch0 + j];
       }
+    }
+    if (a.act && own) {
+#pragma unroll
+      for (int i = 0; i < TOK; ++i)
+        if (i < T_) act_raw<DT>(raw[i]);
     }
     uint32_t kbits[TOK];
     uint32_t ub = 0;
@@ -547,7 +575,9 @@ __device__ __forceinline__ void swizzle_xor_all(uint32_t v, uint32_t (&so)[M]) {
   }
 }
 
-template <int DT, int M>
+// ACT: the squared-ReLU input transform, a template switch so that the plain
+// kernel's code is not touched by it.
+template <int DT, int M, bool ACT>
 __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
   using T = typename Dt<DT>::T;
   constexpr int NW = kT1Waves, NT = kT1Threads, CPL = 8, C = kT1Cols;
@@ -597,7 +627,7 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part[i] += (double)elem16<DT>(u[i], e);
+        for (int e = 0; e < 8; ++e) part[i] += (double)apply_act<DT>(elem16<DT>(u[i], e), ACT);
     }
     const double tot = wave_sum_dpp((part[0] + part[1]) + (part[2] + part[3]));
     if (lane == 0) s_part[wv][0] = tot;
@@ -631,7 +661,7 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
     const int c = cw + lane;
     // 2. score (one loop per score kind under a uniform branch: if-converted,
     //    every kind would pay for CLACT's square root)
-    const float xh = to_f32<DT>((T)xraw[r]) - eta;
+    const float xh = apply_act<DT>(to_f32<DT>((T)xraw[r]), ACT) - eta;
     uint32_t sb;
     if (a.score == SPA_SCORE_MAGNITUDE) {
       sb = __float_as_uint(__builtin_fabsf(xh));
@@ -801,7 +831,7 @@ __global__ void __launch_bounds__(256) k_prune_cols(DecodeArgs a) {
       raw[i] = buffer_load_u16(xr, i < T_ && ch < K ? (uint32_t)(i * K + ch) * 2u : kBufferOutOfRange);
 #pragma unroll
     for (int i = 0; i < kMaxTok; ++i)
-      if (i < T_) s_x[i][c] = ch < K ? to_f32<DT>((T)raw[i]) - (a.eta ? a.eta[i] : 0.f) : 0.f;
+      if (i < T_) s_x[i][c] = ch < K ? apply_act<DT>(to_f32<DT>((T)raw[i]), a.act) - (a.eta ? a.eta[i] : 0.f) : 0.f;
   }
   __syncthreads();
   if ((int)threadIdx.x < CH) {
@@ -1258,7 +1288,10 @@ template <int DT, int M>
 static hipError_t fused_tok(DecodeArgs& a, hipStream_t st) {
   if constexpr (DT != SPA_F32) {
     if (t1_kernel(a.t, DT, a.k, a.n_out)) {
-      hipLaunchKernelGGL((k_decode_t1<DT, M>), dim3(a.tiles * a.splits), dim3(kT1Threads), 0, st, a);
+      if (a.act)
+        hipLaunchKernelGGL((k_decode_t1<DT, M, true>), dim3(a.tiles * a.splits), dim3(kT1Threads), 0, st, a);
+      else
+        hipLaunchKernelGGL((k_decode_t1<DT, M, false>), dim3(a.tiles * a.splits), dim3(kT1Threads), 0, st, a);
       return hipGetLastError();
     }
   }
@@ -1276,7 +1309,7 @@ static hipError_t decode_dt(DecodeArgs& a, hipStream_t st) {
   // (its column norms are taken over the shifted values)
   const bool mean_first = fused ? (size_t)a.t * a.k > 65536 : true;
   if (a.shift == SPA_SHIFT_TOKEN_MEAN && mean_first) {
-    if (hipError_t e = launch_token_mean(DT, a.x, a.t, a.k, a.eta_ws, st)) return e;
+    if (hipError_t e = launch_token_mean(DT, a.x, a.t, a.k, a.act, a.eta_ws, st)) return e;
     a.eta = a.eta_ws;
   }
   if (fused) {

@@ -29,7 +29,7 @@ __device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t r, int seg, bool
     out.q[i] = buffer_load16(r, ok ? (uint32_t)(seg * SEG * Dt<DT>::bytes + 16 * i) : kBufferOutOfRange);
 }
 template <int DT, int SEG>
-__device__ __forceinline__ void unpack_raw(const RawSeg<DT, SEG>& in, float (&v)[SEG]) {
+__device__ __forceinline__ void unpack_raw(const RawSeg<DT, SEG>& in, int act, float (&v)[SEG]) {
   if constexpr (DT == SPA_F32) {
 #pragma unroll
     for (int i = 0; i < SEG / 4; ++i) {
@@ -41,6 +41,10 @@ __device__ __forceinline__ void unpack_raw(const RawSeg<DT, SEG>& in, float (&v)
     for (int i = 0; i < SEG / 8; ++i)
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[8 * i + e] = elem16<DT>(in.q[i], e);
+  }
+  if (act) {
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) v[j] = relu2<DT>(v[j]);
   }
 }
 
@@ -69,7 +73,7 @@ __device__ __forceinline__ uint32_t block_keep(const float* sc, int n) {
 // Token mean of a long row: 16-byte loads, four in flight per thread, four
 // float64 partial sums combined in a fixed order, then the workgroup sum.
 template <int DT>
-__device__ __forceinline__ float row_mean(const typename Dt<DT>::T* __restrict__ row, int k, double* s_red) {
+__device__ __forceinline__ float row_mean(const typename Dt<DT>::T* __restrict__ row, int k, int act, double* s_red) {
   constexpr int PER = 16 / Dt<DT>::bytes;
   const int nq = k / PER;
   double part[4] = {0.0, 0.0, 0.0, 0.0};
@@ -83,11 +87,13 @@ __device__ __forceinline__ float row_mean(const typename Dt<DT>::T* __restrict__
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if constexpr (DT == SPA_F32) {
-        part[r] += ((double)__uint_as_float(u[r].x) + (double)__uint_as_float(u[r].y)) +
-                   ((double)__uint_as_float(u[r].z) + (double)__uint_as_float(u[r].w));
+        part[r] += ((double)apply_act<DT>(__uint_as_float(u[r].x), act) +
+                    (double)apply_act<DT>(__uint_as_float(u[r].y), act)) +
+                   ((double)apply_act<DT>(__uint_as_float(u[r].z), act) +
+                    (double)apply_act<DT>(__uint_as_float(u[r].w), act));
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part[r] += (double)elem16<DT>(u[r], e);
+        for (int e = 0; e < 8; ++e) part[r] += (double)apply_act<DT>(elem16<DT>(u[r], e), act);
       }
     }
   }
@@ -122,7 +128,7 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
   RawSeg<DT, SEG> raw_next;
   load_raw<DT, SEG>(xrs, (int)threadIdx.x, (int)threadIdx.x < nseg, raw_next);
   float xv0[SEG];
-  unpack_raw<DT, SEG>(raw_next, xv0);
+  unpack_raw<DT, SEG>(raw_next, a.act, xv0);
   float eta = 0.f;
   if (a.shift_mean) {
     if (iters == 1) {
@@ -133,7 +139,7 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
       }
       eta = (float)(block_sum(s, s_red) / (double)a.k);
     } else {
-      eta = row_mean<DT>(xr, a.k, s_red);
+      eta = row_mean<DT>(xr, a.k, a.act, s_red);
     }
   } else if (a.eta_given) {
     eta = a.eta_given[row];
@@ -158,7 +164,7 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
 #pragma unroll
       for (int j = 0; j < SEG; ++j) xv[j] = xv0[j];
     } else {
-      unpack_raw<DT, SEG>(raw_next, xv);
+      unpack_raw<DT, SEG>(raw_next, a.act, xv);
     }
     if (it + 1 < iters) load_raw<DT, SEG>(xrs, seg + 256, seg + 256 < nseg, raw_next);
     if (active) {
@@ -302,22 +308,22 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
 }
 
 template <int DT>
-__global__ void __launch_bounds__(256) k_token_mean(const typename Dt<DT>::T* __restrict__ x, int k,
+__global__ void __launch_bounds__(256) k_token_mean(const typename Dt<DT>::T* __restrict__ x, int k, int act,
                                                     float* __restrict__ eta) {
   __shared__ double s_red[4];
-  const float e = row_mean<DT>(x + (size_t)blockIdx.x * k, k, s_red);
+  const float e = row_mean<DT>(x + (size_t)blockIdx.x * k, k, act, s_red);
   if (threadIdx.x == 0) eta[blockIdx.x] = e;
 }
 
 // CLACT column energy, one thread per channel, tokens in ascending order.
 template <int DT>
-__global__ void __launch_bounds__(256) k_colnorm(const typename Dt<DT>::T* __restrict__ x,
+__global__ void __launch_bounds__(256) k_colnorm(const typename Dt<DT>::T* __restrict__ x, int act,
                                                  const float* __restrict__ eta, int t, int k, float* __restrict__ c) {
   const int ch = blockIdx.x * 256 + threadIdx.x;
   if (ch >= k) return;
   float acc = 0.f;
   for (int p = 0; p < t; ++p) {
-    const float v = to_f32<DT>(x[(size_t)p * k + ch]) - (eta ? eta[p] : 0.f);
+    const float v = apply_act<DT>(to_f32<DT>(x[(size_t)p * k + ch]), act) - (eta ? eta[p] : 0.f);
     acc = clact_accumulate(acc, v);
   }
   c[ch] = sqrt_rn(acc);
@@ -351,22 +357,35 @@ hipError_t launch_prune(int dtype, const PruneArgs& a, hipStream_t st) {
   }
 }
 
-hipError_t launch_token_mean(int dtype, const void* x, int t, int k, float* eta, hipStream_t st) {
+hipError_t launch_token_mean(int dtype, const void* x, int t, int k, int act, float* eta, hipStream_t st) {
   if (t == 0) return hipSuccess;
   switch (dtype) {
-    case SPA_F32: hipLaunchKernelGGL(k_token_mean<SPA_F32>, dim3(t), dim3(256), 0, st, (const float*)x, k, eta); break;
-    case SPA_F16: hipLaunchKernelGGL(k_token_mean<SPA_F16>, dim3(t), dim3(256), 0, st, (const uint16_t*)x, k, eta); break;
-    default: hipLaunchKernelGGL(k_token_mean<SPA_BF16>, dim3(t), dim3(256), 0, st, (const uint16_t*)x, k, eta); break;
+    case SPA_F32:
+      hipLaunchKernelGGL(k_token_mean<SPA_F32>, dim3(t), dim3(256), 0, st, (const float*)x, k, act, eta);
+      break;
+    case SPA_F16:
+      hipLaunchKernelGGL(k_token_mean<SPA_F16>, dim3(t), dim3(256), 0, st, (const uint16_t*)x, k, act, eta);
+      break;
+    default:
+      hipLaunchKernelGGL(k_token_mean<SPA_BF16>, dim3(t), dim3(256), 0, st, (const uint16_t*)x, k, act, eta);
+      break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_colnorm(int dtype, const void* x, const float* eta, int t, int k, float* c, hipStream_t st) {
+hipError_t launch_colnorm(int dtype, const void* x, int act, const float* eta, int t, int k, float* c,
+                          hipStream_t st) {
   const dim3 grid((k + 255) / 256);
   switch (dtype) {
-    case SPA_F32: hipLaunchKernelGGL(k_colnorm<SPA_F32>, grid, dim3(256), 0, st, (const float*)x, eta, t, k, c); break;
-    case SPA_F16: hipLaunchKernelGGL(k_colnorm<SPA_F16>, grid, dim3(256), 0, st, (const uint16_t*)x, eta, t, k, c); break;
-    default: hipLaunchKernelGGL(k_colnorm<SPA_BF16>, grid, dim3(256), 0, st, (const uint16_t*)x, eta, t, k, c); break;
+    case SPA_F32:
+      hipLaunchKernelGGL(k_colnorm<SPA_F32>, grid, dim3(256), 0, st, (const float*)x, act, eta, t, k, c);
+      break;
+    case SPA_F16:
+      hipLaunchKernelGGL(k_colnorm<SPA_F16>, grid, dim3(256), 0, st, (const uint16_t*)x, act, eta, t, k, c);
+      break;
+    default:
+      hipLaunchKernelGGL(k_colnorm<SPA_BF16>, grid, dim3(256), 0, st, (const uint16_t*)x, act, eta, t, k, c);
+      break;
   }
   return hipGetLastError();
 }

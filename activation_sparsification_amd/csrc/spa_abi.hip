@@ -21,6 +21,7 @@ bool valid_cfg(const spa_prune_cfg* c) {
   if (c->score < SPA_SCORE_MAGNITUDE || c->score > SPA_SCORE_CLACT) return false;
   if (c->shift < SPA_SHIFT_NONE || c->shift > SPA_SHIFT_GIVEN) return false;
   if (c->var_rescale != 0 && c->var_rescale != 1) return false;
+  if (c->act != SPA_ACT_NONE && c->act != SPA_ACT_RELU2) return false;
   return true;
 }
 
@@ -137,6 +138,7 @@ spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const sp
   spa::PruneArgs a{};
   a.x = x; a.t = t; a.k = k; a.n = cfg->n; a.m = cfg->m;
   a.var = cfg->var_rescale;
+  a.act = cfg->act;
   a.chan_scale = cfg->score == SPA_SCORE_WEIGHT ? chan_scale : nullptr;
   a.eta_given = cfg->shift == SPA_SHIFT_GIVEN ? eta_in : nullptr;
   a.shift_mean = cfg->shift == SPA_SHIFT_TOKEN_MEAN;
@@ -145,12 +147,12 @@ spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const sp
     float* eta_ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)k * 4));
     const float* eta = a.eta_given;
     if (cfg->shift == SPA_SHIFT_TOKEN_MEAN) {
-      if (hipError_t e = spa::launch_token_mean(dtype, x, t, k, eta_ws, st)) return hip_status(e);
+      if (hipError_t e = spa::launch_token_mean(dtype, x, t, k, cfg->act, eta_ws, st)) return hip_status(e);
       eta = eta_ws;
       a.eta_given = eta_ws;
       a.shift_mean = 0;
     }
-    if (hipError_t e = spa::launch_colnorm(dtype, x, eta, t, k, colnorm, st)) return hip_status(e);
+    if (hipError_t e = spa::launch_colnorm(dtype, x, cfg->act, eta, t, k, colnorm, st)) return hip_status(e);
     a.colnorm = colnorm;
   }
   a.pack = spa::kPackVals;
@@ -180,6 +182,7 @@ spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, c
     fix(a.dense);
   }
   a.x = x;
+  a.act = cfg->act;
   a.wt = w->wt;
   a.w = w->w;
   a.chan_scale = w->chan_scale;
@@ -209,17 +212,18 @@ spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, 
   spa::PruneArgs a{};
   a.x = x; a.t = t; a.k = k; a.n = cfg->n; a.m = cfg->m;
   a.var = cfg->var_rescale;
+  a.act = cfg->act;
   a.chan_scale = cfg->score == SPA_SCORE_WEIGHT ? w->chan_scale : nullptr;
   a.eta_given = cfg->shift == SPA_SHIFT_GIVEN ? eta_in : nullptr;
   a.shift_mean = cfg->shift == SPA_SHIFT_TOKEN_MEAN;
   if (cfg->score == SPA_SCORE_CLACT) {
     float* colnorm = reinterpret_cast<float*>(base + pl.colnorm);
     if (cfg->shift == SPA_SHIFT_TOKEN_MEAN) {
-      if (hipError_t e = spa::launch_token_mean(w->dtype, x, t, k, eta_ws, st)) return hip_status(e);
+      if (hipError_t e = spa::launch_token_mean(w->dtype, x, t, k, cfg->act, eta_ws, st)) return hip_status(e);
       a.eta_given = eta_ws;
       a.shift_mean = 0;
     }
-    if (hipError_t e = spa::launch_colnorm(w->dtype, x, a.eta_given, t, k, colnorm, st)) return hip_status(e);
+    if (hipError_t e = spa::launch_colnorm(w->dtype, x, cfg->act, a.eta_given, t, k, colnorm, st)) return hip_status(e);
     a.colnorm = colnorm;
   }
   a.eta_out = eta_ws;

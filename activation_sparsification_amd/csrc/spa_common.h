@@ -41,6 +41,21 @@ template <> __device__ __forceinline__ float from_f32<SPA_F32>(float v) { return
 template <> __device__ __forceinline__ uint16_t from_f32<SPA_F16>(float v) { return (uint16_t)f32_to_f16(v); }
 template <> __device__ __forceinline__ uint16_t from_f32<SPA_BF16>(float v) { return (uint16_t)f32_to_bf16(v); }
 
+// Squared ReLU of a stored input value v (already float32): max(v, 0)^2 in
+// float32 -- exact for 16-bit v -- rounded back to the storage dtype, so the
+// fused path sees what a separate elementwise pass would have stored.
+template <int DT>
+__device__ __forceinline__ float relu2(float v) {
+#pragma clang fp contract(off)
+  const float r = v > 0.f ? v : 0.f;
+  const float sq = r * r;
+  return to_f32<DT>(from_f32<DT>(sq));
+}
+// The input transform of cfg->act (0: none, 1: squared ReLU); act is
+// uniform across the launch.
+template <int DT>
+__device__ __forceinline__ float apply_act(float v, int act) { return act ? relu2<DT>(v) : v; }
+
 // Element e (0..7) of a 16-byte vector of 16-bit values.
 template <int DT> __device__ __forceinline__ float elem16(const uint4& v, int e) {
   uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;

@@ -26,6 +26,7 @@ struct PruneArgs {
   const float* eta_given;    // precomputed / caller shift, or NULL
   int t, k, n, m;
   int shift_mean;            // compute the token mean in-kernel
+  int act;                   // input transform (SPA_ACT_*)
   int var;
   int pack;                  // PackFormat bits
   void* vals;                // kPackVals
@@ -38,8 +39,9 @@ struct PruneArgs {
   float* nu_out;             // may be NULL
 };
 hipError_t launch_prune(int dtype, const PruneArgs& a, hipStream_t st);
-hipError_t launch_token_mean(int dtype, const void* x, int t, int k, float* eta, hipStream_t st);
-hipError_t launch_colnorm(int dtype, const void* x, const float* eta, int t, int k, float* c, hipStream_t st);
+hipError_t launch_token_mean(int dtype, const void* x, int t, int k, int act, float* eta, hipStream_t st);
+hipError_t launch_colnorm(int dtype, const void* x, int act, const float* eta, int t, int k, float* c,
+                          hipStream_t st);
 
 // ---- decode ----
 struct DecodeArgs {
@@ -56,6 +58,7 @@ struct DecodeArgs {
   int score;                 // SPA_SCORE_*
   int shift;                 // SPA_SHIFT_*
   int var;
+  int act;                   // input transform (SPA_ACT_*)
   // workspace carve-up
   float* partial;            // fused: [splits][t][n_out]
   double* stats;             // fused: [tiles][splits][t][4]; matrix-core: [t][4][chunks]

@@ -48,6 +48,7 @@ WORKLOADS = {
     "decode": ("decode", dict()),
     "prefill": ("prefill", dict()),
     "relu2": ("relu2", dict()),
+    "relu2_fused": ("relu2_fused", dict()),
     "batched_t1": ("batched", dict(t=1)),
     "batched_t8": ("batched", dict(t=8)),
     "batched_t32": ("batched", dict(t=32)),
@@ -56,6 +57,8 @@ DESCRIPTION = {
     "decode": "decode GEMV 8:16 weight-aware alpha=0.5 + per-token mean shift, X[1,4096] bf16, W[14336,4096] bf16",
     "prefill": "prefill 2:4 magnitude + per-token mean shift, X[2048,4096] bf16, W[14336,4096] bf16, smfmac",
     "relu2": "squared-ReLU down-projection 2:4, X[4096,16384] bf16, W[4096,16384] bf16, smfmac",
+    "relu2_fused": "the same down-projection fed its pre-activation U[4096,16384] bf16; the squared ReLU "
+                   "is applied inside the pruning pass",
     "batched_t1": "batched decode 16:32 CLACT + variance rescale, X[1,14336] fp16, W[4096,14336] fp16",
     "batched_t8": "batched decode 16:32 CLACT + variance rescale, X[8,14336] fp16, W[4096,14336] fp16",
     "batched_t32": "batched decode 16:32 CLACT + variance rescale, X[32,14336] fp16, W[4096,14336] fp16",
@@ -105,7 +108,7 @@ class Workload:
         self.x = x.to(dev)
         wd = w.to(dev)
         self.pw = spa.prepare_weight(wd, spec.alpha, want_wt=self.decode)
-        self.cfg = spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, spec.var_rescale)
+        self.cfg = spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, spec.var_rescale, spec.act)
         # decode streams the channel-major copy for 1..4 tokens (and float32); more tokens
         # of a 16-bit type read the row-major weight on the matrix cores
         self.reads_wt = self.decode and (spec.t <= 4 or spec.dtype == "f32")
@@ -291,10 +294,10 @@ def main():
     head = measure(args.workload, args.steps, args.warmup)
     secondary = []
     if not args.only:
-        for name in ["prefill", "relu2", "batched_t1", "batched_t8", "batched_t32"]:
+        for name in ["prefill", "relu2", "relu2_fused", "batched_t1", "batched_t8", "batched_t32"]:
             if name == args.workload:
                 continue
-            st = max(10, args.steps // 4) if name in ("prefill", "relu2") else args.steps
+            st = max(10, args.steps // 4) if name in ("prefill", "relu2", "relu2_fused") else args.steps
             secondary.append(measure(name, st, max(5, args.warmup // 2)))
 
     decode = head["unit"] == "GB/s"

@@ -5,6 +5,13 @@
  * For each token x (a row of X[t][k]) and a linear layer y = x W^T with
  * W[n_out][k]:
  *
+ *   x        the layer input, or, with cfg->act == SPA_ACT_RELU2, the
+ *            squared ReLU of the given pre-activation u: x_k = max(u_k, 0)^2
+ *            in float32 (exact for 16-bit u) rounded to dtype to nearest
+ *            even -- the value a separate elementwise pass would store
+ *            ("Accelerating Transformer training and inference with 2:4
+ *            sparsity and Squared-ReLU" s2.2 defines the activation, s3.1
+ *            fuses it into the kernel that prunes and packs);
  *   eta      per-token shift: 0, the token mean (dynamic per-token shift,
  *            "Activation sparsification: a dynamic pruning method for
  *            efficient LLM inference" s3.1), or a caller-given value (the
@@ -64,6 +71,7 @@ typedef enum spa_status {
 enum { SPA_F32 = 0, SPA_F16 = 1, SPA_BF16 = 2 };
 enum { SPA_SCORE_MAGNITUDE = 0, SPA_SCORE_WEIGHT = 1, SPA_SCORE_CLACT = 2 };
 enum { SPA_SHIFT_NONE = 0, SPA_SHIFT_TOKEN_MEAN = 1, SPA_SHIFT_GIVEN = 2 };
+enum { SPA_ACT_NONE = 0, SPA_ACT_RELU2 = 1 };
 enum { SPA_ENTRY_PRUNE = 0, SPA_ENTRY_DECODE = 1, SPA_ENTRY_PREFILL = 2 };
 
 /* Pruning configuration.  m in {4, 8, 16, 32}; 1 <= n <= m; k % m == 0. */
@@ -73,6 +81,7 @@ typedef struct spa_prune_cfg {
   int32_t score;        /* SPA_SCORE_* */
   int32_t shift;        /* SPA_SHIFT_* */
   int32_t var_rescale;  /* 0 or 1 */
+  int32_t act;          /* SPA_ACT_*: activation applied to the input first */
 } spa_prune_cfg;
 
 /* A prepared linear layer.  Fields not needed by an entry point may be NULL:

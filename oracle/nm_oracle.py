@@ -20,8 +20,9 @@ Sources (page titles; sections as numbered on each page):
 * [WiSparse] "LLM inference optimisation: WiSparse activation sparsification
             explained" -- s2.1, equation (4): weight-aware channel score.
 * [SqReLU]  "Accelerating Transformer training and inference with 2:4
-            sparsity and Squared-ReLU" -- s2.2, s3.3: squared-ReLU output as
-            the 2:4 operand; non-zeros stored contiguously with a mask.
+            sparsity and Squared-ReLU" -- s2.2: the activation max(0, x)^2;
+            s3.1: one kernel applies it, prunes 2:4 and packs; s3.3:
+            non-zeros stored contiguously with a mask.
 
 Readings taken where the pages are silent or disagree (each is listed in the
 design notes as well):
@@ -46,6 +47,9 @@ design notes as well):
   float64 over all K positions; a zero denominator gives nu = 1.
 * The dense term of (x_sparse + eta) W^T is split as
   (x_hat * m) W^T + eta * (W 1): only kept rows of W^T are read.
+* Squared ReLU as the input transform: max(0, u)^2 in float32, rounded to
+  the storage dtype -- what a separate elementwise pass would store; the
+  fused kernel must see the same input.
 * Packed values are the float32 shifted values rounded to the storage dtype
   (round-to-nearest-even); the index metadata is one uint8 in-block position
   per kept value, ascending.
@@ -115,6 +119,17 @@ def row_sum(w: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # Per-token steps ([Guide] s2.2, s3.1, s3.2; [WiSparse] s2.1)
 # ----------------------------------------------------------------------------
+
+def squared_relu(u: np.ndarray, dtype: str) -> np.ndarray:
+    """x = max(0, u)^2 ([SqReLU] s2.2), as the layer input the pruning sees.
+
+    The square is one float32 multiply (exact when u is a 16-bit value) and
+    the result is rounded to the storage dtype, to nearest even.
+    """
+    u = np.asarray(u, dtype=np.float32)
+    r = np.where(u > 0, u, np.float32(0.0)).astype(np.float32)
+    return round_to_dtype(r * r, dtype)
+
 
 def token_mean(x: np.ndarray) -> np.ndarray:
     """D-PTS shift eta_i = mean over channels of x_i  ([Guide] s3.1).
@@ -209,13 +224,19 @@ def var_factor(xhat: np.ndarray, keep: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def prune(x, dtype: str, n: int, m: int, score: str = "magnitude", f=None, shift_mode: str = "none",
-          eta_in=None, var_rescale: bool = False) -> dict:
-    """Score -> per-block top-n -> pack -> (nu), for X[t, k] given as float32 values.
+          eta_in=None, var_rescale: bool = False, act: str = "none") -> dict:
+    """(Activation) -> score -> per-block top-n -> pack -> (nu), for X[t, k] given as float32 values.
 
+    ``act``: "none" | "relu2" (``x`` is then the pre-activation u, and the
+    layer input is ``squared_relu(u)``).
     ``score``: "magnitude" | "weight" (needs ``f``) | "clact".
     ``shift_mode``: "none" | "token_mean" (D-PTS) | "given" (S-PTS, ``eta_in``).
     """
     x = np.asarray(x, dtype=np.float32)
+    if act == "relu2":
+        x = squared_relu(x, dtype)
+    elif act != "none":
+        raise ValueError(act)
     t, k = x.shape
     if not (1 <= n <= m) or k % m:
         raise ValueError("need 1 <= n <= m and m | k")

@@ -35,7 +35,7 @@ def oracle_for(spec, x_cpu, w_cpu, f=None, eta_in=None, rows=None):
         f = O.channel_factor(f32(w_cpu), spec.alpha)
     eta = None if eta_in is None else (f32(eta_in) if rows is None else f32(eta_in[rows]))
     pr = O.prune(x, spec.dtype, spec.n, spec.m, score=spec.score, f=f, shift_mode=spec.shift, eta_in=eta,
-                 var_rescale=spec.var_rescale)
+                 var_rescale=spec.var_rescale, act=spec.act)
     if w_cpu is not None:
         pr["y"] = O.linear(pr, f32(w_cpu))
     pr["f"] = f

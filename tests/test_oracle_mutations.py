@@ -64,6 +64,22 @@ def _bf16_truncate(v, dtype):
     return _orig_round(v, dtype)
 
 
+def _relu2_abs(u, dtype):                                # squares negative inputs too
+    u = np.asarray(u, np.float32)
+    return _orig_round(u * u, dtype)
+
+
+def _relu2_unrounded(u, dtype):                          # keeps the float32 square
+    u = np.asarray(u, np.float32)
+    r = np.where(u > 0, u, np.float32(0)).astype(np.float32)
+    return r * r
+
+
+def _relu_only(u, dtype):                                # forgets the square
+    u = np.asarray(u, np.float32)
+    return _orig_round(np.where(u > 0, u, np.float32(0)).astype(np.float32), dtype)
+
+
 _orig_factor = O.channel_factor
 _orig_var = O.var_factor
 _orig_round = O.round_to_dtype
@@ -80,6 +96,9 @@ MUTANTS = {
     "clact_no_square": ("clact_colnorm", _clact_abs),
     "mean_wrong_divisor": ("token_mean", _mean_wrong_div),
     "bf16_truncation": ("round_to_dtype", _bf16_truncate),
+    "relu2_squares_negatives": ("squared_relu", _relu2_abs),
+    "relu2_not_rounded": ("squared_relu", _relu2_unrounded),
+    "relu2_not_squared": ("squared_relu", _relu_only),
 }
 
 

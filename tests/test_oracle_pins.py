@@ -348,6 +348,94 @@ def test_round_to_dtype_matches_torch(dtype, tdt):
 
 
 # --------------------------------------------------------------------------
+# squared ReLU as the input transform
+# --------------------------------------------------------------------------
+
+# (significand bits, smallest normal exponent) of each storage format
+_FORMATS = {"bf16": (8, -126), "f16": (11, -14), "f32": (24, -126)}
+_MAXFIN = {"bf16": (2 - 2 ** -7) * 2.0 ** 127, "f16": 65504.0, "f32": float(np.finfo(np.float32).max)}
+
+
+def _round_exact(v: Fraction, fmt: str) -> float:
+    """Nearest value of ``fmt`` to the exact rational v >= 0, ties to the even significand."""
+    if v == 0:
+        return 0.0
+    p, emin = _FORMATS[fmt]
+    e = v.numerator.bit_length() - v.denominator.bit_length()
+    if Fraction(2) ** e > v:
+        e -= 1
+    e = max(e, emin)                                      # subnormals share the smallest ulp
+    ulp = Fraction(2) ** (e - p + 1)
+    q = v / ulp
+    n = q.numerator // q.denominator
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    r = n * ulp
+    return math.inf if r > Fraction(_MAXFIN[fmt]) else float(r)
+
+
+def _all_finite_16bit(dtype):
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    if dtype == "bf16":
+        v = (bits << np.uint32(16)).view(np.float32)
+    else:
+        v = bits.astype(np.uint16).view(np.float16).astype(np.float32)
+    return v[np.isfinite(v)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_squared_relu_every_16bit_value(dtype):
+    # max(0, u)^2 for every finite value of the format, against the exact square
+    # rounded once to the format by rational arithmetic
+    u = _all_finite_16bit(dtype)
+    with np.errstate(over="ignore"):
+        got = O.squared_relu(u, dtype)
+    want = np.array([_round_exact(Fraction(float(a)) ** 2 if a > 0 else Fraction(0), dtype) for a in u],
+                    dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_squared_relu_float32_rounds_once():
+    rng = np.random.Generator(np.random.PCG64(5))
+    u = np.concatenate([rng.standard_normal(3000), rng.standard_normal(500) * 1e-20,
+                        rng.standard_normal(500) * 1e15]).astype(np.float32)
+    got = O.squared_relu(u, "f32")
+    want = np.array([_round_exact(Fraction(float(a)) ** 2 if a > 0 else Fraction(0), "f32") for a in u],
+                    dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert (got[u <= 0] == 0).all() and not np.signbit(got).any()
+
+
+def test_squared_relu_feeds_the_pruning():
+    # act="relu2" on u gives the same masks and values as pruning max(0, u)^2
+    # written out with exact rational squares
+    spec = wl.SPECS["relu2_fused"].with_(t=4, k=256)
+    u, _ = wl.make_inputs(spec, with_weight=False)
+    u = _x32(u)
+    x = np.array([[_round_exact(Fraction(float(a)) ** 2 if a > 0 else Fraction(0), "bf16") for a in row]
+                  for row in u], dtype=np.float32)
+    a = O.prune(u, "bf16", 2, 4, shift_mode="token_mean", act="relu2")
+    b = O.prune(x, "bf16", 2, 4, shift_mode="token_mean")
+    assert np.array_equal(a["keep"], b["keep"]) and np.array_equal(a["vals"], b["vals"])
+    assert np.array_equal(a["eta"], b["eta"])
+
+
+def test_squared_relu_of_preactivation_closed_form():
+    # z ~ N(-1, 1): max(0, z)^2 is zero with probability Phi(1) = 0.8413
+    spec = wl.SPECS["relu2_fused"].with_(t=256, k=4096)
+    u, _ = wl.make_inputs(spec, with_weight=False)
+    x = O.squared_relu(_x32(u), "bf16")
+    p = 0.5 * math.erfc(1.0 / math.sqrt(2.0))
+    assert abs(float((x == 0).mean()) - (1 - p)) < 0.002
+    gold = _gold("squared_relu_sparsity.json")
+    spec = wl.SPECS["prefill"].with_(t=256, k=4096, n_outliers=0)
+    z, _ = wl.make_inputs(spec, with_weight=False)
+    frac = float((O.squared_relu(_x32(z), "bf16") == 0).mean())
+    assert abs(frac - gold["zero_fraction_standard_normal"]) < 0.005
+
+
+# --------------------------------------------------------------------------
 # workload statistics (generator and mask together)
 # --------------------------------------------------------------------------
 

@@ -26,6 +26,7 @@ FULL = {
     "decode": wl.SPECS["decode"],
     "prefill": wl.SPECS["prefill"],
     "relu2": wl.SPECS["relu2"],
+    "relu2_fused": wl.SPECS["relu2_fused"],
     "batched_t1": wl.SPECS["batched"].with_(t=1),
     "batched_t8": wl.SPECS["batched"].with_(t=8),
     "batched_t32": wl.SPECS["batched"].with_(t=32),
@@ -48,7 +49,7 @@ def test_full_size_sampled(name):
     x, w = wl.make_inputs(spec)
     xd, wd = x.to(dev), w.to(dev)
     pw = spa.prepare_weight(wd, spec.alpha, want_wt=name in DECODE)
-    cfg = spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, spec.var_rescale)
+    cfg = spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, spec.var_rescale, spec.act)
     fn = spa.sparse_linear_decode if name in DECODE else spa.sparse_linear_prefill
     y, idx, nu = fn(xd, pw, cfg, want_idx=True, want_nu=True)
     torch.cuda.synchronize()
@@ -64,7 +65,7 @@ def test_full_size_sampled(name):
     f = f32(pw.chan_scale) if spec.score == "weight" else None
     xs = f32(x) if spec.score == "clact" else f32(x[torch.as_tensor(rows)])
     pr = O.prune(xs, spec.dtype, spec.n, spec.m, score=spec.score, f=f, shift_mode=spec.shift,
-                 var_rescale=spec.var_rescale)
+                 var_rescale=spec.var_rescale, act=spec.act)
     if spec.score == "clact":
         pr = {key: (v[rows] if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == spec.t and key != "factor"
                     else v) for key, v in pr.items()}

@@ -24,7 +24,7 @@ def _dev():
 
 
 def _cfg(spec, n=None, m=None):
-    return spa.PruneConfig(n or spec.n, m or spec.m, spec.score, spec.shift, spec.var_rescale)
+    return spa.PruneConfig(n or spec.n, m or spec.m, spec.score, spec.shift, spec.var_rescale, spec.act)
 
 
 def _check_prune(pr, vals, idx, eta, nu, dtype):
@@ -66,6 +66,18 @@ for dt in ["bf16", "f16", "f32"]:
             base = wl.SPECS["decode"].with_(name="sweep", t=3, k=256, n_out=64, dtype=dt, n=n, m=m, score=score,
                                             shift=shift, var_rescale=var, alpha=0.5)
             PRUNE_CASES.append((f"{dt}-{n}:{m}-{score}-{shift}-{int(var)}", base))
+# the squared-ReLU input transform: every dtype, the shift and CLACT kernels that
+# read the input themselves, and a row longer than one pass (k > 256 x 16)
+for dt in ["bf16", "f16", "f32"]:
+    for n, m in [(2, 4), (8, 16), (16, 32)]:
+        for score, shift, var, xd in [("magnitude", "token_mean", True, "normal"),
+                                      ("clact", "token_mean", False, "preact_shifted"),
+                                      ("weight", "none", False, "normal")]:
+            base = wl.SPECS["decode"].with_(name="sweep_act", t=3, k=256, n_out=64, dtype=dt, n=n, m=m, score=score,
+                                            shift=shift, var_rescale=var, alpha=0.5, act="relu2", x_dist=xd,
+                                            n_outliers=0)
+            PRUNE_CASES.append((f"act-{dt}-{n}:{m}-{score}-{shift}-{int(var)}", base))
+PRUNE_CASES.append(("act-long-row", wl.SPECS["relu2_fused"].with_(t=3, k=8192, shift="token_mean")))
 
 
 @pytest.mark.parametrize("label,spec", PRUNE_CASES, ids=[c[0] for c in PRUNE_CASES])
@@ -146,6 +158,20 @@ DECODE_CASES.append(wl.SPECS["batched"].with_(name="mm_bf16_weight_mean", t=12, 
                                               n=2, m=4, score="weight", alpha=0.5, shift="token_mean",
                                               var_rescale=True))
 DECODE_CASES.append(wl.SPECS["decode"].with_(name="decode_given_shift", t=2, k=512, n_out=256, shift="given"))
+# the squared-ReLU input transform on every decode kernel: one token (wide and
+# narrow outputs), 2-4 tokens, float32, and the matrix-core path
+ACT = dict(act="relu2", x_dist="normal", n_outliers=0)
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="act_t1w", t=1, k=4096, n_out=4096, **ACT))
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="act_t1w_preact", t=1, k=2048, n_out=4608,
+                                             **dict(ACT, x_dist="preact_shifted")))
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="act_t1_narrow", t=1, k=1024, n_out=776, **ACT))
+DECODE_CASES.append(wl.SPECS["batched"].with_(name="act_fused_t3_clact", t=3, k=512, n_out=136, **ACT))
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="act_fused_t4_mean", t=4, k=1024, n_out=776, **ACT))
+DECODE_CASES.append(wl.SPECS["tiny"].with_(name="act_tiny_f32_t8", t=8, shift="token_mean", act="relu2"))
+DECODE_CASES.append(wl.SPECS["batched"].with_(name="act_mm_t20_clact", t=20, k=1056, n_out=328, **ACT))
+DECODE_CASES.append(wl.SPECS["batched"].with_(name="act_mm_t12_bf16_mean", t=12, k=1600, n_out=264, dtype="bf16",
+                                              n=2, m=4, score="weight", alpha=0.5, shift="token_mean",
+                                              var_rescale=True, **ACT))
 
 
 @pytest.mark.parametrize("spec", DECODE_CASES, ids=[s.name for s in DECODE_CASES])
@@ -194,6 +220,13 @@ PREFILL_CASES.append(wl.SPECS["prefill"].with_(name="pre_weight_var", t=300, k=5
 PREFILL_CASES.append(wl.SPECS["prefill"].with_(name="pre_given", t=40, k=256, n_out=520, shift="given"))
 PREFILL_CASES.append(wl.SPECS["batched"].with_(name="pre_clact", t=96, k=512, n_out=264, n=2, m=4))
 PREFILL_CASES.append(wl.SPECS["prefill"].with_(name="pre_one_row", t=1, k=128, n_out=8))
+# squared ReLU applied by the library: CLACT with the token mean (the shift and
+# column kernels), another n:m (dense matrix cores) and a long row
+PREFILL_CASES.append(wl.SPECS["batched"].with_(name="pre_act_clact_mean", t=96, k=512, n_out=264, n=2, m=4,
+                                               shift="token_mean", act="relu2", x_dist="normal"))
+PREFILL_CASES.append(wl.SPECS["relu2_fused"].with_(name="pre_act_8_16", t=77, k=320, n_out=300, n=8, m=16))
+PREFILL_CASES.append(wl.SPECS["relu2_fused"].with_(name="pre_act_long_row", t=40, k=8192, n_out=136,
+                                                   shift="token_mean", var_rescale=True))
 # k-step counts 1, 3 and 12 (the GEMMs run three k steps per loop turn with a
 # peeled tail), and several ragged tiles in both directions
 for n, m in [(2, 4), (4, 8)]:

@@ -26,6 +26,9 @@ The five named workloads mirror the layer shapes of an 8B-class decoder
                down-projection after a squared-ReLU FFN).
 * ``batched``  X[T,14336] fp16 ~Laplace(0,0.3), T in {1,8,32},
                W[4096,14336]; 16:32, CLACT column score, variance rescale.
+* ``relu2_fused``  the relu2 layer fed its pre-activation: X[4096,16384]
+               bf16 = z ~N(-1,1) and the squared ReLU applied by the
+               library (act "relu2") before it prunes and packs.
 """
 from __future__ import annotations
 
@@ -47,7 +50,7 @@ class Spec:
     k: int
     n_out: int
     dtype: str            # "f32" | "f16" | "bf16"
-    x_dist: str           # "normal" | "student_t3_half" | "relu2_shifted" | "laplace"
+    x_dist: str           # "normal" | "student_t3_half" | "relu2_shifted" | "preact_shifted" | "laplace"
     n_outliers: int
     outlier_gain: float
     n: int
@@ -57,6 +60,7 @@ class Spec:
     shift: str            # "none" | "token_mean" | "given"
     var_rescale: bool
     w_std: float = 0.02
+    act: str = "none"     # "none" | "relu2": x holds the pre-activation u
 
     def with_(self, **kw) -> "Spec":
         return dataclasses.replace(self, **kw)
@@ -71,6 +75,8 @@ SPECS = {
     "relu2": Spec("relu2", 4096, 16384, 4096, "bf16", "relu2_shifted", 0, 1.0, 2, 4, "magnitude", 0.0,
                   "none", False),
     "batched": Spec("batched", 8, 14336, 4096, "f16", "laplace", 0, 1.0, 16, 32, "clact", 0.0, "none", True),
+    "relu2_fused": Spec("relu2_fused", 4096, 16384, 4096, "bf16", "preact_shifted", 0, 1.0, 2, 4, "magnitude",
+                        0.0, "none", False, act="relu2"),
 }
 
 
@@ -85,6 +91,8 @@ def _draw_x(rng: np.random.Generator, spec: Spec) -> np.ndarray:
         x = np.square(np.maximum(z, 0.0))
     elif spec.x_dist == "laplace":
         x = rng.laplace(0.0, 0.3, size=shape)
+    elif spec.x_dist == "preact_shifted":        # the up-projection output before max(0, .)^2
+        x = rng.normal(-1.0, 1.0, size=shape)
     elif spec.x_dist == "relu2_standard":
         z = rng.standard_normal(shape)
         x = np.square(np.maximum(z, 0.0))
@@ -161,6 +169,7 @@ def parity_specs() -> list:
         SPECS["decode"].with_(name="decode_small", k=1024, n_out=1000),
         SPECS["prefill"].with_(name="prefill_small", t=200, k=512, n_out=520, n_outliers=5),
         SPECS["relu2"].with_(name="relu2_small", t=136, k=1024, n_out=264),
+        SPECS["relu2_fused"].with_(name="relu2_fused_small", t=136, k=1024, n_out=264),
         SPECS["batched"].with_(name="batched_small_t1", t=1, k=1024, n_out=776),
         SPECS["batched"].with_(name="batched_small_t8", t=8, k=1024, n_out=776),
         SPECS["batched"].with_(name="batched_small_t32", t=32, k=1024, n_out=776),
