@@ -50,6 +50,13 @@ design notes as well):
 * Squared ReLU as the input transform: max(0, u)^2 in float32, rounded to
   the storage dtype -- what a separate elementwise pass would store; the
   fused kernel must see the same input.
+* Compact block metadata ([Guide] s2.1 table, s4.1: 3 bits per 2:4 block):
+  a block's kept positions as one code of ceil(log2 C(m, n)) bits -- the
+  rank of the position set in colexicographic order (the combinatorial
+  number system: sum over the ascending positions c_1 < ... < c_n of
+  C(c_i, i)) -- or as an m-bit mask (bit j = position j kept).  Codes are
+  laid end to end, block 0 in the lowest bits, least significant bit
+  first, in 32-bit words; each row starts on a fresh word.
 * Packed values are the float32 shifted values rounded to the storage dtype
   (round-to-nearest-even); the index metadata is one uint8 in-block position
   per kept value, ascending.
@@ -284,6 +291,86 @@ def linear_pages_form(pr: dict, w) -> np.ndarray:
     w64 = np.asarray(w, dtype=np.float64)
     xs = pr["xhat"].astype(np.float64) * pr["keep"] + pr["eta"].astype(np.float64)[:, None]
     return xs @ w64.T
+
+
+# ----------------------------------------------------------------------------
+# Compact block metadata ([Guide] s2.1 table, s4.1)
+# ----------------------------------------------------------------------------
+
+META_FORMATS = ("bitmap", "comb")
+
+
+def meta_width(n: int, m: int, fmt: str) -> int:
+    """Bits per m-block: m for the mask, ceil(log2 C(m, n)) for the combinatorial code."""
+    if fmt == "bitmap":
+        return m
+    if fmt == "comb":
+        count = math.comb(m, n)
+        return (count - 1).bit_length()            # ceil(log2 count); 0 when only one subset exists
+    raise ValueError(fmt)
+
+
+def meta_row_words(k: int, n: int, m: int, fmt: str) -> int:
+    """32-bit words per token row of codes."""
+    return ((k // m) * meta_width(n, m, fmt) + 31) // 32
+
+
+def comb_rank(positions) -> int:
+    """Colexicographic rank of an ascending position set: sum_i C(c_i, i), i = 1..n."""
+    return sum(math.comb(int(c), i + 1) for i, c in enumerate(positions))
+
+
+def comb_unrank(r: int, n: int, m: int) -> list:
+    """The ascending n-subset of range(m) with colexicographic rank r (greedy, largest first)."""
+    out = []
+    c = m
+    for i in range(n, 0, -1):
+        c -= 1
+        while math.comb(c, i) > r:
+            c -= 1
+        out.append(c)
+        r -= math.comb(c, i)
+    return out[::-1]
+
+
+def encode_meta(idx: np.ndarray, n: int, m: int, fmt: str) -> np.ndarray:
+    """uint8 in-block positions [t, k*n/m] -> uint32 codes [t, row_words]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    t = idx.shape[0]
+    nb = idx.shape[1] // n
+    w = meta_width(n, m, fmt)
+    words = meta_row_words(nb * m, n, m, fmt)
+    out = np.zeros((t, words), dtype=np.uint32)
+    for r in range(t):
+        acc = 0
+        for b in range(nb):
+            pos = idx[r, b * n:(b + 1) * n]
+            code = comb_rank(pos) if fmt == "comb" else sum(1 << int(c) for c in pos)
+            acc |= code << (b * w)
+        for j in range(words):
+            out[r, j] = (acc >> (32 * j)) & 0xFFFFFFFF
+    return out
+
+
+def decode_meta(codes: np.ndarray, k: int, n: int, m: int, fmt: str) -> np.ndarray:
+    """uint32 codes [t, row_words] -> uint8 in-block positions [t, k*n/m]."""
+    codes = np.asarray(codes, dtype=np.uint32)
+    t = codes.shape[0]
+    nb = k // m
+    w = meta_width(n, m, fmt)
+    out = np.zeros((t, nb * n), dtype=np.uint8)
+    for r in range(t):
+        acc = 0
+        for j in range(codes.shape[1]):
+            acc |= int(codes[r, j]) << (32 * j)
+        for b in range(nb):
+            code = (acc >> (b * w)) & ((1 << w) - 1)
+            if fmt == "comb":
+                pos = comb_unrank(code, n, m)
+            else:
+                pos = [c for c in range(m) if (code >> c) & 1]
+            out[r, b * n:(b + 1) * n] = pos
+    return out
 
 
 def rowwise_error(y_test: np.ndarray, y_ref: np.ndarray) -> float:

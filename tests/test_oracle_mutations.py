@@ -5,6 +5,8 @@ CPU, in this process only) and asserts that at least one pin in
 ``test_oracle_pins`` then fails.  This shows the pins are tight enough to
 catch that class of slip.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -80,6 +82,23 @@ def _relu_only(u, dtype):                                # forgets the square
     return _orig_round(np.where(u > 0, u, np.float32(0)).astype(np.float32), dtype)
 
 
+def _lex_rank(positions):                                # lexicographic instead of colex order
+    m = 32
+    n = len(positions)
+    r, prev = 0, -1
+    for i, c in enumerate(positions):
+        for v in range(prev + 1, int(c)):
+            r += math.comb(m - 1 - v, n - 1 - i)
+        prev = int(c)
+    return r
+
+
+def _width_floor(n, m, fmt):                             # floor instead of ceil of log2
+    if fmt == "comb":
+        return max(0, math.comb(m, n).bit_length() - 1)
+    return m
+
+
 _orig_factor = O.channel_factor
 _orig_var = O.var_factor
 _orig_round = O.round_to_dtype
@@ -99,6 +118,8 @@ MUTANTS = {
     "relu2_squares_negatives": ("squared_relu", _relu2_abs),
     "relu2_not_rounded": ("squared_relu", _relu2_unrounded),
     "relu2_not_squared": ("squared_relu", _relu_only),
+    "meta_lex_rank": ("comb_rank", _lex_rank),
+    "meta_width_floor": ("meta_width", _width_floor),
 }
 
 

@@ -348,6 +348,74 @@ def test_round_to_dtype_matches_torch(dtype, tdt):
 
 
 # --------------------------------------------------------------------------
+# compact block metadata
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,m", [(1, 4), (2, 4), (3, 4), (4, 4), (2, 8), (4, 8), (7, 8), (3, 16), (8, 16),
+                                 (1, 32), (2, 32), (31, 32)])
+def test_comb_rank_is_colex_position(n, m):
+    # enumerate every n-subset, sort them colexicographically (compare the
+    # largest position first), and check that the rank is the list position
+    subsets = sorted(itertools.combinations(range(m), n), key=lambda s: tuple(reversed(s)))
+    for pos, sub in enumerate(subsets):
+        assert O.comb_rank(sub) == pos
+        assert O.comb_unrank(pos, n, m) == list(sub)
+    assert len(subsets) == math.comb(m, n)
+
+
+def test_comb_rank_order_16_of_32():
+    # too many subsets to enumerate: the rank must order pairs as colex does
+    rng = np.random.Generator(np.random.PCG64(11))
+    top = math.comb(32, 16)
+    for _ in range(400):
+        a = tuple(sorted(rng.choice(32, 16, replace=False).tolist()))
+        b = tuple(sorted(rng.choice(32, 16, replace=False).tolist()))
+        ra, rb = O.comb_rank(a), O.comb_rank(b)
+        assert 0 <= ra < top and 0 <= rb < top
+        assert (ra < rb) == (tuple(reversed(a)) < tuple(reversed(b)))
+        assert O.comb_unrank(ra, 16, 32) == list(a)
+
+
+def test_meta_widths_match_printed_table():
+    # bits per element printed in the pattern table (4:8's 0.81 is the page's
+    # slip: 7 bits over 8 elements is 0.875) and 3 bits per 2:4 block
+    table = {(2, 4): "0.75", (8, 16): "0.875", (16, 32): "0.94"}
+    for (n, m), printed in table.items():
+        digits = len(printed.split(".")[1])
+        assert round(O.meta_width(n, m, "comb") / m, digits) == float(printed)
+    assert O.meta_width(2, 4, "comb") == 3
+    assert O.meta_width(4, 8, "comb") == 7
+    assert O.meta_width(4, 4, "comb") == 0
+    assert all(O.meta_width(n, m, "bitmap") == m for n, m in [(2, 4), (16, 32)])
+
+
+def test_meta_golden_words():
+    gold = _gold("meta_codes.json")
+    for case in gold["cases"]:
+        n, m, fmt = case["n"], case["m"], case["fmt"]
+        idx = np.array(case["idx"], dtype=np.uint8)
+        k = idx.shape[1] // n * m
+        words = O.encode_meta(idx, n, m, fmt)
+        assert words.tolist() == case["words"], case["derivation"]
+        assert np.array_equal(O.decode_meta(words, k, n, m, fmt), idx)
+
+
+@pytest.mark.parametrize("fmt", ["comb", "bitmap"])
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (4, 8), (8, 16), (16, 32), (5, 32)])
+def test_meta_round_trip_on_masks(fmt, n, m):
+    spec = wl.SPECS["prefill"].with_(t=3, k=32 * 37)
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    pr = O.prune(_x32(x), "bf16", n, m)
+    words = O.encode_meta(pr["idx"], n, m, fmt)
+    assert words.shape == (3, O.meta_row_words(spec.k, n, m, fmt))
+    assert np.array_equal(O.decode_meta(words, spec.k, n, m, fmt), pr["idx"])
+    if fmt == "bitmap":
+        # the mask bits are the kept channels, block after block
+        bits = np.unpackbits(words.view(np.uint8), axis=1, bitorder="little")[:, :spec.k].astype(bool)
+        assert np.array_equal(bits, pr["keep"])
+
+
+# --------------------------------------------------------------------------
 # squared ReLU as the input transform
 # --------------------------------------------------------------------------
 
