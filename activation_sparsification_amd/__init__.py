@@ -9,7 +9,10 @@ from ._binding import (  # noqa: F401
     PreparedWeight,
     PruneConfig,
     SpaError,
+    decode_meta,
+    encode_meta,
     lib,
+    meta_row_bytes,
     prepare_weight,
     prune_nm,
     sparse_linear_decode,

@@ -21,6 +21,7 @@ DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 SCORE = {"magnitude": 0, "weight": 1, "clact": 2}
 SHIFT = {"none": 0, "token_mean": 1, "given": 2}
 ACT = {"none": 0, "relu2": 1}
+META = {"bitmap": 0, "comb": 1}
 ENTRY_PRUNE, ENTRY_DECODE, ENTRY_PREFILL = 0, 1, 2
 
 
@@ -57,6 +58,12 @@ def lib() -> ctypes.CDLL:
         L.spa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(_Cfg)]
         L.prepare_weight.restype = ctypes.c_int
         L.prepare_weight.argtypes = [vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp]
+        L.spa_meta_row_bytes.restype = sz
+        L.spa_meta_row_bytes.argtypes = [i32, i32, i32, i32]
+        for name in ("spa_encode_meta", "spa_decode_meta"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp]
         L.prune_nm.restype = ctypes.c_int
         L.prune_nm.argtypes = [vp, i32, i32, i32, ctypes.POINTER(_Cfg), vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in ("sparse_linear_decode", "sparse_linear_prefill"):
@@ -68,7 +75,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("prepare_weight", "prune_nm", "sparse_linear_decode", "sparse_linear_prefill",
-           "spa_workspace_bytes", "spa_status_str")
+           "spa_workspace_bytes", "spa_status_str", "spa_meta_row_bytes", "spa_encode_meta", "spa_decode_meta")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -177,6 +184,33 @@ def prune_nm(x: torch.Tensor, cfg: PruneConfig, chan_scale: Optional[torch.Tenso
                           _ptr(vals), _ptr(idx), _ptr(eta), _ptr(nu), _ptr(ws), 0 if ws is None else ws.numel(),
                           _stream(dev)), "prune_nm")
     return vals, idx, eta, nu
+
+
+def meta_row_bytes(k: int, n: int, m: int, fmt: str = "comb") -> int:
+    """Bytes of packed block codes per token row (0 for invalid arguments)."""
+    return int(lib().spa_meta_row_bytes(k, n, m, META[fmt]))
+
+
+def encode_meta(idx: torch.Tensor, n: int, m: int, fmt: str = "comb") -> torch.Tensor:
+    """uint8 in-block positions [t, k*n/m] -> packed codes, uint32 [t, row_bytes/4] (as int32 storage)."""
+    dev = _dev(idx)
+    t, kept = idx.shape
+    k = kept // n * m
+    words = meta_row_bytes(k, n, m, fmt) // 4
+    codes = torch.zeros((t, words), dtype=torch.int32, device=dev)
+    _check(lib().spa_encode_meta(_ptr(idx), t, k, n, m, META[fmt], _ptr(codes) if codes.numel() else None,
+                                 _stream(dev)), "spa_encode_meta")
+    return codes
+
+
+def decode_meta(codes: torch.Tensor, k: int, n: int, m: int, fmt: str = "comb") -> torch.Tensor:
+    """Packed codes [t, row_words] -> uint8 in-block positions [t, k*n/m]."""
+    dev = _dev(codes)
+    t = codes.shape[0]
+    idx = torch.empty((t, k // m * n), dtype=torch.uint8, device=dev)
+    _check(lib().spa_decode_meta(_ptr(codes) if codes.numel() else None, t, k, n, m, META[fmt], _ptr(idx),
+                                 _stream(dev)), "spa_decode_meta")
+    return idx
 
 
 def _linear(fn_name: str, entry: int, x: torch.Tensor, pw: PreparedWeight, cfg: PruneConfig,

@@ -1,0 +1,294 @@
+// Compact block metadata: the uint8 in-block positions of the pruning pass
+// to and from packed per-block codes.
+//
+// A block's kept positions c_1 < ... < c_n (of m) become either
+//  - a combinatorial code of ceil(log2 C(m, n)) bits: the rank of the set in
+//    colexicographic order, sum_i C(c_i, i) (the activation sparsification
+//    guide's s2.1 table counts C(m, n) patterns per block and s4.1 stores a
+//    2:4 block in 3 bits), or
+//  - an m-bit mask, bit j set when position j is kept.
+// Codes are laid end to end along a token row, block 0 in the lowest bits,
+// least significant bit first, in 32-bit words; every row starts on a fresh
+// word.  Both kernels are bound by HBM: one thread per block, 256 blocks per
+// workgroup, and a wave's 64 codes fill exactly 2 x width whole words, which
+// the wave assembles in LDS and stores with one coalesced write.
+#include "spa_common.h"
+#include "spa_launch.h"
+
+namespace spa {
+
+// Binomial coefficients C(a, b), 0 <= a, b <= 32 (C(32, 16) = 601080390 fits
+// in 32 bits), from Pascal's rule at compile time.
+struct Binom {
+  uint32_t c[33][33];
+};
+constexpr Binom make_binom() {
+  Binom t{};
+  for (int a = 0; a <= 32; ++a) {
+    t.c[a][0] = 1;
+    for (int b = 1; b <= a; ++b) t.c[a][b] = t.c[a - 1][b - 1] + (b <= a - 1 ? t.c[a - 1][b] : 0u);
+  }
+  return t;
+}
+__constant__ Binom kBinom = make_binom();
+
+// Bits per block: m for the mask; ceil(log2 C(m, n)) for the code (0 when n == m).
+int meta_width(int n, int m, int format) {
+  if (format == SPA_META_BITMAP) return m;
+  const uint32_t count = make_binom().c[m][n];
+  int w = 0;
+  while (w < 32 && (uint64_t(1) << w) < count) ++w;
+  return w;
+}
+
+struct MetaArgs {
+  const uint8_t* idx;   // encode input [t][nb * n]
+  uint8_t* idx_out;     // decode output [t][nb * n]
+  uint32_t* codes;      // [t][row_words]
+  int nb;               // blocks per row
+  int chunks;           // workgroups per row
+  int n, m, width, row_words, format;
+  int aligned;          // rows of positions start on 16-byte boundaries
+};
+
+// Blocks per thread: 16 bytes of positions (one vector access) when n
+// divides 16, else one block with byte accesses.
+template <int NV>
+constexpr int blocks_per_thread() { return NV ? 16 / NV : 1; }
+
+// Positions of blocks b .. b + BT - 1 of one row; blocks past the row read 0.
+template <int NV, int BT>
+__device__ __forceinline__ void load_group(const uint8_t* row, int b, const MetaArgs& a, uint8_t (&c)[BT * NV]) {
+  if (a.aligned && b + BT <= a.nb) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + (size_t)b * NV);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
+  } else {
+#pragma unroll
+    for (int j = 0; j < BT * NV; ++j) c[j] = b + j / NV < a.nb ? row[(size_t)b * NV + j] : (uint8_t)0;
+  }
+}
+
+template <int NV, int BT>
+__device__ __forceinline__ void store_group(uint8_t* row, int b, const MetaArgs& a, const uint8_t (&c)[BT * NV]) {
+  if (a.aligned && b + BT <= a.nb) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (uint32_t)c[4 * q] | ((uint32_t)c[4 * q + 1] << 8) | ((uint32_t)c[4 * q + 2] << 16) |
+             ((uint32_t)c[4 * q + 3] << 24);
+    *reinterpret_cast<uint4*>(row + (size_t)b * NV) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < BT * NV; ++j)
+      if (b + j / NV < a.nb) row[(size_t)b * NV + j] = c[j];
+  }
+}
+
+// The rows C(., i), i = 0..n, of the binomial table into LDS as tab[i][c].
+__device__ __forceinline__ void load_tab(uint32_t (*tab)[33], int n) {
+  for (int e = threadIdx.x; e < (n + 1) * 33; e += blockDim.x) {
+    const int i = e / 33, c = e - i * 33;
+    tab[i][c] = kBinom.c[c][i];
+  }
+}
+
+// One block's code from its positions (an input position >= 32 is folded into
+// range: the code is then unspecified, the table access stays in bounds).
+__device__ __forceinline__ uint32_t add_pos(uint32_t code, uint32_t c, int j, int format,
+                                            const uint32_t (*tab)[33]) {
+  c &= 31u;
+  return code + (format == SPA_META_BITMAP ? (1u << c) : tab[j + 1][c]);
+}
+
+// Work split: a thread takes G groups of BT consecutive blocks (16 bytes of
+// positions per group); group s of lane l in wave v starts at block
+// (((chunk * 4 + v) * G + s) * 64 + l) * BT of its row, so each load is
+// coalesced across the wave.  A wave's codes fill 2 * G * BT * width whole
+// words, assembled in LDS (bitwise OR, as a code may straddle two words) and
+// stored coalesced.  G = 1: token rows are short (a 2:4 row of 16384
+// channels is 8 KB of positions), and larger groups left lanes idle (4
+// groups: 16 -> 27 us for the 2:4 encode at 4096 x 16384).
+template <int NV>
+constexpr int groups_per_thread() { return 1; }
+
+template <int NV>
+__global__ void __launch_bounds__(256) k_encode_meta(MetaArgs a) {
+  constexpr int BT = blocks_per_thread<NV>(), G = groups_per_thread<NV>();
+  extern __shared__ uint32_t s_dyn[];
+  __shared__ uint32_t s_binom[33][33];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row = blockIdx.x / a.chunks;
+  const int chunk = blockIdx.x - row * a.chunks;
+  const int w = a.width;
+  const int nw = 2 * G * BT * w;                           // words of this wave
+  uint32_t* s_words = s_dyn + wv * nw;
+  const int64_t wb = (int64_t)(chunk * 4 + wv) * G * 64 * BT;   // the wave's first block
+  if (a.format == SPA_META_COMB) load_tab(s_binom, NV ? NV : a.n);
+  for (int j = lane; j < nw; j += 64) s_words[j] = 0u;
+
+  const uint8_t* rp = a.idx + (size_t)row * a.nb * (NV ? NV : a.n);
+  uint32_t code[G][BT];
+  if constexpr (NV > 0) {
+    uint8_t c[G][BT * NV];
+#pragma unroll
+    for (int g = 0; g < G; ++g) load_group<NV, BT>(rp, (int)(wb + (g * 64 + lane) * BT), a, c[g]);
+    __syncthreads();                                       // the table and the cleared words
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int b = (int)(wb + (g * 64 + lane) * BT);
+#pragma unroll
+      for (int q = 0; q < BT; ++q) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int jj = 0; jj < NV; ++jj) v = add_pos(v, c[g][q * NV + jj], jj, a.format, s_binom);
+        code[g][q] = b + q < a.nb ? v : 0u;
+      }
+    }
+  } else {
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int b = (int)(wb + g * 64 + lane);
+      uint32_t v = 0;
+      if (b < a.nb)
+        for (int jj = 0; jj < a.n; ++jj) v = add_pos(v, rp[(size_t)b * a.n + jj], jj, a.format, s_binom);
+      code[g][0] = v;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int q = 0; q < BT; ++q) {
+      const int bit = ((g * 64 + lane) * BT + q) * w;
+      if (code[g][q]) {
+        atomicOr(&s_words[bit >> 5], code[g][q] << (bit & 31));
+        if ((bit & 31) + w > 32) atomicOr(&s_words[(bit >> 5) + 1], code[g][q] >> (32 - (bit & 31)));
+      }
+    }
+  __syncthreads();
+  const int64_t gbase = (wb * w) >> 5;                     // wb * w is a multiple of 64
+  uint32_t* out = a.codes + (size_t)row * a.row_words;
+  for (int j = lane; j < nw; j += 64)
+    if (gbase + j < a.row_words) out[gbase + j] = s_words[j];
+}
+
+template <int NV>
+__global__ void __launch_bounds__(256) k_decode_meta(MetaArgs a) {
+  constexpr int BT = blocks_per_thread<NV>(), G = groups_per_thread<NV>();
+  constexpr int CAP = NV ? NV : 32;                        // positions per block held in registers
+  extern __shared__ uint32_t s_dyn[];
+  __shared__ uint32_t s_binom[33][33];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row = blockIdx.x / a.chunks;
+  const int chunk = blockIdx.x - row * a.chunks;
+  const int w = a.width, m = a.m;
+  const int n = NV ? NV : a.n;
+  const int nw = 2 * G * BT * w;
+  uint32_t* s_words = s_dyn + wv * nw;
+  const int64_t wb = (int64_t)(chunk * 4 + wv) * G * 64 * BT;
+  if (a.format == SPA_META_COMB) load_tab(s_binom, n);
+  {
+    const int64_t gbase = (wb * w) >> 5;
+    const uint32_t* in = a.codes + (size_t)row * a.row_words;
+    for (int j = lane; j < nw; j += 64) s_words[j] = gbase + j < a.row_words ? in[gbase + j] : 0u;
+  }
+  __syncthreads();
+
+  uint8_t* rp = a.idx_out + (size_t)row * a.nb * n;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    uint8_t c[BT * CAP];
+#pragma unroll
+    for (int q = 0; q < BT; ++q) {
+      uint32_t code = 0;
+      if (w > 0) {
+        const int bit = ((g * 64 + lane) * BT + q) * w, sh = bit & 31;
+        uint64_t v = s_words[bit >> 5];
+        if (sh + w > 32) v |= (uint64_t)s_words[(bit >> 5) + 1] << 32;
+        code = (uint32_t)((v >> sh) & ((uint64_t(1) << w) - 1));
+      }
+      uint32_t mask = code;
+      if (a.format == SPA_META_COMB) {
+        // greedy unranking in one pass over the positions, largest first: take
+        // c while i positions remain and C(c, i) <= the remaining rank (C(c, i)
+        // is 0 once c < i, so exactly n are taken); the same m steps on every
+        // lane
+        uint32_t r = code;
+        int i = n;
+        mask = 0;
+        for (int cc = m - 1; cc >= 0; --cc) {
+          const uint32_t bin = s_binom[i][cc];
+          const bool take = i > 0 && bin <= r;
+          mask |= take ? (1u << cc) : 0u;
+          r -= take ? bin : 0u;
+          i -= take ? 1 : 0;
+        }
+      }
+      // the set bits in ascending order; a mask without n set bits gives
+      // unspecified positions (zeros), never an access out of bounds
+#pragma unroll
+      for (int s2 = 0; s2 < CAP; ++s2) {
+        c[q * CAP + s2] = (uint8_t)(mask ? __builtin_ctz(mask) : 0);
+        mask &= mask - 1u;
+      }
+    }
+    if constexpr (NV > 0) {
+      store_group<NV, BT>(rp, (int)(wb + (g * 64 + lane) * BT), a, c);
+    } else {
+      const int b = (int)(wb + g * 64 + lane);
+      if (b < a.nb) {
+#pragma unroll
+        for (int s2 = 0; s2 < CAP; ++s2)
+          if (s2 < n) rp[(size_t)b * n + s2] = c[s2];
+      }
+    }
+  }
+}
+
+template <bool ENCODE>
+static hipError_t meta_launch(const MetaArgs& a, int t, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)a.chunks * t));
+#define SPA_META_CASE(NV)                                                                            \
+  {                                                                                                  \
+    const size_t lds = (size_t)4 * 2 * groups_per_thread<NV>() * blocks_per_thread<NV>() * a.width * 4; \
+    if (ENCODE) hipLaunchKernelGGL(k_encode_meta<NV>, grid, dim3(256), lds, st, a);                  \
+    else hipLaunchKernelGGL(k_decode_meta<NV>, grid, dim3(256), lds, st, a);                         \
+  }                                                                                                  \
+  break;
+  switch (a.n) {
+    case 1: SPA_META_CASE(1)
+    case 2: SPA_META_CASE(2)
+    case 4: SPA_META_CASE(4)
+    case 8: SPA_META_CASE(8)
+    case 16: SPA_META_CASE(16)
+    default: SPA_META_CASE(0)
+  }
+#undef SPA_META_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_meta(bool encode, const uint8_t* idx, uint8_t* idx_out, uint32_t* codes, int t, int k, int n,
+                       int m, int format, hipStream_t st) {
+  MetaArgs a{};
+  a.idx = idx;
+  a.idx_out = idx_out;
+  a.codes = codes;
+  a.nb = k / m;
+  a.n = n;
+  a.m = m;
+  a.format = format;
+  a.width = meta_width(n, m, format);
+  a.row_words = (int)(((int64_t)a.nb * a.width + 31) / 32);
+  // blocks per workgroup: 256 threads x G groups (1) x BT blocks
+  const int bt = (n == 1 || n == 2 || n == 4 || n == 8 || n == 16) ? 16 / n : 1;
+  a.chunks = (int)(((int64_t)a.nb + 256 * bt - 1) / (256 * bt));
+  a.aligned = ((int64_t)a.nb * n) % 16 == 0;
+  if (t == 0 || a.nb == 0) return hipSuccess;
+  if ((int64_t)a.chunks * t > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (encode && a.row_words == 0) return hipSuccess;      // nothing to store
+  return encode ? meta_launch<true>(a, t, st) : meta_launch<false>(a, t, st);
+}
+
+}  // namespace spa

@@ -85,6 +85,13 @@ spa_status check_linear(const void* x, int32_t t, const spa_weight* w, const spa
   return SPA_OK;
 }
 
+bool valid_meta(int64_t k, int32_t n, int32_t m, int32_t format) {
+  if (m != 4 && m != 8 && m != 16 && m != 32) return false;
+  if (n < 1 || n > m) return false;
+  if (k < m || k > kMaxDim || k % m) return false;
+  return format == SPA_META_BITMAP || format == SPA_META_COMB;
+}
+
 }  // namespace
 
 extern "C" {
@@ -255,6 +262,31 @@ spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, 
   g.t = t; g.k = k; g.n_out = w->n_out;
   g.sparse24 = s24 ? 1 : 0;
   return hip_status(spa::launch_gemm(w->dtype, g, st));
+}
+
+size_t spa_meta_row_bytes(int32_t k, int32_t n, int32_t m, int32_t format) {
+  if (!valid_meta(k, n, m, format)) return 0;
+  return (size_t)4 * (((int64_t)(k / m) * spa::meta_width(n, m, format) + 31) / 32);
+}
+
+spa_status spa_encode_meta(const uint8_t* idx, int32_t t, int32_t k, int32_t n, int32_t m, int32_t format,
+                           void* codes, void* stream) {
+  if (!valid_meta(k, n, m, format) || t < 0 || t > kMaxDim) return SPA_ERR_INVALID;
+  if (t == 0 || spa_meta_row_bytes(k, n, m, format) == 0) return SPA_OK;
+  if (!idx || !codes || !aligned16(idx) || !aligned16(codes)) return SPA_ERR_INVALID;
+  return hip_status(spa::launch_meta(true, idx, nullptr, static_cast<uint32_t*>(codes), t, k, n, m, format,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+spa_status spa_decode_meta(const void* codes, int32_t t, int32_t k, int32_t n, int32_t m, int32_t format,
+                           uint8_t* idx_out, void* stream) {
+  if (!valid_meta(k, n, m, format) || t < 0 || t > kMaxDim) return SPA_ERR_INVALID;
+  if (t == 0) return SPA_OK;
+  const bool has_codes = spa_meta_row_bytes(k, n, m, format) > 0;
+  if (!idx_out || !aligned16(idx_out) || (has_codes && (!codes || !aligned16(codes)))) return SPA_ERR_INVALID;
+  return hip_status(spa::launch_meta(false, nullptr, idx_out,
+                                     const_cast<uint32_t*>(static_cast<const uint32_t*>(codes)), t, k, n, m,
+                                     format, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

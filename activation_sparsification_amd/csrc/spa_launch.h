@@ -74,6 +74,11 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
                         DecodeArgs* plan);
 hipError_t launch_decode(int dtype, DecodeArgs& a, hipStream_t st);
 
+// ---- compact block metadata ----
+int meta_width(int n, int m, int format);
+hipError_t launch_meta(bool encode, const uint8_t* idx, uint8_t* idx_out, uint32_t* codes, int t, int k, int n,
+                       int m, int format, hipStream_t st);
+
 // ---- prefill ----
 struct PrefillArgs {
   const void* w;             // [n_out][k]

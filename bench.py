@@ -205,6 +205,49 @@ def measure(name, steps, warmup):
     return rec
 
 
+def measure_meta(fmt, n, m, t, k, steps, warmup):
+    """Encode and decode of packed block codes: GB/s of positions plus codes moved."""
+    import ctypes
+    import activation_sparsification_amd as spa
+    from activation_sparsification_amd._binding import META, _stream
+    L = spa.lib()
+    dev = torch.device("cuda:0")
+    idx = wl.random_positions(t, k, n, m).to(dev)
+    row_bytes = spa.meta_row_bytes(k, n, m, fmt)
+    copies = max(3, math.ceil(3 * MALL_BYTES / (idx.numel() + t * row_bytes)))
+    idxs = [idx] + [idx.clone() for _ in range(copies - 1)]
+    codes = [torch.empty((t, row_bytes // 4), dtype=torch.int32, device=dev) for _ in range(copies)]
+    outs = [torch.empty_like(idx) for _ in range(copies)]
+    st = _stream(dev)
+    f = META[fmt]
+    enc = [lambda i=i: L.spa_encode_meta(ctypes.c_void_p(idxs[i].data_ptr()), t, k, n, m, f,
+                                         ctypes.c_void_p(codes[i].data_ptr()), st) for i in range(copies)]
+    dec = [lambda i=i: L.spa_decode_meta(ctypes.c_void_p(codes[i].data_ptr()), t, k, n, m, f,
+                                         ctypes.c_void_p(outs[i].data_ptr()), st) for i in range(copies)]
+    recs = []
+    for name, calls in (("encode", enc), ("decode", dec)):
+        for i in range(warmup):
+            assert calls[i % copies]() == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(2e6))
+        e0.record()
+        for i in range(steps):
+            calls[i % copies]()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        b = idx.numel() + t * row_bytes
+        gbs = b / (ms * 1e-3) / 1e9
+        recs.append(dict(workload=f"meta_{name}_{fmt}_{n}_{m}", unit="GB/s", value=gbs, ms_per_step=ms,
+                         pct_of_peak=100.0 * gbs / PEAK_HBM_GBS, algorithmic_bytes=b, copies=copies,
+                         desc=f"{name} of {fmt} block codes, {n}:{m}, positions [{t},{k * n // m}] uint8"))
+    assert torch.equal(outs[(steps - 1) % copies], idx), "decoded positions differ from the input"
+    del idxs, codes, outs
+    torch.cuda.empty_cache()
+    return recs
+
+
 def cpu_baseline(name, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the workload on the host cores."""
     from oracle import nm_oracle as O
@@ -299,6 +342,7 @@ def main():
                 continue
             st = max(10, args.steps // 4) if name in ("prefill", "relu2", "relu2_fused") else args.steps
             secondary.append(measure(name, st, max(5, args.warmup // 2)))
+        secondary += measure_meta("comb", 2, 4, 4096, 16384, args.steps, max(5, args.warmup // 2))
 
     decode = head["unit"] == "GB/s"
     traffic = read_traffic() if args.workload == "decode" else None

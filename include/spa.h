@@ -72,6 +72,7 @@ enum { SPA_F32 = 0, SPA_F16 = 1, SPA_BF16 = 2 };
 enum { SPA_SCORE_MAGNITUDE = 0, SPA_SCORE_WEIGHT = 1, SPA_SCORE_CLACT = 2 };
 enum { SPA_SHIFT_NONE = 0, SPA_SHIFT_TOKEN_MEAN = 1, SPA_SHIFT_GIVEN = 2 };
 enum { SPA_ACT_NONE = 0, SPA_ACT_RELU2 = 1 };
+enum { SPA_META_BITMAP = 0, SPA_META_COMB = 1 };
 enum { SPA_ENTRY_PRUNE = 0, SPA_ENTRY_DECODE = 1, SPA_ENTRY_PREFILL = 2 };
 
 /* Pruning configuration.  m in {4, 8, 16, 32}; 1 <= n <= m; k % m == 0. */
@@ -170,6 +171,37 @@ spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, c
 spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
                                  const float* eta_in, void* y, uint8_t* idx_out, float* nu_out,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Compact block metadata -- the in-block positions that prune_nm and the
+ * linear calls return (uint8, ascending, n per m-block) to and from packed
+ * per-block codes, for storing pruned activations (e.g. in a cache).
+ *  SPA_META_COMB    ceil(log2 C(m, n)) bits per block (the guide's s2.1
+ *                   table counts C(m, n) patterns per block; its s4.1 keeps a
+ *                   2:4 block in 3 bits): the rank of the position set in
+ *                   colexicographic order, sum_i C(c_i, i) over the
+ *                   ascending positions c_1 < ... < c_n; 0 bits when n == m.
+ *  SPA_META_BITMAP  m bits per block, bit j set when position j is kept.
+ * Codes are laid end to end along a token row, block 0 in the lowest bits,
+ * least significant bit first, in 32-bit words; each row starts on a new
+ * word and its unused high bits are zero.
+ *
+ * spa_meta_row_bytes -- bytes of codes per token row: 4 * ceil((k/m) *
+ *   bits per block / 32).  0 for invalid arguments as well.
+ * spa_encode_meta -- idx [device] [t][k*n/m] uint8 -> codes [device]
+ *   [t][row_bytes/4] uint32.  Positions that are not ascending or not below
+ *   m give unspecified codes (never an access outside the buffers).
+ * spa_decode_meta -- codes -> idx_out [device] [t][k*n/m].  A code that no
+ *   n-subset has (a rank >= C(m, n), a mask without n set bits) gives
+ *   unspecified positions below m.
+ * Both require m in {4, 8, 16, 32}, 1 <= n <= m, k % m == 0, t >= 0 (0 is a
+ * no-op), 16-byte aligned buffers.
+ */
+size_t spa_meta_row_bytes(int32_t k, int32_t n, int32_t m, int32_t format);
+spa_status spa_encode_meta(const uint8_t* idx, int32_t t, int32_t k, int32_t n, int32_t m, int32_t format,
+                           void* codes, void* stream);
+spa_status spa_decode_meta(const void* codes, int32_t t, int32_t k, int32_t n, int32_t m, int32_t format,
+                           uint8_t* idx_out, void* stream);
 
 /* Workspace bytes an entry point needs for these sizes (0 if none); 0 for
  * invalid arguments as well. */

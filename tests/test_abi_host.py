@@ -1,0 +1,103 @@
+"""The C ABI on the host (CPU only, no device call).
+
+The library must load and export every function ``include/spa.h``
+declares; the host-only parts of the ABI (status text, sizes, argument
+validation that rejects before any launch) are checked without a GPU.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spa.h")
+LIB = os.path.join(ROOT, "activation_sparsification_amd", "libspa.so")
+
+SPA_OK, SPA_ERR_INVALID = 0, 1
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} is not built")
+    L = ctypes.CDLL(LIB)
+    L.spa_status_str.restype = ctypes.c_char_p
+    L.spa_status_str.argtypes = [ctypes.c_int]
+    L.spa_meta_row_bytes.restype = ctypes.c_size_t
+    L.spa_meta_row_bytes.argtypes = [ctypes.c_int32] * 4
+    return L
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for need in ["prepare_weight", "prune_nm", "sparse_linear_decode", "sparse_linear_prefill",
+                 "spa_workspace_bytes", "spa_status_str", "spa_meta_row_bytes", "spa_encode_meta",
+                 "spa_decode_meta"]:
+        assert need in names, names
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in _declared():
+        assert hasattr(lib, name), f"{name} declared in spa.h but not exported"
+
+
+def test_binding_lists_every_declared_function():
+    import activation_sparsification_amd as spa
+    assert sorted(spa.EXPORTS) == _declared()
+
+
+def test_status_strings(lib):
+    for code in range(4):
+        assert lib.spa_status_str(code)
+    assert lib.spa_status_str(SPA_ERR_INVALID) != lib.spa_status_str(SPA_OK)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (4, 8), (8, 16), (16, 32), (4, 4), (32, 32)])
+def test_meta_row_bytes(lib, n, m):
+    k = 16384
+    comb = (math.comb(m, n) - 1).bit_length()
+    assert lib.spa_meta_row_bytes(k, n, m, 1) == 4 * ((k // m * comb + 31) // 32)
+    assert lib.spa_meta_row_bytes(k, n, m, 0) == 4 * ((k // m * m + 31) // 32)
+
+
+def test_meta_rejections_happen_before_any_launch(lib):
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.spa_encode_meta.restype = ctypes.c_int
+    lib.spa_encode_meta.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.spa_decode_meta.restype = ctypes.c_int
+    lib.spa_decode_meta.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp]
+    assert lib.spa_meta_row_bytes(64, 2, 3, 1) == 0                     # m not a supported width
+    assert lib.spa_meta_row_bytes(66, 2, 4, 1) == 0                     # k not whole blocks
+    assert lib.spa_meta_row_bytes(64, 5, 4, 1) == 0                     # n > m
+    assert lib.spa_meta_row_bytes(64, 2, 4, 7) == 0                     # unknown format
+    for fn in (lib.spa_encode_meta, lib.spa_decode_meta):
+        assert fn(None, 4, 64, 2, 4, 1, None, None) == SPA_ERR_INVALID  # null buffers
+        assert fn(None, -1, 64, 2, 4, 1, None, None) == SPA_ERR_INVALID
+        assert fn(None, 4, 64, 2, 4, 9, None, None) == SPA_ERR_INVALID
+        assert fn(None, 0, 64, 2, 4, 1, None, None) == SPA_OK           # t == 0: nothing to do
+        assert fn(16, 4, 64, 2, 4, 1, 24, None) == SPA_ERR_INVALID      # unaligned buffers
+
+
+def test_linear_rejections_happen_before_any_launch(lib):
+    import activation_sparsification_amd._binding as B
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L = lib
+    L.prune_nm.restype = ctypes.c_int
+    L.prune_nm.argtypes = [vp, i32, i32, i32, ctypes.POINTER(B._Cfg), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    good = B.PruneConfig(2, 4).c()
+    # k not a multiple of 16 / of m, n > m, an unknown activation, null input
+    assert L.prune_nm(16, 2, 4, 60, ctypes.byref(good), None, None, 32, None, None, None, None, 0, None) == 1
+    bad = B.PruneConfig(5, 4).c()
+    assert L.prune_nm(16, 2, 4, 64, ctypes.byref(bad), None, None, 32, None, None, None, None, 0, None) == 1
+    bad = B._Cfg(2, 4, 0, 0, 0, 9)
+    assert L.prune_nm(16, 2, 4, 64, ctypes.byref(bad), None, None, 32, None, None, None, None, 0, None) == 1
+    assert L.prune_nm(None, 2, 4, 64, ctypes.byref(good), None, None, 32, None, None, None, None, 0, None) == 1
+    assert L.prune_nm(None, 2, 0, 64, ctypes.byref(good), None, None, None, None, None, None, None, 0, None) == 0

@@ -79,3 +79,22 @@ def test_full_size_sampled(name):
     y_got = f32(y)[np.ix_(rows, cols)]
     err = O.rowwise_error(y_got, y_ref)
     assert err <= O.TOLERANCE[spec.dtype], f"{name}: sampled y error {err}"
+
+
+@pytest.mark.parametrize("fmt,n,m,t,k", [("comb", 2, 4, 4096, 16384), ("bitmap", 2, 4, 4096, 16384),
+                                         ("comb", 16, 32, 32, 14336), ("comb", 8, 16, 1, 4096)])
+def test_meta_full_size(fmt, n, m, t, k):
+    # every row: decode(encode(positions)) gives the positions back; sampled
+    # rows: the codes equal the oracle's bit for bit
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    dev = torch.device("cuda:0")
+    print(f"[full-size meta] {fmt} {n}:{m} t={t} k={k}", flush=True)
+    idx = wl.random_positions(t, k, n, m, seed=3)
+    idx_d = idx.to(dev)
+    codes = spa.encode_meta(idx_d, n, m, fmt)
+    back = spa.decode_meta(codes, k, n, m, fmt)
+    torch.cuda.synchronize()
+    assert torch.equal(back, idx_d), "round trip differs"
+    rows = _sample(t, 12, 4)
+    want = O.encode_meta(idx.numpy()[rows], n, m, fmt)
+    assert np.array_equal(codes.cpu().numpy().view(np.uint32)[rows], want)

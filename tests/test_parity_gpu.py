@@ -121,6 +121,61 @@ def test_prune_empty_and_invalid():
 
 
 # ---------------------------------------------------------------------------
+# compact block metadata
+# ---------------------------------------------------------------------------
+META_CASES = []
+for fmt in ["comb", "bitmap"]:
+    for n, m in [(2, 4), (1, 4), (3, 4), (4, 4), (4, 8), (3, 8), (8, 16), (5, 16), (16, 32), (12, 32), (1, 32),
+                 (32, 32)]:
+        META_CASES.append((fmt, n, m, 300))
+    # several workgroups per row, rows that start off 16-byte boundaries
+    for n, m in [(2, 4), (1, 4), (8, 16), (16, 32), (3, 8)]:
+        META_CASES.append((fmt, n, m, 5001))
+
+
+@pytest.mark.parametrize("fmt,n,m,nb", META_CASES)
+def test_meta_parity(fmt, n, m, nb):
+    # rows of 300 blocks: several waves, a partial workgroup, a ragged last word
+    dev = _dev()
+    t, k = 3, nb * m
+    idx = wl.random_positions(t, k, n, m, seed=n * 64 + m)
+    want = O.encode_meta(idx.numpy(), n, m, fmt)
+    codes = spa.encode_meta(idx.to(dev), n, m, fmt)
+    back = spa.decode_meta(codes, k, n, m, fmt)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy().view(np.uint32)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want), "codes differ"
+    assert np.array_equal(back.cpu().numpy(), idx.numpy()), "decoded positions differ"
+    # the oracle's codes decode to the same positions on the GPU
+    back2 = spa.decode_meta(torch.from_numpy(want.view(np.int32)).to(dev), k, n, m, fmt)
+    torch.cuda.synchronize()
+    assert np.array_equal(back2.cpu().numpy(), idx.numpy())
+
+
+@pytest.mark.parametrize("fmt", ["comb", "bitmap"])
+def test_meta_of_pruned_masks(fmt):
+    # the positions prune_nm returns, packed and unpacked
+    dev = _dev()
+    spec = wl.SPECS["relu2"].with_(t=7, k=4096 + 64)
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    pr = oracle_for(spec, x, None)
+    codes = spa.encode_meta(torch.from_numpy(pr["idx"]).to(dev), 2, 4, fmt)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy().view(np.uint32), O.encode_meta(pr["idx"], 2, 4, fmt))
+
+
+def test_meta_empty_and_invalid():
+    dev = _dev()
+    idx = torch.zeros((0, 32), dtype=torch.uint8, device=dev)
+    assert spa.encode_meta(idx, 2, 4).shape == (0, 2)                  # 16 blocks x 3 bits -> 2 words
+    with pytest.raises(spa.SpaError):
+        spa.encode_meta(torch.zeros((2, 30), dtype=torch.uint8, device=dev), 2, 6)   # m = 6 is not a width
+    with pytest.raises(spa.SpaError):
+        spa.decode_meta(torch.zeros((2, 3), dtype=torch.int32, device=dev), 64, 5, 4)  # n > m
+
+
+# ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
 DECODE_CASES = [s for s in wl.parity_specs() if s.t <= 32]

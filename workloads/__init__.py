@@ -33,6 +33,8 @@ The five named workloads mirror the layer shapes of an 8B-class decoder
 from __future__ import annotations
 
 import dataclasses
+import itertools
+import math
 from typing import Optional
 
 import numpy as np
@@ -160,6 +162,19 @@ def adversarial_x(kind: str, t: int, k: int, m: int, dtype: str, seed: int = 0) 
     else:
         raise ValueError(kind)
     return _to_storage(x, dtype)
+
+
+def random_positions(t: int, k: int, n: int, m: int, seed: int = 0) -> torch.Tensor:
+    """Uniformly random kept positions: n distinct ascending in-block indices per m-block, uint8 [t, k*n/m]."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    if math.comb(m, n) <= 1 << 16:
+        # one uniform draw per block from the list of every n-subset
+        subsets = np.array(list(itertools.combinations(range(m), n)), dtype=np.uint8)
+        pos = subsets[rng.integers(0, len(subsets), size=(t, k // m))]
+    else:
+        keys = rng.random((t, k // m, m))
+        pos = np.sort(np.argsort(keys, axis=-1)[..., :n], axis=-1)
+    return torch.from_numpy(np.ascontiguousarray(pos.reshape(t, k // m * n).astype(np.uint8)))
 
 
 def parity_specs() -> list:
