@@ -35,6 +35,12 @@ design notes as well):
   kept).
 * The weight norm of channel k is taken over the outputs: for y = x W^T with
   W[n_out, k], it is the 2-norm of column k of W.
+* Amber-Pruner factor ([Guide] s2.2.2): the 0.5th and 99.5th percentiles of
+  all weights of the matrix (linear interpolation between order statistics,
+  in float64) bound the weights kept; the kept weights are standardised with
+  their own mean and population standard deviation; f_k is the 2-norm over
+  the outputs of channel k's standardised kept weights, to the power alpha.
+  The standard deviation scales every f_k alike, so it cannot change a mask.
 * f_k = ||W[:,k]||_2^alpha is formed once from the exact sum of squares,
   raised to alpha/2 in float64 and rounded to float32.
 * eta (D-PTS) = float32(float64(exact row sum) / K).
@@ -114,6 +120,48 @@ def channel_factor(w: np.ndarray, alpha: float) -> np.ndarray:
     for c in range(k):
         sumsq = math.fsum(sq[:, c].tolist())
         f[c] = np.float32(sumsq ** (alpha / 2.0))
+    return f
+
+
+def percentile_linear(v_sorted: np.ndarray, q: float) -> float:
+    """The q-th percentile (0..100) of sorted values: interpolate between the
+    order statistics at floor and ceil of q/100 * (N - 1), in float64."""
+    n = v_sorted.size
+    pos = q / 100.0 * (n - 1)
+    i = int(math.floor(pos))
+    g = pos - i
+    a = float(v_sorted[i])
+    b = float(v_sorted[min(i + 1, n - 1)])
+    return a + (b - a) * g
+
+
+def amber_factor(w: np.ndarray, alpha: float = 1.0, q_lo: float = 0.5, q_hi: float = 99.5) -> np.ndarray:
+    """Amber-Pruner channel factor ([Guide] s2.2.2), float32 [k].
+
+    1. keep the weights between the q_lo-th and q_hi-th percentiles of the
+       whole matrix (outliers are removed);
+    2. standardise the kept weights: z = (w - mean) / std (their own mean and
+       population standard deviation);
+    3. f_k = (sum over outputs j of z_jk^2, kept weights only) ** (alpha / 2).
+    Differences and squares are float64, their sums exact (math.fsum) and
+    rounded once; the ratio and the power are float64, the result float32.
+    """
+    w64 = np.asarray(w, dtype=np.float64)
+    v = np.sort(w64.ravel())
+    lo, hi = percentile_linear(v, q_lo), percentile_linear(v, q_hi)
+    kept = (w64 >= lo) & (w64 <= hi)
+    vals = w64[kept]
+    cnt = vals.size
+    mean = math.fsum(vals.tolist()) / cnt
+    dev = vals - mean
+    var = math.fsum((dev * dev).tolist()) / cnt
+    k = w64.shape[1]
+    f = np.empty(k, dtype=np.float32)
+    for c in range(k):
+        col = w64[kept[:, c], c]
+        d = col - mean
+        ss = math.fsum((d * d).tolist()) / var if var > 0 else 0.0
+        f[c] = np.float32(ss ** (alpha / 2.0))
     return f
 
 

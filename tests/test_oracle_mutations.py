@@ -99,7 +99,21 @@ def _width_floor(n, m, fmt):                             # floor instead of ceil
     return m
 
 
+def _amber_no_removal(w, alpha=1.0, q_lo=0.5, q_hi=99.5):   # keeps the outliers
+    return _orig_amber(w, alpha, 0.0, 100.0)
+
+
+def _amber_raw_norm(w, alpha=1.0, q_lo=0.5, q_hi=99.5):      # skips the standardisation
+    w64 = np.asarray(w, np.float64)
+    v = np.sort(w64.ravel())
+    lo, hi = O.percentile_linear(v, q_lo), O.percentile_linear(v, q_hi)
+    kept = (w64 >= lo) & (w64 <= hi)
+    ss = np.where(kept, w64 * w64, 0.0).sum(axis=0)
+    return (ss ** (alpha / 2)).astype(np.float32)
+
+
 _orig_factor = O.channel_factor
+_orig_amber = O.amber_factor
 _orig_var = O.var_factor
 _orig_round = O.round_to_dtype
 
@@ -119,6 +133,8 @@ MUTANTS = {
     "relu2_not_rounded": ("squared_relu", _relu2_unrounded),
     "relu2_not_squared": ("squared_relu", _relu_only),
     "meta_lex_rank": ("comb_rank", _lex_rank),
+    "amber_keeps_outliers": ("amber_factor", _amber_no_removal),
+    "amber_raw_norm": ("amber_factor", _amber_raw_norm),
     "meta_width_floor": ("meta_width", _width_floor),
 }
 

@@ -348,6 +348,57 @@ def test_round_to_dtype_matches_torch(dtype, tdt):
 
 
 # --------------------------------------------------------------------------
+# Amber-Pruner channel factor
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,n", [(0, 400), (1, 1001), (2, 65536), (3, 7)])
+def test_amber_percentile_matches_numpy(seed, n):
+    v = np.sort(np.random.Generator(np.random.PCG64(seed)).standard_normal(n))
+    for q in (0.5, 99.5, 50.0, 0.0, 100.0):
+        ref = float(np.percentile(v, q, method="linear"))
+        assert abs(O.percentile_linear(v, q) - ref) <= 2 * np.spacing(abs(ref))
+
+
+def test_amber_removes_planted_outliers_exact():
+    # 200 x 2 weights: two planted low and two planted high outliers fall
+    # outside the 0.5 / 99.5 percentiles (order-statistic positions 1.995 and
+    # 397.005 of 400); the factor is then the exact rational z-score norm of
+    # the other 396 values
+    rng = np.random.Generator(np.random.PCG64(4))
+    w = np.round(rng.uniform(-1, 1, size=(200, 2)) * 64) / 64
+    out = [(3, 0, -100.0), (77, 1, -90.0), (150, 0, 95.0), (9, 1, 120.0)]
+    for j, c, v in out:
+        w[j, c] = v
+    keep = np.ones_like(w, dtype=bool)
+    for j, c, _ in out:
+        keep[j, c] = False
+    vals = [Fraction(float(x)) for x in w[keep]]
+    mean = sum(vals) / len(vals)
+    var = sum((x - mean) ** 2 for x in vals) / len(vals)
+    for alpha in (1.0, 0.5):
+        f = O.amber_factor(w.astype(np.float32), alpha)
+        for c in range(2):
+            ss = sum((Fraction(float(x)) - mean) ** 2 for x in w[keep[:, c], c]) / var
+            want = np.float32(float(ss) ** (alpha / 2))
+            assert abs(float(f[c]) - float(want)) <= 2e-7 * float(want), (c, f[c], want)
+
+
+def test_amber_invariant_to_scale_and_shift():
+    rng = np.random.Generator(np.random.PCG64(5))
+    w = (rng.standard_normal((300, 48)) * 0.02).astype(np.float32)
+    w[rng.integers(0, 300, 6), rng.integers(0, 48, 6)] = 0.5          # a few outliers
+    f = O.amber_factor(w, 1.0)
+    assert np.array_equal(O.amber_factor(w * np.float32(4.0), 1.0), f)  # exact: a power of two
+    g = O.amber_factor(w + np.float32(0.25), 1.0)                       # the mean is removed
+    assert np.allclose(g, f, rtol=1e-5, atol=0)
+    assert np.array_equal(O.amber_factor(w, 0.0), np.ones(48, np.float32))
+    # the outliers are gone: one huge weight does not make its channel stand out
+    w2 = w.copy()
+    w2[0, 7] = 1e3
+    assert abs(float(O.amber_factor(w2, 1.0)[7]) / float(f[7]) - 1.0) < 0.05
+
+
+# --------------------------------------------------------------------------
 # compact block metadata
 # --------------------------------------------------------------------------
 
