@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     encode_meta,
     lib,
     meta_row_bytes,
+    prepare_amber,
     prepare_weight,
     prune_nm,
     sparse_linear_decode,

@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
         L.spa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(_Cfg)]
         L.prepare_weight.restype = ctypes.c_int
         L.prepare_weight.argtypes = [vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp]
+        L.spa_amber_workspace_bytes.restype = sz
+        L.spa_amber_workspace_bytes.argtypes = []
+        L.prepare_amber.restype = ctypes.c_int
+        L.prepare_amber.argtypes = [vp, i32, i32, i32, ctypes.c_float, vp, vp, sz, vp]
         L.spa_meta_row_bytes.restype = sz
         L.spa_meta_row_bytes.argtypes = [i32, i32, i32, i32]
         for name in ("spa_encode_meta", "spa_decode_meta"):
@@ -75,7 +79,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("prepare_weight", "prune_nm", "sparse_linear_decode", "sparse_linear_prefill",
-           "spa_workspace_bytes", "spa_status_str", "spa_meta_row_bytes", "spa_encode_meta", "spa_decode_meta")
+           "spa_workspace_bytes", "spa_status_str", "spa_meta_row_bytes", "spa_encode_meta", "spa_decode_meta",
+           "prepare_amber", "spa_amber_workspace_bytes")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -184,6 +189,18 @@ def prune_nm(x: torch.Tensor, cfg: PruneConfig, chan_scale: Optional[torch.Tenso
                           _ptr(vals), _ptr(idx), _ptr(eta), _ptr(nu), _ptr(ws), 0 if ws is None else ws.numel(),
                           _stream(dev)), "prune_nm")
     return vals, idx, eta, nu
+
+
+def prepare_amber(w: torch.Tensor, alpha: float = 1.0) -> torch.Tensor:
+    """Amber-Pruner channel factor of W[n_out, k]: a float32 [k] chan_scale for the weight-aware score."""
+    dev = _dev(w)
+    n_out, k = w.shape
+    out = torch.empty(k, dtype=torch.float32, device=dev)
+    nb = int(lib().spa_amber_workspace_bytes())
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    _check(lib().prepare_amber(_ptr(w), DTYPE[w.dtype], n_out, k, float(alpha), _ptr(out), _ptr(ws), nb,
+                               _stream(dev)), "prepare_amber")
+    return out
 
 
 def meta_row_bytes(k: int, n: int, m: int, fmt: str = "comb") -> int:

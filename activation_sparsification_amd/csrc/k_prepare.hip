@@ -15,28 +15,6 @@
 
 namespace spa {
 
-// Error-free transformation: s + e == a + b exactly.
-__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
-  s = a + b;
-  const double bb = s - a;
-  e = (a - (s - bb)) + (b - bb);
-}
-
-struct DD { double hi, lo; };
-
-__device__ __forceinline__ void dd_add(DD& acc, double v) {
-  double s, e;
-  two_sum(acc.hi, v, s, e);
-  double lo = acc.lo + e;
-  two_sum(s, lo, acc.hi, acc.lo);
-}
-__device__ __forceinline__ void dd_merge(DD& a, const DD& b) {
-  double s, e;
-  two_sum(a.hi, b.hi, s, e);
-  e += a.lo + b.lo;
-  two_sum(s, e, a.hi, a.lo);
-}
-
 template <int DT>
 __global__ void __launch_bounds__(256) k_transpose(const typename Dt<DT>::T* __restrict__ w,
                                                    typename Dt<DT>::T* __restrict__ wt, int n_out, int k) {
@@ -55,19 +33,17 @@ __global__ void __launch_bounds__(256) k_transpose(const typename Dt<DT>::T* __r
   }
 }
 
-// One thread per channel: squares summed down the column (coalesced across threads).
+// Squares summed down each column (64 columns x 4 row groups per workgroup).
 template <int DT>
 __global__ void __launch_bounds__(256) k_chan_scale(const typename Dt<DT>::T* __restrict__ w, float* __restrict__ out,
                                                     int n_out, int k, double half_alpha) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= k) return;
-  DD acc{0.0, 0.0};
-  for (int j = 0; j < n_out; ++j) {
-    const double v = (double)to_f32<DT>(w[(size_t)j * k + c]);
-    dd_add(acc, v * v);  // exact: a float32 squared fits in 53 bits
-  }
-  const double sumsq = acc.hi + acc.lo;
-  out[c] = (float)pow(sumsq, half_alpha);
+  bool owner;
+  int c;
+  const DD acc = column_dd(
+      w, n_out, k, [](typename Dt<DT>::T x) { return (double)to_f32<DT>(x); },
+      [](DD& a, double v) { dd_add(a, v * v); },   // exact: a float32 squared fits in 53 bits
+      owner, c);
+  if (owner) out[c] = (float)pow(acc.hi + acc.lo, half_alpha);
 }
 
 // One workgroup per output row.
@@ -105,7 +81,7 @@ static hipError_t prepare_impl(const void* w, int n_out, int k, float alpha, voi
     if (hipError_t e = hipGetLastError()) return e;
   }
   if (cs) {
-    hipLaunchKernelGGL(k_chan_scale<DT>, dim3((k + 255) / 256), dim3(256), 0, st, wp, cs, n_out, k,
+    hipLaunchKernelGGL(k_chan_scale<DT>, dim3((k + 63) / 64), dim3(256), 0, st, wp, cs, n_out, k,
                        0.5 * (double)alpha);
     if (hipError_t e = hipGetLastError()) return e;
   }

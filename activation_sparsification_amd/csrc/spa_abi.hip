@@ -264,6 +264,19 @@ spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, 
   return hip_status(spa::launch_gemm(w->dtype, g, st));
 }
 
+size_t spa_amber_workspace_bytes(void) { return spa::amber_workspace_bytes(); }
+
+spa_status prepare_amber(const void* w, int32_t dtype, int32_t n_out, int32_t k, float alpha, float* chan_scale_out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!w || !chan_scale_out || !valid_dtype(dtype)) return SPA_ERR_INVALID;
+  if (n_out < 1 || k < 1 || n_out > kMaxDim || k > kMaxDim) return SPA_ERR_INVALID;
+  if (!(alpha >= 0.f && alpha <= 16.f)) return SPA_ERR_INVALID;
+  if (!aligned16(w) || !workspace || !aligned16(workspace) || workspace_bytes < spa::amber_workspace_bytes())
+    return SPA_ERR_INVALID;
+  return hip_status(spa::launch_amber(dtype, w, n_out, k, alpha, chan_scale_out, workspace,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 size_t spa_meta_row_bytes(int32_t k, int32_t n, int32_t m, int32_t format) {
   if (!valid_meta(k, n, m, format)) return 0;
   return (size_t)4 * (((int64_t)(k / m) * spa::meta_width(n, m, format) + 31) / 32);

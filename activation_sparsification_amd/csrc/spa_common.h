@@ -143,6 +143,64 @@ __device__ __forceinline__ float sqrt_rn(float a) { return (float)__builtin_sqrt
 
 
 // ---------------------------------------------------------------------------
+// Double-double sums (weight preparation): the float64 result of hi + lo is
+// the correctly rounded exact sum in all but pathological cases.
+// ---------------------------------------------------------------------------
+struct DD { double hi, lo; };
+// Error-free transformation: s + e == a + b exactly.
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+#pragma clang fp contract(off)
+  s = a + b;
+  const double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+__device__ __forceinline__ void dd_add(DD& acc, double v) {
+#pragma clang fp contract(off)
+  double s, e;
+  two_sum(acc.hi, v, s, e);
+  two_sum(s, acc.lo + e, acc.hi, acc.lo);
+}
+__device__ __forceinline__ void dd_merge(DD& a, const DD& b) {
+#pragma clang fp contract(off)
+  double s, e;
+  two_sum(a.hi, b.hi, s, e);
+  e += a.lo + b.lo;
+  two_sum(s, e, a.hi, a.lo);
+}
+
+// Column sums of a row-major [n_out][k] matrix: term(v) summed down each
+// column in double-double.  Workgroup = 64 columns x 4 row groups (rows
+// strided by 4, eight loads in flight per thread); the groups are merged in
+// LDS in a fixed order and thread 0..63 receives its column's total.
+template <typename T, typename Load, typename Term>
+__device__ __forceinline__ DD column_dd(const T* __restrict__ w, int n_out, int k, Load load, Term term,
+                                        bool& owner, int& col) {
+  __shared__ double s_hi[4][64], s_lo[4][64];
+  const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  col = blockIdx.x * 64 + cl;
+  DD acc{0.0, 0.0};
+  if (col < k) {
+    int j = rg;
+    for (; j + 28 < n_out; j += 32) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = load(w[(size_t)(j + 4 * u) * k + col]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) term(acc, v[u]);
+    }
+    for (; j < n_out; j += 4) term(acc, load(w[(size_t)j * k + col]));
+  }
+  s_hi[rg][cl] = acc.hi;
+  s_lo[rg][cl] = acc.lo;
+  __syncthreads();
+  owner = rg == 0 && col < k;
+  if (rg == 0) {
+    for (int g = 1; g < 4; ++g) dd_merge(acc, DD{s_hi[g][cl], s_lo[g][cl]});
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
 // Wave and workgroup reductions (block_sum: blockDim.x == 256).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double wave_sum(double v) {

@@ -74,6 +74,11 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
                         DecodeArgs* plan);
 hipError_t launch_decode(int dtype, DecodeArgs& a, hipStream_t st);
 
+// ---- Amber-Pruner channel factor ----
+size_t amber_workspace_bytes();
+hipError_t launch_amber(int dtype, const void* w, int n_out, int k, float alpha, float* out, void* ws,
+                        hipStream_t st);
+
 // ---- compact block metadata ----
 int meta_width(int n, int m, int format);
 hipError_t launch_meta(bool encode, const uint8_t* idx, uint8_t* idx_out, uint32_t* codes, int t, int k, int n,

@@ -112,6 +112,27 @@ spa_status prepare_weight(const void* w, int32_t dtype, int32_t n_out, int32_t k
                           void* wt_out, float* chan_scale_out, float* row_sum_out, void* stream);
 
 /*
+ * prepare_amber -- once per layer, off the timed path: the Amber-Pruner
+ * channel factor (activation sparsification guide s2.2.2), a drop-in
+ * chan_scale for SPA_SCORE_WEIGHT:
+ *   1. the 0.5th and 99.5th percentiles of all n_out*k weights (linear
+ *      interpolation in float64 between the order statistics at floor and
+ *      floor+1 of q/100 * (N-1)) bound the weights kept; the others are
+ *      removed as outliers;
+ *   2. the kept weights are standardised with their own mean and population
+ *      standard deviation;
+ *   3. chan_scale_out[c] = float32((sum over outputs j of the kept
+ *      standardised W[j][c]^2)^(alpha/2)).
+ * Order statistics by an exact radix select on the device; sums in
+ * double-double arithmetic.  w: [device] [n_out][k]; chan_scale_out:
+ * [device] [k]; workspace: [device] spa_amber_workspace_bytes() bytes (no
+ * initial contents needed).  Requires n_out >= 1, k >= 1, 0 <= alpha <= 16.
+ */
+size_t spa_amber_workspace_bytes(void);
+spa_status prepare_amber(const void* w, int32_t dtype, int32_t n_out, int32_t k, float alpha,
+                         float* chan_scale_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * prune_nm -- score, per-block top-n, pack (guide s2.1, s2.2, s3.1, s3.2).
  *  x          [device] [t][k]
  *  chan_scale [device] [k]   required iff cfg->score == SPA_SCORE_WEIGHT

@@ -135,7 +135,7 @@ def percentile_linear(v_sorted: np.ndarray, q: float) -> float:
     return a + (b - a) * g
 
 
-def amber_factor(w: np.ndarray, alpha: float = 1.0, q_lo: float = 0.5, q_hi: float = 99.5) -> np.ndarray:
+def amber_factor(w: np.ndarray, alpha: float = 1.0, q_lo: float = 0.5, q_hi: float = 99.5, cols=None) -> np.ndarray:
     """Amber-Pruner channel factor ([Guide] s2.2.2), float32 [k].
 
     1. keep the weights between the q_lo-th and q_hi-th percentiles of the
@@ -145,6 +145,7 @@ def amber_factor(w: np.ndarray, alpha: float = 1.0, q_lo: float = 0.5, q_hi: flo
     3. f_k = (sum over outputs j of z_jk^2, kept weights only) ** (alpha / 2).
     Differences and squares are float64, their sums exact (math.fsum) and
     rounded once; the ratio and the power are float64, the result float32.
+    ``cols`` restricts step 3 to those channels (the result holds only them).
     """
     w64 = np.asarray(w, dtype=np.float64)
     v = np.sort(w64.ravel())
@@ -155,13 +156,13 @@ def amber_factor(w: np.ndarray, alpha: float = 1.0, q_lo: float = 0.5, q_hi: flo
     mean = math.fsum(vals.tolist()) / cnt
     dev = vals - mean
     var = math.fsum((dev * dev).tolist()) / cnt
-    k = w64.shape[1]
-    f = np.empty(k, dtype=np.float32)
-    for c in range(k):
+    cols = range(w64.shape[1]) if cols is None else list(cols)
+    f = np.empty(len(cols), dtype=np.float32)
+    for out_i, c in enumerate(cols):
         col = w64[kept[:, c], c]
         d = col - mean
         ss = math.fsum((d * d).tolist()) / var if var > 0 else 0.0
-        f[c] = np.float32(ss ** (alpha / 2.0))
+        f[out_i] = np.float32(ss ** (alpha / 2.0))
     return f
 
 

@@ -98,3 +98,19 @@ def test_meta_full_size(fmt, n, m, t, k):
     rows = _sample(t, 12, 4)
     want = O.encode_meta(idx.numpy()[rows], n, m, fmt)
     assert np.array_equal(codes.cpu().numpy().view(np.uint32)[rows], want)
+
+
+def test_amber_full_size():
+    # the Amber-Pruner factor of the decode layer's weight [14336, 4096] bf16:
+    # the global percentiles, mean and variance over all 58.7 M weights; the
+    # per-channel sums on sampled channels
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    dev = torch.device("cuda:0")
+    spec = wl.SPECS["decode"]
+    print(f"[full-size amber] n_out={spec.n_out} k={spec.k}", flush=True)
+    _, w = wl.make_inputs(spec)
+    got = f32(spa.prepare_amber(w.to(dev), 1.0))
+    torch.cuda.synchronize()
+    cols = _sample(spec.k, 32, 5)
+    want = O.amber_factor(f32(w), 1.0, cols=cols)
+    assert np.allclose(got[cols], want, rtol=1e-6, atol=0), np.abs(got[cols] / want - 1).max()

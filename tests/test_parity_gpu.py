@@ -54,6 +54,51 @@ def test_prepare_weight(name, alpha):
 
 
 # ---------------------------------------------------------------------------
+# prepare_amber
+# ---------------------------------------------------------------------------
+def _amber_weights(kind, dtype, n_out, k, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = rng.normal(0.0, 0.02, size=(n_out, k))
+    if kind == "outliers":                                   # a few planted outliers, both signs
+        idx = rng.integers(0, n_out * k, size=max(4, n_out * k // 300))
+        w.ravel()[idx] = rng.choice([-1.0, 1.0], size=idx.size) * rng.uniform(0.2, 2.0, size=idx.size)
+    elif kind == "shifted":                                  # non-zero mean
+        w = w + 0.3
+    elif kind == "levels":                                   # many equal values around the percentiles
+        w = np.round(w * 200) / 200
+    return torch.from_numpy(w.astype(np.float32)).to(TORCH_DT[dtype])
+
+
+AMBER_CASES = [(kind, dt, n_out, k) for kind in ["normal", "outliers", "shifted", "levels"]
+               for dt in ["bf16", "f16", "f32"] for n_out, k in [(300, 77), (1000, 1024)]]
+AMBER_CASES.append(("normal", "bf16", 1, 16))
+
+
+@pytest.mark.parametrize("kind,dtype,n_out,k", AMBER_CASES)
+@pytest.mark.parametrize("alpha", [1.0, 0.5])
+def test_prepare_amber(kind, dtype, n_out, k, alpha):
+    dev = _dev()
+    w = _amber_weights(kind, dtype, n_out, k, seed=n_out + k)
+    got = f32(spa.prepare_amber(w.to(dev), alpha))
+    torch.cuda.synchronize()
+    want = O.amber_factor(f32(w), alpha)
+    assert np.allclose(got, want, rtol=1e-6, atol=0), np.abs(got / want - 1).max()
+
+
+def test_amber_factor_drives_the_masks():
+    # the weight-aware score with the Amber factor (the oracle's float32
+    # vector feeds both sides)
+    dev = _dev()
+    spec = wl.SPECS["decode"].with_(t=5, k=1024, n_out=512)
+    x, w = wl.make_inputs(spec)
+    f = O.amber_factor(f32(w), 1.0)
+    pr = O.prune(f32(x), spec.dtype, spec.n, spec.m, score="weight", f=f, shift_mode=spec.shift)
+    vals, idx, eta, nu = spa.prune_nm(x.to(dev), _cfg(spec), chan_scale=torch.from_numpy(f).to(dev))
+    torch.cuda.synchronize()
+    _check_prune(pr, vals, idx, eta, nu, spec.dtype)
+
+
+# ---------------------------------------------------------------------------
 # prune_nm
 # ---------------------------------------------------------------------------
 PRUNE_CASES = []
