@@ -312,7 +312,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS) + ["meta"],
+                    help="meta: only the block-metadata encode/decode lines (one JSON line)")
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -333,6 +334,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.workload == "meta":
+        recs = []
+        for fmt, n, m, t, k in [("comb", 2, 4, 4096, 16384), ("bitmap", 2, 4, 4096, 16384),
+                                ("comb", 16, 32, 4096, 14336)]:
+            recs += measure_meta(fmt, n, m, t, k, args.steps, args.warmup)
+        print(json.dumps({"meta_codecs": recs}))
+        return
 
     head = measure(args.workload, args.steps, args.warmup)
     secondary = []
