@@ -9,6 +9,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int64_t kMaxPrefillK = int64_t(1) << 23;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int dtype_bytes(int dt) { return dt == SPA_F32 ? 4 : 2; }
@@ -175,6 +176,11 @@ spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, c
                                 size_t workspace_bytes, void* stream) {
   if (spa_status s = check_linear(x, t, w, cfg, eta_in, y, true)) return s;
   if (w->dtype == SPA_F32 && t > 8) return SPA_ERR_UNSUPPORTED;
+  // the channel-major weight of the 1..4-token (and float32) paths must stay
+  // under 2 GiB: larger ones are not validated on the device
+  if ((t <= 4 || w->dtype == SPA_F32) &&
+      (int64_t)w->k * w->n_out * dtype_bytes(w->dtype) >= (int64_t(1) << 31))
+    return SPA_ERR_UNSUPPORTED;
   spa::DecodeArgs a{};
   const size_t need = spa::decode_workspace(t, w->k, w->n_out, w->dtype, cfg->n, cfg->m, cfg->score, cfg->shift,
                                             cfg->var_rescale, &a);
@@ -206,6 +212,8 @@ spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, 
                                  size_t workspace_bytes, void* stream) {
   if (spa_status s = check_linear(x, t, w, cfg, eta_in, y, false)) return s;
   if (w->dtype == SPA_F32) return SPA_ERR_UNSUPPORTED;
+  // the GEMMs address a 256-row weight tile with 32-bit offsets: 255 * k * 2 B < 4 GiB
+  if (w->k > kMaxPrefillK) return SPA_ERR_UNSUPPORTED;
   if (t == 0) return SPA_OK;
   const int k = w->k;
   const PrefillPlan pl = prefill_plan(t, k, w->dtype, cfg);

@@ -172,7 +172,8 @@ spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const sp
  *  nu_out   [device] [t] or NULL
  *  workspace [device] spa_workspace_bytes(SPA_ENTRY_DECODE, ...) bytes,
  *           zero-filled before its first use; each call leaves it reusable.
- * Returns SPA_ERR_UNSUPPORTED for float32 with t > 8.
+ * Returns SPA_ERR_UNSUPPORTED for float32 with t > 8, and when the 1..4-token
+ * (or float32) path would read a channel-major weight of 2 GiB or more.
  */
 spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
                                 const float* eta_in, void* y, uint8_t* idx_out, float* nu_out,
@@ -188,6 +189,7 @@ spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, c
  * masked activations.
  *  Arguments as for sparse_linear_decode; w->w required, n_out % 8 == 0,
  *  k % 64 == 0.  workspace: spa_workspace_bytes(SPA_ENTRY_PREFILL, ...).
+ *  SPA_ERR_UNSUPPORTED for k > 2^23 (8388608).
  */
 spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
                                  const float* eta_in, void* y, uint8_t* idx_out, float* nu_out,

@@ -86,6 +86,36 @@ def test_meta_rejections_happen_before_any_launch(lib):
         assert fn(16, 4, 64, 2, 4, 1, 24, None) == SPA_ERR_INVALID      # unaligned buffers
 
 
+def test_prefill_limits(lib):
+    import activation_sparsification_amd._binding as B
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.sparse_linear_prefill.restype = ctypes.c_int
+    lib.sparse_linear_prefill.argtypes = [vp, i32, ctypes.POINTER(B._Weight), ctypes.POINTER(B._Cfg), vp, vp, vp,
+                                          vp, vp, sz, vp]
+    cfg = B.PruneConfig(2, 4).c()
+    for k, want in [((1 << 23) + 64, 2), ((1 << 24), 2)]:          # above 2^23 channels: unsupported
+        wd = B._Weight(2, 8, k, 256, None, None, None)
+        assert lib.sparse_linear_prefill(512, 4, ctypes.byref(wd), ctypes.byref(cfg), None, 768, None, None, 1024,
+                                         1 << 40, None) == want
+    wd = B._Weight(0, 8, 4096, 256, None, None, None)                 # float32 prefill: unsupported
+    assert lib.sparse_linear_prefill(512, 4, ctypes.byref(wd), ctypes.byref(cfg), None, 768, None, None, 1024,
+                                     1 << 40, None) == 2
+
+
+def test_decode_weight_limit(lib):
+    # 1..4 tokens read the channel-major weight: 2 GiB and more is rejected
+    import activation_sparsification_amd._binding as B
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.sparse_linear_decode.restype = ctypes.c_int
+    lib.sparse_linear_decode.argtypes = [vp, i32, ctypes.POINTER(B._Weight), ctypes.POINTER(B._Cfg), vp, vp, vp,
+                                         vp, vp, sz, vp]
+    cfg = B.PruneConfig(8, 16).c()
+    for k, t, dt in [(262144, 1, 2), (262144, 4, 1), (131072, 2, 0)]:
+        wd = B._Weight(dt, 4096, k, None, 256, None, None)
+        assert lib.sparse_linear_decode(512, t, ctypes.byref(wd), ctypes.byref(cfg), None, 768, None, None, 1024,
+                                        1 << 40, None) == 2
+
+
 def test_linear_rejections_happen_before_any_launch(lib):
     import activation_sparsification_amd._binding as B
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
