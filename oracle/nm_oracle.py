@@ -44,6 +44,10 @@ design notes as well):
 * f_k = ||W[:,k]||_2^alpha is formed once from the exact sum of squares,
   raised to alpha/2 in float64 and rounded to float32.
 * eta (D-PTS) = float32(float64(exact row sum) / K).
+* S-PTS table ([Guide] s3.1): calibration collects each token's D-PTS shift
+  under the caller's token id; the table entry of an id is the mean of its
+  collected shifts (exact sum, divided in float64, rounded to float32), 0
+  for an id never seen; at run time a token takes its id's entry.
 * CLACT: the column energy runs over the tokens of the call, squares and
   adds rounded in float32 with tokens in ascending order, then a correctly
   rounded float32 square root.  The per-row factor 1/||x_i|| is a positive
@@ -195,6 +199,29 @@ def token_mean(x: np.ndarray) -> np.ndarray:
     x64 = np.asarray(x, dtype=np.float64)
     k = x64.shape[1]
     return np.array([np.float32(math.fsum(r.tolist()) / k) for r in x64], dtype=np.float32)
+
+
+def eta_table(batches, vocab: int) -> np.ndarray:
+    """S-PTS table from calibration batches ([Guide] s3.1), float32 [vocab].
+
+    ``batches``: iterable of (x [t, k] float32 values, token_ids [t]).  Each
+    token's D-PTS shift (``token_mean``) is collected under its id; entry id
+    is float32(float64(exact sum of its shifts) / count), 0 when unseen.
+    """
+    buf = [[] for _ in range(vocab)]
+    for x, ids in batches:
+        eta = token_mean(x)
+        for e, i in zip(eta.tolist(), np.asarray(ids).tolist()):
+            buf[int(i)].append(float(e))
+    return np.array([np.float32(math.fsum(b) / len(b)) if b else np.float32(0.0) for b in buf], dtype=np.float32)
+
+
+def eta_lookup(table: np.ndarray, ids) -> np.ndarray:
+    """A token's static shift: its id's table entry; 0 for an id outside the table."""
+    table = np.asarray(table, dtype=np.float32)
+    ids = np.asarray(ids, dtype=np.int64)
+    ok = (ids >= 0) & (ids < table.size)
+    return np.where(ok, table[np.clip(ids, 0, table.size - 1)], np.float32(0.0)).astype(np.float32)
 
 
 def shift(x: np.ndarray, eta: np.ndarray) -> np.ndarray:

@@ -112,6 +112,14 @@ def _amber_raw_norm(w, alpha=1.0, q_lo=0.5, q_hi=99.5):      # skips the standar
     return (ss ** (alpha / 2)).astype(np.float32)
 
 
+def _eta_table_last(batches, vocab):                     # keeps the last shift, not the mean
+    tab = np.zeros(vocab, np.float32)
+    for x, ids in batches:
+        for e, i in zip(O.token_mean(x).tolist(), np.asarray(ids).tolist()):
+            tab[int(i)] = e
+    return tab
+
+
 _orig_factor = O.channel_factor
 _orig_amber = O.amber_factor
 _orig_var = O.var_factor
@@ -135,6 +143,7 @@ MUTANTS = {
     "meta_lex_rank": ("comb_rank", _lex_rank),
     "amber_keeps_outliers": ("amber_factor", _amber_no_removal),
     "amber_raw_norm": ("amber_factor", _amber_raw_norm),
+    "eta_table_last_value": ("eta_table", _eta_table_last),
     "meta_width_floor": ("meta_width", _width_floor),
 }
 

@@ -348,6 +348,34 @@ def test_round_to_dtype_matches_torch(dtype, tdt):
 
 
 # --------------------------------------------------------------------------
+# S-PTS table
+# --------------------------------------------------------------------------
+
+def test_eta_table_exact_means():
+    # rows of a constant value c have shift exactly c; an id's entry is the
+    # exact average of its rows' constants, rounded once
+    consts = [0.5, -1.25, 3.0, 0.75, 2.0, -0.5, 0.125]
+    ids = [3, 0, 3, 5, 3, 0, 1]
+    x = np.array([[c] * 64 for c in consts], dtype=np.float32)
+    tab = O.eta_table([(x[:4], ids[:4]), (x[4:], ids[4:])], vocab=6)
+    for v in range(6):
+        vals = [Fraction(c) for c, i in zip(consts, ids) if i == v]
+        want = np.float32(float(sum(vals) / len(vals))) if vals else np.float32(0.0)
+        assert tab[v] == want, (v, tab[v], want)
+    assert list(O.eta_lookup(tab, [3, 0, 9, -1, 5])) == [tab[3], tab[0], 0.0, 0.0, tab[5]]
+
+
+def test_eta_table_single_occurrence_is_the_dynamic_shift():
+    spec = wl.SPECS["prefill"].with_(t=16, k=512)
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    x = _x32(x)
+    tab = O.eta_table([(x, np.arange(16))], vocab=16)
+    for i in range(16):
+        exact = sum(Fraction(float(v)) for v in x[i]) / 512
+        assert tab[i] == np.float32(float(exact))
+
+
+# --------------------------------------------------------------------------
 # Amber-Pruner channel factor
 # --------------------------------------------------------------------------
 
