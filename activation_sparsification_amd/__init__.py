@@ -5,12 +5,14 @@ declared in ``include/spa.h``); this package is its thin Python binding.
 """
 from ._binding import (  # noqa: F401
     EXPORTS,
+    EtaCalibration,
     PreparedCall,
     PreparedWeight,
     PruneConfig,
     SpaError,
     decode_meta,
     encode_meta,
+    eta_lookup,
     lib,
     meta_row_bytes,
     prepare_amber,

@@ -58,6 +58,12 @@ def lib() -> ctypes.CDLL:
         L.spa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(_Cfg)]
         L.prepare_weight.restype = ctypes.c_int
         L.prepare_weight.argtypes = [vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp]
+        L.spa_eta_calibrate.restype = ctypes.c_int
+        L.spa_eta_calibrate.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, vp]
+        L.spa_eta_table.restype = ctypes.c_int
+        L.spa_eta_table.argtypes = [vp, vp, i32, vp, vp]
+        L.spa_eta_lookup.restype = ctypes.c_int
+        L.spa_eta_lookup.argtypes = [vp, i32, vp, i32, vp, vp]
         L.spa_amber_workspace_bytes.restype = sz
         L.spa_amber_workspace_bytes.argtypes = []
         L.prepare_amber.restype = ctypes.c_int
@@ -80,7 +86,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("prepare_weight", "prune_nm", "sparse_linear_decode", "sparse_linear_prefill",
            "spa_workspace_bytes", "spa_status_str", "spa_meta_row_bytes", "spa_encode_meta", "spa_decode_meta",
-           "prepare_amber", "spa_amber_workspace_bytes")
+           "prepare_amber", "spa_amber_workspace_bytes", "spa_eta_calibrate", "spa_eta_table", "spa_eta_lookup")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -189,6 +195,39 @@ def prune_nm(x: torch.Tensor, cfg: PruneConfig, chan_scale: Optional[torch.Tenso
                           _ptr(vals), _ptr(idx), _ptr(eta), _ptr(nu), _ptr(ws), 0 if ws is None else ws.numel(),
                           _stream(dev)), "prune_nm")
     return vals, idx, eta, nu
+
+
+class EtaCalibration:
+    """Static shift table (S-PTS): add calibration batches, then read the table."""
+
+    def __init__(self, vocab: int, device):
+        self.vocab = vocab
+        self.sums = torch.zeros(vocab, dtype=torch.float64, device=device)
+        self.counts = torch.zeros(vocab, dtype=torch.int32, device=device)
+
+    def add(self, x: torch.Tensor, token_ids: torch.Tensor) -> None:
+        dev = _dev(x)
+        t, k = x.shape
+        ids = token_ids.to(device=dev, dtype=torch.int32).contiguous()
+        _check(lib().spa_eta_calibrate(_ptr(x), DTYPE[x.dtype], t, k, _ptr(ids), self.vocab, _ptr(self.sums),
+                                       _ptr(self.counts), _stream(dev)), "spa_eta_calibrate")
+
+    def table(self) -> torch.Tensor:
+        dev = self.sums.device
+        out = torch.empty(self.vocab, dtype=torch.float32, device=dev)
+        _check(lib().spa_eta_table(_ptr(self.sums), _ptr(self.counts), self.vocab, _ptr(out), _stream(dev)),
+               "spa_eta_table")
+        return out
+
+
+def eta_lookup(table: torch.Tensor, token_ids: torch.Tensor) -> torch.Tensor:
+    """Per-token static shift: the table entry of each token id (0 outside the table)."""
+    dev = _dev(table)
+    ids = token_ids.to(device=dev, dtype=torch.int32).contiguous()
+    out = torch.empty(ids.numel(), dtype=torch.float32, device=dev)
+    _check(lib().spa_eta_lookup(_ptr(table), table.numel(), _ptr(ids), ids.numel(), _ptr(out), _stream(dev)),
+           "spa_eta_lookup")
+    return out
 
 
 def prepare_amber(w: torch.Tensor, alpha: float = 1.0) -> torch.Tensor:

@@ -315,6 +315,73 @@ __global__ void __launch_bounds__(256) k_token_mean(const typename Dt<DT>::T* __
   if (threadIdx.x == 0) eta[blockIdx.x] = e;
 }
 
+// Static shift table (the guide's s3.1, S-PTS): calibration adds each token's
+// dynamic shift (the same float32 token mean as above) and a count under the
+// token's id; the table entry is their mean.  The float64 additions are
+// atomic, so their order (and the last bits of a sum) may vary between runs.
+template <int DT>
+__global__ void __launch_bounds__(256) k_eta_accum(const typename Dt<DT>::T* __restrict__ x, int k,
+                                                   const int32_t* __restrict__ ids, int vocab, double* sums,
+                                                   uint32_t* counts) {
+  __shared__ double s_red[4];
+  const float e = row_mean<DT>(x + (size_t)blockIdx.x * k, k, 0, s_red);
+  if (threadIdx.x == 0) {
+    const int id = ids[blockIdx.x];
+    if (id >= 0 && id < vocab) {
+      atomicAdd(&sums[id], (double)e);
+      atomicAdd(&counts[id], 1u);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) k_eta_finalize(const double* __restrict__ sums,
+                                                      const uint32_t* __restrict__ counts, int vocab,
+                                                      float* __restrict__ table) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < vocab) table[i] = counts[i] ? (float)(sums[i] / (double)counts[i]) : 0.f;
+}
+
+__global__ void __launch_bounds__(256) k_eta_lookup(const float* __restrict__ table, int vocab,
+                                                    const int32_t* __restrict__ ids, int t, float* __restrict__ eta) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < t) {
+    const int id = ids[i];
+    eta[i] = (id >= 0 && id < vocab) ? table[id] : 0.f;
+  }
+}
+
+hipError_t launch_eta_calibrate(int dtype, const void* x, int t, int k, const int32_t* ids, int vocab, double* sums,
+                                uint32_t* counts, hipStream_t st) {
+  if (t == 0) return hipSuccess;
+  switch (dtype) {
+    case SPA_F32:
+      hipLaunchKernelGGL(k_eta_accum<SPA_F32>, dim3(t), dim3(256), 0, st, (const float*)x, k, ids, vocab, sums,
+                         counts);
+      break;
+    case SPA_F16:
+      hipLaunchKernelGGL(k_eta_accum<SPA_F16>, dim3(t), dim3(256), 0, st, (const uint16_t*)x, k, ids, vocab, sums,
+                         counts);
+      break;
+    default:
+      hipLaunchKernelGGL(k_eta_accum<SPA_BF16>, dim3(t), dim3(256), 0, st, (const uint16_t*)x, k, ids, vocab, sums,
+                         counts);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_eta_table(const double* sums, const uint32_t* counts, int vocab, float* table, hipStream_t st) {
+  if (vocab == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_eta_finalize, dim3((vocab + 255) / 256), dim3(256), 0, st, sums, counts, vocab, table);
+  return hipGetLastError();
+}
+
+hipError_t launch_eta_lookup(const float* table, int vocab, const int32_t* ids, int t, float* eta, hipStream_t st) {
+  if (t == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_eta_lookup, dim3((t + 255) / 256), dim3(256), 0, st, table, vocab, ids, t, eta);
+  return hipGetLastError();
+}
+
 // CLACT column energy, one thread per channel, tokens in ascending order.
 template <int DT>
 __global__ void __launch_bounds__(256) k_colnorm(const typename Dt<DT>::T* __restrict__ x, int act,

@@ -272,6 +272,32 @@ spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, 
   return hip_status(spa::launch_gemm(w->dtype, g, st));
 }
 
+spa_status spa_eta_calibrate(const void* x, int32_t dtype, int32_t t, int32_t k, const int32_t* token_ids,
+                             int32_t vocab, double* sums, uint32_t* counts, void* stream) {
+  if (!valid_dtype(dtype) || t < 0 || t > kMaxDim || k < 16 || k > kMaxDim || k % 16 || vocab < 0)
+    return SPA_ERR_INVALID;
+  if (t == 0) return SPA_OK;
+  if (!x || !aligned16(x) || !token_ids || (vocab > 0 && (!sums || !counts))) return SPA_ERR_INVALID;
+  return hip_status(spa::launch_eta_calibrate(dtype, x, t, k, token_ids, vocab, sums, counts,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+spa_status spa_eta_table(const double* sums, const uint32_t* counts, int32_t vocab, float* table_out,
+                         void* stream) {
+  if (vocab < 0) return SPA_ERR_INVALID;
+  if (vocab == 0) return SPA_OK;
+  if (!sums || !counts || !table_out) return SPA_ERR_INVALID;
+  return hip_status(spa::launch_eta_table(sums, counts, vocab, table_out, static_cast<hipStream_t>(stream)));
+}
+
+spa_status spa_eta_lookup(const float* table, int32_t vocab, const int32_t* token_ids, int32_t t, float* eta_out,
+                          void* stream) {
+  if (vocab < 0 || t < 0) return SPA_ERR_INVALID;
+  if (t == 0) return SPA_OK;
+  if (!token_ids || !eta_out || (vocab > 0 && !table)) return SPA_ERR_INVALID;
+  return hip_status(spa::launch_eta_lookup(table, vocab, token_ids, t, eta_out, static_cast<hipStream_t>(stream)));
+}
+
 size_t spa_amber_workspace_bytes(void) { return spa::amber_workspace_bytes(); }
 
 spa_status prepare_amber(const void* w, int32_t dtype, int32_t n_out, int32_t k, float alpha, float* chan_scale_out,

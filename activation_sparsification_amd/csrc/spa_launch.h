@@ -74,6 +74,12 @@ size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int sc
                         DecodeArgs* plan);
 hipError_t launch_decode(int dtype, DecodeArgs& a, hipStream_t st);
 
+// ---- static shift table ----
+hipError_t launch_eta_calibrate(int dtype, const void* x, int t, int k, const int32_t* ids, int vocab, double* sums,
+                                uint32_t* counts, hipStream_t st);
+hipError_t launch_eta_table(const double* sums, const uint32_t* counts, int vocab, float* table, hipStream_t st);
+hipError_t launch_eta_lookup(const float* table, int vocab, const int32_t* ids, int t, float* eta, hipStream_t st);
+
 // ---- Amber-Pruner channel factor ----
 size_t amber_workspace_bytes();
 hipError_t launch_amber(int dtype, const void* w, int n_out, int k, float alpha, float* out, void* ws,

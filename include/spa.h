@@ -133,6 +133,30 @@ spa_status prepare_amber(const void* w, int32_t dtype, int32_t n_out, int32_t k,
                          float* chan_scale_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Static per-token shift table (S-PTS, guide s3.1): calibration collects each
+ * token's dynamic shift (the SPA_SHIFT_TOKEN_MEAN value) under a caller-given
+ * token id; the table entry of an id is the mean of its collected shifts; at
+ * run time a token's shift is its id's entry, passed as eta_in with
+ * SPA_SHIFT_GIVEN.
+ * spa_eta_calibrate -- x [device] [t][k] (k % 16 == 0), token_ids [device]
+ *   [t] int32; adds each token's shift to sums[id] (float64) and 1 to
+ *   counts[id] (uint32), both [device] [vocab] and zero-filled by the caller
+ *   before the first batch.  Ids outside [0, vocab) are skipped.  The float64
+ *   additions are atomic: their order, and so the last bits of a sum, may
+ *   vary between runs.
+ * spa_eta_table -- table[id] = float32(sums[id] / counts[id]), 0 when
+ *   counts[id] == 0; all [device] [vocab].
+ * spa_eta_lookup -- eta_out[i] = table[token_ids[i]] (0 for an id outside
+ *   [0, vocab)); eta_out [device] [t] float32.
+ */
+spa_status spa_eta_calibrate(const void* x, int32_t dtype, int32_t t, int32_t k, const int32_t* token_ids,
+                             int32_t vocab, double* sums, uint32_t* counts, void* stream);
+spa_status spa_eta_table(const double* sums, const uint32_t* counts, int32_t vocab, float* table_out,
+                         void* stream);
+spa_status spa_eta_lookup(const float* table, int32_t vocab, const int32_t* token_ids, int32_t t, float* eta_out,
+                          void* stream);
+
+/*
  * prune_nm -- score, per-block top-n, pack (guide s2.1, s2.2, s3.1, s3.2).
  *  x          [device] [t][k]
  *  chan_scale [device] [k]   required iff cfg->score == SPA_SCORE_WEIGHT

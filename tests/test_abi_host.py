@@ -40,7 +40,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for need in ["prepare_weight", "prune_nm", "sparse_linear_decode", "sparse_linear_prefill",
                  "spa_workspace_bytes", "spa_status_str", "spa_meta_row_bytes", "spa_encode_meta",
-                 "spa_decode_meta", "prepare_amber", "spa_amber_workspace_bytes"]:
+                 "spa_decode_meta", "prepare_amber", "spa_amber_workspace_bytes", "spa_eta_calibrate",
+                 "spa_eta_table", "spa_eta_lookup"]:
         assert need in names, names
 
 

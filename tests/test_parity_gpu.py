@@ -54,6 +54,55 @@ def test_prepare_weight(name, alpha):
 
 
 # ---------------------------------------------------------------------------
+# static shift table (S-PTS)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_eta_table(dtype):
+    # three calibration batches, ids repeating across them, unseen ids and ids
+    # outside the table; the table's float64 sums are atomic, so an entry may
+    # differ from the oracle's in its last float32 unit
+    dev = _dev()
+    vocab = 50
+    cal = spa.EtaCalibration(vocab, dev)
+    batches = []
+    for b, (t, k) in enumerate([(37, 512), (64, 512), (5, 512)]):
+        spec = wl.SPECS["decode"].with_(t=t, k=k, dtype=dtype, n_outliers=0)
+        x, _ = wl.make_inputs(spec, seed=b, with_weight=False)
+        ids = np.random.Generator(np.random.PCG64(100 + b)).integers(-3, vocab + 3, size=t)
+        cal.add(x.to(dev), torch.from_numpy(ids))
+        batches.append((f32(x), ids))
+    got = f32(cal.table())
+    torch.cuda.synchronize()
+    # the oracle collects only ids inside the table
+    inside = [(x[(i >= 0) & (i < vocab)], i[(i >= 0) & (i < vocab)]) for x, i in batches]
+    want = O.eta_table(inside, vocab)
+    ulp = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1, ulp.max()
+    assert (got[want == 0] == 0).all()
+    # lookup: bit for bit on the oracle's table
+    ids = torch.tensor([3, -1, 49, 50, 0, 7, 7], dtype=torch.int32)
+    eta = spa.eta_lookup(torch.from_numpy(want).to(dev), ids)
+    torch.cuda.synchronize()
+    assert np.array_equal(f32(eta), O.eta_lookup(want, ids.numpy()))
+
+
+def test_static_shift_drives_decode():
+    # S-PTS end to end: the looked-up shift as eta_in of a decode call
+    dev = _dev()
+    spec = wl.SPECS["decode"].with_(t=3, k=1024, n_out=776, shift="given")
+    x, w = wl.make_inputs(spec)
+    table = (np.arange(20, dtype=np.float32) - 10) / 64
+    ids = np.array([4, 19, 11])
+    eta = spa.eta_lookup(torch.from_numpy(table).to(dev), torch.from_numpy(ids))
+    pw = spa.prepare_weight(w.to(dev), spec.alpha)
+    y, idx, nu = spa.sparse_linear_decode(x.to(dev), pw, _cfg(spec), eta_in=eta, want_idx=True, want_nu=True)
+    torch.cuda.synchronize()
+    pr = oracle_for(spec, x, w, f=f32(pw.chan_scale), eta_in=torch.from_numpy(O.eta_lookup(table, ids)))
+    assert np.array_equal(idx.cpu().numpy(), pr["idx"])
+    assert O.rowwise_error(f32(y), pr["y"]) <= O.TOLERANCE[spec.dtype]
+
+
+# ---------------------------------------------------------------------------
 # prepare_amber
 # ---------------------------------------------------------------------------
 def _amber_weights(kind, dtype, n_out, k, seed):
