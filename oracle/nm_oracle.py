@@ -55,6 +55,11 @@ design notes as well):
   is |x_ik - eta_i| * c_k.
 * VAR: the closed form of [Guide] s3.2 per token, population variances in
   float64 over all K positions; a zero denominator gives nu = 1.
+* VAR, running-average form (the implementation note of the same section):
+  per token slot a state r, updated as r <- 0.9 r + 0.1 Var[x_hat]; then
+  nu = sqrt(r / (Var[x_hat * m] + 1e-6)).  The listing divides by the dense
+  variance, which would make nu ~ 1; the masked variance of the closed form
+  is taken instead.  State and arithmetic in float64, stored as float32.
 * The dense term of (x_sparse + eta) W^T is split as
   (x_hat * m) W^T + eta * (W 1): only kept rows of W^T are read.
 * Squared ReLU as the input transform: max(0, u)^2 in float32, rounded to
@@ -302,12 +307,27 @@ def var_factor(xhat: np.ndarray, keep: np.ndarray) -> np.ndarray:
     return nu.astype(np.float32)
 
 
+def var_factor_ema(xhat: np.ndarray, keep: np.ndarray, r_in, decay: float = 0.9, eps: float = 1e-6):
+    """Running-average VAR ([Guide] s3.2): returns (nu, r_out), both float32 [t].
+
+    r_out_i = decay * r_in_i + (1 - decay) * Var[x_hat_i];
+    nu_i = sqrt(r_out_i / (Var[x_hat_i * m_i] + eps)).  Population variances,
+    float64 throughout.
+    """
+    xh = np.asarray(xhat, dtype=np.float64)
+    num = xh.var(axis=1)
+    den = (xh * keep).var(axis=1)
+    r = decay * np.asarray(r_in, dtype=np.float64) + (1.0 - decay) * num
+    nu = np.sqrt(r / (den + eps))
+    return nu.astype(np.float32), r.astype(np.float32)
+
+
 # ----------------------------------------------------------------------------
 # The whole pruning step and the linear layer
 # ----------------------------------------------------------------------------
 
 def prune(x, dtype: str, n: int, m: int, score: str = "magnitude", f=None, shift_mode: str = "none",
-          eta_in=None, var_rescale: bool = False, act: str = "none") -> dict:
+          eta_in=None, var_rescale=False, act: str = "none", var_state=None) -> dict:
     """(Activation) -> score -> per-block top-n -> pack -> (nu), for X[t, k] given as float32 values.
 
     ``act``: "none" | "relu2" (``x`` is then the pre-activation u, and the
@@ -344,7 +364,10 @@ def prune(x, dtype: str, n: int, m: int, score: str = "magnitude", f=None, shift
     keep = topn_mask(sc, n, m)
     vals, idx = pack(xhat, keep, n, m, dtype)
     out = dict(eta=eta, xhat=xhat, factor=factor, score=sc, keep=keep, vals=vals, idx=idx)
-    out["nu"] = var_factor(xhat, keep) if var_rescale else np.ones(t, dtype=np.float32)
+    if var_rescale == 2:                     # running-average form, state var_state [t]
+        out["nu"], out["var_state"] = var_factor_ema(xhat, keep, var_state)
+    else:
+        out["nu"] = var_factor(xhat, keep) if var_rescale else np.ones(t, dtype=np.float32)
     return out
 
 

@@ -120,6 +120,13 @@ def _eta_table_last(batches, vocab):                     # keeps the last shift,
     return tab
 
 
+def _ema_dense_denominator(xhat, keep, r_in, decay=0.9, eps=1e-6):   # divides by the dense variance
+    xh = np.asarray(xhat, np.float64)
+    num = xh.var(axis=1)
+    r = decay * np.asarray(r_in, np.float64) + (1.0 - decay) * num
+    return np.sqrt(r / (num + eps)).astype(np.float32), r.astype(np.float32)
+
+
 _orig_factor = O.channel_factor
 _orig_amber = O.amber_factor
 _orig_var = O.var_factor
@@ -144,6 +151,7 @@ MUTANTS = {
     "amber_keeps_outliers": ("amber_factor", _amber_no_removal),
     "amber_raw_norm": ("amber_factor", _amber_raw_norm),
     "eta_table_last_value": ("eta_table", _eta_table_last),
+    "ema_dense_denominator": ("var_factor_ema", _ema_dense_denominator),
     "meta_width_floor": ("meta_width", _width_floor),
 }
 

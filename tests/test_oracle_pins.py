@@ -348,6 +348,40 @@ def test_round_to_dtype_matches_torch(dtype, tdt):
 
 
 # --------------------------------------------------------------------------
+# running-average variance factor
+# --------------------------------------------------------------------------
+
+def test_var_ema_exact_small():
+    # x_hat rows of small integers: the variances are exact rationals
+    xh = np.array([[1, -2, 3, 0, 4, -1, 2, 5], [2, 2, -2, -2, 1, 0, 0, 3]], dtype=np.float32)
+    keep = np.array([[1, 0, 1, 0, 1, 0, 0, 1], [1, 1, 1, 1, 0, 0, 0, 0]], dtype=bool)
+    r_in = np.array([2.5, 0.75], dtype=np.float32)
+    nu, r = O.var_factor_ema(xh, keep, r_in)
+    for i in range(2):
+        vals = [Fraction(int(v)) for v in xh[i]]
+        kept = [v if k else Fraction(0) for v, k in zip(vals, keep[i])]
+        var = lambda a: sum(v * v for v in a) / len(a) - (sum(a) / len(a)) ** 2
+        r_want = Fraction(9, 10) * Fraction(float(r_in[i])) + Fraction(1, 10) * var(vals)
+        nu_want = math.sqrt(float(r_want / (var(kept) + Fraction(1, 10 ** 6))))
+        assert abs(float(r[i]) - float(r_want)) <= 1e-7 * float(r_want)
+        assert abs(float(nu[i]) - nu_want) <= 1e-6 * nu_want
+
+
+def test_var_ema_steady_state_matches_closed_form():
+    # with the state at the dense variance, the state stays and nu is the
+    # closed form times sqrt(D / (D + 1e-6))
+    spec = wl.SPECS["batched"].with_(t=8, k=2048)
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    pr = O.prune(_x32(x), "f16", 16, 32)
+    v = pr["xhat"].astype(np.float64).var(axis=1)
+    d = (pr["xhat"].astype(np.float64) * pr["keep"]).var(axis=1)
+    nu, r = O.var_factor_ema(pr["xhat"], pr["keep"], v)
+    assert np.allclose(r, v, rtol=1e-6, atol=0)
+    closed = O.var_factor(pr["xhat"], pr["keep"]).astype(np.float64)
+    assert np.allclose(nu, closed * np.sqrt(d / (d + 1e-6)), rtol=1e-6, atol=0)
+
+
+# --------------------------------------------------------------------------
 # S-PTS table
 # --------------------------------------------------------------------------
 
