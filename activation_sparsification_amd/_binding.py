@@ -33,7 +33,8 @@ class SpaError(RuntimeError):
 
 class _Cfg(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("m", ctypes.c_int32), ("score", ctypes.c_int32),
-                ("shift", ctypes.c_int32), ("var_rescale", ctypes.c_int32), ("act", ctypes.c_int32)]
+                ("shift", ctypes.c_int32), ("var_rescale", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("var_state", ctypes.c_void_p), ("var_state_out", ctypes.c_void_p)]
 
 
 class _Weight(ctypes.Structure):
@@ -96,11 +97,14 @@ class PruneConfig:
     m: int
     score: str = "magnitude"
     shift: str = "none"
-    var_rescale: bool = False
+    var_rescale: int = 0          # 0, 1 (closed form) or 2 (running average: needs the two state tensors)
     act: str = "none"
+    var_state: Optional[torch.Tensor] = None       # var_rescale == 2: float32 [t] state in
+    var_state_out: Optional[torch.Tensor] = None   # var_rescale == 2: float32 [t] state out
 
     def c(self) -> _Cfg:
-        return _Cfg(self.n, self.m, SCORE[self.score], SHIFT[self.shift], int(self.var_rescale), ACT[self.act])
+        return _Cfg(self.n, self.m, SCORE[self.score], SHIFT[self.shift], int(self.var_rescale), ACT[self.act],
+                    _ptr(self.var_state), _ptr(self.var_state_out))
 
 
 @dataclasses.dataclass

@@ -78,11 +78,11 @@ __device__ __forceinline__ bool arrive_last(unsigned* counter, int expected, int
 }
 
 // nu from the four per-token sums (sum x, sum x^2, sum kept x, sum kept x^2) over all k.
-__device__ __forceinline__ float nu_from_stats(const double* s, int k) {
-  const double kk = (double)k;
+__device__ __forceinline__ float nu_from_stats(const double* s, const DecodeArgs& a, int tok, bool writer) {
+  const double kk = (double)a.k;
   const double vf = s[1] / kk - (s[0] / kk) * (s[0] / kk);
   const double vm = s[3] / kk - (s[2] / kk) * (s[2] / kk);
-  return vm > 0.0 ? (float)__builtin_sqrt(vf / vm) : 1.f;
+  return nu_of(vf, vm, a.var, a.var_in, a.var_out, tok, writer);
 }
 
 // Sum over the splits of a tile, in split order, of entry `e` of each split's
@@ -525,7 +525,7 @@ __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(D
   }
   // 6. epilogue
   if (pi < T_ && pc == 0) {
-    const float nu = a.var ? nu_from_stats(stats, a.k) : 1.f;
+    const float nu = a.var ? nu_from_stats(stats, a, pi, tile == 0) : 1.f;
     s_nu[pi] = nu;
     if (tile == 0 && a.nu_out) a.nu_out[pi] = nu;
   }
@@ -776,7 +776,7 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
   }
   // 6. epilogue
   if (threadIdx.x == 0) {
-    const float nu = a.var ? nu_from_stats(stats, a.k) : 1.f;
+    const float nu = a.var ? nu_from_stats(stats, a, 0, tile == 0) : 1.f;
     s_nu = nu;
     if (tile == 0 && a.nu_out) a.nu_out[0] = nu;
   }
@@ -1100,7 +1100,7 @@ __global__ void __launch_bounds__(512) k_decode_mm(DecodeArgs a) {
     if (lane < 4) {
       const int it = wv + 8 * lane;
       if (it < T_) {
-        const float nu = nu_from_stats(sums, K);
+        const float nu = nu_from_stats(sums, a, it, blockIdx.x == 0);
         s_nu[it] = nu;
         if (blockIdx.x == 0 && a.nu_out) a.nu_out[it] = nu;
       }

@@ -301,7 +301,7 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
       const double kk = (double)a.k;
       const double var_full = txx / kk - (tx / kk) * (tx / kk);
       const double var_mask = tmm / kk - (tm / kk) * (tm / kk);
-      if (var_mask > 0.0) nu = (float)__builtin_sqrt(var_full / var_mask);
+      nu = nu_of(var_full, var_mask, a.var, a.var_in, a.var_out, row, threadIdx.x == 0);
     }
     if (threadIdx.x == 0 && a.nu_out) a.nu_out[row] = nu;
   }

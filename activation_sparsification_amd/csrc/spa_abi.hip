@@ -21,7 +21,8 @@ bool valid_cfg(const spa_prune_cfg* c) {
   if (c->n < 1 || c->n > c->m) return false;
   if (c->score < SPA_SCORE_MAGNITUDE || c->score > SPA_SCORE_CLACT) return false;
   if (c->shift < SPA_SHIFT_NONE || c->shift > SPA_SHIFT_GIVEN) return false;
-  if (c->var_rescale != 0 && c->var_rescale != 1) return false;
+  if (c->var_rescale < 0 || c->var_rescale > 2) return false;
+  if (c->var_rescale == 2 && (!c->var_state || !c->var_state_out || c->var_state == c->var_state_out)) return false;
   if (c->act != SPA_ACT_NONE && c->act != SPA_ACT_RELU2) return false;
   return true;
 }
@@ -146,6 +147,8 @@ spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const sp
   spa::PruneArgs a{};
   a.x = x; a.t = t; a.k = k; a.n = cfg->n; a.m = cfg->m;
   a.var = cfg->var_rescale;
+  a.var_in = cfg->var_state;
+  a.var_out = cfg->var_state_out;
   a.act = cfg->act;
   a.chan_scale = cfg->score == SPA_SCORE_WEIGHT ? chan_scale : nullptr;
   a.eta_given = cfg->shift == SPA_SHIFT_GIVEN ? eta_in : nullptr;
@@ -196,6 +199,8 @@ spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, c
   }
   a.x = x;
   a.act = cfg->act;
+  a.var_in = cfg->var_state;
+  a.var_out = cfg->var_state_out;
   a.wt = w->wt;
   a.w = w->w;
   a.chan_scale = w->chan_scale;
@@ -227,6 +232,8 @@ spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, 
   spa::PruneArgs a{};
   a.x = x; a.t = t; a.k = k; a.n = cfg->n; a.m = cfg->m;
   a.var = cfg->var_rescale;
+  a.var_in = cfg->var_state;
+  a.var_out = cfg->var_state_out;
   a.act = cfg->act;
   a.chan_scale = cfg->score == SPA_SCORE_WEIGHT ? w->chan_scale : nullptr;
   a.eta_given = cfg->shift == SPA_SHIFT_GIVEN ? eta_in : nullptr;

@@ -143,6 +143,23 @@ __device__ __forceinline__ float sqrt_rn(float a) { return (float)__builtin_sqrt
 
 
 // ---------------------------------------------------------------------------
+// The variance factor from a token's dense and masked variances (the guide's
+// s3.2): the closed form sqrt(vf / vm) (1 when vm == 0), or, with mode 2, the
+// running-average form: r = 0.9 r_in + 0.1 vf, nu = sqrt(r / (vm + 1e-6)),
+// the new state written by the one caller that passes `writer`.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float nu_of(double vf, double vm, int mode, const float* r_in, float* r_out, int tok,
+                                       bool writer) {
+#pragma clang fp contract(off)
+  if (mode == 2) {
+    const double r = 0.9 * (double)r_in[tok] + 0.1 * vf;
+    if (writer) r_out[tok] = (float)r;
+    return (float)__builtin_sqrt(r / (vm + 1e-6));
+  }
+  return vm > 0.0 ? (float)__builtin_sqrt(vf / vm) : 1.f;
+}
+
+// ---------------------------------------------------------------------------
 // Double-double sums (weight preparation): the float64 result of hi + lo is
 // the correctly rounded exact sum in all but pathological cases.
 // ---------------------------------------------------------------------------

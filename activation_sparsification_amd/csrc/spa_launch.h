@@ -27,7 +27,9 @@ struct PruneArgs {
   int t, k, n, m;
   int shift_mean;            // compute the token mean in-kernel
   int act;                   // input transform (SPA_ACT_*)
-  int var;
+  int var;                   // 0, 1 (closed form) or 2 (running average)
+  const float* var_in;       // var == 2: state [t]
+  float* var_out;            // var == 2: new state [t]
   int pack;                  // PackFormat bits
   void* vals;                // kPackVals
   uint8_t* idx;              // kPackVals, may be NULL
@@ -57,7 +59,9 @@ struct DecodeArgs {
   int t, k, n_out, n, m;
   int score;                 // SPA_SCORE_*
   int shift;                 // SPA_SHIFT_*
-  int var;
+  int var;                   // 0, 1 (closed form) or 2 (running average)
+  const float* var_in;       // var == 2: state [t]
+  float* var_out;            // var == 2: new state [t]
   int act;                   // input transform (SPA_ACT_*)
   // workspace carve-up
   float* partial;            // fused: [splits][t][n_out]

@@ -26,8 +26,11 @@
  *   mask     keep the n largest scores of every m consecutive channels
  *            (guide s2.1); equal scores go to the lower channel index, so
  *            exactly n are kept per block;
- *   nu       optional variance rescale sqrt(Var[x_hat] / Var[x_hat * mask])
- *            per token (guide s3.2, closed form; 1 when the denominator is 0);
+ *   nu       optional variance rescale per token (guide s3.2): the closed
+ *            form sqrt(Var[x_hat] / Var[x_hat * mask]) (1 when the
+ *            denominator is 0), or its running-average form: a caller-held
+ *            state r per token, r' = 0.9 r + 0.1 Var[x_hat] (written to
+ *            var_state_out), nu = sqrt(r' / (Var[x_hat * mask] + 1e-6));
  *   y        = nu * (x_hat * mask) W^T + eta * (W 1), which equals the
  *            guide's (x_sparse + eta) W^T without reading pruned rows of W.
  *
@@ -81,8 +84,12 @@ typedef struct spa_prune_cfg {
   int32_t m;
   int32_t score;        /* SPA_SCORE_* */
   int32_t shift;        /* SPA_SHIFT_* */
-  int32_t var_rescale;  /* 0 or 1 */
+  int32_t var_rescale;  /* 0, 1 (closed form) or 2 (running average) */
   int32_t act;          /* SPA_ACT_*: activation applied to the input first */
+  /* var_rescale == 2 only: [device] [t] float32 per-token state in, and the
+   * updated state out (must not alias); ignored otherwise. */
+  const float* var_state;
+  float* var_state_out;
 } spa_prune_cfg;
 
 /* A prepared linear layer.  Fields not needed by an entry point may be NULL:

@@ -307,17 +307,18 @@ def var_factor(xhat: np.ndarray, keep: np.ndarray) -> np.ndarray:
     return nu.astype(np.float32)
 
 
-def var_factor_ema(xhat: np.ndarray, keep: np.ndarray, r_in, decay: float = 0.9, eps: float = 1e-6):
+def var_factor_ema(xhat: np.ndarray, keep: np.ndarray, r_in, decay: float = 0.9, gain: float = 0.1,
+                   eps: float = 1e-6):
     """Running-average VAR ([Guide] s3.2): returns (nu, r_out), both float32 [t].
 
-    r_out_i = decay * r_in_i + (1 - decay) * Var[x_hat_i];
+    r_out_i = decay * r_in_i + gain * Var[x_hat_i] (0.9 and 0.1 as printed);
     nu_i = sqrt(r_out_i / (Var[x_hat_i * m_i] + eps)).  Population variances,
     float64 throughout.
     """
     xh = np.asarray(xhat, dtype=np.float64)
     num = xh.var(axis=1)
     den = (xh * keep).var(axis=1)
-    r = decay * np.asarray(r_in, dtype=np.float64) + (1.0 - decay) * num
+    r = decay * np.asarray(r_in, dtype=np.float64) + gain * num
     nu = np.sqrt(r / (den + eps))
     return nu.astype(np.float32), r.astype(np.float32)
 

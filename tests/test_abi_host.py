@@ -128,6 +128,13 @@ def test_linear_rejections_happen_before_any_launch(lib):
     assert L.prune_nm(16, 2, 4, 60, ctypes.byref(good), None, None, 32, None, None, None, None, 0, None) == 1
     bad = B.PruneConfig(5, 4).c()
     assert L.prune_nm(16, 2, 4, 64, ctypes.byref(bad), None, None, 32, None, None, None, None, 0, None) == 1
+    st = ctypes.c_void_p(4096)
+    bad = B._Cfg(2, 4, 0, 0, 2, 0, None, None)                        # running average without its state
+    assert L.prune_nm(16, 2, 4, 64, ctypes.byref(bad), None, None, 32, None, None, None, None, 0, None) == 1
+    bad = B._Cfg(2, 4, 0, 0, 2, 0, st, st)                            # state in and out aliased
+    assert L.prune_nm(16, 2, 4, 64, ctypes.byref(bad), None, None, 32, None, None, None, None, 0, None) == 1
+    bad = B._Cfg(2, 4, 0, 0, 3, 0, None, None)
+    assert L.prune_nm(16, 2, 4, 64, ctypes.byref(bad), None, None, 32, None, None, None, None, 0, None) == 1
     bad = B._Cfg(2, 4, 0, 0, 0, 9)
     assert L.prune_nm(16, 2, 4, 64, ctypes.byref(bad), None, None, 32, None, None, None, None, 0, None) == 1
     assert L.prune_nm(None, 2, 4, 64, ctypes.byref(good), None, None, 32, None, None, None, None, 0, None) == 1

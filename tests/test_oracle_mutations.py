@@ -120,10 +120,10 @@ def _eta_table_last(batches, vocab):                     # keeps the last shift,
     return tab
 
 
-def _ema_dense_denominator(xhat, keep, r_in, decay=0.9, eps=1e-6):   # divides by the dense variance
+def _ema_dense_denominator(xhat, keep, r_in, decay=0.9, gain=0.1, eps=1e-6):   # divides by the dense variance
     xh = np.asarray(xhat, np.float64)
     num = xh.var(axis=1)
-    r = decay * np.asarray(r_in, np.float64) + (1.0 - decay) * num
+    r = decay * np.asarray(r_in, np.float64) + gain * num
     return np.sqrt(r / (num + eps)).astype(np.float32), r.astype(np.float32)
 
 

@@ -54,6 +54,52 @@ def test_prepare_weight(name, alpha):
 
 
 # ---------------------------------------------------------------------------
+# running-average variance factor (var_rescale = 2)
+# ---------------------------------------------------------------------------
+EMA_CASES = [
+    ("prune_bf16_2_4", "prune", wl.SPECS["prefill"].with_(t=37, k=1024, n_outliers=0)),
+    ("prune_f32_16_32", "prune", wl.SPECS["batched"].with_(t=5, k=512, dtype="f32")),
+    ("prefill_2_4", "prefill", wl.SPECS["prefill"].with_(t=300, k=512, n_out=272, n_outliers=0)),
+    ("prefill_8_16", "prefill", wl.SPECS["prefill"].with_(t=77, k=320, n_out=300, n=8, m=16, n_outliers=0)),
+    ("decode_t1_wide", "decode", wl.SPECS["decode"].with_(t=1, k=2048, n_out=4096)),
+    ("decode_t1_narrow", "decode", wl.SPECS["batched"].with_(t=1, k=1024, n_out=776)),
+    ("decode_t3", "decode", wl.SPECS["batched"].with_(t=3, k=512, n_out=136)),
+    ("decode_mm_t20", "decode", wl.SPECS["batched"].with_(t=20, k=1056, n_out=328)),
+    ("decode_f32_t8", "decode", wl.SPECS["tiny"].with_(t=8)),
+]
+
+
+@pytest.mark.parametrize("label,entry,spec", EMA_CASES, ids=[c[0] for c in EMA_CASES])
+def test_var_running_average(label, entry, spec):
+    dev = _dev()
+    spec = spec.with_(var_rescale=2)
+    x, w = wl.make_inputs(spec)
+    r_in = (np.random.Generator(np.random.PCG64(spec.t)).uniform(0.05, 2.0, size=spec.t)).astype(np.float32)
+    st_in = torch.from_numpy(r_in).to(dev)
+    st_out = torch.full((spec.t,), -1.0, dtype=torch.float32, device=dev)
+    cfg = spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, 2, spec.act, st_in, st_out)
+    f = None
+    if entry == "prune":
+        f = O.channel_factor(f32(w), spec.alpha) if spec.score == "weight" else None
+        vals, idx, eta, nu = spa.prune_nm(x.to(dev), cfg, chan_scale=None if f is None else torch.from_numpy(f).to(dev))
+    else:
+        pw = spa.prepare_weight(w.to(dev), spec.alpha, want_wt=entry == "decode")
+        f = f32(pw.chan_scale) if spec.score == "weight" else None
+        fn = spa.sparse_linear_decode if entry == "decode" else spa.sparse_linear_prefill
+        y, idx, nu = fn(x.to(dev), pw, cfg, want_idx=True, want_nu=True)
+    torch.cuda.synchronize()
+    pr = O.prune(f32(x), spec.dtype, spec.n, spec.m, score=spec.score, f=f, shift_mode=spec.shift, var_rescale=2,
+                 var_state=r_in)
+    assert np.array_equal(idx.cpu().numpy(), pr["idx"])
+    assert np.allclose(f32(nu), pr["nu"], rtol=1e-6, atol=0), np.abs(f32(nu) / pr["nu"] - 1).max()
+    assert np.allclose(f32(st_out), pr["var_state"], rtol=1e-6, atol=0)
+    assert np.array_equal(f32(st_in), r_in)                            # the input state is left alone
+    if entry != "prune":
+        err = O.rowwise_error(f32(y), O.linear(pr, f32(w)))
+        assert err <= O.TOLERANCE[spec.dtype], err
+
+
+# ---------------------------------------------------------------------------
 # static shift table (S-PTS)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
