@@ -473,6 +473,23 @@ def decode_meta(codes: np.ndarray, k: int, n: int, m: int, fmt: str) -> np.ndarr
     return out
 
 
+def ffn_relu2(x, w_up, w_down, dtype: str) -> dict:
+    """Squared-ReLU FFN with its activation pruned 2:4 ([SqReLU] s2.2, s3.1).
+
+    u = the up-projection x W_up^T as a float32-accumulating GEMM stores it:
+    the exact sum rounded to float32, then to ``dtype``; the activation
+    squared_relu(u) is pruned 2:4 by magnitude (no shift); y = the
+    down-projection of the pruned activation, float64.
+    Returns the prune record (``u`` included) with ``y``.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    u = round_to_dtype((x64 @ np.asarray(w_up, dtype=np.float64).T).astype(np.float32), dtype)
+    pr = prune(u, dtype, 2, 4, act="relu2")
+    pr["u"] = u
+    pr["y"] = linear(pr, w_down, s=np.zeros(np.asarray(w_down).shape[0]))
+    return pr
+
+
 def rowwise_error(y_test: np.ndarray, y_ref: np.ndarray) -> float:
     """max_i ( max_j |y_test - y_ref| / max_j |y_ref| ): the row-normwise relative error."""
     y_test = np.asarray(y_test, dtype=np.float64)

@@ -348,6 +348,36 @@ def test_round_to_dtype_matches_torch(dtype, tdt):
 
 
 # --------------------------------------------------------------------------
+# squared-ReLU FFN
+# --------------------------------------------------------------------------
+
+def test_ffn_relu2_small_exact():
+    # integer inputs: the up-projection is exact, so u, its square, the mask
+    # and the output follow from integer arithmetic
+    rng = np.random.Generator(np.random.PCG64(8))
+    x = rng.integers(-3, 4, size=(3, 16)).astype(np.float32)
+    w_up = rng.integers(-2, 3, size=(8, 16)).astype(np.float32)
+    w_dn = rng.integers(-2, 3, size=(5, 8)).astype(np.float32)
+    pr = O.ffn_relu2(x, w_up, w_dn, "bf16")
+    u = x.astype(np.int64) @ w_up.astype(np.int64).T
+    # the activation is stored in bf16: each square rounded once (exact rationals)
+    a = np.array([[_round_exact(Fraction(int(v)) ** 2, "bf16") if v > 0 else 0.0 for v in row] for row in u])
+    assert np.array_equal(pr["u"], u.astype(np.float32))
+    for i in range(3):
+        for b in range(2):
+            blk = a[i, 4 * b:4 * b + 4]
+            order = sorted(range(4), key=lambda j: (-blk[j], j))[:2]
+            assert sorted(order) == list(pr["idx"][i, 2 * b:2 * b + 2])
+    keep = np.zeros_like(a)
+    for i in range(3):
+        for b in range(2):
+            for j in pr["idx"][i, 2 * b:2 * b + 2]:
+                keep[i, 4 * b + j] = a[i, 4 * b + j]
+    y = [[float(sum(Fraction(keep[i, c]) * int(w_dn[o, c]) for c in range(8))) for o in range(5)] for i in range(3)]
+    assert np.array_equal(pr["y"], np.array(y))
+
+
+# --------------------------------------------------------------------------
 # running-average variance factor
 # --------------------------------------------------------------------------
 
