@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     prune_nm,
     sparse_linear_decode,
     sparse_linear_prefill,
+    sparse_ffn_relu2_prefill,
     workspace,
     workspace_bytes,
 )

@@ -65,6 +65,11 @@ def lib() -> ctypes.CDLL:
         L.spa_eta_table.argtypes = [vp, vp, i32, vp, vp]
         L.spa_eta_lookup.restype = ctypes.c_int
         L.spa_eta_lookup.argtypes = [vp, i32, vp, i32, vp, vp]
+        L.spa_ffn_workspace_bytes.restype = sz
+        L.spa_ffn_workspace_bytes.argtypes = [i32, i32, i32]
+        L.sparse_ffn_relu2_prefill.restype = ctypes.c_int
+        L.sparse_ffn_relu2_prefill.argtypes = [vp, i32, ctypes.POINTER(_Weight), ctypes.POINTER(_Weight), vp, vp,
+                                               vp, sz, vp]
         L.spa_amber_workspace_bytes.restype = sz
         L.spa_amber_workspace_bytes.argtypes = []
         L.prepare_amber.restype = ctypes.c_int
@@ -87,7 +92,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("prepare_weight", "prune_nm", "sparse_linear_decode", "sparse_linear_prefill",
            "spa_workspace_bytes", "spa_status_str", "spa_meta_row_bytes", "spa_encode_meta", "spa_decode_meta",
-           "prepare_amber", "spa_amber_workspace_bytes", "spa_eta_calibrate", "spa_eta_table", "spa_eta_lookup")
+           "prepare_amber", "spa_amber_workspace_bytes", "spa_eta_calibrate", "spa_eta_table", "spa_eta_lookup",
+           "sparse_ffn_relu2_prefill", "spa_ffn_workspace_bytes")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -199,6 +205,28 @@ def prune_nm(x: torch.Tensor, cfg: PruneConfig, chan_scale: Optional[torch.Tenso
                           _ptr(vals), _ptr(idx), _ptr(eta), _ptr(nu), _ptr(ws), 0 if ws is None else ws.numel(),
                           _stream(dev)), "prune_nm")
     return vals, idx, eta, nu
+
+
+def sparse_ffn_relu2_prefill(x: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, want_idx: bool = False,
+                             out: Optional[torch.Tensor] = None):
+    """y = prune24(max(x W_up^T, 0)^2) W_down^T; returns (y [t, n_out], idx [t, ffn/2] uint8 or None)."""
+    dev = _dev(x)
+    t, hidden = x.shape
+    ffn = w_up.shape[0]
+    n_out = w_down.shape[0]
+    y = torch.empty((t, n_out), dtype=x.dtype, device=dev) if out is None else out
+    idx = torch.empty((t, ffn // 2), dtype=torch.uint8, device=dev) if want_idx else None
+    nb = int(lib().spa_ffn_workspace_bytes(t, ffn, DTYPE[x.dtype]))
+    key = (str(dev), "ffn", nb)
+    ws = _WS_CACHE.get(key)
+    if ws is None:
+        ws = torch.zeros(max(nb, 1), dtype=torch.uint8, device=dev)
+        _WS_CACHE[key] = ws
+    up = _Weight(DTYPE[w_up.dtype], ffn, hidden, _ptr(w_up), None, None, None)
+    dn = _Weight(DTYPE[w_down.dtype], n_out, ffn, _ptr(w_down), None, None, None)
+    _check(lib().sparse_ffn_relu2_prefill(_ptr(x), t, ctypes.byref(up), ctypes.byref(dn), _ptr(y), _ptr(idx), _ptr(ws),
+                                          nb, _stream(dev)), "sparse_ffn_relu2_prefill")
+    return y, idx
 
 
 class EtaCalibration:

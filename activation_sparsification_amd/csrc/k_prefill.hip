@@ -296,8 +296,17 @@ __global__ void __launch_bounds__(512, 1) k_gemm24(PrefillArgs p) {
 // wave issues six 1 KB direct loads per step, so vmcnt <= 6 means "the older
 // step in flight has landed".  Rows past t (or n_out) re-read the last row;
 // their outputs are never stored.  Chunk c of any row r sits at c ^ ((r>>1)&7).
+//
+// EPI = 1 is the up-projection of a squared-ReLU FFN whose activation feeds a
+// 2:4 layer ("Accelerating Transformer training and inference with 2:4
+// sparsity and Squared-ReLU" s3.1: one kernel applies the activation, prunes
+// and packs): the tile's outputs u are rounded to the storage dtype, squared
+// after max(u, 0) and rounded again (what a separate pass would store), held
+// in the freed LDS ring as two 64-channel steps, then pruned 2:4 by magnitude
+// and packed into the tiled operand of the 2:4 GEMM -- the activation never
+// reaches HBM dense.
 // ---------------------------------------------------------------------------
-template <int DT>
+template <int DT, int EPI>
 __global__ void __launch_bounds__(512, 1) k_gemm_dense(PrefillArgs p) {
   constexpr int BM = 256, BN = 128;
   constexpr int WM = 64, WN = 64, FM = 2, FN = 2;
@@ -413,9 +422,84 @@ __global__ void __launch_bounds__(512, 1) k_gemm_dense(PrefillArgs p) {
 #undef SPA_ISSUED
 #undef SPA_COMPUTED
 
-  ts.park(s_nu, s_eta, s_rs);
-  __syncthreads();
-  store_tile<DT, FM, FN>(p, acc, m0, n0, wm0, wn0, g, l32, s_nu, s_eta, s_rs);
+  if constexpr (EPI == 0) {
+    ts.park(s_nu, s_eta, s_rs);
+    __syncthreads();
+    store_tile<DT, FM, FN>(p, acc, m0, n0, wm0, wn0, g, l32, s_nu, s_eta, s_rs);
+  } else {
+    // every wave is past its last read of the ring: step 0 of the tile (its
+    // columns 0..63) goes to sA0, step 1 to sA1, row-major [256][64]
+    __syncthreads();
+    uint16_t* s_step = (wn0 == 0) ? sA0 : sA1;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tr = wm0 + 32 * i + 8 * (r / 4) + 4 * g + (r % 4);
+          const int tc = 32 * j + l32;                          // column inside the step
+          const float u = to_f32<DT>(from_f32<DT>(acc[i][j][r]));
+          s_step[tr * 64 + tc] = from_f32<DT>(relu2<DT>(u));
+        }
+    __syncthreads();
+    // 2 steps x 256 rows x 4 segments of 16 channels (four 2:4 blocks each)
+    const int step0 = n0 / 64;
+    for (int e = threadIdx.x; e < 2 * BM * 4; e += 512) {
+      const int s = e >> 10, rr = (e >> 2) & (BM - 1), q = e & 3;
+      const int row = m0 + rr;
+      if (row >= T || n0 + 64 * s >= N) continue;
+      const uint16_t* src = (s ? sA1 : sA0) + rr * 64 + 16 * q;
+      const uint4 lo4 = *reinterpret_cast<const uint4*>(src);
+      const uint4 hi4 = *reinterpret_cast<const uint4*>(src + 8);
+      const uint32_t w8[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+      uint32_t wds[4], meta = 0;
+      uint32_t pos[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        uint32_t bits[4];
+        float sc[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint32_t wv2 = w8[(4 * b + jj) >> 1];
+          bits[jj] = ((4 * b + jj) & 1) ? (wv2 >> 16) : (wv2 & 0xFFFFu);
+          sc[jj] = __builtin_fabsf(to_f32<DT>((uint16_t)bits[jj]));
+        }
+        // rank rule: j < q beats q unless q's score is strictly larger
+        int rank[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int j0 = 0; j0 < 4; ++j0)
+#pragma unroll
+          for (int j1 = j0 + 1; j1 < 4; ++j1) {
+            const bool w0 = sc[j0] >= sc[j1];
+            rank[j1] += w0 ? 1 : 0;
+            rank[j0] += w0 ? 0 : 1;
+          }
+        uint32_t kb = 0;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) kb |= (rank[jj] < 2 ? 1u : 0u) << jj;
+        const uint32_t lo = __builtin_ctz(kb), hi = 31 - __builtin_clz(kb);
+        meta |= (lo | (hi << 2)) << (4 * b);
+        uint32_t vlo = bits[0], vhi = bits[0];
+#pragma unroll
+        for (int jj = 1; jj < 4; ++jj) {
+          vlo = (int)lo == jj ? bits[jj] : vlo;
+          vhi = (int)hi == jj ? bits[jj] : vhi;
+        }
+        wds[b] = vlo | (vhi << 16);
+        pos[b] = lo | (hi << 8);
+      }
+      const size_t rowpos = (size_t)(step0 + s) * p.out_t_pad + row;
+      reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out_vals) + rowpos * 32)[q] =
+          make_uint4(wds[0], wds[1], wds[2], wds[3]);
+      p.out_meta[rowpos * 4 + q] = (uint16_t)meta;
+      if (p.out_idx) {
+        // positions of the segment's four blocks, two bytes each, row-major [t][n_out/2]
+        uint8_t* ip = p.out_idx + (size_t)row * (N / 2) + (size_t)(n0 + 64 * s + 16 * q) / 2;
+        *reinterpret_cast<uint2*>(ip) = make_uint2(pos[0] | (pos[1] << 16), pos[2] | (pos[3] << 16));
+      }
+    }
+  }
 }
 
 hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st) {
@@ -426,9 +510,17 @@ hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st) {
     else hipLaunchKernelGGL(k_gemm24<SPA_BF16>, dim3(tiles), dim3(512), 0, st, a);
   } else {
     const int tiles = ((a.t + 255) / 256) * ((a.n_out + 127) / 128);
-    if (dtype == SPA_F16) hipLaunchKernelGGL(k_gemm_dense<SPA_F16>, dim3(tiles), dim3(512), 0, st, a);
-    else hipLaunchKernelGGL(k_gemm_dense<SPA_BF16>, dim3(tiles), dim3(512), 0, st, a);
+    if (dtype == SPA_F16) hipLaunchKernelGGL((k_gemm_dense<SPA_F16, 0>), dim3(tiles), dim3(512), 0, st, a);
+    else hipLaunchKernelGGL((k_gemm_dense<SPA_BF16, 0>), dim3(tiles), dim3(512), 0, st, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_up(int dtype, const PrefillArgs& a, hipStream_t st) {
+  if (a.t == 0) return hipSuccess;
+  const int tiles = ((a.t + 255) / 256) * ((a.n_out + 127) / 128);
+  if (dtype == SPA_F16) hipLaunchKernelGGL((k_gemm_dense<SPA_F16, 1>), dim3(tiles), dim3(512), 0, st, a);
+  else hipLaunchKernelGGL((k_gemm_dense<SPA_BF16, 1>), dim3(tiles), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

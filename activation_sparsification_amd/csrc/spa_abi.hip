@@ -305,6 +305,56 @@ spa_status spa_eta_lookup(const float* table, int32_t vocab, const int32_t* toke
   return hip_status(spa::launch_eta_lookup(table, vocab, token_ids, t, eta_out, static_cast<hipStream_t>(stream)));
 }
 
+size_t spa_ffn_workspace_bytes(int32_t t, int32_t ffn, int32_t dtype) {
+  if (t < 0 || t > kMaxDim || ffn < 64 || ffn > kMaxPrefillK || ffn % 64 || (dtype != SPA_F16 && dtype != SPA_BF16))
+    return 0;
+  const size_t rows = (size_t)tiled_rows(t);
+  return round256(rows * (size_t)(ffn / 2) * 2) + round256(rows * (size_t)(ffn / 16) * 2);
+}
+
+spa_status sparse_ffn_relu2_prefill(const void* x, int32_t t, const spa_weight* up, const spa_weight* down,
+                                    void* y, uint8_t* idx_out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (!x || !y || !up || !down || t < 0 || t > kMaxDim) return SPA_ERR_INVALID;
+  if (up->dtype != down->dtype || (up->dtype != SPA_F16 && up->dtype != SPA_BF16)) return SPA_ERR_INVALID;
+  const int hidden = up->k, ffn = up->n_out;
+  if (hidden < 64 || hidden % 64 || ffn < 64 || ffn % 64 || down->k != ffn) return SPA_ERR_INVALID;
+  if (down->n_out < 8 || down->n_out % 8 || down->n_out > kMaxDim) return SPA_ERR_INVALID;
+  if (hidden > kMaxPrefillK || ffn > kMaxPrefillK) return SPA_ERR_UNSUPPORTED;
+  if (!up->w || !down->w || !aligned16(up->w) || !aligned16(down->w) || !aligned16(x) || !aligned16(y))
+    return SPA_ERR_INVALID;
+  if (idx_out && !aligned16(idx_out)) return SPA_ERR_INVALID;
+  if (t == 0) return SPA_OK;
+  const size_t need = spa_ffn_workspace_bytes(t, ffn, up->dtype);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SPA_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int t_pad = tiled_rows(t);
+  char* base = static_cast<char*>(workspace);
+  void* vals = base;
+  uint16_t* meta = reinterpret_cast<uint16_t*>(base + round256((size_t)t_pad * (size_t)(ffn / 2) * 2));
+
+  spa::PrefillArgs u{};
+  u.w = up->w;
+  u.a_vals = x;
+  u.t = t; u.k = hidden; u.n_out = ffn;
+  u.sparse24 = 0;
+  u.out_vals = vals;
+  u.out_meta = meta;
+  u.out_t_pad = t_pad;
+  u.out_idx = idx_out;
+  if (hipError_t e = spa::launch_ffn_up(up->dtype, u, st)) return hip_status(e);
+
+  spa::PrefillArgs g{};
+  g.w = down->w;
+  g.a_vals = vals;
+  g.a_meta = meta;
+  g.t_pad = t_pad;
+  g.y = y;
+  g.t = t; g.k = ffn; g.n_out = down->n_out;
+  g.sparse24 = 1;
+  return hip_status(spa::launch_gemm(down->dtype, g, st));
+}
+
 size_t spa_amber_workspace_bytes(void) { return spa::amber_workspace_bytes(); }
 
 spa_status prepare_amber(const void* w, int32_t dtype, int32_t n_out, int32_t k, float alpha, float* chan_scale_out,

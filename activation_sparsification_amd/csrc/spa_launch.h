@@ -106,7 +106,14 @@ struct PrefillArgs {
   void* y;
   int t, k, n_out;
   int sparse24;
+  // dense GEMM with the squared-ReLU epilogue (launch_ffn_up): the output is
+  // not stored; max(u, 0)^2 is pruned 2:4 and packed in the tiled layout
+  void* out_vals;            // [n_out/64][out_t_pad][32] dtype
+  uint16_t* out_meta;        // [n_out/64][out_t_pad][4]
+  int out_t_pad;
+  uint8_t* out_idx;          // [t][n_out/2] in-block positions, or NULL
 };
 hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st);
+hipError_t launch_ffn_up(int dtype, const PrefillArgs& a, hipStream_t st);
 
 }  // namespace spa

@@ -248,6 +248,74 @@ def measure_meta(fmt, n, m, t, k, steps, warmup):
     return recs
 
 
+def measure_ffn(steps, warmup, t=4096, hidden=4096, ffn=16384, n_out=4096):
+    """The squared-ReLU FFN of the relu2 layer: fused (one call; the up-projection's epilogue prunes
+    and packs) and unfused (a dense up-projection stores u, then the pruning pass applies the squared
+    ReLU); TFLOP/s of 2 t hidden ffn (dense up) + 2 t ffn n_out / 2 (kept down) per step."""
+    import activation_sparsification_amd as spa
+    dev = torch.device("cuda:0")
+    spec = wl.SPECS["prefill"].with_(t=t, k=hidden, n_out=ffn, n_outliers=0)
+    x, w_up = wl.make_inputs(spec)
+    _, w_dn = wl.make_inputs(spec.with_(k=ffn, n_out=n_out), seed=1)
+    x = x.to(dev)
+    ups = [w_up.to(dev)]
+    dns = [w_dn.to(dev)]
+    copies = max(2, math.ceil(3 * MALL_BYTES / (ups[0].numel() * 2 + dns[0].numel() * 2)))
+    ups += [ups[0].clone() for _ in range(copies - 1)]
+    dns += [dns[0].clone() for _ in range(copies - 1)]
+    y = torch.empty((t, n_out), dtype=x.dtype, device=dev)
+    u = torch.empty((t, ffn), dtype=x.dtype, device=dev)
+    pw_up = [spa.PreparedWeight(w, None, None, None) for w in ups]
+    pw_dn = [spa.PreparedWeight(w, None, None, None) for w in dns]
+    dense = spa.PruneConfig(4, 4)
+    relu2 = spa.PruneConfig(2, 4, act="relu2")
+    ws_up = spa.workspace(2, t, hidden, ffn, x.dtype, dense, dev)
+    ws_dn = spa.workspace(2, t, ffn, n_out, x.dtype, relu2, dev)
+    unfused = [(spa.PreparedCall("sparse_linear_prefill", x, pw_up[i], dense, u, ws_up),
+                spa.PreparedCall("sparse_linear_prefill", u, pw_dn[i], relu2, y, ws_dn)) for i in range(copies)]
+    flops = 2.0 * t * hidden * ffn + 2.0 * t * ffn * n_out / 2
+
+    def block(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(2e6))
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def fused(i):
+        spa.sparse_ffn_relu2_prefill(x, ups[i % copies], dns[i % copies], out=y)
+
+    def unf(i):
+        a, b = unfused[i % copies]
+        a()
+        b()
+
+    # the two pipelines alternate in short timed blocks (the clock drifts under sustained load);
+    # the median block of each is reported
+    for i in range(warmup):
+        fused(i)
+        unf(i)
+    torch.cuda.synchronize()
+    per = {"ffn_relu2_fused": [], "ffn_relu2_unfused": []}
+    nblk = max(1, steps // 4)
+    for _ in range(4):
+        per["ffn_relu2_fused"].append(block(fused, nblk))
+        per["ffn_relu2_unfused"].append(block(unf, nblk))
+    recs = []
+    for name in ("ffn_relu2_fused", "ffn_relu2_unfused"):
+        ms = sorted(per[name])[len(per[name]) // 2]
+        tf = flops / (ms * 1e-3) / 1e12
+        recs.append(dict(workload=name, unit="TFLOP/s", value=tf, ms_per_step=ms, pct_of_peak=100.0 * tf / PEAK_BF16_TFLOPS,
+                         flops=flops, weight_copies=copies, blocks_ms=per[name],
+                         desc=f"squared-ReLU FFN x[{t},{hidden}] -> {ffn} -> {n_out} bf16, activation pruned 2:4"))
+    del ups, dns, unfused
+    torch.cuda.empty_cache()
+    return recs
+
+
 def cpu_baseline(name, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the workload on the host cores."""
     from oracle import nm_oracle as O
@@ -312,8 +380,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS) + ["meta"],
-                    help="meta: only the block-metadata encode/decode lines (one JSON line)")
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS) + ["meta", "ffn"],
+                    help="meta / ffn: only the block-metadata codec or squared-ReLU FFN lines (one JSON line)")
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -335,6 +403,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.workload == "ffn":
+        print(json.dumps({"ffn": measure_ffn(args.steps, args.warmup)}))
+        return
     if args.workload == "meta":
         recs = []
         for fmt, n, m, t, k in [("comb", 2, 4, 4096, 16384), ("bitmap", 2, 4, 4096, 16384),
@@ -352,6 +423,7 @@ def main():
             st = max(10, args.steps // 4) if name in ("prefill", "relu2", "relu2_fused") else args.steps
             secondary.append(measure(name, st, max(5, args.warmup // 2)))
         secondary += measure_meta("comb", 2, 4, 4096, 16384, args.steps, max(5, args.warmup // 2))
+        secondary += measure_ffn(max(5, args.steps // 20), 3)
 
     decode = head["unit"] == "GB/s"
     traffic = read_traffic() if args.workload == "decode" else None

@@ -257,6 +257,32 @@ spa_status spa_encode_meta(const uint8_t* idx, int32_t t, int32_t k, int32_t n, 
 spa_status spa_decode_meta(const void* codes, int32_t t, int32_t k, int32_t n, int32_t m, int32_t format,
                            uint8_t* idx_out, void* stream);
 
+/*
+ * sparse_ffn_relu2_prefill -- a squared-ReLU FFN whose activation is pruned
+ * 2:4 on its way to the down-projection, with that activation never stored
+ * dense ("Accelerating Transformer training and inference with 2:4 sparsity
+ * and Squared-ReLU" s2.2, s3.1):
+ *   u = x W_up^T (float32 accumulation, rounded to dtype);
+ *   a = dtype(max(u, 0)^2);  keep 2 of every 4 by |a| (ties to the lower
+ *   index);  y = (a * mask) W_down^T.
+ * The up-projection's epilogue squares, prunes and packs its tile straight
+ * into the 2:4 operand; the down-projection runs on the sparse MFMA.
+ *  x       [device] [t][hidden]; up: w [ffn][hidden]; down: w [n_out][ffn]
+ *          (only dtype, n_out, k and w of the descriptors are read)
+ *  y       [device] [t][n_out]
+ *  idx_out [device] [t][ffn/2] the kept positions of the activation, or NULL
+ *  workspace [device] spa_ffn_workspace_bytes(t, ffn, dtype) bytes
+ * Requires a 16-bit dtype (the same for x, both weights and y),
+ * hidden % 64 == 0, ffn % 64 == 0, both <= 2^23, down.k == ffn,
+ * n_out % 8 == 0.  An activation value that ties exactly inside a block
+ * keeps the lower index; because u comes from a float32-accumulating GEMM,
+ * a near-tie can resolve differently from a float64 reference.
+ */
+size_t spa_ffn_workspace_bytes(int32_t t, int32_t ffn, int32_t dtype);
+spa_status sparse_ffn_relu2_prefill(const void* x, int32_t t, const spa_weight* up, const spa_weight* down,
+                                    void* y, uint8_t* idx_out, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* Workspace bytes an entry point needs for these sizes (0 if none); 0 for
  * invalid arguments as well. */
 size_t spa_workspace_bytes(int32_t entry, int32_t t, int32_t k, int32_t n_out, int32_t dtype,

@@ -28,6 +28,28 @@ def f32(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy()
 
 
+def check_ffn_masks(idx_gpu: np.ndarray, act_ref: np.ndarray, idx_ref: np.ndarray, rel_gap: float = 2.0 ** -5):
+    """Masks of an activation the GPU forms from its own float32-accumulated
+    up-projection.  Where the reference activation has a clear boundary in a
+    block (2nd and 3rd largest more than rel_gap apart), the kept positions
+    must match exactly; elsewhere the GPU's choice must be a top-2 of the
+    reference up to that gap.  Returns the fraction of blocks that differ."""
+    t, half = idx_gpu.shape
+    nb = half // 2
+    a = act_ref.reshape(t, nb, 4).astype(np.float64)
+    g = idx_gpu.reshape(t, nb, 2).astype(np.int64)
+    r = idx_ref.reshape(t, nb, 2).astype(np.int64)
+    assert (g >= 0).all() and (g < 4).all() and (g[..., 0] < g[..., 1]).all(), "invalid positions"
+    srt = -np.sort(-a, axis=-1)
+    second, third = srt[..., 1], srt[..., 2]
+    clear = second - third > rel_gap * np.maximum(second, 1e-30)
+    differ = (g != r).any(axis=-1)
+    assert not (differ & clear).any(), "mask differs where the boundary is clear"
+    kept = np.take_along_axis(a, g, axis=-1).min(axis=-1)
+    assert (kept >= third * (1 - rel_gap) - 1e-30).all(), "a kept value is below a dropped one"
+    return float(differ.mean())
+
+
 def oracle_for(spec, x_cpu, w_cpu, f=None, eta_in=None, rows=None):
     """Oracle prune (+ linear when w_cpu is given) for ``spec`` on CPU tensors."""
     x = f32(x_cpu) if rows is None else f32(x_cpu[rows])

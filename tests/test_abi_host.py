@@ -41,7 +41,7 @@ def test_header_declares_the_entry_points():
     for need in ["prepare_weight", "prune_nm", "sparse_linear_decode", "sparse_linear_prefill",
                  "spa_workspace_bytes", "spa_status_str", "spa_meta_row_bytes", "spa_encode_meta",
                  "spa_decode_meta", "prepare_amber", "spa_amber_workspace_bytes", "spa_eta_calibrate",
-                 "spa_eta_table", "spa_eta_lookup"]:
+                 "spa_eta_table", "spa_eta_lookup", "sparse_ffn_relu2_prefill", "spa_ffn_workspace_bytes"]:
         assert need in names, names
 
 

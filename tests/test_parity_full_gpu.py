@@ -180,3 +180,25 @@ def test_max_decode_weight(k):
     y_ref = O.linear(pr, f32(w[torch.as_tensor(cols)]), s=np.zeros(cols.size))
     err = O.rowwise_error(f32(y)[:, cols], y_ref)
     assert err <= O.TOLERANCE["bf16"], err
+
+
+def test_ffn_relu2_full_size():
+    # the squared-ReLU FFN at the relu2 layer's sizes: x [4096, 4096], up
+    # [16384, 4096], down [4096, 16384], bf16; sampled rows and columns
+    from gpu_util import check_ffn_masks
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    dev = torch.device("cuda:0")
+    t, hidden, ffn, n_out = 4096, 4096, 16384, 4096
+    print(f"[full-size ffn] t={t} hidden={hidden} ffn={ffn} n_out={n_out}", flush=True)
+    spec = wl.SPECS["prefill"].with_(t=t, k=hidden, n_out=ffn, n_outliers=0)
+    x, w_up = wl.make_inputs(spec)
+    _, w_dn = wl.make_inputs(spec.with_(k=ffn, n_out=n_out), seed=1)
+    y, idx = spa.sparse_ffn_relu2_prefill(x.to(dev), w_up.to(dev), w_dn.to(dev), want_idx=True)
+    torch.cuda.synchronize()
+    rows = _sample(t, 16, 8)
+    cols = _sample(n_out, 64, 9)
+    pr = O.ffn_relu2(f32(x[torch.as_tensor(rows)]), f32(w_up), f32(w_dn[torch.as_tensor(cols)]), "bf16")
+    frac = check_ffn_masks(idx.cpu().numpy()[rows], O.squared_relu(pr["u"], "bf16"), pr["idx"])
+    assert frac < 0.01, frac
+    err = O.rowwise_error(f32(y)[np.ix_(rows, cols)], pr["y"])
+    assert err <= O.TOLERANCE["bf16"], err

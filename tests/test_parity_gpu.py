@@ -11,7 +11,7 @@ import torch
 
 import workloads as wl
 from oracle import nm_oracle as O
-from gpu_util import TORCH_DT, f32, oracle_for, storage_bits, tensor_bits
+from gpu_util import TORCH_DT, check_ffn_masks, f32, oracle_for, storage_bits, tensor_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +51,43 @@ def test_prepare_weight(name, alpha):
     assert np.array_equal(got.view(np.uint32), f.view(np.uint32)), (np.abs(got - f) / f).max()
     s = O.row_sum(f32(w)).astype(np.float32)
     assert np.array_equal(f32(pw.row_sum), s)
+
+
+# ---------------------------------------------------------------------------
+# squared-ReLU FFN (up-projection epilogue prunes and packs)
+# ---------------------------------------------------------------------------
+FFN_CASES = [("bf16", 200, 512, 1024, 264), ("f16", 77, 320, 320, 136), ("bf16", 300, 256, 640, 520),
+             ("bf16", 1, 64, 64, 8), ("f16", 513, 128, 192, 40)]
+
+
+def _ffn_inputs(dtype, t, hidden, ffn, n_out, seed):
+    spec = wl.SPECS["prefill"].with_(t=t, k=hidden, n_out=ffn, dtype=dtype, n_outliers=0)
+    x, w_up = wl.make_inputs(spec, seed=seed)
+    _, w_dn = wl.make_inputs(spec.with_(k=ffn, n_out=n_out), seed=seed + 1)
+    return x, w_up, w_dn
+
+
+@pytest.mark.parametrize("dtype,t,hidden,ffn,n_out", FFN_CASES)
+def test_ffn_relu2(dtype, t, hidden, ffn, n_out):
+    dev = _dev()
+    x, w_up, w_dn = _ffn_inputs(dtype, t, hidden, ffn, n_out, seed=t)
+    y, idx = spa.sparse_ffn_relu2_prefill(x.to(dev), w_up.to(dev), w_dn.to(dev), want_idx=True)
+    torch.cuda.synchronize()
+    pr = O.ffn_relu2(f32(x), f32(w_up), f32(w_dn), dtype)
+    frac = check_ffn_masks(idx.cpu().numpy(), O.squared_relu(pr["u"], dtype), pr["idx"])
+    assert frac < 0.01, frac
+    err = O.rowwise_error(f32(y), pr["y"])
+    assert err <= O.TOLERANCE[dtype], err
+
+
+def test_ffn_relu2_invalid():
+    dev = _dev()
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(spa.SpaError):       # ffn not a multiple of 64
+        spa.sparse_ffn_relu2_prefill(x, torch.zeros((96, 64), dtype=torch.bfloat16, device=dev),
+                                     torch.zeros((8, 96), dtype=torch.bfloat16, device=dev))
+    with pytest.raises(spa.SpaError):       # float32
+        spa.sparse_ffn_relu2_prefill(x.float(), torch.zeros((64, 64), device=dev), torch.zeros((8, 64), device=dev))
 
 
 # ---------------------------------------------------------------------------
