@@ -165,11 +165,18 @@ _WS_CACHE: dict = {}
 
 
 def workspace(entry: int, t: int, k: int, n_out: int, dtype: torch.dtype, cfg: PruneConfig, device) -> Optional[torch.Tensor]:
-    """A zero-filled workspace of the size the library asks for (cached per device and size)."""
+    """A zero-filled workspace of the size the library asks for.
+
+    Cached per device, entry point, sizes and the configuration fields that
+    shape its layout: a decode workspace keeps split counters that a call
+    leaves at zero for the next call of the same layout, but another layout
+    of the same byte size could find its counters where partial sums were.
+    """
     nbytes = workspace_bytes(entry, t, k, n_out, dtype, cfg)
     if nbytes == 0:
         return None
-    key = (str(device), entry, nbytes)
+    key = (str(device), entry, nbytes, t, k, n_out, DTYPE[dtype], cfg.n, cfg.m, cfg.score, cfg.shift,
+           int(cfg.var_rescale))
     ws = _WS_CACHE.get(key)
     if ws is None:
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)

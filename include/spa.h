@@ -202,7 +202,9 @@ spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const sp
  *  idx_out  [device] [t][k*n/m] or NULL: the in-block positions the layer used
  *  nu_out   [device] [t] or NULL
  *  workspace [device] spa_workspace_bytes(SPA_ENTRY_DECODE, ...) bytes,
- *           zero-filled before its first use; each call leaves it reusable.
+ *           zero-filled before its first use; each call leaves it reusable
+ *           for later calls with the same sizes and configuration (zero it
+ *           again before using it for other sizes).
  * Returns SPA_ERR_UNSUPPORTED for float32 with t > 8, and when the 1..4-token
  * (or float32) path would read a channel-major weight of 2 GiB or more.
  */

@@ -439,6 +439,27 @@ def test_decode_repeat_reuses_workspace():
     assert torch.equal(y1, y2)
 
 
+def test_decode_workspaces_of_equal_size_do_not_mix():
+    # two layouts that need the same number of workspace bytes (13056): the
+    # binding keeps a workspace per layout, so neither call finds the other's
+    # partial sums where its split counters should be zero
+    dev = _dev()
+    a = wl.SPECS["decode"].with_(t=1, k=1024, n_out=520, n=2, m=4, score="magnitude", shift="none", n_outliers=0)
+    b = wl.SPECS["decode"].with_(t=4, k=512, n_out=776, n=2, m=4, score="magnitude", shift="none", n_outliers=0)
+    sizes = {spa.workspace_bytes(1, s.t, s.k, s.n_out, torch.bfloat16, _cfg(s)) for s in (a, b)}
+    assert len(sizes) == 1, sizes
+    runs = []
+    for s in (a, b):
+        x, w = wl.make_inputs(s)
+        runs.append((s, x.to(dev), spa.prepare_weight(w.to(dev), 0.0), oracle_for(s, x, w)))
+    for _ in range(3):
+        for s, xd, pw, pr in runs:
+            y, idx, _ = spa.sparse_linear_decode(xd, pw, _cfg(s), want_idx=True)
+            torch.cuda.synchronize()
+            assert np.array_equal(idx.cpu().numpy(), pr["idx"])
+            assert O.rowwise_error(f32(y), pr["y"]) <= O.TOLERANCE[s.dtype]
+
+
 # ---------------------------------------------------------------------------
 # prefill
 # ---------------------------------------------------------------------------
