@@ -319,7 +319,7 @@ spa_status sparse_ffn_relu2_prefill(const void* x, int32_t t, const spa_weight* 
   if (up->dtype != down->dtype || (up->dtype != SPA_F16 && up->dtype != SPA_BF16)) return SPA_ERR_INVALID;
   const int hidden = up->k, ffn = up->n_out;
   if (hidden < 64 || hidden % 64 || ffn < 64 || ffn % 64 || down->k != ffn) return SPA_ERR_INVALID;
-  if (down->n_out < 8 || down->n_out % 8 || down->n_out > kMaxDim) return SPA_ERR_INVALID;
+  if (down->n_out < 1 || down->n_out > kMaxDim) return SPA_ERR_INVALID;
   if (hidden > kMaxPrefillK || ffn > kMaxPrefillK) return SPA_ERR_UNSUPPORTED;
   if (!up->w || !down->w || !aligned16(up->w) || !aligned16(down->w) || !aligned16(x) || !aligned16(y))
     return SPA_ERR_INVALID;

@@ -220,7 +220,7 @@ spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, c
  * ("Accelerating Transformer training and inference with 2:4 sparsity and
  * Squared-ReLU" s2.1, s3.1); every other n:m runs dense MFMA on the
  * masked activations.
- *  Arguments as for sparse_linear_decode; w->w required, n_out % 8 == 0,
+ *  Arguments as for sparse_linear_decode; w->w required, any n_out >= 1,
  *  k % 64 == 0.  workspace: spa_workspace_bytes(SPA_ENTRY_PREFILL, ...).
  *  SPA_ERR_UNSUPPORTED for k > 2^23 (8388608).
  */
@@ -275,8 +275,7 @@ spa_status spa_decode_meta(const void* codes, int32_t t, int32_t k, int32_t n, i
  *  idx_out [device] [t][ffn/2] the kept positions of the activation, or NULL
  *  workspace [device] spa_ffn_workspace_bytes(t, ffn, dtype) bytes
  * Requires a 16-bit dtype (the same for x, both weights and y),
- * hidden % 64 == 0, ffn % 64 == 0, both <= 2^23, down.k == ffn,
- * n_out % 8 == 0.  An activation value that ties exactly inside a block
+ * hidden % 64 == 0, ffn % 64 == 0, both <= 2^23, down.k == ffn, n_out >= 1.  An activation value that ties exactly inside a block
  * keeps the lower index; because u comes from a float32-accumulating GEMM,
  * a near-tie can resolve differently from a float64 reference.
  */

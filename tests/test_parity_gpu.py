@@ -57,7 +57,7 @@ def test_prepare_weight(name, alpha):
 # squared-ReLU FFN (up-projection epilogue prunes and packs)
 # ---------------------------------------------------------------------------
 FFN_CASES = [("bf16", 200, 512, 1024, 264), ("f16", 77, 320, 320, 136), ("bf16", 300, 256, 640, 520),
-             ("bf16", 1, 64, 64, 8), ("f16", 513, 128, 192, 40)]
+             ("bf16", 1, 64, 64, 8), ("f16", 513, 128, 192, 40), ("bf16", 33, 128, 256, 37)]
 
 
 def _ffn_inputs(dtype, t, hidden, ffn, n_out, seed):
