@@ -72,6 +72,11 @@ design notes as well):
   C(c_i, i)) -- or as an m-bit mask (bit j = position j kept).  Codes are
   laid end to end, block 0 in the lowest bits, least significant bit
   first, in 32-bit words; each row starts on a fresh word.
+* FP8 2:4 prefill ([SqReLU] s3.1: FP8 with row scales; s5.3: sparsify,
+  then quantise): e4m3 in the OCP form (bias 7, largest 448, no infinity),
+  rounded to nearest even; activation rows scaled by 448 / max|x_hat| of the
+  row, weight rows by 448 / max|w| of the row, both float32; y takes the
+  float64 product of the codes times both scales.
 * Packed values are the float32 shifted values rounded to the storage dtype
   (round-to-nearest-even); the index metadata is one uint8 in-block position
   per kept value, ascending.
@@ -487,6 +492,77 @@ def ffn_relu2(x, w_up, w_down, dtype: str) -> dict:
     pr = prune(u, dtype, 2, 4, act="relu2")
     pr["u"] = u
     pr["y"] = linear(pr, w_down, s=np.zeros(np.asarray(w_down).shape[0]))
+    return pr
+
+
+# ----------------------------------------------------------------------------
+# FP8 (e4m3) 2:4 prefill ([SqReLU] s3.1, s5.3)
+# ----------------------------------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP e4m3 byte: sign, 4 exponent bits (bias 7), 3 mantissa bits;
+    exponent 0 is subnormal; 0x7F / 0xFF are NaN; no infinity."""
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    if e == 0:
+        return s * (m / 8.0) * 2.0 ** -6
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """float32 values -> e4m3 codes (uint8), nearest value, ties to the even code.
+
+    |v| is assumed <= 464 (the scaled operands stay within 448 up to one
+    float32 rounding); larger inputs are outside the format."""
+    table = [(e4m3_value(c), c) for c in range(128) if c != 0x7F]   # non-negative values, ascending
+    vals = np.array([t[0] for t in table])
+    codes = np.array([t[1] for t in table], dtype=np.uint8)
+    x = np.asarray(v, dtype=np.float64).ravel()
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, vals.size - 1)
+    lo = np.clip(hi - 1, 0, vals.size - 1)
+    dl, dh = a - vals[lo], vals[hi] - a
+    pick_hi = (dh < dl) | ((dh == dl) & (codes[hi] % 2 == 0) & (hi != lo))
+    c = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
+    c = np.where(a == vals[hi], codes[hi], c).astype(np.uint8)
+    neg = np.signbit(x) & (c != 0)
+    return (c | np.where(neg, 0x80, 0).astype(np.uint8)).reshape(np.shape(v))
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    lut = np.array([e4m3_value(c) for c in range(256)])
+    return lut[np.asarray(codes, dtype=np.int64)]
+
+
+def fp8_rows(v: np.ndarray):
+    """Per-row scale s = float32(max|v| / 448) and codes e4m3(float32(v * float32(448 / max|v|)));
+    a zero row gets s = 0 and zero codes."""
+    v = np.asarray(v, dtype=np.float32)
+    amax = np.abs(v).max(axis=1).astype(np.float32)
+    ok = amax > 0
+    inv = np.where(ok, np.float32(448.0) / np.where(ok, amax, np.float32(1.0)), np.float32(0.0)).astype(np.float32)
+    scale = np.where(ok, amax / np.float32(448.0), np.float32(0.0)).astype(np.float32)
+    return e4m3_round((v * inv[:, None]).astype(np.float32)), scale
+
+
+def prefill_fp8(x, w, dtype: str, score: str = "magnitude", f=None, shift_mode: str = "none", eta_in=None,
+                var_rescale=False, s=None) -> dict:
+    """2:4 prefill with FP8 operands: the mask of ``prune`` (on the 16-bit input),
+    the kept x_hat quantised per token, W quantised per output row;
+    y_ij = nu_i * sx_i * sw_j * sum_k qx_ik qw_jk + eta_i * s_j (float64)."""
+    pr = prune(x, dtype, 2, 4, score=score, f=f, shift_mode=shift_mode, eta_in=eta_in, var_rescale=var_rescale)
+    xs = (pr["xhat"] * pr["keep"]).astype(np.float32)
+    qx, sx = fp8_rows(pr["xhat"])
+    qx = np.where(pr["keep"], qx, 0).astype(np.uint8)
+    qw, sw = fp8_rows(w)
+    if s is None:
+        s = row_sum(w)
+    acc = e4m3_decode(qx) @ e4m3_decode(qw).T
+    y = pr["nu"].astype(np.float64)[:, None] * (sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] * acc)
+    pr.update(qx=qx, sx=sx, qw=qw, sw=sw, xs=xs)
+    pr["y"] = y + pr["eta"].astype(np.float64)[:, None] * np.asarray(s, dtype=np.float64)[None, :]
     return pr
 
 

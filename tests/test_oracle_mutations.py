@@ -127,6 +127,15 @@ def _ema_dense_denominator(xhat, keep, r_in, decay=0.9, gain=0.1, eps=1e-6):   #
     return np.sqrt(r / (num + eps)).astype(np.float32), r.astype(np.float32)
 
 
+def _e4m3_truncate(v):                                   # rounds toward zero
+    table = [(O.e4m3_value(c), c) for c in range(0x7F)]
+    out = []
+    for x in np.asarray(v, np.float64).ravel().tolist():
+        c = max(c for val, c in table if val <= abs(x))
+        out.append(c | (0x80 if x < 0 and c else 0))
+    return np.array(out, np.uint8).reshape(np.shape(v))
+
+
 _orig_factor = O.channel_factor
 _orig_amber = O.amber_factor
 _orig_var = O.var_factor
@@ -152,6 +161,7 @@ MUTANTS = {
     "amber_raw_norm": ("amber_factor", _amber_raw_norm),
     "eta_table_last_value": ("eta_table", _eta_table_last),
     "ema_dense_denominator": ("var_factor_ema", _ema_dense_denominator),
+    "e4m3_truncation": ("e4m3_round", _e4m3_truncate),
     "meta_width_floor": ("meta_width", _width_floor),
 }
 

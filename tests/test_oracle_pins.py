@@ -348,6 +348,56 @@ def test_round_to_dtype_matches_torch(dtype, tdt):
 
 
 # --------------------------------------------------------------------------
+# FP8 (e4m3)
+# --------------------------------------------------------------------------
+
+def test_e4m3_codes_follow_the_format():
+    # the 256 codes from the OCP e4m3 definition, spot values by hand
+    assert O.e4m3_value(0x38) == 1.0 and O.e4m3_value(0x7E) == 448.0 and O.e4m3_value(0x01) == 2.0 ** -9
+    assert O.e4m3_value(0x08) == 2.0 ** -6 and O.e4m3_value(0x07) == 7 * 2.0 ** -9
+    assert math.isnan(O.e4m3_value(0x7F)) and math.isnan(O.e4m3_value(0xFF))
+    vals = [O.e4m3_value(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))                 # codes ordered like values
+    assert all(O.e4m3_value(c | 0x80) == -O.e4m3_value(c) for c in range(0x7F))
+
+
+def test_e4m3_round_is_nearest_even_by_exhaustive_search():
+    rng = np.random.Generator(np.random.PCG64(12))
+    reps = [O.e4m3_value(c) for c in range(0x7F)]
+    mids = [(a + b) / 2 for a, b in zip(reps, reps[1:])]
+    x = np.concatenate([rng.uniform(-460, 460, 3000), rng.standard_normal(500) * 1e-2, reps, mids,
+                        np.negative(mids), [0.0, -0.0, 448.0, 464.0 - 1e-3]]).astype(np.float32)
+    got = O.e4m3_round(x)
+    for xi, ci in zip(x.tolist(), got.tolist()):
+        cand = [(abs(Fraction(O.e4m3_value(c)) - abs(Fraction(xi))), c & 1, c) for c in range(0x7F)]
+        best = min(cand)[2]
+        want = best | (0x80 if xi < 0 and best != 0 else 0)
+        assert ci == want, (xi, hex(ci), hex(want))
+
+
+def test_fp8_rows_scale_and_extremes():
+    v = np.array([[0.5, -2.0, 1.0, 0.0], [0, 0, 0, 0], [3.0, 3.0, -3.0, 1e-3]], dtype=np.float32)
+    q, s = O.fp8_rows(v)
+    assert s[1] == 0 and (q[1] == 0).all()
+    assert O.e4m3_value(int(q[0, 1])) == -448.0 and O.e4m3_value(int(q[2, 0])) == 448.0
+    assert s[0] == np.float32(2.0 / 448.0)
+    # dequantised values within half an e4m3 step (relative 1/16) of the input
+    deq = O.e4m3_decode(q) * s[:, None]
+    big = np.abs(v) > 0.05
+    assert np.all(np.abs(deq[big] - v[big]) <= np.abs(v[big]) / 16 + 1e-12)
+
+
+def test_prefill_fp8_close_to_bf16():
+    # FP8 quantisation error of y against the 16-bit product: a few per cent
+    spec = wl.SPECS["prefill"].with_(t=16, k=512, n_out=64)
+    x, w = wl.make_inputs(spec)
+    pr8 = O.prefill_fp8(_x32(x), _x32(w), "bf16", shift_mode="token_mean")
+    pr = O.prune(_x32(x), "bf16", 2, 4, shift_mode="token_mean")
+    assert np.array_equal(pr8["keep"], pr["keep"])
+    assert O.rowwise_error(pr8["y"], O.linear(pr, _x32(w))) < 0.08
+
+
+# --------------------------------------------------------------------------
 # squared-ReLU FFN
 # --------------------------------------------------------------------------
 
