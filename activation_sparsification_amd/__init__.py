@@ -6,6 +6,7 @@ declared in ``include/spa.h``); this package is its thin Python binding.
 from ._binding import (  # noqa: F401
     EXPORTS,
     EtaCalibration,
+    Fp8Weight,
     PreparedCall,
     PreparedWeight,
     PruneConfig,
@@ -17,9 +18,11 @@ from ._binding import (  # noqa: F401
     meta_row_bytes,
     prepare_amber,
     prepare_weight,
+    prepare_weight_fp8,
     prune_nm,
     sparse_linear_decode,
     sparse_linear_prefill,
+    sparse_linear_prefill_fp8,
     sparse_ffn_relu2_prefill,
     workspace,
     workspace_bytes,

@@ -74,6 +74,11 @@ def lib() -> ctypes.CDLL:
         L.spa_amber_workspace_bytes.argtypes = []
         L.prepare_amber.restype = ctypes.c_int
         L.prepare_amber.argtypes = [vp, i32, i32, i32, ctypes.c_float, vp, vp, sz, vp]
+        L.prepare_weight_fp8.restype = ctypes.c_int
+        L.prepare_weight_fp8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+        L.sparse_linear_prefill_fp8.restype = ctypes.c_int
+        L.sparse_linear_prefill_fp8.argtypes = [vp, i32, ctypes.POINTER(_Weight), vp, vp, ctypes.POINTER(_Cfg), vp,
+                                                vp, vp, vp, vp, sz, vp]
         L.spa_meta_row_bytes.restype = sz
         L.spa_meta_row_bytes.argtypes = [i32, i32, i32, i32]
         for name in ("spa_encode_meta", "spa_decode_meta"):
@@ -93,7 +98,8 @@ def lib() -> ctypes.CDLL:
 EXPORTS = ("prepare_weight", "prune_nm", "sparse_linear_decode", "sparse_linear_prefill",
            "spa_workspace_bytes", "spa_status_str", "spa_meta_row_bytes", "spa_encode_meta", "spa_decode_meta",
            "prepare_amber", "spa_amber_workspace_bytes", "spa_eta_calibrate", "spa_eta_table", "spa_eta_lookup",
-           "sparse_ffn_relu2_prefill", "spa_ffn_workspace_bytes")
+           "sparse_ffn_relu2_prefill", "spa_ffn_workspace_bytes", "prepare_weight_fp8",
+           "sparse_linear_prefill_fp8")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -336,6 +342,43 @@ def sparse_linear_prefill(x, pw: PreparedWeight, cfg: PruneConfig, eta_in=None, 
                           out=None, ws=None):
     """Prune/pack pass + matrix-core GEMM (sparse MFMA for 2:4).  Returns ``(y, idx, nu)``."""
     return _linear("sparse_linear_prefill", ENTRY_PREFILL, x, pw, cfg, eta_in, want_idx, want_nu, out, ws)
+
+
+@dataclasses.dataclass
+class Fp8Weight:
+    """e4m3 codes of a weight, one float32 scale per output row (prepare_weight_fp8)."""
+    codes: torch.Tensor                  # [n_out, k] uint8
+    scale: torch.Tensor                  # [n_out] float32
+
+
+def prepare_weight_fp8(w: torch.Tensor) -> Fp8Weight:
+    """Row-scaled e4m3 copy of a 16-bit weight ``[n_out, k]`` for the FP8 2:4 prefill."""
+    dev = _dev(w)
+    n_out, k = w.shape
+    codes = torch.empty((n_out, k), dtype=torch.uint8, device=dev)
+    scale = torch.empty(n_out, dtype=torch.float32, device=dev)
+    _check(lib().prepare_weight_fp8(_ptr(w), DTYPE[w.dtype], n_out, k, _ptr(codes), _ptr(scale), _stream(dev)),
+           "prepare_weight_fp8")
+    return Fp8Weight(codes, scale)
+
+
+def sparse_linear_prefill_fp8(x, pw: PreparedWeight, w8: Fp8Weight, cfg: PruneConfig, eta_in=None, want_idx=False,
+                              want_nu=False, out=None, ws=None):
+    """2:4 prefill with FP8 operands (pruning pass + FP8 sparse MFMA GEMM).  Returns ``(y, idx, nu)``."""
+    dev = _dev(x)
+    t, k = x.shape
+    y = torch.empty((t, pw.n_out), dtype=x.dtype, device=dev) if out is None else out
+    idx = torch.empty((t, k // cfg.m * cfg.n), dtype=torch.uint8, device=dev) if want_idx else None
+    nu = torch.empty(t, dtype=torch.float32, device=dev) if want_nu else None
+    if ws is None:
+        ws = workspace(ENTRY_PREFILL, t, k, pw.n_out, x.dtype, cfg, dev)
+    c = cfg.c()
+    wd = pw.c()
+    st = lib().sparse_linear_prefill_fp8(_ptr(x), t, ctypes.byref(wd), _ptr(w8.codes), _ptr(w8.scale),
+                                         ctypes.byref(c), _ptr(eta_in), _ptr(y), _ptr(idx), _ptr(nu), _ptr(ws),
+                                         0 if ws is None else ws.numel(), _stream(dev))
+    _check(st, "sparse_linear_prefill_fp8")
+    return y, idx, nu
 
 
 class PreparedCall:

@@ -516,6 +516,181 @@ hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// FP8 2:4 GEMM ("Accelerating Transformer training and inference with 2:4
+// sparsity and Squared-ReLU" s2.1, s3.1: the sparse GEMM on FP8 with row
+// scales).  gfx950's v_smfmac_f32_32x32x64_fp8_fp8 takes a whole 64-channel
+// step per instruction: A lane l holds row l % 32's 16 kept e4m3 codes of
+// logical channels [32g, 32g + 32) (g = l / 32) with two position bits each
+// in one 32-bit word; B lane l holds column l % 32's codes of channels
+// 16g .. 16g + 15 and 32 + 16g .. 32 + 16g + 15; D as for the 16-bit
+// instruction.  Same tile, wave grid and three-stage ring as k_gemm24, at half
+// the bytes: per step and row 32 B of codes + 8 B of positions (activations)
+// and 64 B of codes (weights), so each wave issues four direct loads per step.
+// Rows are stored unswizzled.  y = nu_i * sx_i * sw_j * acc + eta_i * s_j.
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ void __launch_bounds__(512, 1) k_gemm24_fp8(PrefillArgs p) {
+  constexpr int BM = 256, BN = 256;
+  constexpr int WM = 128, WN = 64, FM = 4, FN = 2;
+  constexpr int AST = BM * 40, BST = BN * 64;               // bytes per stage
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  __shared__ __attribute__((aligned(1024))) unsigned char sA[3 * AST];
+  __shared__ __attribute__((aligned(1024))) unsigned char sB[3 * BST];
+  __shared__ float s_nu[BM], s_eta[BM], s_rs[BN], s_sx[BM], s_sw[BN];
+
+  const int K = p.k, N = p.n_out, TP = p.t_pad;
+  int tm, tn;
+  xcd_tile(p.t, N, BM, BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  TileScalars<BM, BN> ts;
+  ts.fetch(p, m0, n0);
+  const float sx_own = (int)threadIdx.x < BM ? p.sx[min(m0 + (int)threadIdx.x, p.t - 1)] : 0.f;
+  const float sw_own = (int)threadIdx.x < BN ? p.sw[min(n0 + (int)threadIdx.x, N - 1)] : 0.f;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int wm0 = (wv >> 2) * WM, wn0 = (wv & 3) * WN;
+
+  const char* baseA = static_cast<const char*>(p.a_vals) + (size_t)m0 * 32;
+  const char* baseM = reinterpret_cast<const char*>(p.a_meta) + (size_t)m0 * 8;
+  const char* baseW = static_cast<const char*>(p.w) + (size_t)n0 * K;
+  const size_t stepA = (size_t)TP * 32, stepM = (size_t)TP * 8;
+  // activation codes: lane l of wave w loads row 32 w + l / 2, half l % 2
+  const uint32_t offA = (uint32_t)((32 * wv + (lane >> 1)) * 32 + (lane & 1) * 16);
+  // weight codes: run h of wave w, lane l: row 32 w + 16 h + l / 4, quarter l % 4
+  uint32_t offB[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 32 * wv + 16 * h + (lane >> 2);
+    const int rr = min(n0 + r, N - 1) - n0;
+    offB[h] = (uint32_t)rr * (uint32_t)K + (uint32_t)((lane & 3) * 16);
+  }
+  const uint32_t offM = (uint32_t)((wv * 64 + lane) * 4);
+  const uint32_t ldsA0 = lds_addr(sA), ldsB0 = lds_addr(sB);
+
+#define SPA_ISSUE8(KT, ST)                                                                   \
+  do {                                                                                       \
+    const char* w_ = baseW + (size_t)(KT) * 64;                                              \
+    lds_dma16(baseA + (size_t)(KT) * stepA, offA, ldsA0 + (ST) * AST + wv * 1024);           \
+    lds_dma16(w_, offB[0], ldsB0 + (ST) * BST + wv * 2048);                                  \
+    lds_dma16(w_, offB[1], ldsB0 + (ST) * BST + wv * 2048 + 1024);                           \
+    lds_dma4(baseM + (size_t)(KT) * stepM, offM, ldsA0 + (ST) * AST + BM * 32 + wv * 256);   \
+  } while (0)
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = K / 64;
+  SPA_ISSUE8(0, 0);
+  if (nk > 1) SPA_ISSUE8(1, 1);
+  int st = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vm<4>(kt + 1 < nk);                     // step kt landed (kt+1 may be in flight)
+    bare_barrier();                              // every wave's copies visible; stage (kt+2)%3 free
+    if (kt + 2 < nk) SPA_ISSUE8(kt + 2, st == 0 ? 2 : st - 1);
+    const unsigned char* a_ = sA + st * AST;
+    const unsigned char* b_ = sB + st * BST;
+    v8i bf[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn0 + 32 * j + l32;
+      const uint4 lo = *reinterpret_cast<const uint4*>(b_ + row * 64 + g * 16);
+      const uint4 hi = *reinterpret_cast<const uint4*>(b_ + row * 64 + (2 + g) * 16);
+      bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm0 + 32 * i + l32;
+      const uint4 av = *reinterpret_cast<const uint4*>(a_ + row * 32 + g * 16);
+      const int ix = *reinterpret_cast<const int*>(a_ + BM * 32 + row * 8 + g * 4);
+      const v4i af = v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(af, bf[j], acc[i][j], ix, 0, 0);
+    }
+    st = st == 2 ? 0 : st + 1;
+  }
+#undef SPA_ISSUE8
+
+  ts.park(s_nu, s_eta, s_rs);
+  if ((int)threadIdx.x < BM) s_sx[threadIdx.x] = sx_own;
+  if ((int)threadIdx.x < BN) s_sw[threadIdx.x] = sw_own;
+  __syncthreads();
+  uint16_t* Y = static_cast<uint16_t*>(p.y);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tr = wm0 + 32 * i + 8 * (r / 4) + 4 * g + (r % 4);
+      const int row = m0 + tr;
+      if (row >= p.t) continue;
+      const float nsx = s_nu[tr] * s_sx[tr], eta = s_eta[tr];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int tc = wn0 + 32 * j + l32;
+        const int col = n0 + tc;
+        if (col < N) Y[(size_t)row * N + col] = (uint16_t)from_f32<DT>(nsx * s_sw[tc] * acc[i][j][r] + eta * s_rs[tc]);
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm_fp8(int dtype, const PrefillArgs& a, hipStream_t st) {
+  if (a.t == 0) return hipSuccess;
+  const int tiles = ((a.t + 255) / 256) * ((a.n_out + 255) / 256);
+  if (dtype == SPA_F16) hipLaunchKernelGGL(k_gemm24_fp8<SPA_F16>, dim3(tiles), dim3(512), 0, st, a);
+  else hipLaunchKernelGGL(k_gemm24_fp8<SPA_BF16>, dim3(tiles), dim3(512), 0, st, a);
+  return hipGetLastError();
+}
+
+// Weight rows to e4m3 codes with one scale per row (max |w| / 448); one
+// workgroup per row, k % 8 == 0.
+template <int DT>
+__global__ void __launch_bounds__(256) k_quant_rows(const uint16_t* __restrict__ w, int k, uint8_t* __restrict__ codes,
+                                                    float* __restrict__ scale) {
+  __shared__ float s_mx[4];
+  const uint16_t* row = w + (size_t)blockIdx.x * k;
+  float mx = 0.f;
+  for (int q = threadIdx.x; q < k / 8; q += 256) {
+    const uint4 u = reinterpret_cast<const uint4*>(row)[q];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, __builtin_fabsf(elem16<DT>(u, e)));
+  }
+  const float amax = block_max(mx, s_mx);
+  float sc, inv;
+  fp8_scales(amax, sc, inv);
+  if (threadIdx.x == 0) scale[blockIdx.x] = sc;
+  uint8_t* out = codes + (size_t)blockIdx.x * k;
+  for (int q = threadIdx.x; q < k / 8; q += 256) {
+    const uint4 u = reinterpret_cast<const uint4*>(row)[q];
+    const uint32_t lo = fp8_pair(elem16<DT>(u, 0) * inv, elem16<DT>(u, 1) * inv) |
+                        (fp8_pair(elem16<DT>(u, 2) * inv, elem16<DT>(u, 3) * inv) << 16);
+    const uint32_t hi = fp8_pair(elem16<DT>(u, 4) * inv, elem16<DT>(u, 5) * inv) |
+                        (fp8_pair(elem16<DT>(u, 6) * inv, elem16<DT>(u, 7) * inv) << 16);
+    reinterpret_cast<uint2*>(out)[q] = make_uint2(lo, hi);
+  }
+}
+
+hipError_t launch_quant_rows(int dtype, const void* w, int n_out, int k, uint8_t* codes, float* scale,
+                             hipStream_t st) {
+  if (n_out == 0) return hipSuccess;
+  if (dtype == SPA_F16)
+    hipLaunchKernelGGL(k_quant_rows<SPA_F16>, dim3(n_out), dim3(256), 0, st, static_cast<const uint16_t*>(w), k, codes,
+                       scale);
+  else
+    hipLaunchKernelGGL(k_quant_rows<SPA_BF16>, dim3(n_out), dim3(256), 0, st, static_cast<const uint16_t*>(w), k,
+                       codes, scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn_up(int dtype, const PrefillArgs& a, hipStream_t st) {
   if (a.t == 0) return hipSuccess;
   const int tiles = ((a.t + 255) / 256) * ((a.n_out + 127) / 128);

@@ -147,6 +147,32 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
   if (threadIdx.x == 0) {
     if (a.eta_out) a.eta_out[row] = eta;
   }
+  // FP8 packing: the token's scale from max |x - eta| over the row (the
+  // registers of the one-pass case, else a second read of the row)
+  float fp8_inv = 0.f;
+  if (a.fp8) {
+    float mx = 0.f;
+    if (iters == 1) {
+      if ((int)threadIdx.x < nseg) {
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) mx = fmaxf(mx, __builtin_fabsf(xv0[j] - eta));
+      }
+    } else {
+      for (int sg = threadIdx.x; sg < nseg; sg += 256) {
+        RawSeg<DT, SEG> r2;
+        load_raw<DT, SEG>(xrs, sg, true, r2);
+        float v2[SEG];
+        unpack_raw<DT, SEG>(r2, a.act, v2);
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) mx = fmaxf(mx, __builtin_fabsf(v2[j] - eta));
+      }
+    }
+    __shared__ float s_mx[4];
+    const float amax = block_max(mx, s_mx);
+    float scale;
+    fp8_scales(amax, scale, fp8_inv);
+    if (threadIdx.x == 0) a.fp8_scale[row] = scale;
+  }
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -212,6 +238,7 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
         if constexpr (M == 4 && DT != SPA_F32) {
           uint32_t meta = 0;
           uint32_t wds[4];
+          float flo[4], fhi[4];
 #pragma unroll
           for (int b = 0; b < BPS; ++b) {
             const uint32_t kb = keepbits[b];
@@ -224,11 +251,23 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
               vlo = (int)lo == j ? xh[4 * b + j] : vlo;
               vhi = (int)hi == j ? xh[4 * b + j] : vhi;
             }
+            flo[b] = vlo;
+            fhi[b] = vhi;
             wds[b] = (uint32_t)from_f32<DT>(vlo) | ((uint32_t)from_f32<DT>(vhi) << 16);
           }
           const size_t rowpos = (size_t)(seg / 4) * a.t_pad + row;
-          reinterpret_cast<uint4*>(static_cast<T*>(a.tiled_vals) + rowpos * 32)[seg % 4] =
-              make_uint4(wds[0], wds[1], wds[2], wds[3]);
+          if (a.fp8) {
+            // the eight kept values as e4m3 codes of x_hat * (448 / max), in
+            // channel order: 8 bytes at slot seg % 4 of the row's 32 bytes
+            const uint32_t q01 = fp8_pair(flo[0] * fp8_inv, fhi[0] * fp8_inv) |
+                                 (fp8_pair(flo[1] * fp8_inv, fhi[1] * fp8_inv) << 16);
+            const uint32_t q23 = fp8_pair(flo[2] * fp8_inv, fhi[2] * fp8_inv) |
+                                 (fp8_pair(flo[3] * fp8_inv, fhi[3] * fp8_inv) << 16);
+            reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.tiled_vals) + rowpos * 32)[seg % 4] = make_uint2(q01, q23);
+          } else {
+            reinterpret_cast<uint4*>(static_cast<T*>(a.tiled_vals) + rowpos * 32)[seg % 4] =
+                make_uint4(wds[0], wds[1], wds[2], wds[3]);
+          }
           a.tiled_meta[rowpos * 4 + seg % 4] = (uint16_t)meta;
         }
       }

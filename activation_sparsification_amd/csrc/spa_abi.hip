@@ -42,7 +42,7 @@ size_t prune_ws(int t, int k, const spa_prune_cfg* c) {
 
 // ---- prefill workspace ----
 struct PrefillPlan {
-  size_t vals, meta, eta, nu, colnorm, bytes;
+  size_t vals, meta, eta, nu, colnorm, sx, bytes;
 };
 // Rows of the 2:4 tiled operand are padded to the GEMM's 256-token tile.
 int tiled_rows(int t) { return (t + 255) / 256 * 256; }
@@ -57,6 +57,7 @@ PrefillPlan prefill_plan(int t, int k, int dtype, const spa_prune_cfg* c) {
   p.eta = off; off += round256((size_t)t * 4);
   p.nu = off; off += round256((size_t)t * 4);
   p.colnorm = off; off += c->score == SPA_SCORE_CLACT ? round256((size_t)k * 4) : 0;
+  p.sx = off; off += s24 ? round256((size_t)t * 4) : 0;    // FP8 path: per-token scales
   p.bytes = off;
   return p;
 }
@@ -92,6 +93,84 @@ bool valid_meta(int64_t k, int32_t n, int32_t m, int32_t format) {
   if (n < 1 || n > m) return false;
   if (k < m || k > kMaxDim || k % m) return false;
   return format == SPA_META_BITMAP || format == SPA_META_COMB;
+}
+
+// The prefill path; with w8 (FP8 codes of W, one scale per row) the 2:4
+// operand is packed as e4m3 codes and the FP8 GEMM runs.
+static spa_status prefill_common(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
+                                 const float* eta_in, void* y, uint8_t* idx_out, float* nu_out, void* workspace,
+                                 size_t workspace_bytes, void* stream, const uint8_t* w8, const float* w8_scale) {
+  if (w->dtype == SPA_F32) return SPA_ERR_UNSUPPORTED;
+  // the GEMMs address a 256-row weight tile with 32-bit offsets: 255 * k * 2 B < 4 GiB
+  if (w->k > kMaxPrefillK) return SPA_ERR_UNSUPPORTED;
+  if (t == 0) return SPA_OK;
+  const int k = w->k;
+  const PrefillPlan pl = prefill_plan(t, k, w->dtype, cfg);
+  if (!workspace || workspace_bytes < pl.bytes || !aligned16(workspace)) return SPA_ERR_INVALID;
+  char* base = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool s24 = cfg->n == 2 && cfg->m == 4;
+  float* eta_ws = reinterpret_cast<float*>(base + pl.eta);
+  float* nu_ptr = nu_out ? nu_out : reinterpret_cast<float*>(base + pl.nu);
+
+  spa::PruneArgs a{};
+  a.x = x; a.t = t; a.k = k; a.n = cfg->n; a.m = cfg->m;
+  a.var = cfg->var_rescale;
+  a.var_in = cfg->var_state;
+  a.var_out = cfg->var_state_out;
+  a.act = cfg->act;
+  a.chan_scale = cfg->score == SPA_SCORE_WEIGHT ? w->chan_scale : nullptr;
+  a.eta_given = cfg->shift == SPA_SHIFT_GIVEN ? eta_in : nullptr;
+  a.shift_mean = cfg->shift == SPA_SHIFT_TOKEN_MEAN;
+  if (cfg->score == SPA_SCORE_CLACT) {
+    float* colnorm = reinterpret_cast<float*>(base + pl.colnorm);
+    if (cfg->shift == SPA_SHIFT_TOKEN_MEAN) {
+      if (hipError_t e = spa::launch_token_mean(w->dtype, x, t, k, cfg->act, eta_ws, st)) return hip_status(e);
+      a.eta_given = eta_ws;
+      a.shift_mean = 0;
+    }
+    if (hipError_t e = spa::launch_colnorm(w->dtype, x, cfg->act, a.eta_given, t, k, colnorm, st)) return hip_status(e);
+    a.colnorm = colnorm;
+  }
+  a.eta_out = eta_ws;
+  a.nu_out = (cfg->var_rescale || nu_out) ? nu_ptr : nullptr;
+  if (s24) {
+    a.pack = spa::kPackTiled24 | (idx_out ? spa::kPackVals : 0);
+    a.tiled_vals = base + pl.vals;
+    a.tiled_meta = reinterpret_cast<uint16_t*>(base + pl.meta);
+    a.t_pad = tiled_rows(t);
+    a.vals = nullptr;
+    a.idx = idx_out;
+    if (w8) {
+      a.fp8 = 1;
+      a.fp8_scale = reinterpret_cast<float*>(base + pl.sx);
+    }
+  } else {
+    a.pack = spa::kPackDense | (idx_out ? spa::kPackVals : 0);
+    a.dense = base + pl.vals;
+    a.vals = nullptr;
+    a.idx = idx_out;
+  }
+  if (hipError_t e = spa::launch_prune(w->dtype, a, st)) return hip_status(e);
+
+  spa::PrefillArgs g{};
+  g.w = w->w;
+  g.row_sum = w->row_sum;
+  g.a_vals = base + pl.vals;
+  g.a_meta = s24 ? reinterpret_cast<const uint16_t*>(base + pl.meta) : nullptr;
+  g.t_pad = s24 ? tiled_rows(t) : t;
+  g.eta = cfg->shift != SPA_SHIFT_NONE ? eta_ws : nullptr;
+  g.nu = cfg->var_rescale ? nu_ptr : nullptr;
+  g.y = y;
+  g.t = t; g.k = k; g.n_out = w->n_out;
+  g.sparse24 = s24 ? 1 : 0;
+  if (w8) {
+    g.w = w8;
+    g.sx = reinterpret_cast<const float*>(base + pl.sx);
+    g.sw = w8_scale;
+    return hip_status(spa::launch_gemm_fp8(w->dtype, g, st));
+  }
+  return hip_status(spa::launch_gemm(w->dtype, g, st));
 }
 
 }  // namespace
@@ -216,67 +295,30 @@ spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, 
                                  const float* eta_in, void* y, uint8_t* idx_out, float* nu_out, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   if (spa_status s = check_linear(x, t, w, cfg, eta_in, y, false)) return s;
-  if (w->dtype == SPA_F32) return SPA_ERR_UNSUPPORTED;
-  // the GEMMs address a 256-row weight tile with 32-bit offsets: 255 * k * 2 B < 4 GiB
-  if (w->k > kMaxPrefillK) return SPA_ERR_UNSUPPORTED;
-  if (t == 0) return SPA_OK;
-  const int k = w->k;
-  const PrefillPlan pl = prefill_plan(t, k, w->dtype, cfg);
-  if (!workspace || workspace_bytes < pl.bytes || !aligned16(workspace)) return SPA_ERR_INVALID;
-  char* base = static_cast<char*>(workspace);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool s24 = cfg->n == 2 && cfg->m == 4;
-  float* eta_ws = reinterpret_cast<float*>(base + pl.eta);
-  float* nu_ptr = nu_out ? nu_out : reinterpret_cast<float*>(base + pl.nu);
+  return prefill_common(x, t, w, cfg, eta_in, y, idx_out, nu_out, workspace, workspace_bytes, stream, nullptr,
+                        nullptr);
+}
 
-  spa::PruneArgs a{};
-  a.x = x; a.t = t; a.k = k; a.n = cfg->n; a.m = cfg->m;
-  a.var = cfg->var_rescale;
-  a.var_in = cfg->var_state;
-  a.var_out = cfg->var_state_out;
-  a.act = cfg->act;
-  a.chan_scale = cfg->score == SPA_SCORE_WEIGHT ? w->chan_scale : nullptr;
-  a.eta_given = cfg->shift == SPA_SHIFT_GIVEN ? eta_in : nullptr;
-  a.shift_mean = cfg->shift == SPA_SHIFT_TOKEN_MEAN;
-  if (cfg->score == SPA_SCORE_CLACT) {
-    float* colnorm = reinterpret_cast<float*>(base + pl.colnorm);
-    if (cfg->shift == SPA_SHIFT_TOKEN_MEAN) {
-      if (hipError_t e = spa::launch_token_mean(w->dtype, x, t, k, cfg->act, eta_ws, st)) return hip_status(e);
-      a.eta_given = eta_ws;
-      a.shift_mean = 0;
-    }
-    if (hipError_t e = spa::launch_colnorm(w->dtype, x, cfg->act, a.eta_given, t, k, colnorm, st)) return hip_status(e);
-    a.colnorm = colnorm;
-  }
-  a.eta_out = eta_ws;
-  a.nu_out = (cfg->var_rescale || nu_out) ? nu_ptr : nullptr;
-  if (s24) {
-    a.pack = spa::kPackTiled24 | (idx_out ? spa::kPackVals : 0);
-    a.tiled_vals = base + pl.vals;
-    a.tiled_meta = reinterpret_cast<uint16_t*>(base + pl.meta);
-    a.t_pad = tiled_rows(t);
-    a.vals = nullptr;
-    a.idx = idx_out;
-  } else {
-    a.pack = spa::kPackDense | (idx_out ? spa::kPackVals : 0);
-    a.dense = base + pl.vals;
-    a.vals = nullptr;
-    a.idx = idx_out;
-  }
-  if (hipError_t e = spa::launch_prune(w->dtype, a, st)) return hip_status(e);
+spa_status prepare_weight_fp8(const void* w, int32_t dtype, int32_t n_out, int32_t k, uint8_t* codes_out,
+                              float* scale_out, void* stream) {
+  if (!w || !codes_out || !scale_out || (dtype != SPA_F16 && dtype != SPA_BF16)) return SPA_ERR_INVALID;
+  if (n_out < 1 || n_out > kMaxDim || k < 8 || k > kMaxDim || k % 8) return SPA_ERR_INVALID;
+  if (!aligned16(w) || !aligned16(codes_out)) return SPA_ERR_INVALID;
+  return hip_status(spa::launch_quant_rows(dtype, w, n_out, k, codes_out, scale_out, static_cast<hipStream_t>(stream)));
+}
 
-  spa::PrefillArgs g{};
-  g.w = w->w;
-  g.row_sum = w->row_sum;
-  g.a_vals = base + pl.vals;
-  g.a_meta = s24 ? reinterpret_cast<const uint16_t*>(base + pl.meta) : nullptr;
-  g.t_pad = s24 ? tiled_rows(t) : t;
-  g.eta = cfg->shift != SPA_SHIFT_NONE ? eta_ws : nullptr;
-  g.nu = cfg->var_rescale ? nu_ptr : nullptr;
-  g.y = y;
-  g.t = t; g.k = k; g.n_out = w->n_out;
-  g.sparse24 = s24 ? 1 : 0;
-  return hip_status(spa::launch_gemm(w->dtype, g, st));
+spa_status sparse_linear_prefill_fp8(const void* x, int32_t t, const spa_weight* w, const uint8_t* w_codes,
+                                     const float* w_scale, const spa_prune_cfg* cfg, const float* eta_in, void* y,
+                                     uint8_t* idx_out, float* nu_out, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  // check_linear wants the 16-bit weight pointer, which this path does not read
+  if (!w || !w_codes || !w_scale || !aligned16(w_codes)) return SPA_ERR_INVALID;
+  spa_weight wd = *w;
+  wd.w = w_codes;
+  if (spa_status s = check_linear(x, t, &wd, cfg, eta_in, y, false)) return s;
+  if (cfg->n != 2 || cfg->m != 4) return SPA_ERR_UNSUPPORTED;
+  return prefill_common(x, t, &wd, cfg, eta_in, y, idx_out, nu_out, workspace, workspace_bytes, stream, w_codes,
+                        w_scale);
 }
 
 spa_status spa_eta_calibrate(const void* x, int32_t dtype, int32_t t, int32_t k, const int32_t* token_ids,

@@ -56,6 +56,18 @@ __device__ __forceinline__ float relu2(float v) {
 template <int DT>
 __device__ __forceinline__ float apply_act(float v, int act) { return act ? relu2<DT>(v) : v; }
 
+// FP8 (OCP e4m3) codes of two float32 values, rounded to nearest even (the
+// gfx950 conversion; values beyond 464 in magnitude are outside the format).
+__device__ __forceinline__ uint32_t fp8_pair(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+// Per-row FP8 scaling: scale = max / 448 and its inverse 448 / max, both
+// correctly rounded float32 divisions; a zero row gets 0 for both.
+__device__ __forceinline__ void fp8_scales(float amax, float& scale, float& inv) {
+  scale = amax > 0.f ? __fdiv_rn(amax, 448.f) : 0.f;
+  inv = amax > 0.f ? __fdiv_rn(448.f, amax) : 0.f;
+}
+
 // Element e (0..7) of a 16-byte vector of 16-bit values.
 template <int DT> __device__ __forceinline__ float elem16(const uint4& v, int e) {
   uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
@@ -251,6 +263,17 @@ __device__ __forceinline__ double wave_sum_dpp(double v) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Maximum of one float per thread (blockDim.x == 256), identical on every thread.
+__device__ __forceinline__ float block_max(float v, float* s_tmp /*[4]*/) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) s_tmp[w] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(s_tmp[0], s_tmp[1]), fmaxf(s_tmp[2], s_tmp[3]));
 }
 
 // Sum of one double per thread, identical on every thread.  Fixed order:

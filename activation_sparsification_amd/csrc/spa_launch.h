@@ -36,6 +36,8 @@ struct PruneArgs {
   void* tiled_vals;          // kPackTiled24
   uint16_t* tiled_meta;      // kPackTiled24
   int t_pad;                 // kPackTiled24: rows per step (t rounded up to the GEMM tile)
+  int fp8;                   // kPackTiled24: kept values as e4m3 codes (32 bytes per row and step)
+  float* fp8_scale;          // fp8: per-token scale max|x_hat| / 448, [t]
   void* dense;               // kPackDense
   float* eta_out;            // may be NULL
   float* nu_out;             // may be NULL
@@ -112,8 +114,15 @@ struct PrefillArgs {
   uint16_t* out_meta;        // [n_out/64][out_t_pad][4]
   int out_t_pad;
   uint8_t* out_idx;          // [t][n_out/2] in-block positions, or NULL
+  // FP8 2:4 GEMM (launch_gemm_fp8): a_vals holds e4m3 codes, w is [n_out][k]
+  // e4m3 codes; y = sx[i] * sw[j] * acc (* nu) + eta * row_sum
+  const float* sx;           // [t]
+  const float* sw;           // [n_out]
 };
 hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st);
 hipError_t launch_ffn_up(int dtype, const PrefillArgs& a, hipStream_t st);
+hipError_t launch_gemm_fp8(int dtype, const PrefillArgs& a, hipStream_t st);
+hipError_t launch_quant_rows(int dtype, const void* w, int n_out, int k, uint8_t* codes, float* scale,
+                             hipStream_t st);
 
 }  // namespace spa

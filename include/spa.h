@@ -229,6 +229,45 @@ spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, 
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * prepare_weight_fp8 -- FP8 copy of a weight for sparse_linear_prefill_fp8:
+ * each row j of w ([n_out][k], 16-bit) becomes e4m3 codes (OCP FP8, 4
+ * exponent and 3 mantissa bits, largest finite 448) of w[j][c] * (448 /
+ * max_c |w[j][c]|), rounded to nearest even, with scale_out[j] = max |w[j]| /
+ * 448 (0 and all-zero codes for an all-zero row).  One scale per row is the
+ * granularity of the FP8 2:4 GEMM in "Accelerating Transformer training and
+ * inference with 2:4 sparsity and Squared-ReLU" (s2.1, s3.1).
+ *  w          [device] [n_out][k], SPA_F16 or SPA_BF16, 16-byte aligned
+ *  codes_out  [device] [n_out][k] bytes, 16-byte aligned
+ *  scale_out  [device] [n_out] float32
+ * Requires k % 8 == 0.  Run once per layer, off the hot path.
+ */
+spa_status prepare_weight_fp8(const void* w, int32_t dtype, int32_t n_out, int32_t k, uint8_t* codes_out,
+                              float* scale_out, void* stream);
+
+/*
+ * sparse_linear_prefill_fp8 -- sparse_linear_prefill for 2:4 with both
+ * operands in FP8 (the same paper, s2.1 and s3.1: the 2:4 product on FP8
+ * tensors with per-row scales).  The pruning pass selects exactly as in
+ * sparse_linear_prefill (idx_out, nu_out and the eta it uses are the same),
+ * then stores each token's kept x - eta as e4m3 codes of (x - eta) * (448 /
+ * a_i), a_i = max_c |x[i][c] - eta_i| over the whole row, with scale
+ * sx_i = a_i / 448; the GEMM on v_smfmac_f32_32x32x64_fp8_fp8 accumulates
+ * the code products in float32 and writes
+ *   y[i][j] = nu_i * sx_i * sw_j * acc[i][j] + eta_i * row_sum[j].
+ *  w        descriptor of the 16-bit weight: dtype, n_out, k, row_sum and
+ *           chan_scale as for sparse_linear_prefill (w->w is not read)
+ *  w_codes  [device] [n_out][k] from prepare_weight_fp8, 16-byte aligned
+ *  w_scale  [device] [n_out] from prepare_weight_fp8
+ *  Other arguments as for sparse_linear_prefill, same workspace size
+ *  (spa_workspace_bytes(SPA_ENTRY_PREFILL, ...)).  SPA_ERR_UNSUPPORTED
+ *  unless cfg is 2:4, and for k > 2^23.
+ */
+spa_status sparse_linear_prefill_fp8(const void* x, int32_t t, const spa_weight* w, const uint8_t* w_codes,
+                                     const float* w_scale, const spa_prune_cfg* cfg, const float* eta_in, void* y,
+                                     uint8_t* idx_out, float* nu_out, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/*
  * Compact block metadata -- the in-block positions that prune_nm and the
  * linear calls return (uint8, ascending, n per m-block) to and from packed
  * per-block codes, for storing pruned activations (e.g. in a cache).

@@ -139,3 +139,27 @@ def test_linear_rejections_happen_before_any_launch(lib):
     assert L.prune_nm(16, 2, 4, 64, ctypes.byref(bad), None, None, 32, None, None, None, None, 0, None) == 1
     assert L.prune_nm(None, 2, 4, 64, ctypes.byref(good), None, None, 32, None, None, None, None, 0, None) == 1
     assert L.prune_nm(None, 2, 0, 64, ctypes.byref(good), None, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_fp8_rejections_happen_before_any_launch(lib):
+    import activation_sparsification_amd._binding as B
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.prepare_weight_fp8.restype = ctypes.c_int
+    lib.prepare_weight_fp8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    f = lib.sparse_linear_prefill_fp8
+    f.restype = ctypes.c_int
+    f.argtypes = [vp, i32, ctypes.POINTER(B._Weight), vp, vp, ctypes.POINTER(B._Cfg), vp, vp, vp, vp, vp, sz, vp]
+    assert lib.prepare_weight_fp8(256, 0, 8, 64, 512, 768, None) == SPA_ERR_INVALID   # float32 weight
+    assert lib.prepare_weight_fp8(256, 2, 8, 60, 512, 768, None) == SPA_ERR_INVALID   # k % 8 != 0
+    assert lib.prepare_weight_fp8(256, 2, 8, 64, None, 768, None) == SPA_ERR_INVALID  # no codes buffer
+    wd = B._Weight(2, 256, 4096, None, None, None, 1280)
+    c24 = B.PruneConfig(2, 4, shift="token_mean").c()
+    c48 = B.PruneConfig(4, 8, shift="token_mean").c()
+    args = (None, 768, None, None, 1024, 1 << 40, None)
+    assert f(512, 4, ctypes.byref(wd), 2048, 2304, ctypes.byref(c48), *args) == 2     # only 2:4
+    assert f(512, 4, ctypes.byref(wd), None, 2304, ctypes.byref(c24), *args) == SPA_ERR_INVALID
+    assert f(512, 4, ctypes.byref(wd), 2048, None, ctypes.byref(c24), *args) == SPA_ERR_INVALID
+    assert f(512, 4, ctypes.byref(wd), 2056, 2304, ctypes.byref(c24), *args) == SPA_ERR_INVALID  # unaligned
+    big = B._Weight(2, 256, (1 << 23) + 64, None, None, None, 1280)
+    assert f(512, 4, ctypes.byref(big), 2048, 2304, ctypes.byref(c24), *args) == 2
+    assert f(512, 0, ctypes.byref(wd), 2048, 2304, ctypes.byref(c24), *args) == SPA_OK   # no tokens

@@ -1,0 +1,126 @@
+"""GPU parity of the FP8 2:4 prefill against the oracle.
+
+prepare_weight_fp8: codes and row scales bit for bit.  The pruned prefill
+with FP8 operands: in-block positions bit for bit, nu within 1e-6, y within
+the 16-bit tolerance of the oracle's FP8 product (the same e4m3 codes and
+scales, summed in float64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import nm_oracle as O
+from gpu_util import f32
+
+pytestmark = pytest.mark.gpu
+
+spa = pytest.importorskip("activation_sparsification_amd")
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    return torch.device("cuda:0")
+
+
+def _cfg(spec):
+    return spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, spec.var_rescale, spec.act)
+
+
+@pytest.mark.parametrize("dtype,n_out,k", [("bf16", 300, 320), ("f16", 37, 64), ("bf16", 8, 1032)])
+def test_prepare_weight_fp8(dtype, n_out, k):
+    dev = _dev()
+    spec = wl.SPECS["prefill"].with_(t=4, k=k, n_out=n_out, dtype=dtype, n_outliers=0)
+    _, w = wl.make_inputs(spec)
+    w[3] = 0                                                     # an all-zero row: scale 0, codes 0
+    w[5, 7] = 30.0                                               # one large entry sets its row's scale
+    print(f"[fp8 weight] {dtype} n_out={n_out} k={k}", flush=True)
+    w8 = spa.prepare_weight_fp8(w.to(dev))
+    torch.cuda.synchronize()
+    q, s = O.fp8_rows(f32(w))
+    assert np.array_equal(w8.codes.cpu().numpy(), q), "e4m3 codes differ"
+    assert np.array_equal(f32(w8.scale).view(np.uint32), s.view(np.uint32)), "row scales differ"
+
+
+FP8_CASES = [
+    wl.SPECS["prefill"].with_(name="fp8_small", t=200, k=512, n_out=520, n_outliers=5),
+    wl.SPECS["prefill"].with_(name="fp8_f16", t=77, k=320, n_out=300, dtype="f16", n_outliers=3),
+    wl.SPECS["prefill"].with_(name="fp8_k64", t=5, k=64, n_out=40),
+    wl.SPECS["prefill"].with_(name="fp8_k192", t=260, k=192, n_out=300),
+    wl.SPECS["prefill"].with_(name="fp8_tiles", t=600, k=768, n_out=1100, n_outliers=8),
+    wl.SPECS["prefill"].with_(name="fp8_one_row", t=1, k=128, n_out=8),
+    wl.SPECS["prefill"].with_(name="fp8_weight_var", t=300, k=512, n_out=272, score="weight", alpha=0.5,
+                              var_rescale=True),
+    wl.SPECS["prefill"].with_(name="fp8_given", t=40, k=256, n_out=520, shift="given"),
+    wl.SPECS["prefill"].with_(name="fp8_none", t=64, k=256, n_out=264, shift="none"),
+    wl.SPECS["batched"].with_(name="fp8_clact", t=96, k=512, n_out=264, n=2, m=4),
+    wl.SPECS["relu2_fused"].with_(name="fp8_relu2", t=136, k=1024, n_out=264),
+]
+
+
+def _fp8_oracle(spec, x, w, f=None, eta_in=None):
+    if spec.score == "weight" and f is None:
+        f = O.channel_factor(f32(w), spec.alpha)
+    return O.prefill_fp8(f32(x), f32(w), spec.dtype, score=spec.score, f=f, shift_mode=spec.shift,
+                         eta_in=None if eta_in is None else f32(eta_in), var_rescale=spec.var_rescale, act=spec.act)
+
+
+@pytest.mark.parametrize("spec", FP8_CASES, ids=[s.name for s in FP8_CASES])
+def test_prefill_fp8_parity(spec):
+    dev = _dev()
+    x, w = wl.make_inputs(spec)
+    if spec.shift == "token_mean" and spec.t > 2:
+        x[1] = x[1, 0]                                           # a constant row: x - eta == 0, scale 0
+    eta_in = wl.make_eta(spec.t, 9) if spec.shift == "given" else None
+    print(f"[fp8 prefill] {spec.name}: t={spec.t} k={spec.k} n_out={spec.n_out} {spec.score} {spec.shift}",
+          flush=True)
+    wd = w.to(dev)
+    pw = spa.prepare_weight(wd, spec.alpha, want_wt=False)
+    w8 = spa.prepare_weight_fp8(wd)
+    f = f32(pw.chan_scale) if spec.score == "weight" else None
+    pr = _fp8_oracle(spec, x, w, f=f, eta_in=eta_in)
+    y, idx, nu = spa.sparse_linear_prefill_fp8(x.to(dev), pw, w8, _cfg(spec),
+                                               eta_in=None if eta_in is None else eta_in.to(dev), want_idx=True,
+                                               want_nu=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), pr["idx"]), "FP8 prefill masks differ"
+    assert np.allclose(f32(nu), pr["nu"], rtol=1e-6, atol=0)
+    err = O.rowwise_error(f32(y), pr["y"])
+    assert err <= O.TOLERANCE[spec.dtype], err
+
+
+def test_prefill_fp8_rejections():
+    dev = _dev()
+    spec = wl.SPECS["prefill"].with_(t=8, k=256, n_out=64)
+    x, w = wl.make_inputs(spec)
+    wd = w.to(dev)
+    pw = spa.prepare_weight(wd, 0.0, want_wt=False)
+    w8 = spa.prepare_weight_fp8(wd)
+    with pytest.raises(spa.SpaError) as e:                       # only 2:4 runs on the FP8 path
+        spa.sparse_linear_prefill_fp8(x.to(dev), pw, w8, spa.PruneConfig(4, 8, shift="token_mean"))
+    assert e.value.status == 2
+
+
+def test_prefill_fp8_full_size_sampled():
+    # the prompt workload (2048 tokens, 4096 -> 14336) on sampled rows and columns
+    dev = _dev()
+    spec = wl.SPECS["prefill"]
+    print(f"[fp8 full size] t={spec.t} k={spec.k} n_out={spec.n_out}", flush=True)
+    x, w = wl.make_inputs(spec)
+    wd = w.to(dev)
+    pw = spa.prepare_weight(wd, spec.alpha, want_wt=False)
+    w8 = spa.prepare_weight_fp8(wd)
+    y, idx, nu = spa.sparse_linear_prefill_fp8(x.to(dev), pw, w8, _cfg(spec), want_idx=True, want_nu=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([rng.choice(spec.t, 24, replace=False), [0, spec.t - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(spec.n_out, 96, replace=False), [0, spec.n_out - 1]]))
+    xs, ws = x[torch.as_tensor(rows)], w[torch.as_tensor(cols)]
+    pr = _fp8_oracle(spec, xs, ws)
+    assert np.array_equal(idx.cpu().numpy()[rows], pr["idx"])
+    assert np.allclose(f32(nu)[rows], pr["nu"], rtol=1e-6, atol=0)
+    q, s = O.fp8_rows(f32(ws))
+    assert np.array_equal(w8.codes.cpu().numpy()[cols], q)
+    assert np.array_equal(f32(w8.scale)[cols].view(np.uint32), s.view(np.uint32))
+    err = O.rowwise_error(f32(y)[np.ix_(rows, cols)], pr["y"])
+    assert err <= O.TOLERANCE[spec.dtype], err
