@@ -527,7 +527,9 @@ hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st) {
 // instruction.  Same tile, wave grid and three-stage ring as k_gemm24, at half
 // the bytes: per step and row 32 B of codes + 8 B of positions (activations)
 // and 64 B of codes (weights), so each wave issues four direct loads per step.
-// Rows are stored unswizzled.  y = nu_i * sx_i * sw_j * acc + eta_i * s_j.
+// The 16-byte chunks are XOR-swizzled against bank conflicts: chunk c of
+// activation row r sits at c ^ ((r >> 3) & 1), of weight row r at
+// c ^ ((r >> 2) & 3).  y = nu_i * sx_i * sw_j * acc + eta_i * s_j.
 // ---------------------------------------------------------------------------
 template <int DT>
 __global__ void __launch_bounds__(512, 1) k_gemm24_fp8(PrefillArgs p) {
@@ -558,15 +560,16 @@ __global__ void __launch_bounds__(512, 1) k_gemm24_fp8(PrefillArgs p) {
   const char* baseM = reinterpret_cast<const char*>(p.a_meta) + (size_t)m0 * 8;
   const char* baseW = static_cast<const char*>(p.w) + (size_t)n0 * K;
   const size_t stepA = (size_t)TP * 32, stepM = (size_t)TP * 8;
-  // activation codes: lane l of wave w loads row 32 w + l / 2, half l % 2
-  const uint32_t offA = (uint32_t)((32 * wv + (lane >> 1)) * 32 + (lane & 1) * 16);
-  // weight codes: run h of wave w, lane l: row 32 w + 16 h + l / 4, quarter l % 4
+  // activation codes: lane l of wave w fills slot l % 2 of row 32 w + l / 2
+  const int ra = 32 * wv + (lane >> 1);
+  const uint32_t offA = (uint32_t)(ra * 32 + (((lane & 1) ^ ((ra >> 3) & 1)) * 16));
+  // weight codes: run h of wave w, lane l fills slot l % 4 of row 32 w + 16 h + l / 4
   uint32_t offB[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r = 32 * wv + 16 * h + (lane >> 2);
     const int rr = min(n0 + r, N - 1) - n0;
-    offB[h] = (uint32_t)rr * (uint32_t)K + (uint32_t)((lane & 3) * 16);
+    offB[h] = (uint32_t)rr * (uint32_t)K + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
   }
   const uint32_t offM = (uint32_t)((wv * 64 + lane) * 4);
   const uint32_t ldsA0 = lds_addr(sA), ldsB0 = lds_addr(sB);
@@ -602,14 +605,15 @@ __global__ void __launch_bounds__(512, 1) k_gemm24_fp8(PrefillArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int row = wn0 + 32 * j + l32;
-      const uint4 lo = *reinterpret_cast<const uint4*>(b_ + row * 64 + g * 16);
-      const uint4 hi = *reinterpret_cast<const uint4*>(b_ + row * 64 + (2 + g) * 16);
+      const int q = (row >> 2) & 3;
+      const uint4 lo = *reinterpret_cast<const uint4*>(b_ + row * 64 + ((g ^ q) * 16));
+      const uint4 hi = *reinterpret_cast<const uint4*>(b_ + row * 64 + (((2 + g) ^ q) * 16));
       bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = wm0 + 32 * i + l32;
-      const uint4 av = *reinterpret_cast<const uint4*>(a_ + row * 32 + g * 16);
+      const uint4 av = *reinterpret_cast<const uint4*>(a_ + row * 32 + ((g ^ ((row >> 3) & 1)) * 16));
       const int ix = *reinterpret_cast<const int*>(a_ + BM * 32 + row * 8 + g * 4);
       const v4i af = v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
 #pragma unroll

@@ -39,6 +39,7 @@ import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16/fp16 matrix peak
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 matrix peak
 MALL_BYTES = 256 * 2 ** 20
 METRIC = "decode: effective HBM GB/s; prefill: TFLOP/s; both as % of MI355X peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_t1_bf16_k4096_n14336_traffic.txt")
@@ -316,6 +317,67 @@ def measure_ffn(steps, warmup, t=4096, hidden=4096, ffn=16384, n_out=4096):
     return recs
 
 
+def measure_fp8(steps, warmup, name="prefill"):
+    """The 2:4 prefill with 16-bit operands and with FP8 operands on the same input, alternating short
+    timed blocks; TFLOP/s of the kept products 2 t n_out k / 2 (the FP8 line against the FP8 peak)."""
+    import ctypes
+    import activation_sparsification_amd as spa
+    from activation_sparsification_amd._binding import _ptr, _stream
+    dev = torch.device("cuda:0")
+    spec = spec_of(name)
+    x, w = wl.make_inputs(spec)
+    x = x.to(dev)
+    wd = w.to(dev)
+    pw = spa.prepare_weight(wd, spec.alpha, want_wt=False)
+    w8 = spa.prepare_weight_fp8(wd)
+    cfg = spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, spec.var_rescale, spec.act)
+    copies = max(3, math.ceil(3 * MALL_BYTES / (wd.numel() * 2)))
+    mats = [wd] + [wd.clone() for _ in range(copies - 1)]
+    codes = [w8.codes] + [w8.codes.clone() for _ in range(copies - 1)]
+    y = torch.empty((spec.t, spec.n_out), dtype=x.dtype, device=dev)
+    ws = spa.workspace(2, spec.t, spec.k, spec.n_out, x.dtype, cfg, dev)
+    bf = [spa.PreparedCall("sparse_linear_prefill", x, pw, cfg, y, ws, w=m) for m in mats]
+    L = spa.lib()
+    c = cfg.c()
+    wdesc = pw.c()
+    st = _stream(dev)
+    f8 = [lambda i=i: L.sparse_linear_prefill_fp8(_ptr(x), spec.t, ctypes.byref(wdesc), _ptr(codes[i]),
+                                                  _ptr(w8.scale), ctypes.byref(c), None, _ptr(y), None, None,
+                                                  _ptr(ws), ws.numel(), st) for i in range(copies)]
+
+    def block(calls, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(2e6))
+        e0.record()
+        for i in range(n):
+            calls[i % copies]()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for i in range(warmup):
+        bf[i % copies]()
+        assert f8[i % copies]() == 0
+    torch.cuda.synchronize()
+    per = {"prefill_bf16": [], "prefill_fp8": []}
+    nblk = max(1, steps // 4)
+    for _ in range(4):
+        per["prefill_bf16"].append(block(bf, nblk))
+        per["prefill_fp8"].append(block(f8, nblk))
+    flops = 2.0 * spec.t * spec.n_out * spec.k * spec.n / spec.m
+    recs = []
+    for key, peak in (("prefill_bf16", PEAK_BF16_TFLOPS), ("prefill_fp8", PEAK_FP8_TFLOPS)):
+        ms = sorted(per[key])[len(per[key]) // 2]
+        tf = flops / (ms * 1e-3) / 1e12
+        recs.append(dict(workload=key, unit="TFLOP/s", value=tf, ms_per_step=ms, pct_of_peak=100.0 * tf / peak,
+                         kept_flops=flops, weight_copies=copies, blocks_ms=per[key],
+                         desc=f"2:4 prefill x[{spec.t},{spec.k}] -> {spec.n_out}, "
+                              + ("FP8 e4m3 operands, row scales" if key.endswith("fp8") else "bf16 operands")))
+    del mats, codes, bf, f8
+    torch.cuda.empty_cache()
+    return recs
+
+
 def cpu_baseline(name, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the workload on the host cores."""
     from oracle import nm_oracle as O
@@ -380,8 +442,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS) + ["meta", "ffn"],
-                    help="meta / ffn: only the block-metadata codec or squared-ReLU FFN lines (one JSON line)")
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS) + ["meta", "ffn", "fp8"],
+                    help="meta / ffn / fp8: only the block-metadata codec, squared-ReLU FFN or FP8 prefill "
+                         "lines (one JSON line)")
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -406,6 +469,9 @@ def main():
     if args.workload == "ffn":
         print(json.dumps({"ffn": measure_ffn(args.steps, args.warmup)}))
         return
+    if args.workload == "fp8":
+        print(json.dumps({"fp8": measure_fp8(args.steps, args.warmup)}))
+        return
     if args.workload == "meta":
         recs = []
         for fmt, n, m, t, k in [("comb", 2, 4, 4096, 16384), ("bitmap", 2, 4, 4096, 16384),
@@ -424,6 +490,7 @@ def main():
             secondary.append(measure(name, st, max(5, args.warmup // 2)))
         secondary += measure_meta("comb", 2, 4, 4096, 16384, args.steps, max(5, args.warmup // 2))
         secondary += measure_ffn(max(5, args.steps // 20), 3)
+        secondary += measure_fp8(max(8, args.steps // 10), 5)
 
     decode = head["unit"] == "GB/s"
     traffic = read_traffic() if args.workload == "decode" else None
