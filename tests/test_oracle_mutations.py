@@ -136,6 +136,17 @@ def _e4m3_truncate(v):                                   # rounds toward zero
     return np.array(out, np.uint8).reshape(np.shape(v))
 
 
+def _fp8_column_scales(v):                               # scales over the wrong axis
+    q, sc = _orig_fp8_rows(np.asarray(v, np.float32).T.copy())
+    return q.T.copy(), sc
+
+
+def _fp8_inverted_scale(v):                              # stores 448 / max instead of max / 448
+    q, sc = _orig_fp8_rows(v)
+    return q, np.where(sc > 0, np.float32(1.0) / np.where(sc > 0, sc, 1), 0).astype(np.float32)
+
+
+_orig_fp8_rows = O.fp8_rows
 _orig_factor = O.channel_factor
 _orig_amber = O.amber_factor
 _orig_var = O.var_factor
@@ -163,6 +174,8 @@ MUTANTS = {
     "ema_dense_denominator": ("var_factor_ema", _ema_dense_denominator),
     "e4m3_truncation": ("e4m3_round", _e4m3_truncate),
     "meta_width_floor": ("meta_width", _width_floor),
+    "fp8_column_scales": ("fp8_rows", _fp8_column_scales),
+    "fp8_inverted_scale": ("fp8_rows", _fp8_inverted_scale),
 }
 
 

@@ -387,6 +387,22 @@ def test_fp8_rows_scale_and_extremes():
     assert np.all(np.abs(deq[big] - v[big]) <= np.abs(v[big]) / 16 + 1e-12)
 
 
+def test_prefill_fp8_lossless_case_is_the_exact_product():
+    # integers in [-7, 7] with a 7 in every row: the scales are 7 / 448 = 1 / 64
+    # and every scaled value 64 v is an e4m3 value, so the FP8 product equals
+    # the exact integer product of the kept entries
+    rng = np.random.Generator(np.random.PCG64(31))
+    x = rng.integers(-7, 8, size=(5, 64))
+    w = rng.integers(-7, 8, size=(6, 64))
+    x[:, 3], w[:, 10] = 7, -7
+    pr = O.prefill_fp8(x.astype(np.float32), w.astype(np.float32), "bf16")
+    assert (pr["sx"] == np.float32(1 / 64)).all() and (pr["sw"] == np.float32(1 / 64)).all()
+    keep = pr["keep"].astype(np.int64)
+    assert np.array_equal(keep.reshape(5, 16, 4).sum(-1), np.full((5, 16), 2))
+    exact = (x * keep) @ w.T
+    assert np.array_equal(pr["y"], exact.astype(np.float64))
+
+
 def test_prefill_fp8_close_to_bf16():
     # FP8 quantisation error of y against the 16-bit product: a few per cent
     spec = wl.SPECS["prefill"].with_(t=16, k=512, n_out=64)
