@@ -514,6 +514,9 @@ def e4m3_value(code: int) -> float:
 def e4m3_round(v: np.ndarray) -> np.ndarray:
     """float32 values -> e4m3 codes (uint8), nearest value, ties to the even code.
 
+    The sign bit is the operand's, also when the result is zero: the format has
+    both zeros (0x00, 0x80) and IEEE rounding keeps the sign of a zero result.
+
     |v| is assumed <= 464 (the scaled operands stay within 448 up to one
     float32 rounding); larger inputs are outside the format."""
     table = [(e4m3_value(c), c) for c in range(128) if c != 0x7F]   # non-negative values, ascending
@@ -527,7 +530,7 @@ def e4m3_round(v: np.ndarray) -> np.ndarray:
     pick_hi = (dh < dl) | ((dh == dl) & (codes[hi] % 2 == 0) & (hi != lo))
     c = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
     c = np.where(a == vals[hi], codes[hi], c).astype(np.uint8)
-    neg = np.signbit(x) & (c != 0)
+    neg = np.signbit(x)
     return (c | np.where(neg, 0x80, 0).astype(np.uint8)).reshape(np.shape(v))
 
 

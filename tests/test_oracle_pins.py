@@ -366,12 +366,12 @@ def test_e4m3_round_is_nearest_even_by_exhaustive_search():
     reps = [O.e4m3_value(c) for c in range(0x7F)]
     mids = [(a + b) / 2 for a, b in zip(reps, reps[1:])]
     x = np.concatenate([rng.uniform(-460, 460, 3000), rng.standard_normal(500) * 1e-2, reps, mids,
-                        np.negative(mids), [0.0, -0.0, 448.0, 464.0 - 1e-3]]).astype(np.float32)
+                        np.negative(mids), [0.0, -0.0, 448.0, 464.0 - 1e-3, -1e-5, -2.0 ** -11, 2.0 ** -11]]).astype(np.float32)
     got = O.e4m3_round(x)
     for xi, ci in zip(x.tolist(), got.tolist()):
         cand = [(abs(Fraction(O.e4m3_value(c)) - abs(Fraction(xi))), c & 1, c) for c in range(0x7F)]
         best = min(cand)[2]
-        want = best | (0x80 if xi < 0 and best != 0 else 0)
+        want = best | (0x80 if math.copysign(1.0, xi) < 0 else 0)     # signed zeros keep the sign
         assert ci == want, (xi, hex(ci), hex(want))
 
 

@@ -34,6 +34,8 @@ def test_prepare_weight_fp8(dtype, n_out, k):
     _, w = wl.make_inputs(spec)
     w[3] = 0                                                     # an all-zero row: scale 0, codes 0
     w[5, 7] = 30.0                                               # one large entry sets its row's scale
+    w[5, 9] = -1e-6                                              # rounds to zero: the sign stays (0x80)
+    w[6, 2] = -0.0
     print(f"[fp8 weight] {dtype} n_out={n_out} k={k}", flush=True)
     w8 = spa.prepare_weight_fp8(w.to(dev))
     torch.cuda.synchronize()
@@ -123,4 +125,36 @@ def test_prefill_fp8_full_size_sampled():
     assert np.array_equal(w8.codes.cpu().numpy()[cols], q)
     assert np.array_equal(f32(w8.scale)[cols].view(np.uint32), s.view(np.uint32))
     err = O.rowwise_error(f32(y)[np.ix_(rows, cols)], pr["y"])
+    assert err <= O.TOLERANCE[spec.dtype], err
+
+
+def test_prefill_fp8_max_k():
+    # k = 2^23, the largest prefill k: a 256-row tile of weight codes spans
+    # just under 2^31 bytes of 32-bit offsets
+    dev = _dev()
+    spec = wl.SPECS["prefill"].with_(t=3, k=1 << 23, n_out=256, n_outliers=0)
+    print(f"[fp8 max size] t={spec.t} k={spec.k} n_out={spec.n_out}", flush=True)
+    x, _ = wl.make_inputs(spec, with_weight=False)
+    # the 2^31-element weight is drawn on the device (seeded); the oracle gets
+    # copies of the sampled rows of that input
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    wd = torch.randn((spec.n_out, spec.k), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    pw = spa.prepare_weight(wd, 0.0, want_wt=False)
+    w8 = spa.prepare_weight_fp8(wd)
+    y, idx, _ = spa.sparse_linear_prefill_fp8(x.to(dev), pw, w8, _cfg(spec), want_idx=True)
+    torch.cuda.synchronize()
+    cols = np.array([0, 77, 200, spec.n_out - 1])               # the last row carries the largest offset
+    ws = wd[torch.as_tensor(cols, device=dev)].cpu()
+    pr = _fp8_oracle(spec, x, ws)
+    assert np.array_equal(idx.cpu().numpy(), pr["idx"])
+    q, s = O.fp8_rows(f32(ws))
+    got = w8.codes[torch.as_tensor(cols, device=dev)].cpu().numpy()
+    bad = np.argwhere(got != q)
+    wv = f32(ws)
+    detail = [(int(r), int(c), float(wv[r, c]), int(got[r, c]), int(q[r, c])) for r, c in bad[:8]]
+    assert bad.shape[0] == 0, (bad.shape[0], detail, f32(w8.scale)[cols].tolist(), s.tolist())
+    assert np.array_equal(f32(w8.scale)[cols].view(np.uint32), s.view(np.uint32))
+    err = O.rowwise_error(f32(y)[:, cols], pr["y"])
     assert err <= O.TOLERANCE[spec.dtype], err
