@@ -610,16 +610,23 @@ __global__ void __launch_bounds__(512, 1) k_gemm24_fp8(PrefillArgs p) {
       const uint4 hi = *reinterpret_cast<const uint4*>(b_ + row * 64 + (((2 + g) ^ q) * 16));
       bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
+    v4i af[FM];
+    int ix[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = wm0 + 32 * i + l32;
       const uint4 av = *reinterpret_cast<const uint4*>(a_ + row * 32 + ((g ^ ((row >> 3) & 1)) * 16));
-      const int ix = *reinterpret_cast<const int*>(a_ + BM * 32 + row * 8 + g * 4);
-      const v4i af = v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+      ix[i] = *reinterpret_cast<const int*>(a_ + BM * 32 + row * 8 + g * 4);
+      af[i] = v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+    }
+    // every fragment read is issued before the first product, so the LDS
+    // latency is paid once per step rather than once per activation fragment
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(af, bf[j], acc[i][j], ix, 0, 0);
-    }
+        acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(af[i], bf[j], acc[i][j], ix[i], 0, 0);
     st = st == 2 ? 0 : st + 1;
   }
 #undef SPA_ISSUE8
