@@ -67,7 +67,7 @@ extern "C" {
 typedef enum spa_status {
   SPA_OK = 0,
   SPA_ERR_INVALID = 1,      /* rejected argument; nothing launched */
-  SPA_ERR_UNSUPPORTED = 2,  /* valid combination this build does not implement */
+  SPA_ERR_UNSUPPORTED = 2,  /* valid combination the library does not implement */
   SPA_ERR_HIP = 3           /* a HIP launch or runtime call failed */
 } spa_status;
 
