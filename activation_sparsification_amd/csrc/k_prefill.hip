@@ -524,17 +524,21 @@ hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st) {
 // logical channels [32g, 32g + 32) (g = l / 32) with two position bits each
 // in one 32-bit word; B lane l holds column l % 32's codes of channels
 // 16g .. 16g + 15 and 32 + 16g .. 32 + 16g + 15; D as for the 16-bit
-// instruction.  Same tile, wave grid and three-stage ring as k_gemm24, at half
-// the bytes: per step and row 32 B of codes + 8 B of positions (activations)
-// and 64 B of codes (weights), so each wave issues four direct loads per step.
+// instruction.  Same 256 x 256 tile and three-stage ring of direct loads as
+// k_gemm24, at half the bytes: per step and row 32 B of codes + 8 B of
+// positions (activations) and 64 B of codes (weights).  16 waves of 64 x 64
+// outputs (four waves per SIMD; 8 waves of 128 x 64 ran 5 % slower).  Per
+// stage every wave loads one 1 KB run of weight codes (16 rows); waves 0-7
+// also load one run of activation codes (32 rows) and one of positions (32
+// rows).  All of a step's fragment reads are issued before its products.
 // The 16-byte chunks are XOR-swizzled against bank conflicts: chunk c of
 // activation row r sits at c ^ ((r >> 3) & 1), of weight row r at
 // c ^ ((r >> 2) & 3).  y = nu_i * sx_i * sw_j * acc + eta_i * s_j.
 // ---------------------------------------------------------------------------
 template <int DT>
-__global__ void __launch_bounds__(512, 1) k_gemm24_fp8(PrefillArgs p) {
+__global__ void __launch_bounds__(1024, 1) k_gemm24_fp8(PrefillArgs p) {
   constexpr int BM = 256, BN = 256;
-  constexpr int WM = 128, WN = 64, FM = 4, FN = 2;
+  constexpr int WM = 64, WN = 64, FM = 2, FN = 2;
   constexpr int AST = BM * 40, BST = BN * 64;               // bytes per stage
   typedef int v4i __attribute__((ext_vector_type(4)));
   typedef int v8i __attribute__((ext_vector_type(8)));
@@ -555,32 +559,28 @@ __global__ void __launch_bounds__(512, 1) k_gemm24_fp8(PrefillArgs p) {
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int wm0 = (wv >> 2) * WM, wn0 = (wv & 3) * WN;
+  const bool loads_a = wv < 8;                              // wave-uniform
 
   const char* baseA = static_cast<const char*>(p.a_vals) + (size_t)m0 * 32;
   const char* baseM = reinterpret_cast<const char*>(p.a_meta) + (size_t)m0 * 8;
   const char* baseW = static_cast<const char*>(p.w) + (size_t)n0 * K;
   const size_t stepA = (size_t)TP * 32, stepM = (size_t)TP * 8;
-  // activation codes: lane l of wave w fills slot l % 2 of row 32 w + l / 2
-  const int ra = 32 * wv + (lane >> 1);
+  const int wa = wv & 7;
+  const int ra = 32 * wa + (lane >> 1);
   const uint32_t offA = (uint32_t)(ra * 32 + (((lane & 1) ^ ((ra >> 3) & 1)) * 16));
-  // weight codes: run h of wave w, lane l fills slot l % 4 of row 32 w + 16 h + l / 4
-  uint32_t offB[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = 32 * wv + 16 * h + (lane >> 2);
-    const int rr = min(n0 + r, N - 1) - n0;
-    offB[h] = (uint32_t)rr * (uint32_t)K + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
-  }
-  const uint32_t offM = (uint32_t)((wv * 64 + lane) * 4);
+  const uint32_t offM = (uint32_t)((wa * 64 + lane) * 4);
+  const int rb = 16 * wv + (lane >> 2);
+  const int rbc = min(n0 + rb, N - 1) - n0;
+  const uint32_t offB = (uint32_t)rbc * (uint32_t)K + (uint32_t)(((lane & 3) ^ ((rb >> 2) & 3)) * 16);
   const uint32_t ldsA0 = lds_addr(sA), ldsB0 = lds_addr(sB);
 
-#define SPA_ISSUE8(KT, ST)                                                                   \
+#define SPA_ISSUE8W(KT, ST)                                                                  \
   do {                                                                                       \
-    const char* w_ = baseW + (size_t)(KT) * 64;                                              \
-    lds_dma16(baseA + (size_t)(KT) * stepA, offA, ldsA0 + (ST) * AST + wv * 1024);           \
-    lds_dma16(w_, offB[0], ldsB0 + (ST) * BST + wv * 2048);                                  \
-    lds_dma16(w_, offB[1], ldsB0 + (ST) * BST + wv * 2048 + 1024);                           \
-    lds_dma4(baseM + (size_t)(KT) * stepM, offM, ldsA0 + (ST) * AST + BM * 32 + wv * 256);   \
+    lds_dma16(baseW + (size_t)(KT) * 64, offB, ldsB0 + (ST) * BST + wv * 1024);              \
+    if (loads_a) {                                                                           \
+      lds_dma16(baseA + (size_t)(KT) * stepA, offA, ldsA0 + (ST) * AST + wa * 1024);         \
+      lds_dma4(baseM + (size_t)(KT) * stepM, offM, ldsA0 + (ST) * AST + BM * 32 + wa * 256); \
+    }                                                                                        \
   } while (0)
 
   f32x16 acc[FM][FN];
@@ -592,13 +592,15 @@ __global__ void __launch_bounds__(512, 1) k_gemm24_fp8(PrefillArgs p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = K / 64;
-  SPA_ISSUE8(0, 0);
-  if (nk > 1) SPA_ISSUE8(1, 1);
+  SPA_ISSUE8W(0, 0);
+  if (nk > 1) SPA_ISSUE8W(1, 1);
   int st = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    wait_vm<4>(kt + 1 < nk);                     // step kt landed (kt+1 may be in flight)
+    // step kt landed (kt+1 may be in flight: 3 loads for waves 0-7, 1 for the others)
+    if (loads_a) wait_vm<3>(kt + 1 < nk);
+    else wait_vm<1>(kt + 1 < nk);
     bare_barrier();                              // every wave's copies visible; stage (kt+2)%3 free
-    if (kt + 2 < nk) SPA_ISSUE8(kt + 2, st == 0 ? 2 : st - 1);
+    if (kt + 2 < nk) SPA_ISSUE8W(kt + 2, st == 0 ? 2 : st - 1);
     const unsigned char* a_ = sA + st * AST;
     const unsigned char* b_ = sB + st * BST;
     v8i bf[FN];
@@ -619,8 +621,6 @@ __global__ void __launch_bounds__(512, 1) k_gemm24_fp8(PrefillArgs p) {
       ix[i] = *reinterpret_cast<const int*>(a_ + BM * 32 + row * 8 + g * 4);
       af[i] = v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
     }
-    // every fragment read is issued before the first product, so the LDS
-    // latency is paid once per step rather than once per activation fragment
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -629,7 +629,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm24_fp8(PrefillArgs p) {
         acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(af[i], bf[j], acc[i][j], ix[i], 0, 0);
     st = st == 2 ? 0 : st + 1;
   }
-#undef SPA_ISSUE8
+#undef SPA_ISSUE8W
 
   ts.park(s_nu, s_eta, s_rs);
   if ((int)threadIdx.x < BM) s_sx[threadIdx.x] = sx_own;
@@ -657,8 +657,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm24_fp8(PrefillArgs p) {
 hipError_t launch_gemm_fp8(int dtype, const PrefillArgs& a, hipStream_t st) {
   if (a.t == 0) return hipSuccess;
   const int tiles = ((a.t + 255) / 256) * ((a.n_out + 255) / 256);
-  if (dtype == SPA_F16) hipLaunchKernelGGL(k_gemm24_fp8<SPA_F16>, dim3(tiles), dim3(512), 0, st, a);
-  else hipLaunchKernelGGL(k_gemm24_fp8<SPA_BF16>, dim3(tiles), dim3(512), 0, st, a);
+  if (dtype == SPA_F16) hipLaunchKernelGGL(k_gemm24_fp8<SPA_F16>, dim3(tiles), dim3(1024), 0, st, a);
+  else hipLaunchKernelGGL(k_gemm24_fp8<SPA_BF16>, dim3(tiles), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 
