@@ -137,11 +137,13 @@ __device__ __forceinline__ void store_tile(const PrefillArgs& p, const f32x16 (&
 // 2:4 smfmac GEMM.  The pruning pass stores the packed activations and their
 // position words step-major (per 64-channel step: rows padded to t_pad, 64 B
 // of packed values and 8 B of position words per row), so a 256-row tile of
-// one step is one contiguous run.  BM = BN = 256; waves in a 2 x 4 grid of
-// 128 x 64 (4 x 2 fragments of 32 x 32).  Every wave issues exactly seven
-// direct loads per step (two 1 KB runs of packed values, four 1 KB groups of
-// weight rows, one 256 B run of position words); waiting for vmcnt <= 7
-// therefore means "the older of the two steps in flight has landed".
+// one step is one contiguous run.  BM = BN = 256; NW = 8 waves in a 2 x 4
+// grid of 128 x 64 (4 x 2 fragments of 32 x 32), or NW = 16 in a 4 x 4 grid
+// of 64 x 64 (2 x 2 fragments).  With 8 waves every wave issues seven direct
+// loads per step (two 1 KB runs of packed values, four 1 KB groups of weight
+// rows, one 256 B run of position words); with 16, four (waves 0-7) or three.
+// Waiting for vmcnt <= that count therefore means "the older of the two steps
+// in flight has landed".
 //
 // Each stage lives in its own __shared__ arrays.  Rows are unpadded; 16-byte
 // chunks are XOR-swizzled against bank conflicts: chunk c of activation row r
@@ -150,10 +152,11 @@ __device__ __forceinline__ void store_tile(const PrefillArgs& p, const f32x16 (&
 // the workspace held.  Neither reaches y: outputs are stored for rows < t and
 // columns < n_out only, and no row's result depends on another row.
 // ---------------------------------------------------------------------------
-template <int DT>
-__global__ void __launch_bounds__(512, 1) k_gemm24(PrefillArgs p) {
+template <int DT, int NW>
+__global__ void __launch_bounds__(NW * 64, 1) k_gemm24(PrefillArgs p) {
+  static_assert(NW == 8 || NW == 16, "8 waves of 128 x 64 or 16 of 64 x 64");
   constexpr int BM = 256, BN = 256;
-  constexpr int WM = 128, WN = 64, FM = 4, FN = 2;
+  constexpr int WM = NW == 8 ? 128 : 64, WN = 64, FM = WM / 32, FN = 2;
   using V8 = typename Frag<DT>::V8;
   using V16 = typename Frag<DT>::V16;
   // stage = packed activations (BM x 64 B) followed by their position words
@@ -180,19 +183,26 @@ __global__ void __launch_bounds__(512, 1) k_gemm24(PrefillArgs p) {
   const char* baseM = reinterpret_cast<const char*>(p.a_meta) + (size_t)m0 * 8;
   const char* baseW = static_cast<const char*>(p.w) + (size_t)n0 * K * 2;
   const size_t stepA = (size_t)TP * 64, stepM = (size_t)TP * 8;
-  // activation run h of wave wv: LDS slot s holds row 16 (2 wv + h) + s/4
-  const int ra0 = 32 * wv + (lane >> 2), ra1 = ra0 + 16;
-  const uint32_t offA0 = (uint32_t)(ra0 * 64 + (((lane & 3) ^ ((ra0 >> 2) & 3)) * 16));
-  const uint32_t offA1 = (uint32_t)(ra1 * 64 + (((lane & 3) ^ ((ra1 >> 2) & 3)) * 16));
-  // weight group h of wave wv: LDS slot s holds row 8 (4 wv + h) + s/8
-  uint32_t offB[4];
+  // Per step, 8 waves: wave wv loads activation runs h = 0, 1 (LDS slot s of
+  // run h holds row 16 (2 wv + h) + s/4), weight groups h = 0..3 (slot s of
+  // group h holds row 8 (4 wv + h) + s/8) and the position words of rows
+  // 32 wv .. +31.  16 waves: activation run wv, weight groups 2 wv, 2 wv + 1,
+  // and waves 0-7 the position words as above.
+  constexpr int NA = NW == 8 ? 2 : 1, NB = NW == 8 ? 4 : 2;
+  const bool loads_m = NW == 8 || wv < 8;                 // wave-uniform
+  uint32_t offA[NA], offB[NB];
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const int r = 32 * wv + 8 * h + (lane >> 3);
+  for (int h = 0; h < NA; ++h) {
+    const int ra = 16 * (NA * wv + h) + (lane >> 2);
+    offA[h] = (uint32_t)(ra * 64 + (((lane & 3) ^ ((ra >> 2) & 3)) * 16));
+  }
+#pragma unroll
+  for (int h = 0; h < NB; ++h) {
+    const int r = 8 * (NB * wv + h) + (lane >> 3);
     const int rr = min(n0 + r, N - 1) - n0;
     offB[h] = (uint32_t)rr * (uint32_t)K * 2u + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) * 16);
   }
-  const uint32_t offM = (uint32_t)((wv * 64 + lane) * 4);
+  const uint32_t offM = (uint32_t)(((wv & 7) * 64 + lane) * 4);
   const uint32_t ldsA0 = lds_addr(sA), ldsB0 = lds_addr(sB);
 
   // ---- LDS fragment offsets (bytes); the swizzle terms do not depend on i or j ----
@@ -211,14 +221,18 @@ __global__ void __launch_bounds__(512, 1) k_gemm24(PrefillArgs p) {
   do {                                                                                   \
     const char* a_ = baseA + (size_t)(KT) * stepA;                                       \
     const char* w_ = baseW + (size_t)(KT) * 128;                                         \
-    const uint32_t la_ = ldsA0 + (ST) * AST + wv * 2048, lb_ = ldsB0 + (ST) * BST + wv * 4096; \
-    lds_dma16(a_, offA0, la_);                                                           \
-    lds_dma16(a_, offA1, la_ + 1024);                                                    \
-    lds_dma16(w_, offB[0], lb_);                                                         \
-    lds_dma16(w_, offB[1], lb_ + 1024);                                                  \
-    lds_dma16(w_, offB[2], lb_ + 2048);                                                  \
-    lds_dma16(w_, offB[3], lb_ + 3072);                                                  \
-    lds_dma4(baseM + (size_t)(KT) * stepM, offM, ldsA0 + (ST) * AST + BM * 64 + wv * 256); \
+    const uint32_t la_ = ldsA0 + (ST) * AST + wv * (NA * 1024), lb_ = ldsB0 + (ST) * BST + wv * (NB * 1024); \
+    _Pragma("unroll") for (int h = 0; h < NA; ++h) lds_dma16(a_, offA[h], la_ + h * 1024); \
+    _Pragma("unroll") for (int h = 0; h < NB; ++h) lds_dma16(w_, offB[h], lb_ + h * 1024); \
+    if (loads_m)                                                                         \
+      lds_dma4(baseM + (size_t)(KT) * stepM, offM, ldsA0 + (ST) * AST + BM * 64 + (wv & 7) * 256); \
+  } while (0)
+  // loads per step: 7 for 8 waves; 4 (waves 0-7) or 3 for 16 waves
+#define SPA_WAIT24(COND)                                                                 \
+  do {                                                                                   \
+    if constexpr (NW == 8) wait_vm<7>(COND);                                             \
+    else if (loads_m) wait_vm<4>(COND);                                                  \
+    else wait_vm<3>(COND);                                                               \
   } while (0)
 
   // fragments of one 32-wide half step, two register sets (set 0: first
@@ -262,7 +276,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm24(PrefillArgs p) {
   const int nk = K / 64;
   SPA_ISSUE24(0, 0);
   if (nk > 1) SPA_ISSUE24(1, 1);
-  wait_vm<7>(nk > 1);
+  SPA_WAIT24(nk > 1);
   bare_barrier();
   if (nk > 2) SPA_ISSUE24(2, 2);
   SPA_READ24(0, 0);
@@ -271,7 +285,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm24(PrefillArgs p) {
   int st = 0;
   for (int kt = 1; kt < nk; ++kt) {
     st = st == 2 ? 0 : st + 1;                 // kt % 3
-    wait_vm<7>(kt + 1 < nk);                   // step kt landed (kt+1 may be in flight)
+    SPA_WAIT24(kt + 1 < nk);                   // step kt landed (kt+1 may be in flight)
     bare_barrier();                            // B_kt
     if (kt + 2 < nk) SPA_ISSUE24(kt + 2, st == 0 ? 2 : st - 1);
     SPA_READ24(st, 0);
@@ -281,6 +295,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm24(PrefillArgs p) {
   }
   SPA_MMA24(1);                                // last step, second half
 #undef SPA_ISSUE24
+#undef SPA_WAIT24
 #undef SPA_READ24
 #undef SPA_MMA24
 
@@ -506,8 +521,17 @@ hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st) {
   if (a.t == 0) return hipSuccess;
   if (a.sparse24) {
     const int tiles = ((a.t + 255) / 256) * ((a.n_out + 255) / 256);
-    if (dtype == SPA_F16) hipLaunchKernelGGL(k_gemm24<SPA_F16>, dim3(tiles), dim3(512), 0, st, a);
-    else hipLaunchKernelGGL(k_gemm24<SPA_BF16>, dim3(tiles), dim3(512), 0, st, a);
+    // up to 128 k steps per tile, 16 waves (four per SIMD) hide more of each
+    // tile's start and end: 160.8 vs 164.7 us at 2048 x 4096 -> 14336; at
+    // 16384 channels the 8-wave form is level or ahead (321.7 vs 323.3 us)
+    const bool w16 = a.k <= 8192;
+    if (dtype == SPA_F16) {
+      if (w16) hipLaunchKernelGGL((k_gemm24<SPA_F16, 16>), dim3(tiles), dim3(1024), 0, st, a);
+      else hipLaunchKernelGGL((k_gemm24<SPA_F16, 8>), dim3(tiles), dim3(512), 0, st, a);
+    } else {
+      if (w16) hipLaunchKernelGGL((k_gemm24<SPA_BF16, 16>), dim3(tiles), dim3(1024), 0, st, a);
+      else hipLaunchKernelGGL((k_gemm24<SPA_BF16, 8>), dim3(tiles), dim3(512), 0, st, a);
+    }
   } else {
     const int tiles = ((a.t + 255) / 256) * ((a.n_out + 127) / 128);
     if (dtype == SPA_F16) hipLaunchKernelGGL((k_gemm_dense<SPA_F16, 0>), dim3(tiles), dim3(512), 0, st, a);
