@@ -158,3 +158,45 @@ def test_prefill_fp8_max_k():
     assert np.array_equal(f32(w8.scale)[cols].view(np.uint32), s.view(np.uint32))
     err = O.rowwise_error(f32(y)[:, cols], pr["y"])
     assert err <= O.TOLERANCE[spec.dtype], err
+
+
+def test_prefill_fp8_running_average():
+    # the running-average variance factor with caller-held state (in, out)
+    dev = _dev()
+    spec = wl.SPECS["prefill"].with_(t=300, k=512, n_out=272, n_outliers=0, var_rescale=2)
+    x, w = wl.make_inputs(spec)
+    r_in = np.random.Generator(np.random.PCG64(17)).uniform(0.05, 2.0, size=spec.t).astype(np.float32)
+    st_in = torch.from_numpy(r_in).to(dev)
+    st_out = torch.full((spec.t,), -1.0, dtype=torch.float32, device=dev)
+    cfg = spa.PruneConfig(2, 4, spec.score, spec.shift, 2, spec.act, st_in, st_out)
+    wd = w.to(dev)
+    pw = spa.prepare_weight(wd, spec.alpha, want_wt=False)
+    w8 = spa.prepare_weight_fp8(wd)
+    y, idx, nu = spa.sparse_linear_prefill_fp8(x.to(dev), pw, w8, cfg, want_idx=True, want_nu=True)
+    torch.cuda.synchronize()
+    pr = O.prefill_fp8(f32(x), f32(w), spec.dtype, shift_mode=spec.shift, var_rescale=2, var_state=r_in)
+    assert np.array_equal(idx.cpu().numpy(), pr["idx"])
+    assert np.allclose(f32(nu), pr["nu"], rtol=1e-6, atol=0)
+    assert np.allclose(f32(st_out), pr["var_state"], rtol=1e-6, atol=0)
+    assert np.array_equal(f32(st_in), r_in)
+    err = O.rowwise_error(f32(y), pr["y"])
+    assert err <= O.TOLERANCE[spec.dtype], err
+
+
+def test_prefill_fp8_workspace_reused():
+    # one workspace, sized for the larger call, serves a larger then a smaller call
+    dev = _dev()
+    big = wl.SPECS["prefill"].with_(t=600, k=768, n_out=520, n_outliers=4)
+    small = big.with_(t=45)
+    x, w = wl.make_inputs(big)
+    wd = w.to(dev)
+    pw = spa.prepare_weight(wd, big.alpha, want_wt=False)
+    w8 = spa.prepare_weight_fp8(wd)
+    ws = spa.workspace(2, big.t, big.k, big.n_out, x.dtype, _cfg(big), dev)
+    for spec, xs in ((big, x), (small, x[7:7 + small.t].contiguous())):
+        y, idx, _ = spa.sparse_linear_prefill_fp8(xs.to(dev), pw, w8, _cfg(spec), want_idx=True, ws=ws)
+        torch.cuda.synchronize()
+        pr = _fp8_oracle(spec, xs, w)
+        assert np.array_equal(idx.cpu().numpy(), pr["idx"]), spec.t
+        err = O.rowwise_error(f32(y), pr["y"])
+        assert err <= O.TOLERANCE[spec.dtype], (spec.t, err)
