@@ -133,6 +133,56 @@ __device__ __forceinline__ void store_tile(const PrefillArgs& p, const f32x16 (&
   }
 }
 
+// The same outputs written through LDS: the wave stores its (FM*32) x (FN*32)
+// block of 16-bit results row-major into `st` (its own region of the freed
+// operand ring), then writes whole rows back as 16-byte pieces (eight of the
+// fragment layout's two-byte stores become one).  Rows past t are dropped;
+// columns past n_out (or any n_out not a multiple of 8) fall back to element
+// stores.
+template <int DT, int FM, int FN>
+__device__ __forceinline__ void store_tile_lds(const PrefillArgs& p, const f32x16 (&acc)[FM][FN], int m0, int n0,
+                                               int r0, int c0, int g, int l32, int lane, const float* s_nu,
+                                               const float* s_eta, const float* s_rs, uint16_t* st) {
+  constexpr int W = FN * 32, H = FM * 32, GPR = W / 8, RPI = 64 / GPR;
+  static_assert(64 % GPR == 0 && H % RPI == 0, "whole 16-byte groups per row");
+  float rs[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) rs[j] = s_rs[c0 + 32 * j + l32];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lr = 32 * i + 8 * (r / 4) + 4 * g + (r % 4);
+      const float nu = s_nu[r0 + lr], eta = s_eta[r0 + lr];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) st[lr * W + 32 * j + l32] = (uint16_t)from_f32<DT>(nu * acc[i][j][r] + eta * rs[j]);
+    }
+  }
+  // the wave's LDS writes are complete before its reads (one wave, in order)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint16_t* Y = static_cast<uint16_t*>(p.y);
+  const int N = p.n_out;
+  const bool whole = N % 8 == 0;
+#pragma unroll
+  for (int q = 0; q < H / RPI; ++q) {
+    const int rr = q * RPI + lane / GPR, gc = lane % GPR;
+    const int row = m0 + r0 + rr, col = n0 + c0 + gc * 8;
+    if (row >= p.t) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(st + rr * W + gc * 8);
+    uint16_t* dst = Y + (size_t)row * N + col;
+    if (whole && col < N) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (col + e < N) dst[e] = (uint16_t)(wd[e / 2] >> (16 * (e % 2)));
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 2:4 smfmac GEMM.  The pruning pass stores the packed activations and their
 // position words step-major (per 64-channel step: rows padded to t_pad, 64 B
@@ -300,8 +350,13 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm24(PrefillArgs p) {
 #undef SPA_MMA24
 
   ts.park(s_nu, s_eta, s_rs);
-  __syncthreads();
-  store_tile<DT, FM, FN>(p, acc, m0, n0, wm0, wn0, g, l32, s_nu, s_eta, s_rs);
+  __syncthreads();                             // every wave is done with the ring
+  // the wave's output block: the weight ring (3 x 32 KB) first, then the activation ring
+  constexpr int BLK = WM * WN * 2;
+  static_assert(3 * BST % BLK == 0 && NW * BLK <= 3 * BST + 3 * AST, "output blocks fit the ring");
+  const int off = wv * BLK;
+  uint16_t* blk = reinterpret_cast<uint16_t*>(off < 3 * BST ? sB + off : sA + (off - 3 * BST));
+  store_tile_lds<DT, FM, FN>(p, acc, m0, n0, wm0, wn0, g, l32, lane, s_nu, s_eta, s_rs, blk);
 }
 
 // ---------------------------------------------------------------------------
