@@ -139,15 +139,21 @@ __device__ __forceinline__ void store_tile(const PrefillArgs& p, const f32x16 (&
 // fragment layout's two-byte stores become one).  Rows past t are dropped;
 // columns past n_out (or any n_out not a multiple of 8) fall back to element
 // stores.
-template <int DT, int FM, int FN>
+// With a column scale s_cs (the FP8 GEMM's weight-row scales) the value is
+// nu_i * cs_j * acc + eta_i * rs_j.
+template <int DT, int FM, int FN, bool CS = false>
 __device__ __forceinline__ void store_tile_lds(const PrefillArgs& p, const f32x16 (&acc)[FM][FN], int m0, int n0,
                                                int r0, int c0, int g, int l32, int lane, const float* s_nu,
-                                               const float* s_eta, const float* s_rs, uint16_t* st) {
+                                               const float* s_eta, const float* s_rs, uint16_t* st,
+                                               const float* s_cs = nullptr) {
   constexpr int W = FN * 32, H = FM * 32, GPR = W / 8, RPI = 64 / GPR;
   static_assert(64 % GPR == 0 && H % RPI == 0, "whole 16-byte groups per row");
-  float rs[FN];
+  float rs[FN], cs[FN];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) rs[j] = s_rs[c0 + 32 * j + l32];
+  for (int j = 0; j < FN; ++j) {
+    rs[j] = s_rs[c0 + 32 * j + l32];
+    if constexpr (CS) cs[j] = s_cs[c0 + 32 * j + l32];
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -155,7 +161,12 @@ __device__ __forceinline__ void store_tile_lds(const PrefillArgs& p, const f32x1
       const int lr = 32 * i + 8 * (r / 4) + 4 * g + (r % 4);
       const float nu = s_nu[r0 + lr], eta = s_eta[r0 + lr];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) st[lr * W + 32 * j + l32] = (uint16_t)from_f32<DT>(nu * acc[i][j][r] + eta * rs[j]);
+      for (int j = 0; j < FN; ++j) {
+        float v;
+        if constexpr (CS) v = nu * cs[j] * acc[i][j][r] + eta * rs[j];
+        else v = nu * acc[i][j][r] + eta * rs[j];
+        st[lr * W + 32 * j + l32] = (uint16_t)from_f32<DT>(v);
+      }
     }
   }
   // the wave's LDS writes are complete before its reads (one wave, in order)
@@ -621,8 +632,13 @@ __global__ void __launch_bounds__(1024, 1) k_gemm24_fp8(PrefillArgs p) {
   constexpr int AST = BM * 40, BST = BN * 64;               // bytes per stage
   typedef int v4i __attribute__((ext_vector_type(4)));
   typedef int v8i __attribute__((ext_vector_type(8)));
-  __shared__ __attribute__((aligned(1024))) unsigned char sA[3 * AST];
-  __shared__ __attribute__((aligned(1024))) unsigned char sB[3 * BST];
+  // one ring: three activation stages, then three weight stages, sized up
+  // to 128 KB so that it also holds the 16 waves' 8 KB output blocks
+  constexpr int RING = 3 * (AST + BST) > 16 * 8192 ? 3 * (AST + BST) : 16 * 8192;
+  static_assert((3 * AST) % 1024 == 0, "weight stages 1 KB aligned");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[RING];
+  unsigned char* const sA = ring;
+  unsigned char* const sB = ring + 3 * AST;
   __shared__ float s_nu[BM], s_eta[BM], s_rs[BN], s_sx[BM], s_sw[BN];
 
   const int K = p.k, N = p.n_out, TP = p.t_pad;
@@ -711,26 +727,12 @@ __global__ void __launch_bounds__(1024, 1) k_gemm24_fp8(PrefillArgs p) {
 #undef SPA_ISSUE8W
 
   ts.park(s_nu, s_eta, s_rs);
-  if ((int)threadIdx.x < BM) s_sx[threadIdx.x] = sx_own;
+  if ((int)threadIdx.x < BM) s_sx[threadIdx.x] = sx_own * ts.nu;   // nu_i * sx_i
   if ((int)threadIdx.x < BN) s_sw[threadIdx.x] = sw_own;
-  __syncthreads();
-  uint16_t* Y = static_cast<uint16_t*>(p.y);
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tr = wm0 + 32 * i + 8 * (r / 4) + 4 * g + (r % 4);
-      const int row = m0 + tr;
-      if (row >= p.t) continue;
-      const float nsx = s_nu[tr] * s_sx[tr], eta = s_eta[tr];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int tc = wn0 + 32 * j + l32;
-        const int col = n0 + tc;
-        if (col < N) Y[(size_t)row * N + col] = (uint16_t)from_f32<DT>(nsx * s_sw[tc] * acc[i][j][r] + eta * s_rs[tc]);
-      }
-    }
-  }
+  __syncthreads();                             // every wave is done with the ring
+  static_assert(16 * WM * WN * 2 <= RING, "output blocks fit the ring");
+  uint16_t* blk = reinterpret_cast<uint16_t*>(ring + wv * (WM * WN * 2));
+  store_tile_lds<DT, FM, FN, true>(p, acc, m0, n0, wm0, wn0, g, l32, lane, s_sx, s_eta, s_rs, blk, s_sw);
 }
 
 hipError_t launch_gemm_fp8(int dtype, const PrefillArgs& a, hipStream_t st) {
