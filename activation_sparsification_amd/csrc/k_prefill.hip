@@ -104,39 +104,11 @@ struct TileScalars {
 };
 
 // y = nu_i * acc + eta_i * rowsum_j for a wave's FM x FN fragments of 32 x 32
-// at tile-relative (r0, c0) of the tile that starts at (m0, n0).
-template <int DT, int FM, int FN>
-__device__ __forceinline__ void store_tile(const PrefillArgs& p, const f32x16 (&acc)[FM][FN], int m0, int n0,
-                                           int r0, int c0, int g, int l32, const float* s_nu, const float* s_eta,
-                                           const float* s_rs) {
-  uint16_t* Y = static_cast<uint16_t*>(p.y);
-  float rs[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) rs[j] = s_rs[c0 + 32 * j + l32];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tr = r0 + 32 * i + 8 * (r / 4) + 4 * g + (r % 4);
-      const int row = m0 + tr;
-      if (row >= p.t) continue;
-      const float nu = s_nu[tr], eta = s_eta[tr];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + c0 + 32 * j + l32;
-        if (col < p.n_out) {
-          const float v = nu * acc[i][j][r] + eta * rs[j];
-          Y[(size_t)row * p.n_out + col] = (uint16_t)from_f32<DT>(v);
-        }
-      }
-    }
-  }
-}
-
-// The same outputs written through LDS: the wave stores its (FM*32) x (FN*32)
-// block of 16-bit results row-major into `st` (its own region of the freed
-// operand ring), then writes whole rows back as 16-byte pieces (eight of the
-// fragment layout's two-byte stores become one).  Rows past t are dropped;
+// at tile-relative (r0, c0) of the tile that starts at (m0, n0), written
+// through LDS: the wave stores its (FM*32) x (FN*32) block of 16-bit results
+// row-major into `st` (its own region of the freed operand ring), then writes
+// whole rows back as 16-byte pieces (eight of the fragment layout's two-byte
+// stores become one).  Rows past t are dropped;
 // columns past n_out (or any n_out not a multiple of 8) fall back to element
 // stores.
 // With a column scale s_cs (the FP8 GEMM's weight-row scales) the value is
@@ -505,8 +477,11 @@ __global__ void __launch_bounds__(512, 1) k_gemm_dense(PrefillArgs p) {
 
   if constexpr (EPI == 0) {
     ts.park(s_nu, s_eta, s_rs);
-    __syncthreads();
-    store_tile<DT, FM, FN>(p, acc, m0, n0, wm0, wn0, g, l32, s_nu, s_eta, s_rs);
+    __syncthreads();                           // every wave is done with the ring
+    // the wave's 8 KB output block: waves 0-3 in the first activation stage, 4-7 in the second
+    static_assert(WM * WN * 4 <= BM * 64, "four output blocks per activation stage");
+    uint16_t* blk = (wv < 4 ? sA0 : sA1) + (wv & 3) * (WM * WN);
+    store_tile_lds<DT, FM, FN>(p, acc, m0, n0, wm0, wn0, g, l32, lane, s_nu, s_eta, s_rs, blk);
   } else {
     // every wave is past its last read of the ring: step 0 of the tile (its
     // columns 0..63) goes to sA0, step 1 to sA1, row-major [256][64]
