@@ -389,15 +389,21 @@ class PreparedCall:
     """
 
     def __init__(self, fn_name: str, x, pw: PreparedWeight, cfg: PruneConfig, y, ws, eta_in=None, idx=None,
-                 nu=None, wt=None, w=None):
-        self._keep = (x, pw, y, ws, eta_in, idx, nu, wt, w)
+                 nu=None, wt=None, w=None, w8: Optional["Fp8Weight"] = None):
+        self._keep = (x, pw, y, ws, eta_in, idx, nu, wt, w, w8)
         self._cfg = cfg.c()
         self._wd = pw.c(wt=wt, w=w)
         self._fn = getattr(lib(), fn_name)
         self._name = fn_name
         t = x.shape[0]
-        self._args = (_ptr(x), t, ctypes.byref(self._wd), ctypes.byref(self._cfg), _ptr(eta_in), _ptr(y),
-                      _ptr(idx), _ptr(nu), _ptr(ws), 0 if ws is None else ws.numel(), _stream(x.device))
+        fp8 = fn_name == "sparse_linear_prefill_fp8"
+        if fp8 != (w8 is not None):
+            raise ValueError("the FP8 prefill takes the weight's FP8 codes (w8), the other calls do not")
+        head = (_ptr(x), t, ctypes.byref(self._wd))
+        if fp8:
+            head += (_ptr(w8.codes), _ptr(w8.scale))
+        self._args = head + (ctypes.byref(self._cfg), _ptr(eta_in), _ptr(y), _ptr(idx), _ptr(nu), _ptr(ws),
+                             0 if ws is None else ws.numel(), _stream(x.device))
 
     def __call__(self):
         st = self._fn(*self._args)

@@ -320,9 +320,7 @@ def measure_ffn(steps, warmup, t=4096, hidden=4096, ffn=16384, n_out=4096):
 def measure_fp8(steps, warmup, name="prefill"):
     """The 2:4 prefill with 16-bit operands and with FP8 operands on the same input, alternating short
     timed blocks; TFLOP/s of the kept products 2 t n_out k / 2 (the FP8 line against the FP8 peak)."""
-    import ctypes
     import activation_sparsification_amd as spa
-    from activation_sparsification_amd._binding import _ptr, _stream
     dev = torch.device("cuda:0")
     spec = spec_of(name)
     x, w = wl.make_inputs(spec)
@@ -337,13 +335,8 @@ def measure_fp8(steps, warmup, name="prefill"):
     y = torch.empty((spec.t, spec.n_out), dtype=x.dtype, device=dev)
     ws = spa.workspace(2, spec.t, spec.k, spec.n_out, x.dtype, cfg, dev)
     bf = [spa.PreparedCall("sparse_linear_prefill", x, pw, cfg, y, ws, w=m) for m in mats]
-    L = spa.lib()
-    c = cfg.c()
-    wdesc = pw.c()
-    st = _stream(dev)
-    f8 = [lambda i=i: L.sparse_linear_prefill_fp8(_ptr(x), spec.t, ctypes.byref(wdesc), _ptr(codes[i]),
-                                                  _ptr(w8.scale), ctypes.byref(c), None, _ptr(y), None, None,
-                                                  _ptr(ws), ws.numel(), st) for i in range(copies)]
+    f8 = [spa.PreparedCall("sparse_linear_prefill_fp8", x, pw, cfg, y, ws, w8=spa.Fp8Weight(cd, w8.scale))
+          for cd in codes]
 
     def block(calls, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -357,7 +350,7 @@ def measure_fp8(steps, warmup, name="prefill"):
 
     for i in range(warmup):
         bf[i % copies]()
-        assert f8[i % copies]() == 0
+        f8[i % copies]()
     torch.cuda.synchronize()
     per = {"prefill_bf16": [], "prefill_fp8": []}
     nblk = max(1, steps // 4)
