@@ -562,9 +562,10 @@ hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st) {
   if (a.t == 0) return hipSuccess;
   if (a.sparse24) {
     const int tiles = ((a.t + 255) / 256) * ((a.n_out + 255) / 256);
-    // up to 128 k steps per tile, 16 waves (four per SIMD) hide more of each
-    // tile's start and end: 160.8 vs 164.7 us at 2048 x 4096 -> 14336; at
-    // 16384 channels the 8-wave form is level or ahead (321.7 vs 323.3 us)
+    // up to 128 k steps per tile, 16 waves (four per SIMD); with two-byte
+    // epilogue stores they were ahead at 2048 x 4096 -> 14336 (160.8 vs
+    // 164.7 us), with the LDS-staged epilogue the two forms are level there
+    // (160.4 vs 160.3 us) and at 16384 channels
     const bool w16 = a.k <= 8192;
     if (dtype == SPA_F16) {
       if (w16) hipLaunchKernelGGL((k_gemm24<SPA_F16, 16>), dim3(tiles), dim3(1024), 0, st, a);
