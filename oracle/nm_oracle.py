@@ -553,12 +553,14 @@ def fp8_rows(v: np.ndarray):
 def prefill_fp8(x, w, dtype: str, score: str = "magnitude", f=None, shift_mode: str = "none", eta_in=None,
                 var_rescale=False, s=None, act: str = "none", var_state=None) -> dict:
     """2:4 prefill with FP8 operands: the mask of ``prune`` (on the 16-bit input),
-    the kept x_hat quantised per token, W quantised per output row;
+    then the sparsified x_hat quantised per token ([SqReLU] s5.3: sparsify
+    first, then quantise -- the token's scale is the largest kept |x_hat|),
+    W quantised per output row;
     y_ij = nu_i * sx_i * sw_j * sum_k qx_ik qw_jk + eta_i * s_j (float64)."""
     pr = prune(x, dtype, 2, 4, score=score, f=f, shift_mode=shift_mode, eta_in=eta_in, var_rescale=var_rescale,
                act=act, var_state=var_state)
-    xs = (pr["xhat"] * pr["keep"]).astype(np.float32)
-    qx, sx = fp8_rows(pr["xhat"])
+    xs = np.where(pr["keep"], pr["xhat"], np.float32(0.0)).astype(np.float32)
+    qx, sx = fp8_rows(xs)
     qx = np.where(pr["keep"], qx, 0).astype(np.uint8)
     qw, sw = fp8_rows(w)
     if s is None:

@@ -146,6 +146,21 @@ def _fp8_inverted_scale(v):                              # stores 448 / max inst
     return q, np.where(sc > 0, np.float32(1.0) / np.where(sc > 0, sc, 1), 0).astype(np.float32)
 
 
+def _fp8_whole_row_scale(x, w, dtype, score="magnitude", f=None, shift_mode="none", eta_in=None, var_rescale=False,
+                         s=None, act="none", var_state=None):   # token scale over the whole row, pruned entries too
+    pr = O.prune(x, dtype, 2, 4, score=score, f=f, shift_mode=shift_mode, eta_in=eta_in, var_rescale=var_rescale,
+                 act=act, var_state=var_state)
+    qx, sx = O.fp8_rows(pr["xhat"])
+    qx = np.where(pr["keep"], qx, 0).astype(np.uint8)
+    qw, sw = O.fp8_rows(w)
+    s = O.row_sum(w) if s is None else s
+    acc = O.e4m3_decode(qx) @ O.e4m3_decode(qw).T
+    y = pr["nu"].astype(np.float64)[:, None] * (sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] * acc)
+    pr.update(qx=qx, sx=sx, qw=qw, sw=sw)
+    pr["y"] = y + pr["eta"].astype(np.float64)[:, None] * np.asarray(s, np.float64)[None, :]
+    return pr
+
+
 _orig_fp8_rows = O.fp8_rows
 _orig_factor = O.channel_factor
 _orig_amber = O.amber_factor
@@ -176,6 +191,7 @@ MUTANTS = {
     "meta_width_floor": ("meta_width", _width_floor),
     "fp8_column_scales": ("fp8_rows", _fp8_column_scales),
     "fp8_inverted_scale": ("fp8_rows", _fp8_inverted_scale),
+    "fp8_scale_over_whole_row": ("prefill_fp8", _fp8_whole_row_scale),
 }
 
 

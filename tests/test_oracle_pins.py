@@ -403,6 +403,33 @@ def test_prefill_fp8_lossless_case_is_the_exact_product():
     assert np.array_equal(pr["y"], exact.astype(np.float64))
 
 
+def test_prefill_fp8_scale_is_over_the_kept_entries():
+    # [SqReLU] s5.3: sparsify, then quantise.  With the weight-aware score a
+    # row's largest |x_hat| can be pruned (a tiny channel factor); the token's
+    # scale is then the largest KEPT |x_hat| / 448, and that entry codes to
+    # +-448 exactly (0x7E / 0xFE)
+    x = np.array([[10.0, 1.0, 2.0, 0.5, -3.0, 0.25, 1.5, 0.75],
+                  [0.5, -9.0, 0.25, 1.0, 0.0, 0.0, 0.0, 0.0]], np.float32)
+    f = np.array([1e-3, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0, 1.0], np.float32)
+    w = np.eye(8, dtype=np.float32)
+    pr = O.prefill_fp8(x, w, "f32", score="weight", f=f)
+    assert not pr["keep"][0, 0] and pr["keep"][0, 2] and pr["keep"][0, 4]
+    assert pr["sx"][0] == np.float32(3.0) / np.float32(448.0)
+    assert pr["qx"][0, 4] == 0xFE and pr["qx"][0, 2] != 0
+    assert pr["sx"][1] == np.float32(9.0) / np.float32(448.0) and pr["qx"][1, 1] == 0xFE
+    # on a workload sample: every row's largest kept code is +-448
+    spec = wl.SPECS["prefill"].with_(t=12, k=256, n_out=8, score="weight", alpha=1.0, n_outliers=0)
+    xs, ws = wl.make_inputs(spec)
+    xs[:, 7] = 20.0                          # each row's largest value, on a channel of tiny weights
+    ws[:, 7] *= 1e-3
+    fa = O.channel_factor(_x32(ws), 1.0)
+    pr = O.prefill_fp8(_x32(xs), _x32(ws), "bf16", score="weight", f=fa, shift_mode="token_mean")
+    mags = np.abs(O.e4m3_decode(pr["qx"]))
+    assert (mags.max(axis=1) == 448.0).all()
+    xh = np.abs(pr["xhat"])
+    assert (np.where(pr["keep"], xh, 0).max(axis=1) < xh.max(axis=1)).all()   # the readings differ here
+
+
 def test_prefill_fp8_close_to_bf16():
     # FP8 quantisation error of y against the 16-bit product: a few per cent
     spec = wl.SPECS["prefill"].with_(t=16, k=512, n_out=64)
