@@ -29,6 +29,7 @@
 //    and runs the product on matrix cores (mfma 16x16x32).
 #include "spa_common.h"
 #include "spa_launch.h"
+#include "spa_plan.h"
 #include "spa_select.h"
 
 namespace spa {
@@ -38,7 +39,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxTok = 32;
-constexpr int kPruneChan = 256;  // channels per workgroup of the matrix-core path's pruning pass
 
 // ---------------------------------------------------------------------------
 // Split-K hand-off without cache-wide maintenance.  A partial is stored with
@@ -180,10 +180,8 @@ __device__ __forceinline__ void act_raw(uint4 (&raw)[NQ]) {
   }
 }
 
-// Waves per workgroup: 8 for the light cases; 4 (so each wave may use up to 512
-// registers) when several tokens or 32-wide blocks are ranked per lane.
 template <int M, int TOK>
-constexpr int fused_waves() { return (TOK >= 2 || M >= 32) ? 4 : 8; }
+constexpr int fused_waves() { return fused_waves_of(M, TOK); }
 
 template <int DT, int M, int TOK>
 __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(DecodeArgs a) {
@@ -373,7 +371,7 @@ __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(D
     // otherwise an exclusive prefix of the union counts over the workgroup
     int slot, total;
     if (T_ == 1) {
-      slot = base + b * a.n;
+      slot = one_token_list_slot(base, (int)threadIdx.x, a.n);
       total = min(NT, nb - pass * NT) * a.n;
     } else {
       int wtot;
@@ -556,14 +554,8 @@ __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(D
 //     kT1Loads loads per lane in flight, row offsets and coefficients held in
 //     scalar registers.  No wave waits for another before its stream.
 // ---------------------------------------------------------------------------
-constexpr int kT1Waves = 8, kT1Threads = kT1Waves * 64, kT1Cols = 512, kT1MaxChan = 2048, kT1Loads = 32;
-
-// The one-token kernel: 16-bit weights under kBufferOutOfRange bytes (32-bit
-// offsets) and at least eight 512-column tiles.
-__host__ __device__ inline bool t1_kernel(int t, int dtype, int k, int n_out) {
-  return t == 1 && dtype != SPA_F32 && n_out >= 8 * kT1Cols &&
-         (uint64_t)k * (uint64_t)n_out * 2u < (uint64_t)kBufferOutOfRange;
-}
+constexpr int kT1Loads = 32;
+static_assert(kPlanBufferLimit == kBufferOutOfRange, "one buffer limit");
 
 // so[q] = v of lane (lane ^ q), q = 1 .. M-1, inside groups of 32 lanes
 // (ds_swizzle bit mode: and-mask 31, xor-mask q).
@@ -962,7 +954,7 @@ __device__ __forceinline__ uint4 zero_unless(const uint4& v, bool ok) {
   return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
 }
 
-constexpr int kMmStages = 3, kMmRows = 64, kMmSteps = 4;   // ring stages of kMmSteps 64-channel steps
+constexpr int kMmStages = 3, kMmRows = 64;   // ring stages of kMmSteps 64-channel steps
 
 template <int TT>
 constexpr int mm_stage_bytes() { return kMmRows * 128 * kMmSteps + TT * 2048 * kMmSteps; }
@@ -1177,103 +1169,23 @@ __global__ void __launch_bounds__(512) k_decode_mm(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // Host planning and launch
 // ---------------------------------------------------------------------------
-static int pick_splits(int k, int m, int target_splits, int max_k_len) {
-  // largest split count <= target with k_len a multiple of m (and of 64 for MFMA windows)
-  const int blocks = k / m;
-  int s = target_splits < 1 ? 1 : target_splits;
-  if (s > blocks) s = blocks;
-  int bl = (blocks + s - 1) / s;          // m-blocks per split
-  while (bl * m > max_k_len && bl > 1) { ++s; bl = (blocks + s - 1) / s; }
-  return bl;
-}
-
 size_t decode_workspace(int t, int k, int n_out, int dtype, int n, int m, int score, int shift, int var,
                         DecodeArgs* plan) {
-  DecodeArgs p{};
-  p.t = t; p.k = k; p.n_out = n_out; p.n = n; p.m = m; p.score = score; p.shift = shift; p.var = var;
-  const bool fused = t <= 4 || dtype == SPA_F32;
-  size_t bytes = 0;
-  auto carve = [&](size_t nbytes) { size_t off = bytes; bytes += (nbytes + 255) & ~(size_t)255; return off; };
-  if (t1_kernel(t, dtype, k, n_out)) {
-    // one-token kernel: 512-column tiles (1 KB of each kept row per load
-    // instruction); channel splits until about 224 workgroups run (one per CU
-    // for 7/8 of the chip: measured a little faster than 252 for the 8:16
-    // decode shape, where each wave then lists exactly one batch of rows),
-    // each split at most kT1MaxChan channels, the partial traffic near 5 % of
-    // the weight bytes
-    p.col_tile = kT1Cols;
-    p.tiles = (n_out + p.col_tile - 1) / p.col_tile;
-    const int blocks = k / m;
-    int sp = 224 / p.tiles > 1 ? 224 / p.tiles : 1;
-    const double wbytes = (double)k * n / m * n_out * 2.0;
-    const int max_by_traffic = (int)(0.05 * wbytes / (8.0 * n_out));
-    if (sp > max_by_traffic) sp = max_by_traffic > 1 ? max_by_traffic : 1;
-    if (sp > blocks) sp = blocks;
-    int bl = (blocks + sp - 1) / sp;
-    if (bl * m > kT1MaxChan) bl = kT1MaxChan / m;
-    p.k_len = bl * m;
-    p.splits = (blocks + bl - 1) / bl;
-    const size_t o_part = carve((size_t)p.splits * n_out * 4);
-    const size_t o_stats = carve(var ? (size_t)p.tiles * p.splits * 4 * 8 : 0);
-    const size_t o_cnt = carve((size_t)p.tiles * 4);
-    const size_t o_eta = carve(4);
-    p.partial = (float*)o_part; p.stats = (double*)o_stats; p.counters = (unsigned*)o_cnt;
-    p.eta_ws = (float*)o_eta;
-  } else if (fused) {
-    // 8 lanes x one 16-byte load = one 128-byte cache line of every listed row
-    const int cpl = dtype == SPA_F32 ? 4 : 8;
-    p.col_tile = 8 * cpl;
-    p.tiles = (n_out + p.col_tile - 1) / p.col_tile;
-    // split the channels only when the column tiles alone cannot fill the 256 CUs;
-    // each wave keeps at least one block, and the partial traffic stays near 5 % of the weight bytes
-    const int blocks = k / m;
-    int sp = p.tiles >= 192 ? 1 : (256 + p.tiles - 1) / p.tiles;
-    const int max_by_waves = blocks / 8 > 1 ? blocks / 8 : 1;
-    const double wbytes = (double)k * n / m * n_out * 2.0;
-    const int max_by_traffic = (int)(0.05 * wbytes / (8.0 * t * n_out));
-    if (sp > max_by_waves) sp = max_by_waves;
-    if (sp > max_by_traffic) sp = max_by_traffic > 1 ? max_by_traffic : 1;
-    // the workgroup's row list (row index + one coefficient per token per entry) lives in LDS:
-    // at most 54 KiB
-    const int tok = t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : 8;
-    const int per_block = m < n * t ? m : n * t;          // union rows one block can contribute
-    const int max_entries = 55296 / (4 * (1 + tok));
-    const int max_blocks = max_entries / per_block > 1 ? max_entries / per_block : 1;
-    int bl = (blocks + sp - 1) / sp;
-    if (bl > max_blocks) bl = max_blocks;
-    p.k_len = bl * m;
-    p.splits = (k + p.k_len - 1) / p.k_len;
-    p.list_cap = bl * per_block;
-    p.chunk_blocks = bl;
-    const size_t o_part = carve((size_t)p.splits * t * n_out * 4);
-    const size_t o_stats = carve(var ? (size_t)p.tiles * p.splits * t * 4 * 8 : 0);
-    const size_t o_cnt = carve((size_t)p.tiles * 4);
-    const size_t o_eta = carve((size_t)t * 4);
-    p.partial = (float*)o_part; p.stats = (double*)o_stats; p.counters = (unsigned*)o_cnt;
-    p.eta_ws = (float*)o_eta;
-  } else {
-    // matrix-core path: prune once into masked rows (channel chunks of 8
-    // m-blocks), then one pass over w by 64-row tiles, split over k until
-    // about 256 workgroups run
-    p.tiles = (n_out + 63) / 64;
-    const int nsteps = (k + 63) / 64;
-    int sp = (256 + p.tiles - 1) / p.tiles;
-    if (sp > nsteps) sp = nsteps;
-    const int sps = (nsteps + sp - 1) / sp;
-    p.k_len = sps * 64;
-    p.splits = (nsteps + sps - 1) / sps;
-    p.chunks = (k + kPruneChan - 1) / kPruneChan;
-    // fragment order; at least kMmSteps steps, since the matrix-core pass reads them kMmSteps at a time
-    const size_t o_dense = carve((size_t)(nsteps > kMmSteps ? nsteps : kMmSteps) * ((t + 15) / 16) * 2048);
-    const size_t o_stats = carve(var ? (size_t)p.chunks * t * 4 * 8 : 0);
-    const size_t o_eta = carve((size_t)t * 4);
-    const size_t o_part = carve(p.splits > 1 ? (size_t)p.splits * t * n_out * 4 : 0);
-    const size_t o_cnt = carve((size_t)p.tiles * 4);
-    p.dense = (void*)o_dense; p.stats = (double*)o_stats; p.eta_ws = (float*)o_eta;
-    p.partial = (float*)o_part; p.counters = (unsigned*)o_cnt;
+  const DecodePlan p = plan_decode(t, k, n_out, dtype, n, m, var);
+  if (plan) {
+    DecodeArgs a{};
+    a.t = t; a.k = k; a.n_out = n_out; a.n = n; a.m = m; a.score = score; a.shift = shift; a.var = var;
+    a.tiles = p.tiles; a.splits = p.splits; a.k_len = p.k_len; a.col_tile = p.col_tile;
+    a.chunks = p.chunks; a.list_cap = p.list_cap; a.chunk_blocks = p.chunk_blocks;
+    // offsets into the workspace; the caller adds its base address
+    a.partial = reinterpret_cast<float*>(p.partial);
+    a.stats = reinterpret_cast<double*>(p.stats);
+    a.counters = reinterpret_cast<unsigned*>(p.counters);
+    a.eta_ws = reinterpret_cast<float*>(p.eta);
+    a.dense = reinterpret_cast<void*>(p.dense);
+    *plan = a;
   }
-  if (plan) *plan = p;
-  return bytes;
+  return p.bytes;
 }
 
 template <int DT, int M, int TOK>
