@@ -70,6 +70,33 @@ __device__ __forceinline__ uint32_t block_keep(const float* sc, int n) {
   return keep;
 }
 
+// Keep bits of the BPS = SEG / M blocks of one segment of shifted values:
+// score |x_hat| times the CLACT column norm or the weight factor (or alone),
+// then the top n of every m-block.
+template <int M, int SEG>
+__device__ __forceinline__ void seg_keep(const float (&xh)[SEG], int seg, const PruneArgs& a, uint32_t (&keep)[SEG / M]) {
+  float sc[SEG];
+  const float* f = a.colnorm ? a.colnorm + (size_t)seg * SEG : a.chan_scale ? a.chan_scale + (size_t)seg * SEG : nullptr;
+  if (f) {
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) sc[j] = __builtin_fabsf(xh[j]) * f[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) sc[j] = __builtin_fabsf(xh[j]);
+  }
+#pragma unroll
+  for (int b = 0; b < SEG / M; ++b) {
+    if constexpr (M >= 8) {            // selection network on the score bits
+      uint32_t sb[M];
+#pragma unroll
+      for (int j = 0; j < M; ++j) sb[j] = __float_as_uint(sc[b * M + j]);
+      keep[b] = topn_keep_bits<M>(sb, a.n);
+    } else {                           // 4 channels: six pairwise comparisons
+      keep[b] = block_keep<M>(sc + b * M, a.n);
+    }
+  }
+}
+
 // Token mean of a long row: 16-byte loads, four in flight per thread, four
 // float64 partial sums combined in a fixed order, then the workgroup sum.
 template <int DT>
@@ -147,25 +174,34 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
   if (threadIdx.x == 0) {
     if (a.eta_out) a.eta_out[row] = eta;
   }
-  // FP8 packing: the token's scale from max |x - eta| over the row (the
-  // registers of the one-pass case, else a second read of the row)
+  // FP8 packing quantises the sparsified row: the token's scale comes from
+  // max |x - eta| over the kept entries (the selection runs here first, on
+  // the registers of the one-pass case, else on a second read of the row)
   float fp8_inv = 0.f;
+  constexpr int BPS_ = SEG / M;
+  uint32_t keep0[BPS_] = {};
   if (a.fp8) {
     float mx = 0.f;
-    if (iters == 1) {
-      if ((int)threadIdx.x < nseg) {
+    for (int sg = threadIdx.x; sg < nseg; sg += 256) {
+      float v2[SEG];
+      if (iters == 1) {
 #pragma unroll
-        for (int j = 0; j < SEG; ++j) mx = fmaxf(mx, __builtin_fabsf(xv0[j] - eta));
-      }
-    } else {
-      for (int sg = threadIdx.x; sg < nseg; sg += 256) {
+        for (int j = 0; j < SEG; ++j) v2[j] = xv0[j];
+      } else {
         RawSeg<DT, SEG> r2;
         load_raw<DT, SEG>(xrs, sg, true, r2);
-        float v2[SEG];
         unpack_raw<DT, SEG>(r2, a.act, v2);
-#pragma unroll
-        for (int j = 0; j < SEG; ++j) mx = fmaxf(mx, __builtin_fabsf(v2[j] - eta));
       }
+      float xh2[SEG];
+#pragma unroll
+      for (int j = 0; j < SEG; ++j) xh2[j] = v2[j] - eta;
+      uint32_t kb2[BPS_];
+      seg_keep<M, SEG>(xh2, sg, a, kb2);
+#pragma unroll
+      for (int j = 0; j < SEG; ++j)
+        if ((kb2[j / M] >> (j % M)) & 1u) mx = fmaxf(mx, __builtin_fabsf(xh2[j]));
+#pragma unroll
+      for (int b = 0; b < BPS_; ++b) keep0[b] = kb2[b];
     }
     __shared__ float s_mx[4];
     const float amax = block_max(mx, s_mx);
@@ -196,29 +232,11 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
     if (active) {
 #pragma unroll
       for (int j = 0; j < SEG; ++j) xh[j] = xv[j] - eta;
-      float sc[SEG];
-      if (a.colnorm) {
-        const float* f = a.colnorm + (size_t)seg * SEG;
+      if (a.fp8 && iters == 1) {         // selected already, for the FP8 scale
 #pragma unroll
-        for (int j = 0; j < SEG; ++j) sc[j] = __builtin_fabsf(xh[j]) * f[j];
-      } else if (a.chan_scale) {
-        const float* f = a.chan_scale + (size_t)seg * SEG;
-#pragma unroll
-        for (int j = 0; j < SEG; ++j) sc[j] = __builtin_fabsf(xh[j]) * f[j];
+        for (int b = 0; b < BPS; ++b) keepbits[b] = keep0[b];
       } else {
-#pragma unroll
-        for (int j = 0; j < SEG; ++j) sc[j] = __builtin_fabsf(xh[j]);
-      }
-#pragma unroll
-      for (int b = 0; b < BPS; ++b) {
-        if constexpr (M >= 8) {            // selection network on the score bits
-          uint32_t sb[M];
-#pragma unroll
-          for (int j = 0; j < M; ++j) sb[j] = __float_as_uint(sc[b * M + j]);
-          keepbits[b] = topn_keep_bits<M>(sb, n);
-        } else {                           // 4 channels: six pairwise comparisons
-          keepbits[b] = block_keep<M>(sc + b * M, n);
-        }
+        seg_keep<M, SEG>(xh, seg, a, keepbits);
       }
 
       if (a.var) {
