@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     meta_row_bytes,
     prepare_amber,
     prepare_weight,
+    prefill_layout,
     prepare_weight_fp8,
     prune_nm,
     sparse_linear_decode,

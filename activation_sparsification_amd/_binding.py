@@ -37,6 +37,11 @@ class _Cfg(ctypes.Structure):
                 ("var_state", ctypes.c_void_p), ("var_state_out", ctypes.c_void_p)]
 
 
+class _PrefillLayout(ctypes.Structure):
+    _fields_ = [("vals", ctypes.c_size_t), ("meta", ctypes.c_size_t), ("eta", ctypes.c_size_t),
+                ("scale", ctypes.c_size_t), ("t_pad", ctypes.c_int32), ("bytes", ctypes.c_size_t)]
+
+
 class _Weight(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("n_out", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("w", ctypes.c_void_p), ("wt", ctypes.c_void_p), ("chan_scale", ctypes.c_void_p),
@@ -57,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.spa_status_str.argtypes = [ctypes.c_int]
         L.spa_workspace_bytes.restype = sz
         L.spa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(_Cfg)]
+        L.spa_prefill_layout.restype = ctypes.c_int
+        L.spa_prefill_layout.argtypes = [i32, i32, i32, ctypes.POINTER(_Cfg), ctypes.POINTER(_PrefillLayout)]
         L.prepare_weight.restype = ctypes.c_int
         L.prepare_weight.argtypes = [vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp]
         L.spa_eta_calibrate.restype = ctypes.c_int
@@ -99,7 +106,7 @@ EXPORTS = ("prepare_weight", "prune_nm", "sparse_linear_decode", "sparse_linear_
            "spa_workspace_bytes", "spa_status_str", "spa_meta_row_bytes", "spa_encode_meta", "spa_decode_meta",
            "prepare_amber", "spa_amber_workspace_bytes", "spa_eta_calibrate", "spa_eta_table", "spa_eta_lookup",
            "sparse_ffn_relu2_prefill", "spa_ffn_workspace_bytes", "prepare_weight_fp8",
-           "sparse_linear_prefill_fp8")
+           "sparse_linear_prefill_fp8", "spa_prefill_layout")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -165,6 +172,14 @@ def _dev(t: torch.Tensor):
 def workspace_bytes(entry: int, t: int, k: int, n_out: int, dtype: torch.dtype, cfg: PruneConfig) -> int:
     c = cfg.c()
     return int(lib().spa_workspace_bytes(entry, t, k, n_out, DTYPE[dtype], ctypes.byref(c)))
+
+
+def prefill_layout(t: int, k: int, dtype: torch.dtype, cfg: PruneConfig) -> dict:
+    """Byte offsets of the pruned operand, positions, shift and FP8 scales in a prefill workspace."""
+    c = cfg.c()
+    out = _PrefillLayout()
+    _check(lib().spa_prefill_layout(t, k, DTYPE[dtype], ctypes.byref(c), ctypes.byref(out)), "spa_prefill_layout")
+    return {name: getattr(out, name) for name, _ in _PrefillLayout._fields_}
 
 
 _WS_CACHE: dict = {}

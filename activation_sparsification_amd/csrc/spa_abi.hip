@@ -27,8 +27,11 @@ bool valid_cfg(const spa_prune_cfg* c) {
   return true;
 }
 
-// k must hold whole m-blocks and whole 16-channel segments of the pruning pass.
-bool valid_k(int64_t k, const spa_prune_cfg* c) { return k >= 16 && k <= kMaxDim && k % 16 == 0 && k % c->m == 0; }
+// k must hold whole m-blocks (anything else is an invalid argument) ...
+bool valid_k(int64_t k, const spa_prune_cfg* c) { return k >= c->m && k <= kMaxDim && k % c->m == 0; }
+// ... and, to be built, whole 16-channel segments of the pruning pass (a valid
+// k that is not is an unbuilt combination: 2:4 or 4:8 with k = 36, say).
+bool built_k(int64_t k) { return k % 16 == 0; }
 
 spa_status hip_status(hipError_t e) { return e == hipSuccess ? SPA_OK : SPA_ERR_HIP; }
 
@@ -72,19 +75,15 @@ spa_status check_linear(const void* x, int32_t t, const spa_weight* w, const spa
   if (cfg->score == SPA_SCORE_WEIGHT && !w->chan_scale) return SPA_ERR_INVALID;
   if (cfg->shift == SPA_SHIFT_GIVEN && !eta_in) return SPA_ERR_INVALID;
   if (cfg->shift != SPA_SHIFT_NONE && !w->row_sum) return SPA_ERR_INVALID;
-  if (decode) {
-    // 1..4 tokens (and float32) stream the channel-major copy; more tokens of a
-    // 16-bit type run on the matrix cores over the row-major weight
-    if (t <= 4 || w->dtype == SPA_F32) {
-      if (!w->wt || !aligned16(w->wt)) return SPA_ERR_INVALID;
-      if (w->n_out % (16 / dtype_bytes(w->dtype))) return SPA_ERR_INVALID;
-    } else {
-      if (!w->w || !aligned16(w->w)) return SPA_ERR_INVALID;
-    }
-  } else {
-    if (!w->w || !aligned16(w->w)) return SPA_ERR_INVALID;
-    if (w->k % 64) return SPA_ERR_INVALID;
-  }
+  // 1..4 tokens (and float32) stream the channel-major copy; more tokens of a
+  // 16-bit type run on the matrix cores over the row-major weight
+  const bool reads_wt = decode && (t <= 4 || w->dtype == SPA_F32);
+  const void* need = reads_wt ? w->wt : w->w;
+  if (!need || !aligned16(need)) return SPA_ERR_INVALID;
+  // valid, but outside what the kernels are built for
+  if (!built_k(w->k)) return SPA_ERR_UNSUPPORTED;
+  if (reads_wt && w->n_out % (16 / dtype_bytes(w->dtype))) return SPA_ERR_UNSUPPORTED;   // 16-byte weight rows
+  if (!decode && w->k % 64) return SPA_ERR_UNSUPPORTED;                                   // whole GEMM k steps
   return SPA_OK;
 }
 
@@ -189,8 +188,8 @@ const char* spa_status_str(spa_status s) {
 
 size_t spa_workspace_bytes(int32_t entry, int32_t t, int32_t k, int32_t n_out, int32_t dtype,
                            const spa_prune_cfg* cfg) {
-  if (!valid_cfg(cfg) || !valid_dtype(dtype) || !valid_k(k, cfg) || t < 0 || t > kMaxDim || n_out < 0 ||
-      n_out > kMaxDim)
+  if (!valid_cfg(cfg) || !valid_dtype(dtype) || !valid_k(k, cfg) || !built_k(k) || t < 0 || t > kMaxDim ||
+      n_out < 0 || n_out > kMaxDim)
     return 0;
   switch (entry) {
     case SPA_ENTRY_PRUNE: return prune_ws(t, k, cfg);
@@ -201,6 +200,21 @@ size_t spa_workspace_bytes(int32_t entry, int32_t t, int32_t k, int32_t n_out, i
     case SPA_ENTRY_PREFILL: return prefill_plan(t, k, dtype, cfg).bytes;
     default: return 0;
   }
+}
+
+spa_status spa_prefill_layout(int32_t t, int32_t k, int32_t dtype, const spa_prune_cfg* cfg,
+                              spa_operand_layout* out) {
+  if (!out || !valid_cfg(cfg) || !valid_dtype(dtype) || !valid_k(k, cfg) || !built_k(k) || t < 0 || t > kMaxDim)
+    return SPA_ERR_INVALID;
+  const PrefillPlan p = prefill_plan(t, k, dtype, cfg);
+  const bool s24 = cfg->n == 2 && cfg->m == 4;
+  out->vals = p.vals;
+  out->meta = s24 ? p.meta : 0;
+  out->eta = p.eta;
+  out->scale = s24 ? p.sx : 0;
+  out->t_pad = s24 ? tiled_rows(t) : t;
+  out->bytes = p.bytes;
+  return SPA_OK;
 }
 
 spa_status prepare_weight(const void* w, int32_t dtype, int32_t n_out, int32_t k, float alpha, void* wt_out,
@@ -219,6 +233,7 @@ spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const sp
   if (!x || !vals_out || !aligned16(x) || !aligned16(vals_out)) return SPA_ERR_INVALID;
   if (cfg->score == SPA_SCORE_WEIGHT && !chan_scale) return SPA_ERR_INVALID;
   if (cfg->shift == SPA_SHIFT_GIVEN && !eta_in) return SPA_ERR_INVALID;
+  if (!built_k(k)) return SPA_ERR_UNSUPPORTED;
   const size_t need = prune_ws(t, k, cfg);
   if (need && (!workspace || workspace_bytes < need || !aligned16(workspace))) return SPA_ERR_INVALID;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -258,11 +273,6 @@ spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, c
                                 size_t workspace_bytes, void* stream) {
   if (spa_status s = check_linear(x, t, w, cfg, eta_in, y, true)) return s;
   if (w->dtype == SPA_F32 && t > 8) return SPA_ERR_UNSUPPORTED;
-  // the channel-major weight of the 1..4-token (and float32) paths must stay
-  // under 2 GiB: larger ones are not validated on the device
-  if ((t <= 4 || w->dtype == SPA_F32) &&
-      (int64_t)w->k * w->n_out * dtype_bytes(w->dtype) >= (int64_t(1) << 31))
-    return SPA_ERR_UNSUPPORTED;
   spa::DecodeArgs a{};
   const size_t need = spa::decode_workspace(t, w->k, w->n_out, w->dtype, cfg->n, cfg->m, cfg->score, cfg->shift,
                                             cfg->var_rescale, &a);
@@ -301,9 +311,10 @@ spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, 
 
 spa_status prepare_weight_fp8(const void* w, int32_t dtype, int32_t n_out, int32_t k, uint8_t* codes_out,
                               float* scale_out, void* stream) {
-  if (!w || !codes_out || !scale_out || (dtype != SPA_F16 && dtype != SPA_BF16)) return SPA_ERR_INVALID;
-  if (n_out < 1 || n_out > kMaxDim || k < 8 || k > kMaxDim || k % 8) return SPA_ERR_INVALID;
+  if (!w || !codes_out || !scale_out || !valid_dtype(dtype)) return SPA_ERR_INVALID;
+  if (n_out < 1 || n_out > kMaxDim || k < 1 || k > kMaxDim) return SPA_ERR_INVALID;
   if (!aligned16(w) || !aligned16(codes_out)) return SPA_ERR_INVALID;
+  if (dtype == SPA_F32 || k % 8) return SPA_ERR_UNSUPPORTED;      // 16-bit rows in 16-byte pieces
   return hip_status(spa::launch_quant_rows(dtype, w, n_out, k, codes_out, scale_out, static_cast<hipStream_t>(stream)));
 }
 
@@ -323,10 +334,10 @@ spa_status sparse_linear_prefill_fp8(const void* x, int32_t t, const spa_weight*
 
 spa_status spa_eta_calibrate(const void* x, int32_t dtype, int32_t t, int32_t k, const int32_t* token_ids,
                              int32_t vocab, double* sums, uint32_t* counts, void* stream) {
-  if (!valid_dtype(dtype) || t < 0 || t > kMaxDim || k < 16 || k > kMaxDim || k % 16 || vocab < 0)
-    return SPA_ERR_INVALID;
+  if (!valid_dtype(dtype) || t < 0 || t > kMaxDim || k < 1 || k > kMaxDim || vocab < 0) return SPA_ERR_INVALID;
   if (t == 0) return SPA_OK;
   if (!x || !aligned16(x) || !token_ids || (vocab > 0 && (!sums || !counts))) return SPA_ERR_INVALID;
+  if (k % 16) return SPA_ERR_UNSUPPORTED;                          // rows read in 16-channel pieces
   return hip_status(spa::launch_eta_calibrate(dtype, x, t, k, token_ids, vocab, sums, counts,
                                               static_cast<hipStream_t>(stream)));
 }
@@ -358,14 +369,18 @@ spa_status sparse_ffn_relu2_prefill(const void* x, int32_t t, const spa_weight* 
                                     void* y, uint8_t* idx_out, void* workspace, size_t workspace_bytes,
                                     void* stream) {
   if (!x || !y || !up || !down || t < 0 || t > kMaxDim) return SPA_ERR_INVALID;
-  if (up->dtype != down->dtype || (up->dtype != SPA_F16 && up->dtype != SPA_BF16)) return SPA_ERR_INVALID;
+  if (up->dtype != down->dtype || !valid_dtype(up->dtype)) return SPA_ERR_INVALID;
   const int hidden = up->k, ffn = up->n_out;
-  if (hidden < 64 || hidden % 64 || ffn < 64 || ffn % 64 || down->k != ffn) return SPA_ERR_INVALID;
+  // ffn holds whole 2:4 blocks; hidden is any positive width
+  if (hidden < 1 || hidden > kMaxDim || ffn < 4 || ffn > kMaxDim || ffn % 4 || down->k != ffn)
+    return SPA_ERR_INVALID;
   if (down->n_out < 1 || down->n_out > kMaxDim) return SPA_ERR_INVALID;
-  if (hidden > kMaxPrefillK || ffn > kMaxPrefillK) return SPA_ERR_UNSUPPORTED;
   if (!up->w || !down->w || !aligned16(up->w) || !aligned16(down->w) || !aligned16(x) || !aligned16(y))
     return SPA_ERR_INVALID;
   if (idx_out && !aligned16(idx_out)) return SPA_ERR_INVALID;
+  // built for whole 64-channel GEMM steps and 32-bit tile offsets
+  if (up->dtype == SPA_F32 || hidden % 64 || ffn % 64 || hidden > kMaxPrefillK || ffn > kMaxPrefillK)
+    return SPA_ERR_UNSUPPORTED;
   if (t == 0) return SPA_OK;
   const size_t need = spa_ffn_workspace_bytes(t, ffn, up->dtype);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SPA_ERR_INVALID;

@@ -78,7 +78,9 @@ enum { SPA_ACT_NONE = 0, SPA_ACT_RELU2 = 1 };
 enum { SPA_META_BITMAP = 0, SPA_META_COMB = 1 };
 enum { SPA_ENTRY_PRUNE = 0, SPA_ENTRY_DECODE = 1, SPA_ENTRY_PREFILL = 2 };
 
-/* Pruning configuration.  m in {4, 8, 16, 32}; 1 <= n <= m; k % m == 0. */
+/* Pruning configuration.  m in {4, 8, 16, 32}; 1 <= n <= m; k % m == 0
+ * (else SPA_ERR_INVALID).  The kernels are built for k % 16 == 0: a k of
+ * whole m-blocks that is not returns SPA_ERR_UNSUPPORTED. */
 typedef struct spa_prune_cfg {
   int32_t n;
   int32_t m;
@@ -145,7 +147,8 @@ spa_status prepare_amber(const void* w, int32_t dtype, int32_t n_out, int32_t k,
  * token id; the table entry of an id is the mean of its collected shifts; at
  * run time a token's shift is its id's entry, passed as eta_in with
  * SPA_SHIFT_GIVEN.
- * spa_eta_calibrate -- x [device] [t][k] (k % 16 == 0), token_ids [device]
+ * spa_eta_calibrate -- x [device] [t][k] (k % 16 != 0: SPA_ERR_UNSUPPORTED),
+ *   token_ids [device]
  *   [t] int32; adds each token's shift to sums[id] (float64) and 1 to
  *   counts[id] (uint32), both [device] [vocab] and zero-filled by the caller
  *   before the first batch.  Ids outside [0, vocab) are skipped.  The float64
@@ -205,8 +208,9 @@ spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const sp
  *           zero-filled before its first use; each call leaves it reusable
  *           for later calls with the same sizes and configuration (zero it
  *           again before using it for other sizes).
- * Returns SPA_ERR_UNSUPPORTED for float32 with t > 8, and when the 1..4-token
- * (or float32) path would read a channel-major weight of 2 GiB or more.
+ * Returns SPA_ERR_UNSUPPORTED for float32 with t > 8, for k % 16 != 0 and,
+ * on the channel-major paths, for rows of wt that are not whole 16-byte
+ * pieces (n_out % 8 != 0 in 16-bit dtypes, % 4 in float32).
  */
 spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
                                 const float* eta_in, void* y, uint8_t* idx_out, float* nu_out,
@@ -220,9 +224,10 @@ spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, c
  * ("Accelerating Transformer training and inference with 2:4 sparsity and
  * Squared-ReLU" s2.1, s3.1); every other n:m runs dense MFMA on the
  * masked activations.
- *  Arguments as for sparse_linear_decode; w->w required, any n_out >= 1,
- *  k % 64 == 0.  workspace: spa_workspace_bytes(SPA_ENTRY_PREFILL, ...).
- *  SPA_ERR_UNSUPPORTED for k > 2^23 (8388608).
+ *  Arguments as for sparse_linear_decode; w->w required, any n_out >= 1.
+ *  workspace: spa_workspace_bytes(SPA_ENTRY_PREFILL, ...).
+ *  SPA_ERR_UNSUPPORTED for float32, for k % 64 != 0 (whole 64-channel GEMM
+ *  steps) and for k > 2^23 (8388608).
  */
 spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
                                  const float* eta_in, void* y, uint8_t* idx_out, float* nu_out,
@@ -239,7 +244,8 @@ spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, 
  *  w          [device] [n_out][k], SPA_F16 or SPA_BF16, 16-byte aligned
  *  codes_out  [device] [n_out][k] bytes, 16-byte aligned
  *  scale_out  [device] [n_out] float32
- * Requires k % 8 == 0.  Run once per layer, off the hot path.
+ * SPA_ERR_UNSUPPORTED for a float32 weight or k % 8 != 0.  Run once per
+ * layer, off the hot path.
  */
 spa_status prepare_weight_fp8(const void* w, int32_t dtype, int32_t n_out, int32_t k, uint8_t* codes_out,
                               float* scale_out, void* stream);
@@ -313,8 +319,10 @@ spa_status spa_decode_meta(const void* codes, int32_t t, int32_t k, int32_t n, i
  *  y       [device] [t][n_out]
  *  idx_out [device] [t][ffn/2] the kept positions of the activation, or NULL
  *  workspace [device] spa_ffn_workspace_bytes(t, ffn, dtype) bytes
- * Requires a 16-bit dtype (the same for x, both weights and y),
- * hidden % 64 == 0, ffn % 64 == 0, both <= 2^23, down.k == ffn, n_out >= 1.  An activation value that ties exactly inside a block
+ * Requires the same dtype for x, both weights and y, ffn % 4 == 0,
+ * down.k == ffn, n_out >= 1 (else SPA_ERR_INVALID); SPA_ERR_UNSUPPORTED for
+ * float32, for hidden or ffn not a multiple of 64 and for either above 2^23.
+ * An activation value that ties exactly inside a block
  * keeps the lower index; because u comes from a float32-accumulating GEMM,
  * a near-tie can resolve differently from a float64 reference.
  */
@@ -322,6 +330,35 @@ size_t spa_ffn_workspace_bytes(int32_t t, int32_t ffn, int32_t dtype);
 spa_status sparse_ffn_relu2_prefill(const void* x, int32_t t, const spa_weight* up, const spa_weight* down,
                                     void* y, uint8_t* idx_out, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/*
+ * spa_prefill_layout -- where sparse_linear_prefill and
+ * sparse_linear_prefill_fp8 keep the pruned operand inside their workspace
+ * (for inspecting it after a call: tests, debugging; the calls do not need
+ * it).  Byte offsets from the workspace start; a region the configuration
+ * does not use has offset 0 and is not written.
+ *  vals   2:4: per 64-channel step s and row r < t_pad, the step's 32 kept
+ *         values in ascending channel order at ((s * t_pad) + r) * 32
+ *         elements: dtype values, or on the FP8 path e4m3 codes (one byte
+ *         each, 32 bytes per row and step).  Other n:m: the masked rows
+ *         [t][k] (dtype, zeros at pruned channels).
+ *  meta   2:4 only: per step and row four uint16 words at ((s * t_pad) + r)
+ *         * 4, word q holding the 16 channels 16q..16q+15 of the step as
+ *         four nibbles (block b in bits 4b..4b+3: lo | hi << 2, the two kept
+ *         in-block positions).
+ *  eta    [t] float32, the shift the call used.
+ *  scale  FP8 path only: [t] float32, each token's scale max|kept x_hat| / 448.
+ *  t_pad  rows per step of the 2:4 layout (t rounded up to 256); t otherwise.
+ *  bytes  the workspace size (spa_workspace_bytes(SPA_ENTRY_PREFILL, ...)).
+ * SPA_ERR_INVALID for arguments spa_workspace_bytes rejects, or a NULL out.
+ */
+typedef struct spa_operand_layout {
+  size_t vals, meta, eta, scale;
+  int32_t t_pad;
+  size_t bytes;
+} spa_operand_layout;
+spa_status spa_prefill_layout(int32_t t, int32_t k, int32_t dtype, const spa_prune_cfg* cfg,
+                              spa_operand_layout* out);
 
 /* Workspace bytes an entry point needs for these sizes (0 if none); 0 for
  * invalid arguments as well. */

@@ -62,3 +62,25 @@ def oracle_for(spec, x_cpu, w_cpu, f=None, eta_in=None, rows=None):
         pr["y"] = O.linear(pr, f32(w_cpu))
     pr["f"] = f
     return pr
+
+
+def tiled_operand(ws: torch.Tensor, layout: dict, t: int, k: int, fp8: bool, dtype: str):
+    """Read the 2:4 operand a prefill call left in its workspace (layout from
+    ``spa.prefill_layout``): per token row, the kept entries in ascending channel
+    order (e4m3 code bytes, or 16-bit storage bits), the kept in-block
+    positions decoded from the nibble words, and the FP8 scales (or None)."""
+    raw = ws.detach().cpu().numpy().view(np.uint8)
+    steps, t_pad = k // 64, layout["t_pad"]
+    if fp8:
+        v = raw[layout["vals"]:layout["vals"] + steps * t_pad * 32].reshape(steps, t_pad, 32)
+    else:
+        v = raw[layout["vals"]:layout["vals"] + steps * t_pad * 64].view(np.uint16).reshape(steps, t_pad, 32)
+    vals = v[:, :t, :].transpose(1, 0, 2).reshape(t, k // 2)
+    words = raw[layout["meta"]:layout["meta"] + steps * t_pad * 8].view(np.uint16).reshape(steps, t_pad, 4)
+    words = words[:, :t, :].transpose(1, 0, 2).reshape(t, k // 16).astype(np.int64)
+    nib = (words[:, :, None] >> (4 * np.arange(4))[None, None, :]) & 0xF          # [t, k/16, 4 blocks]
+    pos = np.stack([nib & 3, nib >> 2], axis=-1).reshape(t, k // 2).astype(np.uint8)
+    scale = None
+    if fp8:
+        scale = raw[layout["scale"]:layout["scale"] + 4 * t].view(np.float32).copy()
+    return vals, pos, scale

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "spa.h")
 LIB = os.path.join(ROOT, "activation_sparsification_amd", "libspa.so")
 
-SPA_OK, SPA_ERR_INVALID = 0, 1
+SPA_OK, SPA_ERR_INVALID, SPA_ERR_UNSUPPORTED = 0, 1, 2
 
 
 def _declared():
@@ -103,18 +103,15 @@ def test_prefill_limits(lib):
                                      1 << 40, None) == 2
 
 
-def test_decode_weight_limit(lib):
-    # 1..4 tokens read the channel-major weight: 2 GiB and more is rejected
+def test_decode_takes_large_channel_major_weights(lib):
+    # 2 GiB and more of channel-major weight (1..4 tokens, float32) is a
+    # supported decode: the workspace size is defined for it
     import activation_sparsification_amd._binding as B
-    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-    lib.sparse_linear_decode.restype = ctypes.c_int
-    lib.sparse_linear_decode.argtypes = [vp, i32, ctypes.POINTER(B._Weight), ctypes.POINTER(B._Cfg), vp, vp, vp,
-                                         vp, vp, sz, vp]
+    lib.spa_workspace_bytes.restype = ctypes.c_size_t
+    lib.spa_workspace_bytes.argtypes = [ctypes.c_int32] * 5 + [ctypes.POINTER(B._Cfg)]
     cfg = B.PruneConfig(8, 16).c()
-    for k, t, dt in [(262144, 1, 2), (262144, 4, 1), (131072, 2, 0)]:
-        wd = B._Weight(dt, 4096, k, None, 256, None, None)
-        assert lib.sparse_linear_decode(512, t, ctypes.byref(wd), ctypes.byref(cfg), None, 768, None, None, 1024,
-                                        1 << 40, None) == 2
+    for k, t, dt in [(262144, 1, 2), (262144, 4, 1), (131072, 2, 0), (1 << 24, 1, 2)]:
+        assert lib.spa_workspace_bytes(1, t, k, 4096, dt, ctypes.byref(cfg)) > 0, (k, t, dt)
 
 
 def test_linear_rejections_happen_before_any_launch(lib):
@@ -124,8 +121,8 @@ def test_linear_rejections_happen_before_any_launch(lib):
     L.prune_nm.restype = ctypes.c_int
     L.prune_nm.argtypes = [vp, i32, i32, i32, ctypes.POINTER(B._Cfg), vp, vp, vp, vp, vp, vp, vp, sz, vp]
     good = B.PruneConfig(2, 4).c()
-    # k not a multiple of 16 / of m, n > m, an unknown activation, null input
-    assert L.prune_nm(16, 2, 4, 60, ctypes.byref(good), None, None, 32, None, None, None, None, 0, None) == 1
+    # k not a multiple of m, n > m, an unknown activation, null input
+    assert L.prune_nm(16, 2, 4, 62, ctypes.byref(good), None, None, 32, None, None, None, None, 0, None) == 1
     bad = B.PruneConfig(5, 4).c()
     assert L.prune_nm(16, 2, 4, 64, ctypes.byref(bad), None, None, 32, None, None, None, None, 0, None) == 1
     st = ctypes.c_void_p(4096)
@@ -149,8 +146,9 @@ def test_fp8_rejections_happen_before_any_launch(lib):
     f = lib.sparse_linear_prefill_fp8
     f.restype = ctypes.c_int
     f.argtypes = [vp, i32, ctypes.POINTER(B._Weight), vp, vp, ctypes.POINTER(B._Cfg), vp, vp, vp, vp, vp, sz, vp]
-    assert lib.prepare_weight_fp8(256, 0, 8, 64, 512, 768, None) == SPA_ERR_INVALID   # float32 weight
-    assert lib.prepare_weight_fp8(256, 2, 8, 60, 512, 768, None) == SPA_ERR_INVALID   # k % 8 != 0
+    assert lib.prepare_weight_fp8(256, 0, 8, 64, 512, 768, None) == SPA_ERR_UNSUPPORTED   # float32 weight
+    assert lib.prepare_weight_fp8(256, 2, 8, 60, 512, 768, None) == SPA_ERR_UNSUPPORTED   # k % 8 != 0
+    assert lib.prepare_weight_fp8(256, 5, 8, 64, 512, 768, None) == SPA_ERR_INVALID       # unknown dtype
     assert lib.prepare_weight_fp8(256, 2, 8, 64, None, 768, None) == SPA_ERR_INVALID  # no codes buffer
     wd = B._Weight(2, 256, 4096, None, None, None, 1280)
     c24 = B.PruneConfig(2, 4, shift="token_mean").c()
@@ -163,3 +161,50 @@ def test_fp8_rejections_happen_before_any_launch(lib):
     big = B._Weight(2, 256, (1 << 23) + 64, None, None, None, 1280)
     assert f(512, 4, ctypes.byref(big), 2048, 2304, ctypes.byref(c24), *args) == 2
     assert f(512, 0, ctypes.byref(wd), 2048, 2304, ctypes.byref(c24), *args) == SPA_OK   # no tokens
+
+
+def test_valid_but_unbuilt_shapes_are_unsupported(lib):
+    # arguments that are valid (whole m-blocks, supported n:m and dtypes) but
+    # outside the shapes the kernels are built for: SPA_ERR_UNSUPPORTED, before
+    # any launch; the same shapes with a broken argument stay SPA_ERR_INVALID
+    import activation_sparsification_amd._binding as B
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L = lib
+    L.prune_nm.restype = ctypes.c_int
+    L.prune_nm.argtypes = [vp, i32, i32, i32, ctypes.POINTER(B._Cfg), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    c24 = B.PruneConfig(2, 4).c()
+    # k = 36: nine 2:4 blocks, not whole 16-channel segments
+    assert L.prune_nm(16, 2, 4, 36, ctypes.byref(c24), None, None, 32, None, None, None, None, 0, None) == 2
+    assert L.prune_nm(None, 2, 4, 36, ctypes.byref(c24), None, None, 32, None, None, None, None, 0, None) == 1
+    for name in ("sparse_linear_decode", "sparse_linear_prefill"):
+        f = getattr(L, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [vp, i32, ctypes.POINTER(B._Weight), ctypes.POINTER(B._Cfg), vp, vp, vp, vp, vp, sz, vp]
+    args = (None, 768, None, None, 1024, 1 << 40, None)
+    # decode, one bf16 token, 12 outputs: rows of the channel-major weight are not 16-byte pieces
+    wd = B._Weight(2, 12, 4096, None, 256, None, None)
+    assert L.sparse_linear_decode(512, 1, ctypes.byref(wd), ctypes.byref(c24), *args) == 2
+    wd = B._Weight(2, 12, 4096, None, None, None, None)                 # no channel-major weight: invalid
+    assert L.sparse_linear_decode(512, 1, ctypes.byref(wd), ctypes.byref(c24), *args) == 1
+    # decode with k = 36 (valid 2:4 blocks)
+    wd = B._Weight(2, 64, 36, None, 256, None, None)
+    assert L.sparse_linear_decode(512, 1, ctypes.byref(wd), ctypes.byref(c24), *args) == 2
+    # prefill with k = 96: whole segments, not whole 64-channel GEMM steps
+    wd = B._Weight(2, 64, 96, 256, None, None, None)
+    assert L.sparse_linear_prefill(512, 4, ctypes.byref(wd), ctypes.byref(c24), *args) == 2
+    wd = B._Weight(2, 64, 98, 256, None, None, None)                    # 98 % 4 != 0: invalid
+    assert L.sparse_linear_prefill(512, 4, ctypes.byref(wd), ctypes.byref(c24), *args) == 1
+    # the static shift table's calibration reads rows in 16-channel pieces
+    L.spa_eta_calibrate.restype = ctypes.c_int
+    L.spa_eta_calibrate.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, vp]
+    assert L.spa_eta_calibrate(512, 2, 4, 24, 1024, 10, 2048, 4096, None) == 2
+    assert L.spa_eta_calibrate(512, 2, 4, 0, 1024, 10, 2048, 4096, None) == 1
+    # the squared-ReLU FFN: hidden 96, ffn 96, or float32
+    L.sparse_ffn_relu2_prefill.restype = ctypes.c_int
+    L.sparse_ffn_relu2_prefill.argtypes = [vp, i32, ctypes.POINTER(B._Weight), ctypes.POINTER(B._Weight), vp, vp,
+                                           vp, sz, vp]
+    for dt, hidden, ffn, want in [(2, 96, 128, 2), (2, 128, 96, 2), (0, 128, 128, 2), (2, 128, 98, 1)]:
+        up = B._Weight(dt, ffn, hidden, 256, None, None, None)
+        dn = B._Weight(dt, 64, ffn, 512, None, None, None)
+        assert L.sparse_ffn_relu2_prefill(768, 4, ctypes.byref(up), ctypes.byref(dn), 1024, None, 1280, 1 << 40,
+                                          None) == want, (dt, hidden, ffn)

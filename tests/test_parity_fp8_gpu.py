@@ -1,8 +1,10 @@
 """GPU parity of the FP8 2:4 prefill against the oracle.
 
 prepare_weight_fp8: codes and row scales bit for bit.  The pruned prefill
-with FP8 operands: in-block positions bit for bit, nu within 1e-6, y within
-the 16-bit tolerance of the oracle's FP8 product (the same e4m3 codes and
+with FP8 operands: in-block positions bit for bit; the activation operand
+the GEMM reads (per-token scales, every kept e4m3 code, the position words)
+bit for bit, read back from the workspace; nu within 1e-6; y within the
+16-bit tolerance of the oracle's FP8 product (the same e4m3 codes and
 scales, summed in float64).
 """
 import numpy as np
@@ -11,7 +13,7 @@ import torch
 
 import workloads as wl
 from oracle import nm_oracle as O
-from gpu_util import f32
+from gpu_util import f32, tiled_operand
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +59,11 @@ FP8_CASES = [
     wl.SPECS["prefill"].with_(name="fp8_none", t=64, k=256, n_out=264, shift="none"),
     wl.SPECS["batched"].with_(name="fp8_clact", t=96, k=512, n_out=264, n=2, m=4),
     wl.SPECS["relu2_fused"].with_(name="fp8_relu2", t=136, k=1024, n_out=264),
+    # every row's largest |x - eta| sits on a channel of tiny weights, which
+    # the weight-aware score prunes: the token scale must come from the kept
+    # entries (quantisation follows sparsification)
+    wl.SPECS["prefill"].with_(name="fp8_weight_pruned_max", t=70, k=512, n_out=136, score="weight", alpha=1.0,
+                              n_outliers=0),
 ]
 
 
@@ -73,6 +80,9 @@ def test_prefill_fp8_parity(spec):
     x, w = wl.make_inputs(spec)
     if spec.shift == "token_mean" and spec.t > 2:
         x[1] = x[1, 0]                                           # a constant row: x - eta == 0, scale 0
+    if spec.name == "fp8_weight_pruned_max":
+        x[:, 9] = 12.0
+        w[:, 9] *= 1e-3
     eta_in = wl.make_eta(spec.t, 9) if spec.shift == "given" else None
     print(f"[fp8 prefill] {spec.name}: t={spec.t} k={spec.k} n_out={spec.n_out} {spec.score} {spec.shift}",
           flush=True)
@@ -80,13 +90,30 @@ def test_prefill_fp8_parity(spec):
     pw = spa.prepare_weight(wd, spec.alpha, want_wt=False)
     w8 = spa.prepare_weight_fp8(wd)
     f = f32(pw.chan_scale) if spec.score == "weight" else None
+    if f is not None:
+        assert np.array_equal(f.view(np.uint32), O.channel_factor(f32(w), spec.alpha).view(np.uint32))
     pr = _fp8_oracle(spec, x, w, f=f, eta_in=eta_in)
-    y, idx, nu = spa.sparse_linear_prefill_fp8(x.to(dev), pw, w8, _cfg(spec),
+    cfg = _cfg(spec)
+    ws = spa.workspace(2, spec.t, spec.k, spec.n_out, x.dtype, cfg, dev)
+    y, idx, nu = spa.sparse_linear_prefill_fp8(x.to(dev), pw, w8, cfg,
                                                eta_in=None if eta_in is None else eta_in.to(dev), want_idx=True,
-                                               want_nu=True)
+                                               want_nu=True, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), pr["idx"]), "FP8 prefill masks differ"
     assert np.allclose(f32(nu), pr["nu"], rtol=1e-6, atol=0)
+    # the activation operand the GEMM read: per-token scales, every kept e4m3
+    # code and the position words, bit for bit
+    codes, pos, sx = tiled_operand(ws, spa.prefill_layout(spec.t, spec.k, x.dtype, cfg), spec.t, spec.k, True,
+                                   spec.dtype)
+    assert np.array_equal(sx.view(np.uint32), pr["sx"].view(np.uint32)), "FP8 token scales differ"
+    keep = pr["keep"].reshape(spec.t, spec.k)
+    want_codes = pr["qx"][keep].reshape(spec.t, spec.k // 2)
+    assert np.array_equal(codes, want_codes), f"{int((codes != want_codes).sum())} e4m3 activation codes differ"
+    assert np.array_equal(pos, pr["idx"]), "position words differ"
+    if spec.name == "fp8_weight_pruned_max":                     # the two scale readings differ on every row
+        amax = np.abs(pr["xhat"]).max(axis=1)
+        nz = amax > 0
+        assert (pr["sx"][nz] < amax[nz] / np.float32(448.0)).all()
     err = O.rowwise_error(f32(y), pr["y"])
     assert err <= O.TOLERANCE[spec.dtype], err
 
@@ -112,7 +139,9 @@ def test_prefill_fp8_full_size_sampled():
     wd = w.to(dev)
     pw = spa.prepare_weight(wd, spec.alpha, want_wt=False)
     w8 = spa.prepare_weight_fp8(wd)
-    y, idx, nu = spa.sparse_linear_prefill_fp8(x.to(dev), pw, w8, _cfg(spec), want_idx=True, want_nu=True)
+    cfg = _cfg(spec)
+    wsp = spa.workspace(2, spec.t, spec.k, spec.n_out, x.dtype, cfg, dev)
+    y, idx, nu = spa.sparse_linear_prefill_fp8(x.to(dev), pw, w8, cfg, want_idx=True, want_nu=True, ws=wsp)
     torch.cuda.synchronize()
     rng = np.random.default_rng(3)
     rows = np.unique(np.concatenate([rng.choice(spec.t, 24, replace=False), [0, spec.t - 1]]))
@@ -121,6 +150,11 @@ def test_prefill_fp8_full_size_sampled():
     pr = _fp8_oracle(spec, xs, ws)
     assert np.array_equal(idx.cpu().numpy()[rows], pr["idx"])
     assert np.allclose(f32(nu)[rows], pr["nu"], rtol=1e-6, atol=0)
+    codes, pos, sx = tiled_operand(wsp, spa.prefill_layout(spec.t, spec.k, x.dtype, cfg), spec.t, spec.k, True,
+                                   spec.dtype)
+    assert np.array_equal(sx[rows].view(np.uint32), pr["sx"].view(np.uint32)), "FP8 token scales differ"
+    want = pr["qx"][pr["keep"]].reshape(rows.size, spec.k // 2)
+    assert np.array_equal(codes[rows], want), "e4m3 activation codes differ"
     q, s = O.fp8_rows(f32(ws))
     assert np.array_equal(w8.codes.cpu().numpy()[cols], q)
     assert np.array_equal(f32(w8.scale)[cols].view(np.uint32), s.view(np.uint32))

@@ -11,7 +11,7 @@ import torch
 
 import workloads as wl
 from oracle import nm_oracle as O
-from gpu_util import TORCH_DT, check_ffn_masks, f32, oracle_for, storage_bits, tensor_bits
+from gpu_util import TORCH_DT, f32, oracle_for, storage_bits, tensor_bits, tiled_operand
 
 pytestmark = pytest.mark.gpu
 
@@ -67,16 +67,39 @@ def _ffn_inputs(dtype, t, hidden, ffn, n_out, seed):
     return x, w_up, w_dn
 
 
+def ffn_up_reference(x, w_up, dev):
+    """u = x W_up^T from the library's dense GEMM (a 4:4 prefill keeps every
+    channel): the same matrix-core main loop and rounding as the fused
+    up-projection, whose epilogue squares and prunes this u."""
+    pw = spa.PreparedWeight(w_up, None, None, None)
+    u, _, _ = spa.sparse_linear_prefill(x, pw, spa.PruneConfig(4, 4))
+    return u
+
+
 @pytest.mark.parametrize("dtype,t,hidden,ffn,n_out", FFN_CASES)
 def test_ffn_relu2(dtype, t, hidden, ffn, n_out):
     dev = _dev()
     x, w_up, w_dn = _ffn_inputs(dtype, t, hidden, ffn, n_out, seed=t)
-    y, idx = spa.sparse_ffn_relu2_prefill(x.to(dev), w_up.to(dev), w_dn.to(dev), want_idx=True)
+    xd, upd = x.to(dev), w_up.to(dev)
+    nb = spa.lib().spa_ffn_workspace_bytes(t, ffn, spa._binding.DTYPE[x.dtype])
+    y, idx = spa.sparse_ffn_relu2_prefill(xd, upd, w_dn.to(dev), want_idx=True)
+    u = ffn_up_reference(xd, upd, dev)
     torch.cuda.synchronize()
-    pr = O.ffn_relu2(f32(x), f32(w_up), f32(w_dn), dtype)
-    frac = check_ffn_masks(idx.cpu().numpy(), O.squared_relu(pr["u"], dtype), pr["idx"])
-    assert frac < 0.01, frac
-    err = O.rowwise_error(f32(y), pr["y"])
+    ws = spa._binding._WS_CACHE[(str(dev), "ffn", nb)]
+    # the oracle prunes the squared ReLU of the GPU's own u: positions and the
+    # packed operand of the down-projection bit for bit
+    pr = O.prune(f32(u), dtype, 2, 4, act="relu2")
+    assert np.array_equal(idx.cpu().numpy(), pr["idx"]), "fused FFN positions differ"
+    t_pad = (t + 255) // 256 * 256
+    lay = {"vals": 0, "meta": (t_pad * ffn + 255) // 256 * 256, "t_pad": t_pad}
+    vals, pos, _ = tiled_operand(ws, lay, t, ffn, False, dtype)
+    assert np.array_equal(vals, storage_bits(pr["vals"], dtype)), "fused FFN packed operand differs"
+    assert np.array_equal(pos, pr["idx"])
+    # y against the float64 oracle of the whole FFN, and against the oracle's
+    # down-projection of the GPU's activation
+    ref = O.ffn_relu2(f32(x), f32(w_up), f32(w_dn), dtype)
+    assert O.rowwise_error(f32(y), ref["y"]) <= O.TOLERANCE[dtype]
+    err = O.rowwise_error(f32(y), O.linear(pr, f32(w_dn), s=np.zeros(n_out)))
     assert err <= O.TOLERANCE[dtype], err
 
 
@@ -121,7 +144,9 @@ def test_var_running_average(label, entry, spec):
         vals, idx, eta, nu = spa.prune_nm(x.to(dev), cfg, chan_scale=None if f is None else torch.from_numpy(f).to(dev))
     else:
         pw = spa.prepare_weight(w.to(dev), spec.alpha, want_wt=entry == "decode")
-        f = f32(pw.chan_scale) if spec.score == "weight" else None
+        f = O.channel_factor(f32(w), spec.alpha) if spec.score == "weight" else None
+        if f is not None:
+            assert np.array_equal(f32(pw.chan_scale).view(np.uint32), f.view(np.uint32))
         fn = spa.sparse_linear_decode if entry == "decode" else spa.sparse_linear_prefill
         y, idx, nu = fn(x.to(dev), pw, cfg, want_idx=True, want_nu=True)
     torch.cuda.synchronize()
@@ -180,7 +205,9 @@ def test_static_shift_drives_decode():
     pw = spa.prepare_weight(w.to(dev), spec.alpha)
     y, idx, nu = spa.sparse_linear_decode(x.to(dev), pw, _cfg(spec), eta_in=eta, want_idx=True, want_nu=True)
     torch.cuda.synchronize()
-    pr = oracle_for(spec, x, w, f=f32(pw.chan_scale), eta_in=torch.from_numpy(O.eta_lookup(table, ids)))
+    f = O.channel_factor(f32(w), spec.alpha)
+    assert np.array_equal(f32(pw.chan_scale).view(np.uint32), f.view(np.uint32))
+    pr = oracle_for(spec, x, w, f=f, eta_in=torch.from_numpy(O.eta_lookup(table, ids)))
     assert np.array_equal(idx.cpu().numpy(), pr["idx"])
     assert O.rowwise_error(f32(y), pr["y"]) <= O.TOLERANCE[spec.dtype]
 
@@ -390,6 +417,13 @@ DECODE_CASES.append(wl.SPECS["batched"].with_(name="mm_bf16_weight_mean", t=12, 
                                               n=2, m=4, score="weight", alpha=0.5, shift="token_mean",
                                               var_rescale=True))
 DECODE_CASES.append(wl.SPECS["decode"].with_(name="decode_given_shift", t=2, k=512, n_out=256, shift="given"))
+# the fused kernel with more m-blocks per channel split than threads (its row
+# list is built over two passes): float32 one token, a narrow 16-bit output,
+# and two tokens with one split per column tile
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="fused_t1_f32_two_passes", t=1, k=32768, n_out=4096, dtype="f32"))
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="fused_t1_bf16_2of4_two_passes", t=1, k=32768, n_out=2048, n=2,
+                                             m=4))
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="fused_t2_two_passes", t=2, k=8192, n_out=12288))
 # the squared-ReLU input transform on every decode kernel: one token (wide and
 # narrow outputs), 2-4 tokens, float32, and the matrix-core path
 ACT = dict(act="relu2", x_dist="normal", n_outliers=0)
@@ -496,12 +530,26 @@ def test_prefill_parity(spec):
     eta_in = wl.make_eta(spec.t, 9) if spec.shift == "given" else None
     pw = spa.prepare_weight(w.to(dev), spec.alpha, want_wt=False)
     f = f32(pw.chan_scale) if spec.score == "weight" else None
+    if f is not None:
+        assert np.array_equal(f.view(np.uint32), O.channel_factor(f32(w), spec.alpha).view(np.uint32))
     pr = oracle_for(spec, x, w, f=f, eta_in=eta_in)
-    y, idx, nu = spa.sparse_linear_prefill(x.to(dev), pw, _cfg(spec),
-                                           eta_in=None if eta_in is None else eta_in.to(dev), want_idx=True,
-                                           want_nu=True)
+    cfg = _cfg(spec)
+    ws = spa.workspace(2, spec.t, spec.k, spec.n_out, x.dtype, cfg, dev)
+    y, idx, nu = spa.sparse_linear_prefill(x.to(dev), pw, cfg, eta_in=None if eta_in is None else eta_in.to(dev),
+                                           want_idx=True, want_nu=True, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), pr["idx"]), "prefill masks differ"
     assert np.allclose(f32(nu), pr["nu"], rtol=1e-6, atol=0)
+    # the operand the GEMM read, from the workspace: 2:4 packed values and
+    # position words, or the masked rows of other n:m, bit for bit
+    lay = spa.prefill_layout(spec.t, spec.k, x.dtype, cfg)
+    if spec.n == 2 and spec.m == 4:
+        vals, pos, _ = tiled_operand(ws, lay, spec.t, spec.k, False, spec.dtype)
+        assert np.array_equal(vals, storage_bits(pr["vals"], spec.dtype)), "packed operand differs"
+        assert np.array_equal(pos, pr["idx"]), "position words differ"
+    else:
+        raw = ws.cpu().numpy().view(np.uint8)[lay["vals"]:lay["vals"] + spec.t * spec.k * 2].view(np.uint16)
+        masked = np.where(pr["keep"], pr["xhat"], np.float32(0.0))
+        assert np.array_equal(raw.reshape(spec.t, spec.k), storage_bits(masked, spec.dtype)), "masked rows differ"
     err = O.rowwise_error(f32(y), pr["y"])
     assert err <= O.TOLERANCE[spec.dtype], err
