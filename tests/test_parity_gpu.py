@@ -549,7 +549,7 @@ def test_prefill_parity(spec):
         assert np.array_equal(pos, pr["idx"]), "position words differ"
     else:
         raw = ws.cpu().numpy().view(np.uint8)[lay["vals"]:lay["vals"] + spec.t * spec.k * 2].view(np.uint16)
-        masked = np.where(pr["keep"], pr["xhat"], np.float32(0.0))
+        masked = O.round_to_dtype(np.where(pr["keep"], pr["xhat"], np.float32(0.0)), spec.dtype)
         assert np.array_equal(raw.reshape(spec.t, spec.k), storage_bits(masked, spec.dtype)), "masked rows differ"
     err = O.rowwise_error(f32(y), pr["y"])
     assert err <= O.TOLERANCE[spec.dtype], err
