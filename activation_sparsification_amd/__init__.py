@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     prepare_weight_fp8,
     prune_nm,
     sparse_linear_decode,
+    sparse_linear_decode_static,
     sparse_linear_prefill,
     sparse_linear_prefill_fp8,
     sparse_ffn_relu2_prefill,

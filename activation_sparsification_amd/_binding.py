@@ -16,7 +16,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspa.so")
 
-SPA_OK, SPA_ERR_INVALID, SPA_ERR_UNSUPPORTED, SPA_ERR_HIP = 0, 1, 2, 3
+SPA_OK, SPA_ERR_INVALID, SPA_ERR_UNSUPPORTED, SPA_ERR_HIP, SPA_ERR_SCRATCH = 0, 1, 2, 3, 4
 DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 SCORE = {"magnitude": 0, "weight": 1, "clact": 2}
 SHIFT = {"none": 0, "token_mean": 1, "given": 2}
@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [vp, i32, ctypes.POINTER(_Weight), ctypes.POINTER(_Cfg), vp, vp, vp, vp, vp, sz, vp]
+        L.sparse_linear_decode_static.restype = ctypes.c_int
+        L.sparse_linear_decode_static.argtypes = [vp, i32, ctypes.POINTER(_Weight), ctypes.POINTER(_Cfg), vp, vp,
+                                                  vp, vp, vp]
         _lib = L
     return _lib
 
@@ -106,7 +109,7 @@ EXPORTS = ("prepare_weight", "prune_nm", "sparse_linear_decode", "sparse_linear_
            "spa_workspace_bytes", "spa_status_str", "spa_meta_row_bytes", "spa_encode_meta", "spa_decode_meta",
            "prepare_amber", "spa_amber_workspace_bytes", "spa_eta_calibrate", "spa_eta_table", "spa_eta_lookup",
            "sparse_ffn_relu2_prefill", "spa_ffn_workspace_bytes", "prepare_weight_fp8",
-           "sparse_linear_prefill_fp8", "spa_prefill_layout")
+           "sparse_linear_prefill_fp8", "spa_prefill_layout", "sparse_linear_decode_static")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -351,6 +354,21 @@ def sparse_linear_decode(x, pw: PreparedWeight, cfg: PruneConfig, eta_in=None, w
                          out=None, ws=None, wt=None):
     """Fused prune + row-skipping GEMV for 1..32 tokens.  Returns ``(y, idx, nu)``."""
     return _linear("sparse_linear_decode", ENTRY_DECODE, x, pw, cfg, eta_in, want_idx, want_nu, out, ws, wt)
+
+
+def sparse_linear_decode_static(x, pw: PreparedWeight, cfg: PruneConfig, eta_in=None, want_idx=False, want_nu=False,
+                                out=None, wt=None):
+    """sparse_linear_decode on the library's static per-GPU scratch (no workspace).  Returns ``(y, idx, nu)``."""
+    dev = _dev(x)
+    t, k = x.shape
+    y = torch.empty((t, pw.n_out), dtype=x.dtype, device=dev) if out is None else out
+    idx = torch.empty((t, k // cfg.m * cfg.n), dtype=torch.uint8, device=dev) if want_idx else None
+    nu = torch.empty(t, dtype=torch.float32, device=dev) if want_nu else None
+    c = cfg.c()
+    wd = pw.c(wt=wt)
+    _check(lib().sparse_linear_decode_static(_ptr(x), t, ctypes.byref(wd), ctypes.byref(c), _ptr(eta_in), _ptr(y),
+                                             _ptr(idx), _ptr(nu), _stream(dev)), "sparse_linear_decode_static")
+    return y, idx, nu
 
 
 def sparse_linear_prefill(x, pw: PreparedWeight, cfg: PruneConfig, eta_in=None, want_idx=False, want_nu=False,

@@ -3,8 +3,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "spa.h"
 #include "spa_launch.h"
+
+// Device scratch of sparse_linear_decode_static, one copy per GPU, held until
+// the process ends.  The first SPA_STATIC_COUNTER_BYTES hold the split
+// counters (zero between calls); the rest is carved like a decode workspace.
+// In host code `scratch` names a host-side stand-in: kernels get the device
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[SPA_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -182,6 +191,7 @@ const char* spa_status_str(spa_status s) {
     case SPA_ERR_INVALID: return "invalid argument";
     case SPA_ERR_UNSUPPORTED: return "unsupported combination";
     case SPA_ERR_HIP: return "HIP runtime error";
+    case SPA_ERR_SCRATCH: return "needs more device scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -268,16 +278,16 @@ spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const sp
   return hip_status(spa::launch_prune(dtype, a, st));
 }
 
-spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
-                                const float* eta_in, void* y, uint8_t* idx_out, float* nu_out, void* workspace,
-                                size_t workspace_bytes, void* stream) {
-  if (spa_status s = check_linear(x, t, w, cfg, eta_in, y, true)) return s;
-  if (w->dtype == SPA_F32 && t > 8) return SPA_ERR_UNSUPPORTED;
-  spa::DecodeArgs a{};
-  const size_t need = spa::decode_workspace(t, w->k, w->n_out, w->dtype, cfg->n, cfg->m, cfg->score, cfg->shift,
-                                            cfg->var_rescale, &a);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SPA_ERR_INVALID;
-  char* base = static_cast<char*>(workspace);
+}  // extern "C"
+
+namespace {
+
+// The decode call once its workspace is placed: `base` holds the plan's
+// carve-up (a is the plan, offsets relative to base); `counters`, when not
+// NULL, replaces the plan's split counters (which must read zero).
+spa_status decode_launch(spa::DecodeArgs& a, char* base, unsigned* counters, const void* x, int32_t t,
+                         const spa_weight* w, const spa_prune_cfg* cfg, const float* eta_in, void* y,
+                         uint8_t* idx_out, float* nu_out, void* stream) {
   auto fix = [&](auto*& ptr) { ptr = reinterpret_cast<std::remove_reference_t<decltype(ptr)>>(base + reinterpret_cast<uintptr_t>(ptr)); };
   fix(a.partial);
   fix(a.stats);
@@ -286,6 +296,7 @@ spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, c
   if (t > 4 && w->dtype != SPA_F32) {                // matrix-core path (the dense offset is 0)
     fix(a.dense);
   }
+  if (counters) a.counters = counters;
   a.x = x;
   a.act = cfg->act;
   a.var_in = cfg->var_state;
@@ -299,6 +310,66 @@ spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, c
   a.idx_out = idx_out;
   a.nu_out = nu_out;
   return hip_status(spa::launch_decode(w->dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxDevices];
+
+__global__ void __launch_bounds__(256) k_zero_words(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) p[i] = 0u;
+}
+
+// This GPU's scratch: the device address of `scratch` for the current
+// device, looked up once per device; its counter region is cleared then, on
+// `st`, by a fill kernel (no memset node, so a captured first call is safe).
+spa_status scratch_of(hipStream_t st, char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SPA_ERR_HIP;
+    hipLaunchKernelGGL(k_zero_words, dim3(64), dim3(256), 0, st, static_cast<uint32_t*>(ptr),
+                       (uint32_t)(SPA_STATIC_COUNTER_BYTES / 4));
+    if (hipGetLastError() != hipSuccess) return SPA_ERR_HIP;
+    g_scratch[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return SPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
+                                const float* eta_in, void* y, uint8_t* idx_out, float* nu_out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (spa_status s = check_linear(x, t, w, cfg, eta_in, y, true)) return s;
+  if (w->dtype == SPA_F32 && t > 8) return SPA_ERR_UNSUPPORTED;
+  spa::DecodeArgs a{};
+  const size_t need = spa::decode_workspace(t, w->k, w->n_out, w->dtype, cfg->n, cfg->m, cfg->score, cfg->shift,
+                                            cfg->var_rescale, &a);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SPA_ERR_INVALID;
+  return decode_launch(a, static_cast<char*>(workspace), nullptr, x, t, w, cfg, eta_in, y, idx_out, nu_out, stream);
+}
+
+spa_status sparse_linear_decode_static(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
+                                       const float* eta_in, void* y, uint8_t* idx_out, float* nu_out, void* stream) {
+  if (spa_status s = check_linear(x, t, w, cfg, eta_in, y, true)) return s;
+  if (w->dtype == SPA_F32 && t > 8) return SPA_ERR_UNSUPPORTED;
+  spa::DecodeArgs a{};
+  const size_t need = spa::decode_workspace(t, w->k, w->n_out, w->dtype, cfg->n, cfg->m, cfg->score, cfg->shift,
+                                            cfg->var_rescale, &a);
+  if (need > SPA_STATIC_SCRATCH_BYTES - SPA_STATIC_COUNTER_BYTES ||
+      (size_t)a.tiles * 4 > SPA_STATIC_COUNTER_BYTES)
+    return SPA_ERR_SCRATCH;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = nullptr;
+  if (spa_status s = scratch_of(st, &base)) return s;
+  return decode_launch(a, base + SPA_STATIC_COUNTER_BYTES, reinterpret_cast<unsigned*>(base), x, t, w, cfg, eta_in,
+                       y, idx_out, nu_out, stream);
 }
 
 spa_status sparse_linear_prefill(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,

@@ -68,8 +68,16 @@ typedef enum spa_status {
   SPA_OK = 0,
   SPA_ERR_INVALID = 1,      /* rejected argument; nothing launched */
   SPA_ERR_UNSUPPORTED = 2,  /* valid combination the library does not implement */
-  SPA_ERR_HIP = 3           /* a HIP launch or runtime call failed */
+  SPA_ERR_HIP = 3,          /* a HIP launch or runtime call failed */
+  SPA_ERR_SCRATCH = 4       /* sparse_linear_decode_static: the call needs more
+                               than the static scratch buffer holds */
 } spa_status;
+
+/* Size of the per-GPU device scratch of sparse_linear_decode_static (held
+ * from its first call on a GPU until the process ends), and of its leading
+ * split-counter region. */
+#define SPA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+#define SPA_STATIC_COUNTER_BYTES ((size_t)1 << 20)
 
 enum { SPA_F32 = 0, SPA_F16 = 1, SPA_BF16 = 2 };
 enum { SPA_SCORE_MAGNITUDE = 0, SPA_SCORE_WEIGHT = 1, SPA_SCORE_CLACT = 2 };
@@ -215,6 +223,28 @@ spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const sp
 spa_status sparse_linear_decode(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
                                 const float* eta_in, void* y, uint8_t* idx_out, float* nu_out,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sparse_linear_decode_static -- sparse_linear_decode without a caller
+ * workspace, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * call allocates nothing: its partial sums, variance sums, shift and split
+ * counters live in one static device array per GPU of
+ * SPA_STATIC_SCRATCH_BYTES (the first SPA_STATIC_COUNTER_BYTES are the
+ * counters), which the library looks up once per GPU (with the current
+ * device set to the stream's device) and clears there with a fill kernel on
+ * `stream`.  Same kernels, arguments and results as sparse_linear_decode.
+ *  - Returns SPA_ERR_SCRATCH, before any launch, when the call's decode
+ *    workspace (spa_workspace_bytes(SPA_ENTRY_DECODE, ...)) exceeds
+ *    SPA_STATIC_SCRATCH_BYTES - SPA_STATIC_COUNTER_BYTES or its column tiles
+ *    need more than SPA_STATIC_COUNTER_BYTES / 4 counters.
+ *  - Every call on a GPU shares that GPU's array and leaves its counters at
+ *    zero; calls that overlap in time on one GPU (several streams, several
+ *    threads) race and give undefined results.
+ */
+spa_status sparse_linear_decode_static(const void* x, int32_t t, const spa_weight* w, const spa_prune_cfg* cfg,
+                                       const float* eta_in, void* y, uint8_t* idx_out, float* nu_out,
+                                       void* stream);
 
 /*
  * sparse_linear_prefill -- prompt-size batches, t >= 1 (16-bit dtypes):

@@ -56,7 +56,7 @@ def test_binding_lists_every_declared_function():
 
 
 def test_status_strings(lib):
-    for code in range(4):
+    for code in range(5):
         assert lib.spa_status_str(code)
     assert lib.spa_status_str(SPA_ERR_INVALID) != lib.spa_status_str(SPA_OK)
 
@@ -208,3 +208,17 @@ def test_valid_but_unbuilt_shapes_are_unsupported(lib):
         dn = B._Weight(dt, 64, ffn, 512, None, None, None)
         assert L.sparse_ffn_relu2_prefill(768, 4, ctypes.byref(up), ctypes.byref(dn), 1024, None, 1280, 1 << 40,
                                           None) == want, (dt, hidden, ffn)
+
+
+def test_static_decode_rejects_oversize_calls_before_any_launch(lib):
+    # 32 tokens of 2^20 channels: the matrix-core path's masked activations
+    # alone need 64 MiB, more than the static scratch holds
+    import activation_sparsification_amd._binding as B
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    f = lib.sparse_linear_decode_static
+    f.restype = ctypes.c_int
+    f.argtypes = [vp, i32, ctypes.POINTER(B._Weight), ctypes.POINTER(B._Cfg), vp, vp, vp, vp, vp]
+    cfg = B.PruneConfig(8, 16).c()
+    wd = B._Weight(1, 64, 1 << 20, 256, None, None, None)
+    assert f(512, 32, ctypes.byref(wd), ctypes.byref(cfg), None, 768, None, None, None) == 4
+    assert f(None, 32, ctypes.byref(wd), ctypes.byref(cfg), None, 768, None, None, None) == SPA_ERR_INVALID
