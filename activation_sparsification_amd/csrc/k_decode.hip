@@ -782,138 +782,144 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Pruning pass of the matrix-core decode (t > 4): few token rows, so the
-// work is cut by channels instead of rows.  A workgroup owns kPruneChan
-// channels (kPruneChan/m blocks) for every token of the call: it stages
-// x_hat = x - eta for them in LDS, forms the channel factors there (the CLACT
-// column energy needs every token of a channel, which this workgroup holds),
-// then one thread per (token, block) scores, selects the top n with the
-// selection network and writes the masked values, the kept positions and its
-// four variance sums.  The sums of the blocks are added in block order per
-// (chunk, token); the matrix-core pass folds the chunks into nu.
+// work is cut by channels and by token.  Workgroup (chunk, quarter) owns
+// kPruneChan channels and the tokens quarter, quarter + 4, ...: it stages
+// x_hat = x - eta of its channels for every token in LDS (each thread one
+// channel of eight tokens, all of its loads in flight), since the CLACT
+// column energy needs every token of a channel.  16 waves: wave w owns the 64
+// channels 64 (w % 4) .. +63 of the chunk, one per lane, and the quarter's
+// tokens w / 4 and w / 4 + 4 (two tokens of serial work per wave).  A lane
+// forms its channel factor, and for each of its tokens scores its channel,
+// parks the score in the wave's LDS slots, reads its m-block's scores back
+// (broadcast 16-byte reads) and keeps the channel when fewer than n of them
+// beat it (larger, or equal at a lower position).  It writes the masked
+// values, the kept positions and each token's four variance sums of the
+// chunk (the four channel groups added in order); the matrix-core pass
+// folds the chunks into nu.
 //
 // The masked activations are written in the GEMM's operand order ("fragment
 // order"): for 64-channel step s, token block tb (16 tokens) and window h,
 // one 1 KB run where lane d = m + 16 g holds channels 64 s + 16 g + 8 h .. +7
-// of token 16 tb + m.  Token lanes past t are never written or read.
+// of token 16 tb + m.  Token lanes past t, and channel groups past k, are
+// never written or read.
 // ---------------------------------------------------------------------------
+constexpr int kPcThreads = 1024;
+
 __device__ __forceinline__ size_t frag_offset(int step, int tb, int ntb, int h, int lane) {
   return ((((size_t)step * ntb + tb) * 2 + h) * 64 + lane) * 8;   // in 16-bit elements
 }
 
 template <int DT, int M>
-__global__ void __launch_bounds__(256) k_prune_cols(DecodeArgs a) {
+__global__ void __launch_bounds__(kPcThreads) k_prune_cols(DecodeArgs a) {
   using T = typename Dt<DT>::T;
-  constexpr int CH = kPruneChan, NB = CH / M;
-  __shared__ float s_x[kMaxTok][CH + 1];
-  __shared__ float s_f[CH];
-  __shared__ double s_st[kMaxTok][NB][4];
+  constexpr int CH = kPruneChan, NW = kPcThreads / 64;
+  static_assert(CH == 256 && NW == 16, "four waves per 64-channel group, one channel per lane");
+  __shared__ float s_x[kMaxTok][CH];
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[NW][64];   // per wave: the current token's scores
+  __shared__ __attribute__((aligned(16))) uint16_t s_mv[NW][64];   // per wave: its masked values
+  __shared__ double s_st[4][kMaxTok / 4][4];
   const int T_ = a.t, K = a.k;
   const int ntb = (T_ + 15) / 16;
-  const int c0 = blockIdx.x * CH;
-  static_assert(CH == 256, "one channel per thread");
+  const int c0 = blockIdx.x * CH, quarter = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   {
-    // thread c stages channel c0 + c of every token: all loads issued before
-    // any is used (buffer loads; offsets past the end read zeros)
-    const int c = threadIdx.x, ch = c0 + c;
+    // thread (c, p) stages channel c0 + c of tokens p, p + 4, ...: all loads
+    // issued before any is used (buffer loads; offsets past the end read
+    // zeros); rows past t are zero
+    const int c = threadIdx.x % CH, p = threadIdx.x / CH, ch = c0 + c;
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), (short)0, T_ * K * 2, kBufferWord3);
-    uint32_t raw[kMaxTok];
+    uint32_t raw[kMaxTok / 4];
+    float eta[kMaxTok / 4];
 #pragma unroll
-    for (int i = 0; i < kMaxTok; ++i)
-      raw[i] = buffer_load_u16(xr, i < T_ && ch < K ? (uint32_t)(i * K + ch) * 2u : kBufferOutOfRange);
+    for (int j2 = 0; j2 < kMaxTok / 4; ++j2) {
+      const int i = p + 4 * j2;
+      raw[j2] = buffer_load_u16(xr, i < T_ && ch < K ? (uint32_t)(i * K + ch) * 2u : kBufferOutOfRange);
+      eta[j2] = a.eta != nullptr && i < T_ ? a.eta[i] : 0.f;
+    }
 #pragma unroll
-    for (int i = 0; i < kMaxTok; ++i)
-      if (i < T_) s_x[i][c] = ch < K ? apply_act<DT>(to_f32<DT>((T)raw[i]), a.act) - (a.eta ? a.eta[i] : 0.f) : 0.f;
+    for (int j2 = 0; j2 < kMaxTok / 4; ++j2) {
+      const int i = p + 4 * j2;
+      s_x[i][c] = i < T_ && ch < K ? apply_act<DT>(to_f32<DT>((T)raw[j2]), a.act) - eta[j2] : 0.f;
+    }
   }
   __syncthreads();
-  if ((int)threadIdx.x < CH) {
-    const int c = threadIdx.x;
-    float f = 1.f;
-    if (c0 + c < K) {
-      if (a.score == SPA_SCORE_WEIGHT) {
-        f = a.chan_scale[c0 + c];
-      } else if (a.score == SPA_SCORE_CLACT) {
-        float acc = 0.f;
-        for (int i = 0; i < T_; ++i) acc = clact_accumulate(acc, s_x[i][c]);
-        f = sqrt_rn(acc);
-      }
-    }
-    s_f[c] = f;
+  // this lane's channel (wave w: group w % 4) and its factor
+  const int cg = wv & 3, tw = wv >> 2;
+  const int c = 64 * cg + lane, ch = c0 + c;
+  const bool cin = ch < K;
+  float f = 1.f;
+  if (a.score == SPA_SCORE_WEIGHT) {
+    f = cin ? a.chan_scale[ch] : 0.f;
+  } else if (a.score == SPA_SCORE_CLACT) {
+    // column energy over the call's tokens, tokens in order; the zero rows
+    // past t add exactly nothing
+    float v[kMaxTok];
+#pragma unroll
+    for (int i = 0; i < kMaxTok; ++i) v[i] = s_x[i][c];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxTok; ++i) acc = clact_accumulate(acc, v[i]);
+    f = sqrt_rn(acc);
   }
-  __syncthreads();
-  for (int pr = threadIdx.x; pr < T_ * NB; pr += 256) {
-    const int i = pr / NB, b = pr % NB;
-    const int cb = c0 + b * M;
-    const int step = cb / 64;                        // an m-block lies inside one 64-channel step
-    double st[4] = {0.0, 0.0, 0.0, 0.0};
-    if (cb < K) {
-      float xh[M];
-      uint32_t sc[M];
+  const int j = lane % M, b0 = lane - j;                   // position in the block, its first lane
+  const int step = (c0 + 64 * cg) / 64;                     // the group's 64 channels are one step
+  const int kept_row = K / M * a.n;
+  uint16_t* xf = static_cast<uint16_t*>(a.dense);
+  // tokens quarter + 4 sl of the quarter's slots sl = tw, tw + 4
 #pragma unroll
-      for (int j = 0; j < M; ++j) {
-        xh[j] = s_x[i][b * M + j];
-        const float ax = __builtin_fabsf(xh[j]);
-        sc[j] = __float_as_uint(a.score == SPA_SCORE_MAGNITUDE ? ax : ax * s_f[b * M + j]);
-      }
-      const uint32_t keep = topn_keep_bits<M>(sc, a.n);
-      // masked values in fragment order: each 8-channel group is 16 bytes of one lane
-      uint16_t* xf = static_cast<uint16_t*>(a.dense);
-      const int lm = i % 16, tb = i / 16;
+  for (int u = 0; u < 2; ++u) {
+    const int sl = tw + 4 * u, i = quarter + 4 * sl;
+    if (i >= T_) break;                                     // uniform
+    const float xh = s_x[i][c];
+    const float ax = __builtin_fabsf(xh);
+    const uint32_t sb = __float_as_uint(a.score == SPA_SCORE_MAGNITUDE ? ax : ax * f);
+    // rank inside the block: scores are non-negative floats, so their bit
+    // patterns order like the values; the wave's own LDS writes precede its
+    // reads (LDS operations of one wave run in order)
+    s_sc[wv][lane] = sb;
+    __builtin_amdgcn_wave_barrier();
+    uint32_t sc[M];
 #pragma unroll
-      for (int q = 0; q < (M + 7) / 8; ++q) {
-        const int o = b * M + 8 * q;                 // channel offset within the step (M >= 8)
-        const int gg = (o % 64) / 16, hh = ((o % 64) / 8) % 2;
-        uint32_t wds[4];
-        const int nv = M < 8 ? M : 8;
+    for (int q = 0; q < M / 4; ++q) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&s_sc[wv][b0 + 4 * q]);
+      sc[4 * q] = v.x; sc[4 * q + 1] = v.y; sc[4 * q + 2] = v.z; sc[4 * q + 3] = v.w;
+    }
+    int beat = 0;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int j0 = 8 * q + 2 * e2;
-          uint32_t lo = 0u, hi = 0u;
-          if (2 * e2 < nv) {
-            lo = ((keep >> j0) & 1u) ? (uint32_t)from_f32<DT>(xh[j0]) : 0u;
-            hi = ((keep >> (j0 + 1)) & 1u) ? (uint32_t)from_f32<DT>(xh[j0 + 1]) : 0u;
-          }
-          wds[e2] = lo | (hi << 16);
-        }
-        uint16_t* dst = xf + frag_offset(step, tb, ntb, hh, lm + 16 * gg);
-        if constexpr (M >= 8) {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
-        } else {                                     // a block of 4 is half of one lane's 16 bytes
-          *reinterpret_cast<uint2*>(dst + (o % 8)) = make_uint2(wds[0], wds[1]);
-        }
-      }
-      if (a.idx_out) {
-        uint8_t* id = a.idx_out + (size_t)i * (K / M * a.n) + (size_t)(cb / M) * a.n;
-        uint32_t kb = keep;
-        for (int q = 0; q < a.n; ++q) {
-          id[q] = (uint8_t)__builtin_ctz(kb);
-          kb &= kb - 1u;
-        }
-      }
-      if (a.var) {
-#pragma unroll
-        for (int j = 0; j < M; ++j) {
-          const double v = (double)xh[j];
-          st[0] += v;
-          st[1] += v * v;
-          if ((keep >> j) & 1u) { st[2] += v; st[3] += v * v; }
-        }
+    for (int q = 0; q < M; ++q) beat += (sc[q] > sb || (sc[q] == sb && q < j)) ? 1 : 0;
+    const bool keep = cin && beat < a.n;
+    // masked values: eight lanes' values are one 16-byte piece of the operand
+    s_mv[wv][lane] = keep ? (uint16_t)from_f32<DT>(xh) : (uint16_t)0;
+    __builtin_amdgcn_wave_barrier();
+    if (lane < 8 && c0 + 64 * cg + 8 * lane < K) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&s_mv[wv][8 * lane]);
+      *reinterpret_cast<uint4*>(xf + frag_offset(step, i >> 4, ntb, lane & 1, (i & 15) + 16 * (lane >> 1))) = v;
+    }
+    if (a.idx_out != nullptr) {
+      const unsigned long long km = __ballot(keep);
+      const unsigned long long blk = (km >> b0) & ((1ull << M) - 1ull);
+      if (keep) {
+        const int r = __popcll(blk & ((1ull << j) - 1ull));
+        a.idx_out[(size_t)i * kept_row + (size_t)((ch - j) / M) * a.n + r] = (uint8_t)j;
       }
     }
-    if (a.var)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) s_st[i][b][q] = st[q];
+    if (a.var) {
+      const double v = (double)xh;                          // 0 past k
+      const double kv = keep ? v : 0.0;
+      const double t0 = wave_sum_dpp(v), t1 = wave_sum_dpp(v * v), t2 = wave_sum_dpp(kv), t3 = wave_sum_dpp(kv * kv);
+      if (lane == 0) {
+        s_st[cg][sl][0] = t0; s_st[cg][sl][1] = t1; s_st[cg][sl][2] = t2; s_st[cg][sl][3] = t3;
+      }
+    }
   }
   if (a.var) {
-    // this chunk's four sums per token, blocks in order
+    // this chunk's four sums per token of the quarter, the 64-channel groups in order
     __syncthreads();
-    if ((int)threadIdx.x < T_) {
-      double tot[4] = {0.0, 0.0, 0.0, 0.0};
-      for (int b2 = 0; b2 < NB; ++b2)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) tot[q] += s_st[threadIdx.x][b2][q];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) a.stats[((size_t)threadIdx.x * 4 + q) * a.chunks + blockIdx.x] = tot[q];   // [token][sum][chunk]
+    const int sl = threadIdx.x >> 2, q = threadIdx.x & 3, i = quarter + 4 * sl;
+    if (sl < kMaxTok / 4 && i < T_) {
+      const double tot = ((s_st[0][sl][q] + s_st[1][sl][q]) + s_st[2][sl][q]) + s_st[3][sl][q];
+      a.stats[((size_t)i * 4 + q) * a.chunks + blockIdx.x] = tot;   // [token][sum][chunk]
     }
   }
 }
@@ -1234,12 +1240,12 @@ static hipError_t decode_dt(DecodeArgs& a, hipStream_t st) {
   }
   if constexpr (DT != SPA_F32) {
     // prune every token once (score, top-n, masked rows, positions, variance sums) ...
-    const dim3 pg(a.chunks);
+    const dim3 pg(a.chunks, 4);                     // channel chunks x token quarters
     switch (a.m) {
-      case 4: hipLaunchKernelGGL((k_prune_cols<DT, 4>), pg, dim3(256), 0, st, a); break;
-      case 8: hipLaunchKernelGGL((k_prune_cols<DT, 8>), pg, dim3(256), 0, st, a); break;
-      case 16: hipLaunchKernelGGL((k_prune_cols<DT, 16>), pg, dim3(256), 0, st, a); break;
-      default: hipLaunchKernelGGL((k_prune_cols<DT, 32>), pg, dim3(256), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((k_prune_cols<DT, 4>), pg, dim3(kPcThreads), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((k_prune_cols<DT, 8>), pg, dim3(kPcThreads), 0, st, a); break;
+      case 16: hipLaunchKernelGGL((k_prune_cols<DT, 16>), pg, dim3(kPcThreads), 0, st, a); break;
+      default: hipLaunchKernelGGL((k_prune_cols<DT, 32>), pg, dim3(kPcThreads), 0, st, a); break;
     }
     if (hipError_t e = hipGetLastError()) return e;
     // ... then one pass over the row-major weight on the matrix cores
