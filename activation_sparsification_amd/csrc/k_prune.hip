@@ -128,6 +128,13 @@ __device__ __forceinline__ float row_mean(const typename Dt<DT>::T* __restrict__
   return (float)(tot / (double)k);
 }
 
+// Block index -> row such that XCD x (blocks b with b % 8 == x) gets rows
+// [x q, x q + q), q = t / 8; the last t % 8 rows keep their own index.
+__device__ __forceinline__ int xcd_contiguous(int b, int t) {
+  const int q = t / 8;
+  return b < 8 * q ? (b % 8) * q + b / 8 : b;
+}
+
 template <int DT, int M>
 __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
   using T = typename Dt<DT>::T;
@@ -137,7 +144,11 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
   // staging for packed outputs of one wave-iteration: 64 lanes x SEG*n/m values
   extern __shared__ unsigned char s_dyn[];
 
-  const int row = blockIdx.x;
+  // Workgroup b runs on XCD b % 8; each XCD takes a contiguous run of rows,
+  // so the rows that share a line of the step-major packed layout (16 rows of
+  // 8-byte position words, 2 rows of 64-byte values) are written through one
+  // L2, which merges them into whole lines before they reach memory.
+  const int row = xcd_contiguous(blockIdx.x, a.t);
   const int n = a.n;
   const int kept_row = a.k / M * n;        // packed values per row
   const int kept_seg = BPS * n;            // packed values per segment
