@@ -541,10 +541,9 @@ __global__ void __launch_bounds__((fused_waves<M, TOK>() * 64)) k_decode_fused(D
 //     of at most kT1MaxChan channels; a load instruction reads 1 KB of one
 //     weight row (long runs per row stream HBM faster than eight 128-byte
 //     pieces of eight rows).  Splits hand off through the ticket above.
-//   * The mean shift: every thread sums its share of the token row in
-//     float64 (one 16-byte load per thread per 4096 channels); the waves'
-//     sums are combined in a fixed order after the only barrier before the
-//     stream.
+//   * The mean shift: every wave sums the whole token row in float64 (eight
+//     16-byte loads per lane per 4096 channels in flight, then a fixed-order
+//     wave sum), so no workgroup barrier precedes the stream.
 //   * Each wave then works alone on 64 channels at a time: a lane scores its
 //     channel, counts the positions of its m-block that beat it (larger
 //     score, or equal score at a lower position) with xor shuffles inside the
@@ -604,33 +603,29 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
     xraw[r] = buffer_load_u16(xr, c < KL ? (uint32_t)(kb + c) * 2u : kBufferOutOfRange);
     fraw[r] = buffer_load_u32(fr, c < KL ? (uint32_t)(kb + c) * 4u : kBufferOutOfRange);
   }
-  // 1. the shift
+  // 1. the shift: every wave sums the whole row itself (the same loads and
+  //    the same fixed order in every wave and workgroup, so every wave forms
+  //    the same eta), with no workgroup barrier: a wave goes on to its rows
+  //    as soon as its own loads are back
   const bool mean = a.shift == SPA_SHIFT_TOKEN_MEAN && a.eta == nullptr;
+  float eta = 0.f;
   if (mean) {
-    const int nq = a.k / 8;
+    const int nq = a.k / 8;                                // 16-byte pieces of the row
     double part[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int q0 = 0; q0 < nq; q0 += 4 * NT) {
-      uint4 u[4];
+    for (int q0 = 0; q0 < nq; q0 += 8 * 64) {
+      uint4 u[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = q0 + NT * i + threadIdx.x;
+      for (int i = 0; i < 8; ++i) {
+        const int q = q0 + 64 * i + lane;
         u[i] = buffer_load16(xr, q < nq ? (uint32_t)q * 16u : kBufferOutOfRange);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part[i] += (double)apply_act<DT>(elem16<DT>(u[i], e), ACT);
+        for (int e = 0; e < 8; ++e) part[i & 3] += (double)apply_act<DT>(elem16<DT>(u[i], e), ACT);
     }
     const double tot = wave_sum_dpp((part[0] + part[1]) + (part[2] + part[3]));
-    if (lane == 0) s_part[wv][0] = tot;
-    __syncthreads();
-  }
-  float eta = 0.f;
-  if (mean) {
-    double s = 0.0;
-#pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) s += s_part[w2][0];
-    eta = (float)(s / (double)a.k);
+    eta = (float)(tot / (double)a.k);
   } else if (a.eta != nullptr) {
     eta = a.eta[0];
   }
