@@ -42,8 +42,32 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16/fp16 matrix peak
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 matrix peak
 MALL_BYTES = 256 * 2 ** 20
 METRIC = "decode: effective HBM GB/s; prefill: TFLOP/s; both as % of MI355X peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_t1_bf16_k4096_n14336_traffic.txt")
-DECODE_SOURCES = ["activation_sparsification_amd/csrc/k_decode.hip", "activation_sparsification_amd/csrc/spa_common.h"]
+CSRC = "activation_sparsification_amd/csrc/"
+DECODE_SOURCES = [CSRC + f for f in ("k_decode.hip", "spa_common.h", "spa_plan.h", "spa_select.h")]
+PREFILL_SOURCES = [CSRC + f for f in ("k_prune.hip", "k_prefill.hip", "spa_common.h", "spa_select.h")]
+
+# The kernels of one step of each workload, the bound that prices them and the
+# algorithmic unit behind `achieved` (bytes or kept flops per launch).  A step
+# that launches two kernels is priced whole: achieved = the step's algorithmic
+# work over the event-timed step.
+ROOFLINE = {
+    "decode": dict(profile="decode_t1_bf16_k4096_n14336", kernel="k_decode_t1<bf16,16>", bound="hbm", sources=DECODE_SOURCES,
+                   per_unit="one kept row of W^T: n_out x 2 B = 28,672 B; a launch reads the kept rows "
+                            "(2048 here) plus x, the channel factors, the row sums and y"),
+    "batched_t1": dict(profile="decode_t1_f16_batched_k14336_n4096", kernel="k_decode_t1<f16,32>", bound="hbm", sources=DECODE_SOURCES,
+                       per_unit="one kept row of W^T: n_out x 2 B = 8,192 B; plus x and y"),
+    "batched_t8": dict(profile="decode_mm_f16_batched_t8_k14336_n4096", kernel="k_prune_cols<f16,32> + k_decode_mm<f16,1>", bound="hbm", sources=DECODE_SOURCES,
+                       per_unit="one union channel's weights: n_out x 2 B = 8,192 B; plus x and y"),
+    "batched_t32": dict(profile="decode_mm_f16_batched_t32_k14336_n4096", kernel="k_prune_cols<f16,32> + k_decode_mm<f16,2>", bound="hbm", sources=DECODE_SOURCES,
+                        per_unit="one union channel's weights: n_out x 2 B = 8,192 B; plus x and y"),
+    "prefill": dict(profile="gemm24_bf16_prefill_t2048_k4096_n14336", kernel="k_prune<bf16,4> + k_gemm24<bf16,16>", bound="mfma", sources=PREFILL_SOURCES,
+                    per_unit="one 256 x 256 x 64 tile step: 4.19 MFLOP kept (2 t n_out k n/m in all)"),
+    "relu2": dict(profile="gemm24_bf16_relu2_t4096_k16384_n4096", kernel="k_prune<bf16,4> + k_gemm24<bf16,8>", bound="mfma", sources=PREFILL_SOURCES,
+                  per_unit="one 256 x 256 x 64 tile step: 4.19 MFLOP kept (2 t n_out k n/m in all)"),
+    "relu2_fused": dict(profile="gemm24_bf16_relu2_fused_t4096_k16384_n4096", kernel="k_prune<bf16,4> (squared ReLU fused) + k_gemm24<bf16,8>", bound="mfma",
+                        sources=PREFILL_SOURCES,
+                        per_unit="one 256 x 256 x 64 tile step: 4.19 MFLOP kept (2 t n_out k n/m in all)"),
+}
 
 WORKLOADS = {
     "decode": ("decode", dict()),
@@ -79,19 +103,39 @@ def sources_sha(paths):
     return h.hexdigest()
 
 
-def read_traffic():
-    """HBM bytes per launch of the decode kernel from the committed counter summary,
-    or None when the kernel source changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_counters(name):
+    """The committed counter record of a workload (first line of its
+    profiles/<kernel>_<workload>_counters.txt: HBM bytes per step, the
+    sustained clock and the matrix-core busy fraction), or None when a source
+    of its kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{ROOFLINE[name]['profile']}_counters.txt") if name in ROOFLINE else ""
+    if name not in ROOFLINE or not os.path.exists(path):
         return None
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             rec = json.loads(fh.readline())
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != sources_sha(DECODE_SOURCES):
+    if rec.get("source_sha256") != sources_sha(ROOFLINE[name]["sources"]):
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
+
+
+def roofline(name, rec):
+    """The roofline object of one bench record."""
+    r = ROOFLINE.get(name)
+    if r is None:
+        return None
+    peak = PEAK_HBM_GBS if r["bound"] == "hbm" else PEAK_BF16_TFLOPS
+    ctr = read_counters(name)
+    out = dict(bound=r["bound"], achieved=rec["value"], peak=peak, unit=rec["unit"], frac=rec["value"] / peak,
+               traffic=None if ctr is None else ctr.get("traffic_bytes_per_step"), kernel=r["kernel"],
+               per_unit=r["per_unit"])
+    if ctr is not None:
+        for key in ("mfma_busy", "clock_ghz", "algorithmic_bytes_per_step"):
+            if key in ctr:
+                out[key] = ctr[key]
+    return out
 
 
 class Workload:
@@ -114,8 +158,13 @@ class Workload:
         # of a 16-bit type read the row-major weight on the matrix cores
         self.reads_wt = self.decode and (spec.t <= 4 or spec.dtype == "f32")
         big = self.pw.wt if self.reads_wt else self.pw.w
-        wbytes = big.numel() * big.element_size()
-        self.copies = max(3, math.ceil(3 * MALL_BYTES / wbytes))
+        # weight copies rotated so that the bytes a step touches, summed over
+        # the copies, exceed the 256 MB MALL three times over: the kept rows
+        # on the channel-major path, the whole weight otherwise
+        touched = big.numel() * big.element_size()
+        if self.reads_wt:
+            touched = self.union_rows() * spec.n_out * big.element_size()
+        self.copies = max(3, math.ceil(3 * MALL_BYTES / touched))
         mats = [big] + [big.clone() for _ in range(self.copies - 1)]
         self.y = torch.empty((spec.t, spec.n_out), dtype=x.dtype, device=dev)
         entry = 1 if self.decode else 2
@@ -162,7 +211,7 @@ class Workload:
         ev_s, ev0, ev1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         # keep the GPU busy while the host queues every timed call
         ev_s.record()
-        torch.cuda._sleep(int(2e6) + 60000 * steps)
+        torch.cuda._sleep(int(4e6) + 200000 * steps)
         ev0.record()
         h0 = time.perf_counter()
         for i in range(steps):
@@ -175,7 +224,7 @@ class Workload:
         # per-call durations in a second pass: an event after every call (the
         # events add a little to each step, so the headline is the pass above)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        torch.cuda._sleep(int(2e6) + 60000 * steps)
+        torch.cuda._sleep(int(4e6) + 200000 * steps)
         evs[0].record()
         for i in range(steps):
             calls[i % len(calls)]()
@@ -201,6 +250,7 @@ def measure(name, steps, warmup):
         tf = flops / (ms * 1e-3) / 1e12
         rec.update(unit="TFLOP/s", value=tf, pct_of_peak=100.0 * tf / PEAK_BF16_TFLOPS, kept_flops=flops,
                    algorithmic_bytes=b)
+    rec["roofline"] = roofline(name, rec)
     del w
     torch.cuda.empty_cache()
     return rec
@@ -240,9 +290,13 @@ def measure_meta(fmt, n, m, t, k, steps, warmup):
         ms = e0.elapsed_time(e1) / steps
         b = idx.numel() + t * row_bytes
         gbs = b / (ms * 1e-3) / 1e9
+        kern = f"k_{name}_meta<{n}>"
         recs.append(dict(workload=f"meta_{name}_{fmt}_{n}_{m}", unit="GB/s", value=gbs, ms_per_step=ms,
                          pct_of_peak=100.0 * gbs / PEAK_HBM_GBS, algorithmic_bytes=b, copies=copies,
-                         desc=f"{name} of {fmt} block codes, {n}:{m}, positions [{t},{k * n // m}] uint8"))
+                         desc=f"{name} of {fmt} block codes, {n}:{m}, positions [{t},{k * n // m}] uint8",
+                         roofline=dict(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s",
+                                       frac=gbs / PEAK_HBM_GBS, traffic=None, kernel=kern,
+                                       per_unit="one m-block: n bytes of positions + its code bits / 8")))
     assert torch.equal(outs[(steps - 1) % copies], idx), "decoded positions differ from the input"
     del idxs, codes, outs
     torch.cuda.empty_cache()
@@ -309,9 +363,15 @@ def measure_ffn(steps, warmup, t=4096, hidden=4096, ffn=16384, n_out=4096):
     for name in ("ffn_relu2_fused", "ffn_relu2_unfused"):
         ms = sorted(per[name])[len(per[name]) // 2]
         tf = flops / (ms * 1e-3) / 1e12
+        kern = ("k_gemm_dense<bf16,1> (prunes in its epilogue) + k_gemm24<bf16,8>" if name.endswith("_fused") else
+                "k_gemm_dense<bf16,0> + k_prune<bf16,4> + k_prune<bf16,4> (squared ReLU) + k_gemm24<bf16,8>")
         recs.append(dict(workload=name, unit="TFLOP/s", value=tf, ms_per_step=ms, pct_of_peak=100.0 * tf / PEAK_BF16_TFLOPS,
                          flops=flops, weight_copies=copies, blocks_ms=per[name],
-                         desc=f"squared-ReLU FFN x[{t},{hidden}] -> {ffn} -> {n_out} bf16, activation pruned 2:4"))
+                         desc=f"squared-ReLU FFN x[{t},{hidden}] -> {ffn} -> {n_out} bf16, activation pruned 2:4",
+                         roofline=dict(bound="mfma", achieved=tf, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                                       frac=tf / PEAK_BF16_TFLOPS, traffic=None, kernel=kern,
+                                       per_unit="dense up-projection flops 2 t hidden ffn + kept down-projection "
+                                                "flops 2 t ffn n_out / 2")))
     del ups, dns, unfused
     torch.cuda.empty_cache()
     return recs
@@ -362,10 +422,16 @@ def measure_fp8(steps, warmup, name="prefill"):
     for key, peak in (("prefill_bf16", PEAK_BF16_TFLOPS), ("prefill_fp8", PEAK_FP8_TFLOPS)):
         ms = sorted(per[key])[len(per[key]) // 2]
         tf = flops / (ms * 1e-3) / 1e12
+        kern = ("k_prune<bf16,4> (e4m3 packing) + k_gemm24_fp8<bf16>" if key.endswith("fp8") else
+                "k_prune<bf16,4> + k_gemm24<bf16,16>")
         recs.append(dict(workload=key, unit="TFLOP/s", value=tf, ms_per_step=ms, pct_of_peak=100.0 * tf / peak,
                          kept_flops=flops, weight_copies=copies, blocks_ms=per[key],
                          desc=f"2:4 prefill x[{spec.t},{spec.k}] -> {spec.n_out}, "
-                              + ("FP8 e4m3 operands, row scales" if key.endswith("fp8") else "bf16 operands")))
+                              + ("FP8 e4m3 operands, row scales" if key.endswith("fp8") else "bf16 operands"),
+                         roofline=dict(bound="mfma", achieved=tf, peak=peak, unit="TFLOP/s", frac=tf / peak,
+                                       traffic=None, kernel=kern,
+                                       per_unit="one 256 x 256 x 64 tile step: 4.19 MFLOP kept; the FP8 line "
+                                                "against the dense fp8 peak")))
     del mats, codes, bf, f8
     torch.cuda.empty_cache()
     return recs
@@ -486,15 +552,7 @@ def main():
         secondary += measure_fp8(max(8, args.steps // 10), 5)
 
     decode = head["unit"] == "GB/s"
-    traffic = read_traffic() if args.workload == "decode" else None
-    roof = dict(bound="hbm" if decode else "mfma",
-                achieved=head["value"],
-                peak=PEAK_HBM_GBS if decode else PEAK_BF16_TFLOPS,
-                unit=head["unit"],
-                frac=head["value"] / (PEAK_HBM_GBS if decode else PEAK_BF16_TFLOPS),
-                traffic=traffic,
-                kernel="k_decode_t1<bf16,16>" if args.workload == "decode" else None,
-                per_unit="bytes per kept weight row = n_out * 2; one launch reads the call's kept rows")
+    roof = head.pop("roofline")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload if decode else "decode")
