@@ -128,6 +128,35 @@ __device__ __forceinline__ float row_mean(const typename Dt<DT>::T* __restrict__
   return (float)(tot / (double)k);
 }
 
+// Running max of |x - eta| over the kept entries of one segment (the FP8
+// token scale is taken over the sparsified row).
+template <int M, int SEG>
+__device__ __forceinline__ float kept_absmax(const float (&v)[SEG], float eta, int seg, const PruneArgs& a, float mx) {
+  float xh[SEG];
+#pragma unroll
+  for (int j = 0; j < SEG; ++j) xh[j] = v[j] - eta;
+  if constexpr (M == 4) {
+    if (a.n == 2) {
+      const float* f = a.colnorm ? a.colnorm + (size_t)seg * SEG : a.chan_scale ? a.chan_scale + (size_t)seg * SEG : nullptr;
+#pragma unroll
+      for (int b = 0; b < SEG / 4; ++b) {
+        float sc[4], lo, hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[j] = f ? __builtin_fabsf(xh[4 * b + j]) * f[4 * b + j] : __builtin_fabsf(xh[4 * b + j]);
+        top2of4(sc, xh + 4 * b, lo, hi);
+        mx = fmaxf(mx, fmaxf(__builtin_fabsf(lo), __builtin_fabsf(hi)));
+      }
+      return mx;
+    }
+  }
+  uint32_t kb[SEG / M];
+  seg_keep<M, SEG>(xh, seg, a, kb);
+#pragma unroll
+  for (int j = 0; j < SEG; ++j)
+    if ((kb[j / M] >> (j % M)) & 1u) mx = fmaxf(mx, __builtin_fabsf(xh[j]));
+  return mx;
+}
+
 // Block index -> row such that XCD x (blocks b with b % 8 == x) gets rows
 // [x q, x q + q), q = t / 8; the last t % 8 rows keep their own index.
 __device__ __forceinline__ int xcd_contiguous(int b, int t) {
@@ -155,25 +184,36 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
   const T* xr = static_cast<const T*>(a.x) + (size_t)row * a.k;
 
   const int nseg = a.k / SEG;
-  // All lanes of a wave run the same number of iterations so the wave-wide
+  // All lanes of a wave run the same number of passes so the wave-wide
   // copy-out below stays convergent.
   const int iters = (nseg + 255) / 256;
-  // the first pass's segment is requested before the shift is known; when the
-  // whole row is one pass, the shift is summed from these same registers.
-  // Each pass then requests the next pass's segment before its own work.
+  // A ring of G segment loads per thread (at most 32 data registers): pass p
+  // is requested G passes before its use, so a workgroup keeps G x 256
+  // segments of its row outstanding.  A row of at most G passes is read once:
+  // the shift and the FP8 scale come from these same registers.
+  constexpr int NQ = RawSeg<DT, SEG>::NQ;
+  constexpr int G = NQ >= 8 ? 1 : 8 / NQ;
   const __amdgpu_buffer_rsrc_t xrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(xr), (short)0, a.k * (int)sizeof(T), kBufferWord3);
-  RawSeg<DT, SEG> raw_next;
-  load_raw<DT, SEG>(xrs, (int)threadIdx.x, (int)threadIdx.x < nseg, raw_next);
-  float xv0[SEG];
-  unpack_raw<DT, SEG>(raw_next, a.act, xv0);
+  RawSeg<DT, SEG> raw[G];
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    const int sg = u * 256 + (int)threadIdx.x;
+    load_raw<DT, SEG>(xrs, sg, sg < nseg, raw[u]);
+  }
+  const bool resident = iters <= G;
   float eta = 0.f;
   if (a.shift_mean) {
-    if (iters == 1) {
+    if (resident) {
       double s = 0.0;
-      if ((int)threadIdx.x < nseg) {
 #pragma unroll
-        for (int j = 0; j < SEG; ++j) s += (double)xv0[j];
+      for (int u = 0; u < G; ++u) {
+        if (u * 256 + (int)threadIdx.x < nseg) {
+          float v[SEG];
+          unpack_raw<DT, SEG>(raw[u], a.act, v);
+#pragma unroll
+          for (int j = 0; j < SEG; ++j) s += (double)v[j];
+        }
       }
       eta = (float)(block_sum(s, s_red) / (double)a.k);
     } else {
@@ -186,33 +226,29 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
     if (a.eta_out) a.eta_out[row] = eta;
   }
   // FP8 packing quantises the sparsified row: the token's scale comes from
-  // max |x - eta| over the kept entries (the selection runs here first, on
-  // the registers of the one-pass case, else on a second read of the row)
+  // max |x - eta| over the kept entries (selected here first, from the
+  // registers of a resident row, else from a second read of the row)
   float fp8_inv = 0.f;
-  constexpr int BPS_ = SEG / M;
-  uint32_t keep0[BPS_] = {};
   if (a.fp8) {
     float mx = 0.f;
-    for (int sg = threadIdx.x; sg < nseg; sg += 256) {
-      float v2[SEG];
-      if (iters == 1) {
+    if (resident) {
 #pragma unroll
-        for (int j = 0; j < SEG; ++j) v2[j] = xv0[j];
-      } else {
+      for (int u = 0; u < G; ++u) {
+        const int sg = u * 256 + (int)threadIdx.x;
+        if (sg < nseg) {
+          float v[SEG];
+          unpack_raw<DT, SEG>(raw[u], a.act, v);
+          mx = kept_absmax<M, SEG>(v, eta, sg, a, mx);
+        }
+      }
+    } else {
+      for (int sg = threadIdx.x; sg < nseg; sg += 256) {
         RawSeg<DT, SEG> r2;
         load_raw<DT, SEG>(xrs, sg, true, r2);
-        unpack_raw<DT, SEG>(r2, a.act, v2);
+        float v[SEG];
+        unpack_raw<DT, SEG>(r2, a.act, v);
+        mx = kept_absmax<M, SEG>(v, eta, sg, a, mx);
       }
-      float xh2[SEG];
-#pragma unroll
-      for (int j = 0; j < SEG; ++j) xh2[j] = v2[j] - eta;
-      uint32_t kb2[BPS_];
-      seg_keep<M, SEG>(xh2, sg, a, kb2);
-#pragma unroll
-      for (int j = 0; j < SEG; ++j)
-        if ((kb2[j / M] >> (j % M)) & 1u) mx = fmaxf(mx, __builtin_fabsf(xh2[j]));
-#pragma unroll
-      for (int b = 0; b < BPS_; ++b) keep0[b] = kb2[b];
     }
     __shared__ float s_mx[4];
     const float amax = block_max(mx, s_mx);
@@ -227,25 +263,42 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
   uint8_t* s_idx = reinterpret_cast<uint8_t*>(s_dyn + (size_t)4 * 64 * kept_seg * sizeof(T)) + (size_t)wv * 64 * kept_seg;
 
   double sx = 0.0, sxx = 0.0, sm = 0.0, smm = 0.0;
-  for (int it = 0; it < iters; ++it) {
+  // One pass: this thread's segment `it * 256 + tid` of the row.
+  auto pass = [&](int it, const float (&xv)[SEG]) {
     const int seg = it * 256 + threadIdx.x;
-    const bool active = seg < nseg;
-    uint32_t keepbits[BPS];
-    float xh[SEG];
-    float xv[SEG];
-    if (it == 0) {
-#pragma unroll
-      for (int j = 0; j < SEG; ++j) xv[j] = xv0[j];
-    } else {
-      unpack_raw<DT, SEG>(raw_next, a.act, xv);
-    }
-    if (it + 1 < iters) load_raw<DT, SEG>(xrs, seg + 256, seg + 256 < nseg, raw_next);
-    if (active) {
+    if (seg < nseg) {
+      uint32_t keepbits[BPS];
+      float xh[SEG];
 #pragma unroll
       for (int j = 0; j < SEG; ++j) xh[j] = xv[j] - eta;
-      if (a.fp8 && iters == 1) {         // selected already, for the FP8 scale
+      // 2:4 (the only pattern of the tiled operand): each block's position
+      // code, four to a 16-bit word, and its two kept values, by tournament;
+      // the keep bits only where an output needs them
+      uint32_t meta24 = 0;
+      float flo[BPS], fhi[BPS];
+      if (M == 4 && n == 2) {
+        if constexpr (M == 4) {
+          const float* f = a.colnorm ? a.colnorm + (size_t)seg * SEG : a.chan_scale ? a.chan_scale + (size_t)seg * SEG : nullptr;
 #pragma unroll
-        for (int b = 0; b < BPS; ++b) keepbits[b] = keep0[b];
+          for (int b = 0; b < BPS; ++b) {
+            float sc[4];
+            if (f) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) sc[j] = __builtin_fabsf(xh[4 * b + j]) * f[4 * b + j];
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) sc[j] = __builtin_fabsf(xh[4 * b + j]);
+            }
+            meta24 |= top2of4(sc, xh + 4 * b, flo[b], fhi[b]) << (4 * b);
+          }
+          if (a.var || (a.pack & (kPackDense | kPackVals))) {
+#pragma unroll
+            for (int b = 0; b < BPS; ++b) {
+              const uint32_t code = meta24 >> (4 * b);
+              keepbits[b] = (1u << (code & 3u)) | (1u << ((code >> 2) & 3u));
+            }
+          }
+        }
       } else {
         seg_keep<M, SEG>(xh, seg, a, keepbits);
       }
@@ -265,25 +318,9 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
         // 2:4: the segment's 16 channels are 4 blocks -> 8 kept values (16 bytes) and
         // one 16-bit word of positions, stored at step seg / 4, slot seg % 4
         if constexpr (M == 4 && DT != SPA_F32) {
-          uint32_t meta = 0;
           uint32_t wds[4];
-          float flo[4], fhi[4];
 #pragma unroll
-          for (int b = 0; b < BPS; ++b) {
-            const uint32_t kb = keepbits[b];
-            const uint32_t lo = __builtin_ctz(kb);
-            const uint32_t hi = 31 - __builtin_clz(kb);
-            meta |= (lo | (hi << 2)) << (4 * b);
-            float vlo = xh[4 * b], vhi = xh[4 * b];
-#pragma unroll
-            for (int j = 1; j < 4; ++j) {
-              vlo = (int)lo == j ? xh[4 * b + j] : vlo;
-              vhi = (int)hi == j ? xh[4 * b + j] : vhi;
-            }
-            flo[b] = vlo;
-            fhi[b] = vhi;
-            wds[b] = (uint32_t)from_f32<DT>(vlo) | ((uint32_t)from_f32<DT>(vhi) << 16);
-          }
+          for (int b = 0; b < BPS; ++b) wds[b] = pack2<DT>(flo[b], fhi[b]);
           const size_t rowpos = (size_t)(seg / 4) * a.t_pad + row;
           if (a.fp8) {
             // the eight kept values as e4m3 codes of x_hat * (448 / max), in
@@ -297,7 +334,7 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
             reinterpret_cast<uint4*>(static_cast<T*>(a.tiled_vals) + rowpos * 32)[seg % 4] =
                 make_uint4(wds[0], wds[1], wds[2], wds[3]);
           }
-          a.tiled_meta[rowpos * 4 + seg % 4] = (uint16_t)meta;
+          a.tiled_meta[rowpos * 4 + seg % 4] = (uint16_t)meta24;
         }
       }
       if (a.pack & kPackDense) {
@@ -356,6 +393,21 @@ __global__ void __launch_bounds__(256) k_prune(PruneArgs a) {
         }
       }
       __syncthreads();
+    }
+  };
+  for (int g = 0; g < iters; g += G) {
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int it = g + u;
+      if (it < iters) {                  // the same for the whole workgroup
+        float xv[SEG];
+        unpack_raw<DT, SEG>(raw[u], a.act, xv);
+        if (it + G < iters) {
+          const int nx = (it + G) * 256 + (int)threadIdx.x;
+          load_raw<DT, SEG>(xrs, nx, nx < nseg, raw[u]);
+        }
+        pass(it, xv);
+      }
     }
   }
 
@@ -464,6 +516,197 @@ __global__ void __launch_bounds__(256) k_colnorm(const typename Dt<DT>::T* __res
   c[ch] = sqrt_rn(acc);
 }
 
+// The 2:4 sparse-MFMA operand alone (16-bit rows of at most 16384 channels;
+// no variance factor and no separate positions): the same shift, score,
+// selection and packing as k_prune, laid out for throughput.
+//
+// A grid of about a thousand workgroups walks the rows: the j-th row of
+// workgroup b is xcd_contiguous(j * grid + b), so at every step the
+// workgroups of one XCD hold adjacent rows and their stores meet in one L2.
+// A row is P passes of 256 sixteen-channel segments; a register ring of
+// R rows (R * P passes) keeps the next rows' loads in flight while one is
+// ranked (pass p of a row is refilled with pass p of the row R places on as
+// soon as it is unpacked, so every load is issued four passes ahead of its
+// use), and a row in the ring is whole, so the token mean and the FP8 scale
+// are formed from the registers.  Each 4-block is ranked by the tournament
+// and packed by gfx950's packed conversion.
+// The 16 channel factors of segment seg (CLACT column norm or weight factor).
+__device__ __forceinline__ void seg_factors(const PruneArgs& a, int seg, float (&fv)[16]) {
+  const float4* f4 = reinterpret_cast<const float4*>((a.colnorm ? a.colnorm : a.chan_scale) + (size_t)seg * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 q = f4[i];
+    fv[4 * i] = q.x; fv[4 * i + 1] = q.y; fv[4 * i + 2] = q.z; fv[4 * i + 3] = q.w;
+  }
+}
+
+// Ranks the four 4-blocks of one segment of shifted values xh (scores
+// |xh| * fv, or |xh|): the 16-bit word of position codes and each block's
+// two kept values.
+template <bool FAC>
+__device__ __forceinline__ uint32_t seg_top2(const float (&xh)[16], const float (&fv)[16], float (&flo)[4],
+                                             float (&fhi)[4]) {
+  uint32_t meta = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    float sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sc[j] = FAC ? __builtin_fabsf(xh[4 * b + j]) * fv[4 * b + j] : __builtin_fabsf(xh[4 * b + j]);
+    meta |= top2of4(sc, xh + 4 * b, flo[b], fhi[b]) << (4 * b);
+  }
+  return meta;
+}
+
+template <int DT, int P, bool FP8, bool FAC>
+__global__ void __launch_bounds__(256) k_prune24(PruneArgs a) {
+  using T = typename Dt<DT>::T;
+  constexpr int R = 4 / P;                   // rows in the ring (four passes)
+  constexpr int G = R * P;
+  __shared__ double s_red[4];
+  __shared__ float s_mx[4];
+  const int nseg = a.k / 16;
+  const int tid = threadIdx.x;
+  const T* x = static_cast<const T*>(a.x);
+  auto row_of = [&](int j) -> int {          // the j-th row of this workgroup, or -1
+    const long v = (long)j * gridDim.x + blockIdx.x;
+    return v < a.t ? xcd_contiguous((int)v, a.t) : -1;
+  };
+  // a row's buffer descriptor (an absent row reads as zeros)
+  auto rsrc_of = [&](int row) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(x) + (size_t)(row < 0 ? 0 : row) * a.k, (short)0,
+                                             row < 0 ? 0 : a.k * (int)sizeof(T), kBufferWord3);
+  };
+  RawSeg<DT, 16> raw[G];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int row = row_of(rr);
+    const auto rs = rsrc_of(row);
+#pragma unroll
+    for (int p = 0; p < P; ++p) load_raw<DT, 16>(rs, p * 256 + tid, row >= 0 && p * 256 + tid < nseg, raw[rr * P + p]);
+  }
+
+  for (int j0 = 0; row_of(j0) >= 0; j0 += R) {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int row = row_of(j0 + rr);
+      if (row < 0) break;                    // the same for the whole workgroup
+      float eta = 0.f;
+      if (a.shift_mean) {
+        double s = 0.0;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          if (p * 256 + tid < nseg) {
+            float v[16];
+            unpack_raw<DT, 16>(raw[rr * P + p], a.act, v);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s += (double)v[j];
+          }
+        }
+        eta = (float)(block_sum(s, s_red) / (double)a.k);
+      } else if (a.eta_given) {
+        // a scalar load: kept off the vector-memory counter, whose in-order
+        // waits would otherwise hold back on the ring's loads
+        eta = ((const __attribute__((address_space(4))) float*)(uintptr_t)a.eta_given)[row];
+      }
+      if (tid == 0 && a.eta_out) a.eta_out[row] = eta;
+      float fp8_inv = 0.f;
+      if constexpr (FP8) {
+        float mx = 0.f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const int seg = p * 256 + tid;
+          if (seg < nseg) {
+            float v[16], fv[16], flo[4], fhi[4];
+            unpack_raw<DT, 16>(raw[rr * P + p], a.act, v);
+            if constexpr (FAC) seg_factors(a, seg, fv);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] -= eta;
+            seg_top2<FAC>(v, fv, flo, fhi);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) mx = fmaxf(mx, fmaxf(__builtin_fabsf(flo[b]), __builtin_fabsf(fhi[b])));
+          }
+        }
+        const float amax = block_max(mx, s_mx);
+        float scale;
+        fp8_scales(amax, scale, fp8_inv);
+        if (tid == 0) a.fp8_scale[row] = scale;
+      }
+      const int next = row_of(j0 + rr + R);
+      const auto rs_next = rsrc_of(next);
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int seg = p * 256 + tid;
+        float v[16];
+        unpack_raw<DT, 16>(raw[rr * P + p], a.act, v);
+        load_raw<DT, 16>(rs_next, seg, next >= 0 && seg < nseg, raw[rr * P + p]);
+        if (seg < nseg) {
+          float fv[16], flo[4], fhi[4];
+          if constexpr (FAC) seg_factors(a, seg, fv);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[j] -= eta;
+          const uint32_t meta = seg_top2<FAC>(v, fv, flo, fhi);
+          const size_t rowpos = (size_t)(seg / 4) * a.t_pad + row;
+          if constexpr (FP8) {
+            const uint32_t q01 = fp8_pair(flo[0] * fp8_inv, fhi[0] * fp8_inv) |
+                                 (fp8_pair(flo[1] * fp8_inv, fhi[1] * fp8_inv) << 16);
+            const uint32_t q23 = fp8_pair(flo[2] * fp8_inv, fhi[2] * fp8_inv) |
+                                 (fp8_pair(flo[3] * fp8_inv, fhi[3] * fp8_inv) << 16);
+            reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.tiled_vals) + rowpos * 32)[seg % 4] = make_uint2(q01, q23);
+          } else {
+            reinterpret_cast<uint4*>(static_cast<T*>(a.tiled_vals) + rowpos * 32)[seg % 4] =
+                make_uint4(pack2<DT>(flo[0], fhi[0]), pack2<DT>(flo[1], fhi[1]), pack2<DT>(flo[2], fhi[2]),
+                           pack2<DT>(flo[3], fhi[3]));
+          }
+          a.tiled_meta[rowpos * 4 + seg % 4] = (uint16_t)meta;
+        }
+      }
+    }
+  }
+}
+
+// As many workgroups as the GPU holds at once (CUs x the kernel's
+// workgroups per CU, queried once per instantiation), fewer when that leaves
+// the rows uneven, and a multiple of the 8 XCDs.
+struct Residency {
+  hipError_t err;
+  int per_gpu;
+};
+template <int DT, int P, bool FP8, bool FAC>
+static hipError_t prune24_launch(const PruneArgs& a, hipStream_t st) {
+  static const Residency res = [] {
+    int dev = 0, nb = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_prune24<DT, P, FP8, FAC>, 256, 0);
+    return Residency{e, (ncu > 0 ? ncu : 1) * (nb > 0 ? nb : 1)};
+  }();
+  if (res.err != hipSuccess) return res.err;
+  const long per = (a.t + (long)res.per_gpu - 1) / res.per_gpu;    // rows per workgroup
+  const long grid = ((a.t + per - 1) / per + 7) / 8 * 8;
+  hipLaunchKernelGGL((k_prune24<DT, P, FP8, FAC>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DT, int P>
+static hipError_t prune24_p(const PruneArgs& a, hipStream_t st) {
+  const bool fac = a.colnorm || a.chan_scale;
+  if (a.fp8) return fac ? prune24_launch<DT, P, true, true>(a, st) : prune24_launch<DT, P, true, false>(a, st);
+  return fac ? prune24_launch<DT, P, false, true>(a, st) : prune24_launch<DT, P, false, false>(a, st);
+}
+
+// The lean pass applies: 16-bit 2:4 rows of at most 16384 channels, the
+// tiled operand the only output.
+static bool lean24(int dtype, const PruneArgs& a) {
+  return dtype != SPA_F32 && a.m == 4 && a.n == 2 && a.pack == kPackTiled24 && !a.var && !a.nu_out &&
+         a.k % 64 == 0 && a.k <= 16384;
+}
+
+template <int DT>
+static hipError_t prune24_dt(const PruneArgs& a, hipStream_t st) {
+  const int passes = (a.k / 16 + 255) / 256;
+  return passes <= 1 ? prune24_p<DT, 1>(a, st) : passes <= 2 ? prune24_p<DT, 2>(a, st) : prune24_p<DT, 4>(a, st);
+}
+
 template <int DT, int M>
 static hipError_t prune_m(const PruneArgs& a, hipStream_t st) {
   constexpr int SEG = M > 16 ? M : 16;
@@ -485,6 +728,7 @@ static hipError_t prune_dt(const PruneArgs& a, hipStream_t st) {
 
 hipError_t launch_prune(int dtype, const PruneArgs& a, hipStream_t st) {
   if (a.t == 0) return hipSuccess;
+  if (lean24(dtype, a)) return dtype == SPA_F16 ? prune24_dt<SPA_F16>(a, st) : prune24_dt<SPA_BF16>(a, st);
   switch (dtype) {
     case SPA_F32: return prune_dt<SPA_F32>(a, st);
     case SPA_F16: return prune_dt<SPA_F16>(a, st);

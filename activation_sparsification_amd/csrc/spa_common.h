@@ -31,6 +31,22 @@ __device__ __forceinline__ uint32_t f32_to_f16(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// Two float32 values as one word of 16-bit values (lo in the low half), each
+// rounded to nearest even by gfx950's packed conversion (v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32; the kernels run with float32 denormals preserved, so the
+// bf16 result equals f32_to_bf16's for every finite input).
+template <int DT> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<SPA_BF16>(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+template <> __device__ __forceinline__ uint32_t pack2<SPA_F16>(float lo, float hi) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t p = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
 template <int DT> __device__ __forceinline__ float to_f32(typename Dt<DT>::T v);
 template <> __device__ __forceinline__ float to_f32<SPA_F32>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f32<SPA_F16>(uint16_t v) { return f16_to_f32(v); }

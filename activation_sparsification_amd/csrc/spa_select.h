@@ -70,4 +70,26 @@ SPA_HD uint32_t topn_keep_bits(const uint32_t (&s)[M], int n) {
   return keep;
 }
 
+// Top 2 of one 4-block by score (ties to the lower channel) as a tournament:
+// the winner of each pair, the better of the two winners, then the runner-up
+// -- the first pair's loser or the second pair's winner when the first pair
+// holds the best, else the first pair's winner or the second pair's loser.
+// Every channel of the first pair precedes every channel of the second, so a
+// tie across the pairs goes to the first.  Four comparisons where the rank
+// count takes six, and no bit scan: returns the 2:4 position code
+// lo | hi << 2 and the kept values v[lo], v[hi].
+SPA_HD uint32_t top2of4(const float (&s)[4], const float* v, float& vlo, float& vhi) {
+  const bool a = s[0] >= s[1];                           // channel 0 wins its pair
+  const bool b = s[2] >= s[3];                           // channel 2 wins its pair
+  const float wa = __builtin_fmaxf(s[0], s[1]), la = __builtin_fminf(s[0], s[1]);
+  const float wb = __builtin_fmaxf(s[2], s[3]), lb = __builtin_fminf(s[2], s[3]);
+  const bool c = wa >= wb;                               // the first pair holds the best
+  const bool d = c ? la >= wb : wa >= lb;                // ... and the runner-up
+  const bool same = c == d;                              // both kept entries from one pair
+  const float va = a ? v[0] : v[1], vb = b ? v[2] : v[3];
+  vlo = same ? (c ? v[0] : v[2]) : va;
+  vhi = same ? (c ? v[1] : v[3]) : vb;
+  return same ? (c ? 4u : 14u) : ((a ? 0u : 1u) | (b ? 8u : 12u));
+}
+
 }  // namespace spa

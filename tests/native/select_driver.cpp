@@ -2,6 +2,9 @@
 // scores from stdin, writes the keep bits of each block to stdout.
 //   input:  m n count, then count*m floats
 //   output: count unsigned integers
+// With m = 0 it runs the 2:4 tournament instead (n ignored, blocks of 4):
+// each line is the keep bits of the returned position code, then the
+// positions of the two values it returned (values v[j] = j are passed in).
 #include <cstdio>
 #include <cstring>
 #include <vector>
@@ -20,10 +23,25 @@ static void run(int n, int count) {
   }
 }
 
+static void run_top2(int count) {
+  std::vector<float> f((size_t)count * 4);
+  for (auto& v : f)
+    if (std::scanf("%f", &v) != 1) return;
+  const float pos[4] = {0.f, 1.f, 2.f, 3.f};
+  for (int b = 0; b < count; ++b) {
+    const float s[4] = {f[4 * b], f[4 * b + 1], f[4 * b + 2], f[4 * b + 3]};
+    float lo = -1.f, hi = -1.f;
+    const uint32_t code = spa::top2of4(s, pos, lo, hi);
+    const uint32_t keep = (1u << (code & 3u)) | (1u << ((code >> 2) & 3u));
+    std::printf("%u %d %d %u\n", keep, (int)lo, (int)hi, code);
+  }
+}
+
 int main() {
   int m, n, count;
   if (std::scanf("%d %d %d", &m, &n, &count) != 3) return 1;
   switch (m) {
+    case 0: run_top2(count); break;
     case 4: run<4>(n, count); break;
     case 8: run<8>(n, count); break;
     case 16: run<16>(n, count); break;

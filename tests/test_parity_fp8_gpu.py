@@ -74,15 +74,20 @@ def _fp8_oracle(spec, x, w, f=None, eta_in=None):
                          eta_in=None if eta_in is None else f32(eta_in), var_rescale=spec.var_rescale, act=spec.act)
 
 
-@pytest.mark.parametrize("spec", FP8_CASES, ids=[s.name for s in FP8_CASES])
-def test_prefill_fp8_parity(spec):
-    dev = _dev()
+def _fp8_inputs(spec):
     x, w = wl.make_inputs(spec)
     if spec.shift == "token_mean" and spec.t > 2:
         x[1] = x[1, 0]                                           # a constant row: x - eta == 0, scale 0
     if spec.name == "fp8_weight_pruned_max":
         x[:, 9] = 12.0
         w[:, 9] *= 1e-3
+    return x, w
+
+
+@pytest.mark.parametrize("spec", FP8_CASES, ids=[s.name for s in FP8_CASES])
+def test_prefill_fp8_parity(spec):
+    dev = _dev()
+    x, w = _fp8_inputs(spec)
     eta_in = wl.make_eta(spec.t, 9) if spec.shift == "given" else None
     print(f"[fp8 prefill] {spec.name}: t={spec.t} k={spec.k} n_out={spec.n_out} {spec.score} {spec.shift}",
           flush=True)
@@ -118,6 +123,41 @@ def test_prefill_fp8_parity(spec):
     assert err <= O.TOLERANCE[spec.dtype], err
 
 
+# Neither positions nor nu asked for, no variance factor (the benchmark's
+# call): the lean pruning pass, here also on rows of two and four passes.
+FP8_LEAN_CASES = [s for s in FP8_CASES if not s.var_rescale] + [
+    wl.SPECS["prefill"].with_(name="fp8_k8192", t=21, k=8192, n_out=40),
+    wl.SPECS["relu2_fused"].with_(name="fp8_k16384_mean", t=18, k=16384, n_out=40, shift="token_mean"),
+]
+
+
+@pytest.mark.parametrize("spec", FP8_LEAN_CASES, ids=[s.name for s in FP8_LEAN_CASES])
+def test_prefill_fp8_operand_only(spec):
+    dev = _dev()
+    x, w = _fp8_inputs(spec)
+    eta_in = wl.make_eta(spec.t, 9) if spec.shift == "given" else None
+    print(f"[fp8 operand only] {spec.name}: t={spec.t} k={spec.k} n_out={spec.n_out}", flush=True)
+    wd = w.to(dev)
+    pw = spa.prepare_weight(wd, spec.alpha, want_wt=False)
+    w8 = spa.prepare_weight_fp8(wd)
+    f = f32(pw.chan_scale) if spec.score == "weight" else None
+    pr = _fp8_oracle(spec, x, w, f=f, eta_in=eta_in)
+    cfg = _cfg(spec)
+    ws = spa.workspace(2, spec.t, spec.k, spec.n_out, x.dtype, cfg, dev)
+    y, idx, nu = spa.sparse_linear_prefill_fp8(x.to(dev), pw, w8, cfg,
+                                               eta_in=None if eta_in is None else eta_in.to(dev), ws=ws)
+    torch.cuda.synchronize()
+    assert idx is None and nu is None
+    codes, pos, sx = tiled_operand(ws, spa.prefill_layout(spec.t, spec.k, x.dtype, cfg), spec.t, spec.k, True,
+                                   spec.dtype)
+    assert np.array_equal(pos, pr["idx"]), "position words differ"
+    assert np.array_equal(sx.view(np.uint32), pr["sx"].view(np.uint32)), "FP8 token scales differ"
+    want_codes = pr["qx"][pr["keep"].reshape(spec.t, spec.k)].reshape(spec.t, spec.k // 2)
+    assert np.array_equal(codes, want_codes), f"{int((codes != want_codes).sum())} e4m3 activation codes differ"
+    err = O.rowwise_error(f32(y), pr["y"])
+    assert err <= O.TOLERANCE[spec.dtype], err
+
+
 def test_prefill_fp8_rejections():
     dev = _dev()
     spec = wl.SPECS["prefill"].with_(t=8, k=256, n_out=64)
@@ -130,8 +170,10 @@ def test_prefill_fp8_rejections():
     assert e.value.status == 2
 
 
-def test_prefill_fp8_full_size_sampled():
-    # the prompt workload (2048 tokens, 4096 -> 14336) on sampled rows and columns
+@pytest.mark.parametrize("outputs", ["all", "operand"])
+def test_prefill_fp8_full_size_sampled(outputs):
+    # the prompt workload (2048 tokens, 4096 -> 14336) on sampled rows and
+    # columns, with positions and nu asked for, and without (the lean pass)
     dev = _dev()
     spec = wl.SPECS["prefill"]
     print(f"[fp8 full size] t={spec.t} k={spec.k} n_out={spec.n_out}", flush=True)
@@ -141,20 +183,23 @@ def test_prefill_fp8_full_size_sampled():
     w8 = spa.prepare_weight_fp8(wd)
     cfg = _cfg(spec)
     wsp = spa.workspace(2, spec.t, spec.k, spec.n_out, x.dtype, cfg, dev)
-    y, idx, nu = spa.sparse_linear_prefill_fp8(x.to(dev), pw, w8, cfg, want_idx=True, want_nu=True, ws=wsp)
+    every = outputs == "all"
+    y, idx, nu = spa.sparse_linear_prefill_fp8(x.to(dev), pw, w8, cfg, want_idx=every, want_nu=every, ws=wsp)
     torch.cuda.synchronize()
     rng = np.random.default_rng(3)
     rows = np.unique(np.concatenate([rng.choice(spec.t, 24, replace=False), [0, spec.t - 1]]))
     cols = np.unique(np.concatenate([rng.choice(spec.n_out, 96, replace=False), [0, spec.n_out - 1]]))
     xs, ws = x[torch.as_tensor(rows)], w[torch.as_tensor(cols)]
     pr = _fp8_oracle(spec, xs, ws)
-    assert np.array_equal(idx.cpu().numpy()[rows], pr["idx"])
-    assert np.allclose(f32(nu)[rows], pr["nu"], rtol=1e-6, atol=0)
+    if every:
+        assert np.array_equal(idx.cpu().numpy()[rows], pr["idx"])
+        assert np.allclose(f32(nu)[rows], pr["nu"], rtol=1e-6, atol=0)
     codes, pos, sx = tiled_operand(wsp, spa.prefill_layout(spec.t, spec.k, x.dtype, cfg), spec.t, spec.k, True,
                                    spec.dtype)
     assert np.array_equal(sx[rows].view(np.uint32), pr["sx"].view(np.uint32)), "FP8 token scales differ"
     want = pr["qx"][pr["keep"]].reshape(rows.size, spec.k // 2)
     assert np.array_equal(codes[rows], want), "e4m3 activation codes differ"
+    assert np.array_equal(pos[rows], pr["idx"]), "position words differ"
     q, s = O.fp8_rows(f32(ws))
     assert np.array_equal(w8.codes.cpu().numpy()[cols], q)
     assert np.array_equal(f32(w8.scale)[cols].view(np.uint32), s.view(np.uint32))

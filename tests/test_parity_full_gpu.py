@@ -17,7 +17,7 @@ import torch
 
 import workloads as wl
 from oracle import nm_oracle as O
-from gpu_util import f32
+from gpu_util import f32, storage_bits, tiled_operand
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +84,40 @@ def test_full_size_sampled(name):
     y_ref = O.linear(pr, f32(w[torch.as_tensor(cols)]))
     y_got = f32(y)[np.ix_(rows, cols)]
     err = O.rowwise_error(y_got, y_ref)
+    assert err <= O.TOLERANCE[spec.dtype], f"{name}: sampled y error {err}"
+
+
+@pytest.mark.parametrize("name", ["prefill", "relu2", "relu2_fused"])
+def test_full_size_operand_as_timed(name):
+    """The prompt workloads called as they are timed (no positions, no nu:
+    the lean pruning pass): the 2:4 operand on every row holds two ascending
+    in-block positions per block; on sampled rows the packed values, the
+    positions and the shift equal the oracle's bit for bit; y on sampled rows
+    x sampled columns."""
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    dev = torch.device("cuda:0")
+    spec = FULL[name]
+    print(f"[full-size operand] {name}: t={spec.t} k={spec.k} n_out={spec.n_out}", flush=True)
+    x, w = wl.make_inputs(spec)
+    pw = spa.prepare_weight(w.to(dev), spec.alpha, want_wt=False)
+    cfg = spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, spec.var_rescale, spec.act)
+    ws = spa.workspace(2, spec.t, spec.k, spec.n_out, x.dtype, cfg, dev)
+    y, idx, nu = spa.sparse_linear_prefill(x.to(dev), pw, cfg, ws=ws)
+    torch.cuda.synchronize()
+    assert idx is None and nu is None
+    lay = spa.prefill_layout(spec.t, spec.k, x.dtype, cfg)
+    vals, pos, _ = tiled_operand(ws, lay, spec.t, spec.k, False, spec.dtype)
+    p2 = pos.reshape(spec.t, spec.k // 4, 2).astype(np.int64)
+    assert p2.max() < 4 and (p2[..., 0] < p2[..., 1]).all(), "position words malformed"
+    rows = _sample(spec.t, 24, 5)
+    pr = O.prune(f32(x[torch.as_tensor(rows)]), spec.dtype, spec.n, spec.m, score=spec.score, shift_mode=spec.shift,
+                 act=spec.act)
+    assert np.array_equal(pos[rows], pr["idx"]), f"{name}: positions differ on sampled rows"
+    assert np.array_equal(vals[rows], storage_bits(pr["vals"], spec.dtype)), f"{name}: packed values differ"
+    eta = ws.cpu().numpy().view(np.uint8)[lay["eta"]:lay["eta"] + 4 * spec.t].view(np.float32)
+    assert np.array_equal(eta[rows].view(np.uint32), pr["eta"].view(np.uint32)), f"{name}: shift differs"
+    cols = _sample(spec.n_out, 96, 6)
+    err = O.rowwise_error(f32(y)[np.ix_(rows, cols)], O.linear(pr, f32(w[torch.as_tensor(cols)])))
     assert err <= O.TOLERANCE[spec.dtype], f"{name}: sampled y error {err}"
 
 

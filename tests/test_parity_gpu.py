@@ -553,3 +553,44 @@ def test_prefill_parity(spec):
         assert np.array_equal(raw.reshape(spec.t, spec.k), storage_bits(masked, spec.dtype)), "masked rows differ"
     err = O.rowwise_error(f32(y), pr["y"])
     assert err <= O.TOLERANCE[spec.dtype], err
+
+
+# A call that asks for neither positions nor nu, with no variance factor, as
+# the benchmark makes it: 16-bit 2:4 rows of at most 16384 channels take the
+# lean pruning pass (a persistent grid over the rows, a register ring).  The
+# 2:4 cases above, plus rows of two, three and four 256-segment passes, a
+# token count that gives each workgroup several rows, and the weight factor.
+LEAN_CASES = [s for s in PREFILL_CASES if s.n == 2 and s.m == 4 and not s.var_rescale]
+LEAN_CASES += [
+    wl.SPECS["relu2"].with_(name="lean_k16384", t=24, k=16384, n_out=72),
+    wl.SPECS["relu2_fused"].with_(name="lean_k12288_mean", t=19, k=12288, n_out=40, shift="token_mean"),
+    wl.SPECS["prefill"].with_(name="lean_k8192_given", t=33, k=8192, n_out=48, shift="given"),
+    wl.SPECS["prefill"].with_(name="lean_many_rows", t=3000, k=128, n_out=40),
+    wl.SPECS["prefill"].with_(name="lean_weight", t=50, k=1024, n_out=96, score="weight", alpha=0.5),
+]
+
+
+@pytest.mark.parametrize("spec", LEAN_CASES, ids=[s.name for s in LEAN_CASES])
+def test_prefill_operand_only(spec):
+    dev = _dev()
+    x, w = wl.make_inputs(spec)
+    eta_in = wl.make_eta(spec.t, 9) if spec.shift == "given" else None
+    print(f"[prefill operand only] {spec.name}: t={spec.t} k={spec.k} n_out={spec.n_out}", flush=True)
+    pw = spa.prepare_weight(w.to(dev), spec.alpha, want_wt=False)
+    f = f32(pw.chan_scale) if spec.score == "weight" else None
+    pr = oracle_for(spec, x, w, f=f, eta_in=eta_in)
+    cfg = _cfg(spec)
+    ws = spa.workspace(2, spec.t, spec.k, spec.n_out, x.dtype, cfg, dev)
+    y, idx, nu = spa.sparse_linear_prefill(x.to(dev), pw, cfg, eta_in=None if eta_in is None else eta_in.to(dev),
+                                           ws=ws)
+    torch.cuda.synchronize()
+    assert idx is None and nu is None
+    # every row: the packed values and position words, and the shift, bit for bit
+    lay = spa.prefill_layout(spec.t, spec.k, x.dtype, cfg)
+    vals, pos, _ = tiled_operand(ws, lay, spec.t, spec.k, False, spec.dtype)
+    assert np.array_equal(pos, pr["idx"]), "position words differ"
+    assert np.array_equal(vals, storage_bits(pr["vals"], spec.dtype)), "packed operand differs"
+    eta = ws.cpu().numpy().view(np.uint8)[lay["eta"]:lay["eta"] + 4 * spec.t].view(np.float32)
+    assert np.array_equal(eta.view(np.uint32), pr["eta"].view(np.uint32)), "shift differs"
+    err = O.rowwise_error(f32(y), pr["y"])
+    assert err <= O.TOLERANCE[spec.dtype], err
