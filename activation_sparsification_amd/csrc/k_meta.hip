@@ -113,7 +113,8 @@ __device__ __forceinline__ uint32_t add_pos(uint32_t code, uint32_t c, int j, in
 template <int NV>
 constexpr int groups_per_thread() { return 1; }
 
-template <int NV>
+// C24: 2:4 combinatorial codes, formed and read without the table.
+template <int NV, bool C24>
 __global__ void __launch_bounds__(256) k_encode_meta(MetaArgs a) {
   constexpr int BT = blocks_per_thread<NV>(), G = groups_per_thread<NV>();
   extern __shared__ uint32_t s_dyn[];
@@ -125,7 +126,8 @@ __global__ void __launch_bounds__(256) k_encode_meta(MetaArgs a) {
   const int nw = 2 * G * BT * w;                           // words of this wave
   uint32_t* s_words = s_dyn + wv * nw;
   const int64_t wb = (int64_t)(chunk * 4 + wv) * G * 64 * BT;   // the wave's first block
-  if (a.format == SPA_META_COMB) load_tab(s_binom, NV ? NV : a.n);
+  // 2:4 codes need no table: C(lo, 1) + C(hi, 2) = lo + hi (hi - 1) / 2
+  if (a.format == SPA_META_COMB && !C24) load_tab(s_binom, NV ? NV : a.n);
   for (int j = lane; j < nw; j += 64) s_words[j] = 0u;
 
   const uint8_t* rp = a.idx + (size_t)row * a.nb * (NV ? NV : a.n);
@@ -141,8 +143,13 @@ __global__ void __launch_bounds__(256) k_encode_meta(MetaArgs a) {
 #pragma unroll
       for (int q = 0; q < BT; ++q) {
         uint32_t v = 0;
+        if constexpr (C24) {
+          const uint32_t lo = c[g][q * NV] & 31u, hi = c[g][q * NV + NV - 1] & 31u;
+          v = lo + hi * (hi - 1u) / 2u;
+        } else {
 #pragma unroll
-        for (int jj = 0; jj < NV; ++jj) v = add_pos(v, c[g][q * NV + jj], jj, a.format, s_binom);
+          for (int jj = 0; jj < NV; ++jj) v = add_pos(v, c[g][q * NV + jj], jj, a.format, s_binom);
+        }
         code[g][q] = b + q < a.nb ? v : 0u;
       }
     }
@@ -174,7 +181,7 @@ __global__ void __launch_bounds__(256) k_encode_meta(MetaArgs a) {
     if (gbase + j < a.row_words) out[gbase + j] = s_words[j];
 }
 
-template <int NV>
+template <int NV, bool C24>
 __global__ void __launch_bounds__(256) k_decode_meta(MetaArgs a) {
   constexpr int BT = blocks_per_thread<NV>(), G = groups_per_thread<NV>();
   constexpr int CAP = NV ? NV : 32;                        // positions per block held in registers
@@ -188,7 +195,11 @@ __global__ void __launch_bounds__(256) k_decode_meta(MetaArgs a) {
   const int nw = 2 * G * BT * w;
   uint32_t* s_words = s_dyn + wv * nw;
   const int64_t wb = (int64_t)(chunk * 4 + wv) * G * 64 * BT;
-  if (a.format == SPA_META_COMB) load_tab(s_binom, n);
+  // 2:4 codes 0..5 name the pairs {0,1}, {0,2}, {1,2}, {0,3}, {1,3}, {2,3}
+  // (colex order): nibble `code` of kPairs24 holds lo | hi << 2; the unused
+  // codes 6 and 7 give {2,3}, as the greedy unranking below does
+  constexpr uint32_t kPairs24 = 0xEEEDC984u;
+  if (a.format == SPA_META_COMB && !C24) load_tab(s_binom, n);
   {
     const int64_t gbase = (wb * w) >> 5;
     const uint32_t* in = a.codes + (size_t)row * a.row_words;
@@ -210,7 +221,10 @@ __global__ void __launch_bounds__(256) k_decode_meta(MetaArgs a) {
         code = (uint32_t)((v >> sh) & ((uint64_t(1) << w) - 1));
       }
       uint32_t mask = code;
-      if (a.format == SPA_META_COMB) {
+      if constexpr (C24) {
+        const uint32_t pr = (kPairs24 >> (4u * code)) & 15u;    // code < 8 (3 bits)
+        mask = (1u << (pr & 3u)) | (1u << (pr >> 2));
+      } else if (a.format == SPA_META_COMB) {
         // greedy unranking in one pass over the positions, largest first: take
         // c while i positions remain and C(c, i) <= the remaining rank (C(c, i)
         // is 0 once c < i, so exactly n are taken); the same m steps on every
@@ -253,10 +267,16 @@ static hipError_t meta_launch(const MetaArgs& a, int t, hipStream_t st) {
 #define SPA_META_CASE(NV)                                                                            \
   {                                                                                                  \
     const size_t lds = (size_t)4 * 2 * groups_per_thread<NV>() * blocks_per_thread<NV>() * a.width * 4; \
-    if (ENCODE) hipLaunchKernelGGL(k_encode_meta<NV>, grid, dim3(256), lds, st, a);                  \
-    else hipLaunchKernelGGL(k_decode_meta<NV>, grid, dim3(256), lds, st, a);                         \
+    if (ENCODE) hipLaunchKernelGGL((k_encode_meta<NV, false>), grid, dim3(256), lds, st, a);         \
+    else hipLaunchKernelGGL((k_decode_meta<NV, false>), grid, dim3(256), lds, st, a);                \
   }                                                                                                  \
   break;
+  if (a.n == 2 && a.m == 4 && a.format == SPA_META_COMB) {
+    const size_t lds = (size_t)4 * 2 * groups_per_thread<2>() * blocks_per_thread<2>() * a.width * 4;
+    if (ENCODE) hipLaunchKernelGGL((k_encode_meta<2, true>), grid, dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((k_decode_meta<2, true>), grid, dim3(256), lds, st, a);
+    return hipGetLastError();
+  }
   switch (a.n) {
     case 1: SPA_META_CASE(1)
     case 2: SPA_META_CASE(2)
