@@ -187,9 +187,10 @@ __device__ __forceinline__ void store_tile_lds(const PrefillArgs& p, const f32x1
 // ---------------------------------------------------------------------------
 template <int DT, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) k_gemm24(PrefillArgs p) {
-  static_assert(NW == 8 || NW == 16, "8 waves of 128 x 64 or 16 of 64 x 64");
-  constexpr int BM = 256, BN = 256;
+  static_assert(NW == 8 || NW == 12 || NW == 16, "8 waves of 128 x 64, or 12 or 16 of 64 x 64");
+  constexpr int BM = 256, BN = NW == 12 ? 192 : 256;
   constexpr int WM = NW == 8 ? 128 : 64, WN = 64, FM = WM / 32, FN = 2;
+  constexpr int WC = BN / WN;                              // wave columns
   using V8 = typename Frag<DT>::V8;
   using V16 = typename Frag<DT>::V16;
   // stage = packed activations (BM x 64 B) followed by their position words
@@ -201,32 +202,38 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm24(PrefillArgs p) {
 
   const int K = p.k, N = p.n_out, TP = p.t_pad;
   int tm, tn;
-  xcd_tile(p.t, N, BM, BN, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  xcd_tile(p.t, p.col1 - p.col0, BM, BN, tm, tn);
+  const int m0 = tm * BM, n0 = p.col0 + tn * BN;
   TileScalars<BM, BN> ts;
   ts.fetch(p, m0, n0);
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int g = lane >> 5, l32 = lane & 31;
-  const int wm0 = (wv >> 2) * WM, wn0 = (wv & 3) * WN;
+  const int wm0 = (wv / WC) * WM, wn0 = (wv % WC) * WN;
 
   // ---- direct-load sources: uniform per-step bases + 32-bit lane offsets ----
   const char* baseA = static_cast<const char*>(p.a_vals) + (size_t)m0 * 64;
   const char* baseM = reinterpret_cast<const char*>(p.a_meta) + (size_t)m0 * 8;
   const char* baseW = static_cast<const char*>(p.w) + (size_t)n0 * K * 2;
   const size_t stepA = (size_t)TP * 64, stepM = (size_t)TP * 8;
-  // Per step, 8 waves: wave wv loads activation runs h = 0, 1 (LDS slot s of
-  // run h holds row 16 (2 wv + h) + s/4), weight groups h = 0..3 (slot s of
-  // group h holds row 8 (4 wv + h) + s/8) and the position words of rows
-  // 32 wv .. +31.  16 waves: activation run wv, weight groups 2 wv, 2 wv + 1,
-  // and waves 0-7 the position words as above.
-  constexpr int NA = NW == 8 ? 2 : 1, NB = NW == 8 ? 4 : 2;
+  // Per step, 8 waves: wave wv loads activation runs 2 wv, 2 wv + 1 (LDS slot
+  // s of run r holds row 16 r + s/4), weight groups h = 0..3 (slot s of group
+  // h holds row 8 (4 wv + h) + s/8) and the position words of rows 32 wv ..
+  // +31.  16 waves: activation run wv, weight groups 2 wv, 2 wv + 1, and waves
+  // 0-7 the position words as above.  12 waves (192 columns): activation run
+  // wv and, for waves 0-3, run 12 + wv; weight groups 2 wv, 2 wv + 1; waves
+  // 0-7 the position words.
+  constexpr int NA = NW == 16 ? 1 : 2, NB = NW == 8 ? 4 : 2;
   const bool loads_m = NW == 8 || wv < 8;                 // wave-uniform
+  const bool loads_a2 = NW != 12 || wv < 4;               // the second activation run
+  int runA[NA];
+#pragma unroll
+  for (int h = 0; h < NA; ++h) runA[h] = NW == 8 ? 2 * wv + h : h == 0 ? wv : 12 + wv;
   uint32_t offA[NA], offB[NB];
 #pragma unroll
   for (int h = 0; h < NA; ++h) {
-    const int ra = 16 * (NA * wv + h) + (lane >> 2);
+    const int ra = 16 * runA[h] + (lane >> 2);
     offA[h] = (uint32_t)(ra * 64 + (((lane & 3) ^ ((ra >> 2) & 3)) * 16));
   }
 #pragma unroll
@@ -254,16 +261,19 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm24(PrefillArgs p) {
   do {                                                                                   \
     const char* a_ = baseA + (size_t)(KT) * stepA;                                       \
     const char* w_ = baseW + (size_t)(KT) * 128;                                         \
-    const uint32_t la_ = ldsA0 + (ST) * AST + wv * (NA * 1024), lb_ = ldsB0 + (ST) * BST + wv * (NB * 1024); \
-    _Pragma("unroll") for (int h = 0; h < NA; ++h) lds_dma16(a_, offA[h], la_ + h * 1024); \
+    const uint32_t la_ = ldsA0 + (ST) * AST, lb_ = ldsB0 + (ST) * BST + wv * (NB * 1024); \
+    _Pragma("unroll") for (int h = 0; h < NA; ++h)                                       \
+      if (h == 0 || loads_a2) lds_dma16(a_, offA[h], la_ + runA[h] * 1024);             \
     _Pragma("unroll") for (int h = 0; h < NB; ++h) lds_dma16(w_, offB[h], lb_ + h * 1024); \
     if (loads_m)                                                                         \
       lds_dma4(baseM + (size_t)(KT) * stepM, offM, ldsA0 + (ST) * AST + BM * 64 + (wv & 7) * 256); \
   } while (0)
-  // loads per step: 7 for 8 waves; 4 (waves 0-7) or 3 for 16 waves
+  // loads per step: 7 for 8 waves; 4 (waves 0-7) or 3 for 16 waves; 5 (waves
+  // 0-3), 4 (waves 4-7) or 3 for 12 waves
 #define SPA_WAIT24(COND)                                                                 \
   do {                                                                                   \
     if constexpr (NW == 8) wait_vm<7>(COND);                                             \
+    else if (NW == 12 && loads_a2) wait_vm<5>(COND);                                     \
     else if (loads_m) wait_vm<4>(COND);                                                  \
     else wait_vm<3>(COND);                                                               \
   } while (0)
@@ -558,22 +568,51 @@ __global__ void __launch_bounds__(512, 1) k_gemm_dense(PrefillArgs p) {
   }
 }
 
+// The CUs of the current device (queried once).
+static int device_cus() {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 256;
+    return n > 0 ? n : 256;
+  }();
+  return cus;
+}
+
+template <int DT>
+static void gemm24_launch(const PrefillArgs& a, hipStream_t st) {
+  // One workgroup per CU at a time.  When the 256 x 256 tiles leave a last
+  // round at most three quarters full, whole rounds of them cover the first
+  // columns and one round of 256 x 192 tiles the rest: 2048 x 4096 -> 14336
+  // runs 256 + 256 workgroups (about 1.75 tile times) instead of 448 (two).
+  // Up to 128 k steps per tile the 256-column tiles use 16 waves (four per
+  // SIMD), beyond that 8: level with each other where both were measured.
+  const bool w16 = a.k <= 8192;
+  const int tm = (a.t + 255) / 256, tn = (a.n_out + 255) / 256, cus = device_cus();
+  const int full = tm * tn / cus, rem = tm * tn - full * cus;
+  int n1 = a.n_out;
+  if (full >= 1 && rem > 0 && 4 * rem <= 3 * cus && (full * cus) % tm == 0) {
+    const int c1 = full * cus / tm * 256;
+    if (c1 < a.n_out && tm * ((a.n_out - c1 + 191) / 192) <= cus) n1 = c1;
+  }
+  PrefillArgs b = a;
+  b.col0 = 0;
+  b.col1 = n1;
+  const int tiles = tm * ((n1 + 255) / 256);
+  if (w16) hipLaunchKernelGGL((k_gemm24<DT, 16>), dim3(tiles), dim3(1024), 0, st, b);
+  else hipLaunchKernelGGL((k_gemm24<DT, 8>), dim3(tiles), dim3(512), 0, st, b);
+  if (n1 < a.n_out) {
+    b.col0 = n1;
+    b.col1 = a.n_out;
+    hipLaunchKernelGGL((k_gemm24<DT, 12>), dim3(tm * ((a.n_out - n1 + 191) / 192)), dim3(768), 0, st, b);
+  }
+}
+
 hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st) {
   if (a.t == 0) return hipSuccess;
   if (a.sparse24) {
-    const int tiles = ((a.t + 255) / 256) * ((a.n_out + 255) / 256);
-    // up to 128 k steps per tile, 16 waves (four per SIMD); with two-byte
-    // epilogue stores they were ahead at 2048 x 4096 -> 14336 (160.8 vs
-    // 164.7 us), with the LDS-staged epilogue the two forms are level there
-    // (160.4 vs 160.3 us) and at 16384 channels
-    const bool w16 = a.k <= 8192;
-    if (dtype == SPA_F16) {
-      if (w16) hipLaunchKernelGGL((k_gemm24<SPA_F16, 16>), dim3(tiles), dim3(1024), 0, st, a);
-      else hipLaunchKernelGGL((k_gemm24<SPA_F16, 8>), dim3(tiles), dim3(512), 0, st, a);
-    } else {
-      if (w16) hipLaunchKernelGGL((k_gemm24<SPA_BF16, 16>), dim3(tiles), dim3(1024), 0, st, a);
-      else hipLaunchKernelGGL((k_gemm24<SPA_BF16, 8>), dim3(tiles), dim3(512), 0, st, a);
-    }
+    if (dtype == SPA_F16) gemm24_launch<SPA_F16>(a, st);
+    else gemm24_launch<SPA_BF16>(a, st);
   } else {
     const int tiles = ((a.t + 255) / 256) * ((a.n_out + 127) / 128);
     if (dtype == SPA_F16) hipLaunchKernelGGL((k_gemm_dense<SPA_F16, 0>), dim3(tiles), dim3(512), 0, st, a);

@@ -118,6 +118,8 @@ struct PrefillArgs {
   // e4m3 codes; y = sx[i] * sw[j] * acc (* nu) + eta * row_sum
   const float* sx;           // [t]
   const float* sw;           // [n_out]
+  // 2:4 GEMM: the output columns [col0, col1) this launch covers (launch_gemm sets them)
+  int col0, col1;
 };
 hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st);
 hipError_t launch_ffn_up(int dtype, const PrefillArgs& a, hipStream_t st);

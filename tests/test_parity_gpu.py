@@ -514,6 +514,10 @@ PREFILL_CASES.append(wl.SPECS["batched"].with_(name="pre_act_clact_mean", t=96, 
 PREFILL_CASES.append(wl.SPECS["relu2_fused"].with_(name="pre_act_8_16", t=77, k=320, n_out=300, n=8, m=16))
 PREFILL_CASES.append(wl.SPECS["relu2_fused"].with_(name="pre_act_long_row", t=40, k=8192, n_out=136,
                                                    shift="token_mean", var_rescale=True))
+# more 256 x 256 tiles than one round of 256 CUs, the last round at most three
+# quarters full: whole rounds of those tiles, then one round of 256 x 192
+# tiles over the last columns (ragged token tile, ragged last column tile)
+PREFILL_CASES.append(wl.SPECS["prefill"].with_(name="pre_tail_split", t=300, k=128, n_out=35000, n_outliers=2))
 # k-step counts 1, 3 and 12 (the GEMMs run three k steps per loop turn with a
 # peeled tail), and several ragged tiles in both directions
 for n, m in [(2, 4), (4, 8)]:
@@ -552,6 +556,23 @@ def test_prefill_parity(spec):
         masked = O.round_to_dtype(np.where(pr["keep"], pr["xhat"], np.float32(0.0)), spec.dtype)
         assert np.array_equal(raw.reshape(spec.t, spec.k), storage_bits(masked, spec.dtype)), "masked rows differ"
     err = O.rowwise_error(f32(y), pr["y"])
+    assert err <= O.TOLERANCE[spec.dtype], err
+
+
+def test_prefill_tail_split_eight_waves():
+    # the same split behind the 8-wave tiles of rows over 8192 channels:
+    # 1024 x 8256 -> 16640 is 260 tiles, 256 of them one round and the last
+    # 256 columns two 192-wide tiles per token tile; sampled rows, every column
+    dev = _dev()
+    spec = wl.SPECS["prefill"].with_(name="pre_tail_split_8w", t=1024, k=8256, n_out=16640, n_outliers=4)
+    x, w = wl.make_inputs(spec)
+    pw = spa.prepare_weight(w.to(dev), spec.alpha, want_wt=False)
+    y, idx, nu = spa.sparse_linear_prefill(x.to(dev), pw, _cfg(spec), want_idx=True, want_nu=True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 511, 700, 1022, 1023])
+    pr = O.prune(f32(x[torch.as_tensor(rows)]), spec.dtype, spec.n, spec.m, score=spec.score, shift_mode=spec.shift)
+    assert np.array_equal(idx.cpu().numpy()[rows], pr["idx"]), "positions differ on sampled rows"
+    err = O.rowwise_error(f32(y)[rows], O.linear(pr, f32(w)))
     assert err <= O.TOLERANCE[spec.dtype], err
 
 
