@@ -579,22 +579,27 @@ static int device_cus() {
   return cus;
 }
 
+// One workgroup per CU at a time.  When the 256 x 256 tiles leave a last
+// round at most three quarters full, whole rounds of them cover the first
+// columns and one round of 256 x 192 tiles the rest: 2048 x 4096 -> 14336
+// runs 256 + 256 workgroups (about 1.75 tile times) instead of 448 (two).
+// Returns where the 192-column tiles start (n_out: no split).
+static int balanced_cols(int t, int n_out) {
+  const int tm = (t + 255) / 256, tn = (n_out + 255) / 256, cus = device_cus();
+  const int full = tm * tn / cus, rem = tm * tn - full * cus;
+  if (full >= 1 && rem > 0 && 4 * rem <= 3 * cus && (full * cus) % tm == 0) {
+    const int c1 = full * cus / tm * 256;
+    if (c1 < n_out && tm * ((n_out - c1 + 191) / 192) <= cus) return c1;
+  }
+  return n_out;
+}
+
 template <int DT>
 static void gemm24_launch(const PrefillArgs& a, hipStream_t st) {
-  // One workgroup per CU at a time.  When the 256 x 256 tiles leave a last
-  // round at most three quarters full, whole rounds of them cover the first
-  // columns and one round of 256 x 192 tiles the rest: 2048 x 4096 -> 14336
-  // runs 256 + 256 workgroups (about 1.75 tile times) instead of 448 (two).
   // Up to 128 k steps per tile the 256-column tiles use 16 waves (four per
   // SIMD), beyond that 8: level with each other where both were measured.
   const bool w16 = a.k <= 8192;
-  const int tm = (a.t + 255) / 256, tn = (a.n_out + 255) / 256, cus = device_cus();
-  const int full = tm * tn / cus, rem = tm * tn - full * cus;
-  int n1 = a.n_out;
-  if (full >= 1 && rem > 0 && 4 * rem <= 3 * cus && (full * cus) % tm == 0) {
-    const int c1 = full * cus / tm * 256;
-    if (c1 < a.n_out && tm * ((a.n_out - c1 + 191) / 192) <= cus) n1 = c1;
-  }
+  const int tm = (a.t + 255) / 256, n1 = balanced_cols(a.t, a.n_out);
   PrefillArgs b = a;
   b.col0 = 0;
   b.col1 = n1;
@@ -640,16 +645,17 @@ hipError_t launch_gemm(int dtype, const PrefillArgs& a, hipStream_t st) {
 // activation row r sits at c ^ ((r >> 3) & 1), of weight row r at
 // c ^ ((r >> 2) & 3).  y = nu_i * sx_i * sw_j * acc + eta_i * s_j.
 // ---------------------------------------------------------------------------
-template <int DT>
-__global__ void __launch_bounds__(1024, 1) k_gemm24_fp8(PrefillArgs p) {
-  constexpr int BM = 256, BN = 256;
-  constexpr int WM = 64, WN = 64, FM = 2, FN = 2;
+template <int DT, int NW>
+__global__ void __launch_bounds__(NW * 64, 1) k_gemm24_fp8(PrefillArgs p) {
+  static_assert(NW == 12 || NW == 16, "waves of 64 x 64 over 192 or 256 columns");
+  constexpr int BM = 256, BN = NW == 12 ? 192 : 256;
+  constexpr int WM = 64, WN = 64, FM = 2, FN = 2, WC = BN / WN;
   constexpr int AST = BM * 40, BST = BN * 64;               // bytes per stage
   typedef int v4i __attribute__((ext_vector_type(4)));
   typedef int v8i __attribute__((ext_vector_type(8)));
   // one ring: three activation stages, then three weight stages, sized up
-  // to 128 KB so that it also holds the 16 waves' 8 KB output blocks
-  constexpr int RING = 3 * (AST + BST) > 16 * 8192 ? 3 * (AST + BST) : 16 * 8192;
+  // so that it also holds the waves' 8 KB output blocks
+  constexpr int RING = 3 * (AST + BST) > NW * 8192 ? 3 * (AST + BST) : NW * 8192;
   static_assert((3 * AST) % 1024 == 0, "weight stages 1 KB aligned");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[RING];
   unsigned char* const sA = ring;
@@ -658,8 +664,8 @@ __global__ void __launch_bounds__(1024, 1) k_gemm24_fp8(PrefillArgs p) {
 
   const int K = p.k, N = p.n_out, TP = p.t_pad;
   int tm, tn;
-  xcd_tile(p.t, N, BM, BN, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  xcd_tile(p.t, p.col1 - p.col0, BM, BN, tm, tn);
+  const int m0 = tm * BM, n0 = p.col0 + tn * BN;
   TileScalars<BM, BN> ts;
   ts.fetch(p, m0, n0);
   const float sx_own = (int)threadIdx.x < BM ? p.sx[min(m0 + (int)threadIdx.x, p.t - 1)] : 0.f;
@@ -668,7 +674,7 @@ __global__ void __launch_bounds__(1024, 1) k_gemm24_fp8(PrefillArgs p) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int g = lane >> 5, l32 = lane & 31;
-  const int wm0 = (wv >> 2) * WM, wn0 = (wv & 3) * WN;
+  const int wm0 = (wv / WC) * WM, wn0 = (wv % WC) * WN;
   const bool loads_a = wv < 8;                              // wave-uniform
 
   const char* baseA = static_cast<const char*>(p.a_vals) + (size_t)m0 * 32;
@@ -745,16 +751,31 @@ __global__ void __launch_bounds__(1024, 1) k_gemm24_fp8(PrefillArgs p) {
   if ((int)threadIdx.x < BM) s_sx[threadIdx.x] = sx_own * ts.nu;   // nu_i * sx_i
   if ((int)threadIdx.x < BN) s_sw[threadIdx.x] = sw_own;
   __syncthreads();                             // every wave is done with the ring
-  static_assert(16 * WM * WN * 2 <= RING, "output blocks fit the ring");
+  static_assert(NW * WM * WN * 2 <= RING, "output blocks fit the ring");
   uint16_t* blk = reinterpret_cast<uint16_t*>(ring + wv * (WM * WN * 2));
   store_tile_lds<DT, FM, FN, true>(p, acc, m0, n0, wm0, wn0, g, l32, lane, s_sx, s_eta, s_rs, blk, s_sw);
 }
 
+template <int DT>
+static void gemm24_fp8_launch(const PrefillArgs& a, hipStream_t st) {
+  // the column split of gemm24_launch: whole rounds of 256-column tiles, then
+  // one round of 192-column tiles
+  const int tm = (a.t + 255) / 256, n1 = balanced_cols(a.t, a.n_out);
+  PrefillArgs b = a;
+  b.col0 = 0;
+  b.col1 = n1;
+  hipLaunchKernelGGL((k_gemm24_fp8<DT, 16>), dim3(tm * ((n1 + 255) / 256)), dim3(1024), 0, st, b);
+  if (n1 < a.n_out) {
+    b.col0 = n1;
+    b.col1 = a.n_out;
+    hipLaunchKernelGGL((k_gemm24_fp8<DT, 12>), dim3(tm * ((a.n_out - n1 + 191) / 192)), dim3(768), 0, st, b);
+  }
+}
+
 hipError_t launch_gemm_fp8(int dtype, const PrefillArgs& a, hipStream_t st) {
   if (a.t == 0) return hipSuccess;
-  const int tiles = ((a.t + 255) / 256) * ((a.n_out + 255) / 256);
-  if (dtype == SPA_F16) hipLaunchKernelGGL(k_gemm24_fp8<SPA_F16>, dim3(tiles), dim3(1024), 0, st, a);
-  else hipLaunchKernelGGL(k_gemm24_fp8<SPA_BF16>, dim3(tiles), dim3(1024), 0, st, a);
+  if (dtype == SPA_F16) gemm24_fp8_launch<SPA_F16>(a, st);
+  else gemm24_fp8_launch<SPA_BF16>(a, st);
   return hipGetLastError();
 }
 

@@ -53,6 +53,8 @@ FP8_CASES = [
     wl.SPECS["prefill"].with_(name="fp8_k192", t=260, k=192, n_out=300),
     wl.SPECS["prefill"].with_(name="fp8_tiles", t=600, k=768, n_out=1100, n_outliers=8),
     wl.SPECS["prefill"].with_(name="fp8_one_row", t=1, k=128, n_out=8),
+    # a last round of 192-column tiles (more 256 x 256 tiles than 256 CUs hold)
+    wl.SPECS["prefill"].with_(name="fp8_tail_split", t=300, k=128, n_out=35000, n_outliers=2),
     wl.SPECS["prefill"].with_(name="fp8_weight_var", t=300, k=512, n_out=272, score="weight", alpha=0.5,
                               var_rescale=True),
     wl.SPECS["prefill"].with_(name="fp8_given", t=40, k=256, n_out=520, shift="given"),
