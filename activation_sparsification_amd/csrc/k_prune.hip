@@ -694,6 +694,90 @@ static hipError_t prune24_p(const PruneArgs& a, hipStream_t st) {
   return fac ? prune24_launch<DT, P, false, true>(a, st) : prune24_launch<DT, P, false, false>(a, st);
 }
 
+// The 2:4 operand by blocks of 16 token rows, for calls that form neither a
+// token mean nor an FP8 scale in the pass: wave w of a workgroup takes one
+// 64-channel step of its 16 rows per pass, lane 4 r + q holding segment q of
+// row r, so that the wave's packed values of that step are one contiguous
+// 1 KB run of the step-major operand and its position words one whole
+// 128-byte line (a workgroup per row writes 64-byte pieces 256 KB apart).
+// Workgroup (row block, column group) walks the column group's steps four at
+// a time, a four-pass register ring holding the next passes' loads.
+template <int DT, bool FAC>
+__global__ void __launch_bounds__(256) k_prune24_rows(PruneArgs a) {
+  using T = typename Dt<DT>::T;
+  constexpr int G = 4;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r = lane >> 2, q = lane & 3;
+  const int row = blockIdx.x * 16 + r;
+  const bool live = row < a.t;
+  const int rowc = live ? row : a.t - 1;                   // rows past t read the last row, store nothing
+  const int nsteps = a.k / 64, npass = (nsteps + 3) / 4;
+  const int per = (npass + (int)gridDim.y - 1) / (int)gridDim.y;
+  const int p0 = (int)blockIdx.y * per, p1 = min(npass, p0 + per);
+  float eta = 0.f;
+  if (a.eta_given) eta = a.eta_given[rowc];
+  if (blockIdx.y == 0 && wv == 0 && q == 0 && live && a.eta_out) a.eta_out[row] = eta;
+  // Descriptors over x and the operand (the host keeps each below 2^31
+  // bytes): a load or store at kBufferOutOfRange is dropped, so passes past
+  // the column group, steps past k and rows past t need no branch, and the
+  // loop's memory counts stay the same on every path.
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.x), (short)0, (int)((size_t)a.t * a.k * sizeof(T)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      a.tiled_vals, (short)0, (int)((size_t)a.t_pad * a.k * sizeof(T) / 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+      a.tiled_meta, (short)0, (int)((size_t)a.t_pad * (a.k / 16) * 2), kBufferWord3);
+  const uint32_t rowoff = (uint32_t)rowc * (uint32_t)a.k * (uint32_t)sizeof(T);
+  // pass p's segment of this lane: step 4 p + wv, slot q of its row
+  auto load = [&](int p, RawSeg<DT, 16>& raw) {
+    const int s = 4 * p + wv;
+    const bool ok = p < p1 && s < nsteps;
+#pragma unroll
+    for (int i = 0; i < RawSeg<DT, 16>::NQ; ++i)
+      raw.q[i] = buffer_load16(xrs, ok ? rowoff + (uint32_t)((4 * s + q) * 16 * sizeof(T) + 16 * i) : kBufferOutOfRange);
+  };
+  RawSeg<DT, 16> raw[G];
+#pragma unroll
+  for (int u = 0; u < G; ++u) load(p0 + u, raw[u]);
+  for (int pb = p0; pb < p1; pb += G) {
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int p = pb + u;
+      float v[16];
+      unpack_raw<DT, 16>(raw[u], a.act, v);
+      load(p + G, raw[u]);
+      const int s = 4 * p + wv;
+      const bool ok = live && p < p1 && s < nsteps;
+      const int seg = 4 * min(s, nsteps - 1) + q;
+      float fv[16], flo[4], fhi[4];
+      if constexpr (FAC) seg_factors(a, seg, fv);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] -= eta;
+      const uint32_t meta = seg_top2<FAC>(v, fv, flo, fhi);
+      const uint32_t rowpos = (uint32_t)s * (uint32_t)a.t_pad + (uint32_t)row;
+      const auto pk = __builtin_bit_cast(
+          __attribute__((ext_vector_type(4))) uint32_t,
+          make_uint4(pack2<DT>(flo[0], fhi[0]), pack2<DT>(flo[1], fhi[1]), pack2<DT>(flo[2], fhi[2]),
+                     pack2<DT>(flo[3], fhi[3])));
+      __builtin_amdgcn_raw_buffer_store_b128(pk, vrs, (int)(ok ? rowpos * 64u + 16u * q : kBufferOutOfRange), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)meta, mrs, (int)(ok ? rowpos * 8u + 2u * q : kBufferOutOfRange), 0, 0);
+    }
+  }
+}
+
+template <int DT>
+static hipError_t prune24_rows(const PruneArgs& a, hipStream_t st) {
+  // about four workgroups per CU: row blocks x column groups of whole passes
+  const int rbs = (a.t + 15) / 16, npass = (a.k / 64 + 3) / 4;
+  int cg = (1024 + rbs - 1) / rbs;
+  if (cg > npass) cg = npass;
+  if (cg < 1) cg = 1;
+  const dim3 grid((unsigned)rbs, (unsigned)cg);
+  if (a.colnorm || a.chan_scale) hipLaunchKernelGGL((k_prune24_rows<DT, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_prune24_rows<DT, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 // The lean pass applies: 16-bit 2:4 rows of at most 16384 channels, the
 // tiled operand the only output.
 static bool lean24(int dtype, const PruneArgs& a) {
@@ -703,6 +787,10 @@ static bool lean24(int dtype, const PruneArgs& a) {
 
 template <int DT>
 static hipError_t prune24_dt(const PruneArgs& a, hipStream_t st) {
+  // no token mean or FP8 scale to form from whole rows: blocks of 16 rows
+  if (!a.shift_mean && !a.fp8 && (size_t)a.t * a.k * Dt<DT>::bytes < (size_t)kBufferOutOfRange &&
+      (size_t)a.t_pad * a.k * Dt<DT>::bytes / 2 < (size_t)kBufferOutOfRange)
+    return prune24_rows<DT>(a, st);
   const int passes = (a.k / 16 + 255) / 256;
   return passes <= 1 ? prune24_p<DT, 1>(a, st) : passes <= 2 ? prune24_p<DT, 2>(a, st) : prune24_p<DT, 4>(a, st);
 }
