@@ -702,18 +702,17 @@ static hipError_t prune24_p(const PruneArgs& a, hipStream_t st) {
 // 128-byte line (a workgroup per row writes 64-byte pieces 256 KB apart).
 // Workgroup (row block, column group) walks the column group's steps four at
 // a time, a four-pass register ring holding the next passes' loads.
-template <int DT, bool FAC>
+template <int DT, bool FAC, int PER>
 __global__ void __launch_bounds__(256) k_prune24_rows(PruneArgs a) {
   using T = typename Dt<DT>::T;
-  constexpr int G = 4;
+  constexpr int G = PER < 4 ? PER : 4;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r = lane >> 2, q = lane & 3;
   const int row = blockIdx.x * 16 + r;
   const bool live = row < a.t;
   const int rowc = live ? row : a.t - 1;                   // rows past t read the last row, store nothing
   const int nsteps = a.k / 64, npass = (nsteps + 3) / 4;
-  const int per = (npass + (int)gridDim.y - 1) / (int)gridDim.y;
-  const int p0 = (int)blockIdx.y * per, p1 = min(npass, p0 + per);
+  const int p0 = (int)blockIdx.y * PER, p1 = min(npass, p0 + PER);
   float eta = 0.f;
   if (a.eta_given) eta = a.eta_given[rowc];
   if (blockIdx.y == 0 && wv == 0 && q == 0 && live && a.eta_out) a.eta_out[row] = eta;
@@ -736,16 +735,19 @@ __global__ void __launch_bounds__(256) k_prune24_rows(PruneArgs a) {
     for (int i = 0; i < RawSeg<DT, 16>::NQ; ++i)
       raw.q[i] = buffer_load16(xrs, ok ? rowoff + (uint32_t)((4 * s + q) * 16 * sizeof(T) + 16 * i) : kBufferOutOfRange);
   };
+  // PER passes, unrolled whole: the ring's slots are fixed registers with no
+  // loop-carried copies, so each wait counts exactly the loads it needs
   RawSeg<DT, 16> raw[G];
 #pragma unroll
   for (int u = 0; u < G; ++u) load(p0 + u, raw[u]);
-  for (int pb = p0; pb < p1; pb += G) {
+#pragma unroll
+  for (int pb = 0; pb < PER; pb += G) {
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const int p = pb + u;
+      const int p = p0 + pb + u;
       float v[16];
       unpack_raw<DT, 16>(raw[u], a.act, v);
-      load(p + G, raw[u]);
+      if (pb + u + G < PER) load(p + G, raw[u]);
       const int s = 4 * p + wv;
       const bool ok = live && p < p1 && s < nsteps;
       const int seg = 4 * min(s, nsteps - 1) + q;
@@ -765,16 +767,28 @@ __global__ void __launch_bounds__(256) k_prune24_rows(PruneArgs a) {
   }
 }
 
+template <int DT, int PER>
+static void prune24_rows_per(const PruneArgs& a, dim3 grid, hipStream_t st) {
+  if (a.colnorm || a.chan_scale) hipLaunchKernelGGL((k_prune24_rows<DT, true, PER>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_prune24_rows<DT, false, PER>), grid, dim3(256), 0, st, a);
+}
+
 template <int DT>
 static hipError_t prune24_rows(const PruneArgs& a, hipStream_t st) {
-  // about four workgroups per CU: row blocks x column groups of whole passes
+  // about four workgroups per CU: row blocks x column groups of PER passes,
+  // PER a power of two up to 16
   const int rbs = (a.t + 15) / 16, npass = (a.k / 64 + 3) / 4;
-  int cg = (1024 + rbs - 1) / rbs;
-  if (cg > npass) cg = npass;
-  if (cg < 1) cg = 1;
-  const dim3 grid((unsigned)rbs, (unsigned)cg);
-  if (a.colnorm || a.chan_scale) hipLaunchKernelGGL((k_prune24_rows<DT, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_prune24_rows<DT, false>), grid, dim3(256), 0, st, a);
+  const int want = (npass * rbs + 1023) / 1024;            // passes per workgroup for ~1024 workgroups
+  int per = 1;
+  while (per < want && per < 16) per *= 2;
+  const dim3 grid((unsigned)rbs, (unsigned)((npass + per - 1) / per));
+  switch (per) {
+    case 1: prune24_rows_per<DT, 1>(a, grid, st); break;
+    case 2: prune24_rows_per<DT, 2>(a, grid, st); break;
+    case 4: prune24_rows_per<DT, 4>(a, grid, st); break;
+    case 8: prune24_rows_per<DT, 8>(a, grid, st); break;
+    default: prune24_rows_per<DT, 16>(a, grid, st); break;
+  }
   return hipGetLastError();
 }
 
