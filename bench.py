@@ -60,11 +60,11 @@ ROOFLINE = {
                        per_unit="one union channel's weights: n_out x 2 B = 8,192 B; plus x and y"),
     "batched_t32": dict(profile="decode_mm_f16_batched_t32_k14336_n4096", kernel="k_prune_cols<f16,32> + k_decode_mm<f16,2>", bound="hbm", sources=DECODE_SOURCES,
                         per_unit="one union channel's weights: n_out x 2 B = 8,192 B; plus x and y"),
-    "prefill": dict(profile="gemm24_bf16_prefill_t2048_k4096_n14336", kernel="k_prune24<bf16,1> + k_gemm24<bf16,16>", bound="mfma", sources=PREFILL_SOURCES,
+    "prefill": dict(profile="gemm24_bf16_prefill_t2048_k4096_n14336", kernel="k_prune24<bf16,1> + k_gemm24<bf16,16> (256 columns) + k_gemm24<bf16,12> (192 columns)", bound="mfma", sources=PREFILL_SOURCES,
                     per_unit="one 256 x 256 x 64 tile step: 4.19 MFLOP kept (2 t n_out k n/m in all)"),
-    "relu2": dict(profile="gemm24_bf16_relu2_t4096_k16384_n4096", kernel="k_prune24<bf16,4> + k_gemm24<bf16,8>", bound="mfma", sources=PREFILL_SOURCES,
+    "relu2": dict(profile="gemm24_bf16_relu2_t4096_k16384_n4096", kernel="k_prune24_rows<bf16,16> + k_gemm24<bf16,8>", bound="mfma", sources=PREFILL_SOURCES,
                   per_unit="one 256 x 256 x 64 tile step: 4.19 MFLOP kept (2 t n_out k n/m in all)"),
-    "relu2_fused": dict(profile="gemm24_bf16_relu2_fused_t4096_k16384_n4096", kernel="k_prune24<bf16,4> (squared ReLU fused) + k_gemm24<bf16,8>", bound="mfma",
+    "relu2_fused": dict(profile="gemm24_bf16_relu2_fused_t4096_k16384_n4096", kernel="k_prune24_rows<bf16,16> (squared ReLU fused) + k_gemm24<bf16,8>", bound="mfma",
                         sources=PREFILL_SOURCES,
                         per_unit="one 256 x 256 x 64 tile step: 4.19 MFLOP kept (2 t n_out k n/m in all)"),
 }
@@ -364,7 +364,7 @@ def measure_ffn(steps, warmup, t=4096, hidden=4096, ffn=16384, n_out=4096):
         ms = sorted(per[name])[len(per[name]) // 2]
         tf = flops / (ms * 1e-3) / 1e12
         kern = ("k_gemm_dense<bf16,1> (prunes in its epilogue) + k_gemm24<bf16,8>" if name.endswith("_fused") else
-                "k_gemm_dense<bf16,0> + k_prune<bf16,4> + k_prune24<bf16,4> (squared ReLU) + k_gemm24<bf16,8>")
+                "k_gemm_dense<bf16,0> + k_prune<bf16,4> + k_prune24_rows<bf16,16> (squared ReLU) + k_gemm24<bf16,8>")
         recs.append(dict(workload=name, unit="TFLOP/s", value=tf, ms_per_step=ms, pct_of_peak=100.0 * tf / PEAK_BF16_TFLOPS,
                          flops=flops, weight_copies=copies, blocks_ms=per[name],
                          desc=f"squared-ReLU FFN x[{t},{hidden}] -> {ffn} -> {n_out} bf16, activation pruned 2:4",
@@ -422,8 +422,8 @@ def measure_fp8(steps, warmup, name="prefill"):
     for key, peak in (("prefill_bf16", PEAK_BF16_TFLOPS), ("prefill_fp8", PEAK_FP8_TFLOPS)):
         ms = sorted(per[key])[len(per[key]) // 2]
         tf = flops / (ms * 1e-3) / 1e12
-        kern = ("k_prune24<bf16,1> (e4m3 packing) + k_gemm24_fp8<bf16>" if key.endswith("fp8") else
-                "k_prune24<bf16,1> + k_gemm24<bf16,16>")
+        kern = ("k_prune24<bf16,1> (e4m3 packing) + k_gemm24_fp8<bf16,16> + k_gemm24_fp8<bf16,12>" if key.endswith("fp8") else
+                "k_prune24<bf16,1> + k_gemm24<bf16,16> + k_gemm24<bf16,12>")
         recs.append(dict(workload=key, unit="TFLOP/s", value=tf, ms_per_step=ms, pct_of_peak=100.0 * tf / peak,
                          kept_flops=flops, weight_copies=copies, blocks_ms=per[key],
                          desc=f"2:4 prefill x[{spec.t},{spec.k}] -> {spec.n_out}, "
