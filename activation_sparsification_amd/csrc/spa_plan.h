@@ -25,7 +25,7 @@ constexpr uint32_t kPlanBufferLimit = 0x80000000u;
 
 // One-token kernel: 512-column tiles, 8 waves, a channel split covers at most
 // 2048 channels.
-constexpr int kT1Waves = 8, kT1Threads = kT1Waves * 64, kT1Cols = 512, kT1MaxChan = 2048;
+constexpr int kT1Waves = 8, kT1Threads = kT1Waves * 64, kT1Cols = 512, kT1MaxChan = 2048, kT1MaxSplits = 16;
 // Matrix-core path: channels per workgroup of its pruning pass, 64-channel
 // steps per ring stage.
 constexpr int kPruneChan = 256, kMmSteps = 4;
@@ -71,12 +71,16 @@ inline DecodePlan plan_decode(int t, int k, int n_out, int dtype, int n, int m, 
   auto carve = [&](size_t nbytes) { size_t off = bytes; bytes += (nbytes + 255) & ~(size_t)255; return off; };
   if (t1_kernel(t, dtype, k, n_out)) {
     // 512-column tiles (1 KB of each kept row per load instruction); channel
-    // splits until about 224 workgroups run, each split at most kT1MaxChan
-    // channels, the partial traffic near 5 % of the weight bytes
+    // splits until about 224 workgroups run, but at most kT1MaxSplits, so the
+    // last arrival reads every split's partial in one batch of loads (28
+    // splits took two round trips: 21.0 against 19.3 us for a 4096-column
+    // output); each split at most kT1MaxChan channels, the partial traffic
+    // near 5 % of the weight bytes
     p.col_tile = kT1Cols;
     p.tiles = (n_out + p.col_tile - 1) / p.col_tile;
     const int blocks = k / m;
     int sp = 224 / p.tiles > 1 ? 224 / p.tiles : 1;
+    if (sp > kT1MaxSplits) sp = kT1MaxSplits;
     const double wbytes = (double)k * n / m * n_out * 2.0;
     const int max_by_traffic = (int)(0.05 * wbytes / (8.0 * n_out));
     if (sp > max_by_traffic) sp = max_by_traffic > 1 ? max_by_traffic : 1;
