@@ -11,7 +11,9 @@
 // least significant bit first, in 32-bit words; every row starts on a fresh
 // word.  Both kernels are bound by HBM: one thread per block, 256 blocks per
 // workgroup, and a wave's 64 codes fill exactly 2 x width whole words, which
-// the wave assembles in LDS and stores with one coalesced write.
+// the wave assembles in LDS and stores with one coalesced write.  2:4 codes
+// and masks of rows that fill whole words take a flat-stream pair of kernels
+// instead (k_encode24_flat, k_decode24_flat below).
 #include "spa_common.h"
 #include "spa_launch.h"
 
@@ -261,6 +263,105 @@ __global__ void __launch_bounds__(256) k_decode_meta(MetaArgs a) {
   }
 }
 
+// 2:4 combinatorial codes of rows whose codes fill whole words (blocks per
+// row a multiple of 32): 32 blocks are 64 bytes of positions and exactly three
+// code words, so over all rows the positions and the codes are each one flat
+// stream.  Lanes 4u .. 4u + 3 share unit u of 32 blocks: lane 4u + r holds
+// blocks 8r .. 8r + 7 (one 16-byte piece of positions, loaded coalesced) and
+// their 24 code bits, bits 24r .. 24r + 23 of the unit's 96.  Code word r is
+// then lane r's bits from 8r up and lane r + 1's below (encode), and lane r's
+// piece is its word from 8r down and lane r - 1's word above (decode): one
+// in-quad move each way, no LDS and no barrier.  Each thread takes kFlatG
+// pieces, all loads in flight first.
+constexpr int kFlatG = 4;
+
+__device__ __forceinline__ uint32_t quad_next(uint32_t v) {    // lane r + 1 of the quad (lane 3: itself)
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xF9, 0xF, 0xF, false);   // quad_perm [1,2,3,3]
+}
+__device__ __forceinline__ uint32_t quad_prev(uint32_t v) {    // lane r - 1 of the quad (lane 0: itself)
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x90, 0xF, 0xF, false);   // quad_perm [0,0,1,2]
+}
+
+// pieces: 16-byte pieces of positions over all rows (four per unit).  With
+// BITMAP (4-bit masks, blocks per row a multiple of 8) a piece's eight blocks
+// are exactly one code word: lane p stores word p, and no lanes are shared.
+template <bool BITMAP>
+__global__ void __launch_bounds__(256) k_encode24_flat(const uint4* __restrict__ pos, uint32_t* __restrict__ codes,
+                                                        int64_t pieces) {
+  const int64_t stride = (int64_t)gridDim.x * 256, p0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const uint32_t r = threadIdx.x & 3u;
+  uint4 v[kFlatG];
+#pragma unroll
+  for (int g = 0; g < kFlatG; ++g) {
+    const int64_t p = p0 + g * stride;
+    v[g] = p < pieces ? pos[p] : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int g = 0; g < kFlatG; ++g) {
+    const int64_t p = p0 + g * stride;                     // p % 4 == r: a unit's lanes are all in or all out
+    const uint32_t d[4] = {v[g].x, v[g].y, v[g].z, v[g].w};
+    uint32_t bits = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // block e: positions lo, hi in bytes 2e, 2e + 1; C(lo, 1) + C(hi, 2), held
+      // to its 3 bits (positions past the block give an unspecified code only)
+      const uint32_t lo = (d[e >> 1] >> (16 * (e & 1))) & 31u, hi = (d[e >> 1] >> (16 * (e & 1) + 8)) & 31u;
+      if constexpr (BITMAP) bits |= (((1u << lo) | (1u << hi)) & 15u) << (4 * e);
+      else bits |= ((lo + hi * (hi - 1u) / 2u) & 7u) << (3 * e);
+    }
+    if constexpr (BITMAP) {
+      if (p < pieces) codes[p] = bits;
+    } else {
+      const uint32_t next = quad_next(bits);
+      if (p < pieces && r < 3u) codes[(p >> 2) * 3 + r] = (bits >> (8u * r)) | (next << (24u - 8u * r));
+    }
+  }
+}
+
+template <bool BITMAP>
+__global__ void __launch_bounds__(256) k_decode24_flat(const uint32_t* __restrict__ codes, uint4* __restrict__ pos,
+                                                        int64_t pieces) {
+  // 2:4 codes 0..5 name the pairs {0,1}, {0,2}, {1,2}, {0,3}, {1,3}, {2,3};
+  // nibble `code` of kPairs holds lo | hi << 2 (6 and 7 give {2,3})
+  constexpr uint32_t kPairs = 0xEEEDC984u;
+  const int64_t stride = (int64_t)gridDim.x * 256, p0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const uint32_t r = threadIdx.x & 3u;
+  uint32_t own[kFlatG];
+#pragma unroll
+  for (int g = 0; g < kFlatG; ++g) {
+    const int64_t p = p0 + g * stride;
+    if constexpr (BITMAP) own[g] = p < pieces ? codes[p] : 0u;
+    else own[g] = p < pieces ? codes[(p >> 2) * 3 + (r < 3u ? r : 2u)] : 0u;   // lane 3 reads word 2 as lane 2
+  }
+#pragma unroll
+  for (int g = 0; g < kFlatG; ++g) {
+    const int64_t p = p0 + g * stride;
+    uint32_t bits = own[g];
+    if constexpr (!BITMAP) {
+      const uint32_t prev = quad_prev(own[g]);
+      bits = r == 0u ? own[g] : r == 3u ? own[g] >> 8 : (prev >> (32u - 8u * r)) | (own[g] << (8u * r));
+    }
+    uint32_t d[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t lo, hi;
+      if constexpr (BITMAP) {
+        // the two lowest set bits (a mask without two gives zeros, below m)
+        uint32_t mk = (bits >> (4 * e)) & 15u;
+        lo = mk ? (uint32_t)__builtin_ctz(mk) : 0u;
+        mk &= mk - 1u;
+        hi = mk ? (uint32_t)__builtin_ctz(mk) : 0u;
+      } else {
+        const uint32_t pr = (kPairs >> (4u * ((bits >> (3 * e)) & 7u))) & 15u;
+        lo = pr & 3u;
+        hi = pr >> 2;
+      }
+      d[e >> 1] |= (lo | (hi << 8)) << (16 * (e & 1));
+    }
+    if (p < pieces) pos[p] = make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
 template <bool ENCODE>
 static hipError_t meta_launch(const MetaArgs& a, int t, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)a.chunks * t));
@@ -308,6 +409,20 @@ hipError_t launch_meta(bool encode, const uint8_t* idx, uint8_t* idx_out, uint32
   if (t == 0 || a.nb == 0) return hipSuccess;
   if ((int64_t)a.chunks * t > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (encode && a.row_words == 0) return hipSuccess;      // nothing to store
+  const bool bitmap = format == SPA_META_BITMAP;
+  if (n == 2 && m == 4 && a.nb % (bitmap ? 8 : 32) == 0) {
+    const int64_t pieces = (int64_t)t * a.nb / 8;          // 16 bytes of positions = 8 blocks
+    const int64_t grid = (pieces + 256 * kFlatG - 1) / (256 * kFlatG);
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const dim3 g((unsigned)grid);
+    const uint4* in = reinterpret_cast<const uint4*>(idx);
+    uint4* out = reinterpret_cast<uint4*>(idx_out);
+    if (encode && bitmap) hipLaunchKernelGGL(k_encode24_flat<true>, g, dim3(256), 0, st, in, codes, pieces);
+    else if (encode) hipLaunchKernelGGL(k_encode24_flat<false>, g, dim3(256), 0, st, in, codes, pieces);
+    else if (bitmap) hipLaunchKernelGGL(k_decode24_flat<true>, g, dim3(256), 0, st, codes, out, pieces);
+    else hipLaunchKernelGGL(k_decode24_flat<false>, g, dim3(256), 0, st, codes, out, pieces);
+    return hipGetLastError();
+  }
   return encode ? meta_launch<true>(a, t, st) : meta_launch<false>(a, t, st);
 }
 

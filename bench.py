@@ -290,7 +290,9 @@ def measure_meta(fmt, n, m, t, k, steps, warmup):
         ms = e0.elapsed_time(e1) / steps
         b = idx.numel() + t * row_bytes
         gbs = b / (ms * 1e-3) / 1e9
-        kern = f"k_{name}_meta<{n}>"
+        nb = k // m
+        flat = n == 2 and m == 4 and nb % (8 if fmt == "bitmap" else 32) == 0
+        kern = f"k_{name}24_flat<{'true' if fmt == 'bitmap' else 'false'}>" if flat else f"k_{name}_meta<{n}>"
         recs.append(dict(workload=f"meta_{name}_{fmt}_{n}_{m}", unit="GB/s", value=gbs, ms_per_step=ms,
                          pct_of_peak=100.0 * gbs / PEAK_HBM_GBS, algorithmic_bytes=b, copies=copies,
                          desc=f"{name} of {fmt} block codes, {n}:{m}, positions [{t},{k * n // m}] uint8",

@@ -335,6 +335,10 @@ for fmt in ["comb", "bitmap"]:
     # several workgroups per row, rows that start off 16-byte boundaries
     for n, m in [(2, 4), (1, 4), (8, 16), (16, 32), (3, 8)]:
         META_CASES.append((fmt, n, m, 5001))
+# 2:4 codes and masks of rows that fill whole words (blocks per row a multiple
+# of 32, of 8 for masks): one flat stream over all rows; one partial
+# workgroup, and two workgroups whose later pieces run past the end
+META_CASES += [("comb", 2, 4, 96), ("comb", 2, 4, 4128), ("bitmap", 2, 4, 40), ("bitmap", 2, 4, 4104)]
 
 
 @pytest.mark.parametrize("fmt,n,m,nb", META_CASES)
