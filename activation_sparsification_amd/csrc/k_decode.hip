@@ -16,9 +16,10 @@
 //
 // Variants:
 //  * one token, 16-bit weights under 2 GiB, at least eight 512-column tiles
-//    (k_decode_t1): after one barrier for the shift, each wave selects its
-//    own 64 channels by in-block rank and streams its kept rows, 1 KB of a
-//    row per load, 32 buffer loads per lane in flight;
+//    (k_decode_t1): each wave forms the shift itself, selects its own 64
+//    channels at a time by in-block rank and streams their kept rows, 1 KB
+//    of a row per load, 32 buffer loads per lane in flight, with no
+//    workgroup barrier before the stream;
 //  * fused (2..4 tokens, float32, and one token with narrower outputs): each
 //    workgroup prunes its own channel range in LDS (the same few thousand
 //    comparisons in every tile) and streams the union of kept rows with

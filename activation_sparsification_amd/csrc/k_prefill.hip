@@ -18,10 +18,11 @@
 //   D:        register r holds row 8(r/4) + 4g + r%4, column l32.
 //
 // Both kernels stream 64-wide k steps through a three-stage LDS ring filled
-// by direct global->LDS loads (no register staging), 512 threads = 8 waves
-// (two per SIMD, so one wave's matrix instructions cover the other's LDS
-// reads), and order workgroups so that one XCD (each has its own L2) works
-// through all the token tiles of one weight tile before moving on.
+// by direct global->LDS loads (no register staging), with two or more waves
+// per SIMD (so one wave's matrix instructions cover another's LDS reads):
+// 8 waves for the dense GEMM; 8, 12 or 16 for the 2:4 GEMM (see k_gemm24).
+// Workgroups are ordered so that one XCD (each has its own L2) works through
+// a block of token tiles by weight tiles before moving on.
 #include "spa_common.h"
 #include "spa_launch.h"
 

@@ -1,14 +1,17 @@
 // Pruning pass: shift, score, per-block top-n, pack, variance factor.
 //
-// One workgroup (256 threads) per token row.  Each lane owns a segment of
-// max(16, m) consecutive channels -- whole m-blocks -- and ranks every block
-// in registers (guide s2.1: keep n of every m; ties to the lower channel
-// index, so exactly n survive): six pairwise comparisons for m = 4, the
+// k_prune: one workgroup (256 threads) per token row.  Each lane owns a
+// segment of max(16, m) consecutive channels -- whole m-blocks -- and ranks
+// every block in registers (guide s2.1: keep n of every m; ties to the lower
+// channel index, so exactly n survive): for 2:4 the four-comparison
+// tournament of spa_select.h, six pairwise comparisons for other n of 4, the
 // selection network of spa_select.h for wider blocks.
 //
 // Outputs (any subset): packed values + uint8 in-block positions; the
 // 2:4 nibble metadata the sparse MFMA consumes; or masked dense rows for
-// the dense-MFMA path of other n:m patterns.
+// the dense-MFMA path of other n:m patterns.  Calls that want only the 2:4
+// operand of 16-bit rows take the lean passes further down (k_prune24,
+// k_prune24_rows).
 #include "spa_common.h"
 #include "spa_launch.h"
 #include "spa_select.h"
