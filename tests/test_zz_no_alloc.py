@@ -17,10 +17,12 @@ pytestmark = pytest.mark.gpu
 
 spa = pytest.importorskip("activation_sparsification_amd")
 
-# one-token kernel (9 channel splits), then the matrix-core path, then the
-# fused kernel: each call smaller than the one before, then the first again
+# one-token kernel (8 channel splits; then 16 with the variance sums), then
+# the matrix-core path, then the fused kernel: each call smaller than the one
+# before, then the first again
 CALLS = [
     ("decode_layer", wl.SPECS["decode"]),
+    ("batched_t1", wl.SPECS["batched"].with_(t=1)),
     ("batched_t20", wl.SPECS["batched"].with_(t=20, k=2048, n_out=1000)),
     ("fused_t3", wl.SPECS["batched"].with_(t=3, k=512, n_out=136)),
     ("decode_layer_again", wl.SPECS["decode"]),
