@@ -801,6 +801,25 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kPcThreads = 1024;
 
+// The value of lane (lane ^ K) of the wave: DPP for K = 1, 2 (quad
+// permutes) and 8 (a rotation by 8 inside each row of 16 lanes), a swizzle
+// inside each half-wave for K = 4 and 16, an LDS permute for K = 32.
+template <int K>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
+  if constexpr (K == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+  else if constexpr (K == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+  else if constexpr (K == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);
+  else if constexpr (K == 32)
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((threadIdx.x & 63) ^ 32) * 4), (int)v);
+  else return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (K << 10));
+}
+template <int K>
+__device__ __forceinline__ double lane_xor_f64(double d) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, d);
+  const uint32_t lo = lane_xor_u32<K>((uint32_t)u), hi = lane_xor_u32<K>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ size_t frag_offset(int step, int tb, int ntb, int h, int lane) {
   return ((((size_t)step * ntb + tb) * 2 + h) * 64 + lane) * 8;   // in 16-bit elements
 }
@@ -811,7 +830,7 @@ __global__ void __launch_bounds__(kPcThreads) k_prune_cols(DecodeArgs a) {
   constexpr int CH = kPruneChan, NW = kPcThreads / 64;
   static_assert(CH == 256 && NW == 16, "four waves per 64-channel group, one channel per lane");
   __shared__ float s_x[kMaxTok][CH];
-  __shared__ __attribute__((aligned(16))) uint32_t s_sc[NW][64];   // per wave: the current token's scores
+  __shared__ __attribute__((aligned(16))) unsigned long long s_sc[NW][64];   // per wave: the current token's rank keys
   __shared__ __attribute__((aligned(16))) uint16_t s_mv[NW][64];   // per wave: its masked values
   __shared__ double s_st[4][kMaxTok / 4][4];
   const int T_ = a.t, K = a.k;
@@ -862,7 +881,9 @@ __global__ void __launch_bounds__(kPcThreads) k_prune_cols(DecodeArgs a) {
   const int step = (c0 + 64 * cg) / 64;                     // the group's 64 channels are one step
   const int kept_row = K / M * a.n;
   uint16_t* xf = static_cast<uint16_t*>(a.dense);
-  // tokens quarter + 4 sl of the quarter's slots sl = tw, tw + 4
+  // tokens quarter + 4 sl of the quarter's slots sl = tw, tw + 4; this lane's
+  // four variance terms of slot u in pv[4 u + q]
+  double pv[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int sl = tw + 4 * u, i = quarter + 4 * sl;
@@ -870,20 +891,24 @@ __global__ void __launch_bounds__(kPcThreads) k_prune_cols(DecodeArgs a) {
     const float xh = s_x[i][c];
     const float ax = __builtin_fabsf(xh);
     const uint32_t sb = __float_as_uint(a.score == SPA_SCORE_MAGNITUDE ? ax : ax * f);
-    // rank inside the block: scores are non-negative floats, so their bit
-    // patterns order like the values; the wave's own LDS writes precede its
-    // reads (LDS operations of one wave run in order)
-    s_sc[wv][lane] = sb;
+    // rank inside the block by 64-bit keys (score bits, 31 - position):
+    // scores are non-negative floats, so their bit patterns order like the
+    // values, and a larger key is a larger score or an equal score at a
+    // lower position; one compare per block member.  The wave's own LDS
+    // writes precede its reads (LDS operations of one wave run in order).
+    const unsigned long long key = ((unsigned long long)sb << 32) | (uint32_t)(31 - j);
+    s_sc[wv][lane] = key;
     __builtin_amdgcn_wave_barrier();
-    uint32_t sc[M];
+    unsigned long long sc[M];
 #pragma unroll
-    for (int q = 0; q < M / 4; ++q) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&s_sc[wv][b0 + 4 * q]);
-      sc[4 * q] = v.x; sc[4 * q + 1] = v.y; sc[4 * q + 2] = v.z; sc[4 * q + 3] = v.w;
+    for (int q = 0; q < M / 2; ++q) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&s_sc[wv][b0 + 2 * q]);
+      sc[2 * q] = ((unsigned long long)v.y << 32) | v.x;
+      sc[2 * q + 1] = ((unsigned long long)v.w << 32) | v.z;
     }
     int beat = 0;
 #pragma unroll
-    for (int q = 0; q < M; ++q) beat += (sc[q] > sb || (sc[q] == sb && q < j)) ? 1 : 0;
+    for (int q = 0; q < M; ++q) beat += sc[q] > key ? 1 : 0;
     const bool keep = cin && beat < a.n;
     // masked values: eight lanes' values are one 16-byte piece of the operand
     s_mv[wv][lane] = keep ? (uint16_t)from_f32<DT>(xh) : (uint16_t)0;
@@ -903,11 +928,30 @@ __global__ void __launch_bounds__(kPcThreads) k_prune_cols(DecodeArgs a) {
     if (a.var) {
       const double v = (double)xh;                          // 0 past k
       const double kv = keep ? v : 0.0;
-      const double t0 = wave_sum_dpp(v), t1 = wave_sum_dpp(v * v), t2 = wave_sum_dpp(kv), t3 = wave_sum_dpp(kv * kv);
-      if (lane == 0) {
-        s_st[cg][sl][0] = t0; s_st[cg][sl][1] = t1; s_st[cg][sl][2] = t2; s_st[cg][sl][3] = t3;
-      }
+      pv[4 * u] = v;
+      pv[4 * u + 1] = v * v;
+      pv[4 * u + 2] = kv;
+      pv[4 * u + 3] = kv * kv;
     }
+  }
+  if (a.var && quarter + 4 * tw < T_) {                     // the wave has at least one token (uniform)
+    // the eight sums over the wave's 64 lanes, in a fixed order: lanes
+    // halve the set of sums they carry at each of the first three
+    // exchanges (partners lane ^ 1, ^ 2, ^ 4), then the remaining sum is
+    // added over lanes ^ 8, ^ 16, ^ 32; lane L < 8 ends with sum
+    // 4 (L & 1) + 2 ((L >> 1) & 1) + ((L >> 2) & 1)
+    const int p0 = lane & 1, p1 = (lane >> 1) & 1, p2 = (lane >> 2) & 1;
+    double w4[4], w2[2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w4[e] = (p0 ? pv[4 + e] : pv[e]) + lane_xor_f64<1>(p0 ? pv[e] : pv[4 + e]);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) w2[e] = (p1 ? w4[2 + e] : w4[e]) + lane_xor_f64<2>(p1 ? w4[e] : w4[2 + e]);
+    double r = (p2 ? w2[1] : w2[0]) + lane_xor_f64<4>(p2 ? w2[0] : w2[1]);
+    r += lane_xor_f64<8>(r);
+    r += lane_xor_f64<16>(r);
+    r += lane_xor_f64<32>(r);
+    const int idx = 4 * p0 + 2 * p1 + p2, sl = tw + 4 * (idx >> 2);
+    if (lane < 8 && quarter + 4 * sl < T_) s_st[cg][sl][idx & 3] = r;
   }
   if (a.var) {
     // this chunk's four sums per token of the quarter, the 64-channel groups in order
