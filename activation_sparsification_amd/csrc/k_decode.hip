@@ -620,6 +620,10 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
         const int q = q0 + 64 * i + lane;
         u[i] = buffer_load16(xr, q < nq ? (uint32_t)q * 16u : kBufferOutOfRange);
       }
+      // every load issued before the first use (the scheduler would otherwise
+      // start the sums on the first piece and wait for it, all loads
+      // outstanding, before issuing the other seven: two round trips)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
