@@ -464,6 +464,32 @@ def test_decode_parity(spec):
     assert err <= O.TOLERANCE[spec.dtype], err
 
 
+# Tie-heavy tokens through each decode kernel: the one-token kernel (rank by
+# lane swizzles; n_out >= 4096), the fused 2-4 token kernel (selection
+# network) and the matrix-core path's pruning pass (64-bit rank keys).  Ties
+# go to the lower position, as in the oracle.
+DECODE_TIE_CASES = [("t1_8_16", 1, 8, 16, 4096, "bf16", "none"), ("t1_16_32", 1, 16, 32, 4096, "f16", "token_mean"),
+                    ("fused_t3_8_16", 3, 8, 16, 264, "bf16", "none"), ("mm_t8_16_32", 8, 16, 32, 256, "f16", "none"),
+                    ("mm_t20_2_4", 20, 2, 4, 256, "bf16", "token_mean"), ("mm_t6_1_4", 6, 1, 4, 200, "f16", "none")]
+
+
+@pytest.mark.parametrize("kind", ["equal", "zeros", "signed_pairs", "one_big", "few_levels"])
+@pytest.mark.parametrize("label,t,n,m,n_out,dtype,shift", DECODE_TIE_CASES, ids=[c[0] for c in DECODE_TIE_CASES])
+def test_decode_ties(kind, label, t, n, m, n_out, dtype, shift):
+    dev = _dev()
+    spec = wl.SPECS["decode"].with_(t=t, k=1024, n_out=n_out, n=n, m=m, dtype=dtype, score="magnitude",
+                                    shift=shift, alpha=0.0, n_outliers=0)
+    _, w = wl.make_inputs(spec)
+    x = wl.adversarial_x(kind, t, spec.k, m, dtype, seed=t + n + m)
+    pw = spa.prepare_weight(w.to(dev), 0.0)
+    pr = oracle_for(spec, x, w)
+    y, idx, nu = spa.sparse_linear_decode(x.to(dev), pw, _cfg(spec), want_idx=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), pr["idx"]), f"{label}/{kind}: decode masks differ"
+    err = O.rowwise_error(f32(y), pr["y"])
+    assert err <= O.TOLERANCE[dtype], (label, kind, err)
+
+
 def test_decode_repeat_reuses_workspace():
     # Counters left at zero: a second call on the same workspace gives the same bytes.
     dev = _dev()
