@@ -490,6 +490,35 @@ def test_decode_ties(kind, label, t, n, m, n_out, dtype, shift):
     assert err <= O.TOLERANCE[dtype], (label, kind, err)
 
 
+# The matrix-core path at a wide ragged output: a ragged last 64-row tile
+# (3576 = 55 x 64 + 56), a ragged last 64-channel step and a last stage that
+# overhangs k (1056 channels = 16.5 steps), one and two token blocks, with and
+# without the shift and the variance factor.
+MM16_CASES = [("t5_mag_mean", 5, "bf16", "magnitude", "token_mean", False, 2, 4),
+              ("t16_clact_var", 16, "f16", "clact", "none", True, 16, 32),
+              ("t17_weight", 17, "bf16", "weight", "none", False, 8, 16),
+              ("t32_clact_var_mean", 32, "f16", "clact", "token_mean", True, 16, 32)]
+
+
+@pytest.mark.parametrize("label,t,dtype,score,shift,var,n,m", MM16_CASES, ids=[c[0] for c in MM16_CASES])
+def test_decode_matrix_core_wide_ragged(label, t, dtype, score, shift, var, n, m):
+    dev = _dev()
+    spec = wl.SPECS["batched"].with_(t=t, k=1056, n_out=3576, dtype=dtype, score=score, shift=shift,
+                                     var_rescale=var, n=n, m=m, alpha=0.5 if score == "weight" else 0.0)
+    x, w = wl.make_inputs(spec)
+    pw = spa.prepare_weight(w.to(dev), spec.alpha, want_wt=False)
+    f = f32(pw.chan_scale) if score == "weight" else None
+    if f is not None:
+        assert np.array_equal(f.view(np.uint32), O.channel_factor(f32(w), spec.alpha).view(np.uint32))
+    pr = oracle_for(spec, x, w, f=f)
+    y, idx, nu = spa.sparse_linear_decode(x.to(dev), pw, _cfg(spec), want_idx=True, want_nu=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), pr["idx"]), f"{label}: decode masks differ"
+    assert np.allclose(f32(nu), pr["nu"], rtol=1e-6, atol=0), label
+    err = O.rowwise_error(f32(y), pr["y"])
+    assert err <= O.TOLERANCE[dtype], (label, err)
+
+
 def test_decode_repeat_reuses_workspace():
     # Counters left at zero: a second call on the same workspace gives the same bytes.
     dev = _dev()
