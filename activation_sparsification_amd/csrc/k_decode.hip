@@ -577,7 +577,7 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
   constexpr int R = kT1MaxChan / NT;                       // channel rounds per thread
   static_assert(64 % M == 0 && M <= 32, "an m-block must sit inside one wave");
   __shared__ float s_acc[NW][C];
-  __shared__ uint2 s_ent[NW][64];                          // per wave: (row, coefficient bits) of its kept channels
+  __shared__ __attribute__((aligned(16))) uint2 s_ent[NW][64];   // per wave: (row, coefficient bits) of its kept channels
   __shared__ __attribute__((aligned(16))) unsigned long long s_key[NW][64];   // per wave: the round's rank keys
   __shared__ double s_part[NW][5];                         // row-sum partial, then the four variance sums
   __shared__ double s_stsum[4];
@@ -713,19 +713,37 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 4. stream the wave's kept rows, kT1Loads at a time.  For m <= 16 every
+    //    lane reads the batch's entries itself (broadcast LDS reads, two
+    //    entries each), so row offsets and coefficients sit in vector
+    //    registers; as scalars (read lane by lane) 64 of them per batch
+    //    spilled to vector lanes and back.  32-wide blocks keep the scalar
+    //    form: their swizzled rank already fills the vector registers.
     const uint2 mine = s_ent[wv][lane];                    // entry `lane` (stale past cnt, never used)
-    // 4. stream the wave's kept rows, kT1Loads at a time
     for (int b0 = 0; b0 < cnt; b0 += kT1Loads) {
       uint32_t soff[kT1Loads], voff[kT1Loads];
       float cf[kT1Loads];
+      if constexpr (M <= 16) {
 #pragma unroll
-      for (int i = 0; i < kT1Loads; ++i) {
-        const int e = b0 + i;
-        const bool ok = e < cnt;                             // uniform
-        const uint32_t row = (uint32_t)__builtin_amdgcn_readlane((int)mine.x, e & 63);
-        soff[i] = ok ? row * row_bytes : 0u;
-        voff[i] = ok ? col_bytes : kBufferOutOfRange;
-        cf[i] = ok ? __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)mine.y, e & 63)) : 0.f;
+        for (int i = 0; i < kT1Loads; i += 2) {
+          const uint4 pr = *reinterpret_cast<const uint4*>(&s_ent[wv][(b0 + i) & 63]);   // entries b0 + i, + 1
+          const bool ok0 = b0 + i < cnt, ok1 = b0 + i + 1 < cnt;   // uniform
+          soff[i] = soff[i + 1] = 0u;
+          voff[i] = ok0 ? pr.x * row_bytes + col_bytes : kBufferOutOfRange;
+          cf[i] = ok0 ? __uint_as_float(pr.y) : 0.f;
+          voff[i + 1] = ok1 ? pr.z * row_bytes + col_bytes : kBufferOutOfRange;
+          cf[i + 1] = ok1 ? __uint_as_float(pr.w) : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kT1Loads; ++i) {
+          const int e = b0 + i;
+          const bool ok = e < cnt;                           // uniform
+          const uint32_t row = (uint32_t)__builtin_amdgcn_readlane((int)mine.x, e & 63);
+          soff[i] = ok ? row * row_bytes : 0u;
+          voff[i] = ok ? col_bytes : kBufferOutOfRange;
+          cf[i] = ok ? __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)mine.y, e & 63)) : 0.f;
+        }
       }
       uint4 w[kT1Loads];
 #pragma unroll
