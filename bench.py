@@ -103,22 +103,33 @@ def sources_sha(paths):
     return h.hexdigest()
 
 
-def read_counters(name):
-    """The committed counter record of a workload (first line of its
-    profiles/<kernel>_<workload>_counters.txt: HBM bytes per step, the
-    sustained clock and the matrix-core busy fraction), or None when a source
-    of its kernels changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{ROOFLINE[name]['profile']}_counters.txt") if name in ROOFLINE else ""
-    if name not in ROOFLINE or not os.path.exists(path):
+def read_counter_file(profile, sources):
+    """The committed counter record of a profile (first line of
+    profiles/<profile>_counters.txt: HBM bytes per step, the sustained clock
+    and the matrix-core busy fraction), or None when a source of its kernels
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{profile}_counters.txt")
+    if not os.path.exists(path):
         return None
     try:
         with open(path) as fh:
             rec = json.loads(fh.readline())
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != sources_sha(ROOFLINE[name]["sources"]):
+    if rec.get("source_sha256") != sources_sha(sources):
         return None
     return rec
+
+
+def read_counters(name):
+    """The counter record of a workload of ROOFLINE, or None."""
+    if name not in ROOFLINE:
+        return None
+    return read_counter_file(ROOFLINE[name]["profile"], ROOFLINE[name]["sources"])
+
+
+# counter record of the FP8 pipeline of --workload fp8 (its step kernels only)
+FP8_PROFILE = "gemm24_fp8_prefill_t2048_k4096_n14336"
 
 
 def roofline(name, rec):
@@ -426,14 +437,19 @@ def measure_fp8(steps, warmup, name="prefill"):
         tf = flops / (ms * 1e-3) / 1e12
         kern = ("k_prune24<bf16,1> (e4m3 packing) + k_gemm24_fp8<bf16,16> + k_gemm24_fp8<bf16,12>" if key.endswith("fp8") else
                 "k_prune24<bf16,1> + k_gemm24<bf16,16> + k_gemm24<bf16,12>")
+        roof = dict(bound="mfma", achieved=tf, peak=peak, unit="TFLOP/s", frac=tf / peak, traffic=None, kernel=kern,
+                    per_unit="one 256 x 256 x 64 tile step: 4.19 MFLOP kept; the FP8 line against the dense fp8 peak")
+        ctr = read_counter_file(FP8_PROFILE, PREFILL_SOURCES) if key.endswith("fp8") else None
+        if ctr is not None:
+            roof["traffic"] = ctr.get("traffic_bytes_per_step")
+            for k2 in ("mfma_busy", "ta_busy", "algorithmic_bytes_per_step"):
+                if k2 in ctr:
+                    roof[k2] = ctr[k2]
         recs.append(dict(workload=key, unit="TFLOP/s", value=tf, ms_per_step=ms, pct_of_peak=100.0 * tf / peak,
                          kept_flops=flops, weight_copies=copies, blocks_ms=per[key],
                          desc=f"2:4 prefill x[{spec.t},{spec.k}] -> {spec.n_out}, "
                               + ("FP8 e4m3 operands, row scales" if key.endswith("fp8") else "bf16 operands"),
-                         roofline=dict(bound="mfma", achieved=tf, peak=peak, unit="TFLOP/s", frac=tf / peak,
-                                       traffic=None, kernel=kern,
-                                       per_unit="one 256 x 256 x 64 tile step: 4.19 MFLOP kept; the FP8 line "
-                                                "against the dense fp8 peak")))
+                         roofline=roof))
     del mats, codes, bf, f8
     torch.cuda.empty_cache()
     return recs
