@@ -128,8 +128,23 @@ def read_counters(name):
     return read_counter_file(ROOFLINE[name]["profile"], ROOFLINE[name]["sources"])
 
 
-# counter record of the FP8 pipeline of --workload fp8 (its step kernels only)
+# counter records of the lines outside ROOFLINE: the FP8 pipeline of
+# --workload fp8 (its step kernels only), the two FFN pipelines of --workload
+# ffn, and the codec kernels of --workload meta (bytes per launch of each)
 FP8_PROFILE = "gemm24_fp8_prefill_t2048_k4096_n14336"
+FFN_PROFILE = "ffn_relu2_fused_t4096_h4096_f16384_n4096"
+META_PROFILE = "meta_codecs_t4096_k16384"
+META_SOURCES = [CSRC + f for f in ("k_meta.hip", "spa_common.h")]
+
+
+def kernel_bytes(ctr, kernel):
+    """HBM bytes per launch of one kernel in a counter record, or None."""
+    if ctr is None:
+        return None
+    for r in ctr.get("step_kernels", []):
+        if r["kernel"] == kernel:
+            return r["bytes"]
+    return None
 
 
 def roofline(name, rec):
@@ -304,11 +319,12 @@ def measure_meta(fmt, n, m, t, k, steps, warmup):
         nb = k // m
         flat = n == 2 and m == 4 and nb % (8 if fmt == "bitmap" else 32) == 0
         kern = f"k_{name}24_flat<{'true' if fmt == 'bitmap' else 'false'}>" if flat else f"k_{name}_meta<{n}>"
+        traffic = kernel_bytes(read_counter_file(META_PROFILE, META_SOURCES), "spa::" + kern) if (t, k) == (4096, 16384) else None
         recs.append(dict(workload=f"meta_{name}_{fmt}_{n}_{m}", unit="GB/s", value=gbs, ms_per_step=ms,
                          pct_of_peak=100.0 * gbs / PEAK_HBM_GBS, algorithmic_bytes=b, copies=copies,
                          desc=f"{name} of {fmt} block codes, {n}:{m}, positions [{t},{k * n // m}] uint8",
                          roofline=dict(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s",
-                                       frac=gbs / PEAK_HBM_GBS, traffic=None, kernel=kern,
+                                       frac=gbs / PEAK_HBM_GBS, traffic=traffic, kernel=kern,
                                        per_unit="one m-block: n bytes of positions + its code bits / 8")))
     assert torch.equal(outs[(steps - 1) % copies], idx), "decoded positions differ from the input"
     del idxs, codes, outs
@@ -378,11 +394,13 @@ def measure_ffn(steps, warmup, t=4096, hidden=4096, ffn=16384, n_out=4096):
         tf = flops / (ms * 1e-3) / 1e12
         kern = ("k_gemm_dense<bf16,1> (prunes in its epilogue) + k_gemm24<bf16,8>" if name.endswith("_fused") else
                 "k_gemm_dense<bf16,0> + k_prune<bf16,4> + k_prune24_rows<bf16,16> (squared ReLU) + k_gemm24<bf16,8>")
+        ctr = read_counter_file(FFN_PROFILE, PREFILL_SOURCES) if (t, hidden, ffn, n_out) == (4096, 4096, 16384, 4096) else None
+        traffic = None if ctr is None else ctr.get("traffic_fused" if name.endswith("_fused") else "traffic_unfused")
         recs.append(dict(workload=name, unit="TFLOP/s", value=tf, ms_per_step=ms, pct_of_peak=100.0 * tf / PEAK_BF16_TFLOPS,
                          flops=flops, weight_copies=copies, blocks_ms=per[name],
                          desc=f"squared-ReLU FFN x[{t},{hidden}] -> {ffn} -> {n_out} bf16, activation pruned 2:4",
                          roofline=dict(bound="mfma", achieved=tf, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                                       frac=tf / PEAK_BF16_TFLOPS, traffic=None, kernel=kern,
+                                       frac=tf / PEAK_BF16_TFLOPS, traffic=traffic, kernel=kern,
                                        per_unit="dense up-projection flops 2 t hidden ffn + kept down-projection "
                                                 "flops 2 t ffn n_out / 2")))
     del ups, dns, unfused
