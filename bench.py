@@ -457,7 +457,10 @@ def measure_fp8(steps, warmup, name="prefill"):
                 "k_prune24<bf16,1> + k_gemm24<bf16,16> + k_gemm24<bf16,12>")
         roof = dict(bound="mfma", achieved=tf, peak=peak, unit="TFLOP/s", frac=tf / peak, traffic=None, kernel=kern,
                     per_unit="one 256 x 256 x 64 tile step: 4.19 MFLOP kept; the FP8 line against the dense fp8 peak")
-        ctr = read_counter_file(FP8_PROFILE, PREFILL_SOURCES) if key.endswith("fp8") else None
+        # the FP8 pipeline's own record; the bf16 pipeline is the prefill workload's
+        ctr = read_counter_file(FP8_PROFILE, PREFILL_SOURCES) if key.endswith("fp8") else read_counters("prefill")
+        if not key.endswith("fp8") and name != "prefill":
+            ctr = None
         if ctr is not None:
             roof["traffic"] = ctr.get("traffic_bytes_per_step")
             for k2 in ("mfma_busy", "ta_busy", "algorithmic_bytes_per_step"):
