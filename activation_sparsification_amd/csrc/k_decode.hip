@@ -672,7 +672,7 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
       // score or an equal score at a lower position.  The wave parks its
       // keys in its own LDS slots and reads its block's back as broadcast
       // 16-byte reads (the wave's LDS operations run in order); one compare
-      // per block member (same-box: 17.07 -> 16.91 us at the decode layer)
+      // per block member (17.07 -> 16.91 us at the decode layer, alternating runs)
       const unsigned long long key = ((unsigned long long)sb << 32) | (uint32_t)(31 - j);
       s_key[wv][lane] = key;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
