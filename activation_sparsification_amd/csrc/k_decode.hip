@@ -748,7 +748,8 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
       uint4 w[kT1Loads];
 #pragma unroll
       for (int i = 0; i < kT1Loads; ++i) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)voff[i], (int)soff[i], 0);
+        // non-temporal: each kept row is read once per call
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)voff[i], (int)soff[i], kCacheNonTemporal);
         w[i] = make_uint4(v[0], v[1], v[2], v[3]);
       }
       __builtin_amdgcn_sched_barrier(0);                   // every load issued before the first use
@@ -1101,7 +1102,7 @@ __global__ void __launch_bounds__(512) k_decode_mm(DecodeArgs a) {
       const int dr = 8 * wv + 2 * j + (lane >> 5);
       const uint32_t rbytes = (uint32_t)(min(n0 + dr, N - 1) - n0) * (uint32_t)K * 2u;
       const int kc = st0 * 64 + 8 * (dp ^ (dr & 15));       // chunks past k read chunk 0 (their activations are zero)
-      lds_dma16(wbase, rbytes + (uint32_t)(kc < K ? kc : 0) * 2u, q + (uint32_t)(wv * 4 + j) * 1024u);
+      lds_dma16_nt(wbase, rbytes + (uint32_t)(kc < K ? kc : 0) * 2u, q + (uint32_t)(wv * 4 + j) * 1024u);
     }
     // steps past this split or past k: any in-bounds activations (multiplied as zeros)
     const int stx = min(st0, nsteps - SU > 0 ? nsteps - SU : 0);
