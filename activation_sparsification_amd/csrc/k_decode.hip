@@ -41,6 +41,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxTok = 32;
 
+// Loads of the weight streams carry the non-temporal hint: each weight row is
+// read once per call, so its lines need not displace reused data in L2 or
+// the MALL.  kCacheNonTemporal is the buffer-load cache-policy value of the
+// nt bit on gfx950.
+constexpr int kCacheNonTemporal = 2;
+__device__ __forceinline__ void lds_dma16_nt(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(sbase), "s"(lds)
+               : "m0");
+}
+
 // ---------------------------------------------------------------------------
 // Split-K hand-off without cache-wide maintenance.  A partial is stored with
 // agent-scope atomic stores (coherent across the XCDs' private L2s), every

@@ -96,7 +96,6 @@ template <int DT> __device__ __forceinline__ float elem16(const uint4& v, int e)
 // returns zeros instead of touching memory.
 constexpr int kBufferWord3 = 0x00020000;
 constexpr uint32_t kBufferOutOfRange = 0x80000000u;   // past every buffer smaller than 2 GiB
-constexpr int kCacheNonTemporal = 2;                   // buffer-load cache policy: the nt bit (gfx950)
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
@@ -125,13 +124,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // LDS-DMA reading M0 needs one wait state after the M0 write (s_nop 0).
 __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
-               : "m0");
-}
-// The same with the non-temporal hint, for data read once per call (a
-// streamed weight): its lines are not kept in the caches at the cost of data
-// that is read again.
-__device__ __forceinline__ void lds_dma16_nt(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(sbase), "s"(lds)
                : "m0");
 }
 __device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds) {
