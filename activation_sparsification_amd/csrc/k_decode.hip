@@ -1317,7 +1317,7 @@ static hipError_t fused_tok(DecodeArgs& a, hipStream_t st) {
 
 template <int DT>
 static hipError_t decode_dt(DecodeArgs& a, hipStream_t st) {
-  const bool fused = a.t <= 4 || DT == SPA_F32;
+  const bool fused = !decode_on_matrix_cores(a.t, DT);
   // the token mean ahead of the main kernel: for long fused rows, and for CLACT
   // (its column norms are taken over the shifted values)
   const bool mean_first = fused ? (size_t)a.t * a.k > 65536 : true;

@@ -212,9 +212,7 @@ spa_status decode_launch(spa::DecodeArgs& a, char* base, unsigned* counters, con
   fix(a.stats);
   fix(a.counters);
   fix(a.eta_ws);
-  if (t > 4 && w->dtype != SPA_F32) {                // matrix-core path (the dense offset is 0)
-    fix(a.dense);
-  }
+  if (spa::decode_on_matrix_cores(t, w->dtype)) fix(a.dense);   // matrix-core path (the dense offset is 0)
   if (counters) a.counters = counters;
   a.x = x;
   a.act = cfg->act;

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "spa.h"
+#include "spa_plan.h"
 
 namespace spa_check {
 
@@ -76,9 +77,9 @@ inline spa_status check_linear(const void* x, int32_t t, const spa_weight* w, co
   if (cfg->score == SPA_SCORE_WEIGHT && !w->chan_scale) return SPA_ERR_INVALID;
   if (cfg->shift == SPA_SHIFT_GIVEN && !eta_in) return SPA_ERR_INVALID;
   if (cfg->shift != SPA_SHIFT_NONE && !w->row_sum) return SPA_ERR_INVALID;
-  // 1..4 tokens (and float32) stream the channel-major copy; more tokens of a
-  // 16-bit type run on the matrix cores over the row-major weight
-  const bool reads_wt = decode && (t <= 4 || w->dtype == SPA_F32);
+  // the matrix-core decode reads the row-major weight, every other decode
+  // the channel-major copy
+  const bool reads_wt = decode && !spa::decode_on_matrix_cores(t, w->dtype);
   const void* need = reads_wt ? w->wt : w->w;
   if (!need || !aligned16(need)) return SPA_ERR_INVALID;
   // valid, but outside what the kernels are built for

@@ -40,6 +40,13 @@ SPA_PLAN_HD bool t1_kernel(int t, int dtype, int k, int n_out) {
          (uint64_t)k * (uint64_t)n_out * 2u < (uint64_t)kPlanBufferLimit;
 }
 
+// The decode path for t tokens of a dtype: more than four tokens of a 16-bit
+// type run on the matrix cores over the row-major weight; every other call
+// streams the channel-major copy.  The planner, the argument check and the
+// launcher all decide by this one function, so the workspace carve-up, the
+// weight that must be present and the kernels launched cannot disagree.
+SPA_PLAN_HD constexpr bool decode_on_matrix_cores(int t, int dtype) { return t > 4 && dtype != kPlanF32; }
+
 // Waves per workgroup of the fused kernel: 8 for the light cases, 4 (so each
 // wave may hold up to 512 registers) when several tokens or 32-wide blocks
 // are ranked per lane.
@@ -66,7 +73,7 @@ struct DecodePlan {
 
 inline DecodePlan plan_decode(int t, int k, int n_out, int dtype, int n, int m, int var) {
   DecodePlan p;
-  const bool fused = t <= 4 || dtype == kPlanF32;
+  const bool fused = !decode_on_matrix_cores(t, dtype);
   size_t bytes = 0;
   auto carve = [&](size_t nbytes) { size_t off = bytes; bytes += (nbytes + 255) & ~(size_t)255; return off; };
   if (t1_kernel(t, dtype, k, n_out)) {
