@@ -20,13 +20,15 @@
 //    channels at a time by in-block rank and streams their kept rows, 1 KB
 //    of a row per load, 32 buffer loads per lane in flight, with no
 //    workgroup barrier before the stream;
-//  * fused (2..4 tokens, float32, and one token with narrower outputs): each
-//    workgroup prunes its own channel range in LDS (the same few thousand
-//    comparisons in every tile) and streams the union of kept rows with
-//    float32 VALU FMAs, 16 bytes per lane per row;
-//  * matrix-core (5..32 tokens, 16-bit): the union of kept rows is nearly all
-//    of W, so k_prune_cols prunes every channel once into masked rows in the
-//    matrix cores' operand order, and k_decode_mm reads the row-major W once
+//  * fused (float32 up to 8 tokens, and one 16-bit token with narrower
+//    outputs or a weight of 2 GiB or more): each workgroup prunes its own
+//    channel range in LDS (the same few thousand comparisons in every tile)
+//    and streams the union of kept rows with float32 VALU FMAs, 16 bytes per
+//    lane per row;
+//  * matrix-core (2..32 tokens, 16-bit): the union of kept rows is most or
+//    nearly all of W (three quarters at two tokens of 8:16), so k_prune_cols
+//    prunes every channel once into masked rows in the matrix cores' operand
+//    order, and k_decode_mm reads the row-major W once
 //    and runs the product on matrix cores (mfma 16x16x32).
 #include "spa_common.h"
 #include "spa_launch.h"
@@ -832,7 +834,7 @@ __global__ void __launch_bounds__(kT1Threads) k_decode_t1(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pruning pass of the matrix-core decode (t > 4): few token rows, so the
+// Pruning pass of the matrix-core decode (t >= 2): few token rows, so the
 // work is cut by channels and by token.  Workgroup (chunk, quarter) owns
 // kPruneChan channels and the tokens quarter, quarter + 4, ...: it stages
 // x_hat = x - eta of its channels for every token in LDS (each thread one
@@ -1020,7 +1022,7 @@ __global__ void __launch_bounds__(kPcThreads) k_prune_cols(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core decode (t > 4, 16-bit).  With several tokens the union of kept
+// Matrix-core decode (t >= 2, 16-bit).  With several tokens the union of kept
 // channels covers nearly every row of the weight (each token keeps its own
 // n of every m), so the product runs as a skinny dense GEMM over the masked
 // rows xm that the pruning pass writes in fragment order (zeros at pruned
@@ -1309,9 +1311,11 @@ static hipError_t fused_tok(DecodeArgs& a, hipStream_t st) {
     }
   }
   if (a.t <= 1) return fused_launch<DT, M, 1>(a, st);
-  if (a.t <= 2) return fused_launch<DT, M, 2>(a, st);
-  if (a.t <= 4) return fused_launch<DT, M, 4>(a, st);
-  if constexpr (DT == SPA_F32) return fused_launch<DT, M, 8>(a, st);  // 16-bit t > 4 takes the MFMA path
+  if constexpr (DT == SPA_F32) {                    // 16-bit t >= 2 takes the matrix-core path
+    if (a.t <= 2) return fused_launch<DT, M, 2>(a, st);
+    if (a.t <= 4) return fused_launch<DT, M, 4>(a, st);
+    return fused_launch<DT, M, 8>(a, st);
+  }
   return hipErrorInvalidValue;
 }
 

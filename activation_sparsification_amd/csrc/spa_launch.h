@@ -50,8 +50,8 @@ hipError_t launch_colnorm(int dtype, const void* x, int act, const float* eta, i
 // ---- decode ----
 struct DecodeArgs {
   const void* x;
-  const void* wt;            // [k][n_out] channel-major (t <= 4, and float32)
-  const void* w;             // [n_out][k] row-major (16-bit, t > 4)
+  const void* wt;            // [k][n_out] channel-major (one token, and float32)
+  const void* w;             // [n_out][k] row-major (16-bit, t >= 2)
   const float* chan_scale;
   const float* row_sum;
   const float* eta;          // precomputed or caller-given shift, or NULL

@@ -40,12 +40,17 @@ SPA_PLAN_HD bool t1_kernel(int t, int dtype, int k, int n_out) {
          (uint64_t)k * (uint64_t)n_out * 2u < (uint64_t)kPlanBufferLimit;
 }
 
-// The decode path for t tokens of a dtype: more than four tokens of a 16-bit
-// type run on the matrix cores over the row-major weight; every other call
-// streams the channel-major copy.  The planner, the argument check and the
+// The decode path for t tokens of a dtype: two or more tokens of a 16-bit
+// type run on the matrix cores over the row-major weight; one token, and
+// float32, stream the channel-major copy.  With two tokens the union of kept
+// rows is already about 1 - (1 - n/m)^2 of the weight (three quarters at
+// 8:16), so reading all of W at the matrix cores' rate beats gathering the
+// union rows: 2 and 4 tokens at the 14336 x 4096 layer took 30.4 us against
+// 38.1 and 50.9 us streamed, 2 and 4 tokens of the 4096 x 14336 CLACT layer
+// 27.7 us against 43.0 and 119 us.  The planner, the argument check and the
 // launcher all decide by this one function, so the workspace carve-up, the
 // weight that must be present and the kernels launched cannot disagree.
-SPA_PLAN_HD constexpr bool decode_on_matrix_cores(int t, int dtype) { return t > 4 && dtype != kPlanF32; }
+SPA_PLAN_HD constexpr bool decode_on_matrix_cores(int t, int dtype) { return t > 1 && dtype != kPlanF32; }
 
 // Waves per workgroup of the fused kernel: 8 for the light cases, 4 (so each
 // wave may hold up to 512 registers) when several tokens or 32-wide blocks

@@ -180,9 +180,9 @@ class Workload:
         wd = w.to(dev)
         self.pw = spa.prepare_weight(wd, spec.alpha, want_wt=self.decode)
         self.cfg = spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, spec.var_rescale, spec.act)
-        # decode streams the channel-major copy for 1..4 tokens (and float32); more tokens
-        # of a 16-bit type read the row-major weight on the matrix cores
-        self.reads_wt = self.decode and (spec.t <= 4 or spec.dtype == "f32")
+        # decode streams the channel-major copy for one token (and float32); two or
+        # more tokens of a 16-bit type read the row-major weight on the matrix cores
+        self.reads_wt = self.decode and (spec.t <= 1 or spec.dtype == "f32")
         big = self.pw.wt if self.reads_wt else self.pw.w
         # weight copies rotated so that the bytes a step touches, summed over
         # the copies, exceed the 256 MB MALL three times over: the kept rows

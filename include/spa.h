@@ -103,7 +103,8 @@ typedef struct spa_prune_cfg {
 } spa_prune_cfg;
 
 /* A prepared linear layer.  Fields not needed by an entry point may be NULL:
- * decode reads wt, prefill reads w; chan_scale is needed for
+ * one-token and float32 decode read wt, decode of 2..32 16-bit tokens and
+ * prefill read w; chan_scale is needed for
  * SPA_SCORE_WEIGHT, row_sum whenever shift != SPA_SHIFT_NONE. */
 typedef struct spa_weight {
   int32_t dtype;
@@ -195,19 +196,20 @@ spa_status prune_nm(const void* x, int32_t dtype, int32_t t, int32_t k, const sp
 /*
  * sparse_linear_decode -- the decode step, 1 <= t <= 32 tokens, float32
  * accumulation, y = nu * acc + eta * row_sum.
- *  - 1..4 tokens, and float32 (t <= 8): prune in registers, then stream
+ *  - one token, and float32 (t <= 8): prune in registers, then stream
  *    only the rows of wt that some token of the call keeps (the
  *    memory-bound GEMV; guide s1.1 and s12.3: zero activations need not
  *    move, and bandwidth comes first).
- *  - 5..32 tokens of a 16-bit type: every token keeps its own n of each m
- *    channels, so their union covers nearly all of wt; a pruning pass
- *    writes the masked rows, and one pass over the row-major w on the
- *    matrix cores forms the product (per-token masks differ within a
- *    batch; WiSparse s5.1 separates small-batch from large-batch use).
+ *  - 2..32 tokens of a 16-bit type: every token keeps its own n of each m
+ *    channels, so their union covers most of wt (three quarters at two
+ *    tokens of 8:16, nearly all from eight); a pruning pass writes the
+ *    masked rows, and one pass over the row-major w on the matrix cores
+ *    forms the product (per-token masks differ within a batch; WiSparse
+ *    s5.1 separates small-batch from large-batch use).
  *  x        [device] [t][k]
- *  w        weight descriptor: wt required for 1..4 tokens and for float32
+ *  w        weight descriptor: wt required for one token and for float32
  *           (n_out % 8 == 0 for 16-bit dtypes, % 4 for float32); w->w
- *           required for 5..32 tokens of a 16-bit dtype
+ *           required for 2..32 tokens of a 16-bit dtype
  *  eta_in   [device] [t], required iff cfg->shift == SPA_SHIFT_GIVEN
  *  y        [device] [t][n_out]
  *  idx_out  [device] [t][k*n/m] or NULL: the in-block positions the layer used

@@ -22,7 +22,7 @@ static int replay(int t, int k, int n_out, int dtype, int n, int m, int var, int
     std::printf("ok t1 %d 0 0 0\n", p.splits);
     return 0;
   }
-  if (!(t <= 4 || dtype == spa::kPlanF32)) {
+  if (spa::decode_on_matrix_cores(t, dtype)) {
     std::printf("ok mm %d 0 0 0\n", p.splits);
     return 0;
   }

@@ -37,7 +37,8 @@ def _replay(exe, cases, rule=1):
 
 # (t, k, n_out, dtype, n, m, var): every fused-path shape of the GPU tests plus
 # long channel ranges (several passes of the workgroup's threads per split),
-# the largest k and the 2 GiB channel-major weight
+# the largest k and the 2 GiB channel-major weight; several tokens stream the
+# channel-major weight in float32 only (16-bit ones take the matrix cores)
 CASES = [
     (1, 262144, 4096, BF16, 8, 16, 0),       # exactly 2^31 bytes of weight
     (1, 262080, 4096, BF16, 8, 16, 0),
@@ -47,12 +48,14 @@ CASES = [
     (1, 1 << 24, 8, BF16, 1, 4, 0),
     (1, 1 << 24, 8, F32, 4, 4, 0),
     (1, 1024, 776, BF16, 8, 16, 0),
-    (2, 262144, 1024, BF16, 8, 16, 0),
-    (3, 1 << 20, 136, F16, 16, 32, 1),
-    (4, 1 << 20, 776, BF16, 8, 16, 0),
+    (2, 262144, 1024, F32, 8, 16, 0),
+    (3, 1 << 20, 136, F32, 16, 32, 1),
+    (4, 1 << 20, 776, F32, 8, 16, 0),
+    (2, 8192, 12288, F32, 8, 16, 0),
     (8, 65536, 64, F32, 2, 4, 1),
     (1, 4096, 14336, BF16, 8, 16, 0),        # one-token kernel (the decode layer)
     (8, 14336, 4096, F16, 16, 32, 1),        # matrix-core path (the batched layer)
+    (2, 4096, 14336, BF16, 8, 16, 0),        # matrix-core path from two 16-bit tokens
 ]
 
 
@@ -77,3 +80,11 @@ def test_pass_offset_counted_twice_overruns_the_list(driver):
     # had written, and the weight loads went far outside the weight
     res = _replay(driver, [CASES[0]], rule=0)[0]
     assert res[0] == "fail" and res[1] in ("slot_past_cap", "slot_unwritten"), res
+
+
+def test_decode_path_by_tokens_and_dtype(driver):
+    # one wide 16-bit token: the one-token kernel; two or more 16-bit tokens:
+    # the matrix cores; float32, and a narrow 16-bit token: the fused kernel
+    cases = [(1, 4096, 14336, BF16, 8, 16, 0), (2, 4096, 14336, BF16, 8, 16, 0), (4, 512, 136, F16, 16, 32, 1),
+             (2, 8192, 12288, F32, 8, 16, 0), (1, 1024, 776, BF16, 8, 16, 0)]
+    assert [r[1] for r in _replay(driver, cases)] == ["t1", "mm", "mm", "fused", "fused"]

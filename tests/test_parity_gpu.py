@@ -427,7 +427,15 @@ DECODE_CASES.append(wl.SPECS["decode"].with_(name="decode_given_shift", t=2, k=5
 DECODE_CASES.append(wl.SPECS["decode"].with_(name="fused_t1_f32_two_passes", t=1, k=32768, n_out=4096, dtype="f32"))
 DECODE_CASES.append(wl.SPECS["decode"].with_(name="fused_t1_bf16_2of4_two_passes", t=1, k=32768, n_out=2048, n=2,
                                              m=4))
-DECODE_CASES.append(wl.SPECS["decode"].with_(name="fused_t2_two_passes", t=2, k=8192, n_out=12288))
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="fused_f32_t2_two_passes", t=2, k=8192, n_out=12288, dtype="f32"))
+# two to four 16-bit tokens take the matrix-core path: wide and narrow outputs,
+# ragged tiles and a k that ends inside a 64-channel step
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="mm_t2_wide", t=2, k=8192, n_out=12288))
+DECODE_CASES.append(wl.SPECS["batched"].with_(name="mm_t2_clact_var", t=2, k=2080, n_out=520))
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="mm_t4_given", t=4, k=1040, n_out=200, shift="given"))
+# float32 with 2 and 3 tokens (the fused kernel's multi-token forms)
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="fused_f32_t2", t=2, k=1024, n_out=776, dtype="f32"))
+DECODE_CASES.append(wl.SPECS["batched"].with_(name="fused_f32_t3_clact_var", t=3, k=512, n_out=136, dtype="f32"))
 # the squared-ReLU input transform on every decode kernel: one token (wide and
 # narrow outputs), 2-4 tokens, float32, and the matrix-core path
 ACT = dict(act="relu2", x_dist="normal", n_outliers=0)
@@ -538,7 +546,7 @@ def test_decode_workspaces_of_equal_size_do_not_mix():
     # partial sums where its split counters should be zero
     dev = _dev()
     a = wl.SPECS["decode"].with_(t=1, k=1024, n_out=520, n=2, m=4, score="magnitude", shift="none", n_outliers=0)
-    b = wl.SPECS["decode"].with_(t=4, k=512, n_out=776, n=2, m=4, score="magnitude", shift="none", n_outliers=0)
+    b = wl.SPECS["decode"].with_(t=2, k=256, n_out=136, n=2, m=4, score="magnitude", shift="none", n_outliers=0)
     sizes = {spa.workspace_bytes(1, s.t, s.k, s.n_out, torch.bfloat16, _cfg(s)) for s in (a, b)}
     assert len(sizes) == 1, sizes
     runs = []

@@ -18,13 +18,14 @@ pytestmark = pytest.mark.gpu
 spa = pytest.importorskip("activation_sparsification_amd")
 
 # one-token kernel (8 channel splits; then 16 with the variance sums), then
-# the matrix-core path, then the fused kernel: each call smaller than the one
-# before, then the first again
+# the matrix-core path (20 tokens, then 3), then the fused kernel (float32):
+# each call smaller than the one before, then the first again
 CALLS = [
     ("decode_layer", wl.SPECS["decode"]),
     ("batched_t1", wl.SPECS["batched"].with_(t=1)),
     ("batched_t20", wl.SPECS["batched"].with_(t=20, k=2048, n_out=1000)),
-    ("fused_t3", wl.SPECS["batched"].with_(t=3, k=512, n_out=136)),
+    ("mm_t3", wl.SPECS["batched"].with_(t=3, k=1024, n_out=776)),
+    ("fused_f32_t3", wl.SPECS["batched"].with_(t=3, k=512, n_out=136, dtype="f32")),
     ("decode_layer_again", wl.SPECS["decode"]),
 ]
 
@@ -36,7 +37,7 @@ def test_static_decode_matches_workspace_decode():
         print(f"[no-alloc decode] {label}: t={spec.t} k={spec.k} n_out={spec.n_out} {spec.n}:{spec.m}", flush=True)
         x, w = wl.make_inputs(spec)
         xd = x.to(dev)
-        pw = spa.prepare_weight(w.to(dev), spec.alpha, want_wt=spec.t <= 4)
+        pw = spa.prepare_weight(w.to(dev), spec.alpha, want_wt=spec.t <= 1 or spec.dtype == "f32")
         cfg = spa.PruneConfig(spec.n, spec.m, spec.score, spec.shift, spec.var_rescale, spec.act)
         y0, i0, n0 = spa.sparse_linear_decode(xd, pw, cfg, want_idx=True, want_nu=True)
         y1, i1, n1 = spa.sparse_linear_decode_static(xd, pw, cfg, want_idx=True, want_nu=True)
