@@ -894,6 +894,41 @@ __global__ void __launch_bounds__(kPcThreads) k_prune_cols(DecodeArgs a) {
   const int ntb = (T_ + 15) / 16;
   const int c0 = blockIdx.x * CH, quarter = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // The token means, when this pass forms them (short calls, t k <= 65536; a
+  // separate pass otherwise): every workgroup sums every token row itself,
+  // wave w rows w, w + 16, ...: float64 over 16-byte loads (eight per lane in
+  // flight), then a fixed butterfly over the lanes.  Workgroup (0, 0) leaves
+  // the means in the workspace for the product's epilogue.
+  __shared__ float s_eta[kMaxTok];
+  const bool own_mean = a.shift == SPA_SHIFT_TOKEN_MEAN && a.eta == nullptr;
+  if (own_mean) {
+    const int nq = K / 8;                                   // k % 16 == 0: whole 16-byte pieces
+    for (int i = wv; i < T_; i += NW) {
+      const uint4* row = reinterpret_cast<const uint4*>(static_cast<const T*>(a.x) + (size_t)i * K);
+      double part = 0.0;
+      for (int q0 = 0; q0 < nq; q0 += 8 * 64) {
+        uint4 u[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int q = q0 + 64 * r + lane;
+          u[r] = q < nq ? row[q] : make_uint4(0u, 0u, 0u, 0u);   // zeros add nothing (also squared)
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part += (double)apply_act<DT>(elem16<DT>(u[r], e), a.act);
+      }
+      part += lane_xor_f64<1>(part);
+      part += lane_xor_f64<2>(part);
+      part += lane_xor_f64<4>(part);
+      part += lane_xor_f64<8>(part);
+      part += lane_xor_f64<16>(part);
+      part += lane_xor_f64<32>(part);
+      if (lane == 0) s_eta[i] = (float)(part / (double)K);
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && blockIdx.y == 0 && (int)threadIdx.x < T_) a.eta_ws[threadIdx.x] = s_eta[threadIdx.x];
+  }
   {
     // thread (c, p) stages channel c0 + c of tokens p, p + 4, ...: all loads
     // issued before any is used (buffer loads; offsets past the end read
@@ -907,7 +942,7 @@ __global__ void __launch_bounds__(kPcThreads) k_prune_cols(DecodeArgs a) {
     for (int j2 = 0; j2 < kMaxTok / 4; ++j2) {
       const int i = p + 4 * j2;
       raw[j2] = buffer_load_u16(xr, i < T_ && ch < K ? (uint32_t)(i * K + ch) * 2u : kBufferOutOfRange);
-      eta[j2] = a.eta != nullptr && i < T_ ? a.eta[i] : 0.f;
+      eta[j2] = i >= T_ ? 0.f : own_mean ? s_eta[i] : a.eta != nullptr ? a.eta[i] : 0.f;
     }
 #pragma unroll
     for (int j2 = 0; j2 < kMaxTok / 4; ++j2) {
@@ -1322,9 +1357,9 @@ static hipError_t fused_tok(DecodeArgs& a, hipStream_t st) {
 template <int DT>
 static hipError_t decode_dt(DecodeArgs& a, hipStream_t st) {
   const bool fused = !decode_on_matrix_cores(a.t, DT);
-  // the token mean ahead of the main kernel: for long fused rows, and for CLACT
-  // (its column norms are taken over the shifted values)
-  const bool mean_first = fused ? (size_t)a.t * a.k > 65536 : true;
+  // the token mean ahead of the main kernel for long rows; shorter calls form
+  // it inside the fused kernel or the matrix-core path's pruning pass
+  const bool mean_first = (size_t)a.t * a.k > 65536;
   if (a.shift == SPA_SHIFT_TOKEN_MEAN && mean_first) {
     if (hipError_t e = launch_token_mean(DT, a.x, a.t, a.k, a.act, a.eta_ws, st)) return e;
     a.eta = a.eta_ws;
@@ -1347,6 +1382,7 @@ static hipError_t decode_dt(DecodeArgs& a, hipStream_t st) {
       default: hipLaunchKernelGGL((k_prune_cols<DT, 32>), pg, dim3(kPcThreads), 0, st, a); break;
     }
     if (hipError_t e = hipGetLastError()) return e;
+    if (a.shift == SPA_SHIFT_TOKEN_MEAN) a.eta = a.eta_ws;   // the means the pass (or the mean pass) wrote
     // ... then one pass over the row-major weight on the matrix cores
     if (a.t <= 16)
       hipLaunchKernelGGL((k_decode_mm<DT, 1>), dim3(a.tiles * a.splits), dim3(512), 0, st, a);

@@ -60,6 +60,12 @@ ROOFLINE = {
                        per_unit="one union channel's weights: n_out x 2 B = 8,192 B; plus x and y"),
     "batched_t32": dict(profile="decode_mm_f16_batched_t32_k14336_n4096", kernel="k_prune_cols<f16,32> + k_decode_mm<f16,2>", bound="hbm", sources=DECODE_SOURCES,
                         per_unit="one union channel's weights: n_out x 2 B = 8,192 B; plus x and y"),
+    "decode_t4": dict(profile="decode_mm_bf16_t4_k4096_n14336", kernel="k_token_mean + k_prune_cols<bf16,16> + k_decode_mm<bf16,1>", bound="hbm",
+                      sources=DECODE_SOURCES + [CSRC + "k_prune.hip"],
+                      per_unit="one union channel's weights: n_out x 2 B = 28,672 B; plus x, the channel factors, the row sums and y "
+                               "(the pass reads all of W)"),
+    "batched_t4": dict(profile="decode_mm_f16_batched_t4_k14336_n4096", kernel="k_prune_cols<f16,32> + k_decode_mm<f16,1>", bound="hbm", sources=DECODE_SOURCES,
+                       per_unit="one union channel's weights: n_out x 2 B = 8,192 B; plus x and y (the pass reads all of W)"),
     "prefill": dict(profile="gemm24_bf16_prefill_t2048_k4096_n14336", kernel="k_prune24<bf16,1> + k_gemm24<bf16,16> (256 columns) + k_gemm24<bf16,12> (192 columns)", bound="mfma", sources=PREFILL_SOURCES,
                     per_unit="one 256 x 256 x 64 tile step: 4.19 MFLOP kept (2 t n_out k n/m in all)"),
     "relu2": dict(profile="gemm24_bf16_relu2_t4096_k16384_n4096", kernel="k_prune24_rows<bf16,16> + k_gemm24<bf16,8>", bound="mfma", sources=PREFILL_SOURCES,
@@ -74,7 +80,9 @@ WORKLOADS = {
     "prefill": ("prefill", dict()),
     "relu2": ("relu2", dict()),
     "relu2_fused": ("relu2_fused", dict()),
+    "decode_t4": ("decode", dict(t=4)),
     "batched_t1": ("batched", dict(t=1)),
+    "batched_t4": ("batched", dict(t=4)),
     "batched_t8": ("batched", dict(t=8)),
     "batched_t32": ("batched", dict(t=32)),
 }
@@ -85,6 +93,8 @@ DESCRIPTION = {
     "relu2_fused": "the same down-projection fed its pre-activation U[4096,16384] bf16; the squared ReLU "
                    "is applied inside the pruning pass",
     "batched_t1": "batched decode 16:32 CLACT + variance rescale, X[1,14336] fp16, W[4096,14336] fp16",
+    "decode_t4": "small-batch decode, the decode layer with 4 tokens: X[4,4096] bf16, W[14336,4096] bf16, matrix cores",
+    "batched_t4": "batched decode 16:32 CLACT + variance rescale, X[4,14336] fp16, W[4096,14336] fp16",
     "batched_t8": "batched decode 16:32 CLACT + variance rescale, X[8,14336] fp16, W[4096,14336] fp16",
     "batched_t32": "batched decode 16:32 CLACT + variance rescale, X[32,14336] fp16, W[4096,14336] fp16",
 }
@@ -581,7 +591,7 @@ def main():
     head = measure(args.workload, args.steps, args.warmup)
     secondary = []
     if not args.only:
-        for name in ["prefill", "relu2", "relu2_fused", "batched_t1", "batched_t8", "batched_t32"]:
+        for name in ["prefill", "relu2", "relu2_fused", "decode_t4", "batched_t1", "batched_t4", "batched_t8", "batched_t32"]:
             if name == args.workload:
                 continue
             st = max(10, args.steps // 4) if name in ("prefill", "relu2", "relu2_fused") else args.steps
