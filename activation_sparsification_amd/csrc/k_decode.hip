@@ -886,7 +886,7 @@ __global__ void __launch_bounds__(kPcThreads) k_prune_cols(DecodeArgs a) {
   using T = typename Dt<DT>::T;
   constexpr int CH = kPruneChan, NW = kPcThreads / 64;
   static_assert(CH == 256 && NW == 16, "four waves per 64-channel group, one channel per lane");
-  __shared__ float s_x[kMaxTok][CH];
+  __shared__ __attribute__((aligned(16))) float s_x[kMaxTok][CH];
   __shared__ __attribute__((aligned(16))) unsigned long long s_sc[NW][64];   // per wave: the current token's rank keys
   __shared__ __attribute__((aligned(16))) uint16_t s_mv[NW][64];   // per wave: its masked values
   __shared__ double s_st[4][kMaxTok / 4][4];
@@ -930,25 +930,22 @@ __global__ void __launch_bounds__(kPcThreads) k_prune_cols(DecodeArgs a) {
     if (blockIdx.x == 0 && blockIdx.y == 0 && (int)threadIdx.x < T_) a.eta_ws[threadIdx.x] = s_eta[threadIdx.x];
   }
   {
-    // thread (c, p) stages channel c0 + c of tokens p, p + 4, ...: all loads
-    // issued before any is used (buffer loads; offsets past the end read
-    // zeros); rows past t are zero
-    const int c = threadIdx.x % CH, p = threadIdx.x / CH, ch = c0 + c;
+    // thread (i, p) stages channels c0 + 8 p .. + 7 of token i = thread / 32
+    // with one 16-byte buffer load (offsets past the end read zeros); rows
+    // past t, and channels past k, are zero
+    const int i = threadIdx.x >> 5, p = threadIdx.x & 31, ch = c0 + 8 * p;
+    static_assert(kPcThreads == kMaxTok * CH / 8, "one 16-byte piece per thread");
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.x), (short)0, T_ * K * 2, kBufferWord3);
-    uint32_t raw[kMaxTok / 4];
-    float eta[kMaxTok / 4];
+    const bool in = i < T_ && ch < K;                       // k % 16 == 0: a piece is wholly in or out
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, in ? (int)((uint32_t)(i * K + ch) * 2u) : (int)kBufferOutOfRange, 0, 0);
+    const float eta = i >= T_ ? 0.f : own_mean ? s_eta[i] : a.eta != nullptr ? a.eta[i] : 0.f;
+    const uint4 u = make_uint4(v[0], v[1], v[2], v[3]);
+    float xs[8];
 #pragma unroll
-    for (int j2 = 0; j2 < kMaxTok / 4; ++j2) {
-      const int i = p + 4 * j2;
-      raw[j2] = buffer_load_u16(xr, i < T_ && ch < K ? (uint32_t)(i * K + ch) * 2u : kBufferOutOfRange);
-      eta[j2] = i >= T_ ? 0.f : own_mean ? s_eta[i] : a.eta != nullptr ? a.eta[i] : 0.f;
-    }
-#pragma unroll
-    for (int j2 = 0; j2 < kMaxTok / 4; ++j2) {
-      const int i = p + 4 * j2;
-      s_x[i][c] = i < T_ && ch < K ? apply_act<DT>(to_f32<DT>((T)raw[j2]), a.act) - eta[j2] : 0.f;
-    }
+    for (int e = 0; e < 8; ++e) xs[e] = in ? apply_act<DT>(elem16<DT>(u, e), a.act) - eta : 0.f;
+    *reinterpret_cast<float4*>(&s_x[i][8 * p]) = make_float4(xs[0], xs[1], xs[2], xs[3]);
+    *reinterpret_cast<float4*>(&s_x[i][8 * p + 4]) = make_float4(xs[4], xs[5], xs[6], xs[7]);
   }
   __syncthreads();
   // this lane's channel (wave w: group w % 4) and its factor
@@ -961,12 +958,9 @@ __global__ void __launch_bounds__(kPcThreads) k_prune_cols(DecodeArgs a) {
   } else if (a.score == SPA_SCORE_CLACT) {
     // column energy over the call's tokens, tokens in order; the zero rows
     // past t add exactly nothing
-    float v[kMaxTok];
-#pragma unroll
-    for (int i = 0; i < kMaxTok; ++i) v[i] = s_x[i][c];
     float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxTok; ++i) acc = clact_accumulate(acc, v[i]);
+#pragma unroll 8
+    for (int i = 0; i < T_; ++i) acc = clact_accumulate(acc, s_x[i][c]);
     f = sqrt_rn(acc);
   }
   const int j = lane % M, b0 = lane - j;                   // position in the block, its first lane
