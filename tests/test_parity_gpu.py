@@ -433,6 +433,12 @@ DECODE_CASES.append(wl.SPECS["decode"].with_(name="fused_f32_t2_two_passes", t=2
 DECODE_CASES.append(wl.SPECS["decode"].with_(name="mm_t2_wide", t=2, k=8192, n_out=12288))
 DECODE_CASES.append(wl.SPECS["batched"].with_(name="mm_t2_clact_var", t=2, k=2080, n_out=520))
 DECODE_CASES.append(wl.SPECS["decode"].with_(name="mm_t4_given", t=4, k=1040, n_out=200, shift="given"))
+# the token mean on the matrix-core path: formed inside the pruning pass up to
+# t k = 65536 (the limit itself here), by a pass of its own beyond it
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="mm_t16_mean_in_pass_at_limit", t=16, k=4096, n_out=264))
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="mm_t8_mean_pass_long_rows", t=8, k=16384, n_out=264))
+DECODE_CASES.append(wl.SPECS["decode"].with_(name="mm_t3_mean_pass_relu2", t=3, k=32768, n_out=136, act="relu2",
+                                             x_dist="normal", n_outliers=0))
 # float32 with 2 and 3 tokens (the fused kernel's multi-token forms)
 DECODE_CASES.append(wl.SPECS["decode"].with_(name="fused_f32_t2", t=2, k=1024, n_out=776, dtype="f32"))
 DECODE_CASES.append(wl.SPECS["batched"].with_(name="fused_f32_t3_clact_var", t=3, k=512, n_out=136, dtype="f32"))
