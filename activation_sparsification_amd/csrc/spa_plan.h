@@ -138,10 +138,13 @@ inline DecodePlan plan_decode(int t, int k, int n_out, int dtype, int n, int m, 
   } else {
     // matrix-core path: prune once into masked rows (channel chunks of
     // kPruneChan), then one pass over w by 64-row tiles, split over k until
-    // about 256 workgroups run
+    // about 256 workgroups run; from 192 tiles on, no split (one round of
+    // workgroups and no hand-off: 224 tiles x 2 splits, 1.75 rounds on 256
+    // CUs, took 29.4-29.9 us at 2 and 4 tokens of the 14336 x 4096 layer,
+    // 224 unsplit tiles 26.0-26.1 us)
     p.tiles = (n_out + 63) / 64;
     const int nsteps = (k + 63) / 64;
-    int sp = (256 + p.tiles - 1) / p.tiles;
+    int sp = p.tiles >= 192 ? 1 : (256 + p.tiles - 1) / p.tiles;
     if (sp > nsteps) sp = nsteps;
     const int sps = (nsteps + sp - 1) / sp;
     p.k_len = sps * 64;
